@@ -1,0 +1,147 @@
+/*
+ * hqml -- batched state-vector training step of a hardware-efficient ansatz
+ * on AMD Instinct MI355X (gfx950), with gate fusion in the forward pass and in
+ * the adjoint backward pass.
+ *
+ * The operation (Kawase, "Fast and memory-efficient classical simulation of
+ * quantum machine learning via forward and backward gate fusion",
+ * arXiv:2603.02804; hugo-pages summary, sections 1.2 and 2.1):
+ *   per sample b, psi_0 = prod_q Ry(x[b][q]) |0...0>; then L layers, each
+ *   applying Rx(theta[l][q][0]), Ry(theta[l][q][1]), Rz(theta[l][q][2]) to every
+ *   qubit q followed by CZ(q, q+1) for q = 0..n-2; R_s(t) = exp(-i t s/2);
+ *   qubit q is bit q of the amplitude index.  E_b = <psi_M|Z_0|psi_M>.
+ *   The gradient is the adjoint-method gradient of section 1.2:
+ *   dL/dtheta_j = Re<lambda_j| dU_j/dtheta_j |psi_{j-1}>, lambda_{j-1} = U_j^dag lambda_j,
+ *   seeded with lambda_M = 2 (dL/dE_b) Z_0 psi_M, summed over the batch.
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers to contiguous row-major fp32
+ *     arrays owned by the caller; the library never frees or keeps them.
+ *     x: [B][n] encoding angles; theta: [L][n][3] (Rx, Ry, Rz angle of qubit q
+ *     in layer l); y: [B] labels; expz: [B]; loss: [1]; grad: [L][n][3];
+ *     dL_dE: [B].
+ *   - Work is queued on the context's stream and is asynchronous: outputs are
+ *     valid once that stream has synchronised.  Argument errors are detected
+ *     on the host before anything is queued.
+ *   - Return value: HQML_OK or a negative hqml_status.  On error, outputs are
+ *     unspecified, nothing leaks, and hqml_last_error(ctx) describes it.
+ *     No entry point aborts or throws across the ABI.
+ *   - Results are bitwise reproducible: every reduction has a fixed order and
+ *     no floating-point atomics are used.
+ *   - A context is used by one host thread at a time; distinct contexts are
+ *     independent.
+ */
+#ifndef HQML_H
+#define HQML_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct hqml_ctx hqml_ctx;
+
+typedef enum {
+    HQML_OK = 0,
+    HQML_ERR_ARG = -1,          /* invalid argument (null pointer, size out of range) */
+    HQML_ERR_OOM = -2,          /* device memory could not be reserved */
+    HQML_ERR_HIP = -3,          /* a HIP runtime call or kernel launch failed */
+    HQML_ERR_STATE = -4,        /* call out of order (e.g. backward without a saved forward) */
+    HQML_ERR_UNSUPPORTED = -5   /* valid request this build does not implement */
+} hqml_status;
+
+typedef enum {
+    HQML_STORE_FP32 = 0,        /* saved states as complex fp32 (8 bytes per amplitude) */
+    HQML_STORE_BF16 = 1         /* saved states as bf16 (re, im) pairs, round to nearest even;
+                                   arithmetic stays fp32 (the pages' mem-save mode, section 2.3) */
+} hqml_storage;
+
+typedef struct {
+    int n_qubits;      /* 1..29 */
+    int n_layers;      /* >= 1 */
+    int max_batch;     /* >= 1; workspaces are sized for this many samples */
+    int storage;       /* hqml_storage */
+    int ckpt_block;    /* 0: keep every fused-pass output for the backward pass;
+                          b > 0: keep only one state every b layers and recompute the
+                          block's forward passes during the backward pass
+                          (gradient checkpointing, section 2.3) */
+    int device;        /* HIP device ordinal */
+    void *stream;      /* hipStream_t to queue work on; NULL = the null stream */
+} hqml_config;
+
+/* Device bytes hqml_create would reserve for cfg.  Host-only: makes no HIP call.
+ * Returns 0 for an invalid cfg. */
+size_t hqml_workspace_bytes(const hqml_config *cfg);
+
+/* Validate cfg, reserve every device workspace once, and return a context in
+ * *out.  HQML_ERR_OOM if the workspace exceeds the device's free memory (checked
+ * before any allocation) or an allocation fails.  Nothing is allocated later. */
+int hqml_create(const hqml_config *cfg, hqml_ctx **out);
+
+/* Release the context and its workspaces (waits for its stream).  NULL is a no-op. */
+int hqml_destroy(hqml_ctx *ctx);
+
+/* Forward pass for B samples (0 <= B <= max_batch): expz[b] = <Z_0> of sample b.
+ * save_for_backward != 0 keeps what hqml_backward needs (the fused-pass outputs,
+ * or checkpoints) until the next forward on this context.  B == 0 queues nothing. */
+int hqml_forward(hqml_ctx *ctx, int B, const float *x, const float *theta, float *expz,
+                 int save_for_backward);
+
+/* Adjoint backward pass for the batch of the last hqml_forward(..., 1) on this
+ * context: grad[l][q][a] = sum_b dL_dE[b] * dE_b/dtheta[l][q][a] (fp64 reduction,
+ * stored as fp32).  HQML_ERR_STATE if no forward was saved; theta and x are the
+ * ones that forward saw. */
+int hqml_backward(hqml_ctx *ctx, const float *dL_dE, float *grad);
+
+/* One training step with the mean-squared-error loss on <Z_0> (the pages' training
+ * objective; mean over the batch): expz = E_b, loss = (1/B) sum_b (E_b - y_b)^2,
+ * grad = dloss/dtheta.  1 <= B <= max_batch.  Equivalent to forward + backward with
+ * dL_dE[b] = 2 (E_b - y_b) / B, with the last fused pass of the forward sweep and the
+ * first of the backward sweep run as one kernel. */
+int hqml_train_step(hqml_ctx *ctx, int B, const float *x, const float *theta, const float *y,
+                    float *expz, float *loss, float *grad);
+
+/* Static text for a status code. */
+const char *hqml_status_str(int status);
+
+/* Text of the last error on ctx ("" if none); with ctx == NULL, the last error of
+ * hqml_create on this thread. */
+const char *hqml_last_error(const hqml_ctx *ctx);
+
+/* ---- instrumentation (benchmarking; not needed for training) ---- */
+
+/* Kernel families timed by hqml_kernel_times. */
+typedef enum {
+    HQML_K_FWD_PASS = 0,    /* fused forward tile pass (one per fused block) */
+    HQML_K_BWD_PASS = 1,    /* fused adjoint tile pass (one per fused block) */
+    HQML_K_SMALL = 2,       /* whole-circuit kernel for n <= 13 */
+    HQML_K_OTHER = 3,       /* table preparation and reductions */
+    HQML_K_COUNT = 4
+} hqml_kernel_kind;
+
+/* Enable (1) or disable (0) per-launch HIP event timing on ctx's stream.  While
+ * enabled, every kernel launch is bracketed by a pair of HIP events. */
+int hqml_set_timing(hqml_ctx *ctx, int enable);
+
+/* Synchronise ctx's stream and report, per hqml_kernel_kind, the summed event time
+ * in milliseconds (ms[HQML_K_COUNT]) and the number of launches (count[HQML_K_COUNT])
+ * since timing was enabled or last reset; reset != 0 clears the counters. */
+int hqml_kernel_times(hqml_ctx *ctx, double *ms, long long *count, int reset);
+
+/* Plan facts for reporting: fused forward passes per training step, backward
+ * passes per training step, tile workgroups per pass, bytes of state per sample. */
+int hqml_plan_info(const hqml_ctx *ctx, int *fwd_passes, int *bwd_passes,
+                   int *tiles_per_sample, size_t *state_bytes);
+
+/* JSON description of the fused-pass schedule hqml_create would use for cfg (views,
+ * passes, where each layer's gradient statistics are formed).  Host-only.  Writes at
+ * most len bytes including the terminating NUL and returns the full length needed
+ * (excluding the NUL), or a negative hqml_status for an invalid cfg. */
+long long hqml_describe_plan(const hqml_config *cfg, char *buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HQML_H */

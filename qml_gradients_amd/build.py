@@ -1,0 +1,44 @@
+"""Build the hqml shared library (libhqml.so) in-tree with hipcc for gfx950.
+
+    python -m qml_gradients_amd.build          # or: python qml_gradients_amd/build.py
+
+Always recompiles.  The library is written next to this file; the Python binding
+loads it from there.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libhqml.so")
+SOURCES = ["hqml_kernels.hip", "hqml_abi.cpp", "hqml_plan.cpp"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = os.environ.get("HQML_OFFLOAD_ARCH", "gfx950")
+
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}",
+    # keep packed-FP32 instructions out of the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + f".tmp{os.getpid()}"
+    cmd = [HIPCC, *FLAGS, "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
+    sys.exit(0)

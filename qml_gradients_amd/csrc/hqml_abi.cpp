@@ -1,0 +1,582 @@
+// C ABI of the hqml library: argument checks, workspace ownership, and the order
+// of kernel launches for forward, backward and training steps.
+//
+// Backward gate fusion (hugo-pages summary, section 1.4 item 2): each backward
+// pass reads the saved output of one fused forward pass and the adjoint state,
+// re-derives the pass's input on chip with U^dagger while forming the gradient
+// terms, and writes the propagated adjoint state.  Gradient checkpointing
+// (section 2.3): with ckpt_block = b, only one state every b layers is kept and a
+// block's forward passes are recomputed just before its backward passes.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/hqml.h"
+#include "hqml_internal.hpp"
+#include "hqml_plan.hpp"
+
+namespace hqml {
+hipError_t launch_prep(const float *theta, const float *x, int L, int n, int B, double *zyz, float *rot_cs,
+                       float *dw, double *H, float *init_u, hipStream_t s);
+hipError_t launch_tile_fwd(const TilePassArgs &a, int B, int storage, hipStream_t s);
+hipError_t launch_tile_bwd(const TilePassArgs &a, int B, int storage, hipStream_t s);
+hipError_t launch_small(const SmallArgs &a, int B, hipStream_t s);
+hipError_t configure_small(size_t shm_bytes);
+hipError_t launch_ez_reduce(const float *e_part, int B, int T, const float *y, float *e_out, float *loss,
+                            double *dlde, double *e_work, hipStream_t s);
+hipError_t launch_copy_dlde(const float *src, int B, double *dlde, hipStream_t s);
+hipError_t launch_stats_reduce(const float *part, const int2 *map, int B, int L, int n, int T, int pass_lo,
+                               int pass_hi, double *S, hipStream_t s);
+hipError_t launch_grad_reduce(const double *S, const double *H, const double *dlde, int B, int L, int n,
+                              float *grad, hipStream_t s);
+}  // namespace hqml
+
+using namespace hqml;
+
+struct hqml_ctx {
+    hqml_config cfg{};
+    Plan plan;
+    Workspace ws;
+    hipStream_t stream = nullptr;
+    std::vector<void *> allocs;
+    // device buffers
+    char *saved = nullptr;       // saved states (n_saved buffers of max_batch samples)
+    float *lam = nullptr;
+    float *part = nullptr;
+    float *e_part = nullptr;
+    double *S = nullptr;
+    double *zyz = nullptr;
+    float *rot_cs = nullptr;
+    float *dw = nullptr;
+    double *H = nullptr;
+    float *init_u = nullptr;
+    ViewDev *views = nullptr;
+    int2 *statmap = nullptr;
+    double *dlde = nullptr;
+    double *e_work = nullptr;
+    float *loss_tmp = nullptr;
+    // saved-forward bookkeeping
+    int saved_B = -1;
+    std::string err;
+    // instrumentation
+    bool timing = false;
+    struct Rec {
+        int kind;
+        hipEvent_t a, b;
+    };
+    std::vector<Rec> recs;
+    std::vector<hipEvent_t> pool;
+    size_t pool_used = 0;
+};
+
+namespace {
+
+thread_local std::string g_create_err;
+
+int fail(hqml_ctx *c, int code, const std::string &msg)
+{
+    if (c) c->err = msg;
+    else g_create_err = msg;
+    return code;
+}
+
+int hip_fail(hqml_ctx *c, hipError_t e, const char *what)
+{
+    return fail(c, HQML_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t elem_bytes(const hqml_ctx *c) { return c->cfg.storage == HQML_STORE_BF16 ? 4 : 8; }
+
+hipEvent_t take_event(hqml_ctx *c)
+{
+    if (c->pool_used == c->pool.size()) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        c->pool.push_back(e);
+    }
+    return c->pool[c->pool_used++];
+}
+
+template <class F>
+int run(hqml_ctx *c, int kind, const char *what, F f)
+{
+    hipEvent_t a = nullptr, b = nullptr;
+    if (c->timing) {
+        a = take_event(c);
+        b = take_event(c);
+        if (a && b) (void)hipEventRecord(a, c->stream);
+    }
+    hipError_t e = f();
+    if (c->timing && a && b) {
+        (void)hipEventRecord(b, c->stream);
+        c->recs.push_back({kind, a, b});
+    }
+    if (e != hipSuccess) return hip_fail(c, e, what);
+    return HQML_OK;
+}
+
+// Saved state buffer i (each holds max_batch samples).
+void *saved_buf(hqml_ctx *c, int i)
+{
+    return c->saved + (size_t)i * c->ws.state_bytes;
+}
+
+// Where the output of forward pass p lives (same mapping in the forward sweep, the
+// checkpoint recompute and the backward sweep).
+void *pass_out(hqml_ctx *c, int p)
+{
+    const Plan &pl = c->plan;
+    if (pl.c == 0) return saved_buf(c, p);
+    const int k = p / pl.c, lo = k * pl.c;
+    const int P = pl.n_fwd();
+    const int hi = std::min(P, lo + pl.c);
+    if (p == hi - 1 && k < pl.nblocks - 1) return saved_buf(c, pl.c + k);   // checkpoint k+1
+    return saved_buf(c, p - lo);
+}
+
+TilePassArgs base_args(hqml_ctx *c)
+{
+    TilePassArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.lam = c->lam;
+    a.e_part = c->e_part;
+    a.rot_cs = c->rot_cs;
+    a.dw = c->dw;
+    a.init_u = c->init_u;
+    a.n = c->plan.n;
+    a.L = c->plan.L;
+    a.T = c->plan.T;
+    return a;
+}
+
+int fwd_pass(hqml_ctx *c, int B, int p, int extra_flags)
+{
+    const PassPlan &pp = c->plan.fwd[p];
+    TilePassArgs a = base_args(c);
+    a.view = c->views + pp.view;
+    a.psi_in = p == 0 ? nullptr : pass_out(c, p - 1);
+    a.psi_out = pass_out(c, p);
+    a.rotA = pp.rotA;
+    a.diag = pp.diag;
+    a.rotB = pp.rotB;
+    a.flags = (pp.init ? PF_INIT : 0) | PF_STORE | extra_flags;
+    return run(c, HQML_K_FWD_PASS, "forward pass launch",
+               [&] { return launch_tile_fwd(a, B, c->cfg.storage, c->stream); });
+}
+
+// Backward pass k (forward pass index, or n_fwd + i for the i-th layer-0 stats-only pass).
+int bwd_pass(hqml_ctx *c, int B, int k, int part_lo, float *part_base, int extra_flags)
+{
+    const Plan &pl = c->plan;
+    const int P = pl.n_fwd();
+    TilePassArgs a = base_args(c);
+    a.stat_part = part_base + (size_t)(k - part_lo) * B * pl.T * kSlots;
+    if (k >= P) {
+        a.view = c->views + pl.stats_only[k - P];
+        a.rotA = a.diag = a.rotB = -1;
+        a.flags = PF_STATS_ONLY | PF_INIT;
+    } else {
+        const PassPlan &pp = pl.fwd[k];
+        a.view = c->views + pp.view;
+        a.rotA = pp.rotA;
+        a.diag = pp.diag;
+        a.rotB = pp.rotB;
+        a.flags = (pp.init ? PF_INIT : 0) | extra_flags;
+        if (extra_flags & PF_FUSED)
+            a.psi_in = k == 0 ? nullptr : pass_out(c, k - 1);
+        else
+            a.psi_in = pass_out(c, k);
+    }
+    return run(c, HQML_K_BWD_PASS, "backward pass launch",
+               [&] { return launch_tile_bwd(a, B, c->cfg.storage, c->stream); });
+}
+
+int prep(hqml_ctx *c, int B, const float *x, const float *theta)
+{
+    return run(c, HQML_K_OTHER, "table preparation", [&] {
+        return launch_prep(theta, x, c->plan.L, c->plan.n, B, c->zyz, c->rot_cs, c->dw, c->H, c->init_u,
+                           c->stream);
+    });
+}
+
+int check_config(const hqml_config *cfg, Plan *plan, std::string *err)
+{
+    if (!cfg) {
+        *err = "cfg is NULL";
+        return HQML_ERR_ARG;
+    }
+    if (cfg->max_batch < 1) {
+        *err = "max_batch must be >= 1";
+        return HQML_ERR_ARG;
+    }
+    if (cfg->storage != HQML_STORE_FP32 && cfg->storage != HQML_STORE_BF16) {
+        *err = "storage must be HQML_STORE_FP32 or HQML_STORE_BF16";
+        return HQML_ERR_ARG;
+    }
+    if (!make_plan(cfg->n_qubits, cfg->n_layers, cfg->ckpt_block, plan, err)) return HQML_ERR_ARG;
+    if (!plan->small && (size_t)cfg->max_batch * plan->T > 0x7FFFFFFFull) {
+        *err = "max_batch * tiles per sample exceeds the grid limit";
+        return HQML_ERR_ARG;
+    }
+    return HQML_OK;
+}
+
+// Forward sweep of the tile path.  'fuse_last' leaves the last pass to the caller.
+int tile_forward_sweep(hqml_ctx *c, int B, bool fuse_last)
+{
+    const Plan &pl = c->plan;
+    const int P = pl.n_fwd();
+    const int last = fuse_last ? P - 1 : P;
+    for (int p = 0; p < last; ++p) {
+        const int rc = fwd_pass(c, B, p, (!fuse_last && p == P - 1) ? PF_EMIT_E : 0);
+        if (rc) return rc;
+    }
+    return HQML_OK;
+}
+
+// Backward sweep of the tile path.  The last forward pass is either fused here
+// (train_step: forward ops, E, seed, adjoint ops in one kernel) or seeded from its
+// saved output.
+int tile_backward_sweep(hqml_ctx *c, int B, bool fused_last)
+{
+    const Plan &pl = c->plan;
+    const int P = pl.n_fwd();
+    const int nso = (int)pl.stats_only.size();
+    int rc;
+    const int2 *map = c->statmap;
+    if (pl.c == 0) {
+        for (int k = P - 1; k >= 0; --k) {
+            int fl = 0;
+            if (k == P - 1) fl = fused_last ? (PF_FUSED | PF_EMIT_E) : PF_SEED;
+            if ((rc = bwd_pass(c, B, k, 0, c->part, fl))) return rc;
+        }
+        for (int i = 0; i < nso; ++i)
+            if ((rc = bwd_pass(c, B, P + i, 0, c->part, 0))) return rc;
+        return run(c, HQML_K_OTHER, "statistics reduction", [&] {
+            return launch_stats_reduce(c->part, map, B, pl.L, pl.n, pl.T, 0, P + nso, c->S, c->stream);
+        });
+    }
+    for (int k = pl.nblocks - 1; k >= 0; --k) {
+        const int lo = k * pl.c, hi = std::min(P, lo + pl.c);
+        if (k < pl.nblocks - 1) {
+            for (int p = lo; p < hi - 1; ++p)
+                if ((rc = fwd_pass(c, B, p, 0))) return rc;
+        }
+        for (int p = hi - 1; p >= lo; --p) {
+            int fl = 0;
+            if (p == P - 1) fl = fused_last ? (PF_FUSED | PF_EMIT_E) : PF_SEED;
+            if ((rc = bwd_pass(c, B, p, lo, c->part, fl))) return rc;
+        }
+        rc = run(c, HQML_K_OTHER, "statistics reduction", [&] {
+            return launch_stats_reduce(c->part, map, B, pl.L, pl.n, pl.T, lo, hi, c->S, c->stream);
+        });
+        if (rc) return rc;
+    }
+    float *so_base = c->part + (size_t)pl.c * B * pl.T * kSlots;
+    for (int i = 0; i < nso; ++i)
+        if ((rc = bwd_pass(c, B, P + i, P, so_base, 0))) return rc;
+    if (nso > 0)
+        return run(c, HQML_K_OTHER, "statistics reduction", [&] {
+            return launch_stats_reduce(so_base, map, B, pl.L, pl.n, pl.T, P, P + nso, c->S, c->stream);
+        });
+    return HQML_OK;
+}
+
+SmallArgs small_args(hqml_ctx *c, int mode)
+{
+    SmallArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.init_u = c->init_u;
+    a.rot_cs = c->rot_cs;
+    a.dw = c->dw;
+    a.psi_save = reinterpret_cast<float *>(c->saved);
+    a.e_out = c->e_part;
+    a.stats = c->S;
+    a.n = c->plan.n;
+    a.L = c->plan.L;
+    a.mode = mode;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hqml_workspace_bytes(const hqml_config *cfg)
+{
+    Plan plan;
+    std::string err;
+    if (check_config(cfg, &plan, &err) != HQML_OK) return 0;
+    return size_workspace(plan, cfg->max_batch, cfg->storage).total;
+}
+
+long long hqml_describe_plan(const hqml_config *cfg, char *buf, size_t len)
+{
+    Plan plan;
+    std::string err;
+    const int rc = check_config(cfg, &plan, &err);
+    if (rc != HQML_OK) return rc;
+    const std::string s = describe_plan(plan);
+    if (buf && len > 0) {
+        const size_t k = std::min(len - 1, s.size());
+        std::memcpy(buf, s.data(), k);
+        buf[k] = '\0';
+    }
+    return (long long)s.size();
+}
+
+int hqml_create(const hqml_config *cfg, hqml_ctx **out)
+{
+    if (!out) return fail(nullptr, HQML_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    Plan plan;
+    std::string err;
+    int rc = check_config(cfg, &plan, &err);
+    if (rc != HQML_OK) return fail(nullptr, rc, err);
+    hqml_ctx *c = new (std::nothrow) hqml_ctx;
+    if (!c) return fail(nullptr, HQML_ERR_OOM, "host allocation failed");
+    c->cfg = *cfg;
+    c->plan = plan;
+    c->ws = size_workspace(plan, cfg->max_batch, cfg->storage);
+    c->stream = reinterpret_cast<hipStream_t>(cfg->stream);
+    hipError_t e = hipSetDevice(cfg->device);
+    if (e != hipSuccess) {
+        delete c;
+        return fail(nullptr, HQML_ERR_HIP, std::string("hipSetDevice: ") + hipGetErrorString(e));
+    }
+    size_t free_b = 0, total_b = 0;
+    e = hipMemGetInfo(&free_b, &total_b);
+    if (e != hipSuccess) {
+        delete c;
+        return fail(nullptr, HQML_ERR_HIP, std::string("hipMemGetInfo: ") + hipGetErrorString(e));
+    }
+    if (c->ws.total > free_b) {
+        char msg[160];
+        std::snprintf(msg, sizeof msg, "workspace needs %zu bytes, device has %zu free", c->ws.total, free_b);
+        delete c;
+        return fail(nullptr, HQML_ERR_OOM, msg);
+    }
+    const int B = cfg->max_batch;
+    const size_t Ln = (size_t)plan.L * plan.n;
+    bool ok = true;
+    auto grab = [&](size_t bytes) -> void * {
+        if (!ok || bytes == 0) return nullptr;
+        void *p = nullptr;
+        if (hipMalloc(&p, bytes) != hipSuccess) {
+            ok = false;
+            return nullptr;
+        }
+        c->allocs.push_back(p);
+        return p;
+    };
+    c->saved = static_cast<char *>(grab((size_t)c->ws.n_saved * c->ws.state_bytes));
+    c->lam = static_cast<float *>(grab(c->ws.lam_bytes));
+    c->part = static_cast<float *>(grab(c->ws.part_bytes));
+    c->e_part = static_cast<float *>(grab((size_t)B * plan.T * 4));
+    c->S = static_cast<double *>(grab((size_t)B * Ln * 3 * 8));
+    c->zyz = static_cast<double *>(grab(Ln * 6 * 8));
+    c->rot_cs = static_cast<float *>(grab(Ln * 2 * 4));
+    c->dw = static_cast<float *>(grab(Ln * 2 * 4));
+    c->H = static_cast<double *>(grab(Ln * 9 * 8));
+    c->init_u = static_cast<float *>(grab((size_t)B * plan.n * 16));
+    if (!plan.small) c->views = static_cast<ViewDev *>(grab(plan.views.size() * sizeof(ViewDev)));
+    c->statmap = static_cast<int2 *>(grab(Ln * sizeof(int2)));
+    c->dlde = static_cast<double *>(grab((size_t)B * 8));
+    c->e_work = static_cast<double *>(grab((size_t)B * 8));
+    c->loss_tmp = static_cast<float *>(grab(64));
+    if (!ok) {
+        hqml_destroy(c);
+        return fail(nullptr, HQML_ERR_OOM, "hipMalloc failed while reserving the workspace");
+    }
+    std::vector<int2> sm(Ln);
+    for (size_t i = 0; i < Ln; ++i) sm[i] = make_int2(plan.statmap[i].pass, plan.statmap[i].slot);
+    e = hipMemcpy(c->statmap, sm.data(), Ln * sizeof(int2), hipMemcpyHostToDevice);
+    if (e == hipSuccess && !plan.small)
+        e = hipMemcpy(c->views, plan.views.data(), plan.views.size() * sizeof(ViewDev), hipMemcpyHostToDevice);
+    if (e == hipSuccess && plan.small) e = configure_small((size_t)2 * ((size_t)1 << plan.n) * 8);
+    if (e != hipSuccess) {
+        const std::string m = std::string("workspace set-up: ") + hipGetErrorString(e);
+        hqml_destroy(c);
+        return fail(nullptr, HQML_ERR_HIP, m);
+    }
+    *out = c;
+    return HQML_OK;
+}
+
+int hqml_destroy(hqml_ctx *c)
+{
+    if (!c) return HQML_OK;
+    (void)hipSetDevice(c->cfg.device);
+    (void)hipStreamSynchronize(c->stream);
+    for (void *p : c->allocs) (void)hipFree(p);
+    for (hipEvent_t e : c->pool) (void)hipEventDestroy(e);
+    delete c;
+    return HQML_OK;
+}
+
+int hqml_forward(hqml_ctx *c, int B, const float *x, const float *theta, float *expz, int save_for_backward)
+{
+    if (!c) return HQML_ERR_ARG;
+    c->err.clear();
+    if (B < 0 || B > c->cfg.max_batch) return fail(c, HQML_ERR_ARG, "B must be in 0..max_batch");
+    c->saved_B = -1;
+    if (B == 0) {
+        if (save_for_backward) c->saved_B = 0;
+        return HQML_OK;
+    }
+    if (!x || !theta || !expz) return fail(c, HQML_ERR_ARG, "x, theta and expz must be device pointers");
+    hipError_t e = hipSetDevice(c->cfg.device);
+    if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
+    int rc = prep(c, B, x, theta);
+    if (rc) return rc;
+    const Plan &pl = c->plan;
+    if (pl.small) {
+        const SmallArgs a = small_args(c, 0);
+        if ((rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->stream); })))
+            return rc;
+        rc = run(c, HQML_K_OTHER, "E reduction", [&] {
+            return launch_ez_reduce(c->e_part, B, 1, nullptr, expz, nullptr, nullptr, c->e_work, c->stream);
+        });
+    } else {
+        if ((rc = tile_forward_sweep(c, B, false))) return rc;
+        rc = run(c, HQML_K_OTHER, "E reduction", [&] {
+            return launch_ez_reduce(c->e_part, B, pl.T, nullptr, expz, nullptr, nullptr, c->e_work, c->stream);
+        });
+    }
+    if (rc) return rc;
+    if (save_for_backward) c->saved_B = B;
+    return HQML_OK;
+}
+
+int hqml_backward(hqml_ctx *c, const float *dL_dE, float *grad)
+{
+    if (!c) return HQML_ERR_ARG;
+    c->err.clear();
+    if (c->saved_B < 0) return fail(c, HQML_ERR_STATE, "no saved forward pass on this context");
+    if (!grad) return fail(c, HQML_ERR_ARG, "grad must be a device pointer");
+    const int B = c->saved_B;
+    hipError_t e = hipSetDevice(c->cfg.device);
+    if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
+    const Plan &pl = c->plan;
+    if (B == 0)   // empty batch: the gradient is zero (the reduction over no samples)
+        return run(c, HQML_K_OTHER, "gradient reduction", [&] {
+            return launch_grad_reduce(c->S, c->H, c->dlde, 0, pl.L, pl.n, grad, c->stream);
+        });
+    if (!dL_dE) return fail(c, HQML_ERR_ARG, "dL_dE must be a device pointer");
+    int rc = run(c, HQML_K_OTHER, "dL/dE copy", [&] { return launch_copy_dlde(dL_dE, B, c->dlde, c->stream); });
+    if (rc) return rc;
+    if (pl.small) {
+        const SmallArgs a = small_args(c, 1);
+        rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->stream); });
+    } else {
+        rc = tile_backward_sweep(c, B, false);
+    }
+    if (rc) return rc;
+    return run(c, HQML_K_OTHER, "gradient reduction", [&] {
+        return launch_grad_reduce(c->S, c->H, c->dlde, B, pl.L, pl.n, grad, c->stream);
+    });
+}
+
+int hqml_train_step(hqml_ctx *c, int B, const float *x, const float *theta, const float *y, float *expz,
+                    float *loss, float *grad)
+{
+    if (!c) return HQML_ERR_ARG;
+    c->err.clear();
+    if (B < 1 || B > c->cfg.max_batch) return fail(c, HQML_ERR_ARG, "B must be in 1..max_batch");
+    if (!x || !theta || !y || !expz || !loss || !grad)
+        return fail(c, HQML_ERR_ARG, "x, theta, y, expz, loss and grad must be device pointers");
+    hipError_t e = hipSetDevice(c->cfg.device);
+    if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
+    c->saved_B = -1;
+    int rc = prep(c, B, x, theta);
+    if (rc) return rc;
+    const Plan &pl = c->plan;
+    if (pl.small) {
+        const SmallArgs a = small_args(c, 2);
+        if ((rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->stream); })))
+            return rc;
+        rc = run(c, HQML_K_OTHER, "E reduction", [&] {
+            return launch_ez_reduce(c->e_part, B, 1, y, expz, loss, c->dlde, c->e_work, c->stream);
+        });
+        if (rc) return rc;
+    } else {
+        if ((rc = tile_forward_sweep(c, B, true))) return rc;
+        // The fused last pass emits E; the loss and dL/dE are needed only by the final
+        // gradient reduction, so the E reduction runs after the backward sweep.
+        if ((rc = tile_backward_sweep(c, B, true))) return rc;
+        rc = run(c, HQML_K_OTHER, "E reduction", [&] {
+            return launch_ez_reduce(c->e_part, B, pl.T, y, expz, loss, c->dlde, c->e_work, c->stream);
+        });
+        if (rc) return rc;
+    }
+    return run(c, HQML_K_OTHER, "gradient reduction", [&] {
+        return launch_grad_reduce(c->S, c->H, c->dlde, B, pl.L, pl.n, grad, c->stream);
+    });
+}
+
+const char *hqml_status_str(int s)
+{
+    switch (s) {
+    case HQML_OK: return "ok";
+    case HQML_ERR_ARG: return "invalid argument";
+    case HQML_ERR_OOM: return "out of device memory";
+    case HQML_ERR_HIP: return "HIP runtime error";
+    case HQML_ERR_STATE: return "call out of order";
+    case HQML_ERR_UNSUPPORTED: return "unsupported";
+    default: return "unknown status";
+    }
+}
+
+const char *hqml_last_error(const hqml_ctx *c)
+{
+    return c ? c->err.c_str() : g_create_err.c_str();
+}
+
+int hqml_set_timing(hqml_ctx *c, int enable)
+{
+    if (!c) return HQML_ERR_ARG;
+    c->timing = enable != 0;
+    return HQML_OK;
+}
+
+int hqml_kernel_times(hqml_ctx *c, double *ms, long long *count, int reset)
+{
+    if (!c || !ms || !count) return HQML_ERR_ARG;
+    hipError_t e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
+    for (int k = 0; k < HQML_K_COUNT; ++k) {
+        ms[k] = 0.0;
+        count[k] = 0;
+    }
+    for (const auto &r : c->recs) {
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, r.a, r.b) == hipSuccess) {
+            ms[r.kind] += t;
+            count[r.kind] += 1;
+        }
+    }
+    if (reset) {
+        c->recs.clear();
+        c->pool_used = 0;
+    }
+    return HQML_OK;
+}
+
+int hqml_plan_info(const hqml_ctx *c, int *fwd_passes, int *bwd_passes, int *tiles_per_sample,
+                   size_t *state_bytes)
+{
+    if (!c) return HQML_ERR_ARG;
+    const Plan &pl = c->plan;
+    if (fwd_passes) *fwd_passes = pl.small ? 1 : pl.n_fwd();
+    if (bwd_passes) *bwd_passes = pl.small ? 1 : pl.n_bwd();
+    if (tiles_per_sample) *tiles_per_sample = pl.T;
+    if (state_bytes) *state_bytes = ((size_t)1 << pl.n) * elem_bytes(c);
+    return HQML_OK;
+}
+
+}  // extern "C"

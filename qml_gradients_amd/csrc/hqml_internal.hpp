@@ -1,0 +1,109 @@
+// Internal structures shared by the host scheduler (hqml_plan.cpp, hqml_abi.cpp)
+// and the gfx950 kernels (hqml_kernels.hip).  Not part of the public ABI.
+//
+// Method: Kawase, "Fast and memory-efficient classical simulation of quantum
+// machine learning via forward and backward gate fusion" (arXiv:2603.02804),
+// hugo-pages summary sections 1.2-1.4: forward gate fusion applies a block of
+// gates to a state kept on chip and writes the block output once; backward gate
+// fusion re-derives each earlier state on chip with U^dagger while forming the
+// adjoint gradient terms and propagating lambda.
+//
+// Layer algebra used by the kernels.  Layer l applies U_{l,q} = Rz(g) Ry(b) Rx(a)
+// to every qubit q (R_s(t) = exp(-i t s/2)) and then the CZ chain.  U is in SU(2),
+// so it factors exactly as
+//     U_{l,q} = diag(p, conj p) * Ry(beta) * diag(r, conj r),  beta in [0, pi],
+// (cos(beta/2) = |U00|, sin(beta/2) = |U10|, p r = U00/|U00|, conj(p) r = U10/|U10|).
+// Between the real rotation layers Ry(beta_l) and Ry(beta_{l+1}) every factor is
+// diagonal: left factors of layer l, the CZ chain of layer l, right factors of
+// layer l+1.  They merge into one diagonal
+//     D_l(i) = czsign_l(i) * prod_q (bit_q(i) ? conj(w_{l,q}) : w_{l,q}),
+//     w_{l,q} = p_{l,q} r_{l+1,q},
+// so the simulated circuit is
+//     psi_0 (product state, all of layer 0's right factors and Ry applied),
+//     D_0, Ry-layer 1, D_1, ..., Ry-layer L-1,
+// and the trailing diagonal (layer L-1's left factors and CZ chain) is dropped:
+// it commutes with Z_0 and does not change E or any gradient.  Gradients are taken
+// at the point P_l just after Ry-layer l: with S_s = Im<mu|s_q|psi> (s = X, Y, Z
+// on qubit q, mu the back-propagated Z_0 psi_M),
+//     dE/dtheta[l][q][a] = sum_s H[l][q][a][s] * S_s,
+// where H holds the Pauli coefficients of p-conjugated rotated generators
+// (computed in k_prep_layers).
+#pragma once
+#include <stdint.h>
+
+namespace hqml {
+
+// ---- tile geometry (n > kTileBits) ----
+// A tile holds 2^13 amplitudes of one sample: 13 "local positions", each bound to
+// one global qubit by the tile's view.  256 threads x 32 registers.
+// Layout L1 (global-memory layout):  regs  <- positions 4..8
+//                                     lanes <- positions 0,1,2,3,9,10
+//                                     waves <- positions 11,12
+// Layout L2 (after one LDS transpose): regs  <- positions 0,1,9,10,11
+//                                     lanes <- positions 2..7
+//                                     waves <- positions 8,12
+// Rotations act on register bits only, so a view rotates qubits at positions
+// {4..8} (in L1) and {0,1,9,10,11} (in L2).  Positions 0..3 always hold global
+// qubits 0..3 (any order), so 16 consecutive amplitudes (128 bytes) are
+// contiguous in memory for every view.
+constexpr int kTileBits = 13;
+constexpr int kRegBits = 5;
+constexpr int kRegs = 32;
+constexpr int kThreads = 256;
+constexpr int kSlots = 80;           // per-tile statistics slots: (sel*13 + pos)*3 + pauli
+constexpr int kMaxQubits = 29;
+constexpr int kSmallMaxQubits = 13;  // whole state of one sample in one workgroup
+constexpr uint32_t kRotatableMask = 0x0FF3u;  // positions 0,1,4..11
+
+struct ViewDev {
+    int32_t perm[kTileBits];   // global qubit held at local position
+    int32_t inv[32];           // local position of a global qubit, -1 if it is a tile bit
+    int32_t n_tile;            // number of tile-index bits
+    int32_t tile_q[32];        // global qubit of tile-index bit k
+    int32_t group_mask;        // local positions whose qubits this view rotates
+    int32_t pad[3];
+};
+
+enum PassFlags : int {
+    PF_INIT = 1,         // generate the layer-0 product state instead of loading a state
+    PF_EMIT_E = 2,       // write per-tile <Z_0> partial sums
+    PF_STORE = 4,        // forward: write the pass output
+    PF_FUSED = 8,        // forward ops of the (last) pass followed by its backward ops
+    PF_STATS_ONLY = 16,  // backward: layer-0 statistics of this view only (no state update)
+    PF_SEED = 32         // backward: lambda = Z_0 psi formed from the pass output (last pass)
+};
+
+struct TilePassArgs {
+    const void *psi_in;     // fwd: input state (previous pass output); bwd: saved output of this pass
+    void *psi_out;          // fwd: output state
+    float *lam;             // bwd: adjoint state, fp32 complex, updated in place
+    float *e_part;          // [B][T] per-tile <Z_0> partial sums
+    float *stat_part;       // [B][T][kSlots] per-tile gradient statistics of this pass
+    const float *rot_cs;    // [L][n][2]: cos, sin of beta/2 (the real rotation)
+    const float *dw;        // [L][n][2]: w_{l,q} of D_l
+    const float *init_u;    // [B][n][4]: (u0.re, u0.im, u1.re, u1.im) layer-0 product factors
+    const ViewDev *view;
+    int n;
+    int L;
+    int T;                  // tiles per sample = 2^(n-13)
+    int rotA;               // first rotation layer of the pass (-1: none)
+    int diag;               // diagonal layer D_l (-1: none)
+    int rotB;               // second rotation layer (-1: none)
+    int flags;
+    int pad;
+};
+
+struct SmallArgs {
+    const float *init_u;    // [B][n][4]
+    const float *rot_cs;    // [L][n][2]
+    const float *dw;        // [L][n][2]
+    float *psi_save;        // [B][2^n][2]: final state (forward mode writes, backward mode reads)
+    float *e_out;           // [B] per-sample <Z_0> (fp32, from an fp64 in-block sum)
+    double *stats;          // [B][L][n][3] per-sample statistics S_s at point P_l
+    int n;
+    int L;
+    int mode;               // 0: forward only; 1: backward only (from psi_save); 2: both
+    int pad;
+};
+
+}  // namespace hqml

@@ -1,0 +1,1150 @@
+// gfx950 kernels of the fused forward / fused adjoint training step.
+//
+// Method: Kawase, arXiv:2603.02804 (hugo-pages summary "深度解析：正向与反向门融合
+// 驱动的高效量子机器学习仿真", sections 1.2-1.4 and 3.2).  The layer algebra (each
+// layer = one real rotation layer plus one merged diagonal) is described in
+// hqml_internal.hpp.
+//
+// Kernels:
+//   k_prep_zyz      theta -> per (layer, qubit) factorisation U = diag(p) Ry(beta) diag(r)
+//   k_prep_tables   -> rot_cs (cos, sin of beta/2), dw (w = p_l r_{l+1}), H (gradient map)
+//   k_prep_init     x -> layer-0 product-state factors u_q per sample
+//   k_tile_fwd      fused forward pass over one 2^13-amplitude tile (forward gate fusion)
+//   k_tile_bwd      fused adjoint pass over one tile (backward gate fusion): re-derives the
+//                   earlier state with U^dagger on chip, forms the gradient statistics and
+//                   propagates lambda <- U^dagger lambda
+//   k_small         n <= 13: the whole circuit of one sample in one workgroup
+//   k_ez_reduce     per-tile <Z_0> partials -> E_b, loss, dL/dE_b (fixed-order fp64)
+//   k_stats_reduce  per-tile statistics -> per-sample statistics (fixed-order fp64)
+//   k_grad_reduce   per-sample statistics x dL/dE x H -> dL/dtheta (fixed-order fp64)
+// No floating-point atomics anywhere: every reduction has a fixed order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hqml_internal.hpp"
+
+namespace hqml {
+
+// ------------------------------------------------------------------ helpers
+
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                  0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row ends with the row sum.
+__device__ __forceinline__ float row_sum16(float v)
+{
+    v += dppf<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dppf<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dppf<0x141>(v);  // row_half_mirror
+    v += dppf<0x140>(v);  // row_mirror
+    return v;
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h)
+{
+    return __builtin_bit_cast(float, h << 16);
+}
+
+// Storage element of a state: ST = 0 -> float2 (re, im); ST = 1 -> packed bf16 (re low, im high).
+template <int ST>
+struct StateIO;
+
+template <>
+struct StateIO<0> {
+    using elem = float2;
+    __device__ static __forceinline__ void load(const elem *p, float &re, float &im)
+    {
+        const float2 v = *p;
+        re = v.x;
+        im = v.y;
+    }
+    __device__ static __forceinline__ void store(elem *p, float re, float im) { *p = make_float2(re, im); }
+};
+
+template <>
+struct StateIO<1> {
+    using elem = uint32_t;
+    __device__ static __forceinline__ void load(const elem *p, float &re, float &im)
+    {
+        const uint32_t v = *p;
+        re = bf16_to_f32(v & 0xFFFFu);
+        im = bf16_to_f32(v >> 16);
+    }
+    __device__ static __forceinline__ void store(elem *p, float re, float im)
+    {
+        *p = f32_to_bf16_rne(re) | (f32_to_bf16_rne(im) << 16);
+    }
+};
+
+// ------------------------------------------------------------------ tile layouts
+
+// LDS bank swizzle on the 8-byte amplitude index.  Linear over GF(2), so
+// swz(a ^ b) = swz(a) ^ swz(b).  Chosen so that both L1 and L2 accesses of a
+// half-wave touch 32 distinct 8-byte slots (no bank conflicts with 64 x 4-byte banks).
+__host__ __device__ constexpr uint32_t swz(uint32_t l)
+{
+    return l ^ ((l >> 4) & 3u) ^ ((((l >> 6) ^ (l >> 9)) & 1u) << 4);
+}
+
+// Local index of register j in each layout (register part only).
+__host__ __device__ constexpr uint32_t l1_reg(int j) { return (uint32_t)j << 4; }
+__host__ __device__ constexpr uint32_t l2_reg(int j) { return ((uint32_t)j & 3u) | (((uint32_t)j >> 2) << 9); }
+
+struct Tile {
+    float re[kRegs];
+    float im[kRegs];
+};
+
+__device__ __forceinline__ uint32_t l1_thread_local(int lane, int w)
+{
+    return (uint32_t)(lane & 15) | ((uint32_t)(lane >> 4) << 9) | ((uint32_t)w << 11);
+}
+
+__device__ __forceinline__ uint32_t l2_thread_local(int lane, int w)
+{
+    return ((uint32_t)lane << 2) | ((uint32_t)(w & 1) << 8) | ((uint32_t)(w >> 1) << 12);
+}
+
+// Move a tile between layouts through LDS (64 KB).  'from_l1' selects direction.
+__device__ __forceinline__ void transpose(Tile &t, float2 *lds, uint32_t a1, uint32_t a2, bool from_l1)
+{
+    __syncthreads();
+    if (from_l1) {
+#pragma unroll
+        for (int j = 0; j < kRegs; ++j) lds[a1 ^ swz(l1_reg(j))] = make_float2(t.re[j], t.im[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kRegs; ++j) lds[a2 ^ swz(l2_reg(j))] = make_float2(t.re[j], t.im[j]);
+    }
+    __syncthreads();
+    if (from_l1) {
+#pragma unroll
+        for (int j = 0; j < kRegs; ++j) {
+            const float2 v = lds[a2 ^ swz(l2_reg(j))];
+            t.re[j] = v.x;
+            t.im[j] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kRegs; ++j) {
+            const float2 v = lds[a1 ^ swz(l1_reg(j))];
+            t.re[j] = v.x;
+            t.im[j] = v.y;
+        }
+    }
+}
+
+// Real rotation Ry on register bit M: [[c, -s], [s, c]] (sgn = +1) or its inverse (sgn = -1).
+template <int M>
+__device__ __forceinline__ void rot_bit(Tile &t, float c, float s)
+{
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+        if (j & (1 << M)) continue;
+        const int k = j | (1 << M);
+        const float ar = t.re[j], ai = t.im[j], br = t.re[k], bi = t.im[k];
+        t.re[j] = c * ar - s * br;
+        t.im[j] = c * ai - s * bi;
+        t.re[k] = s * ar + c * br;
+        t.im[k] = s * ai + c * bi;
+    }
+}
+
+template <int M>
+__device__ __forceinline__ void rot_bit2(Tile &a, Tile &b, float c, float s)
+{
+    rot_bit<M>(a, c, s);
+    rot_bit<M>(b, c, s);
+}
+
+// Rotation coefficients of register bits for one layer, loaded once per use.
+struct RotCoef {
+    float c[5], s[5];
+};
+
+__device__ __forceinline__ RotCoef load_coef(const float *rot_cs, int n, int layer, const int *qpos_to_q,
+                                             uint32_t regmask, float sgn)
+{
+    RotCoef rc;
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+        if (regmask & (1u << m)) {
+            const int q = qpos_to_q[m];
+            rc.c[m] = rot_cs[((size_t)layer * n + q) * 2 + 0];
+            rc.s[m] = sgn * rot_cs[((size_t)layer * n + q) * 2 + 1];
+        } else {
+            rc.c[m] = 1.f;
+            rc.s[m] = 0.f;
+        }
+    }
+    return rc;
+}
+
+__device__ __forceinline__ void rot_layer(Tile &t, const RotCoef &rc, uint32_t regmask)
+{
+    if (regmask & 1u) rot_bit<0>(t, rc.c[0], rc.s[0]);
+    if (regmask & 2u) rot_bit<1>(t, rc.c[1], rc.s[1]);
+    if (regmask & 4u) rot_bit<2>(t, rc.c[2], rc.s[2]);
+    if (regmask & 8u) rot_bit<3>(t, rc.c[3], rc.s[3]);
+    if (regmask & 16u) rot_bit<4>(t, rc.c[4], rc.s[4]);
+}
+
+__device__ __forceinline__ void rot_layer2(Tile &a, Tile &b, const RotCoef &rc, uint32_t regmask)
+{
+    if (regmask & 1u) rot_bit2<0>(a, b, rc.c[0], rc.s[0]);
+    if (regmask & 2u) rot_bit2<1>(a, b, rc.c[1], rc.s[1]);
+    if (regmask & 4u) rot_bit2<2>(a, b, rc.c[2], rc.s[2]);
+    if (regmask & 8u) rot_bit2<3>(a, b, rc.c[3], rc.s[3]);
+    if (regmask & 16u) rot_bit2<4>(a, b, rc.c[4], rc.s[4]);
+}
+
+// X / Y statistics of register bit M: Im<lam|X_q|psi>, Im<lam|Y_q|psi> partial sums.
+template <int M>
+__device__ __forceinline__ void xy_stats(const Tile &p, const Tile &l, float &sx, float &sy)
+{
+    float ax = 0.f, ay = 0.f;
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+        if (j & (1 << M)) continue;
+        const int k = j | (1 << M);
+        // Im(conj(l_j) p_k) + Im(conj(l_k) p_j)
+        ax += l.re[j] * p.im[k] - l.im[j] * p.re[k];
+        ax += l.re[k] * p.im[j] - l.im[k] * p.re[j];
+        // Re(conj(l_k) p_j) - Re(conj(l_j) p_k)
+        ay += l.re[k] * p.re[j] + l.im[k] * p.im[j];
+        ay -= l.re[j] * p.re[k] + l.im[j] * p.im[k];
+    }
+    sx = ax;
+    sy = ay;
+}
+
+// Reduce one statistic over the workgroup into the LDS stat area (16 row partials per slot).
+__device__ __forceinline__ void stat_out(float v, float *lds_stat, int slot, int lane, int w)
+{
+    v = row_sum16(v);
+    if ((lane & 15) == 15) lds_stat[slot * 16 + w * 4 + (lane >> 4)] = v;
+}
+
+// Local position of register bit m in layout L1 / L2.
+__host__ __device__ constexpr int l1_pos(int m) { return 4 + m; }
+__host__ __device__ constexpr int l2_pos(int m) { return m < 2 ? m : 7 + m; }
+
+// Z statistics of all 5 register bits: d_m = sum_j (-1)^{bit m of j} w_j with
+// w_j = Im(conj(l_j) p_j), by pairwise halving (level m folds bit m).
+template <int LEVEL>
+__device__ __forceinline__ void z_fold(float *wv, float *dz)
+{
+    constexpr int cnt = kRegs >> LEVEL;
+    float d = 0.f;
+#pragma unroll
+    for (int k = 0; k < cnt / 2; ++k) {
+        d += wv[2 * k] - wv[2 * k + 1];
+        wv[k] = wv[2 * k] + wv[2 * k + 1];
+    }
+    dz[LEVEL] = d;
+    if constexpr (LEVEL < 4) z_fold<LEVEL + 1>(wv, dz);
+}
+
+// Statistics of every selected register bit: slots ((sel*13 + pos)*3 + {X,Y,Z}).
+template <bool L2>
+__device__ __forceinline__ void stats_visit(const Tile &p, const Tile &l, uint32_t regmask, int sel,
+                                            float *lds_stat, int lane, int w)
+{
+    float wv[kRegs];
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) wv[j] = l.re[j] * p.im[j] - l.im[j] * p.re[j];
+    float dz[5];
+    z_fold<0>(wv, dz);
+    float sx, sy;
+#define HQML_STAT_BIT(M)                                                        \
+    if (regmask & (1u << M)) {                                                  \
+        xy_stats<M>(p, l, sx, sy);                                              \
+        const int base = (sel * 13 + (L2 ? l2_pos(M) : l1_pos(M))) * 3;         \
+        stat_out(sx, lds_stat, base + 0, lane, w);                              \
+        stat_out(sy, lds_stat, base + 1, lane, w);                              \
+        stat_out(dz[M], lds_stat, base + 2, lane, w);                           \
+    }
+    HQML_STAT_BIT(0)
+    HQML_STAT_BIT(1)
+    HQML_STAT_BIT(2)
+    HQML_STAT_BIT(3)
+    HQML_STAT_BIT(4)
+#undef HQML_STAT_BIT
+}
+
+__device__ __forceinline__ float2 cmul(float2 a, float2 b)
+{
+    return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+
+// Per-thread factor tables of the diagonal D_l in layout L2:
+// D(i) = Plo[j & 3] * Phi[j >> 2] for register j of this thread.
+struct DiagTables {
+    float2 lo[4];
+    float2 hi[8];
+};
+
+__device__ __forceinline__ DiagTables diag_tables(const float *dw, int n, int layer, const int *rq,
+                                                  uint32_t fixed_bits)
+{
+    const float2 *wl = reinterpret_cast<const float2 *>(dw) + (size_t)layer * n;
+    uint32_t regq = 0;
+#pragma unroll
+    for (int m = 0; m < 5; ++m) regq |= 1u << rq[m];
+    // Thread constant: product over fixed qubits, CZ signs among fixed neighbours.
+    float2 c = make_float2(1.f, 0.f);
+    for (int q = 0; q < n; ++q) {
+        if (regq & (1u << q)) continue;
+        float2 f = wl[q];
+        if ((fixed_bits >> q) & 1u) f.y = -f.y;
+        c = cmul(c, f);
+    }
+    if (__builtin_popcount(fixed_bits & (fixed_bits >> 1)) & 1) {
+        c.x = -c.x;
+        c.y = -c.y;
+    }
+    float2 g0[5], g1[5];
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+        const int q = rq[m];
+        const float2 f = wl[q];
+        g0[m] = f;
+        g1[m] = make_float2(f.x, -f.y);
+        uint32_t nb = (fixed_bits >> (q + 1)) & 1u;
+        if (q > 0) nb += (fixed_bits >> (q - 1)) & 1u;
+        if (nb & 1u) {
+            g1[m].x = -g1[m].x;
+            g1[m].y = -g1[m].y;
+        }
+    }
+    auto adj = [&](int a, int b) { const int d = rq[a] - rq[b]; return d == 1 || d == -1; };
+    DiagTables t;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        float2 v = cmul(c, cmul((a & 1) ? g1[0] : g0[0], (a & 2) ? g1[1] : g0[1]));
+        if (a == 3 && adj(0, 1)) { v.x = -v.x; v.y = -v.y; }
+        t.lo[a] = v;
+    }
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+        float2 v = cmul(cmul((h & 1) ? g1[2] : g0[2], (h & 2) ? g1[3] : g0[3]), (h & 4) ? g1[4] : g0[4]);
+        int flips = 0;
+        if ((h & 3) == 3 && adj(2, 3)) ++flips;
+        if ((h & 6) == 6 && adj(3, 4)) ++flips;
+        if ((h & 5) == 5 && adj(2, 4)) ++flips;
+        if (flips & 1) { v.x = -v.x; v.y = -v.y; }
+        t.hi[h] = v;
+    }
+    return t;
+}
+
+// Apply D (conj = false) or D^dagger (conj = true) in layout L2.
+__device__ __forceinline__ void apply_diag(Tile &t, const DiagTables &d, bool conj_)
+{
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+        float2 f = cmul(d.lo[j & 3], d.hi[j >> 2]);
+        if (conj_) f.y = -f.y;
+        const float r = t.re[j], i = t.im[j];
+        t.re[j] = r * f.x - i * f.y;
+        t.im[j] = r * f.y + i * f.x;
+    }
+}
+
+__device__ __forceinline__ void apply_diag2(Tile &a, Tile &b, const DiagTables &d)
+{
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+        float2 f = cmul(d.lo[j & 3], d.hi[j >> 2]);
+        f.y = -f.y;
+        float r = a.re[j], i = a.im[j];
+        a.re[j] = r * f.x - i * f.y;
+        a.im[j] = r * f.y + i * f.x;
+        r = b.re[j];
+        i = b.im[j];
+        b.re[j] = r * f.x - i * f.y;
+        b.im[j] = r * f.y + i * f.x;
+    }
+}
+
+// Per-tile geometry shared by the forward and backward tile kernels.
+struct TileCtx {
+    int lane, w, sample, tile;
+    uint64_t tile_off;        // global amplitude offset of the tile's fixed (tile-index) bits
+    uint32_t tile_bits;       // the same as a qubit bitmask (bit q = value of qubit q)
+    uint32_t t1;              // L1: thread's amplitude offset within the tile
+    uint32_t a1, a2;          // LDS base addresses (swizzled) of the thread in L1 / L2
+    uint32_t fixed1, fixed2;  // qubit bitmask of this thread's fixed bits (incl. tile) in L1 / L2
+    uint32_t rs[5];           // L1: amplitude stride of each register bit (uniform)
+    int q1[5], q2[5];         // global qubits of the register bits in L1 / L2
+    uint32_t gm1, gm2;        // register masks of the rotated group in L1 / L2
+};
+
+__device__ __forceinline__ void tile_ctx(TileCtx &c, const ViewDev &v, int T)
+{
+    const int tid = threadIdx.x;
+    c.lane = tid & 63;
+    c.w = tid >> 6;
+    c.sample = blockIdx.x / T;
+    c.tile = blockIdx.x - c.sample * T;
+    uint64_t toff = 0;
+    uint32_t tb = 0;
+    for (int k = 0; k < v.n_tile; ++k) {
+        if ((c.tile >> k) & 1) {
+            toff |= 1ull << v.tile_q[k];
+            tb |= 1u << v.tile_q[k];
+        }
+    }
+    c.tile_off = toff;
+    c.tile_bits = tb;
+    const int lane = c.lane, w = c.w;
+    // L1 thread bits: lane 0..3 -> pos 0..3, lane 4,5 -> pos 9,10, wave 0,1 -> pos 11,12
+    const int l1p[8] = {0, 1, 2, 3, 9, 10, 11, 12};
+    const uint32_t l1v = (uint32_t)(lane & 15) | ((uint32_t)(lane >> 4) << 4) | ((uint32_t)w << 6);
+    uint32_t t1 = 0, f1 = tb;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if ((l1v >> k) & 1u) {
+            t1 |= 1u << v.perm[l1p[k]];
+            f1 |= 1u << v.perm[l1p[k]];
+        }
+    }
+    c.t1 = t1;
+    c.fixed1 = f1;
+    // L2 thread bits: lane 0..5 -> pos 2..7, wave 0 -> pos 8, wave 1 -> pos 12
+    const int l2p[8] = {2, 3, 4, 5, 6, 7, 8, 12};
+    const uint32_t l2v = (uint32_t)lane | ((uint32_t)w << 6);
+    uint32_t f2 = tb;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        if ((l2v >> k) & 1u) f2 |= 1u << v.perm[l2p[k]];
+    c.fixed2 = f2;
+    c.a1 = swz(l1_thread_local(lane, w));
+    c.a2 = swz(l2_thread_local(lane, w));
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+        c.q1[m] = v.perm[4 + m];
+        c.q2[m] = v.perm[m < 2 ? m : 7 + m];
+        c.rs[m] = 1u << c.q1[m];
+    }
+    const uint32_t gm = (uint32_t)v.group_mask;
+    c.gm1 = (gm >> 4) & 31u;
+    c.gm2 = (gm & 3u) | (((gm >> 9) & 7u) << 2);
+}
+
+// Amplitude offset of register j in layout L1 (sum of the strides of its set bits).
+__device__ __forceinline__ uint32_t roff(const TileCtx &c, int j)
+{
+    uint32_t o = 0;
+#pragma unroll
+    for (int m = 0; m < 5; ++m)
+        if (j & (1 << m)) o += c.rs[m];
+    return o;
+}
+
+template <int ST>
+__device__ __forceinline__ void load_l1(Tile &t, const void *state, const TileCtx &c, uint64_t nelem)
+{
+    using IO = StateIO<ST>;
+    const typename IO::elem *base =
+        reinterpret_cast<const typename IO::elem *>(state) + (uint64_t)c.sample * nelem + c.tile_off;
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) IO::load((base + roff(c, j)) + c.t1, t.re[j], t.im[j]);
+}
+
+template <int ST>
+__device__ __forceinline__ void store_l1(const Tile &t, void *state, const TileCtx &c, uint64_t nelem)
+{
+    using IO = StateIO<ST>;
+    typename IO::elem *base = reinterpret_cast<typename IO::elem *>(state) + (uint64_t)c.sample * nelem + c.tile_off;
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) IO::store((base + roff(c, j)) + c.t1, t.re[j], t.im[j]);
+}
+
+// Layer-0 product state in layout L1: psi(i) = prod_q u_q[bit_q(i)].
+__device__ __forceinline__ void init_l1(Tile &t, const float *init_u, const TileCtx &c, int n)
+{
+    const float4 *u = reinterpret_cast<const float4 *>(init_u) + (size_t)c.sample * n;
+    uint32_t regq = 0;
+#pragma unroll
+    for (int m = 0; m < 5; ++m) regq |= 1u << c.q1[m];
+    float2 cst = make_float2(1.f, 0.f);
+    for (int q = 0; q < n; ++q) {
+        if (regq & (1u << q)) continue;
+        const float4 f = u[q];
+        const float2 g = ((c.fixed1 >> q) & 1u) ? make_float2(f.z, f.w) : make_float2(f.x, f.y);
+        cst = cmul(cst, g);
+    }
+    t.re[0] = cst.x;
+    t.im[0] = cst.y;
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+        const float4 f = u[c.q1[m]];
+        const float2 g0 = make_float2(f.x, f.y), g1 = make_float2(f.z, f.w);
+        const int half = 1 << m;
+#pragma unroll
+        for (int k = 0; k < half; ++k) {
+            const float2 v = make_float2(t.re[k], t.im[k]);
+            const float2 a = cmul(v, g0), b = cmul(v, g1);
+            t.re[k] = a.x;
+            t.im[k] = a.y;
+            t.re[k + half] = b.x;
+            t.im[k + half] = b.y;
+        }
+    }
+}
+
+// Sign mask of Z_0 for the 32 registers of this thread (bit j set: qubit 0 is 1).
+__device__ __forceinline__ uint32_t z0_mask_l1(const TileCtx &c)
+{
+    return (c.fixed1 & 1u) ? 0xFFFFFFFFu : 0u;   // qubit 0 sits at a lane position in L1
+}
+
+__device__ __forceinline__ uint32_t z0_mask_l2(const TileCtx &c)
+{
+    if (c.q2[0] == 0) return 0xAAAAAAAAu;
+    if (c.q2[1] == 0) return 0xCCCCCCCCu;
+    return (c.fixed2 & 1u) ? 0xFFFFFFFFu : 0u;
+}
+
+// Workgroup sum of the per-thread <Z_0> partial -> e_part[sample][tile].
+__device__ __forceinline__ void emit_e(float e, float *lds_stat, float *e_part, const TileCtx &c, int T)
+{
+    e = row_sum16(e);
+    __syncthreads();
+    if ((c.lane & 15) == 15) lds_stat[kSlots * 16 + c.w * 4 + (c.lane >> 4)] = e;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float s = 0.f;
+        for (int k = 0; k < 16; ++k) s += lds_stat[kSlots * 16 + k];
+        e_part[(size_t)c.sample * T + c.tile] = s;
+    }
+}
+
+__device__ __forceinline__ float z0_partial(const Tile &t, uint32_t zmask)
+{
+    float e = 0.f;
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+        const float p = t.re[j] * t.re[j] + t.im[j] * t.im[j];
+        e += ((zmask >> j) & 1u) ? -p : p;
+    }
+    return e;
+}
+
+__device__ __forceinline__ void seed_lambda(Tile &l, const Tile &p, uint32_t zmask)
+{
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+        const bool neg = (zmask >> j) & 1u;
+        l.re[j] = neg ? -p.re[j] : p.re[j];
+        l.im[j] = neg ? -p.im[j] : p.im[j];
+    }
+}
+
+// ------------------------------------------------------------------ forward tile pass
+
+template <int ST>
+__global__ __launch_bounds__(kThreads, 2) void k_tile_fwd(TilePassArgs a)
+{
+    __shared__ float2 lds[1 << kTileBits];
+    __shared__ float lds_stat[kSlots * 16 + 16];
+    const ViewDev &v = *a.view;
+    TileCtx c;
+    tile_ctx(c, v, a.T);
+    const uint64_t nelem = 1ull << a.n;
+
+    Tile t;
+    if (a.flags & PF_INIT)
+        init_l1(t, a.init_u, c, a.n);
+    else
+        load_l1<ST>(t, a.psi_in, c, nelem);
+
+    const bool need_l2 = (a.rotA >= 0) || (a.diag >= 0) || (a.rotB >= 0);
+    if (a.rotA >= 0) rot_layer(t, load_coef(a.rot_cs, a.n, a.rotA, c.q1, c.gm1, 1.f), c.gm1);
+    if (need_l2) {
+        transpose(t, lds, c.a1, c.a2, true);
+        if (a.rotA >= 0) rot_layer(t, load_coef(a.rot_cs, a.n, a.rotA, c.q2, c.gm2, 1.f), c.gm2);
+        if (a.diag >= 0) apply_diag(t, diag_tables(a.dw, a.n, a.diag, c.q2, c.fixed2), false);
+        if (a.rotB >= 0) rot_layer(t, load_coef(a.rot_cs, a.n, a.rotB, c.q2, c.gm2, 1.f), c.gm2);
+        transpose(t, lds, c.a1, c.a2, false);
+        if (a.rotB >= 0) rot_layer(t, load_coef(a.rot_cs, a.n, a.rotB, c.q1, c.gm1, 1.f), c.gm1);
+    }
+    if (a.flags & PF_EMIT_E) emit_e(z0_partial(t, z0_mask_l1(c)), lds_stat, a.e_part, c, a.T);
+    if (a.flags & PF_STORE) store_l1<ST>(t, a.psi_out, c, nelem);
+}
+
+// ------------------------------------------------------------------ backward tile pass
+
+__device__ __forceinline__ void zero_stats(float *lds_stat)
+{
+    for (int i = threadIdx.x; i < kSlots * 16 + 16; i += kThreads) lds_stat[i] = 0.f;
+}
+
+__device__ __forceinline__ void flush_stats(const float *lds_stat, float *stat_part, const TileCtx &c, int T)
+{
+    __syncthreads();
+    if (threadIdx.x < kSlots) {
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) s += lds_stat[threadIdx.x * 16 + k];
+        stat_part[((size_t)c.sample * T + c.tile) * kSlots + threadIdx.x] = s;
+    }
+}
+
+// Backward pass shapes (one kernel instance each, to keep register use per shape low).
+enum BwdShape : int {
+    BW_GENERAL = 0,      // [rotA(la) | init, D_la, rotB(la+1)]
+    BW_ROTA = 1,         // [rotA(la)]
+    BW_L0 = 2,           // layer-0 statistics only (one-layer circuit, or stats-only view)
+    BW_FUSED_LAST = 3,   // forward [rotA(la)] + E + seed + its backward
+    BW_FUSED_INIT = 4    // one-layer circuit: product state + E + seed + layer-0 statistics
+};
+
+template <int ST, int SHAPE>
+__global__ __launch_bounds__(kThreads, 2) void k_tile_bwd(TilePassArgs a)
+{
+    __shared__ float2 lds[1 << kTileBits];
+    __shared__ float lds_stat[kSlots * 16 + 16];
+    const ViewDev &v = *a.view;
+    TileCtx c;
+    tile_ctx(c, v, a.T);
+    zero_stats(lds_stat);
+    __syncthreads();
+    const uint64_t nelem = 1ull << a.n;
+    const bool init = (a.flags & PF_INIT) != 0;
+    const int la = init ? 0 : a.rotA;   // layer of the A-side statistics
+    Tile p, l;
+
+    if constexpr (SHAPE == BW_FUSED_INIT) {
+        init_l1(p, a.init_u, c, a.n);
+        const uint32_t zm = z0_mask_l1(c);
+        emit_e(z0_partial(p, zm), lds_stat, a.e_part, c, a.T);
+        seed_lambda(l, p, zm);
+        stats_visit<false>(p, l, c.gm1, 0, lds_stat, c.lane, c.w);
+        transpose(p, lds, c.a1, c.a2, true);
+        transpose(l, lds, c.a1, c.a2, true);
+        stats_visit<true>(p, l, c.gm2, 0, lds_stat, c.lane, c.w);
+        transpose(l, lds, c.a1, c.a2, false);
+    } else if constexpr (SHAPE == BW_FUSED_LAST) {
+        load_l1<ST>(p, a.psi_in, c, nelem);
+        rot_layer(p, load_coef(a.rot_cs, a.n, la, c.q1, c.gm1, 1.f), c.gm1);
+        transpose(p, lds, c.a1, c.a2, true);
+        rot_layer(p, load_coef(a.rot_cs, a.n, la, c.q2, c.gm2, 1.f), c.gm2);
+        const uint32_t zm = z0_mask_l2(c);
+        emit_e(z0_partial(p, zm), lds_stat, a.e_part, c, a.T);
+        seed_lambda(l, p, zm);
+        stats_visit<true>(p, l, c.gm2, 0, lds_stat, c.lane, c.w);
+        rot_layer2(p, l, load_coef(a.rot_cs, a.n, la, c.q2, c.gm2, -1.f), c.gm2);
+        transpose(p, lds, c.a1, c.a2, false);
+        transpose(l, lds, c.a1, c.a2, false);
+        stats_visit<false>(p, l, c.gm1, 0, lds_stat, c.lane, c.w);
+        rot_layer(l, load_coef(a.rot_cs, a.n, la, c.q1, c.gm1, -1.f), c.gm1);
+    } else {
+        if (a.flags & PF_STATS_ONLY)
+            init_l1(p, a.init_u, c, a.n);
+        else
+            load_l1<ST>(p, a.psi_in, c, nelem);
+        if (a.flags & PF_SEED)
+            seed_lambda(l, p, z0_mask_l1(c));
+        else
+            load_l1<0>(l, a.lam, c, nelem);
+        if constexpr (SHAPE == BW_GENERAL) {
+            stats_visit<false>(p, l, c.gm1, 1, lds_stat, c.lane, c.w);
+            rot_layer2(p, l, load_coef(a.rot_cs, a.n, a.rotB, c.q1, c.gm1, -1.f), c.gm1);
+            transpose(p, lds, c.a1, c.a2, true);
+            transpose(l, lds, c.a1, c.a2, true);
+            stats_visit<true>(p, l, c.gm2, 1, lds_stat, c.lane, c.w);
+            rot_layer2(p, l, load_coef(a.rot_cs, a.n, a.rotB, c.q2, c.gm2, -1.f), c.gm2);
+            apply_diag2(p, l, diag_tables(a.dw, a.n, a.diag, c.q2, c.fixed2));
+            stats_visit<true>(p, l, c.gm2, 0, lds_stat, c.lane, c.w);
+            if (!init) rot_layer2(p, l, load_coef(a.rot_cs, a.n, la, c.q2, c.gm2, -1.f), c.gm2);
+            transpose(p, lds, c.a1, c.a2, false);
+            transpose(l, lds, c.a1, c.a2, false);
+            stats_visit<false>(p, l, c.gm1, 0, lds_stat, c.lane, c.w);
+            if (!init) rot_layer(l, load_coef(a.rot_cs, a.n, la, c.q1, c.gm1, -1.f), c.gm1);
+        } else if constexpr (SHAPE == BW_ROTA) {
+            stats_visit<false>(p, l, c.gm1, 0, lds_stat, c.lane, c.w);
+            rot_layer2(p, l, load_coef(a.rot_cs, a.n, la, c.q1, c.gm1, -1.f), c.gm1);
+            transpose(p, lds, c.a1, c.a2, true);
+            transpose(l, lds, c.a1, c.a2, true);
+            stats_visit<true>(p, l, c.gm2, 0, lds_stat, c.lane, c.w);
+            rot_layer(l, load_coef(a.rot_cs, a.n, la, c.q2, c.gm2, -1.f), c.gm2);
+            transpose(l, lds, c.a1, c.a2, false);
+        } else {   // BW_L0
+            stats_visit<false>(p, l, c.gm1, 0, lds_stat, c.lane, c.w);
+            transpose(p, lds, c.a1, c.a2, true);
+            transpose(l, lds, c.a1, c.a2, true);
+            stats_visit<true>(p, l, c.gm2, 0, lds_stat, c.lane, c.w);
+            if (a.flags & PF_STATS_ONLY) {
+                flush_stats(lds_stat, a.stat_part, c, a.T);
+                return;
+            }
+            transpose(l, lds, c.a1, c.a2, false);
+        }
+    }
+    store_l1<0>(l, a.lam, c, nelem);
+    flush_stats(lds_stat, a.stat_part, c, a.T);
+}
+
+template __global__ void k_tile_fwd<0>(TilePassArgs);
+template __global__ void k_tile_fwd<1>(TilePassArgs);
+
+// ------------------------------------------------------------------ small circuits (n <= 13)
+
+// D_l applied to amplitude i (conj_ selects D^dagger).
+__device__ __forceinline__ float2 small_diag(const float2 *wl, int n, uint32_t i)
+{
+    float2 f = make_float2(1.f, 0.f);
+    for (int q = 0; q < n; ++q) {
+        float2 g = wl[q];
+        if ((i >> q) & 1u) g.y = -g.y;
+        f = cmul(f, g);
+    }
+    if (__builtin_popcount(i & (i >> 1)) & 1) {
+        f.x = -f.x;
+        f.y = -f.y;
+    }
+    return f;
+}
+
+__device__ __forceinline__ uint32_t pair_index(uint32_t k, int q)
+{
+    return ((k >> q) << (q + 1)) | (k & ((1u << q) - 1u));
+}
+
+__global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
+{
+    extern __shared__ float2 sm[];
+    __shared__ float red[3 * kSmallMaxQubits * 16 + 16];
+    const int n = a.n, L = a.L;
+    const uint32_t N = 1u << n;
+    float2 *psi = sm;
+    float2 *lam = sm + N;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const float2 *rcs = reinterpret_cast<const float2 *>(a.rot_cs);
+    const float2 *dw = reinterpret_cast<const float2 *>(a.dw);
+    float2 *save = reinterpret_cast<float2 *>(a.psi_save) + (size_t)b * N;
+
+    if (a.mode != 1) {
+        const float4 *u = reinterpret_cast<const float4 *>(a.init_u) + (size_t)b * n;
+        for (uint32_t i = tid; i < N; i += kThreads) {
+            float2 v = make_float2(1.f, 0.f);
+            for (int q = 0; q < n; ++q) {
+                const float4 f = u[q];
+                v = cmul(v, ((i >> q) & 1u) ? make_float2(f.z, f.w) : make_float2(f.x, f.y));
+            }
+            psi[i] = v;
+        }
+        __syncthreads();
+        for (int l = 0; l + 1 < L; ++l) {
+            const float2 *wl = dw + (size_t)l * n;
+            for (uint32_t i = tid; i < N; i += kThreads) psi[i] = cmul(psi[i], small_diag(wl, n, i));
+            __syncthreads();
+            for (int q = 0; q < n; ++q) {
+                const float2 cs = rcs[(size_t)(l + 1) * n + q];
+                for (uint32_t k = tid; k < N / 2; k += kThreads) {
+                    const uint32_t i = pair_index(k, q), j = i | (1u << q);
+                    const float2 x = psi[i], y = psi[j];
+                    psi[i] = make_float2(cs.x * x.x - cs.y * y.x, cs.x * x.y - cs.y * y.y);
+                    psi[j] = make_float2(cs.y * x.x + cs.x * y.x, cs.y * x.y + cs.x * y.y);
+                }
+                __syncthreads();
+            }
+        }
+        // <Z_0>
+        float e = 0.f;
+        for (uint32_t i = tid; i < N; i += kThreads) {
+            const float2 v = psi[i];
+            const float pr = v.x * v.x + v.y * v.y;
+            e += (i & 1u) ? -pr : pr;
+        }
+        e = row_sum16(e);
+        if ((lane & 15) == 15) red[w * 4 + (lane >> 4)] = e;
+        __syncthreads();
+        if (tid == 0) {
+            double s = 0.0;
+            for (int k = 0; k < 16; ++k) s += (double)red[k];
+            a.e_out[b] = (float)s;
+        }
+        if (a.mode == 0) {
+            for (uint32_t i = tid; i < N; i += kThreads) save[i] = psi[i];
+            return;
+        }
+        __syncthreads();
+    } else {
+        for (uint32_t i = tid; i < N; i += kThreads) psi[i] = save[i];
+        __syncthreads();
+    }
+
+    // Adjoint sweep: lambda = Z_0 psi at P_{L-1}; statistics at every P_l; uncompute.
+    for (uint32_t i = tid; i < N; i += kThreads) {
+        const float2 v = psi[i];
+        lam[i] = (i & 1u) ? make_float2(-v.x, -v.y) : v;
+    }
+    __syncthreads();
+    for (int l = L - 1; l >= 0; --l) {
+        for (int q = 0; q < n; ++q) {
+            float sx = 0.f, sy = 0.f, sz = 0.f;
+            for (uint32_t k = tid; k < N / 2; k += kThreads) {
+                const uint32_t i = pair_index(k, q), j = i | (1u << q);
+                const float2 pi_ = psi[i], pj = psi[j], li = lam[i], lj = lam[j];
+                sx += li.x * pj.y - li.y * pj.x + lj.x * pi_.y - lj.y * pi_.x;
+                sy += lj.x * pi_.x + lj.y * pi_.y - li.x * pj.x - li.y * pj.y;
+                sz += (li.x * pi_.y - li.y * pi_.x) - (lj.x * pj.y - lj.y * pj.x);
+            }
+            sx = row_sum16(sx);
+            sy = row_sum16(sy);
+            sz = row_sum16(sz);
+            if ((lane & 15) == 15) {
+                const int r = w * 4 + (lane >> 4);
+                red[(q * 3 + 0) * 16 + r] = sx;
+                red[(q * 3 + 1) * 16 + r] = sy;
+                red[(q * 3 + 2) * 16 + r] = sz;
+            }
+        }
+        __syncthreads();
+        if (tid < 3 * n) {
+            double s = 0.0;
+            for (int k = 0; k < 16; ++k) s += (double)red[tid * 16 + k];
+            a.stats[(((size_t)b * L + l) * n) * 3 + tid] = s;
+        }
+        if (l == 0) break;
+        // uncompute Ry-layer l and D_{l-1} on psi and lambda
+        for (int q = 0; q < n; ++q) {
+            const float2 cs = rcs[(size_t)l * n + q];
+            for (uint32_t k = tid; k < N / 2; k += kThreads) {
+                const uint32_t i = pair_index(k, q), j = i | (1u << q);
+                float2 x = psi[i], y = psi[j];
+                psi[i] = make_float2(cs.x * x.x + cs.y * y.x, cs.x * x.y + cs.y * y.y);
+                psi[j] = make_float2(-cs.y * x.x + cs.x * y.x, -cs.y * x.y + cs.x * y.y);
+                x = lam[i];
+                y = lam[j];
+                lam[i] = make_float2(cs.x * x.x + cs.y * y.x, cs.x * x.y + cs.y * y.y);
+                lam[j] = make_float2(-cs.y * x.x + cs.x * y.x, -cs.y * x.y + cs.x * y.y);
+            }
+            __syncthreads();
+        }
+        const float2 *wl = dw + (size_t)(l - 1) * n;
+        for (uint32_t i = tid; i < N; i += kThreads) {
+            float2 f = small_diag(wl, n, i);
+            f.y = -f.y;
+            psi[i] = cmul(psi[i], f);
+            lam[i] = cmul(lam[i], f);
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------ table preparation (fp64)
+
+struct cd {
+    double re, im;
+};
+__device__ __forceinline__ cd cmk(double r, double i) { return cd{r, i}; }
+__device__ __forceinline__ cd operator*(cd a, cd b) { return cd{a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re}; }
+__device__ __forceinline__ cd operator+(cd a, cd b) { return cd{a.re + b.re, a.im + b.im}; }
+__device__ __forceinline__ cd cconj(cd a) { return cd{a.re, -a.im}; }
+
+struct m2 {
+    cd m[4];
+};
+__device__ __forceinline__ m2 mmul(const m2 &a, const m2 &b)
+{
+    m2 r;
+    r.m[0] = a.m[0] * b.m[0] + a.m[1] * b.m[2];
+    r.m[1] = a.m[0] * b.m[1] + a.m[1] * b.m[3];
+    r.m[2] = a.m[2] * b.m[0] + a.m[3] * b.m[2];
+    r.m[3] = a.m[2] * b.m[1] + a.m[3] * b.m[3];
+    return r;
+}
+__device__ __forceinline__ m2 mdag(const m2 &a)
+{
+    m2 r;
+    r.m[0] = cconj(a.m[0]);
+    r.m[1] = cconj(a.m[2]);
+    r.m[2] = cconj(a.m[1]);
+    r.m[3] = cconj(a.m[3]);
+    return r;
+}
+__device__ __forceinline__ m2 m_rx(double t)
+{
+    double s, c;
+    sincos(0.5 * t, &s, &c);
+    return m2{{cmk(c, 0), cmk(0, -s), cmk(0, -s), cmk(c, 0)}};
+}
+__device__ __forceinline__ m2 m_ry(double t)
+{
+    double s, c;
+    sincos(0.5 * t, &s, &c);
+    return m2{{cmk(c, 0), cmk(-s, 0), cmk(s, 0), cmk(c, 0)}};
+}
+__device__ __forceinline__ m2 m_rz(double t)
+{
+    double s, c;
+    sincos(0.5 * t, &s, &c);
+    return m2{{cmk(c, -s), cmk(0, 0), cmk(0, 0), cmk(c, s)}};
+}
+
+// zyz[(l*n+q)*6]: cos(beta/2), sin(beta/2), p.re, p.im, r.re, r.im
+__global__ void k_prep_zyz(const float *theta, int L, int n, double *zyz)
+{
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= L * n) return;
+    const double ax = theta[idx * 3 + 0], ay = theta[idx * 3 + 1], az = theta[idx * 3 + 2];
+    const m2 U = mmul(m_rz(az), mmul(m_ry(ay), m_rx(ax)));
+    const cd x = U.m[0], y = U.m[2];
+    const double ax_ = sqrt(x.re * x.re + x.im * x.im), ay_ = sqrt(y.re * y.re + y.im * y.im);
+    const double nrm = sqrt(ax_ * ax_ + ay_ * ay_);
+    const double cb = ax_ / nrm, sb = ay_ / nrm;
+    const cd xh = ax_ > 1e-300 ? cmk(x.re / ax_, x.im / ax_) : cmk(1, 0);
+    const cd yh = ay_ > 1e-300 ? cmk(y.re / ay_, y.im / ay_) : cmk(1, 0);
+    // r = principal sqrt of xh*yh (a unit complex number); p = xh * conj(r)
+    const cd z = xh * yh;
+    const double ang = atan2(z.im, z.re) * 0.5;
+    double sr, cr;
+    sincos(ang, &sr, &cr);
+    const cd r = cmk(cr, sr);
+    const cd p = xh * cconj(r);
+    double *o = zyz + (size_t)idx * 6;
+    o[0] = cb;
+    o[1] = sb;
+    o[2] = p.re;
+    o[3] = p.im;
+    o[4] = r.re;
+    o[5] = r.im;
+}
+
+// rot_cs[l][q] = (cos, sin)(beta/2); dw[l][q] = p_{l,q} r_{l+1,q} (l < L-1);
+// H[l][q][a][s]: Pauli coefficients of diag(p)^dag G_a diag(p), G_a the generator of
+// theta[l][q][a] moved to just after U_{l,q}: G_z = Z, G_y = Rz Y Rz^dag,
+// G_x = Rz Ry X Ry^dag Rz^dag.
+__global__ void k_prep_tables(const float *theta, const double *zyz, int L, int n, float *rot_cs, float *dw,
+                              double *H)
+{
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= L * n) return;
+    const int l = idx / n;
+    const double *z = zyz + (size_t)idx * 6;
+    rot_cs[idx * 2 + 0] = (float)z[0];
+    rot_cs[idx * 2 + 1] = (float)z[1];
+    if (l + 1 < L) {
+        const double *zn = zyz + (size_t)(idx + n) * 6;
+        const cd w = cmk(z[2], z[3]) * cmk(zn[4], zn[5]);
+        dw[idx * 2 + 0] = (float)w.re;
+        dw[idx * 2 + 1] = (float)w.im;
+    } else {
+        dw[idx * 2 + 0] = 1.f;
+        dw[idx * 2 + 1] = 0.f;
+    }
+    const double ay = theta[idx * 3 + 1], az = theta[idx * 3 + 2];
+    const m2 X = m2{{cmk(0, 0), cmk(1, 0), cmk(1, 0), cmk(0, 0)}};
+    const m2 Y = m2{{cmk(0, 0), cmk(0, -1), cmk(0, 1), cmk(0, 0)}};
+    const m2 Z = m2{{cmk(1, 0), cmk(0, 0), cmk(0, 0), cmk(-1, 0)}};
+    const m2 Rz = m_rz(az), RzRy = mmul(m_rz(az), m_ry(ay));
+    const cd p = cmk(z[2], z[3]);
+    const m2 Lp = m2{{p, cmk(0, 0), cmk(0, 0), cconj(p)}};
+    m2 G[3];
+    G[0] = mmul(RzRy, mmul(X, mdag(RzRy)));
+    G[1] = mmul(Rz, mmul(Y, mdag(Rz)));
+    G[2] = Z;
+    for (int a = 0; a < 3; ++a) {
+        const m2 S = mmul(mdag(Lp), mmul(G[a], Lp));
+        double *h = H + ((size_t)idx * 3 + a) * 3;
+        h[0] = S.m[1].re;    // X coefficient
+        h[1] = -S.m[1].im;   // Y coefficient
+        h[2] = S.m[0].re;    // Z coefficient
+    }
+}
+
+// u[b][q] = Ry(beta_{0,q}) diag(r, conj r) (cos x/2, sin x/2): the layer-0 product factor.
+__global__ void k_prep_init(const float *x, const double *zyz, int B, int n, float *init_u)
+{
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= B * n) return;
+    const int q = idx % n;
+    const double *z = zyz + (size_t)q * 6;
+    double s, c;
+    sincos(0.5 * (double)x[idx], &s, &c);
+    const cd r = cmk(z[4], z[5]);
+    const cd a0 = cmk(r.re * c, r.im * c);        // r cos
+    const cd a1 = cmk(r.re * s, -r.im * s);       // conj(r) sin
+    const double cb = z[0], sb = z[1];
+    float *o = init_u + (size_t)idx * 4;
+    o[0] = (float)(cb * a0.re - sb * a1.re);
+    o[1] = (float)(cb * a0.im - sb * a1.im);
+    o[2] = (float)(sb * a0.re + cb * a1.re);
+    o[3] = (float)(sb * a0.im + cb * a1.im);
+}
+
+// ------------------------------------------------------------------ reductions (fixed order)
+
+// E_b = sum over tiles (fp64); with y: loss = mean (E - y)^2 and dLdE = 2 (E - y) / B.
+__global__ void k_ez_reduce(const float *e_part, int B, int T, const float *y, float *e_out, float *loss,
+                            double *dlde, double *e_work)
+{
+    for (int b = threadIdx.x; b < B; b += blockDim.x) {
+        double s = 0.0;
+        for (int t = 0; t < T; ++t) s += (double)e_part[(size_t)b * T + t];
+        e_work[b] = s;
+        e_out[b] = (float)s;
+        if (y) dlde[b] = 2.0 * (s - (double)y[b]) / (double)B;
+    }
+    __syncthreads();
+    if (y && threadIdx.x == 0) {
+        double acc = 0.0;
+        for (int b = 0; b < B; ++b) {
+            const double d = e_work[b] - (double)y[b];
+            acc += d * d;
+        }
+        *loss = (float)(acc / (double)B);
+    }
+}
+
+__global__ void k_copy_dlde(const float *src, int B, double *dlde)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B) dlde[b] = (double)src[b];
+}
+
+// S[b][l][q][s] = sum over tiles of the slot that holds (l, q, s).  map[l*n+q] = (pass, slot base).
+__global__ void k_stats_reduce(const float *part, const int2 *map, int B, int L, int n, int T, int pass_lo,
+                               int pass_hi, double *S)
+{
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t total = (size_t)B * L * n * 3;
+    if (idx >= total) return;
+    const int s = (int)(idx % 3);
+    const size_t lq = (idx / 3) % ((size_t)L * n);
+    const int b = (int)(idx / 3 / ((size_t)L * n));
+    const int2 m = map[lq];
+    if (m.x < pass_lo || m.x >= pass_hi) return;
+    const float *pp = part + (((size_t)(m.x - pass_lo) * B + b) * T) * kSlots + m.y + s;
+    double acc = 0.0;
+    for (int t = 0; t < T; ++t) acc += (double)pp[(size_t)t * kSlots];
+    S[((size_t)b * L * n + lq) * 3 + s] = acc;
+}
+
+// grad[l][q][a] = sum_b dLdE_b * sum_s H[l][q][a][s] * S[b][l][q][s]
+__global__ void k_grad_reduce(const double *S, const double *H, const double *dlde, int B, int L, int n,
+                              float *grad)
+{
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= L * n * 3) return;
+    const int lq = idx / 3;
+    const double *h = H + (size_t)idx * 3;
+    double acc = 0.0;
+    for (int b = 0; b < B; ++b) {
+        const double *sb = S + ((size_t)b * L * n + lq) * 3;
+        acc += dlde[b] * (h[0] * sb[0] + h[1] * sb[1] + h[2] * sb[2]);
+    }
+    grad[idx] = (float)acc;
+}
+
+}  // namespace hqml
+
+// ------------------------------------------------------------------ launch wrappers (host)
+
+namespace hqml {
+
+hipError_t launch_prep(const float *theta, const float *x, int L, int n, int B, double *zyz, float *rot_cs,
+                       float *dw, double *H, float *init_u, hipStream_t s)
+{
+    const int ln = L * n;
+    k_prep_zyz<<<(ln + 127) / 128, 128, 0, s>>>(theta, L, n, zyz);
+    k_prep_tables<<<(ln + 127) / 128, 128, 0, s>>>(theta, zyz, L, n, rot_cs, dw, H);
+    if (B > 0) k_prep_init<<<(B * n + 127) / 128, 128, 0, s>>>(x, zyz, B, n, init_u);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_fwd(const TilePassArgs &a, int B, int storage, hipStream_t s)
+{
+    const dim3 grid((unsigned)(B * a.T));
+    if (storage == 1)
+        k_tile_fwd<1><<<grid, kThreads, 0, s>>>(a);
+    else
+        k_tile_fwd<0><<<grid, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int ST>
+static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s)
+{
+    if (a.flags & PF_FUSED) {
+        if (a.flags & PF_INIT)
+            k_tile_bwd<ST, BW_FUSED_INIT><<<grid, kThreads, 0, s>>>(a);
+        else
+            k_tile_bwd<ST, BW_FUSED_LAST><<<grid, kThreads, 0, s>>>(a);
+    } else if (a.rotB >= 0) {
+        k_tile_bwd<ST, BW_GENERAL><<<grid, kThreads, 0, s>>>(a);
+    } else if (a.rotA >= 0 && !(a.flags & (PF_INIT | PF_STATS_ONLY))) {
+        k_tile_bwd<ST, BW_ROTA><<<grid, kThreads, 0, s>>>(a);
+    } else {
+        k_tile_bwd<ST, BW_L0><<<grid, kThreads, 0, s>>>(a);
+    }
+}
+
+hipError_t launch_tile_bwd(const TilePassArgs &a, int B, int storage, hipStream_t s)
+{
+    const dim3 grid((unsigned)(B * a.T));
+    if (storage == 1)
+        launch_bwd_shape<1>(a, grid, s);
+    else
+        launch_bwd_shape<0>(a, grid, s);
+    return hipGetLastError();
+}
+
+hipError_t configure_small(size_t shm_bytes)
+{
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_small), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)shm_bytes);
+}
+
+hipError_t launch_small(const SmallArgs &a, int B, hipStream_t s)
+{
+    const size_t shm = (size_t)2 * ((size_t)1 << a.n) * sizeof(float2);
+    k_small<<<B, kThreads, shm, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_ez_reduce(const float *e_part, int B, int T, const float *y, float *e_out, float *loss,
+                            double *dlde, double *e_work, hipStream_t s)
+{
+    k_ez_reduce<<<1, 256, 0, s>>>(e_part, B, T, y, e_out, loss, dlde, e_work);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_dlde(const float *src, int B, double *dlde, hipStream_t s)
+{
+    k_copy_dlde<<<(B + 255) / 256, 256, 0, s>>>(src, B, dlde);
+    return hipGetLastError();
+}
+
+hipError_t launch_stats_reduce(const float *part, const int2 *map, int B, int L, int n, int T, int pass_lo,
+                               int pass_hi, double *S, hipStream_t s)
+{
+    const size_t total = (size_t)B * L * n * 3;
+    k_stats_reduce<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(part, map, B, L, n, T, pass_lo, pass_hi, S);
+    return hipGetLastError();
+}
+
+hipError_t launch_grad_reduce(const double *S, const double *H, const double *dlde, int B, int L, int n,
+                              float *grad, hipStream_t s)
+{
+    const int total = L * n * 3;
+    k_grad_reduce<<<(total + 255) / 256, 256, 0, s>>>(S, H, dlde, B, L, n, grad);
+    return hipGetLastError();
+}
+
+}  // namespace hqml

@@ -1,0 +1,302 @@
+// Host scheduler for the fused training step (no HIP calls).
+//
+// Forward gate fusion (hugo-pages summary, section 1.4 item 1): each fused pass
+// reads a state once, applies a block of gates on chip and writes the block's
+// output once.  A tile view keeps 13 of the n qubits on chip; rotations of one
+// layer commute across qubits, so each layer's real rotations are split into one
+// group per view, and consecutive layers are interleaved so that a pass applies
+// [group of layer l, merged diagonal D_l, the same group of layer l+1].  With two
+// views (14 <= n <= 20) that is one pass per layer; with V views, V-1 passes.
+#include "hqml_plan.hpp"
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+
+namespace hqml {
+
+namespace {
+
+constexpr int kLowQubits = 4;   // positions 0..3 always hold qubits 0..3 (128-byte runs)
+
+// Local positions a view may rotate, in fill order for a view's own high qubits.
+const int kHighRotPos[8] = {4, 5, 6, 7, 8, 9, 10, 11};
+
+bool build_views(int n, Plan &p, std::string *err)
+{
+    const int nhigh = n - kLowQubits;
+    int V = std::max(2, (nhigh + 7) / 8);
+    p.V = V;
+    p.T = 1 << (n - kTileBits);
+    // Balance rotations per view: views 0 and 1 also rotate two low qubits each.
+    std::vector<int> load(V, 0), hcount(V, 0);
+    load[0] = 2;
+    load[1] = 2;
+    for (int k = 0; k < nhigh; ++k) {
+        int best = -1;
+        for (int v = 0; v < V; ++v) {
+            if (hcount[v] >= 8) continue;
+            if (best < 0 || load[v] < load[best]) best = v;
+        }
+        if (best < 0) {
+            if (err) *err = "no view has room for another high qubit";
+            return false;
+        }
+        ++hcount[best];
+        ++load[best];
+    }
+    // Contiguous ranges of high qubits per view, in view order.
+    std::vector<std::vector<int>> own(V);
+    int next = kLowQubits;
+    for (int v = 0; v < V; ++v)
+        for (int k = 0; k < hcount[v]; ++k) own[v].push_back(next++);
+
+    p.views.assign(V, ViewDev{});
+    for (int v = 0; v < V; ++v) {
+        ViewDev &d = p.views[v];
+        std::memset(&d, 0, sizeof(d));
+        for (int i = 0; i < 32; ++i) d.inv[i] = -1;
+        int perm[kTileBits];
+        for (int i = 0; i < kTileBits; ++i) perm[i] = -1;
+        uint32_t group = 0;
+        // low positions
+        if (v == 1) {
+            perm[0] = 2; perm[1] = 3; perm[2] = 0; perm[3] = 1;
+        } else {
+            perm[0] = 0; perm[1] = 1; perm[2] = 2; perm[3] = 3;
+        }
+        if (v <= 1) group |= 0x3u;   // positions 0,1 rotated by views 0 and 1
+        // own high qubits at rotatable high positions
+        for (size_t k = 0; k < own[v].size(); ++k) {
+            perm[kHighRotPos[k]] = own[v][k];
+            group |= 1u << kHighRotPos[k];
+        }
+        // fillers: other high qubits, highest first (qubit 4 last)
+        std::vector<int> cand;
+        for (int q = n - 1; q >= kLowQubits; --q)
+            if (std::find(own[v].begin(), own[v].end(), q) == own[v].end()) cand.push_back(q);
+        size_t ci = 0;
+        for (int pos = 4; pos < kTileBits; ++pos) {
+            if (perm[pos] >= 0) continue;
+            if (ci >= cand.size()) {
+                if (err) *err = "not enough qubits to fill a tile view";
+                return false;
+            }
+            perm[pos] = cand[ci++];
+        }
+        // The diagonal's per-thread factor tables need: if qubit 3 sits at an L2 register
+        // position 0/1, qubit 4 is not at the other L2 register positions 9..11.
+        auto at = [&](int q) { for (int i = 0; i < kTileBits; ++i) if (perm[i] == q) return i; return -1; };
+        const int p3 = at(3), p4 = at(4);
+        if ((p3 == 0 || p3 == 1) && p4 >= 9 && p4 <= 11) {
+            const bool in_group = (group >> p4) & 1u;
+            int swap_with = -1;
+            for (int pos : {4, 5, 6, 7, 8, 12}) {
+                if (((group >> pos) & 1u) == (in_group ? 1u : 0u)) { swap_with = pos; break; }
+            }
+            if (swap_with < 0) {
+                if (err) *err = "cannot place qubit 4 away from the L2 register positions";
+                return false;
+            }
+            std::swap(perm[p4], perm[swap_with]);
+        }
+        for (int i = 0; i < kTileBits; ++i) {
+            d.perm[i] = perm[i];
+            d.inv[perm[i]] = i;
+        }
+        d.group_mask = (int32_t)group;
+        int nt = 0;
+        for (int q = 0; q < n; ++q)
+            if (d.inv[q] < 0) d.tile_q[nt++] = q;
+        d.n_tile = nt;
+        if (nt != n - kTileBits) {
+            if (err) *err = "tile view does not cover the qubits";
+            return false;
+        }
+    }
+    return true;
+}
+
+}  // namespace
+
+bool make_plan(int n, int L, int ckpt_block, Plan *out, std::string *err)
+{
+    Plan p;
+    p.n = n;
+    p.L = L;
+    if (n < 1 || n > kMaxQubits) {
+        if (err) *err = "n_qubits must be in 1..29";
+        return false;
+    }
+    if (L < 1) {
+        if (err) *err = "n_layers must be >= 1";
+        return false;
+    }
+    if (ckpt_block < 0) {
+        if (err) *err = "ckpt_block must be >= 0";
+        return false;
+    }
+    p.statmap.assign((size_t)L * n, StatLoc{-1, 0});
+    if (n <= kSmallMaxQubits) {
+        p.small = true;
+        p.V = 1;
+        p.T = 1;
+        *out = p;
+        return true;
+    }
+    if (!build_views(n, p, err)) return false;
+    const int V = p.V;
+    auto group_has = [&](int v, int q) {
+        const int pos = p.views[v].inv[q];
+        return pos >= 0 && ((p.views[v].group_mask >> pos) & 1);
+    };
+    auto slot_of = [&](int v, int q, int sel) { return (sel * 13 + p.views[v].inv[q]) * 3; };
+
+    // Pass 0: layer-0 product state, D_0, Ry-layer 1 of view 0's group.
+    p.fwd.push_back(PassPlan{0, true, -1, L >= 2 ? 0 : -1, L >= 2 ? 1 : -1});
+    int prev = 0;                       // view holding the last slot of the previous layer
+    // layer 1's first slot (view 0) is the rotB of pass 0
+    std::vector<int> first_view(L, -1), first_pass(L, -1);
+    std::vector<std::vector<int>> rotA_pass(L, std::vector<int>(V, -1));
+    if (L >= 2) { first_view[1] = 0; first_pass[1] = 0; }
+    for (int l = 1; l < L; ++l) {
+        std::vector<int> ord;
+        ord.push_back(prev);
+        for (int k = 1; k < V; ++k) ord.push_back((prev + k) % V);
+        for (int k = 1; k + 1 < V; ++k) {           // middle slots: own pass, no diagonal
+            rotA_pass[l][ord[k]] = (int)p.fwd.size();
+            p.fwd.push_back(PassPlan{ord[k], false, l, -1, -1});
+        }
+        const int last = ord[V - 1];
+        rotA_pass[l][last] = (int)p.fwd.size();
+        if (l + 1 < L) {
+            first_view[l + 1] = last;
+            first_pass[l + 1] = (int)p.fwd.size();
+            p.fwd.push_back(PassPlan{last, false, l, l, l + 1});
+        } else {
+            p.fwd.push_back(PassPlan{last, false, l, -1, -1});
+        }
+        prev = last;
+    }
+    const int P = (int)p.fwd.size();
+    for (int v = 1; v < V; ++v) p.stats_only.push_back(v);
+    // Statistics locations.
+    for (int q = 0; q < n; ++q) {
+        int v0 = -1;
+        for (int v = 0; v < V; ++v)
+            if (group_has(v, q)) v0 = v;
+        if (v0 < 0) {
+            if (err) *err = "a qubit is rotated by no view";
+            return false;
+        }
+        // layer 0
+        if (v0 == 0)
+            p.statmap[q] = StatLoc{0, slot_of(0, q, 0)};
+        else
+            p.statmap[q] = StatLoc{P + (v0 - 1), slot_of(v0, q, 0)};
+        for (int l = 1; l < L; ++l) {
+            if (first_view[l] == v0)
+                p.statmap[(size_t)l * n + q] = StatLoc{first_pass[l], slot_of(v0, q, 1)};
+            else
+                p.statmap[(size_t)l * n + q] = StatLoc{rotA_pass[l][v0], slot_of(v0, q, 0)};
+        }
+    }
+    for (const StatLoc &s : p.statmap)
+        if (s.pass < 0) {
+            if (err) *err = "statistics map incomplete";
+            return false;
+        }
+    if (ckpt_block > 0) {
+        p.c = std::max(1, ckpt_block * (V - 1));
+        if (p.c >= P) p.c = 0;           // one block: same as keeping every output
+    }
+    p.nblocks = p.c > 0 ? (P + p.c - 1) / p.c : 1;
+    *out = p;
+    return true;
+}
+
+Workspace size_workspace(const Plan &p, int max_batch, int storage)
+{
+    Workspace w;
+    const size_t B = (size_t)std::max(max_batch, 0);
+    w.state_elems = (size_t)1 << p.n;
+    const size_t elem = storage == 1 ? 4 : 8;
+    w.state_bytes = B * w.state_elems * elem;
+    const size_t Ln = (size_t)p.L * p.n;
+    // tables: zyz (6 doubles), rot_cs, dw (2 floats each), H (9 doubles), statmap (int2),
+    // init_u (4 floats per sample and qubit), views, per-sample E / dL/dE / scratch, loss.
+    w.tables_bytes = Ln * (6 * 8 + 2 * 4 + 2 * 4 + 9 * 8 + 8) + B * p.n * 16 +
+                     (size_t)std::max(p.V, 1) * sizeof(ViewDev) + B * (8 * 3 + 4) + 64;
+    const size_t S_bytes = B * Ln * 3 * 8;
+    if (p.small) {
+        w.n_saved = 1;
+        w.lam_bytes = 0;
+        w.state_bytes = B * w.state_elems * 8;   // final state, fp32 (on-chip path)
+        w.part_passes = 0;
+        w.part_bytes = 0;
+        w.total = w.state_bytes + w.tables_bytes + S_bytes + B * 4;
+        return w;
+    }
+    const int P = p.n_fwd();
+    w.lam_bytes = B * w.state_elems * 8;
+    if (p.c == 0) {
+        w.n_saved = P;
+        w.n_ckpt = 0;
+        w.part_passes = p.n_bwd();
+    } else {
+        w.n_ckpt = p.nblocks - 1;
+        w.n_saved = p.c + w.n_ckpt;
+        w.part_passes = p.c + (int)p.stats_only.size();
+    }
+    w.part_bytes = (size_t)w.part_passes * B * p.T * kSlots * 4;
+    const size_t epart = B * p.T * 4;
+    w.total = (size_t)w.n_saved * w.state_bytes + w.lam_bytes + w.part_bytes + w.tables_bytes + S_bytes + epart;
+    return w;
+}
+
+std::string describe_plan(const Plan &p)
+{
+    std::string s = "{";
+    char buf[256];
+    std::snprintf(buf, sizeof buf, "\"n\":%d,\"L\":%d,\"small\":%s,\"V\":%d,\"T\":%d,\"c\":%d,\"nblocks\":%d,",
+                  p.n, p.L, p.small ? "true" : "false", p.V, p.T, p.c, p.nblocks);
+    s += buf;
+    s += "\"views\":[";
+    for (size_t v = 0; v < p.views.size(); ++v) {
+        const ViewDev &d = p.views[v];
+        s += v ? ",{" : "{";
+        s += "\"perm\":[";
+        for (int i = 0; i < kTileBits; ++i) {
+            std::snprintf(buf, sizeof buf, "%s%d", i ? "," : "", d.perm[i]);
+            s += buf;
+        }
+        s += "],\"tile_q\":[";
+        for (int i = 0; i < d.n_tile; ++i) {
+            std::snprintf(buf, sizeof buf, "%s%d", i ? "," : "", d.tile_q[i]);
+            s += buf;
+        }
+        std::snprintf(buf, sizeof buf, "],\"group_mask\":%d}", d.group_mask);
+        s += buf;
+    }
+    s += "],\"passes\":[";
+    for (size_t i = 0; i < p.fwd.size(); ++i) {
+        const PassPlan &q = p.fwd[i];
+        std::snprintf(buf, sizeof buf, "%s{\"view\":%d,\"init\":%s,\"rotA\":%d,\"diag\":%d,\"rotB\":%d}", i ? "," : "",
+                      q.view, q.init ? "true" : "false", q.rotA, q.diag, q.rotB);
+        s += buf;
+    }
+    s += "],\"stats_only\":[";
+    for (size_t i = 0; i < p.stats_only.size(); ++i) {
+        std::snprintf(buf, sizeof buf, "%s%d", i ? "," : "", p.stats_only[i]);
+        s += buf;
+    }
+    s += "],\"statmap\":[";
+    for (size_t i = 0; i < p.statmap.size(); ++i) {
+        std::snprintf(buf, sizeof buf, "%s[%d,%d]", i ? "," : "", p.statmap[i].pass, p.statmap[i].slot);
+        s += buf;
+    }
+    s += "]}";
+    return s;
+}
+
+}  // namespace hqml

@@ -1,0 +1,67 @@
+// Host scheduler: views, fused-pass schedule, checkpoint plan and workspace sizes.
+// Pure C++ (no HIP calls), so it can size a workspace on a machine without a GPU.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "hqml_internal.hpp"
+
+namespace hqml {
+
+struct PassPlan {
+    int view;
+    bool init;    // generates the layer-0 product state (all of Ry-layer 0)
+    int rotA;     // Ry-layer applied to the view's group first (-1: none)
+    int diag;     // diagonal D_l applied next (-1: none)
+    int rotB;     // Ry-layer applied to the view's group last (-1: none)
+};
+
+struct StatLoc {
+    int pass;     // backward pass index (forward passes, then layer-0 stats-only passes)
+    int slot;     // (sel*13 + pos)*3
+};
+
+struct Plan {
+    int n = 0, L = 0;
+    bool small = false;                  // n <= 13: whole circuit in one workgroup per sample
+    int V = 0;                           // views (tile path)
+    int T = 1;                           // tiles per sample
+    std::vector<ViewDev> views;
+    std::vector<PassPlan> fwd;           // forward passes in order
+    std::vector<int> stats_only;         // views needing a layer-0 stats-only backward pass
+    std::vector<StatLoc> statmap;        // [L*n]
+    // checkpointing (tile path): block of c passes; ckpt_block = 0 keeps every output
+    int c = 0;                           // passes per block (0: store every pass output)
+    int nblocks = 1;
+
+    int n_fwd() const { return (int)fwd.size(); }
+    int n_bwd() const { return (int)fwd.size() + (int)stats_only.size(); }
+};
+
+// Build the plan for an n-qubit, L-layer circuit; ckpt_block = layers per
+// checkpoint block (0 = keep every fused-pass output).  Returns false with a
+// message in *err for unsupported sizes.
+bool make_plan(int n, int L, int ckpt_block, Plan *plan, std::string *err);
+
+// Device memory layout of a context.
+struct Workspace {
+    size_t state_elems = 0;     // amplitudes per sample
+    size_t state_bytes = 0;     // bytes of one saved state for the whole batch
+    size_t lam_bytes = 0;       // adjoint state, fp32
+    int n_saved = 0;            // saved-state buffers (pass outputs, or block buffers + checkpoints)
+    int n_ckpt = 0;             // of which checkpoints
+    int part_passes = 0;        // passes whose statistics partials are held at once
+    size_t part_bytes = 0;
+    size_t tables_bytes = 0;
+    size_t total = 0;
+};
+
+Workspace size_workspace(const Plan &p, int max_batch, int storage);
+
+// Human-readable JSON description of a plan (for tests and reports).
+std::string describe_plan(const Plan &p);
+
+}  // namespace hqml

@@ -1,0 +1,126 @@
+"""GPU path vs the CPU oracle, element by element, through the C ABI.
+
+Tolerances (fp32 state storage): <Z_0> within 1e-5 relative to
+max(|E_ref|, 2^(-n/2)); every dL/dtheta within 1e-4 absolute.  bf16 state
+storage: 2e-2 absolute on both.  Inputs come from ``hqml_inputs`` (seeded).
+"""
+import numpy as np
+import pytest
+
+import hqml_inputs
+import oracle
+from gpu_util import assert_e_close, assert_grad_close, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _ctx(n, L, B, **kw):
+    import qml_gradients_amd as hq
+    return hq.Context(n, L, B, **kw)
+
+
+def _run_train(n, L, B, seed, **kw):
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed)
+    say(f"[gpu] train_step n={n} L={L} B={B} seed={seed} {kw}")
+    ctx = _ctx(n, L, B, **kw)
+    e, loss, g = ctx.train_step(torch.from_numpy(x), torch.from_numpy(th), torch.from_numpy(y))
+    torch.cuda.synchronize()
+    out = (e.cpu().numpy(), float(loss.cpu()[0]), g.cpu().numpy())
+    ctx.close()
+    return (x, th, y), out
+
+
+@pytest.mark.parametrize("n,L,B", [(1, 1, 3), (2, 1, 2), (4, 2, 8), (5, 3, 5), (7, 2, 3), (13, 2, 2)])
+def test_small_path_train_step(n, L, B):
+    (x, th, y), (e, loss, g) = _run_train(n, L, B, seed=10 + n)
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
+    assert_e_close(e, e_ref, n)
+    assert abs(loss - loss_ref) <= 1e-5 * max(1.0, loss_ref)
+    assert_grad_close(g, g_ref)
+
+
+@pytest.mark.parametrize("n,L,B", [(14, 1, 2), (14, 2, 2), (14, 3, 3), (15, 4, 2), (16, 3, 2), (17, 5, 2)])
+def test_tile_path_train_step(n, L, B):
+    (x, th, y), (e, loss, g) = _run_train(n, L, B, seed=20 + n + L)
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
+    assert_e_close(e, e_ref, n)
+    assert abs(loss - loss_ref) <= 1e-5 * max(1.0, loss_ref)
+    assert_grad_close(g, g_ref)
+
+
+def test_tile_path_three_views():
+    n, L, B = 21, 3, 1
+    (x, th, y), (e, loss, g) = _run_train(n, L, B, seed=5)
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
+    assert_e_close(e, e_ref, n)
+    assert_grad_close(g, g_ref)
+
+
+@pytest.mark.parametrize("n,L,B", [(4, 2, 8), (12, 3, 4), (14, 3, 3), (16, 2, 2)])
+def test_forward_backward_split(n, L, B):
+    x, th, _ = hqml_inputs.make_inputs(n, L, B, seed=33)
+    w = np.linspace(-0.7, 1.3, B).astype(np.float32)
+    say(f"[gpu] forward+backward n={n} L={L} B={B}")
+    ctx = _ctx(n, L, B)
+    e = ctx.forward(torch.from_numpy(x), torch.from_numpy(th), save_for_backward=True)
+    g = ctx.backward(torch.from_numpy(w))
+    torch.cuda.synchronize()
+    g_ref, e_ref = oracle.backward(x, th, w)
+    assert_e_close(e.cpu().numpy(), e_ref, n)
+    assert_grad_close(g.cpu().numpy(), g_ref)
+    ctx.close()
+
+
+@pytest.mark.parametrize("name", ["hea4q2l", "hea12q20l"])
+def test_named_workload_full(name):
+    w = hqml_inputs.WORKLOADS[name]
+    x, th, y = hqml_inputs.workload_inputs(name)
+    say(f"[gpu] workload {name}")
+    ctx = _ctx(w.n_qubits, w.n_layers, w.batch)
+    e, loss, g = ctx.train_step(torch.from_numpy(x), torch.from_numpy(th), torch.from_numpy(y))
+    torch.cuda.synchronize()
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
+    assert_e_close(e.cpu().numpy(), e_ref, w.n_qubits)
+    assert_grad_close(g.cpu().numpy(), g_ref)
+    ctx.close()
+
+
+def test_deterministic_and_batch_additive():
+    n, L, B = 15, 3, 4
+    x, th, _ = hqml_inputs.make_inputs(n, L, B, seed=44)
+    w = np.array([0.3, -1.0, 0.5, 2.0], dtype=np.float32)
+    say("[gpu] determinism / additivity")
+    ctx = _ctx(n, L, B)
+    X, TH = torch.from_numpy(x), torch.from_numpy(th)
+    ctx.forward(X, TH)
+    g1 = ctx.backward(torch.from_numpy(w)).cpu().numpy()
+    ctx.forward(X, TH)
+    g2 = ctx.backward(torch.from_numpy(w)).cpu().numpy()
+    assert np.array_equal(g1, g2)
+    parts = np.zeros_like(g1, dtype=np.float64)
+    for b in range(B):
+        ctx.forward(X[b:b + 1], TH)
+        parts += ctx.backward(torch.from_numpy(w[b:b + 1])).cpu().numpy()
+    assert np.max(np.abs(parts - g1)) < 1e-5
+    ctx.close()
+
+
+def test_error_paths():
+    import qml_gradients_amd as hq
+    say("[gpu] error paths")
+    ctx = _ctx(14, 2, 2)
+    g = torch.empty((2, 14, 3), device="cuda")
+    with pytest.raises(hq.HqmlError) as e:
+        hq.hqml_backward(ctx.handle, g.data_ptr(), g.data_ptr())
+    assert e.value.status == hq.HQML_ERR_STATE
+    with pytest.raises(hq.HqmlError) as e:
+        ctx.forward(torch.zeros((3, 14)), torch.zeros((2, 14, 3)))
+    assert e.value.status == hq.HQML_ERR_ARG
+    # empty batch: forward does nothing, backward gives a zero gradient
+    hq.hqml_forward(ctx.handle, 0, 0, 0, 0, 1)
+    hq.hqml_backward(ctx.handle, 0, g.data_ptr())
+    torch.cuda.synchronize()
+    assert float(g[:2].abs().max()) == 0.0
+    ctx.close()

@@ -1,0 +1,164 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+* the library loads and exports every function include/hqml.h declares;
+* argument validation and workspace sizing work without touching a device;
+* the fused-pass schedule the library plans is complete and consistent;
+* a NumPy model of the kernels' algebra on that schedule matches the oracle;
+* the tile layouts used by the kernels are bijective and bank-conflict free.
+"""
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import hqml_inputs
+import oracle
+import qml_gradients_amd as hq
+from tile_model import Model
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    if not os.path.exists(hq.LIB_PATH):
+        from qml_gradients_amd import build
+        build.build()
+    return hq.load()
+
+
+def test_exports_every_declared_function():
+    lib = _lib()
+    header = open(os.path.join(ROOT, "include", "hqml.h")).read()
+    declared = set(re.findall(r"\b(hqml_[a-z_]+)\s*\(", header))
+    assert declared == set(hq.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_workspace_and_validation_host_only():
+    _lib()
+    assert hq.hqml_workspace_bytes(hq.make_config(20, 100, 32)) > 100 * 32 * (1 << 20) * 8
+    for bad in (hq.make_config(0, 1, 1), hq.make_config(30, 1, 1), hq.make_config(4, 0, 1),
+                hq.make_config(4, 1, 0), hq.make_config(4, 1, 1, storage=7),
+                hq.make_config(4, 1, 1, ckpt_block=-1)):
+        assert hq.hqml_workspace_bytes(bad) == 0
+        with pytest.raises(hq.HqmlError) as e:
+            hq.hqml_create(bad)
+        assert e.value.status == hq.HQML_ERR_ARG
+    assert hq.load().hqml_status_str(hq.HQML_ERR_STATE) == b"call out of order"
+
+
+def test_workspace_scaling_checkpoint_and_bf16():
+    _lib()
+    full = hq.hqml_workspace_bytes(hq.make_config(20, 1000, 60))
+    ck20 = hq.hqml_workspace_bytes(hq.make_config(20, 1000, 60, ckpt_block=20))
+    ck20b = hq.hqml_workspace_bytes(hq.make_config(20, 1000, 60, storage="bf16", ckpt_block=20))
+    st = 60 * (1 << 20) * 8
+    # store-all keeps ~1000 states; b=20 keeps 20 block states + 49 checkpoints + lambda
+    assert full > 990 * st
+    assert 60 * st < ck20 < 80 * st
+    assert ck20b < ck20
+
+
+def _plan(n, L, ckpt=0):
+    _lib()
+    return json.loads(hq.hqml_describe_plan(hq.make_config(n, L, 1, ckpt_block=ckpt)))
+
+
+@pytest.mark.parametrize("n", list(range(1, 30)))
+def test_plan_invariants(n):
+    for L in (1, 2, 3, 5):
+        p = _plan(n, L)
+        assert len(p["statmap"]) == L * n
+        if n <= 13:
+            assert p["small"]
+            continue
+        V = p["V"]
+        assert V == max(2, (n - 4 + 7) // 8)
+        assert p["T"] == 1 << (n - 13)
+        assert len(p["passes"]) == 1 + (L - 1) * (V - 1)
+        seen = set()
+        owner = {}
+        for vi, v in enumerate(p["views"]):
+            perm = v["perm"]
+            assert sorted(perm[:4]) == [0, 1, 2, 3]
+            assert len(set(perm)) == 13 and sorted(perm + v["tile_q"]) == list(range(n))
+            assert v["group_mask"] & ~0x0FF3 == 0          # only rotatable positions
+            for pos in range(13):
+                if (v["group_mask"] >> pos) & 1:
+                    assert perm[pos] not in owner
+                    owner[perm[pos]] = vi
+            # qubit 3 at an L2 low register position => qubit 4 not at L2 positions 9..11
+            if perm.index(3) in (0, 1) and 4 in perm:
+                assert perm.index(4) not in (9, 10, 11)
+        assert sorted(owner) == list(range(n))
+        for k, s in p["statmap"]:
+            assert (k, s) not in seen
+            seen.add((k, s))
+            assert 0 <= k < len(p["passes"]) + len(p["stats_only"])
+        # each pass rotates only its own view's group and the layers appear in order
+        last_layer = {}
+        for ps in p["passes"]:
+            for key in ("rotA", "rotB"):
+                if ps[key] >= 0:
+                    assert ps[key] >= last_layer.get(ps["view"], 0)
+                    last_layer[ps["view"]] = ps[key]
+
+
+@pytest.mark.parametrize("n,L,B", [(14, 1, 2), (14, 3, 2), (15, 4, 2), (17, 2, 1), (16, 5, 1)])
+def test_model_of_kernel_algebra_matches_oracle(n, L, B):
+    x, th, _ = hqml_inputs.make_inputs(n, L, B, seed=100 + n + L)
+    m = Model(hq.hqml_describe_plan(hq.make_config(n, L, B)), x, th)
+    w = np.linspace(0.5, -1.0, B)
+    e, g = m.backward(w)
+    g_ref, e_ref = oracle.backward(x, th, w)
+    assert np.max(np.abs(e - e_ref)) < 1e-10
+    assert np.max(np.abs(g - g_ref)) < 1e-10
+
+
+@pytest.mark.slow
+def test_model_three_views_matches_oracle():
+    n, L, B = 21, 3, 1
+    x, th, _ = hqml_inputs.make_inputs(n, L, B, seed=7)
+    m = Model(hq.hqml_describe_plan(hq.make_config(n, L, B)), x, th)
+    assert m.plan["V"] == 3
+    e, g = m.backward(np.ones(B))
+    g_ref, e_ref = oracle.backward(x, th, np.ones(B))
+    assert np.max(np.abs(e - e_ref)) < 1e-10
+    assert np.max(np.abs(g - g_ref)) < 1e-10
+
+
+# ---- tile layouts (restated from the kernel source's layout comments) ----
+
+def swz(l):
+    return l ^ ((l >> 4) & 3) ^ ((((l >> 6) ^ (l >> 9)) & 1) << 4)
+
+
+def l1(lane, w, j):
+    return (lane & 15) | ((lane >> 4) << 9) | (w << 11) | (j << 4)
+
+
+def l2(lane, w, j):
+    return (lane << 2) | ((w & 1) << 8) | ((w >> 1) << 12) | (j & 3) | ((j >> 2) << 9)
+
+
+def test_tile_layouts_bijective_and_conflict_free():
+    a1 = {l1(la, w, j) for la in range(64) for w in range(4) for j in range(32)}
+    a2 = {l2(la, w, j) for la in range(64) for w in range(4) for j in range(32)}
+    assert a1 == a2 == set(range(8192))
+    assert {swz(i) for i in range(8192)} == set(range(8192))
+    for f in (l1, l2):
+        for w in range(4):
+            for j in range(32):
+                for half in range(2):        # 64 banks x 4 B: 32 lanes x 8 B per cycle
+                    slots = {swz(f(la, w, j)) & 31 for la in range(32 * half, 32 * half + 32)}
+                    assert len(slots) == 32
+                for quarter in range(4):     # 32 banks x 4 B: 16 lanes x 8 B per cycle
+                    slots = {swz(f(la, w, j)) & 15 for la in range(16 * quarter, 16 * quarter + 16)}
+                    assert len(slots) == 16
+    # linearity used to split addresses into thread and register parts
+    for t in range(0, 8192, 97):
+        for j in range(32):
+            assert swz(l1(t & 63, t >> 6 & 3, 0) ^ (j << 4)) == swz(l1(t & 63, t >> 6 & 3, 0)) ^ swz(j << 4)

@@ -1,0 +1,186 @@
+"""NumPy model of the GPU path's algebra and schedule (host-logic test aid).
+
+This is not the oracle.  It re-states, on whole state vectors, what the
+library's kernels do -- the SU(2) factorisation of each layer into
+diag(p) Ry(beta) diag(r), the merged diagonal D_l, the fused-pass schedule and
+the places where gradient statistics are taken -- using the schedule the
+library itself reports (``hqml_describe_plan``).  Comparing it with the oracle
+on the CPU checks the algebra and the planner before any GPU run; the GPU
+kernels are then compared with the oracle directly.
+"""
+from __future__ import annotations
+
+import json
+
+import numpy as np
+
+
+def _rx(t):
+    c, s = np.cos(t / 2), np.sin(t / 2)
+    return np.array([[c, -1j * s], [-1j * s, c]])
+
+
+def _ry(t):
+    c, s = np.cos(t / 2), np.sin(t / 2)
+    return np.array([[c, -s], [s, c]], dtype=complex)
+
+
+def _rz(t):
+    return np.diag([np.exp(-0.5j * t), np.exp(0.5j * t)])
+
+
+X = np.array([[0, 1], [1, 0]], dtype=complex)
+Y = np.array([[0, -1j], [1j, 0]])
+Z = np.diag([1.0 + 0j, -1.0])
+
+
+def factorise(theta):
+    """Per (l, q): cos(beta/2), sin(beta/2), p, r with U = diag(p, p*) Ry(beta) diag(r, r*)."""
+    L, n, _ = theta.shape
+    cb = np.zeros((L, n))
+    sb = np.zeros((L, n))
+    p = np.zeros((L, n), dtype=complex)
+    r = np.zeros((L, n), dtype=complex)
+    H = np.zeros((L, n, 3, 3))
+    for l in range(L):
+        for q in range(n):
+            a, b, g = (float(v) for v in theta[l, q])
+            U = _rz(g) @ _ry(b) @ _rx(a)
+            x, y = U[0, 0], U[1, 0]
+            ax, ay = abs(x), abs(y)
+            xh = x / ax if ax > 1e-300 else 1.0
+            yh = y / ay if ay > 1e-300 else 1.0
+            rr = np.exp(0.5j * np.angle(xh * yh))
+            pp = xh * np.conj(rr)
+            cb[l, q], sb[l, q], p[l, q], r[l, q] = ax, ay, pp, rr
+            Lp = np.diag([pp, np.conj(pp)])
+            G = [(_rz(g) @ _ry(b)) @ X @ (_rz(g) @ _ry(b)).conj().T, _rz(g) @ Y @ _rz(g).conj().T, Z]
+            for k in range(3):
+                S = Lp.conj().T @ G[k] @ Lp
+                H[l, q, k] = [S[0, 1].real, -S[0, 1].imag, S[0, 0].real]
+    return cb, sb, p, r, H
+
+
+class Model:
+    def __init__(self, plan_json: str, x, theta):
+        self.plan = json.loads(plan_json)
+        self.x = np.asarray(x, dtype=np.float64)
+        self.theta = np.asarray(theta, dtype=np.float64)
+        self.L, self.n = self.theta.shape[0], self.theta.shape[1]
+        self.cb, self.sb, self.p, self.r, self.H = factorise(self.theta)
+        n = self.n
+        self.idx = np.arange(1 << n, dtype=np.int64)
+        self.bits = [((self.idx >> q) & 1).astype(bool) for q in range(n)]
+        self.cz = np.where(np.bitwise_count(self.idx & (self.idx >> 1) & ((1 << (n - 1)) - 1)) & 1, -1.0, 1.0)
+        self.groups = []
+        for v in self.plan["views"]:
+            perm, gm = v["perm"], v["group_mask"]
+            self.groups.append([perm[pos] for pos in range(13) if (gm >> pos) & 1])
+
+    # --- circuit pieces -------------------------------------------------
+    def init_state(self, b):
+        n = self.n
+        psi = np.ones(1, dtype=complex)
+        for q in range(n - 1, -1, -1):
+            c, s = np.cos(self.x[b, q] / 2), np.sin(self.x[b, q] / 2)
+            v = np.array([self.r[0, q] * c, np.conj(self.r[0, q]) * s])
+            u = np.array([[self.cb[0, q], -self.sb[0, q]], [self.sb[0, q], self.cb[0, q]]]) @ v
+            psi = np.kron(psi, u)
+        return psi
+
+    def rot(self, psi, l, qubits, inverse=False):
+        psi = psi.copy()
+        for q in qubits:
+            c, s = self.cb[l, q], self.sb[l, q] * (-1 if inverse else 1)
+            v = psi.reshape(-1, 2, 1 << q)
+            a, bb = v[:, 0, :].copy(), v[:, 1, :].copy()
+            v[:, 0, :] = c * a - s * bb
+            v[:, 1, :] = s * a + c * bb
+        return psi
+
+    def diag(self, l):
+        w = self.p[l] * self.r[l + 1]
+        d = self.cz.astype(complex)
+        for q in range(self.n):
+            d = d * np.where(self.bits[q], np.conj(w[q]), w[q])
+        return d
+
+    def stats(self, psi, lam, q):
+        b = self.bits[q]
+        i0 = self.idx[~b]
+        i1 = i0 | (1 << q)
+        li, lj, pi, pj = lam[i0], lam[i1], psi[i0], psi[i1]
+        sx = np.sum(np.imag(np.conj(li) * pj) + np.imag(np.conj(lj) * pi))
+        sy = np.sum(np.real(np.conj(lj) * pi) - np.real(np.conj(li) * pj))
+        sz = np.sum(np.imag(np.conj(li) * pi) - np.imag(np.conj(lj) * pj))
+        return np.array([sx, sy, sz])
+
+    # --- fused passes -------------------------------------------------
+    def forward_pass(self, k, psi, b):
+        ps = self.plan["passes"][k]
+        g = self.groups[ps["view"]]
+        if ps["init"]:
+            psi = self.init_state(b)
+        if ps["rotA"] >= 0:
+            psi = self.rot(psi, ps["rotA"], g)
+        if ps["diag"] >= 0:
+            psi = psi * self.diag(ps["diag"])
+        if ps["rotB"] >= 0:
+            psi = self.rot(psi, ps["rotB"], g)
+        return psi
+
+    def run_sample(self, b):
+        P = len(self.plan["passes"])
+        outs = []
+        psi = None
+        for k in range(P):
+            psi = self.forward_pass(k, psi, b)
+            outs.append(psi)
+        e = float(np.sum(np.where(self.bits[0], -1.0, 1.0) * np.abs(psi) ** 2))
+        lam = np.where(self.bits[0], -1.0, 1.0) * psi
+        part = {}
+        for k in range(P - 1, -1, -1):
+            ps = self.plan["passes"][k]
+            g = self.groups[ps["view"]]
+            v = self.plan["views"][ps["view"]]
+            inv = {q: pos for pos, q in enumerate(v["perm"])}
+            psi = outs[k]
+            if ps["rotB"] >= 0:
+                for q in g:
+                    part[(k, (13 + inv[q]) * 3)] = self.stats(psi, lam, q)
+                psi = self.rot(psi, ps["rotB"], g, inverse=True)
+                lam = self.rot(lam, ps["rotB"], g, inverse=True)
+                d = np.conj(self.diag(ps["diag"]))
+                psi, lam = psi * d, lam * d
+                for q in g:
+                    part[(k, inv[q] * 3)] = self.stats(psi, lam, q)
+                if not ps["init"]:
+                    lam = self.rot(lam, ps["rotA"], g, inverse=True)
+            elif ps["rotA"] >= 0:
+                for q in g:
+                    part[(k, inv[q] * 3)] = self.stats(psi, lam, q)
+                lam = self.rot(lam, ps["rotA"], g, inverse=True)
+            else:
+                for q in g:
+                    part[(k, inv[q] * 3)] = self.stats(psi, lam, q)
+        psi0 = self.init_state(b)
+        for i, vi in enumerate(self.plan["stats_only"]):
+            v = self.plan["views"][vi]
+            inv = {q: pos for pos, q in enumerate(v["perm"])}
+            for q in self.groups[vi]:
+                part[(P + i, inv[q] * 3)] = self.stats(psi0, lam, q)
+        S = np.zeros((self.L, self.n, 3))
+        for l in range(self.L):
+            for q in range(self.n):
+                pk, slot = self.plan["statmap"][l * self.n + q]
+                S[l, q] = part[(pk, slot)]
+        return e, S
+
+    def backward(self, dlde):
+        B = self.x.shape[0]
+        E = np.zeros(B)
+        grad = np.zeros((self.L, self.n, 3))
+        for b in range(B):
+            E[b], S = self.run_sample(b)
+            grad += dlde[b] * np.einsum("lqas,lqs->lqa", self.H, S)
+        return E, grad
