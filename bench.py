@@ -99,6 +99,8 @@ def main():
     ap.add_argument("--workload", default="hea20q100l")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--instrumented-steps", type=int, default=3)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
@@ -109,6 +111,17 @@ def main():
 
     import hqml_inputs
     import qml_gradients_amd as hq
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read_per_launch": src.numel() * 4,
+                          "copy_bytes_written_per_launch": src.numel() * 4}), flush=True)
+        return
 
     w = hqml_inputs.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
@@ -154,9 +167,9 @@ def main():
     n_steps = args.instrumented_steps
 
     def roof(kind, total_bytes_per_step, kernel_name):
-        launches = cnt_k[kind] / n_steps
-        if launches == 0:
+        if n_steps == 0 or cnt_k[kind] == 0:
             return None
+        launches = cnt_k[kind] / n_steps
         per_launch_bytes = total_bytes_per_step / launches
         avg_ms = ms_k[kind] / cnt_k[kind]
         achieved = per_launch_bytes / (avg_ms / 1e3) / 1e9
@@ -192,7 +205,7 @@ def main():
                    "per_layer": round(len(plan["passes"]) / w.n_layers, 3)},
         "roofline": roof_bwd if roof_bwd else roof_fwd,
         "roofline_fwd": roof_fwd,
-        "kernel_ms_per_step": {k: round(ms_k[i] / n_steps, 3) for i, k in
+        "kernel_ms_per_step": {k: round(ms_k[i] / max(n_steps, 1), 3) for i, k in
                                enumerate(["fwd_pass", "bwd_pass", "small", "other"])},
     }
     ctx.close()

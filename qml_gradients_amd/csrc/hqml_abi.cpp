@@ -21,8 +21,8 @@
 #include "hqml_plan.hpp"
 
 namespace hqml {
-hipError_t launch_prep(const float *theta, const float *x, int L, int n, int B, double *zyz, float *rot_cs,
-                       float *dw, double *H, float *init_u, hipStream_t s);
+hipError_t launch_prep(const float *theta, const float *x, int L, int n, int B, double *zyz, unsigned char *G,
+                       float *rot_tf, float *dw, double *H, float *init_u, hipStream_t s);
 hipError_t launch_tile_fwd(const TilePassArgs &a, int B, int storage, hipStream_t s);
 hipError_t launch_tile_bwd(const TilePassArgs &a, int B, int storage, hipStream_t s);
 hipError_t launch_small(const SmallArgs &a, int B, hipStream_t s);
@@ -51,7 +51,8 @@ struct hqml_ctx {
     float *e_part = nullptr;
     double *S = nullptr;
     double *zyz = nullptr;
-    float *rot_cs = nullptr;
+    unsigned char *frame = nullptr;
+    float *rot_tf = nullptr;
     float *dw = nullptr;
     double *H = nullptr;
     float *init_u = nullptr;
@@ -145,7 +146,7 @@ TilePassArgs base_args(hqml_ctx *c)
     std::memset(&a, 0, sizeof a);
     a.lam = c->lam;
     a.e_part = c->e_part;
-    a.rot_cs = c->rot_cs;
+    a.rot_tf = c->rot_tf;
     a.dw = c->dw;
     a.init_u = c->init_u;
     a.n = c->plan.n;
@@ -199,8 +200,8 @@ int bwd_pass(hqml_ctx *c, int B, int k, int part_lo, float *part_base, int extra
 int prep(hqml_ctx *c, int B, const float *x, const float *theta)
 {
     return run(c, HQML_K_OTHER, "table preparation", [&] {
-        return launch_prep(theta, x, c->plan.L, c->plan.n, B, c->zyz, c->rot_cs, c->dw, c->H, c->init_u,
-                           c->stream);
+        return launch_prep(theta, x, c->plan.L, c->plan.n, B, c->zyz, c->frame, c->rot_tf, c->dw, c->H,
+                           c->init_u, c->stream);
     });
 }
 
@@ -292,7 +293,7 @@ SmallArgs small_args(hqml_ctx *c, int mode)
     SmallArgs a;
     std::memset(&a, 0, sizeof a);
     a.init_u = c->init_u;
-    a.rot_cs = c->rot_cs;
+    a.rot_tf = c->rot_tf;
     a.dw = c->dw;
     a.psi_save = reinterpret_cast<float *>(c->saved);
     a.e_out = c->e_part;
@@ -380,8 +381,9 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     c->e_part = static_cast<float *>(grab((size_t)B * plan.T * 4));
     c->S = static_cast<double *>(grab((size_t)B * Ln * 3 * 8));
     c->zyz = static_cast<double *>(grab(Ln * 6 * 8));
-    c->rot_cs = static_cast<float *>(grab(Ln * 2 * 4));
-    c->dw = static_cast<float *>(grab(Ln * 2 * 4));
+    c->frame = static_cast<unsigned char *>(grab(Ln));
+    c->rot_tf = static_cast<float *>(grab(Ln * 2 * 4));
+    c->dw = static_cast<float *>(grab(Ln * 4 * 4));
     c->H = static_cast<double *>(grab(Ln * 9 * 8));
     c->init_u = static_cast<float *>(grab((size_t)B * plan.n * 16));
     if (!plan.small) c->views = static_cast<ViewDev *>(grab(plan.views.size() * sizeof(ViewDev)));

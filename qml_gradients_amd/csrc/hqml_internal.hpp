@@ -27,7 +27,8 @@
 // on qubit q, mu the back-propagated Z_0 psi_M),
 //     dE/dtheta[l][q][a] = sum_s H[l][q][a][s] * S_s,
 // where H holds the Pauli coefficients of p-conjugated rotated generators
-// (computed in k_prep_layers).
+// (computed in k_prep_tables).  A Pauli frame (k_prep_frame) then keeps every
+// simulated rotation in the form f [[1, -k], [k, 1]] with |k| <= 1.
 #pragma once
 #include <stdint.h>
 
@@ -79,8 +80,8 @@ struct TilePassArgs {
     float *lam;             // bwd: adjoint state, fp32 complex, updated in place
     float *e_part;          // [B][T] per-tile <Z_0> partial sums
     float *stat_part;       // [B][T][kSlots] per-tile gradient statistics of this pass
-    const float *rot_cs;    // [L][n][2]: cos, sin of beta/2 (the real rotation)
-    const float *dw;        // [L][n][2]: w_{l,q} of D_l
+    const float *rot_tf;    // [L][n][2]: tan form (k, f) of the real rotation
+    const float *dw;        // [L][n][4]: factors (f0, f1) of qubit q in D_l
     const float *init_u;    // [B][n][4]: (u0.re, u0.im, u1.re, u1.im) layer-0 product factors
     const ViewDev *view;
     int n;
@@ -95,8 +96,8 @@ struct TilePassArgs {
 
 struct SmallArgs {
     const float *init_u;    // [B][n][4]
-    const float *rot_cs;    // [L][n][2]
-    const float *dw;        // [L][n][2]
+    const float *rot_tf;    // [L][n][2]
+    const float *dw;        // [L][n][4]
     float *psi_save;        // [B][2^n][2]: final state (forward mode writes, backward mode reads)
     float *e_out;           // [B] per-sample <Z_0> (fp32, from an fp64 in-block sum)
     double *stats;          // [B][L][n][3] per-sample statistics S_s at point P_l

@@ -7,7 +7,8 @@
 //
 // Kernels:
 //   k_prep_zyz      theta -> per (layer, qubit) factorisation U = diag(p) Ry(beta) diag(r)
-//   k_prep_tables   -> rot_cs (cos, sin of beta/2), dw (w = p_l r_{l+1}), H (gradient map)
+//   k_prep_frame    Pauli frame that keeps every simulated rotation in tan form
+//   k_prep_tables   -> rot_tf (tan form of each rotation), dw (diagonal factors), H (gradient map)
 //   k_prep_init     x -> layer-0 product-state factors u_q per sample
 //   k_tile_fwd      fused forward pass over one 2^13-amplitude tile (forward gate fusion)
 //   k_tile_bwd      fused adjoint pass over one tile (backward gate fusion): re-derives the
@@ -145,88 +146,102 @@ __device__ __forceinline__ void transpose(Tile &t, float2 *lds, uint32_t a1, uin
     }
 }
 
-// Real rotation Ry on register bit M: [[c, -s], [s, c]] (sgn = +1) or its inverse (sgn = -1).
-template <int M>
-__device__ __forceinline__ void rot_bit(Tile &t, float c, float s)
+// Real rotation Ry(beta) on register bit M in scaled form, one FMA per real output:
+//   Ry(beta) = f * [[1, -k], [k, 1]],  k = tan(beta/2) in [-1, 1],  f = cos(beta/2).
+// INV applies Ry^dagger.  The scale f (>= 1/sqrt 2) is not applied here: callers track
+// it as a uniform scalar and fold it into the next diagonal, a statistics correction
+// or the final store.  k = 0 is the identity (used for register bits a view does not
+// rotate), so the code has no data-dependent branches.
+template <int M, bool INV>
+__device__ __forceinline__ void rot_bit(Tile &t, float k)
 {
+    const float kk = INV ? -k : k;
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
         if (j & (1 << M)) continue;
-        const int k = j | (1 << M);
-        const float ar = t.re[j], ai = t.im[j], br = t.re[k], bi = t.im[k];
-        t.re[j] = c * ar - s * br;
-        t.im[j] = c * ai - s * bi;
-        t.re[k] = s * ar + c * br;
-        t.im[k] = s * ai + c * bi;
+        const int o = j | (1 << M);
+        const float ar = t.re[j], ai = t.im[j], br = t.re[o], bi = t.im[o];
+        t.re[j] = fmaf(-kk, br, ar);
+        t.im[j] = fmaf(-kk, bi, ai);
+        t.re[o] = fmaf(kk, ar, br);
+        t.im[o] = fmaf(kk, ai, bi);
     }
 }
 
-template <int M>
-__device__ __forceinline__ void rot_bit2(Tile &a, Tile &b, float c, float s)
-{
-    rot_bit<M>(a, c, s);
-    rot_bit<M>(b, c, s);
-}
-
-// Rotation coefficients of register bits for one layer, loaded once per use.
+// Rotation coefficients of the register bits for one layer.
 struct RotCoef {
-    float c[5], s[5];
+    float k[5];
+    float F;         // product of the scale factors of the rotated bits
 };
 
-__device__ __forceinline__ RotCoef load_coef(const float *rot_cs, int n, int layer, const int *qpos_to_q,
-                                             uint32_t regmask, float sgn)
+// rot_tf[l][q] = (k, f).  Bits outside regmask get k = 0, f = 1 (identity).
+__device__ __forceinline__ RotCoef load_coef(const float *rot_tf, int n, int layer, const int *qpos_to_q,
+                                             uint32_t regmask)
 {
     RotCoef rc;
+    rc.F = 1.f;
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
+        rc.k[m] = 0.f;
         if (regmask & (1u << m)) {
             const int q = qpos_to_q[m];
-            rc.c[m] = rot_cs[((size_t)layer * n + q) * 2 + 0];
-            rc.s[m] = sgn * rot_cs[((size_t)layer * n + q) * 2 + 1];
-        } else {
-            rc.c[m] = 1.f;
-            rc.s[m] = 0.f;
+            rc.k[m] = rot_tf[((size_t)layer * n + q) * 2 + 0];
+            rc.F *= rot_tf[((size_t)layer * n + q) * 2 + 1];
         }
     }
     return rc;
 }
 
-__device__ __forceinline__ void rot_layer(Tile &t, const RotCoef &rc, uint32_t regmask)
+template <bool INV>
+__device__ __forceinline__ void rot_layer(Tile &t, const RotCoef &rc)
 {
-    if (regmask & 1u) rot_bit<0>(t, rc.c[0], rc.s[0]);
-    if (regmask & 2u) rot_bit<1>(t, rc.c[1], rc.s[1]);
-    if (regmask & 4u) rot_bit<2>(t, rc.c[2], rc.s[2]);
-    if (regmask & 8u) rot_bit<3>(t, rc.c[3], rc.s[3]);
-    if (regmask & 16u) rot_bit<4>(t, rc.c[4], rc.s[4]);
+    rot_bit<0, INV>(t, rc.k[0]);
+    rot_bit<1, INV>(t, rc.k[1]);
+    rot_bit<2, INV>(t, rc.k[2]);
+    rot_bit<3, INV>(t, rc.k[3]);
+    rot_bit<4, INV>(t, rc.k[4]);
 }
 
-__device__ __forceinline__ void rot_layer2(Tile &a, Tile &b, const RotCoef &rc, uint32_t regmask)
+template <bool INV>
+__device__ __forceinline__ void rot_layer2(Tile &a, Tile &b, const RotCoef &rc)
 {
-    if (regmask & 1u) rot_bit2<0>(a, b, rc.c[0], rc.s[0]);
-    if (regmask & 2u) rot_bit2<1>(a, b, rc.c[1], rc.s[1]);
-    if (regmask & 4u) rot_bit2<2>(a, b, rc.c[2], rc.s[2]);
-    if (regmask & 8u) rot_bit2<3>(a, b, rc.c[3], rc.s[3]);
-    if (regmask & 16u) rot_bit2<4>(a, b, rc.c[4], rc.s[4]);
+    rot_layer<INV>(a, rc);
+    rot_layer<INV>(b, rc);
 }
 
-// X / Y statistics of register bit M: Im<lam|X_q|psi>, Im<lam|Y_q|psi> partial sums.
+__device__ __forceinline__ void scale_tile(Tile &t, float s)
+{
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+        t.re[j] *= s;
+        t.im[j] *= s;
+    }
+}
+
+// X / Y statistics of register bit M (pairs j, o = j | 2^M):
+//   Im<lam|X_q|psi> = sum Im(conj(l_j) p_o) + Im(conj(l_o) p_j)
+//   Im<lam|Y_q|psi> = sum Re(conj(l_o) p_j) - Re(conj(l_j) p_o)
+// written as chains of plain FMAs into separate positive / negative accumulators
+// (no negated operand copies).
 template <int M>
 __device__ __forceinline__ void xy_stats(const Tile &p, const Tile &l, float &sx, float &sy)
 {
-    float ax = 0.f, ay = 0.f;
+    float xp = 0.f, xn = 0.f, yp = 0.f, yn = 0.f;
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
         if (j & (1 << M)) continue;
-        const int k = j | (1 << M);
-        // Im(conj(l_j) p_k) + Im(conj(l_k) p_j)
-        ax += l.re[j] * p.im[k] - l.im[j] * p.re[k];
-        ax += l.re[k] * p.im[j] - l.im[k] * p.re[j];
-        // Re(conj(l_k) p_j) - Re(conj(l_j) p_k)
-        ay += l.re[k] * p.re[j] + l.im[k] * p.im[j];
-        ay -= l.re[j] * p.re[k] + l.im[j] * p.im[k];
+        const int o = j | (1 << M);
+        xp = fmaf(l.re[j], p.im[o], xp);
+        xp = fmaf(l.re[o], p.im[j], xp);
+        xn = fmaf(l.im[j], p.re[o], xn);
+        xn = fmaf(l.im[o], p.re[j], xn);
+        yp = fmaf(l.re[o], p.re[j], yp);
+        yp = fmaf(l.im[o], p.im[j], yp);
+        yn = fmaf(l.re[j], p.re[o], yn);
+        yn = fmaf(l.im[j], p.im[o], yn);
     }
-    sx = ax;
-    sy = ay;
+    sx = xp - xn;
+    sy = yp - yn;
 }
 
 // Reduce one statistic over the workgroup into the LDS stat area (16 row partials per slot).
@@ -240,8 +255,8 @@ __device__ __forceinline__ void stat_out(float v, float *lds_stat, int slot, int
 __host__ __device__ constexpr int l1_pos(int m) { return 4 + m; }
 __host__ __device__ constexpr int l2_pos(int m) { return m < 2 ? m : 7 + m; }
 
-// Z statistics of all 5 register bits: d_m = sum_j (-1)^{bit m of j} w_j with
-// w_j = Im(conj(l_j) p_j), by pairwise halving (level m folds bit m).
+// Z statistics of register bits LEVEL..4 from the pairwise sums left by the
+// previous level: d_m = sum_j (-1)^{bit m of j} w_j with w_j = Im(conj(l_j) p_j).
 template <int LEVEL>
 __device__ __forceinline__ void z_fold(float *wv, float *dz)
 {
@@ -256,24 +271,35 @@ __device__ __forceinline__ void z_fold(float *wv, float *dz)
     if constexpr (LEVEL < 4) z_fold<LEVEL + 1>(wv, dz);
 }
 
-// Statistics of every selected register bit: slots ((sel*13 + pos)*3 + {X,Y,Z}).
+// Statistics of the 5 register bits: slots ((sel*13 + pos)*3 + {X,Y,Z}).  Bits a
+// view does not rotate land in slots nobody reads.  'corr' is the uniform factor
+// (product of the tracked scales of psi and lambda) that turns the stored-state
+// statistics into those of the true states.
 template <bool L2>
-__device__ __forceinline__ void stats_visit(const Tile &p, const Tile &l, uint32_t regmask, int sel,
-                                            float *lds_stat, int lane, int w)
+__device__ __forceinline__ void stats_visit(const Tile &p, const Tile &l, int sel, float *lds_stat, int lane,
+                                            int w, float corr)
 {
-    float wv[kRegs];
-#pragma unroll
-    for (int j = 0; j < kRegs; ++j) wv[j] = l.re[j] * p.im[j] - l.im[j] * p.re[j];
+    // level 0 folded while forming w, so only 16 partial sums are live
+    float wv[kRegs / 2];
     float dz[5];
-    z_fold<0>(wv, dz);
+    float d0 = 0.f;
+#pragma unroll
+    for (int k = 0; k < kRegs / 2; ++k) {
+        const float w0 = fmaf(l.re[2 * k], p.im[2 * k], -l.im[2 * k] * p.re[2 * k]);
+        const float w1 = fmaf(l.re[2 * k + 1], p.im[2 * k + 1], -l.im[2 * k + 1] * p.re[2 * k + 1]);
+        d0 += w0 - w1;
+        wv[k] = w0 + w1;
+    }
+    dz[0] = d0;
+    z_fold<1>(wv, dz);
     float sx, sy;
 #define HQML_STAT_BIT(M)                                                        \
-    if (regmask & (1u << M)) {                                                  \
+    {                                                                           \
         xy_stats<M>(p, l, sx, sy);                                              \
         const int base = (sel * 13 + (L2 ? l2_pos(M) : l1_pos(M))) * 3;         \
-        stat_out(sx, lds_stat, base + 0, lane, w);                              \
-        stat_out(sy, lds_stat, base + 1, lane, w);                              \
-        stat_out(dz[M], lds_stat, base + 2, lane, w);                           \
+        stat_out(sx * corr, lds_stat, base + 0, lane, w);                       \
+        stat_out(sy * corr, lds_stat, base + 1, lane, w);                       \
+        stat_out(dz[M] * corr, lds_stat, base + 2, lane, w);                    \
     }
     HQML_STAT_BIT(0)
     HQML_STAT_BIT(1)
@@ -289,7 +315,11 @@ __device__ __forceinline__ float2 cmul(float2 a, float2 b)
 }
 
 // Per-thread factor tables of the diagonal D_l in layout L2:
-// D(i) = Plo[j & 3] * Phi[j >> 2] for register j of this thread.
+// D(i) = Plo[j & 3] * Phi[j >> 2] for register j of this thread.  dw[l][q] holds the
+// factor (f0, f1) of qubit q for bit value 0 / 1; CZ signs between register and
+// fixed qubits are folded into the register factors, signs between two register
+// qubits of the same table into its entries (the planner keeps the two tables'
+// qubits non-adjacent).
 struct DiagTables {
     float2 lo[4];
     float2 hi[8];
@@ -298,7 +328,7 @@ struct DiagTables {
 __device__ __forceinline__ DiagTables diag_tables(const float *dw, int n, int layer, const int *rq,
                                                   uint32_t fixed_bits)
 {
-    const float2 *wl = reinterpret_cast<const float2 *>(dw) + (size_t)layer * n;
+    const float4 *wl = reinterpret_cast<const float4 *>(dw) + (size_t)layer * n;
     uint32_t regq = 0;
 #pragma unroll
     for (int m = 0; m < 5; ++m) regq |= 1u << rq[m];
@@ -306,9 +336,8 @@ __device__ __forceinline__ DiagTables diag_tables(const float *dw, int n, int la
     float2 c = make_float2(1.f, 0.f);
     for (int q = 0; q < n; ++q) {
         if (regq & (1u << q)) continue;
-        float2 f = wl[q];
-        if ((fixed_bits >> q) & 1u) f.y = -f.y;
-        c = cmul(c, f);
+        const float4 f = wl[q];
+        c = cmul(c, ((fixed_bits >> q) & 1u) ? make_float2(f.z, f.w) : make_float2(f.x, f.y));
     }
     if (__builtin_popcount(fixed_bits & (fixed_bits >> 1)) & 1) {
         c.x = -c.x;
@@ -318,9 +347,9 @@ __device__ __forceinline__ DiagTables diag_tables(const float *dw, int n, int la
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
         const int q = rq[m];
-        const float2 f = wl[q];
-        g0[m] = f;
-        g1[m] = make_float2(f.x, -f.y);
+        const float4 f = wl[q];
+        g0[m] = make_float2(f.x, f.y);
+        g1[m] = make_float2(f.z, f.w);
         uint32_t nb = (fixed_bits >> (q + 1)) & 1u;
         if (q > 0) nb += (fixed_bits >> (q - 1)) & 1u;
         if (nb & 1u) {
@@ -349,21 +378,32 @@ __device__ __forceinline__ DiagTables diag_tables(const float *dw, int n, int la
     return t;
 }
 
-// Apply D (conj = false) or D^dagger (conj = true) in layout L2.
-__device__ __forceinline__ void apply_diag(Tile &t, const DiagTables &d, bool conj_)
+__device__ __forceinline__ void scale_lo(DiagTables &d, float s)
 {
 #pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        d.lo[a].x *= s;
+        d.lo[a].y *= s;
+    }
+}
+
+// Apply s * D in layout L2 (s folded into the thread's factor table).
+__device__ __forceinline__ void apply_diag(Tile &t, DiagTables d, float s)
+{
+    scale_lo(d, s);
+#pragma unroll
     for (int j = 0; j < kRegs; ++j) {
-        float2 f = cmul(d.lo[j & 3], d.hi[j >> 2]);
-        if (conj_) f.y = -f.y;
+        const float2 f = cmul(d.lo[j & 3], d.hi[j >> 2]);
         const float r = t.re[j], i = t.im[j];
         t.re[j] = r * f.x - i * f.y;
         t.im[j] = r * f.y + i * f.x;
     }
 }
 
-__device__ __forceinline__ void apply_diag2(Tile &a, Tile &b, const DiagTables &d)
+// Apply s * D^dagger to two tiles in layout L2.
+__device__ __forceinline__ void apply_diag2(Tile &a, Tile &b, DiagTables d, float s)
 {
+    scale_lo(d, s);
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
         float2 f = cmul(d.lo[j & 3], d.hi[j >> 2]);
@@ -571,16 +611,43 @@ __global__ __launch_bounds__(kThreads, 2) void k_tile_fwd(TilePassArgs a)
     else
         load_l1<ST>(t, a.psi_in, c, nelem);
 
+    // true state = stored tile * sigma (uniform), see rot_bit
+    float sigma = 1.f;
     const bool need_l2 = (a.rotA >= 0) || (a.diag >= 0) || (a.rotB >= 0);
-    if (a.rotA >= 0) rot_layer(t, load_coef(a.rot_cs, a.n, a.rotA, c.q1, c.gm1, 1.f), c.gm1);
+    if (a.rotA >= 0) {
+        const RotCoef r = load_coef(a.rot_tf, a.n, a.rotA, c.q1, c.gm1);
+        rot_layer<false>(t, r);
+        sigma *= r.F;
+    }
     if (need_l2) {
         transpose(t, lds, c.a1, c.a2, true);
-        if (a.rotA >= 0) rot_layer(t, load_coef(a.rot_cs, a.n, a.rotA, c.q2, c.gm2, 1.f), c.gm2);
-        if (a.diag >= 0) apply_diag(t, diag_tables(a.dw, a.n, a.diag, c.q2, c.fixed2), false);
-        if (a.rotB >= 0) rot_layer(t, load_coef(a.rot_cs, a.n, a.rotB, c.q2, c.gm2, 1.f), c.gm2);
+        if (a.rotA >= 0) {
+            const RotCoef r = load_coef(a.rot_tf, a.n, a.rotA, c.q2, c.gm2);
+            rot_layer<false>(t, r);
+            sigma *= r.F;
+        }
+        RotCoef rb1, rb2;
+        if (a.rotB >= 0) {
+            rb1 = load_coef(a.rot_tf, a.n, a.rotB, c.q1, c.gm1);
+            rb2 = load_coef(a.rot_tf, a.n, a.rotB, c.q2, c.gm2);
+        }
+        if (a.diag >= 0) {
+            // fold the pending scale and the scale of the rotations that follow into D
+            const float fb = a.rotB >= 0 ? rb1.F * rb2.F : 1.f;
+            apply_diag(t, diag_tables(a.dw, a.n, a.diag, c.q2, c.fixed2), sigma * fb);
+            sigma = 1.f / fb;
+        }
+        if (a.rotB >= 0) {
+            rot_layer<false>(t, rb2);
+            sigma *= rb2.F;
+        }
         transpose(t, lds, c.a1, c.a2, false);
-        if (a.rotB >= 0) rot_layer(t, load_coef(a.rot_cs, a.n, a.rotB, c.q1, c.gm1, 1.f), c.gm1);
+        if (a.rotB >= 0) {
+            rot_layer<false>(t, rb1);
+            sigma *= rb1.F;
+        }
     }
+    if (a.diag < 0 && (a.rotA >= 0 || a.rotB >= 0)) scale_tile(t, sigma);
     if (a.flags & PF_EMIT_E) emit_e(z0_partial(t, z0_mask_l1(c)), lds_stat, a.e_part, c, a.T);
     if (a.flags & PF_STORE) store_l1<ST>(t, a.psi_out, c, nelem);
 }
@@ -605,7 +672,8 @@ __device__ __forceinline__ void flush_stats(const float *lds_stat, float *stat_p
 
 // Backward pass shapes (one kernel instance each, to keep register use per shape low).
 enum BwdShape : int {
-    BW_GENERAL = 0,      // [rotA(la) | init, D_la, rotB(la+1)]
+    BW_GENERAL = 0,      // [rotA(la), D_la, rotB(la+1)]
+    BW_INIT_GENERAL = 5, // [init, D_0, rotB(1)]
     BW_ROTA = 1,         // [rotA(la)]
     BW_L0 = 2,           // layer-0 statistics only (one-layer circuit, or stats-only view)
     BW_FUSED_LAST = 3,   // forward [rotA(la)] + E + seed + its backward
@@ -626,31 +694,38 @@ __global__ __launch_bounds__(kThreads, 2) void k_tile_bwd(TilePassArgs a)
     const bool init = (a.flags & PF_INIT) != 0;
     const int la = init ? 0 : a.rotA;   // layer of the A-side statistics
     Tile p, l;
+    // Scales: true psi = stored psi * sp, true lambda = stored lambda * sl (uniform).
+    float sl = 1.f;
 
     if constexpr (SHAPE == BW_FUSED_INIT) {
         init_l1(p, a.init_u, c, a.n);
         const uint32_t zm = z0_mask_l1(c);
         emit_e(z0_partial(p, zm), lds_stat, a.e_part, c, a.T);
         seed_lambda(l, p, zm);
-        stats_visit<false>(p, l, c.gm1, 0, lds_stat, c.lane, c.w);
+        stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, 1.f);
         transpose(p, lds, c.a1, c.a2, true);
         transpose(l, lds, c.a1, c.a2, true);
-        stats_visit<true>(p, l, c.gm2, 0, lds_stat, c.lane, c.w);
+        stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, 1.f);
         transpose(l, lds, c.a1, c.a2, false);
     } else if constexpr (SHAPE == BW_FUSED_LAST) {
         load_l1<ST>(p, a.psi_in, c, nelem);
-        rot_layer(p, load_coef(a.rot_cs, a.n, la, c.q1, c.gm1, 1.f), c.gm1);
+        const RotCoef r1 = load_coef(a.rot_tf, a.n, la, c.q1, c.gm1);
+        const RotCoef r2 = load_coef(a.rot_tf, a.n, la, c.q2, c.gm2);
+        rot_layer<false>(p, r1);
         transpose(p, lds, c.a1, c.a2, true);
-        rot_layer(p, load_coef(a.rot_cs, a.n, la, c.q2, c.gm2, 1.f), c.gm2);
+        rot_layer<false>(p, r2);
+        const float fa = r1.F * r2.F;          // psi (and the seeded lambda) carry scale fa
         const uint32_t zm = z0_mask_l2(c);
-        emit_e(z0_partial(p, zm), lds_stat, a.e_part, c, a.T);
+        emit_e(z0_partial(p, zm) * (fa * fa), lds_stat, a.e_part, c, a.T);
         seed_lambda(l, p, zm);
-        stats_visit<true>(p, l, c.gm2, 0, lds_stat, c.lane, c.w);
-        rot_layer2(p, l, load_coef(a.rot_cs, a.n, la, c.q2, c.gm2, -1.f), c.gm2);
+        stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, fa * fa);
+        rot_layer2<true>(p, l, r2);
         transpose(p, lds, c.a1, c.a2, false);
         transpose(l, lds, c.a1, c.a2, false);
-        stats_visit<false>(p, l, c.gm1, 0, lds_stat, c.lane, c.w);
-        rot_layer(l, load_coef(a.rot_cs, a.n, la, c.q1, c.gm1, -1.f), c.gm1);
+        const float s2 = fa * r2.F;
+        stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, s2 * s2);
+        rot_layer<true>(l, r1);
+        sl = s2 * r1.F;
     } else {
         if (a.flags & PF_STATS_ONLY)
             init_l1(p, a.init_u, c, a.n);
@@ -660,33 +735,50 @@ __global__ __launch_bounds__(kThreads, 2) void k_tile_bwd(TilePassArgs a)
             seed_lambda(l, p, z0_mask_l1(c));
         else
             load_l1<0>(l, a.lam, c, nelem);
-        if constexpr (SHAPE == BW_GENERAL) {
-            stats_visit<false>(p, l, c.gm1, 1, lds_stat, c.lane, c.w);
-            rot_layer2(p, l, load_coef(a.rot_cs, a.n, a.rotB, c.q1, c.gm1, -1.f), c.gm1);
+        if constexpr (SHAPE == BW_GENERAL || SHAPE == BW_INIT_GENERAL) {
+            const RotCoef b1 = load_coef(a.rot_tf, a.n, a.rotB, c.q1, c.gm1);
+            stats_visit<false>(p, l, 1, lds_stat, c.lane, c.w, 1.f);
+            rot_layer2<true>(p, l, b1);
+            const float fb1 = b1.F;
             transpose(p, lds, c.a1, c.a2, true);
             transpose(l, lds, c.a1, c.a2, true);
-            stats_visit<true>(p, l, c.gm2, 1, lds_stat, c.lane, c.w);
-            rot_layer2(p, l, load_coef(a.rot_cs, a.n, a.rotB, c.q2, c.gm2, -1.f), c.gm2);
-            apply_diag2(p, l, diag_tables(a.dw, a.n, a.diag, c.q2, c.fixed2));
-            stats_visit<true>(p, l, c.gm2, 0, lds_stat, c.lane, c.w);
-            if (!init) rot_layer2(p, l, load_coef(a.rot_cs, a.n, la, c.q2, c.gm2, -1.f), c.gm2);
-            transpose(p, lds, c.a1, c.a2, false);
-            transpose(l, lds, c.a1, c.a2, false);
-            stats_visit<false>(p, l, c.gm1, 0, lds_stat, c.lane, c.w);
-            if (!init) rot_layer(l, load_coef(a.rot_cs, a.n, la, c.q1, c.gm1, -1.f), c.gm1);
+            stats_visit<true>(p, l, 1, lds_stat, c.lane, c.w, fb1 * fb1);
+            const RotCoef b2 = load_coef(a.rot_tf, a.n, a.rotB, c.q2, c.gm2);
+            rot_layer2<true>(p, l, b2);
+            // both states carry scale fb = fb1 * b2.F; D^dagger removes it
+            apply_diag2(p, l, diag_tables(a.dw, a.n, a.diag, c.q2, c.fixed2), fb1 * b2.F);
+            stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, 1.f);
+            if constexpr (SHAPE == BW_GENERAL) {
+                const RotCoef a2 = load_coef(a.rot_tf, a.n, la, c.q2, c.gm2);
+                rot_layer2<true>(p, l, a2);
+                const float fa2 = a2.F;
+                transpose(p, lds, c.a1, c.a2, false);
+                transpose(l, lds, c.a1, c.a2, false);
+                stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, fa2 * fa2);
+                const RotCoef a1 = load_coef(a.rot_tf, a.n, la, c.q1, c.gm1);
+                rot_layer<true>(l, a1);
+                sl = fa2 * a1.F;
+            } else {
+                transpose(p, lds, c.a1, c.a2, false);
+                transpose(l, lds, c.a1, c.a2, false);
+                stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, 1.f);
+            }
         } else if constexpr (SHAPE == BW_ROTA) {
-            stats_visit<false>(p, l, c.gm1, 0, lds_stat, c.lane, c.w);
-            rot_layer2(p, l, load_coef(a.rot_cs, a.n, la, c.q1, c.gm1, -1.f), c.gm1);
+            const RotCoef a1 = load_coef(a.rot_tf, a.n, la, c.q1, c.gm1);
+            const RotCoef a2 = load_coef(a.rot_tf, a.n, la, c.q2, c.gm2);
+            stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, 1.f);
+            rot_layer2<true>(p, l, a1);
             transpose(p, lds, c.a1, c.a2, true);
             transpose(l, lds, c.a1, c.a2, true);
-            stats_visit<true>(p, l, c.gm2, 0, lds_stat, c.lane, c.w);
-            rot_layer(l, load_coef(a.rot_cs, a.n, la, c.q2, c.gm2, -1.f), c.gm2);
+            stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, a1.F * a1.F);
+            rot_layer<true>(l, a2);
             transpose(l, lds, c.a1, c.a2, false);
+            sl = a1.F * a2.F;
         } else {   // BW_L0
-            stats_visit<false>(p, l, c.gm1, 0, lds_stat, c.lane, c.w);
+            stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, 1.f);
             transpose(p, lds, c.a1, c.a2, true);
             transpose(l, lds, c.a1, c.a2, true);
-            stats_visit<true>(p, l, c.gm2, 0, lds_stat, c.lane, c.w);
+            stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, 1.f);
             if (a.flags & PF_STATS_ONLY) {
                 flush_stats(lds_stat, a.stat_part, c, a.T);
                 return;
@@ -694,6 +786,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_tile_bwd(TilePassArgs a)
             transpose(l, lds, c.a1, c.a2, false);
         }
     }
+    if (sl != 1.f) scale_tile(l, sl);
     store_l1<0>(l, a.lam, c, nelem);
     flush_stats(lds_stat, a.stat_part, c, a.T);
 }
@@ -703,14 +796,13 @@ template __global__ void k_tile_fwd<1>(TilePassArgs);
 
 // ------------------------------------------------------------------ small circuits (n <= 13)
 
-// D_l applied to amplitude i (conj_ selects D^dagger).
-__device__ __forceinline__ float2 small_diag(const float2 *wl, int n, uint32_t i)
+// D_l of amplitude i: CZ-chain sign times the per-qubit factors f0 / f1.
+__device__ __forceinline__ float2 small_diag(const float4 *wl, int n, uint32_t i)
 {
     float2 f = make_float2(1.f, 0.f);
     for (int q = 0; q < n; ++q) {
-        float2 g = wl[q];
-        if ((i >> q) & 1u) g.y = -g.y;
-        f = cmul(f, g);
+        const float4 g = wl[q];
+        f = cmul(f, ((i >> q) & 1u) ? make_float2(g.z, g.w) : make_float2(g.x, g.y));
     }
     if (__builtin_popcount(i & (i >> 1)) & 1) {
         f.x = -f.x;
@@ -733,8 +825,8 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
     float2 *psi = sm;
     float2 *lam = sm + N;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const float2 *rcs = reinterpret_cast<const float2 *>(a.rot_cs);
-    const float2 *dw = reinterpret_cast<const float2 *>(a.dw);
+    const float2 *rtf = reinterpret_cast<const float2 *>(a.rot_tf);
+    const float4 *dw = reinterpret_cast<const float4 *>(a.dw);
     float2 *save = reinterpret_cast<float2 *>(a.psi_save) + (size_t)b * N;
 
     if (a.mode != 1) {
@@ -749,11 +841,12 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
         }
         __syncthreads();
         for (int l = 0; l + 1 < L; ++l) {
-            const float2 *wl = dw + (size_t)l * n;
+            const float4 *wl = dw + (size_t)l * n;
             for (uint32_t i = tid; i < N; i += kThreads) psi[i] = cmul(psi[i], small_diag(wl, n, i));
             __syncthreads();
             for (int q = 0; q < n; ++q) {
-                const float2 cs = rcs[(size_t)(l + 1) * n + q];
+                const float2 tf = rtf[(size_t)(l + 1) * n + q];
+                const float2 cs = make_float2(tf.y, tf.x * tf.y);   // (cos, sin) of the rotation
                 for (uint32_t k = tid; k < N / 2; k += kThreads) {
                     const uint32_t i = pair_index(k, q), j = i | (1u << q);
                     const float2 x = psi[i], y = psi[j];
@@ -823,7 +916,8 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
         if (l == 0) break;
         // uncompute Ry-layer l and D_{l-1} on psi and lambda
         for (int q = 0; q < n; ++q) {
-            const float2 cs = rcs[(size_t)l * n + q];
+            const float2 tf = rtf[(size_t)l * n + q];
+            const float2 cs = make_float2(tf.y, tf.x * tf.y);
             for (uint32_t k = tid; k < N / 2; k += kThreads) {
                 const uint32_t i = pair_index(k, q), j = i | (1u << q);
                 float2 x = psi[i], y = psi[j];
@@ -836,7 +930,7 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
             }
             __syncthreads();
         }
-        const float2 *wl = dw + (size_t)(l - 1) * n;
+        const float4 *wl = dw + (size_t)(l - 1) * n;
         for (uint32_t i = tid; i < N; i += kThreads) {
             float2 f = small_diag(wl, n, i);
             f.y = -f.y;
@@ -926,27 +1020,72 @@ __global__ void k_prep_zyz(const float *theta, int L, int n, double *zyz)
     o[5] = r.im;
 }
 
-// rot_cs[l][q] = (cos, sin)(beta/2); dw[l][q] = p_{l,q} r_{l+1,q} (l < L-1);
+// Pauli frame.  Where beta_{l,q} > pi/2 (sin > cos, l >= 1) the real rotation is
+// rewritten exactly as Ry(beta) = Ry(beta - pi) X Z, so every rotation the tile
+// kernels apply has |tan(beta'/2)| <= 1.  Each X is moved to the start of the
+// circuit: it flips the sign of every earlier Ry angle of that qubit, swaps the
+// qubit's factors in every earlier diagonal (and turns CZ(q, q +- 1) into CZ times a
+// Z on the neighbour), and swaps the qubit's layer-0 product factors.  Each Z merges
+// into the preceding diagonal.  Global phases are dropped (they cancel in E and in
+// every gradient statistic).  G[l][q] = parity of the X's from layers after l; the
+// simulated state at P_l is X^G times the original one, so the Y and Z statistics
+// of such qubits change sign, which the gradient map H absorbs.
+__global__ void k_prep_frame(const double *zyz, int L, int n, unsigned char *G)
+{
+    const int q = blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= n) return;
+    unsigned char g = 0;
+    for (int l = L - 1; l >= 0; --l) {
+        G[(size_t)l * n + q] = g;
+        const double *z = zyz + ((size_t)l * n + q) * 6;
+        if (l >= 1 && z[1] > z[0]) g ^= 1;
+    }
+}
+
+// rot_tf[l][q] = (k, f): the simulated rotation is Ry(beta') = f [[1, -k], [k, 1]],
+//   f = cos(beta'/2) >= 1/sqrt 2, k = tan(beta'/2) in [-1, 1] (frame sign included);
+// dw[l][q] = (f0, f1): D_l's factor of qubit q for bit value 0 / 1 (l < L-1),
+//   from w = p_{l,q} r_{l+1,q} (f0 = w, f1 = conj w) in the frame described above;
 // H[l][q][a][s]: Pauli coefficients of diag(p)^dag G_a diag(p), G_a the generator of
-// theta[l][q][a] moved to just after U_{l,q}: G_z = Z, G_y = Rz Y Rz^dag,
-// G_x = Rz Ry X Ry^dag Rz^dag.
-__global__ void k_prep_tables(const float *theta, const double *zyz, int L, int n, float *rot_cs, float *dw,
-                              double *H)
+//   theta[l][q][a] moved to just after U_{l,q} (G_z = Z, G_y = Rz Y Rz^dag,
+//   G_x = Rz Ry X Ry^dag Rz^dag), with the Y and Z coefficients negated where G[l][q].
+__global__ void k_prep_tables(const float *theta, const double *zyz, const unsigned char *G, int L, int n,
+                              float *rot_tf, float *dw, double *H)
 {
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= L * n) return;
-    const int l = idx / n;
+    const int l = idx / n, q = idx - l * n;
     const double *z = zyz + (size_t)idx * 6;
-    rot_cs[idx * 2 + 0] = (float)z[0];
-    rot_cs[idx * 2 + 1] = (float)z[1];
+    const bool gq = G[idx] != 0;
+    const bool x_here = l >= 1 && z[1] > z[0];
+    double k = x_here ? -z[0] / z[1] : z[1] / z[0];
+    const double f = x_here ? z[1] : z[0];
+    if (gq) k = -k;
+    rot_tf[idx * 2 + 0] = (float)k;
+    rot_tf[idx * 2 + 1] = (float)f;
+    float *d = dw + (size_t)idx * 4;
     if (l + 1 < L) {
         const double *zn = zyz + (size_t)(idx + n) * 6;
         const cd w = cmk(z[2], z[3]) * cmk(zn[4], zn[5]);
-        dw[idx * 2 + 0] = (float)w.re;
-        dw[idx * 2 + 1] = (float)w.im;
+        cd f0 = w, f1 = cconj(w);
+        if (gq) {
+            const cd t = f0;
+            f0 = f1;
+            f1 = t;
+        }
+        int sflip = (zn[1] > zn[0]) ? 1 : 0;            // Z from the next layer's rewrite
+        if (q > 0) sflip ^= G[idx - 1];                 // CZ(q-1, q) conjugated by X on q-1
+        if (q + 1 < n) sflip ^= G[idx + 1];             // CZ(q, q+1) conjugated by X on q+1
+        if (sflip) f1 = cmk(-f1.re, -f1.im);
+        d[0] = (float)f0.re;
+        d[1] = (float)f0.im;
+        d[2] = (float)f1.re;
+        d[3] = (float)f1.im;
     } else {
-        dw[idx * 2 + 0] = 1.f;
-        dw[idx * 2 + 1] = 0.f;
+        d[0] = 1.f;
+        d[1] = 0.f;
+        d[2] = 1.f;
+        d[3] = 0.f;
     }
     const double ay = theta[idx * 3 + 1], az = theta[idx * 3 + 2];
     const m2 X = m2{{cmk(0, 0), cmk(1, 0), cmk(1, 0), cmk(0, 0)}};
@@ -955,21 +1094,23 @@ __global__ void k_prep_tables(const float *theta, const double *zyz, int L, int 
     const m2 Rz = m_rz(az), RzRy = mmul(m_rz(az), m_ry(ay));
     const cd p = cmk(z[2], z[3]);
     const m2 Lp = m2{{p, cmk(0, 0), cmk(0, 0), cconj(p)}};
-    m2 G[3];
-    G[0] = mmul(RzRy, mmul(X, mdag(RzRy)));
-    G[1] = mmul(Rz, mmul(Y, mdag(Rz)));
-    G[2] = Z;
+    m2 Gen[3];
+    Gen[0] = mmul(RzRy, mmul(X, mdag(RzRy)));
+    Gen[1] = mmul(Rz, mmul(Y, mdag(Rz)));
+    Gen[2] = Z;
     for (int a = 0; a < 3; ++a) {
-        const m2 S = mmul(mdag(Lp), mmul(G[a], Lp));
+        const m2 S = mmul(mdag(Lp), mmul(Gen[a], Lp));
         double *h = H + ((size_t)idx * 3 + a) * 3;
-        h[0] = S.m[1].re;    // X coefficient
-        h[1] = -S.m[1].im;   // Y coefficient
-        h[2] = S.m[0].re;    // Z coefficient
+        h[0] = S.m[1].re;                        // X coefficient
+        h[1] = gq ? S.m[1].im : -S.m[1].im;      // Y coefficient
+        h[2] = gq ? -S.m[0].re : S.m[0].re;      // Z coefficient
     }
 }
 
-// u[b][q] = Ry(beta_{0,q}) diag(r, conj r) (cos x/2, sin x/2): the layer-0 product factor.
-__global__ void k_prep_init(const float *x, const double *zyz, int B, int n, float *init_u)
+// u[b][q] = Ry(beta_{0,q}) diag(r, conj r) (cos x/2, sin x/2): the layer-0 product
+// factor, with its two components swapped where the frame has an X on qubit q.
+__global__ void k_prep_init(const float *x, const double *zyz, const unsigned char *G, int B, int n,
+                            float *init_u)
 {
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= B * n) return;
@@ -981,11 +1122,14 @@ __global__ void k_prep_init(const float *x, const double *zyz, int B, int n, flo
     const cd a0 = cmk(r.re * c, r.im * c);        // r cos
     const cd a1 = cmk(r.re * s, -r.im * s);       // conj(r) sin
     const double cb = z[0], sb = z[1];
+    const cd u0 = cmk(cb * a0.re - sb * a1.re, cb * a0.im - sb * a1.im);
+    const cd u1 = cmk(sb * a0.re + cb * a1.re, sb * a0.im + cb * a1.im);
+    const bool sw = G[q] != 0;
     float *o = init_u + (size_t)idx * 4;
-    o[0] = (float)(cb * a0.re - sb * a1.re);
-    o[1] = (float)(cb * a0.im - sb * a1.im);
-    o[2] = (float)(sb * a0.re + cb * a1.re);
-    o[3] = (float)(sb * a0.im + cb * a1.im);
+    o[0] = (float)(sw ? u1.re : u0.re);
+    o[1] = (float)(sw ? u1.im : u0.im);
+    o[2] = (float)(sw ? u0.re : u1.re);
+    o[3] = (float)(sw ? u0.im : u1.im);
 }
 
 // ------------------------------------------------------------------ reductions (fixed order)
@@ -1058,13 +1202,14 @@ __global__ void k_grad_reduce(const double *S, const double *H, const double *dl
 
 namespace hqml {
 
-hipError_t launch_prep(const float *theta, const float *x, int L, int n, int B, double *zyz, float *rot_cs,
-                       float *dw, double *H, float *init_u, hipStream_t s)
+hipError_t launch_prep(const float *theta, const float *x, int L, int n, int B, double *zyz, unsigned char *G,
+                       float *rot_tf, float *dw, double *H, float *init_u, hipStream_t s)
 {
     const int ln = L * n;
     k_prep_zyz<<<(ln + 127) / 128, 128, 0, s>>>(theta, L, n, zyz);
-    k_prep_tables<<<(ln + 127) / 128, 128, 0, s>>>(theta, zyz, L, n, rot_cs, dw, H);
-    if (B > 0) k_prep_init<<<(B * n + 127) / 128, 128, 0, s>>>(x, zyz, B, n, init_u);
+    k_prep_frame<<<1, 64, 0, s>>>(zyz, L, n, G);
+    k_prep_tables<<<(ln + 127) / 128, 128, 0, s>>>(theta, zyz, G, L, n, rot_tf, dw, H);
+    if (B > 0) k_prep_init<<<(B * n + 127) / 128, 128, 0, s>>>(x, zyz, G, B, n, init_u);
     return hipGetLastError();
 }
 
@@ -1087,7 +1232,10 @@ static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s)
         else
             k_tile_bwd<ST, BW_FUSED_LAST><<<grid, kThreads, 0, s>>>(a);
     } else if (a.rotB >= 0) {
-        k_tile_bwd<ST, BW_GENERAL><<<grid, kThreads, 0, s>>>(a);
+        if (a.flags & PF_INIT)
+            k_tile_bwd<ST, BW_INIT_GENERAL><<<grid, kThreads, 0, s>>>(a);
+        else
+            k_tile_bwd<ST, BW_GENERAL><<<grid, kThreads, 0, s>>>(a);
     } else if (a.rotA >= 0 && !(a.flags & (PF_INIT | PF_STATS_ONLY))) {
         k_tile_bwd<ST, BW_ROTA><<<grid, kThreads, 0, s>>>(a);
     } else {

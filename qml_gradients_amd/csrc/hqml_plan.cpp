@@ -223,9 +223,9 @@ Workspace size_workspace(const Plan &p, int max_batch, int storage)
     const size_t elem = storage == 1 ? 4 : 8;
     w.state_bytes = B * w.state_elems * elem;
     const size_t Ln = (size_t)p.L * p.n;
-    // tables: zyz (6 doubles), rot_cs, dw (2 floats each), H (9 doubles), statmap (int2),
+    // tables: zyz (6 doubles), frame (1 byte), rot_tf (2 floats), dw (4 floats), H (9 doubles), statmap (int2),
     // init_u (4 floats per sample and qubit), views, per-sample E / dL/dE / scratch, loss.
-    w.tables_bytes = Ln * (6 * 8 + 2 * 4 + 2 * 4 + 9 * 8 + 8) + B * p.n * 16 +
+    w.tables_bytes = Ln * (6 * 8 + 1 + 2 * 4 + 4 * 4 + 9 * 8 + 8) + B * p.n * 16 +
                      (size_t)std::max(p.V, 1) * sizeof(ViewDev) + B * (8 * 3 + 4) + 64;
     const size_t S_bytes = B * Ln * 3 * 8;
     if (p.small) {

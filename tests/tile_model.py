@@ -61,13 +61,45 @@ def factorise(theta):
     return cb, sb, p, r, H
 
 
+def pauli_frame(cb, sb, p, r, H):
+    """Rewrite every Ry(beta) with beta > pi/2 (layers >= 1) as Ry(beta - pi) X Z and
+    move the X's to the start of the circuit (see the kernels' frame comment).
+    Returns (c, s) of the simulated rotations, the diagonal factors f0/f1 of D_l,
+    the frame G and the adjusted gradient map."""
+    L, n = cb.shape
+    x = np.zeros((L, n), dtype=bool)
+    x[1:] = sb[1:] > cb[1:]
+    G = np.zeros((L, n), dtype=bool)
+    for l in range(L - 2, -1, -1):
+        G[l] = G[l + 1] ^ x[l + 1]
+    c = np.where(x, sb, cb)
+    s = np.where(x, -cb, sb)
+    s = np.where(G, -s, s)
+    f0 = np.ones((L, n), dtype=complex)
+    f1 = np.ones((L, n), dtype=complex)
+    for l in range(L - 1):
+        w = p[l] * r[l + 1]
+        a, b = w, np.conj(w)
+        f0[l] = np.where(G[l], b, a)
+        f1[l] = np.where(G[l], a, b)
+        flip = x[l + 1].copy()
+        flip[1:] ^= G[l][:-1]
+        flip[:-1] ^= G[l][1:]
+        f1[l] = np.where(flip, -f1[l], f1[l])
+    H2 = H.copy()
+    H2[..., 1] = np.where(G[..., None], -H[..., 1], H[..., 1])
+    H2[..., 2] = np.where(G[..., None], -H[..., 2], H[..., 2])
+    return c, s, f0, f1, G, H2
+
+
 class Model:
     def __init__(self, plan_json: str, x, theta):
         self.plan = json.loads(plan_json)
         self.x = np.asarray(x, dtype=np.float64)
         self.theta = np.asarray(theta, dtype=np.float64)
         self.L, self.n = self.theta.shape[0], self.theta.shape[1]
-        self.cb, self.sb, self.p, self.r, self.H = factorise(self.theta)
+        self.cb, self.sb, self.p, self.r, H0 = factorise(self.theta)
+        self.c, self.s, self.f0, self.f1, self.G, self.H = pauli_frame(self.cb, self.sb, self.p, self.r, H0)
         n = self.n
         self.idx = np.arange(1 << n, dtype=np.int64)
         self.bits = [((self.idx >> q) & 1).astype(bool) for q in range(n)]
@@ -85,13 +117,15 @@ class Model:
             c, s = np.cos(self.x[b, q] / 2), np.sin(self.x[b, q] / 2)
             v = np.array([self.r[0, q] * c, np.conj(self.r[0, q]) * s])
             u = np.array([[self.cb[0, q], -self.sb[0, q]], [self.sb[0, q], self.cb[0, q]]]) @ v
+            if self.G[0, q]:
+                u = u[::-1]
             psi = np.kron(psi, u)
         return psi
 
     def rot(self, psi, l, qubits, inverse=False):
         psi = psi.copy()
         for q in qubits:
-            c, s = self.cb[l, q], self.sb[l, q] * (-1 if inverse else 1)
+            c, s = self.c[l, q], self.s[l, q] * (-1 if inverse else 1)
             v = psi.reshape(-1, 2, 1 << q)
             a, bb = v[:, 0, :].copy(), v[:, 1, :].copy()
             v[:, 0, :] = c * a - s * bb
@@ -99,10 +133,9 @@ class Model:
         return psi
 
     def diag(self, l):
-        w = self.p[l] * self.r[l + 1]
         d = self.cz.astype(complex)
         for q in range(self.n):
-            d = d * np.where(self.bits[q], np.conj(w[q]), w[q])
+            d = d * np.where(self.bits[q], self.f1[l, q], self.f0[l, q])
         return d
 
     def stats(self, psi, lam, q):
