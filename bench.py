@@ -99,6 +99,8 @@ def main():
     ap.add_argument("--workload", default="hea20q100l")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--instrumented-steps", type=int, default=3)
+    ap.add_argument("--overlap", type=int, default=0,
+                    help="batch chunks pipelined over two streams (0 = library default, 1 = off)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -132,6 +134,7 @@ def main():
     Y = torch.from_numpy(y).to(dev)
     B = X.shape[0]
     ctx = hq.Context(w.n_qubits, w.n_layers, B, storage=w.storage, ckpt_block=w.ckpt_block)
+    ctx.set_overlap(args.overlap)
     plan = json.loads(hq.hqml_describe_plan(ctx.cfg))
     expz = torch.empty(B, device=dev)
     loss = torch.empty(1, device=dev)
@@ -197,7 +200,7 @@ def main():
         "data": "synthetic (seeded x~U[0,pi), theta~U[0,2pi), y in {-1,+1})",
         "config": {"workload": args.workload, "n_qubits": w.n_qubits, "n_layers": w.n_layers,
                    "batch": B, "state_storage": w.storage, "ckpt_block": w.ckpt_block,
-                   "parallelism": "single GPU"},
+                   "overlap_chunks": args.overlap, "parallelism": "single GPU"},
         "step_state_bytes": step_bytes,
         "step_hbm_GBps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),

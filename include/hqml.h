@@ -129,6 +129,13 @@ int hqml_set_timing(hqml_ctx *ctx, int enable);
  * since timing was enabled or last reset; reset != 0 clears the counters. */
 int hqml_kernel_times(hqml_ctx *ctx, double *ms, long long *count, int reset);
 
+/* Number of batch chunks a training step on the tile path (n >= 14) pipelines: chunk
+ * k+1's forward sweep runs on a second stream of the context while chunk k's adjoint
+ * sweep runs on the context's stream.  Samples are independent, so results are
+ * bitwise the same for every chunk count.  0 = automatic (2), 1 = no overlap,
+ * at most 8.  Per-launch timing (hqml_set_timing) also disables the overlap. */
+int hqml_set_overlap(hqml_ctx *ctx, int chunks);
+
 /* Plan facts for reporting: fused forward passes per training step, backward
  * passes per training step, tile workgroups per pass, bytes of state per sample. */
 int hqml_plan_info(const hqml_ctx *ctx, int *fwd_passes, int *bwd_passes,

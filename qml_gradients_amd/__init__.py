@@ -69,6 +69,7 @@ def load() -> ctypes.CDLL:
         "hqml_status_str": (ctypes.c_char_p, [i]),
         "hqml_last_error": (ctypes.c_char_p, [P]),
         "hqml_set_timing": (i, [P, i]),
+        "hqml_set_overlap": (i, [P, i]),
         "hqml_kernel_times": (i, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong), i]),
         "hqml_plan_info": (i, [P, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i),
                               ctypes.POINTER(ctypes.c_size_t)]),
@@ -84,7 +85,7 @@ def load() -> ctypes.CDLL:
 
 EXPORTED = ("hqml_workspace_bytes", "hqml_create", "hqml_destroy", "hqml_forward", "hqml_backward",
             "hqml_train_step", "hqml_status_str", "hqml_last_error", "hqml_set_timing",
-            "hqml_kernel_times", "hqml_plan_info", "hqml_describe_plan")
+            "hqml_set_overlap", "hqml_kernel_times", "hqml_plan_info", "hqml_describe_plan")
 
 
 def make_config(n_qubits, n_layers, max_batch, storage="fp32", ckpt_block=0, device=0, stream=None):
@@ -141,6 +142,10 @@ def hqml_train_step(ctx, B, x_ptr, theta_ptr, y_ptr, expz_ptr, loss_ptr, grad_pt
 
 def hqml_set_timing(ctx, enable: bool) -> None:
     _check(ctx, load().hqml_set_timing(ctx, int(bool(enable))))
+
+
+def hqml_set_overlap(ctx, chunks: int) -> None:
+    _check(ctx, load().hqml_set_overlap(ctx, int(chunks)))
 
 
 def hqml_kernel_times(ctx, reset: bool = True):
@@ -231,6 +236,9 @@ class Context:
 
     def set_timing(self, enable=True):
         hqml_set_timing(self.handle, enable)
+
+    def set_overlap(self, chunks):
+        hqml_set_overlap(self.handle, chunks)
 
     def kernel_times(self, reset=True):
         return hqml_kernel_times(self.handle, reset)

@@ -30,8 +30,8 @@ hipError_t configure_small(size_t shm_bytes);
 hipError_t launch_ez_reduce(const float *e_part, int B, int T, const float *y, float *e_out, float *loss,
                             double *dlde, double *e_work, hipStream_t s);
 hipError_t launch_copy_dlde(const float *src, int B, double *dlde, hipStream_t s);
-hipError_t launch_stats_reduce(const float *part, const int2 *map, int B, int L, int n, int T, int pass_lo,
-                               int pass_hi, double *S, hipStream_t s);
+hipError_t launch_stats_reduce(const float *part, const int2 *map, int Bs, int b0, int Bc, int L, int n, int T,
+                               int pass_lo, int pass_hi, double *S, hipStream_t s);
 hipError_t launch_grad_reduce(const double *S, const double *H, const double *dlde, int B, int L, int n,
                               float *grad, hipStream_t s);
 }  // namespace hqml
@@ -43,6 +43,13 @@ struct hqml_ctx {
     Plan plan;
     Workspace ws;
     hipStream_t stream = nullptr;
+    // Second stream (default priority, non-blocking): in a training step the batch is
+    // split into chunks; chunk k+1's forward sweep runs there while chunk k's adjoint
+    // sweep runs on 'stream' (the forward is memory-bound, the adjoint ALU-bound).
+    hipStream_t aux = nullptr;
+    hipEvent_t ev_start = nullptr;
+    hipEvent_t ev_fwd[8] = {};
+    int chunks = 0;              // 0: automatic
     std::vector<void *> allocs;
     // device buffers
     char *saved = nullptr;       // saved states (n_saved buffers of max_batch samples)
@@ -104,22 +111,33 @@ hipEvent_t take_event(hqml_ctx *c)
 }
 
 template <class F>
-int run(hqml_ctx *c, int kind, const char *what, F f)
+int run_on(hqml_ctx *c, hipStream_t st, int kind, const char *what, F f)
 {
     hipEvent_t a = nullptr, b = nullptr;
     if (c->timing) {
         a = take_event(c);
         b = take_event(c);
-        if (a && b) (void)hipEventRecord(a, c->stream);
+        if (a && b) (void)hipEventRecord(a, st);
     }
     hipError_t e = f();
     if (c->timing && a && b) {
-        (void)hipEventRecord(b, c->stream);
+        (void)hipEventRecord(b, st);
         c->recs.push_back({kind, a, b});
     }
     if (e != hipSuccess) return hip_fail(c, e, what);
     return HQML_OK;
 }
+
+template <class F>
+int run(hqml_ctx *c, int kind, const char *what, F f)
+{
+    return run_on(c, c->stream, kind, what, f);
+}
+
+// A chunk of the batch: samples b0 .. b0+bc-1 of a batch of bs samples.
+struct Span {
+    int b0, bc, bs;
+};
 
 // Saved state buffer i (each holds max_batch samples).
 void *saved_buf(hqml_ctx *c, int i)
@@ -155,7 +173,7 @@ TilePassArgs base_args(hqml_ctx *c)
     return a;
 }
 
-int fwd_pass(hqml_ctx *c, int B, int p, int extra_flags)
+int fwd_pass(hqml_ctx *c, hipStream_t st, Span sp, int p, int extra_flags)
 {
     const PassPlan &pp = c->plan.fwd[p];
     TilePassArgs a = base_args(c);
@@ -166,17 +184,19 @@ int fwd_pass(hqml_ctx *c, int B, int p, int extra_flags)
     a.diag = pp.diag;
     a.rotB = pp.rotB;
     a.flags = (pp.init ? PF_INIT : 0) | PF_STORE | extra_flags;
-    return run(c, HQML_K_FWD_PASS, "forward pass launch",
-               [&] { return launch_tile_fwd(a, B, c->cfg.storage, c->stream); });
+    a.sample0 = sp.b0;
+    return run_on(c, st, HQML_K_FWD_PASS, "forward pass launch",
+                  [&] { return launch_tile_fwd(a, sp.bc, c->cfg.storage, st); });
 }
 
 // Backward pass k (forward pass index, or n_fwd + i for the i-th layer-0 stats-only pass).
-int bwd_pass(hqml_ctx *c, int B, int k, int part_lo, float *part_base, int extra_flags)
+int bwd_pass(hqml_ctx *c, hipStream_t st, Span sp, int k, int part_lo, float *part_base, int extra_flags)
 {
     const Plan &pl = c->plan;
     const int P = pl.n_fwd();
     TilePassArgs a = base_args(c);
-    a.stat_part = part_base + (size_t)(k - part_lo) * B * pl.T * kSlots;
+    a.stat_part = part_base + (size_t)(k - part_lo) * sp.bs * pl.T * kSlots;
+    a.sample0 = sp.b0;
     if (k >= P) {
         a.view = c->views + pl.stats_only[k - P];
         a.rotA = a.diag = a.rotB = -1;
@@ -193,8 +213,8 @@ int bwd_pass(hqml_ctx *c, int B, int k, int part_lo, float *part_base, int extra
         else
             a.psi_in = pass_out(c, k);
     }
-    return run(c, HQML_K_BWD_PASS, "backward pass launch",
-               [&] { return launch_tile_bwd(a, B, c->cfg.storage, c->stream); });
+    return run_on(c, st, HQML_K_BWD_PASS, "backward pass launch",
+                  [&] { return launch_tile_bwd(a, sp.bc, c->cfg.storage, st); });
 }
 
 int prep(hqml_ctx *c, int B, const float *x, const float *theta)
@@ -227,65 +247,73 @@ int check_config(const hqml_config *cfg, Plan *plan, std::string *err)
     return HQML_OK;
 }
 
-// Forward sweep of the tile path.  'fuse_last' leaves the last pass to the caller.
-int tile_forward_sweep(hqml_ctx *c, int B, bool fuse_last)
+// Forward sweep of the tile path for one chunk.  'fuse_last' leaves the last pass to
+// the backward sweep.
+int tile_forward_sweep(hqml_ctx *c, hipStream_t st, Span sp, bool fuse_last)
 {
     const Plan &pl = c->plan;
     const int P = pl.n_fwd();
     const int last = fuse_last ? P - 1 : P;
     for (int p = 0; p < last; ++p) {
-        const int rc = fwd_pass(c, B, p, (!fuse_last && p == P - 1) ? PF_EMIT_E : 0);
+        const int rc = fwd_pass(c, st, sp, p, (!fuse_last && p == P - 1) ? PF_EMIT_E : 0);
         if (rc) return rc;
     }
     return HQML_OK;
 }
 
-// Backward sweep of the tile path.  The last forward pass is either fused here
-// (train_step: forward ops, E, seed, adjoint ops in one kernel) or seeded from its
-// saved output.
-int tile_backward_sweep(hqml_ctx *c, int B, bool fused_last)
+// Backward sweep of the tile path for one chunk.  The last forward pass is either
+// fused here (train_step: forward ops, E, seed, adjoint ops in one kernel) or seeded
+// from its saved output.  Ends with the per-sample statistics of the chunk in S.
+int tile_backward_sweep(hqml_ctx *c, hipStream_t st, Span sp, bool fused_last)
 {
     const Plan &pl = c->plan;
     const int P = pl.n_fwd();
     const int nso = (int)pl.stats_only.size();
     int rc;
     const int2 *map = c->statmap;
+    auto reduce = [&](const float *base, int lo, int hi) {
+        return run_on(c, st, HQML_K_OTHER, "statistics reduction", [&] {
+            return launch_stats_reduce(base, map, sp.bs, sp.b0, sp.bc, pl.L, pl.n, pl.T, lo, hi, c->S, st);
+        });
+    };
     if (pl.c == 0) {
         for (int k = P - 1; k >= 0; --k) {
             int fl = 0;
             if (k == P - 1) fl = fused_last ? (PF_FUSED | PF_EMIT_E) : PF_SEED;
-            if ((rc = bwd_pass(c, B, k, 0, c->part, fl))) return rc;
+            if ((rc = bwd_pass(c, st, sp, k, 0, c->part, fl))) return rc;
         }
         for (int i = 0; i < nso; ++i)
-            if ((rc = bwd_pass(c, B, P + i, 0, c->part, 0))) return rc;
-        return run(c, HQML_K_OTHER, "statistics reduction", [&] {
-            return launch_stats_reduce(c->part, map, B, pl.L, pl.n, pl.T, 0, P + nso, c->S, c->stream);
-        });
+            if ((rc = bwd_pass(c, st, sp, P + i, 0, c->part, 0))) return rc;
+        return reduce(c->part, 0, P + nso);
     }
     for (int k = pl.nblocks - 1; k >= 0; --k) {
         const int lo = k * pl.c, hi = std::min(P, lo + pl.c);
         if (k < pl.nblocks - 1) {
             for (int p = lo; p < hi - 1; ++p)
-                if ((rc = fwd_pass(c, B, p, 0))) return rc;
+                if ((rc = fwd_pass(c, st, sp, p, 0))) return rc;
         }
         for (int p = hi - 1; p >= lo; --p) {
             int fl = 0;
             if (p == P - 1) fl = fused_last ? (PF_FUSED | PF_EMIT_E) : PF_SEED;
-            if ((rc = bwd_pass(c, B, p, lo, c->part, fl))) return rc;
+            if ((rc = bwd_pass(c, st, sp, p, lo, c->part, fl))) return rc;
         }
-        rc = run(c, HQML_K_OTHER, "statistics reduction", [&] {
-            return launch_stats_reduce(c->part, map, B, pl.L, pl.n, pl.T, lo, hi, c->S, c->stream);
-        });
-        if (rc) return rc;
+        if ((rc = reduce(c->part, lo, hi))) return rc;
     }
-    float *so_base = c->part + (size_t)pl.c * B * pl.T * kSlots;
+    float *so_base = c->part + (size_t)pl.c * sp.bs * pl.T * kSlots;
     for (int i = 0; i < nso; ++i)
-        if ((rc = bwd_pass(c, B, P + i, P, so_base, 0))) return rc;
-    if (nso > 0)
-        return run(c, HQML_K_OTHER, "statistics reduction", [&] {
-            return launch_stats_reduce(so_base, map, B, pl.L, pl.n, pl.T, P, P + nso, c->S, c->stream);
-        });
+        if ((rc = bwd_pass(c, st, sp, P + i, P, so_base, 0))) return rc;
+    if (nso > 0) return reduce(so_base, P, P + nso);
     return HQML_OK;
+}
+
+// Number of batch chunks for a training step on the tile path.
+int chunk_count(const hqml_ctx *c, int B)
+{
+    if (c->timing || !c->aux) return 1;
+    int C = c->chunks > 0 ? c->chunks : 2;
+    C = std::min(C, std::min(B, 8));
+    while (C > 1 && (long long)(B / C) * c->plan.T < 256) --C;   // keep >= 256 workgroups a chunk
+    return std::max(C, 1);
 }
 
 SmallArgs small_args(hqml_ctx *c, int mode)
@@ -406,6 +434,16 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
         hqml_destroy(c);
         return fail(nullptr, HQML_ERR_HIP, m);
     }
+    if (!plan.small) {
+        e = hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_start, hipEventDisableTiming);
+        for (int k = 0; k < 8 && e == hipSuccess; ++k) e = hipEventCreateWithFlags(&c->ev_fwd[k], hipEventDisableTiming);
+        if (e != hipSuccess) {
+            const std::string m = std::string("stream set-up: ") + hipGetErrorString(e);
+            hqml_destroy(c);
+            return fail(nullptr, HQML_ERR_HIP, m);
+        }
+    }
     *out = c;
     return HQML_OK;
 }
@@ -415,6 +453,13 @@ int hqml_destroy(hqml_ctx *c)
     if (!c) return HQML_OK;
     (void)hipSetDevice(c->cfg.device);
     (void)hipStreamSynchronize(c->stream);
+    if (c->aux) {
+        (void)hipStreamSynchronize(c->aux);
+        (void)hipStreamDestroy(c->aux);
+    }
+    if (c->ev_start) (void)hipEventDestroy(c->ev_start);
+    for (hipEvent_t e : c->ev_fwd)
+        if (e) (void)hipEventDestroy(e);
     for (void *p : c->allocs) (void)hipFree(p);
     for (hipEvent_t e : c->pool) (void)hipEventDestroy(e);
     delete c;
@@ -445,7 +490,7 @@ int hqml_forward(hqml_ctx *c, int B, const float *x, const float *theta, float *
             return launch_ez_reduce(c->e_part, B, 1, nullptr, expz, nullptr, nullptr, c->e_work, c->stream);
         });
     } else {
-        if ((rc = tile_forward_sweep(c, B, false))) return rc;
+        if ((rc = tile_forward_sweep(c, c->stream, Span{0, B, B}, false))) return rc;
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {
             return launch_ez_reduce(c->e_part, B, pl.T, nullptr, expz, nullptr, nullptr, c->e_work, c->stream);
         });
@@ -476,7 +521,7 @@ int hqml_backward(hqml_ctx *c, const float *dL_dE, float *grad)
         const SmallArgs a = small_args(c, 1);
         rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->stream); });
     } else {
-        rc = tile_backward_sweep(c, B, false);
+        rc = tile_backward_sweep(c, c->stream, Span{0, B, B}, false);
     }
     if (rc) return rc;
     return run(c, HQML_K_OTHER, "gradient reduction", [&] {
@@ -507,10 +552,32 @@ int hqml_train_step(hqml_ctx *c, int B, const float *x, const float *theta, cons
         });
         if (rc) return rc;
     } else {
-        if ((rc = tile_forward_sweep(c, B, true))) return rc;
         // The fused last pass emits E; the loss and dL/dE are needed only by the final
-        // gradient reduction, so the E reduction runs after the backward sweep.
-        if ((rc = tile_backward_sweep(c, B, true))) return rc;
+        // gradient reduction, so the E reduction runs after the backward sweeps.
+        const int C = chunk_count(c, B);
+        if (C == 1) {
+            if ((rc = tile_forward_sweep(c, c->stream, Span{0, B, B}, true))) return rc;
+            if ((rc = tile_backward_sweep(c, c->stream, Span{0, B, B}, true))) return rc;
+        } else {
+            hipError_t he = hipEventRecord(c->ev_start, c->stream);
+            if (he == hipSuccess) he = hipStreamWaitEvent(c->aux, c->ev_start, 0);
+            if (he != hipSuccess) return hip_fail(c, he, "stream ordering");
+            std::vector<Span> spans;
+            for (int k = 0; k < C; ++k) {
+                const int b0 = (int)((long long)B * k / C), b1 = (int)((long long)B * (k + 1) / C);
+                spans.push_back(Span{b0, b1 - b0, B});
+            }
+            for (int k = 0; k < C; ++k) {
+                if ((rc = tile_forward_sweep(c, c->aux, spans[k], true))) return rc;
+                he = hipEventRecord(c->ev_fwd[k], c->aux);
+                if (he != hipSuccess) return hip_fail(c, he, "stream ordering");
+            }
+            for (int k = 0; k < C; ++k) {
+                he = hipStreamWaitEvent(c->stream, c->ev_fwd[k], 0);
+                if (he != hipSuccess) return hip_fail(c, he, "stream ordering");
+                if ((rc = tile_backward_sweep(c, c->stream, spans[k], true))) return rc;
+            }
+        }
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {
             return launch_ez_reduce(c->e_part, B, pl.T, y, expz, loss, c->dlde, c->e_work, c->stream);
         });
@@ -543,6 +610,14 @@ int hqml_set_timing(hqml_ctx *c, int enable)
 {
     if (!c) return HQML_ERR_ARG;
     c->timing = enable != 0;
+    return HQML_OK;
+}
+
+int hqml_set_overlap(hqml_ctx *c, int chunks)
+{
+    if (!c) return HQML_ERR_ARG;
+    if (chunks < 0 || chunks > 8) return fail(c, HQML_ERR_ARG, "chunks must be in 0..8");
+    c->chunks = chunks;
     return HQML_OK;
 }
 

@@ -91,7 +91,7 @@ struct TilePassArgs {
     int diag;               // diagonal layer D_l (-1: none)
     int rotB;               // second rotation layer (-1: none)
     int flags;
-    int pad;
+    int sample0;            // first sample of this launch (the grid covers samples sample0 ..)
 };
 
 struct SmallArgs {

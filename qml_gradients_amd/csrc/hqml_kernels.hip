@@ -28,6 +28,29 @@ namespace hqml {
 
 // ------------------------------------------------------------------ helpers
 
+// Read a value that is the same for the whole workgroup (tables, views) through the
+// constant address space: a scalar load, which does not share the vector-memory
+// counter with the state loads and so never waits on a prefetched tile.
+__device__ __forceinline__ float ldu(const float *p)
+{
+    return *(const __attribute__((address_space(4))) float *)(p);
+}
+
+__device__ __forceinline__ int ldu(const int *p)
+{
+    return *(const __attribute__((address_space(4))) int *)(p);
+}
+
+__device__ __forceinline__ float2 ldu2(const float *p)
+{
+    return make_float2(ldu(p), ldu(p + 1));
+}
+
+__device__ __forceinline__ float4 ldu4(const float *p)
+{
+    return make_float4(ldu(p), ldu(p + 1), ldu(p + 2), ldu(p + 3));
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dppf(float v)
 {
@@ -146,6 +169,46 @@ __device__ __forceinline__ void transpose(Tile &t, float2 *lds, uint32_t a1, uin
     }
 }
 
+// The same move through a 32 KB buffer.  Local position 12 is wave bit 1 in both
+// layouts, so waves 0-1 and waves 2-3 hold disjoint halves of the tile in both and
+// never exchange data; the two halves take turns in the buffer.  (swz keeps bit 12.)
+__device__ __forceinline__ void transpose_half(Tile &t, float2 *lds, uint32_t a1, uint32_t a2, bool from_l1,
+                                               int w)
+{
+    constexpr uint32_t kHalf = (1u << (kTileBits - 1)) - 1u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        __syncthreads();
+        if ((w >> 1) == h) {
+            if (from_l1) {
+#pragma unroll
+                for (int j = 0; j < kRegs; ++j) lds[(a1 ^ swz(l1_reg(j))) & kHalf] = make_float2(t.re[j], t.im[j]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < kRegs; ++j) lds[(a2 ^ swz(l2_reg(j))) & kHalf] = make_float2(t.re[j], t.im[j]);
+            }
+        }
+        __syncthreads();
+        if ((w >> 1) == h) {
+            if (from_l1) {
+#pragma unroll
+                for (int j = 0; j < kRegs; ++j) {
+                    const float2 v = lds[(a2 ^ swz(l2_reg(j))) & kHalf];
+                    t.re[j] = v.x;
+                    t.im[j] = v.y;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < kRegs; ++j) {
+                    const float2 v = lds[(a1 ^ swz(l1_reg(j))) & kHalf];
+                    t.re[j] = v.x;
+                    t.im[j] = v.y;
+                }
+            }
+        }
+    }
+}
+
 // Real rotation Ry(beta) on register bit M in scaled form, one FMA per real output:
 //   Ry(beta) = f * [[1, -k], [k, 1]],  k = tan(beta/2) in [-1, 1],  f = cos(beta/2).
 // INV applies Ry^dagger.  The scale f (>= 1/sqrt 2) is not applied here: callers track
@@ -185,8 +248,9 @@ __device__ __forceinline__ RotCoef load_coef(const float *rot_tf, int n, int lay
         rc.k[m] = 0.f;
         if (regmask & (1u << m)) {
             const int q = qpos_to_q[m];
-            rc.k[m] = rot_tf[((size_t)layer * n + q) * 2 + 0];
-            rc.F *= rot_tf[((size_t)layer * n + q) * 2 + 1];
+            const float2 kf = ldu2(rot_tf + ((size_t)layer * n + q) * 2);
+            rc.k[m] = kf.x;
+            rc.F *= kf.y;
         }
     }
     return rc;
@@ -244,11 +308,35 @@ __device__ __forceinline__ void xy_stats(const Tile &p, const Tile &l, float &sx
     sy = yp - yn;
 }
 
-// Reduce one statistic over the workgroup into the LDS stat area (16 row partials per slot).
-__device__ __forceinline__ void stat_out(float v, float *lds_stat, int slot, int lane, int w)
+// Row sums of three independent values, interleaved so that no DPP step waits on
+// the one just before it.
+__device__ __forceinline__ void row_sum16x3(float &a, float &b, float &c)
 {
-    v = row_sum16(v);
-    if ((lane & 15) == 15) lds_stat[slot * 16 + w * 4 + (lane >> 4)] = v;
+    a += dppf<0xB1>(a);
+    b += dppf<0xB1>(b);
+    c += dppf<0xB1>(c);
+    a += dppf<0x4E>(a);
+    b += dppf<0x4E>(b);
+    c += dppf<0x4E>(c);
+    a += dppf<0x141>(a);
+    b += dppf<0x141>(b);
+    c += dppf<0x141>(c);
+    a += dppf<0x140>(a);
+    b += dppf<0x140>(b);
+    c += dppf<0x140>(c);
+}
+
+// Reduce the three statistics of one qubit over the workgroup into the LDS stat
+// area (16 row partials per slot, slots base .. base+2).
+__device__ __forceinline__ void stat_out3(float x, float y, float z, float *lds_stat, int base, int lane, int w)
+{
+    row_sum16x3(x, y, z);
+    if ((lane & 15) == 15) {
+        const int r = w * 4 + (lane >> 4);
+        lds_stat[(base + 0) * 16 + r] = x;
+        lds_stat[(base + 1) * 16 + r] = y;
+        lds_stat[(base + 2) * 16 + r] = z;
+    }
 }
 
 // Local position of register bit m in layout L1 / L2.
@@ -297,9 +385,7 @@ __device__ __forceinline__ void stats_visit(const Tile &p, const Tile &l, int se
     {                                                                           \
         xy_stats<M>(p, l, sx, sy);                                              \
         const int base = (sel * 13 + (L2 ? l2_pos(M) : l1_pos(M))) * 3;         \
-        stat_out(sx * corr, lds_stat, base + 0, lane, w);                       \
-        stat_out(sy * corr, lds_stat, base + 1, lane, w);                       \
-        stat_out(dz[M] * corr, lds_stat, base + 2, lane, w);                    \
+        stat_out3(sx * corr, sy * corr, dz[M] * corr, lds_stat, base, lane, w);  \
     }
     HQML_STAT_BIT(0)
     HQML_STAT_BIT(1)
@@ -336,7 +422,7 @@ __device__ __forceinline__ DiagTables diag_tables(const float *dw, int n, int la
     float2 c = make_float2(1.f, 0.f);
     for (int q = 0; q < n; ++q) {
         if (regq & (1u << q)) continue;
-        const float4 f = wl[q];
+        const float4 f = ldu4(reinterpret_cast<const float *>(wl + q));
         c = cmul(c, ((fixed_bits >> q) & 1u) ? make_float2(f.z, f.w) : make_float2(f.x, f.y));
     }
     if (__builtin_popcount(fixed_bits & (fixed_bits >> 1)) & 1) {
@@ -347,7 +433,7 @@ __device__ __forceinline__ DiagTables diag_tables(const float *dw, int n, int la
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
         const int q = rq[m];
-        const float4 f = wl[q];
+        const float4 f = ldu4(reinterpret_cast<const float *>(wl + q));
         g0[m] = make_float2(f.x, f.y);
         g1[m] = make_float2(f.z, f.w);
         uint32_t nb = (fixed_bits >> (q + 1)) & 1u;
@@ -426,61 +512,69 @@ struct TileCtx {
     uint32_t t1;              // L1: thread's amplitude offset within the tile
     uint32_t a1, a2;          // LDS base addresses (swizzled) of the thread in L1 / L2
     uint32_t fixed1, fixed2;  // qubit bitmask of this thread's fixed bits (incl. tile) in L1 / L2
+    uint32_t fx1t, fx2t;      // the thread (lane and wave) part of fixed1 / fixed2
     uint32_t rs[5];           // L1: amplitude stride of each register bit (uniform)
     int q1[5], q2[5];         // global qubits of the register bits in L1 / L2
     uint32_t gm1, gm2;        // register masks of the rotated group in L1 / L2
 };
 
-__device__ __forceinline__ void tile_ctx(TileCtx &c, const ViewDev &v, int T)
+// Point the context at tile 'blk' (= (sample - sample0) * T + tile index).
+__device__ __forceinline__ void tile_retarget(TileCtx &c, const ViewDev &v, int T, int blk, int sample0)
 {
-    const int tid = threadIdx.x;
-    c.lane = tid & 63;
-    c.w = tid >> 6;
-    c.sample = blockIdx.x / T;
-    c.tile = blockIdx.x - c.sample * T;
+    const int rel = blk / T;
+    c.tile = blk - rel * T;
+    c.sample = sample0 + rel;
     uint64_t toff = 0;
     uint32_t tb = 0;
-    for (int k = 0; k < v.n_tile; ++k) {
+    const int nt = ldu(&v.n_tile);
+    for (int k = 0; k < nt; ++k) {
         if ((c.tile >> k) & 1) {
-            toff |= 1ull << v.tile_q[k];
-            tb |= 1u << v.tile_q[k];
+            const int q = ldu(&v.tile_q[k]);
+            toff |= 1ull << q;
+            tb |= 1u << q;
         }
     }
     c.tile_off = toff;
     c.tile_bits = tb;
+    c.fixed1 = c.fx1t | tb;
+    c.fixed2 = c.fx2t | tb;
+}
+
+__device__ __forceinline__ void tile_ctx(TileCtx &c, const ViewDev &v, int T, int blk, int sample0)
+{
+    const int tid = threadIdx.x;
+    c.lane = tid & 63;
+    c.w = tid >> 6;
     const int lane = c.lane, w = c.w;
     // L1 thread bits: lane 0..3 -> pos 0..3, lane 4,5 -> pos 9,10, wave 0,1 -> pos 11,12
     const int l1p[8] = {0, 1, 2, 3, 9, 10, 11, 12};
     const uint32_t l1v = (uint32_t)(lane & 15) | ((uint32_t)(lane >> 4) << 4) | ((uint32_t)w << 6);
-    uint32_t t1 = 0, f1 = tb;
+    uint32_t t1 = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        if ((l1v >> k) & 1u) {
-            t1 |= 1u << v.perm[l1p[k]];
-            f1 |= 1u << v.perm[l1p[k]];
-        }
-    }
+    for (int k = 0; k < 8; ++k)
+        if ((l1v >> k) & 1u) t1 |= 1u << ldu(&v.perm[l1p[k]]);
     c.t1 = t1;
-    c.fixed1 = f1;
+    c.fx1t = t1;
     // L2 thread bits: lane 0..5 -> pos 2..7, wave 0 -> pos 8, wave 1 -> pos 12
     const int l2p[8] = {2, 3, 4, 5, 6, 7, 8, 12};
     const uint32_t l2v = (uint32_t)lane | ((uint32_t)w << 6);
-    uint32_t f2 = tb;
+    uint32_t f2 = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-        if ((l2v >> k) & 1u) f2 |= 1u << v.perm[l2p[k]];
-    c.fixed2 = f2;
+        if ((l2v >> k) & 1u) f2 |= 1u << ldu(&v.perm[l2p[k]]);
+    c.fx2t = f2;
     c.a1 = swz(l1_thread_local(lane, w));
     c.a2 = swz(l2_thread_local(lane, w));
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
-        c.q1[m] = v.perm[4 + m];
-        c.q2[m] = v.perm[m < 2 ? m : 7 + m];
+        c.q1[m] = ldu(&v.perm[4 + m]);
+        c.q2[m] = ldu(&v.perm[m < 2 ? m : 7 + m]);
         c.rs[m] = 1u << c.q1[m];
     }
-    const uint32_t gm = (uint32_t)v.group_mask;
+    const uint32_t gm = (uint32_t)ldu(&v.group_mask);
     c.gm1 = (gm >> 4) & 31u;
     c.gm2 = (gm & 3u) | (((gm >> 9) & 7u) << 2);
+    tile_retarget(c, v, T, blk, sample0);
 }
 
 // Amplitude offset of register j in layout L1 (sum of the strides of its set bits).
@@ -493,23 +587,35 @@ __device__ __forceinline__ uint32_t roff(const TileCtx &c, int j)
     return o;
 }
 
+// Global-memory access of a tile in layout L1: a workgroup-uniform 64-bit tile
+// origin plus a 32-bit byte offset (thread part + register part), which maps onto
+// the scalar-base + vector-offset addressing form.
 template <int ST>
 __device__ __forceinline__ void load_l1(Tile &t, const void *state, const TileCtx &c, uint64_t nelem)
 {
     using IO = StateIO<ST>;
-    const typename IO::elem *base =
-        reinterpret_cast<const typename IO::elem *>(state) + (uint64_t)c.sample * nelem + c.tile_off;
+    constexpr uint32_t esz = sizeof(typename IO::elem);
+    const char *base = reinterpret_cast<const char *>(state) + ((uint64_t)c.sample * nelem + c.tile_off) * esz;
+    const uint32_t tb = c.t1 * esz;
 #pragma unroll
-    for (int j = 0; j < kRegs; ++j) IO::load((base + roff(c, j)) + c.t1, t.re[j], t.im[j]);
+    for (int j = 0; j < kRegs; ++j) {
+        const uint32_t off = tb + roff(c, j) * esz;      // < 2^32 for n <= 29
+        IO::load(reinterpret_cast<const typename IO::elem *>(base + off), t.re[j], t.im[j]);
+    }
 }
 
 template <int ST>
 __device__ __forceinline__ void store_l1(const Tile &t, void *state, const TileCtx &c, uint64_t nelem)
 {
     using IO = StateIO<ST>;
-    typename IO::elem *base = reinterpret_cast<typename IO::elem *>(state) + (uint64_t)c.sample * nelem + c.tile_off;
+    constexpr uint32_t esz = sizeof(typename IO::elem);
+    char *base = reinterpret_cast<char *>(state) + ((uint64_t)c.sample * nelem + c.tile_off) * esz;
+    const uint32_t tb = c.t1 * esz;
 #pragma unroll
-    for (int j = 0; j < kRegs; ++j) IO::store((base + roff(c, j)) + c.t1, t.re[j], t.im[j]);
+    for (int j = 0; j < kRegs; ++j) {
+        const uint32_t off = tb + roff(c, j) * esz;
+        IO::store(reinterpret_cast<typename IO::elem *>(base + off), t.re[j], t.im[j]);
+    }
 }
 
 // Layer-0 product state in layout L1: psi(i) = prod_q u_q[bit_q(i)].
@@ -522,7 +628,7 @@ __device__ __forceinline__ void init_l1(Tile &t, const float *init_u, const Tile
     float2 cst = make_float2(1.f, 0.f);
     for (int q = 0; q < n; ++q) {
         if (regq & (1u << q)) continue;
-        const float4 f = u[q];
+        const float4 f = ldu4(reinterpret_cast<const float *>(u + q));
         const float2 g = ((c.fixed1 >> q) & 1u) ? make_float2(f.z, f.w) : make_float2(f.x, f.y);
         cst = cmul(cst, g);
     }
@@ -530,7 +636,7 @@ __device__ __forceinline__ void init_l1(Tile &t, const float *init_u, const Tile
     t.im[0] = cst.y;
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
-        const float4 f = u[c.q1[m]];
+        const float4 f = ldu4(reinterpret_cast<const float *>(u + c.q1[m]));
         const float2 g0 = make_float2(f.x, f.y), g1 = make_float2(f.z, f.w);
         const int half = 1 << m;
 #pragma unroll
@@ -595,22 +701,11 @@ __device__ __forceinline__ void seed_lambda(Tile &l, const Tile &p, uint32_t zma
 
 // ------------------------------------------------------------------ forward tile pass
 
+// Forward ops of one pass on a tile held in layout L1; stores the pass output.
 template <int ST>
-__global__ __launch_bounds__(kThreads, 2) void k_tile_fwd(TilePassArgs a)
+__device__ __forceinline__ void fwd_ops(Tile &t, const TilePassArgs &a, const TileCtx &c, float2 *lds,
+                                        float *lds_stat, uint64_t nelem)
 {
-    __shared__ float2 lds[1 << kTileBits];
-    __shared__ float lds_stat[kSlots * 16 + 16];
-    const ViewDev &v = *a.view;
-    TileCtx c;
-    tile_ctx(c, v, a.T);
-    const uint64_t nelem = 1ull << a.n;
-
-    Tile t;
-    if (a.flags & PF_INIT)
-        init_l1(t, a.init_u, c, a.n);
-    else
-        load_l1<ST>(t, a.psi_in, c, nelem);
-
     // true state = stored tile * sigma (uniform), see rot_bit
     float sigma = 1.f;
     const bool need_l2 = (a.rotA >= 0) || (a.diag >= 0) || (a.rotB >= 0);
@@ -620,7 +715,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_tile_fwd(TilePassArgs a)
         sigma *= r.F;
     }
     if (need_l2) {
-        transpose(t, lds, c.a1, c.a2, true);
+        transpose_half(t, lds, c.a1, c.a2, true, c.w);
         if (a.rotA >= 0) {
             const RotCoef r = load_coef(a.rot_tf, a.n, a.rotA, c.q2, c.gm2);
             rot_layer<false>(t, r);
@@ -641,7 +736,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_tile_fwd(TilePassArgs a)
             rot_layer<false>(t, rb2);
             sigma *= rb2.F;
         }
-        transpose(t, lds, c.a1, c.a2, false);
+        transpose_half(t, lds, c.a1, c.a2, false, c.w);
         if (a.rotB >= 0) {
             rot_layer<false>(t, rb1);
             sigma *= rb1.F;
@@ -650,6 +745,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_tile_fwd(TilePassArgs a)
     if (a.diag < 0 && (a.rotA >= 0 || a.rotB >= 0)) scale_tile(t, sigma);
     if (a.flags & PF_EMIT_E) emit_e(z0_partial(t, z0_mask_l1(c)), lds_stat, a.e_part, c, a.T);
     if (a.flags & PF_STORE) store_l1<ST>(t, a.psi_out, c, nelem);
+}
+
+// 37 KB of LDS and 128 VGPRs: four workgroups (16 waves) per compute unit, so one
+// workgroup's loads overlap another's rotations.
+template <int ST>
+__global__ __launch_bounds__(kThreads, 4) void k_tile_fwd(TilePassArgs a)
+{
+    __shared__ float2 lds[1 << (kTileBits - 1)];
+    __shared__ float lds_stat[kSlots * 16 + 16];
+    const ViewDev &v = *a.view;
+    TileCtx c;
+    tile_ctx(c, v, a.T, blockIdx.x, a.sample0);
+    const uint64_t nelem = 1ull << a.n;
+    Tile t;
+    if (a.flags & PF_INIT)
+        init_l1(t, a.init_u, c, a.n);
+    else
+        load_l1<ST>(t, a.psi_in, c, nelem);
+    fwd_ops<ST>(t, a, c, lds, lds_stat, nelem);
 }
 
 // ------------------------------------------------------------------ backward tile pass
@@ -687,7 +801,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_tile_bwd(TilePassArgs a)
     __shared__ float lds_stat[kSlots * 16 + 16];
     const ViewDev &v = *a.view;
     TileCtx c;
-    tile_ctx(c, v, a.T);
+    tile_ctx(c, v, a.T, blockIdx.x, a.sample0);
     zero_stats(lds_stat);
     __syncthreads();
     const uint64_t nelem = 1ull << a.n;
@@ -1162,19 +1276,20 @@ __global__ void k_copy_dlde(const float *src, int B, double *dlde)
     if (b < B) dlde[b] = (double)src[b];
 }
 
-// S[b][l][q][s] = sum over tiles of the slot that holds (l, q, s).  map[l*n+q] = (pass, slot base).
-__global__ void k_stats_reduce(const float *part, const int2 *map, int B, int L, int n, int T, int pass_lo,
-                               int pass_hi, double *S)
+// S[b][l][q][s] = sum over tiles of the slot that holds (l, q, s), for samples
+// b0 .. b0+Bc-1.  map[l*n+q] = (pass, slot base); part is [pass - pass_lo][Bs][T][slots].
+__global__ void k_stats_reduce(const float *part, const int2 *map, int Bs, int b0, int Bc, int L, int n, int T,
+                               int pass_lo, int pass_hi, double *S)
 {
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t total = (size_t)B * L * n * 3;
+    const size_t total = (size_t)Bc * L * n * 3;
     if (idx >= total) return;
     const int s = (int)(idx % 3);
     const size_t lq = (idx / 3) % ((size_t)L * n);
-    const int b = (int)(idx / 3 / ((size_t)L * n));
+    const int b = b0 + (int)(idx / 3 / ((size_t)L * n));
     const int2 m = map[lq];
     if (m.x < pass_lo || m.x >= pass_hi) return;
-    const float *pp = part + (((size_t)(m.x - pass_lo) * B + b) * T) * kSlots + m.y + s;
+    const float *pp = part + (((size_t)(m.x - pass_lo) * Bs + b) * T) * kSlots + m.y + s;
     double acc = 0.0;
     for (int t = 0; t < T; ++t) acc += (double)pp[(size_t)t * kSlots];
     S[((size_t)b * L * n + lq) * 3 + s] = acc;
@@ -1279,11 +1394,12 @@ hipError_t launch_copy_dlde(const float *src, int B, double *dlde, hipStream_t s
     return hipGetLastError();
 }
 
-hipError_t launch_stats_reduce(const float *part, const int2 *map, int B, int L, int n, int T, int pass_lo,
-                               int pass_hi, double *S, hipStream_t s)
+hipError_t launch_stats_reduce(const float *part, const int2 *map, int Bs, int b0, int Bc, int L, int n, int T,
+                               int pass_lo, int pass_hi, double *S, hipStream_t s)
 {
-    const size_t total = (size_t)B * L * n * 3;
-    k_stats_reduce<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(part, map, B, L, n, T, pass_lo, pass_hi, S);
+    const size_t total = (size_t)Bc * L * n * 3;
+    k_stats_reduce<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(part, map, Bs, b0, Bc, L, n, T, pass_lo,
+                                                                     pass_hi, S);
     return hipGetLastError();
 }
 

@@ -161,3 +161,27 @@ def test_forward_without_save_then_backward_is_an_error():
         ctx.backward(torch.ones(B))
     assert e.value.status == hq.HQML_ERR_STATE
     ctx.close()
+
+
+@pytest.mark.parametrize("storage,ckpt", [("fp32", 0), ("fp32", 3), ("bf16", 2)])
+def test_chunked_overlap_is_bitwise_identical(storage, ckpt):
+    """Pipelining the batch in chunks over two streams gives the same bits."""
+    n, L, B = 15, 7, 7
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=91)
+    X, TH, Y = (torch.from_numpy(a) for a in (x, th, y))
+    ctx = _ctx(n, L, B, storage=storage, ckpt_block=ckpt)
+    outs = []
+    for chunks in (1, 2, 3, 4, 7):
+        say(f"[gpu] overlap chunks={chunks} storage={storage} ckpt={ckpt}")
+        ctx.set_overlap(chunks)
+        e, loss, g = ctx.train_step(X, TH, Y)
+        torch.cuda.synchronize()
+        outs.append((e.cpu().numpy(), loss.cpu().numpy(), g.cpu().numpy()))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b)
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
+    if storage == "fp32":
+        assert_e_close(outs[0][0], e_ref, n)
+        assert_grad_close(outs[0][2], g_ref)
+    ctx.close()
