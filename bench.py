@@ -8,12 +8,14 @@ fused forward pass, the fused adjoint passes and all reductions, with inputs
 already resident in device memory.  Prints one JSON line.
 
 Besides the throughput, the line carries:
-  roofline      the dominant kernel (the fused adjoint tile pass): algorithmic
-                bytes per launch / its mean launch time, from HIP events recorded
-                around every launch in a separate instrumented loop, against the
-                8 TB/s HBM peak; "traffic" is the measured HBM bytes per launch from
-                rocprofv3 counters when the kernel source still matches them;
-  roofline_fwd  the same for the fused forward tile pass;
+  roofline      the dominant kernel (the fused adjoint tile pass, bound by plain
+                fp32 ALU work): algorithmic flops per launch / its mean launch time,
+                from HIP events recorded around every launch in a separate
+                instrumented loop (batch chunking off), against the plain fp32 FMA
+                peak; also its HBM rate (algorithmic bytes / time vs 8 TB/s) and
+                "traffic", the measured HBM bytes per launch from rocprofv3 counters
+                when the kernel source still matches them;
+  roofline_fwd  the fused forward tile pass (memory-bound) against 8 TB/s;
   cpu_baseline  the CPU oracle (fp64, gate by gate) timed on this host for a
                 bounded sample of the same workload.
 """
@@ -30,7 +32,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# Plain (non-packed) fp32 FMA rate: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz.
+# Packed-FP32 instructions are excluded from the build, so this is the ALU peak the
+# kernels can reach (the published 157.3 TFLOP/s counts packed FP32).
+ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+FP32_PUBLISHED_TFLOPS = 157.3
 PROFILES = os.path.join(ROOT, "profiles")
+L2_POSITIONS = (0, 1, 9, 10, 11)
 
 
 def kernel_source_hash() -> str:
@@ -63,6 +71,38 @@ def algorithmic_bytes(plan: dict, B: int, storage: str):
         bwd += (s + 8 + 8) * N * B
     bwd += 8 * N * B * len(plan["stats_only"])
     return fwd, bwd
+
+
+def algorithmic_flops_bwd(plan: dict, B: int):
+    """Floating-point operations the fused adjoint kernels perform per train step
+    (FMA = 2, multiply or add = 1), per amplitude and sample of each launch:
+      rotation (scaled tan form) on one state: 4 per qubit;
+      X and Y statistics of one qubit: 8; Z statistics of a register layout: 5;
+      merged diagonal applied to psi and lambda: 18; final lambda scale: 2.
+    g = qubits the pass's view rotates, g2 = those at L2 register positions."""
+    N = 1 << plan["n"]
+    P = len(plan["passes"])
+    total = 0
+    for k, ps in enumerate(plan["passes"]):
+        gm = plan["views"][ps["view"]]["group_mask"]
+        g = bin(gm).count("1")
+        g2 = sum((gm >> p) & 1 for p in L2_POSITIONS)
+        if k == P - 1 and not ps["init"]:
+            # forward rotations, E, seed, statistics, un-rotations, scale
+            f = 4 * g + 3 + 8 * g + 10 + 4 * g2 + 4 * g + 2
+        elif ps["rotB"] >= 0 and ps["init"]:
+            f = 8 * g + 16 * g + 20 + 18
+        elif ps["rotB"] >= 0:
+            f = 8 * g + 4 * (g + g2) + 16 * g + 20 + 18 + 2
+        elif ps["rotA"] >= 0:
+            f = 8 * g + 10 + 4 * g + 4 * g + 2
+        else:
+            f = 8 * g + 10
+        total += f * N * B
+    for v in plan["stats_only"]:
+        g = bin(plan["views"][v]["group_mask"]).count("1")
+        total += (8 * g + 10) * N * B
+    return total
 
 
 def traffic_record(kernel: str, workload: str):
@@ -169,12 +209,18 @@ def main():
     fwd_b, bwd_b = algorithmic_bytes(plan, B, w.storage)
     n_steps = args.instrumented_steps
 
-    def roof(kind, total_bytes_per_step, kernel_name):
+    bwd_flops = algorithmic_flops_bwd(plan, B)
+
+    def launches_and_ms(kind):
         if n_steps == 0 or cnt_k[kind] == 0:
+            return None, None
+        return cnt_k[kind] / n_steps, ms_k[kind] / cnt_k[kind]
+
+    def roof_hbm(kind, total_bytes_per_step, kernel_name):
+        launches, avg_ms = launches_and_ms(kind)
+        if launches is None:
             return None
-        launches = cnt_k[kind] / n_steps
         per_launch_bytes = total_bytes_per_step / launches
-        avg_ms = ms_k[kind] / cnt_k[kind]
         achieved = per_launch_bytes / (avg_ms / 1e3) / 1e9
         return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -182,8 +228,24 @@ def main():
                 "kernel": kernel_name, "avg_launch_ms": round(avg_ms, 4),
                 "launches_per_step": launches, "algorithmic_bytes_per_launch": int(per_launch_bytes)}
 
-    roof_bwd = roof(hq.HQML_K_BWD_PASS, bwd_b, "k_tile_bwd")
-    roof_fwd = roof(hq.HQML_K_FWD_PASS, fwd_b, "k_tile_fwd")
+    def roof_alu(kind, flops_per_step, bytes_per_step, kernel_name):
+        launches, avg_ms = launches_and_ms(kind)
+        if launches is None:
+            return None
+        per_launch = flops_per_step / launches
+        achieved = per_launch / (avg_ms / 1e3) / 1e12
+        hbm = bytes_per_step / launches / (avg_ms / 1e3) / 1e9
+        return {"bound": "alu", "achieved": round(achieved, 2), "peak": round(ALU_PEAK_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / ALU_PEAK_TFLOPS, 4),
+                "traffic": traffic_record(kernel_name, args.workload),
+                "kernel": kernel_name, "avg_launch_ms": round(avg_ms, 4), "launches_per_step": launches,
+                "algorithmic_flops_per_launch": int(per_launch),
+                "algorithmic_bytes_per_launch": int(bytes_per_step / launches),
+                "hbm_achieved_GBps": round(hbm, 1), "hbm_frac": round(hbm / HBM_PEAK_GBPS, 4),
+                "frac_of_published_fp32_peak": round(achieved / FP32_PUBLISHED_TFLOPS, 4)}
+
+    roof_bwd = roof_alu(hq.HQML_K_BWD_PASS, bwd_flops, bwd_b, "k_tile_bwd")
+    roof_fwd = roof_hbm(hq.HQML_K_FWD_PASS, fwd_b, "k_tile_fwd")
     step_bytes = fwd_b + bwd_b
     out = {
         "metric": "train samples/sec (fwd+adjoint bwd) 20q HEA 100L; achieved HBM GB/s vs peak",
