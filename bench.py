@@ -70,6 +70,13 @@ def algorithmic_bytes(plan: dict, B: int, storage: str):
         fwd += ((0 if ps["init"] else s) + s) * N * B
         bwd += (s + 8 + 8) * N * B
     bwd += 8 * N * B * len(plan["stats_only"])
+    # checkpointing: every block but the last is recomputed from its checkpoint
+    # (the block's last output is itself the next checkpoint, kept from the forward)
+    c = plan["c"]
+    if c:
+        for k in range(plan["nblocks"] - 1):
+            for p in range(k * c, min(P, (k + 1) * c) - 1):
+                fwd += ((0 if plan["passes"][p]["init"] else s) + s) * N * B
     return fwd, bwd
 
 
@@ -131,6 +138,53 @@ def cpu_baseline(workload: str, timeout_s: float = 60.0):
                       f"{dt:.1f} s on {threads} OpenMP threads"}
 
 
+def run_epoch(args, w, ctx, dev, memory):
+    """One epoch over the deep model's fixed 1000-sample set: mini-batches of the
+    workload's batch size in order (the last one smaller), each a full train step,
+    with a plain SGD update of theta on the device between steps.  One untimed
+    warm-up step on the first batch precedes the timed epoch."""
+    import torch
+
+    import hqml_inputs
+    import qml_gradients_amd as hq
+    total = 1000
+    nb = (total + w.batch - 1) // w.batch
+    batches = []
+    for i in range(nb):
+        x, th, y = hqml_inputs.workload_inputs(w.name, batch_index=i)
+        batches.append((torch.from_numpy(x).to(dev), torch.from_numpy(y).to(dev)))
+    TH = torch.from_numpy(th).to(dev)
+    expz = torch.empty(w.batch, device=dev)
+    loss = torch.empty(1, device=dev)
+    grad = torch.empty((w.n_layers, w.n_qubits, 3), device=dev)
+
+    def step(X, Y):
+        hq.hqml_train_step(ctx.handle, X.shape[0], X.data_ptr(), TH.data_ptr(), Y.data_ptr(),
+                           expz.data_ptr(), loss.data_ptr(), grad.data_ptr())
+        TH.sub_(args.lr * grad)
+
+    step(*batches[0])
+    torch.cuda.synchronize()
+    TH.copy_(torch.from_numpy(th).to(dev))
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    losses = torch.empty(nb, device=dev)
+    ev0.record(stream)
+    for i, (X, Y) in enumerate(batches):
+        step(X, Y)
+        losses[i] = loss[0]
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    sec = ev0.elapsed_time(ev1) / 1e3
+    return {"metric": "seconds per 1000-sample epoch (train steps + SGD update)", "value": round(sec, 3),
+            "unit": "s/epoch", "higher_is_better": False, "samples_per_s": round(total / sec, 2),
+            "n_gpus": 1, "dtype": "f32", "data": "synthetic 1000-sample set (seeded)",
+            "config": {"workload": w.name, "n_qubits": w.n_qubits, "n_layers": w.n_layers,
+                       "batch": w.batch, "batches": nb, "state_storage": w.storage,
+                       "ckpt_block": w.ckpt_block, "lr": args.lr},
+            "memory": memory, "first_last_loss": [float(losses[0]), float(losses[-1])]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +195,10 @@ def main():
     ap.add_argument("--instrumented-steps", type=int, default=3)
     ap.add_argument("--overlap", type=int, default=0,
                     help="batch chunks pipelined over two streams (0 = library default, 1 = off)")
+    ap.add_argument("--epoch", action="store_true",
+                    help="deep model only: time one epoch over its 1000-sample set, applying "
+                         "theta -= lr * grad between steps (lr = --lr)")
+    ap.add_argument("--lr", type=float, default=0.01)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -173,7 +231,15 @@ def main():
     TH = torch.from_numpy(th).to(dev)
     Y = torch.from_numpy(y).to(dev)
     B = X.shape[0]
+    free0 = torch.cuda.mem_get_info(0)[0]
     ctx = hq.Context(w.n_qubits, w.n_layers, B, storage=w.storage, ckpt_block=w.ckpt_block)
+    torch.cuda.synchronize()
+    memory = {"workspace_bytes": hq.hqml_workspace_bytes(ctx.cfg),
+              "device_mem_delta_bytes": int(free0 - torch.cuda.mem_get_info(0)[0])}
+    if args.epoch:
+        print(json.dumps(run_epoch(args, w, ctx, dev, memory)), flush=True)
+        ctx.close()
+        return
     ctx.set_overlap(args.overlap)
     plan = json.loads(hq.hqml_describe_plan(ctx.cfg))
     expz = torch.empty(B, device=dev)
@@ -263,6 +329,7 @@ def main():
         "config": {"workload": args.workload, "n_qubits": w.n_qubits, "n_layers": w.n_layers,
                    "batch": B, "state_storage": w.storage, "ckpt_block": w.ckpt_block,
                    "overlap_chunks": args.overlap, "parallelism": "single GPU"},
+        "memory": memory,
         "step_state_bytes": step_bytes,
         "step_hbm_GBps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),

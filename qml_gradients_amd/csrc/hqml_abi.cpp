@@ -28,10 +28,10 @@ hipError_t launch_tile_bwd(const TilePassArgs &a, int B, int storage, hipStream_
 hipError_t launch_small(const SmallArgs &a, int B, hipStream_t s);
 hipError_t configure_small(size_t shm_bytes);
 hipError_t launch_ez_reduce(const float *e_part, int B, int T, const float *y, float *e_out, float *loss,
-                            double *dlde, double *e_work, hipStream_t s);
+                            double *dlde, double *e_work, double *chunks, hipStream_t s);
 hipError_t launch_copy_dlde(const float *src, int B, double *dlde, hipStream_t s);
 hipError_t launch_stats_reduce(const float *part, const int2 *map, int Bs, int b0, int Bc, int L, int n, int T,
-                               int pass_lo, int pass_hi, double *S, hipStream_t s);
+                               int pass_lo, int pass_hi, double *S, double *chunks, hipStream_t s);
 hipError_t launch_grad_reduce(const double *S, const double *H, const double *dlde, int B, int L, int n,
                               float *grad, hipStream_t s);
 }  // namespace hqml
@@ -67,6 +67,8 @@ struct hqml_ctx {
     int2 *statmap = nullptr;
     double *dlde = nullptr;
     double *e_work = nullptr;
+    double *part2 = nullptr;    // first-stage statistics sums (samples with many tiles)
+    double *epart2 = nullptr;   // first-stage <Z_0> sums
     float *loss_tmp = nullptr;
     // saved-forward bookkeeping
     int saved_B = -1;
@@ -273,7 +275,7 @@ int tile_backward_sweep(hqml_ctx *c, hipStream_t st, Span sp, bool fused_last)
     const int2 *map = c->statmap;
     auto reduce = [&](const float *base, int lo, int hi) {
         return run_on(c, st, HQML_K_OTHER, "statistics reduction", [&] {
-            return launch_stats_reduce(base, map, sp.bs, sp.b0, sp.bc, pl.L, pl.n, pl.T, lo, hi, c->S, st);
+            return launch_stats_reduce(base, map, sp.bs, sp.b0, sp.bc, pl.L, pl.n, pl.T, lo, hi, c->S, c->part2, st);
         });
     };
     if (pl.c == 0) {
@@ -418,6 +420,8 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     c->statmap = static_cast<int2 *>(grab(Ln * sizeof(int2)));
     c->dlde = static_cast<double *>(grab((size_t)B * 8));
     c->e_work = static_cast<double *>(grab((size_t)B * 8));
+    c->part2 = static_cast<double *>(grab(c->ws.part2_bytes));
+    c->epart2 = static_cast<double *>(grab(c->ws.epart2_bytes));
     c->loss_tmp = static_cast<float *>(grab(64));
     if (!ok) {
         hqml_destroy(c);
@@ -487,12 +491,12 @@ int hqml_forward(hqml_ctx *c, int B, const float *x, const float *theta, float *
         if ((rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->stream); })))
             return rc;
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {
-            return launch_ez_reduce(c->e_part, B, 1, nullptr, expz, nullptr, nullptr, c->e_work, c->stream);
+            return launch_ez_reduce(c->e_part, B, 1, nullptr, expz, nullptr, nullptr, c->e_work, c->epart2, c->stream);
         });
     } else {
         if ((rc = tile_forward_sweep(c, c->stream, Span{0, B, B}, false))) return rc;
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {
-            return launch_ez_reduce(c->e_part, B, pl.T, nullptr, expz, nullptr, nullptr, c->e_work, c->stream);
+            return launch_ez_reduce(c->e_part, B, pl.T, nullptr, expz, nullptr, nullptr, c->e_work, c->epart2, c->stream);
         });
     }
     if (rc) return rc;
@@ -548,7 +552,7 @@ int hqml_train_step(hqml_ctx *c, int B, const float *x, const float *theta, cons
         if ((rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->stream); })))
             return rc;
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {
-            return launch_ez_reduce(c->e_part, B, 1, y, expz, loss, c->dlde, c->e_work, c->stream);
+            return launch_ez_reduce(c->e_part, B, 1, y, expz, loss, c->dlde, c->e_work, c->epart2, c->stream);
         });
         if (rc) return rc;
     } else {
@@ -579,7 +583,7 @@ int hqml_train_step(hqml_ctx *c, int B, const float *x, const float *theta, cons
             }
         }
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {
-            return launch_ez_reduce(c->e_part, B, pl.T, y, expz, loss, c->dlde, c->e_work, c->stream);
+            return launch_ez_reduce(c->e_part, B, pl.T, y, expz, loss, c->dlde, c->e_work, c->epart2, c->stream);
         });
         if (rc) return rc;
     }

@@ -1249,7 +1249,26 @@ __global__ void k_prep_init(const float *x, const double *zyz, const unsigned ch
 // ------------------------------------------------------------------ reductions (fixed order)
 
 // E_b = sum over tiles (fp64); with y: loss = mean (E - y)^2 and dLdE = 2 (E - y) / B.
-__global__ void k_ez_reduce(const float *e_part, int B, int T, const float *y, float *e_out, float *loss,
+// First stage for samples with many tiles: out[b][ch] = sum of the <Z_0> partials of
+// tiles ch*kTileChunk .. (ch+1)*kTileChunk-1 of sample b, by a fixed-order tree.
+// Grid (T / kTileChunk, B), kTileChunk threads.
+__global__ void __launch_bounds__(kTileChunk) k_ez_chunks(const float *e_part, int T, double *out)
+{
+    __shared__ double red[kTileChunk];
+    const int nch = gridDim.x, ch = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
+    red[i] = (double)e_part[(size_t)b * T + (size_t)ch * kTileChunk + i];
+    __syncthreads();
+    for (int h = kTileChunk / 2; h > 0; h >>= 1) {
+        if (i < h) red[i] += red[i + h];
+        __syncthreads();
+    }
+    if (i == 0) out[(size_t)b * nch + ch] = red[0];
+}
+
+// E_b = sum over the T per-tile (or per-chunk) partials of sample b in order; with
+// labels y also the MSE loss and dL/dE_b = 2 (E_b - y_b) / B.
+template <typename P>
+__global__ void k_ez_reduce(const P *e_part, int B, int T, const float *y, float *e_out, float *loss,
                             double *dlde, double *e_work)
 {
     for (int b = threadIdx.x; b < B; b += blockDim.x) {
@@ -1276,10 +1295,33 @@ __global__ void k_copy_dlde(const float *src, int B, double *dlde)
     if (b < B) dlde[b] = (double)src[b];
 }
 
-// S[b][l][q][s] = sum over tiles of the slot that holds (l, q, s), for samples
-// b0 .. b0+Bc-1.  map[l*n+q] = (pass, slot base); part is [pass - pass_lo][Bs][T][slots].
-__global__ void k_stats_reduce(const float *part, const int2 *map, int Bs, int b0, int Bc, int L, int n, int T,
-                               int pass_lo, int pass_hi, double *S)
+// First stage for samples with many tiles: for pass p (relative to the first pass
+// of the range), sample b0+bi and chunk ch, out[p][bi][ch][slot] = sum of the slot
+// over tiles ch*kTileChunk .. (ch+1)*kTileChunk-1.  Thread i owns slot i % kSlots of
+// every fourth tile starting at i / kSlots (consecutive threads read consecutive
+// floats); the four lanes are then added in a fixed order.
+// Grid (T / kTileChunk, Bc, passes), 4 * kSlots threads.
+__global__ void __launch_bounds__(4 * kSlots) k_stats_chunks(const float *part, int Bs, int b0, int T, double *out)
+{
+    __shared__ double red[4 * kSlots];
+    const int nch = gridDim.x, ch = blockIdx.x, bi = blockIdx.y, p = blockIdx.z, Bc = gridDim.y;
+    const int i = threadIdx.x, slot = i % kSlots, lane = i / kSlots;
+    const float *src = part + (((size_t)p * Bs + b0 + bi) * T + (size_t)ch * kTileChunk) * kSlots + slot;
+    double acc = 0.0;
+    for (int t = lane; t < kTileChunk; t += 4) acc += (double)src[(size_t)t * kSlots];
+    red[i] = acc;
+    __syncthreads();
+    if (i < kSlots)
+        out[(((size_t)p * Bc + bi) * nch + ch) * kSlots + i] =
+            ((red[i] + red[kSlots + i]) + red[2 * kSlots + i]) + red[3 * kSlots + i];
+}
+
+// S[b][l][q][s] = sum over tiles (or first-stage chunks) of the slot that holds
+// (l, q, s), for samples b0 .. b0+Bc-1.  map[l*n+q] = (pass, slot base); part is
+// [pass - pass_lo][Bs][T][slots], its sample index being b - bofs.
+template <typename P>
+__global__ void k_stats_reduce(const P *part, const int2 *map, int Bs, int bofs, int b0, int Bc, int L, int n,
+                               int T, int pass_lo, int pass_hi, double *S)
 {
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t total = (size_t)Bc * L * n * 3;
@@ -1289,7 +1331,7 @@ __global__ void k_stats_reduce(const float *part, const int2 *map, int Bs, int b
     const int b = b0 + (int)(idx / 3 / ((size_t)L * n));
     const int2 m = map[lq];
     if (m.x < pass_lo || m.x >= pass_hi) return;
-    const float *pp = part + (((size_t)(m.x - pass_lo) * Bs + b) * T) * kSlots + m.y + s;
+    const P *pp = part + (((size_t)(m.x - pass_lo) * Bs + (b - bofs)) * T) * kSlots + m.y + s;
     double acc = 0.0;
     for (int t = 0; t < T; ++t) acc += (double)pp[(size_t)t * kSlots];
     S[((size_t)b * L * n + lq) * 3 + s] = acc;
@@ -1382,9 +1424,15 @@ hipError_t launch_small(const SmallArgs &a, int B, hipStream_t s)
 }
 
 hipError_t launch_ez_reduce(const float *e_part, int B, int T, const float *y, float *e_out, float *loss,
-                            double *dlde, double *e_work, hipStream_t s)
+                            double *dlde, double *e_work, double *chunks, hipStream_t s)
 {
-    k_ez_reduce<<<1, 256, 0, s>>>(e_part, B, T, y, e_out, loss, dlde, e_work);
+    if (T > kTileChunk) {
+        const int nch = T / kTileChunk;
+        k_ez_chunks<<<dim3((unsigned)nch, (unsigned)B), kTileChunk, 0, s>>>(e_part, T, chunks);
+        k_ez_reduce<double><<<1, 256, 0, s>>>(chunks, B, nch, y, e_out, loss, dlde, e_work);
+    } else {
+        k_ez_reduce<float><<<1, 256, 0, s>>>(e_part, B, T, y, e_out, loss, dlde, e_work);
+    }
     return hipGetLastError();
 }
 
@@ -1395,11 +1443,18 @@ hipError_t launch_copy_dlde(const float *src, int B, double *dlde, hipStream_t s
 }
 
 hipError_t launch_stats_reduce(const float *part, const int2 *map, int Bs, int b0, int Bc, int L, int n, int T,
-                               int pass_lo, int pass_hi, double *S, hipStream_t s)
+                               int pass_lo, int pass_hi, double *S, double *chunks, hipStream_t s)
 {
     const size_t total = (size_t)Bc * L * n * 3;
-    k_stats_reduce<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(part, map, Bs, b0, Bc, L, n, T, pass_lo,
-                                                                     pass_hi, S);
+    const unsigned grid = (unsigned)((total + 255) / 256);
+    if (T > kTileChunk) {
+        const int nch = T / kTileChunk;
+        k_stats_chunks<<<dim3((unsigned)nch, (unsigned)Bc, (unsigned)(pass_hi - pass_lo)), 4 * kSlots, 0, s>>>(
+            part, Bs, b0, T, chunks);
+        k_stats_reduce<double><<<grid, 256, 0, s>>>(chunks, map, Bc, b0, b0, Bc, L, n, nch, pass_lo, pass_hi, S);
+    } else {
+        k_stats_reduce<float><<<grid, 256, 0, s>>>(part, map, Bs, 0, b0, Bc, L, n, T, pass_lo, pass_hi, S);
+    }
     return hipGetLastError();
 }
 

@@ -250,7 +250,13 @@ Workspace size_workspace(const Plan &p, int max_batch, int storage)
     }
     w.part_bytes = (size_t)w.part_passes * B * p.T * kSlots * 4;
     const size_t epart = B * p.T * 4;
-    w.total = (size_t)w.n_saved * w.state_bytes + w.lam_bytes + w.part_bytes + w.tables_bytes + S_bytes + epart;
+    if (p.T > kTileChunk) {
+        w.tile_chunks = p.T / kTileChunk;
+        w.part2_bytes = (size_t)w.part_passes * B * w.tile_chunks * kSlots * 8;
+        w.epart2_bytes = B * (size_t)w.tile_chunks * 8;
+    }
+    w.total = (size_t)w.n_saved * w.state_bytes + w.lam_bytes + w.part_bytes + w.tables_bytes + S_bytes + epart +
+              w.part2_bytes + w.epart2_bytes;
     return w;
 }
 

@@ -55,6 +55,9 @@ struct Workspace {
     int n_ckpt = 0;             // of which checkpoints
     int part_passes = 0;        // passes whose statistics partials are held at once
     size_t part_bytes = 0;
+    int tile_chunks = 0;        // first-stage reduction blocks per sample (0: tiles summed directly)
+    size_t part2_bytes = 0;     // first-stage sums of the statistics partials, fp64
+    size_t epart2_bytes = 0;    // first-stage sums of the <Z_0> partials, fp64
     size_t tables_bytes = 0;
     size_t total = 0;
 };

@@ -58,6 +58,25 @@ def test_tile_path_three_views():
     assert_grad_close(g, g_ref)
 
 
+@pytest.mark.parametrize("ckpt", [0, 1])
+def test_two_stage_reductions(ckpt):
+    """n = 22: 512 tiles per sample, so the per-tile <Z_0> and statistics partials are
+    first summed in 256-tile chunks.  Batch 3 in two pipelined chunks (the second one
+    starting at sample 1) and a forward/backward split."""
+    n, L, B = 22, 3, 3
+    (x, th, y), (e, loss, g) = _run_train(n, L, B, seed=42, ckpt_block=ckpt)
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
+    assert_e_close(e, e_ref, n)
+    assert abs(loss - loss_ref) <= 1e-5 * max(1.0, loss_ref)
+    assert_grad_close(g, g_ref)
+    ctx = _ctx(n, L, B, ckpt_block=ckpt)
+    e2 = ctx.forward(torch.from_numpy(x), torch.from_numpy(th)).cpu().numpy()
+    g2 = ctx.backward(torch.from_numpy((2.0 * (e2 - y) / B).astype(np.float32))).cpu().numpy()
+    ctx.close()
+    assert_e_close(e2, e_ref, n)
+    assert_grad_close(g2, g_ref)
+
+
 @pytest.mark.parametrize("n,L,B", [(4, 2, 8), (12, 3, 4), (14, 3, 3), (16, 2, 2)])
 def test_forward_backward_split(n, L, B):
     x, th, _ = hqml_inputs.make_inputs(n, L, B, seed=33)
