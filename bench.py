@@ -138,6 +138,29 @@ def cpu_baseline(workload: str, timeout_s: float = 60.0):
                       f"{dt:.1f} s on {threads} OpenMP threads"}
 
 
+def gate_by_gate(w, X, TH, Y, steps):
+    """The same train step on the comparator without fusion (one kernel per gate,
+    gate-by-gate adjoint): one untimed step, then `steps` timed ones."""
+    import torch
+
+    import qml_gradients_amd as hq
+    B = X.shape[0]
+    ctx = hq.Context(w.n_qubits, w.n_layers, B, fusion="gate_by_gate")
+    info = ctx.plan_info()
+    ctx.train_step(X, TH, Y)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        ctx.train_step(X, TH, Y)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    ctx.close()
+    return {"value": round(B / (ms / 1e3), 3), "unit": "samples/s", "ms_per_step": round(ms, 2), "steps": steps,
+            "gate_kernels_per_step": info["fwd_passes"] + info["bwd_passes"]}
+
+
 def run_epoch(args, w, ctx, dev, memory):
     """One epoch over the deep model's fixed 1000-sample set: mini-batches of the
     workload's batch size in order (the last one smaller), each a full train step,
@@ -199,6 +222,8 @@ def main():
                     help="deep model only: time one epoch over its 1000-sample set, applying "
                          "theta -= lr * grad between steps (lr = --lr)")
     ap.add_argument("--lr", type=float, default=0.01)
+    ap.add_argument("--gbg-steps", type=int, default=2,
+                    help="timed steps of the gate-by-gate comparator on the same workload (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -341,6 +366,10 @@ def main():
                                enumerate(["fwd_pass", "bwd_pass", "small", "other"])},
     }
     ctx.close()
+    if args.gbg_steps > 0 and w.storage == "fp32" and w.ckpt_block == 0:
+        g = gate_by_gate(w, X, TH, Y, args.gbg_steps)
+        g["fused_speedup"] = round(value / g["value"], 2)
+        out["gate_by_gate"] = g
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(out), flush=True)

@@ -57,6 +57,14 @@ typedef enum {
                                    arithmetic stays fp32 (the pages' mem-save mode, section 2.3) */
 } hqml_storage;
 
+typedef enum {
+    HQML_FUSED = 0,             /* fused forward and adjoint passes (the method itself) */
+    HQML_GATE_BY_GATE = 1       /* comparator without fusion: one kernel per gate in the forward
+                                   pass and per gate in the adjoint pass, which un-computes psi
+                                   gate by gate (sections 2.1-2.2 compare the two); fp32 states
+                                   only, no checkpointing */
+} hqml_fusion;
+
 typedef struct {
     int n_qubits;      /* 1..29 */
     int n_layers;      /* >= 1 */
@@ -68,6 +76,7 @@ typedef struct {
                           (gradient checkpointing, section 2.3) */
     int device;        /* HIP device ordinal */
     void *stream;      /* hipStream_t to queue work on; NULL = the null stream */
+    int fusion;        /* hqml_fusion; 0 = HQML_FUSED */
 } hqml_config;
 
 /* Device bytes hqml_create would reserve for cfg.  Host-only: makes no HIP call.
@@ -91,7 +100,9 @@ int hqml_forward(hqml_ctx *ctx, int B, const float *x, const float *theta, float
 /* Adjoint backward pass for the batch of the last hqml_forward(..., 1) on this
  * context: grad[l][q][a] = sum_b dL_dE[b] * dE_b/dtheta[l][q][a] (fp64 reduction,
  * stored as fp32).  HQML_ERR_STATE if no forward was saved; theta and x are the
- * ones that forward saw. */
+ * ones that forward saw.  Fused contexts keep the saved forward, so several
+ * backward calls may follow one forward; a HQML_GATE_BY_GATE context un-computes
+ * its one saved state in place, so each backward needs a new saved forward. */
 int hqml_backward(hqml_ctx *ctx, const float *dL_dE, float *grad);
 
 /* One training step with the mean-squared-error loss on <Z_0> (the pages' training
@@ -117,7 +128,8 @@ typedef enum {
     HQML_K_BWD_PASS = 1,    /* fused adjoint tile pass (one per fused block) */
     HQML_K_SMALL = 2,       /* whole-circuit kernel for n <= 13 */
     HQML_K_OTHER = 3,       /* table preparation and reductions */
-    HQML_K_COUNT = 4
+    HQML_K_GATE = 4,        /* one gate of a HQML_GATE_BY_GATE context (forward or adjoint) */
+    HQML_K_COUNT = 5
 } hqml_kernel_kind;
 
 /* Enable (1) or disable (0) per-launch HIP event timing on ctx's stream.  While
@@ -137,7 +149,9 @@ int hqml_kernel_times(hqml_ctx *ctx, double *ms, long long *count, int reset);
 int hqml_set_overlap(hqml_ctx *ctx, int chunks);
 
 /* Plan facts for reporting: fused forward passes per training step, backward
- * passes per training step, tile workgroups per pass, bytes of state per sample. */
+ * passes per training step, tile workgroups per pass, bytes of state per sample.
+ * For a HQML_GATE_BY_GATE context: forward gate kernels, adjoint gate kernels and
+ * workgroups per sample of one gate kernel. */
 int hqml_plan_info(const hqml_ctx *ctx, int *fwd_passes, int *bwd_passes,
                    int *tiles_per_sample, size_t *state_bytes);
 

@@ -23,7 +23,9 @@ HQML_ERR_STATE = -4
 HQML_ERR_UNSUPPORTED = -5
 HQML_STORE_FP32 = 0
 HQML_STORE_BF16 = 1
-HQML_K_FWD_PASS, HQML_K_BWD_PASS, HQML_K_SMALL, HQML_K_OTHER, HQML_K_COUNT = range(5)
+HQML_FUSED = 0
+HQML_GATE_BY_GATE = 1
+HQML_K_FWD_PASS, HQML_K_BWD_PASS, HQML_K_SMALL, HQML_K_OTHER, HQML_K_GATE, HQML_K_COUNT = range(6)
 
 
 class hqml_config(ctypes.Structure):
@@ -35,6 +37,7 @@ class hqml_config(ctypes.Structure):
         ("ckpt_block", ctypes.c_int),
         ("device", ctypes.c_int),
         ("stream", ctypes.c_void_p),
+        ("fusion", ctypes.c_int),
     ]
 
 
@@ -88,10 +91,12 @@ EXPORTED = ("hqml_workspace_bytes", "hqml_create", "hqml_destroy", "hqml_forward
             "hqml_set_overlap", "hqml_kernel_times", "hqml_plan_info", "hqml_describe_plan")
 
 
-def make_config(n_qubits, n_layers, max_batch, storage="fp32", ckpt_block=0, device=0, stream=None):
+def make_config(n_qubits, n_layers, max_batch, storage="fp32", ckpt_block=0, device=0, stream=None,
+                fusion="fused"):
     st = {"fp32": HQML_STORE_FP32, "bf16": HQML_STORE_BF16}.get(storage, storage)
+    fu = {"fused": HQML_FUSED, "gate_by_gate": HQML_GATE_BY_GATE}.get(fusion, fusion)
     return hqml_config(int(n_qubits), int(n_layers), int(max_batch), int(st), int(ckpt_block),
-                       int(device), ctypes.c_void_p(stream or 0))
+                       int(device), ctypes.c_void_p(stream or 0), int(fu))
 
 
 # ---- the C entry points, same names, argument marshalling only ----
@@ -173,7 +178,7 @@ class Context:
     """
 
     def __init__(self, n_qubits, n_layers, max_batch, storage="fp32", ckpt_block=0, device=None,
-                 stream=None):
+                 stream=None, fusion="fused"):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("hqml needs a GPU (torch.cuda.is_available() is False)")
@@ -183,7 +188,7 @@ class Context:
         self.torch = torch
         self.device = torch.device("cuda", dev)
         self.n, self.L, self.max_batch = int(n_qubits), int(n_layers), int(max_batch)
-        self.cfg = make_config(n_qubits, n_layers, max_batch, storage, ckpt_block, dev, stream)
+        self.cfg = make_config(n_qubits, n_layers, max_batch, storage, ckpt_block, dev, stream, fusion)
         self.handle = hqml_create(self.cfg)
 
     def close(self):

@@ -34,6 +34,18 @@ hipError_t launch_stats_reduce(const float *part, const int2 *map, int Bs, int b
                                int pass_lo, int pass_hi, double *S, double *chunks, hipStream_t s);
 hipError_t launch_grad_reduce(const double *S, const double *H, const double *dlde, int B, int L, int n,
                               float *grad, hipStream_t s);
+// gate-by-gate comparator (hqml_gbg.hip)
+hipError_t launch_gbg_zero(float2 *psi, int n, int B, hipStream_t s);
+hipError_t launch_gbg_rot(int gate, float2 *psi, int n, int B, int q, const float *ang, int ang_stride,
+                          hipStream_t s);
+hipError_t launch_gbg_cz(float2 *psi, float2 *lam, int n, int B, int q, hipStream_t s);
+hipError_t launch_gbg_expz(const float2 *psi, int n, int B, float *e_part, hipStream_t s);
+hipError_t launch_gbg_seed(const float2 *psi, float2 *lam, int n, int B, hipStream_t s);
+hipError_t launch_gbg_rot_adj(int gate, float2 *psi, float2 *lam, int n, int B, int q, const float *ang,
+                              double *gpart, hipStream_t s);
+hipError_t launch_gbg_grad(const double *gpart, const double *dlde, int B, int n, int n_params, float *grad,
+                           hipStream_t s);
+hipError_t launch_gbg_copy(const float *src, int count, float *dst, hipStream_t s);
 }  // namespace hqml
 
 using namespace hqml;
@@ -70,6 +82,13 @@ struct hqml_ctx {
     double *part2 = nullptr;    // first-stage statistics sums (samples with many tiles)
     double *epart2 = nullptr;   // first-stage <Z_0> sums
     float *loss_tmp = nullptr;
+    // gate-by-gate comparator
+    bool gbg = false;
+    float *gbg_psi = nullptr;    // [B][2^n] complex fp32
+    float *gbg_lam = nullptr;
+    double *gbg_part = nullptr;  // [3nL][B][blocks] gradient block sums
+    float *gbg_theta = nullptr;  // theta of the saved forward
+    int gbg_blocks = 0;
     // saved-forward bookkeeping
     int saved_B = -1;
     std::string err;
@@ -241,6 +260,18 @@ int check_config(const hqml_config *cfg, Plan *plan, std::string *err)
         *err = "storage must be HQML_STORE_FP32 or HQML_STORE_BF16";
         return HQML_ERR_ARG;
     }
+    if (cfg->fusion != HQML_FUSED && cfg->fusion != HQML_GATE_BY_GATE) {
+        *err = "fusion must be HQML_FUSED or HQML_GATE_BY_GATE";
+        return HQML_ERR_ARG;
+    }
+    if (cfg->fusion == HQML_GATE_BY_GATE && cfg->max_batch > 65535) {
+        *err = "the gate-by-gate comparator takes at most 65535 samples";
+        return HQML_ERR_ARG;
+    }
+    if (cfg->fusion == HQML_GATE_BY_GATE && (cfg->storage != HQML_STORE_FP32 || cfg->ckpt_block != 0)) {
+        *err = "the gate-by-gate comparator supports fp32 storage without checkpointing only";
+        return HQML_ERR_UNSUPPORTED;
+    }
     if (!make_plan(cfg->n_qubits, cfg->n_layers, cfg->ckpt_block, plan, err)) return HQML_ERR_ARG;
     if (!plan->small && (size_t)cfg->max_batch * plan->T > 0x7FFFFFFFull) {
         *err = "max_batch * tiles per sample exceeds the grid limit";
@@ -334,6 +365,78 @@ SmallArgs small_args(hqml_ctx *c, int mode)
     return a;
 }
 
+// ---- gate-by-gate comparator ----
+
+Workspace workspace_for(const hqml_config *cfg, const Plan &plan)
+{
+    if (cfg->fusion == HQML_GATE_BY_GATE) return size_workspace_gbg(plan.n, plan.L, cfg->max_batch);
+    return size_workspace(plan, cfg->max_batch, cfg->storage);
+}
+
+int gbg_forward_sweep(hqml_ctx *c, int B, const float *x, const float *theta)
+{
+    const int n = c->plan.n, L = c->plan.L;
+    float2 *psi = reinterpret_cast<float2 *>(c->gbg_psi);
+    int rc = run(c, HQML_K_OTHER, "theta copy",
+                 [&] { return launch_gbg_copy(theta, L * n * 3, c->gbg_theta, c->stream); });
+    if (rc) return rc;
+    if ((rc = run(c, HQML_K_GATE, "state initialisation", [&] { return launch_gbg_zero(psi, n, B, c->stream); })))
+        return rc;
+    for (int q = 0; q < n; ++q)   // encoding Ry(x[b][q])
+        if ((rc = run(c, HQML_K_GATE, "encoding gate",
+                      [&] { return launch_gbg_rot(1, psi, n, B, q, x + q, n, c->stream); })))
+            return rc;
+    for (int l = 0; l < L; ++l) {
+        for (int q = 0; q < n; ++q)
+            for (int g = 0; g < 3; ++g)
+                if ((rc = run(c, HQML_K_GATE, "rotation gate", [&] {
+                         return launch_gbg_rot(g, psi, n, B, q, c->gbg_theta + ((size_t)l * n + q) * 3 + g, 0,
+                                               c->stream);
+                     })))
+                    return rc;
+        for (int q = 0; q + 1 < n; ++q)
+            if ((rc = run(c, HQML_K_GATE, "CZ gate", [&] { return launch_gbg_cz(psi, nullptr, n, B, q, c->stream); })))
+                return rc;
+    }
+    return run(c, HQML_K_GATE, "<Z_0> partials",
+               [&] { return launch_gbg_expz(psi, n, B, c->e_part, c->stream); });
+}
+
+// Adjoint sweep from the final state left in gbg_psi; leaves the gradient block sums
+// in gbg_part and psi un-computed back to the encoded state.
+int gbg_backward_sweep(hqml_ctx *c, int B)
+{
+    const int n = c->plan.n, L = c->plan.L;
+    float2 *psi = reinterpret_cast<float2 *>(c->gbg_psi);
+    float2 *lam = reinterpret_cast<float2 *>(c->gbg_lam);
+    const size_t per_gate = (size_t)B * c->gbg_blocks;
+    int rc = run(c, HQML_K_GATE, "adjoint seed", [&] { return launch_gbg_seed(psi, lam, n, B, c->stream); });
+    if (rc) return rc;
+    for (int l = L - 1; l >= 0; --l) {
+        for (int q = n - 2; q >= 0; --q)
+            if ((rc = run(c, HQML_K_GATE, "CZ adjoint", [&] { return launch_gbg_cz(psi, lam, n, B, q, c->stream); })))
+                return rc;
+        for (int q = n - 1; q >= 0; --q)
+            for (int g = 2; g >= 0; --g) {
+                const size_t p = ((size_t)l * n + q) * 3 + g;
+                if ((rc = run(c, HQML_K_GATE, "rotation adjoint", [&] {
+                         return launch_gbg_rot_adj(g, psi, lam, n, B, q, c->gbg_theta + p, c->gbg_part + p * per_gate,
+                                                   c->stream);
+                     })))
+                    return rc;
+            }
+    }
+    return HQML_OK;
+}
+
+int gbg_grad(hqml_ctx *c, int B, float *grad)
+{
+    const Plan &pl = c->plan;
+    return run(c, HQML_K_OTHER, "gradient reduction", [&] {
+        return launch_gbg_grad(c->gbg_part, c->dlde, B, pl.n, pl.L * pl.n * 3, grad, c->stream);
+    });
+}
+
 }  // namespace
 
 extern "C" {
@@ -343,7 +446,7 @@ size_t hqml_workspace_bytes(const hqml_config *cfg)
     Plan plan;
     std::string err;
     if (check_config(cfg, &plan, &err) != HQML_OK) return 0;
-    return size_workspace(plan, cfg->max_batch, cfg->storage).total;
+    return workspace_for(cfg, plan).total;
 }
 
 long long hqml_describe_plan(const hqml_config *cfg, char *buf, size_t len)
@@ -352,7 +455,15 @@ long long hqml_describe_plan(const hqml_config *cfg, char *buf, size_t len)
     std::string err;
     const int rc = check_config(cfg, &plan, &err);
     if (rc != HQML_OK) return rc;
-    const std::string s = describe_plan(plan);
+    std::string s;
+    if (cfg->fusion == HQML_GATE_BY_GATE) {
+        char tmp[128];
+        std::snprintf(tmp, sizeof tmp, "{\"n\": %d, \"L\": %d, \"gate_by_gate\": true, \"blocks\": %d}", plan.n,
+                      plan.L, gbg_blocks_per_sample(plan.n));
+        s = tmp;
+    } else {
+        s = describe_plan(plan);
+    }
     if (buf && len > 0) {
         const size_t k = std::min(len - 1, s.size());
         std::memcpy(buf, s.data(), k);
@@ -373,7 +484,8 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     if (!c) return fail(nullptr, HQML_ERR_OOM, "host allocation failed");
     c->cfg = *cfg;
     c->plan = plan;
-    c->ws = size_workspace(plan, cfg->max_batch, cfg->storage);
+    c->gbg = cfg->fusion == HQML_GATE_BY_GATE;
+    c->ws = workspace_for(cfg, plan);
     c->stream = reinterpret_cast<hipStream_t>(cfg->stream);
     hipError_t e = hipSetDevice(cfg->device);
     if (e != hipSuccess) {
@@ -405,6 +517,25 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
         c->allocs.push_back(p);
         return p;
     };
+    if (c->gbg) {
+        const int nblk = gbg_blocks_per_sample(plan.n);
+        c->gbg_blocks = nblk;
+        c->gbg_psi = static_cast<float *>(grab(c->ws.state_bytes));
+        c->gbg_lam = static_cast<float *>(grab(c->ws.lam_bytes));
+        c->gbg_part = static_cast<double *>(grab(c->ws.part_bytes));
+        c->gbg_theta = static_cast<float *>(grab(Ln * 3 * 4));
+        c->e_part = static_cast<float *>(grab((size_t)B * nblk * 4));
+        c->dlde = static_cast<double *>(grab((size_t)B * 8));
+        c->e_work = static_cast<double *>(grab((size_t)B * 8));
+        c->epart2 = static_cast<double *>(grab(c->ws.epart2_bytes));
+        c->loss_tmp = static_cast<float *>(grab(64));
+        if (!ok) {
+            hqml_destroy(c);
+            return fail(nullptr, HQML_ERR_OOM, "hipMalloc failed while reserving the workspace");
+        }
+        *out = c;
+        return HQML_OK;
+    }
     c->saved = static_cast<char *>(grab((size_t)c->ws.n_saved * c->ws.state_bytes));
     c->lam = static_cast<float *>(grab(c->ws.lam_bytes));
     c->part = static_cast<float *>(grab(c->ws.part_bytes));
@@ -483,7 +614,18 @@ int hqml_forward(hqml_ctx *c, int B, const float *x, const float *theta, float *
     if (!x || !theta || !expz) return fail(c, HQML_ERR_ARG, "x, theta and expz must be device pointers");
     hipError_t e = hipSetDevice(c->cfg.device);
     if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
-    int rc = prep(c, B, x, theta);
+    int rc;
+    if (c->gbg) {
+        if ((rc = gbg_forward_sweep(c, B, x, theta))) return rc;
+        rc = run(c, HQML_K_OTHER, "E reduction", [&] {
+            return launch_ez_reduce(c->e_part, B, c->gbg_blocks, nullptr, expz, nullptr, nullptr, c->e_work,
+                                    c->epart2, c->stream);
+        });
+        if (rc) return rc;
+        if (save_for_backward) c->saved_B = B;
+        return HQML_OK;
+    }
+    rc = prep(c, B, x, theta);
     if (rc) return rc;
     const Plan &pl = c->plan;
     if (pl.small) {
@@ -514,13 +656,20 @@ int hqml_backward(hqml_ctx *c, const float *dL_dE, float *grad)
     hipError_t e = hipSetDevice(c->cfg.device);
     if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
     const Plan &pl = c->plan;
-    if (B == 0)   // empty batch: the gradient is zero (the reduction over no samples)
+    if (B == 0) {  // empty batch: the gradient is zero (the reduction over no samples)
+        if (c->gbg) return gbg_grad(c, 0, grad);
         return run(c, HQML_K_OTHER, "gradient reduction", [&] {
             return launch_grad_reduce(c->S, c->H, c->dlde, 0, pl.L, pl.n, grad, c->stream);
         });
+    }
     if (!dL_dE) return fail(c, HQML_ERR_ARG, "dL_dE must be a device pointer");
     int rc = run(c, HQML_K_OTHER, "dL/dE copy", [&] { return launch_copy_dlde(dL_dE, B, c->dlde, c->stream); });
     if (rc) return rc;
+    if (c->gbg) {
+        c->saved_B = -1;   // the adjoint sweep un-computes the saved state in place
+        if ((rc = gbg_backward_sweep(c, B))) return rc;
+        return gbg_grad(c, B, grad);
+    }
     if (pl.small) {
         const SmallArgs a = small_args(c, 1);
         rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->stream); });
@@ -544,7 +693,18 @@ int hqml_train_step(hqml_ctx *c, int B, const float *x, const float *theta, cons
     hipError_t e = hipSetDevice(c->cfg.device);
     if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
     c->saved_B = -1;
-    int rc = prep(c, B, x, theta);
+    int rc;
+    if (c->gbg) {
+        if ((rc = gbg_forward_sweep(c, B, x, theta))) return rc;
+        rc = run(c, HQML_K_OTHER, "E reduction", [&] {
+            return launch_ez_reduce(c->e_part, B, c->gbg_blocks, y, expz, loss, c->dlde, c->e_work, c->epart2,
+                                    c->stream);
+        });
+        if (rc) return rc;
+        if ((rc = gbg_backward_sweep(c, B))) return rc;
+        return gbg_grad(c, B, grad);
+    }
+    rc = prep(c, B, x, theta);
     if (rc) return rc;
     const Plan &pl = c->plan;
     if (pl.small) {
@@ -653,6 +813,14 @@ int hqml_plan_info(const hqml_ctx *c, int *fwd_passes, int *bwd_passes, int *til
 {
     if (!c) return HQML_ERR_ARG;
     const Plan &pl = c->plan;
+    if (c->gbg) {
+        const int gates = pl.L * (4 * pl.n - 1);   // 3n rotations and n-1 CZ per layer
+        if (fwd_passes) *fwd_passes = gates + pl.n;
+        if (bwd_passes) *bwd_passes = gates;
+        if (tiles_per_sample) *tiles_per_sample = c->gbg_blocks;
+        if (state_bytes) *state_bytes = ((size_t)1 << pl.n) * 8;
+        return HQML_OK;
+    }
     if (fwd_passes) *fwd_passes = pl.small ? 1 : pl.n_fwd();
     if (bwd_passes) *bwd_passes = pl.small ? 1 : pl.n_bwd();
     if (tiles_per_sample) *tiles_per_sample = pl.T;

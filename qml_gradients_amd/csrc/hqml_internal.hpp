@@ -51,6 +51,7 @@ constexpr int kTileBits = 13;
 constexpr int kRegBits = 5;
 constexpr int kRegs = 32;
 constexpr int kThreads = 256;
+constexpr int kGbgPairsPerBlock = 4096; // gate-by-gate kernels: amplitude pairs per workgroup
 constexpr int kTileChunk = 256;     // tiles per first-stage reduction block (samples with more tiles)
 constexpr int kSlots = 80;           // per-tile statistics slots: (sel*13 + pos)*3 + pauli
 constexpr int kMaxQubits = 29;

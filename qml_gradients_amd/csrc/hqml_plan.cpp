@@ -260,6 +260,32 @@ Workspace size_workspace(const Plan &p, int max_batch, int storage)
     return w;
 }
 
+int gbg_blocks_per_sample(int n)
+{
+    const size_t half = (size_t)1 << (n - 1);
+    return (int)((half + kGbgPairsPerBlock - 1) / kGbgPairsPerBlock);
+}
+
+Workspace size_workspace_gbg(int n, int L, int max_batch)
+{
+    Workspace w;
+    const size_t B = (size_t)max_batch;
+    const size_t nblk = (size_t)gbg_blocks_per_sample(n);
+    const size_t n_params = (size_t)L * n * 3;
+    w.state_elems = (size_t)1 << n;
+    w.state_bytes = B * w.state_elems * 8;
+    w.n_saved = 1;
+    w.lam_bytes = w.state_bytes;
+    w.part_passes = 0;
+    w.part_bytes = n_params * B * nblk * 8;
+    w.tile_chunks = nblk > (size_t)kTileChunk ? (int)(nblk / kTileChunk) : 0;
+    w.epart2_bytes = B * (size_t)w.tile_chunks * 8;
+    // theta copy, dL/dE, E scratch, loss, per-block <Z_0> partials
+    w.tables_bytes = n_params * 4 + B * 16 + 64 + B * nblk * 4;
+    w.total = w.state_bytes + w.lam_bytes + w.part_bytes + w.epart2_bytes + w.tables_bytes;
+    return w;
+}
+
 std::string describe_plan(const Plan &p)
 {
     std::string s = "{";

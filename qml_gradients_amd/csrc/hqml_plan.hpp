@@ -64,6 +64,12 @@ struct Workspace {
 
 Workspace size_workspace(const Plan &p, int max_batch, int storage);
 
+// Gate-by-gate comparator: workgroups per sample of one gate kernel, and its
+// workspace (psi and lambda as fp32 states, per-gate fp64 block sums of the
+// gradient terms in part_bytes, per-block <Z_0> partials, a copy of theta).
+int gbg_blocks_per_sample(int n);
+Workspace size_workspace_gbg(int n, int L, int max_batch);
+
 // Human-readable JSON description of a plan (for tests and reports).
 std::string describe_plan(const Plan &p);
 

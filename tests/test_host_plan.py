@@ -50,6 +50,26 @@ def test_workspace_and_validation_host_only():
     assert hq.load().hqml_status_str(hq.HQML_ERR_STATE) == b"call out of order"
 
 
+def test_gate_by_gate_config_host_only():
+    _lib()
+    cfg = hq.make_config(20, 100, 32, fusion="gate_by_gate")
+    d = json.loads(hq.hqml_describe_plan(cfg))
+    assert d == {"n": 20, "L": 100, "gate_by_gate": True, "blocks": (1 << 19) // 4096}
+    # psi + lambda, fp64 block sums per parameter, sample and block, and small tables
+    N, B, P, nblk = 1 << 20, 32, 6000, 128
+    ws = hq.hqml_workspace_bytes(cfg)
+    assert 2 * B * N * 8 + P * B * nblk * 8 <= ws < 2 * B * N * 8 + P * B * nblk * 8 + (1 << 20)
+    assert json.loads(hq.hqml_describe_plan(hq.make_config(3, 2, 1, fusion="gate_by_gate")))["blocks"] == 1
+    for bad in (hq.make_config(4, 1, 1, storage="bf16", fusion="gate_by_gate"),
+                hq.make_config(4, 1, 1, ckpt_block=2, fusion="gate_by_gate")):
+        assert hq.hqml_workspace_bytes(bad) == 0
+        with pytest.raises(hq.HqmlError) as e:
+            hq.hqml_create(bad)
+        assert e.value.status == hq.HQML_ERR_UNSUPPORTED
+    for bad in (hq.make_config(4, 1, 1, fusion=2), hq.make_config(4, 1, 70000, fusion="gate_by_gate")):
+        assert hq.hqml_workspace_bytes(bad) == 0
+
+
 def test_workspace_scaling_checkpoint_and_bf16():
     _lib()
     full = hq.hqml_workspace_bytes(hq.make_config(20, 1000, 60))
