@@ -10,7 +10,8 @@ adjoint state at all.  Used to check the gate-by-gate oracle in
 Conventions are the same readings as the gate-by-gate oracle: qubit q is bit q
 of the amplitude index, so in a Kronecker product the factor for qubit 0 is the
 rightmost one; R_s(t) = exp(-i t s/2); encoding Ry(x_q) on |0...0>; each layer
-applies Rx, Ry, Rz to every qubit, then CZ(q, q+1) for q = 0..n-2; O = Z_0.
+applies Rx, Ry, Rz to every qubit, then CZ(q, q+1) for q = 0..n-2; O = the
+Kronecker product of Z on the qubits of a mask (default: Z_0) and identities.
 """
 from __future__ import annotations
 
@@ -79,15 +80,23 @@ def state(x, theta) -> np.ndarray:
     return U @ psi0
 
 
-def expz(x, theta) -> float:
+def observable(n: int, zmask: int = 1) -> np.ndarray:
+    """Full matrix of prod_{q in zmask} Z_q."""
+    out = np.array([[1.0 + 0j]])
+    for k in range(n - 1, -1, -1):
+        out = np.kron(out, PAULI["Z"] if (zmask >> k) & 1 else np.eye(2))
+    return out
+
+
+def expz(x, theta, zmask: int = 1) -> float:
     x = np.asarray(x, dtype=np.float64).ravel()
     n = x.size
     psi = state(x, theta)
-    O = embed(PAULI["Z"], 0, n)
+    O = observable(n, zmask)
     return float(np.real(np.vdot(psi, O @ psi)))
 
 
-def grad_expz(x, theta) -> np.ndarray:
+def grad_expz(x, theta, zmask: int = 1) -> np.ndarray:
     """dE/dtheta [L][n][3] by the product rule on the dense circuit unitary."""
     x = np.asarray(x, dtype=np.float64).ravel()
     n = x.size
@@ -95,7 +104,7 @@ def grad_expz(x, theta) -> np.ndarray:
     gates = gate_list(x, theta, n)
     psi0 = np.zeros(1 << n, dtype=np.complex128)
     psi0[0] = 1.0
-    O = embed(PAULI["Z"], 0, n)
+    O = observable(n, zmask)
     # prefix[k] = G_{k-1} ... G_0 psi0 ; suffix[k] = G_{m-1} ... G_{k+1}
     prefix = [psi0]
     for g, _, _ in gates:

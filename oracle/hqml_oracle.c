@@ -24,7 +24,9 @@
  *   - encoding: Ry(x_q)|0> on every qubit, once;
  *   - layer l: on every qubit q apply Rx(theta[l][q][0]), then Ry(theta[l][q][1]),
  *     then Rz(theta[l][q][2]); then CZ(q, q+1) for q = 0..n-2 (open chain);
- *   - observable O = Z on qubit 0; loss = mean over the batch of (E_b - y_b)^2;
+ *   - observable O = product of Z over the qubits in a bit mask S (bit q =
+ *     qubit q; the default is S = {0}, i.e. Z on qubit 0), a diagonal case of
+ *     the general O of section 1.2; loss = mean over the batch of (E_b - y_b)^2;
  *   - the factor 2 of d<psi|O|psi> is carried by the adjoint seed:
  *     lambda_M = 2 (dL/dE) O psi_M, so the section-1.2 gradient formula holds
  *     literally.
@@ -143,8 +145,14 @@ static double re_braket_1q(const cplx *lam, const cplx *phi, int n, int q, gate2
     return acc;
 }
 
-/* <Z_0> = sum_i (1 - 2 bit_0(i)) |psi_i|^2. */
-static double expect_z0(const cplx *psi, int n, int par)
+/* Eigenvalue of O = prod_{q in S} Z_q on basis state i: (-1)^(number of qubits of S set in i). */
+static double zs_sign(int64_t i, uint32_t zmask)
+{
+    return (__builtin_popcountll((uint64_t)i & zmask) & 1) ? -1.0 : 1.0;
+}
+
+/* <O> = sum_i sign_S(i) |psi_i|^2. */
+static double expect_zs(const cplx *psi, int n, uint32_t zmask, int par)
 {
     const int64_t dim = (int64_t)1 << n;
     double acc = 0.0;
@@ -152,7 +160,7 @@ static double expect_z0(const cplx *psi, int n, int par)
 #pragma omp parallel for if (par) schedule(static) reduction(+ : acc)
     for (int64_t i = 0; i < dim; ++i) {
         const double p = creal(psi[i]) * creal(psi[i]) + cimag(psi[i]) * cimag(psi[i]);
-        acc += (i & 1) ? -p : p;
+        acc += zs_sign(i, zmask) * p;
     }
     return acc;
 }
@@ -175,12 +183,12 @@ static void run_circuit(cplx *psi, int n, int L, const double *x, const double *
 /* Adjoint sweep for one sample.  psi holds psi_M on entry (it is uncomputed
  * gate by gate), lam is scratch.  grad[(l*n+q)*3+a] receives dL/dtheta for
  * upstream derivative g = dL/dE. */
-static void adjoint_sample(cplx *psi, cplx *lam, int n, int L, const double *theta, double g,
-                           double *grad, int par)
+static void adjoint_sample(cplx *psi, cplx *lam, int n, int L, const double *theta, uint32_t zmask,
+                           double g, double *grad, int par)
 {
     const int64_t dim = (int64_t)1 << n;
-    /* lambda_M = 2 g O psi_M, O = Z_0. */
-    for (int64_t i = 0; i < dim; ++i) lam[i] = ((i & 1) ? -2.0 * g : 2.0 * g) * psi[i];
+    /* lambda_M = 2 g O psi_M */
+    for (int64_t i = 0; i < dim; ++i) lam[i] = 2.0 * g * zs_sign(i, zmask) * psi[i];
     for (int l = L - 1; l >= 0; --l) {
         /* CZ chain, in reverse order (the CZs commute; order kept for clarity). */
         for (int q = n - 2; q >= 0; --q) { apply_cz(psi, n, q, par); apply_cz(lam, n, q, par); }
@@ -267,10 +275,17 @@ double oracle_max_norm_drift(int n, int L, const double *x, const double *theta)
     return worst;
 }
 
-/* E_b = <psi_M|Z_0|psi_M> for every sample.  x: [B][n], theta: [L][n][3]. */
-int oracle_forward(int n, int L, int B, const double *x, const double *theta, double *expz)
+/* Observable masks must name qubits of the circuit; 0 is rejected. */
+static int bad_mask(int n, uint32_t zmask)
 {
-    if (n < 1 || n > 30 || L < 0 || B < 0 || (B > 0 && (!x || !expz)) || (L > 0 && !theta)) return -1;
+    return zmask == 0 || (n < 32 && (zmask >> n) != 0);
+}
+
+/* E_b = <psi_M|O|psi_M> for every sample.  x: [B][n], theta: [L][n][3]. */
+int oracle_forward(int n, int L, int B, uint32_t zmask, const double *x, const double *theta, double *expz)
+{
+    if (n < 1 || n > 30 || L < 0 || B < 0 || (B > 0 && (!x || !expz)) || (L > 0 && !theta) || bad_mask(n, zmask))
+        return -1;
     const int par = choose_par(n, B);
     const int64_t dim = (int64_t)1 << n;
     int err = 0;
@@ -279,7 +294,7 @@ int oracle_forward(int n, int L, int B, const double *x, const double *theta, do
         cplx *psi = (cplx *)malloc(sizeof(cplx) * (size_t)dim);
         if (!psi) { err |= 1; continue; }
         run_circuit(psi, n, L, x + (size_t)b * n, theta, par);
-        expz[b] = expect_z0(psi, n, par);
+        expz[b] = expect_zs(psi, n, zmask, par);
         free(psi);
     }
     return err ? -1 : 0;
@@ -288,10 +303,11 @@ int oracle_forward(int n, int L, int B, const double *x, const double *theta, do
 /* Adjoint gradient for an arbitrary upstream derivative dLdE[b]:
  * grad[(l*n+q)*3+a] = sum_b (per-sample adjoint gradient), summed in sample
  * order.  expz (optional) receives E_b. */
-int oracle_backward(int n, int L, int B, const double *x, const double *theta, const double *dLdE,
-                    double *grad, double *expz)
+int oracle_backward(int n, int L, int B, uint32_t zmask, const double *x, const double *theta,
+                    const double *dLdE, double *grad, double *expz)
 {
-    if (n < 1 || n > 30 || L < 0 || B < 0 || (B > 0 && (!x || !dLdE)) || (L > 0 && (!theta || !grad)))
+    if (n < 1 || n > 30 || L < 0 || B < 0 || (B > 0 && (!x || !dLdE)) || (L > 0 && (!theta || !grad)) ||
+        bad_mask(n, zmask))
         return -1;
     const size_t P = (size_t)L * n * 3;
     const int par = choose_par(n, B);
@@ -305,8 +321,8 @@ int oracle_backward(int n, int L, int B, const double *x, const double *theta, c
         cplx *lam = (cplx *)malloc(sizeof(cplx) * (size_t)dim);
         if (!psi || !lam) { free(psi); free(lam); err |= 1; continue; }
         run_circuit(psi, n, L, x + (size_t)b * n, theta, par);
-        if (expz) expz[b] = expect_z0(psi, n, par);
-        adjoint_sample(psi, lam, n, L, theta, dLdE[b], per + (size_t)b * P, par);
+        if (expz) expz[b] = expect_zs(psi, n, zmask, par);
+        adjoint_sample(psi, lam, n, L, theta, zmask, dLdE[b], per + (size_t)b * P, par);
         free(psi);
         free(lam);
     }
@@ -319,13 +335,14 @@ int oracle_backward(int n, int L, int B, const double *x, const double *theta, c
     return err ? -1 : 0;
 }
 
-/* One training step with the mean-squared-error loss on <Z_0>:
+/* One training step with the mean-squared-error loss on <O>:
  * loss = (1/B) sum_b (E_b - y_b)^2, dL/dE_b = 2 (E_b - y_b) / B.
  * Each sample is simulated once: forward, E_b, then its adjoint sweep. */
-int oracle_train_step(int n, int L, int B, const double *x, const double *theta, const double *y,
-                      double *expz, double *loss, double *grad)
+int oracle_train_step(int n, int L, int B, uint32_t zmask, const double *x, const double *theta,
+                      const double *y, double *expz, double *loss, double *grad)
 {
-    if (n < 1 || n > 30 || L < 0 || B < 1 || !x || !y || !expz || !loss || (L > 0 && (!theta || !grad)))
+    if (n < 1 || n > 30 || L < 0 || B < 1 || !x || !y || !expz || !loss || (L > 0 && (!theta || !grad)) ||
+        bad_mask(n, zmask))
         return -1;
     const size_t P = (size_t)L * n * 3;
     const int par = choose_par(n, B);
@@ -339,9 +356,9 @@ int oracle_train_step(int n, int L, int B, const double *x, const double *theta,
         cplx *lam = (cplx *)malloc(sizeof(cplx) * (size_t)dim);
         if (!psi || !lam) { free(psi); free(lam); err |= 1; continue; }
         run_circuit(psi, n, L, x + (size_t)b * n, theta, par);
-        expz[b] = expect_z0(psi, n, par);
+        expz[b] = expect_zs(psi, n, zmask, par);
         const double g = 2.0 * (expz[b] - y[b]) / (double)B;
-        adjoint_sample(psi, lam, n, L, theta, g, per + (size_t)b * P, par);
+        adjoint_sample(psi, lam, n, L, theta, zmask, g, per + (size_t)b * P, par);
         free(psi);
         free(lam);
     }

@@ -178,6 +178,46 @@ def pin_train_step_is_mse(o):
     assert np.max(np.abs(g - g_sum)) < 1e-13
 
 
+def pin_zstring_product_state(o):
+    """No layers, O = prod_{q in S} Z_q: the state is a product of Ry(x_q)|0>, so
+    E = prod_{q in S} cos x_q (section 1.2's E(theta) with a Z-string O)."""
+    n = 5
+    x, _ = _rand(n, 0, 3, 800)
+    for mask in (1, 2, 5, 0b01011, 0b11111):
+        e = o.forward(x, np.zeros((0, n, 3)), mask)
+        ref = np.prod([np.cos(x[:, q]) for q in range(n) if (mask >> q) & 1], axis=0)
+        assert np.max(np.abs(e - ref)) < 1e-14, (mask, e, ref)
+
+
+def pin_zstring_dense_and_parameter_shift(o):
+    """Z-string observables: E and the adjoint gradient equal the dense checker's
+    (n <= 4) and the exact parameter-shift derivative (n = 5)."""
+    for n, L, mask in ((2, 2, 3), (3, 2, 0b110), (4, 2, 0b1010)):
+        x, th = _rand(n, L, 2, 900 + n)
+        e = o.forward(x, th, mask)
+        ed = np.array([dense.expz(x[b], th, mask) for b in range(2)])
+        assert np.max(np.abs(e - ed)) < 1e-12, (n, mask)
+        w = np.array([0.4, -1.1])
+        g, _ = o.backward(x, th, w, mask)
+        gd = sum(w[b] * dense.grad_expz(x[b], th, mask) for b in range(2))
+        assert np.max(np.abs(g - gd)) < 1e-12, (n, mask)
+    n, L, mask = 5, 2, 0b10110
+    x, th = _rand(n, L, 2, 950)
+    w = np.array([1.0, 0.3])
+    g, _ = o.backward(x, th, w, mask)
+    ref = np.zeros_like(th)
+    for idx in np.ndindex(th.shape):
+        tp, tm = th.copy(), th.copy()
+        tp[idx] += math.pi / 2
+        tm[idx] -= math.pi / 2
+        ref[idx] = np.sum(w * (o.forward(x, tp, mask) - o.forward(x, tm, mask)) / 2)
+    assert np.max(np.abs(g - ref)) < 1e-12, np.max(np.abs(g - ref))
+    y = np.array([1.0, -1.0])
+    e, loss, gt = o.train_step(x, th, y, mask)
+    gb, _ = o.backward(x, th, 2 * (e - y) / 2, mask)
+    assert np.max(np.abs(gt - gb)) < 1e-13
+
+
 ALL_PINS = [
     pin_ry_closed_form,
     pin_one_layer_closed_form,
@@ -189,4 +229,6 @@ ALL_PINS = [
     pin_last_layer_rz_zero,
     pin_trig_degree_one,
     pin_train_step_is_mse,
+    pin_zstring_product_state,
+    pin_zstring_dense_and_parameter_shift,
 ]

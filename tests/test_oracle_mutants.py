@@ -31,9 +31,13 @@ MUTANTS = [
      "for (int a = 2; a >= 0; --a)\n                apply_1q(psi, n, q, rotation(a,", 0),
     ("encode_rx", "apply_1q(psi, n, q, rotation(AX_Y, x[q]), par);",
      "apply_1q(psi, n, q, rotation(AX_X, x[q]), par);", 0),
-    ("observable_qubit1", "acc += (i & 1) ? -p : p;", "acc += (i & 2) ? -p : p;", 0),
-    ("seed_no_factor2", "lam[i] = ((i & 1) ? -2.0 * g : 2.0 * g) * psi[i];",
-     "lam[i] = ((i & 1) ? -g : g) * psi[i];", 0),
+    ("observable_shifted_qubit", "return (__builtin_popcountll((uint64_t)i & zmask) & 1) ? -1.0 : 1.0;",
+     "return (__builtin_popcountll(((uint64_t)i << 1) & zmask) & 1) ? -1.0 : 1.0;", 0),
+    ("observable_ignores_mask", "acc += zs_sign(i, zmask) * p;", "acc += zs_sign(i, 1u) * p;", 0),
+    ("seed_no_factor2", "lam[i] = 2.0 * g * zs_sign(i, zmask) * psi[i];",
+     "lam[i] = g * zs_sign(i, zmask) * psi[i];", 0),
+    ("seed_ignores_mask", "lam[i] = 2.0 * g * zs_sign(i, zmask) * psi[i];",
+     "lam[i] = 2.0 * g * zs_sign(i, 1u) * psi[i];", 0),
     ("no_uncompute", "apply_1q(psi, n, q, dagger(u), par);", "(void)u;", 0),
     ("lambda_not_propagated", "apply_1q(lam, n, q, dagger(u), par);", "(void)u;", 0),
     ("ry_derivative_sign", "g.m[0] = -0.5 * s; g.m[1] = -0.5 * c; g.m[2] = 0.5 * c;",
