@@ -9,10 +9,11 @@
  *   per sample b, psi_0 = prod_q Ry(x[b][q]) |0...0>; then L layers, each
  *   applying Rx(theta[l][q][0]), Ry(theta[l][q][1]), Rz(theta[l][q][2]) to every
  *   qubit q followed by CZ(q, q+1) for q = 0..n-2; R_s(t) = exp(-i t s/2);
- *   qubit q is bit q of the amplitude index.  E_b = <psi_M|Z_0|psi_M>.
+ *   qubit q is bit q of the amplitude index.  E_b = <psi_M|O|psi_M> with
+ *   O = Z_0 by default, or a product of Z over any set of qubits (obs_mask).
  *   The gradient is the adjoint-method gradient of section 1.2:
  *   dL/dtheta_j = Re<lambda_j| dU_j/dtheta_j |psi_{j-1}>, lambda_{j-1} = U_j^dag lambda_j,
- *   seeded with lambda_M = 2 (dL/dE_b) Z_0 psi_M, summed over the batch.
+ *   seeded with lambda_M = 2 (dL/dE_b) O psi_M, summed over the batch.
  *
  * Conventions for every entry point:
  *   - All array arguments are DEVICE pointers to contiguous row-major fp32
@@ -77,6 +78,9 @@ typedef struct {
     int device;        /* HIP device ordinal */
     void *stream;      /* hipStream_t to queue work on; NULL = the null stream */
     int fusion;        /* hqml_fusion; 0 = HQML_FUSED */
+    int obs_mask;      /* observable O = product of Z_q over the qubits q whose bit is set
+                          (bit q = qubit q, only qubits 0..n_qubits-1); 0 = Z on qubit 0.
+                          A diagonal case of the general O of section 1.2 */
 } hqml_config;
 
 /* Device bytes hqml_create would reserve for cfg.  Host-only: makes no HIP call.
@@ -91,7 +95,7 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out);
 /* Release the context and its workspaces (waits for its stream).  NULL is a no-op. */
 int hqml_destroy(hqml_ctx *ctx);
 
-/* Forward pass for B samples (0 <= B <= max_batch): expz[b] = <Z_0> of sample b.
+/* Forward pass for B samples (0 <= B <= max_batch): expz[b] = <O> of sample b.
  * save_for_backward != 0 keeps what hqml_backward needs (the fused-pass outputs,
  * or checkpoints) until the next forward on this context.  B == 0 queues nothing. */
 int hqml_forward(hqml_ctx *ctx, int B, const float *x, const float *theta, float *expz,
@@ -105,7 +109,7 @@ int hqml_forward(hqml_ctx *ctx, int B, const float *x, const float *theta, float
  * its one saved state in place, so each backward needs a new saved forward. */
 int hqml_backward(hqml_ctx *ctx, const float *dL_dE, float *grad);
 
-/* One training step with the mean-squared-error loss on <Z_0> (the pages' training
+/* One training step with the mean-squared-error loss on <O> (the pages' training
  * objective; mean over the batch): expz = E_b, loss = (1/B) sum_b (E_b - y_b)^2,
  * grad = dloss/dtheta.  1 <= B <= max_batch.  Equivalent to forward + backward with
  * dL_dE[b] = 2 (E_b - y_b) / B, with the last fused pass of the forward sweep and the

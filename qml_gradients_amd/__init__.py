@@ -38,6 +38,7 @@ class hqml_config(ctypes.Structure):
         ("device", ctypes.c_int),
         ("stream", ctypes.c_void_p),
         ("fusion", ctypes.c_int),
+        ("obs_mask", ctypes.c_int),
     ]
 
 
@@ -92,11 +93,11 @@ EXPORTED = ("hqml_workspace_bytes", "hqml_create", "hqml_destroy", "hqml_forward
 
 
 def make_config(n_qubits, n_layers, max_batch, storage="fp32", ckpt_block=0, device=0, stream=None,
-                fusion="fused"):
+                fusion="fused", obs_mask=0):
     st = {"fp32": HQML_STORE_FP32, "bf16": HQML_STORE_BF16}.get(storage, storage)
     fu = {"fused": HQML_FUSED, "gate_by_gate": HQML_GATE_BY_GATE}.get(fusion, fusion)
     return hqml_config(int(n_qubits), int(n_layers), int(max_batch), int(st), int(ckpt_block),
-                       int(device), ctypes.c_void_p(stream or 0), int(fu))
+                       int(device), ctypes.c_void_p(stream or 0), int(fu), int(obs_mask))
 
 
 # ---- the C entry points, same names, argument marshalling only ----
@@ -178,7 +179,7 @@ class Context:
     """
 
     def __init__(self, n_qubits, n_layers, max_batch, storage="fp32", ckpt_block=0, device=None,
-                 stream=None, fusion="fused"):
+                 stream=None, fusion="fused", obs_mask=0):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("hqml needs a GPU (torch.cuda.is_available() is False)")
@@ -188,7 +189,8 @@ class Context:
         self.torch = torch
         self.device = torch.device("cuda", dev)
         self.n, self.L, self.max_batch = int(n_qubits), int(n_layers), int(max_batch)
-        self.cfg = make_config(n_qubits, n_layers, max_batch, storage, ckpt_block, dev, stream, fusion)
+        self.cfg = make_config(n_qubits, n_layers, max_batch, storage, ckpt_block, dev, stream, fusion,
+                               obs_mask)
         self.handle = hqml_create(self.cfg)
 
     def close(self):

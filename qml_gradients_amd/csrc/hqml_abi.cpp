@@ -39,8 +39,8 @@ hipError_t launch_gbg_zero(float2 *psi, int n, int B, hipStream_t s);
 hipError_t launch_gbg_rot(int gate, float2 *psi, int n, int B, int q, const float *ang, int ang_stride,
                           hipStream_t s);
 hipError_t launch_gbg_cz(float2 *psi, float2 *lam, int n, int B, int q, hipStream_t s);
-hipError_t launch_gbg_expz(const float2 *psi, int n, int B, float *e_part, hipStream_t s);
-hipError_t launch_gbg_seed(const float2 *psi, float2 *lam, int n, int B, hipStream_t s);
+hipError_t launch_gbg_expz(const float2 *psi, int n, int B, uint32_t obs, float *e_part, hipStream_t s);
+hipError_t launch_gbg_seed(const float2 *psi, float2 *lam, int n, int B, uint32_t obs, hipStream_t s);
 hipError_t launch_gbg_rot_adj(int gate, float2 *psi, float2 *lam, int n, int B, int q, const float *ang,
                               double *gpart, hipStream_t s);
 hipError_t launch_gbg_grad(const double *gpart, const double *dlde, int B, int n, int n_params, float *grad,
@@ -80,8 +80,9 @@ struct hqml_ctx {
     double *dlde = nullptr;
     double *e_work = nullptr;
     double *part2 = nullptr;    // first-stage statistics sums (samples with many tiles)
-    double *epart2 = nullptr;   // first-stage <Z_0> sums
+    double *epart2 = nullptr;   // first-stage <O> sums
     float *loss_tmp = nullptr;
+    uint32_t obs = 1;            // observable: product of Z over the qubits of this mask
     // gate-by-gate comparator
     bool gbg = false;
     float *gbg_psi = nullptr;    // [B][2^n] complex fp32
@@ -191,6 +192,7 @@ TilePassArgs base_args(hqml_ctx *c)
     a.n = c->plan.n;
     a.L = c->plan.L;
     a.T = c->plan.T;
+    a.obs = c->obs;
     return a;
 }
 
@@ -258,6 +260,10 @@ int check_config(const hqml_config *cfg, Plan *plan, std::string *err)
     }
     if (cfg->storage != HQML_STORE_FP32 && cfg->storage != HQML_STORE_BF16) {
         *err = "storage must be HQML_STORE_FP32 or HQML_STORE_BF16";
+        return HQML_ERR_ARG;
+    }
+    if (cfg->obs_mask < 0 || (cfg->n_qubits >= 1 && cfg->n_qubits < 31 && (cfg->obs_mask >> cfg->n_qubits) != 0)) {
+        *err = "obs_mask may only name qubits 0..n_qubits-1";
         return HQML_ERR_ARG;
     }
     if (cfg->fusion != HQML_FUSED && cfg->fusion != HQML_GATE_BY_GATE) {
@@ -362,6 +368,7 @@ SmallArgs small_args(hqml_ctx *c, int mode)
     a.n = c->plan.n;
     a.L = c->plan.L;
     a.mode = mode;
+    a.obs = c->obs;
     return a;
 }
 
@@ -398,8 +405,8 @@ int gbg_forward_sweep(hqml_ctx *c, int B, const float *x, const float *theta)
             if ((rc = run(c, HQML_K_GATE, "CZ gate", [&] { return launch_gbg_cz(psi, nullptr, n, B, q, c->stream); })))
                 return rc;
     }
-    return run(c, HQML_K_GATE, "<Z_0> partials",
-               [&] { return launch_gbg_expz(psi, n, B, c->e_part, c->stream); });
+    return run(c, HQML_K_GATE, "<O> partials",
+               [&] { return launch_gbg_expz(psi, n, B, c->obs, c->e_part, c->stream); });
 }
 
 // Adjoint sweep from the final state left in gbg_psi; leaves the gradient block sums
@@ -410,7 +417,7 @@ int gbg_backward_sweep(hqml_ctx *c, int B)
     float2 *psi = reinterpret_cast<float2 *>(c->gbg_psi);
     float2 *lam = reinterpret_cast<float2 *>(c->gbg_lam);
     const size_t per_gate = (size_t)B * c->gbg_blocks;
-    int rc = run(c, HQML_K_GATE, "adjoint seed", [&] { return launch_gbg_seed(psi, lam, n, B, c->stream); });
+    int rc = run(c, HQML_K_GATE, "adjoint seed", [&] { return launch_gbg_seed(psi, lam, n, B, c->obs, c->stream); });
     if (rc) return rc;
     for (int l = L - 1; l >= 0; --l) {
         for (int q = n - 2; q >= 0; --q)
@@ -485,6 +492,7 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     c->cfg = *cfg;
     c->plan = plan;
     c->gbg = cfg->fusion == HQML_GATE_BY_GATE;
+    c->obs = cfg->obs_mask ? (uint32_t)cfg->obs_mask : 1u;
     c->ws = workspace_for(cfg, plan);
     c->stream = reinterpret_cast<hipStream_t>(cfg->stream);
     hipError_t e = hipSetDevice(cfg->device);

@@ -120,9 +120,10 @@ __global__ void __launch_bounds__(kGbgThreads) k_gbg_cz(float2 *psi, float2 *lam
     }
 }
 
-// Per-block <Z_0> partials: e_part[b][blk] = sum over the block's pairs (bit 0) of
-// |psi_even|^2 - |psi_odd|^2.  Grid (nblk, B).
-__global__ void __launch_bounds__(kGbgThreads) k_gbg_expz(const float2 *psi, uint32_t N, float *e_part)
+// Per-block <O> partials, O = prod of Z over the qubits of obs: e_part[b][blk] = sum over
+// the block's amplitude pairs (2k, 2k+1) of sign_O |psi|^2.  Grid (nblk, B).
+__global__ void __launch_bounds__(kGbgThreads) k_gbg_expz(const float2 *psi, uint32_t N, uint32_t obs,
+                                                           float *e_part)
 {
     __shared__ double red[kGbgThreads];
     const int b = blockIdx.y;
@@ -133,20 +134,22 @@ __global__ void __launch_bounds__(kGbgThreads) k_gbg_expz(const float2 *psi, uin
         const uint32_t k = blockIdx.x * kGbgPairsPerBlock + j * kGbgThreads + threadIdx.x;
         if (k >= half) break;
         const float2 a = s[2 * k], c = s[2 * k + 1];
-        acc += (a.x * a.x + a.y * a.y) - (c.x * c.x + c.y * c.y);
+        const float pa = a.x * a.x + a.y * a.y, pc = c.x * c.x + c.y * c.y;
+        acc += (__builtin_popcount((2 * k) & obs) & 1) ? -pa : pa;
+        acc += (__builtin_popcount((2 * k + 1) & obs) & 1) ? -pc : pc;
     }
     const double t = gbg_block_sum((double)acc, red);
     if (threadIdx.x == 0) e_part[(size_t)b * gridDim.x + blockIdx.x] = (float)t;
 }
 
-// lambda = 2 Z_0 psi (the upstream dL/dE_b is applied in the final reduction).
+// lambda = 2 O psi (the upstream dL/dE_b is applied in the final reduction).
 // Grid (ceil(N / 256), B).
-__global__ void __launch_bounds__(kGbgThreads) k_gbg_seed(const float2 *psi, float2 *lam, uint32_t N)
+__global__ void __launch_bounds__(kGbgThreads) k_gbg_seed(const float2 *psi, float2 *lam, uint32_t N, uint32_t obs)
 {
     const uint32_t i = blockIdx.x * kGbgThreads + threadIdx.x;
     if (i >= N) return;
     const size_t o = (size_t)blockIdx.y * N + i;
-    const float f = (i & 1u) ? -2.f : 2.f;
+    const float f = (__builtin_popcount(i & obs) & 1) ? -2.f : 2.f;
     const float2 v = psi[o];
     lam[o] = make_float2(f * v.x, f * v.y);
 }
@@ -248,16 +251,16 @@ hipError_t launch_gbg_cz(float2 *psi, float2 *lam, int n, int B, int q, hipStrea
     return hipGetLastError();
 }
 
-hipError_t launch_gbg_expz(const float2 *psi, int n, int B, float *e_part, hipStream_t s)
+hipError_t launch_gbg_expz(const float2 *psi, int n, int B, uint32_t obs, float *e_part, hipStream_t s)
 {
-    k_gbg_expz<<<dim3((unsigned)gbg_blocks(n), (unsigned)B), kGbgThreads, 0, s>>>(psi, 1u << n, e_part);
+    k_gbg_expz<<<dim3((unsigned)gbg_blocks(n), (unsigned)B), kGbgThreads, 0, s>>>(psi, 1u << n, obs, e_part);
     return hipGetLastError();
 }
 
-hipError_t launch_gbg_seed(const float2 *psi, float2 *lam, int n, int B, hipStream_t s)
+hipError_t launch_gbg_seed(const float2 *psi, float2 *lam, int n, int B, uint32_t obs, hipStream_t s)
 {
     const uint32_t N = 1u << n;
-    k_gbg_seed<<<dim3((N + kGbgThreads - 1) / kGbgThreads, (unsigned)B), kGbgThreads, 0, s>>>(psi, lam, N);
+    k_gbg_seed<<<dim3((N + kGbgThreads - 1) / kGbgThreads, (unsigned)B), kGbgThreads, 0, s>>>(psi, lam, N, obs);
     return hipGetLastError();
 }
 

@@ -22,9 +22,9 @@
 //     psi_0 (product state, all of layer 0's right factors and Ry applied),
 //     D_0, Ry-layer 1, D_1, ..., Ry-layer L-1,
 // and the trailing diagonal (layer L-1's left factors and CZ chain) is dropped:
-// it commutes with Z_0 and does not change E or any gradient.  Gradients are taken
+// it commutes with the (diagonal) observable and does not change E or any gradient.  Gradients are taken
 // at the point P_l just after Ry-layer l: with S_s = Im<mu|s_q|psi> (s = X, Y, Z
-// on qubit q, mu the back-propagated Z_0 psi_M),
+// on qubit q, mu the back-propagated O psi_M),
 //     dE/dtheta[l][q][a] = sum_s H[l][q][a][s] * S_s,
 // where H holds the Pauli coefficients of p-conjugated rotated generators
 // (computed in k_prep_tables).  A Pauli frame (k_prep_frame) then keeps every
@@ -69,18 +69,18 @@ struct ViewDev {
 
 enum PassFlags : int {
     PF_INIT = 1,         // generate the layer-0 product state instead of loading a state
-    PF_EMIT_E = 2,       // write per-tile <Z_0> partial sums
+    PF_EMIT_E = 2,       // write per-tile <O> partial sums
     PF_STORE = 4,        // forward: write the pass output
     PF_FUSED = 8,        // forward ops of the (last) pass followed by its backward ops
     PF_STATS_ONLY = 16,  // backward: layer-0 statistics of this view only (no state update)
-    PF_SEED = 32         // backward: lambda = Z_0 psi formed from the pass output (last pass)
+    PF_SEED = 32         // backward: lambda = O psi formed from the pass output (last pass)
 };
 
 struct TilePassArgs {
     const void *psi_in;     // fwd: input state (previous pass output); bwd: saved output of this pass
     void *psi_out;          // fwd: output state
     float *lam;             // bwd: adjoint state, fp32 complex, updated in place
-    float *e_part;          // [B][T] per-tile <Z_0> partial sums
+    float *e_part;          // [B][T] per-tile <O> partial sums
     float *stat_part;       // [B][T][kSlots] per-tile gradient statistics of this pass
     const float *rot_tf;    // [L][n][2]: tan form (k, f) of the real rotation
     const float *dw;        // [L][n][4]: factors (f0, f1) of qubit q in D_l
@@ -94,6 +94,7 @@ struct TilePassArgs {
     int rotB;               // second rotation layer (-1: none)
     int flags;
     int sample0;            // first sample of this launch (the grid covers samples sample0 ..)
+    uint32_t obs;           // observable O = prod of Z over the qubits of this mask
 };
 
 struct SmallArgs {
@@ -101,12 +102,12 @@ struct SmallArgs {
     const float *rot_tf;    // [L][n][2]
     const float *dw;        // [L][n][4]
     float *psi_save;        // [B][2^n][2]: final state (forward mode writes, backward mode reads)
-    float *e_out;           // [B] per-sample <Z_0> (fp32, from an fp64 in-block sum)
+    float *e_out;           // [B] per-sample <O> (fp32, from an fp64 in-block sum)
     double *stats;          // [B][L][n][3] per-sample statistics S_s at point P_l
     int n;
     int L;
     int mode;               // 0: forward only; 1: backward only (from psi_save); 2: both
-    int pad;
+    uint32_t obs;           // observable O = prod of Z over the qubits of this mask
 };
 
 }  // namespace hqml

@@ -15,7 +15,7 @@
 //                   earlier state with U^dagger on chip, forms the gradient statistics and
 //                   propagates lambda <- U^dagger lambda
 //   k_small         n <= 13: the whole circuit of one sample in one workgroup
-//   k_ez_reduce     per-tile <Z_0> partials -> E_b, loss, dL/dE_b (fixed-order fp64)
+//   k_ez_reduce     per-tile <O> partials -> E_b, loss, dL/dE_b (fixed-order fp64)
 //   k_stats_reduce  per-tile statistics -> per-sample statistics (fixed-order fp64)
 //   k_grad_reduce   per-sample statistics x dL/dE x H -> dL/dtheta (fixed-order fp64)
 // No floating-point atomics anywhere: every reduction has a fixed order.
@@ -651,20 +651,31 @@ __device__ __forceinline__ void init_l1(Tile &t, const float *init_u, const Tile
     }
 }
 
-// Sign mask of Z_0 for the 32 registers of this thread (bit j set: qubit 0 is 1).
-__device__ __forceinline__ uint32_t z0_mask_l1(const TileCtx &c)
+// Sign pattern of the observable O = prod_{q in S} Z_q over the 32 registers of this
+// thread: bit j is set when O has eigenvalue -1 on register j's amplitude, i.e. when
+// an odd number of the qubits of S are 1 there.  'fixed' holds the thread's non-register
+// qubit values (lane, wave and tile bits); register bit m holds qubit q[m].
+__device__ __forceinline__ uint32_t obs_sign_mask(uint32_t fixed, const int *q, uint32_t S)
 {
-    return (c.fixed1 & 1u) ? 0xFFFFFFFFu : 0u;   // qubit 0 sits at a lane position in L1
+    constexpr uint32_t kRegBit[5] = {0xAAAAAAAAu, 0xCCCCCCCCu, 0xF0F0F0F0u, 0xFF00FF00u, 0xFFFF0000u};
+    uint32_t m = (__builtin_popcount(fixed & S) & 1) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int r = 0; r < 5; ++r)
+        if ((S >> q[r]) & 1u) m ^= kRegBit[r];
+    return m;
 }
 
-__device__ __forceinline__ uint32_t z0_mask_l2(const TileCtx &c)
+__device__ __forceinline__ uint32_t obs_mask_l1(const TileCtx &c, uint32_t S)
 {
-    if (c.q2[0] == 0) return 0xAAAAAAAAu;
-    if (c.q2[1] == 0) return 0xCCCCCCCCu;
-    return (c.fixed2 & 1u) ? 0xFFFFFFFFu : 0u;
+    return obs_sign_mask(c.fixed1, c.q1, S);
 }
 
-// Workgroup sum of the per-thread <Z_0> partial -> e_part[sample][tile].
+__device__ __forceinline__ uint32_t obs_mask_l2(const TileCtx &c, uint32_t S)
+{
+    return obs_sign_mask(c.fixed2, c.q2, S);
+}
+
+// Workgroup sum of the per-thread <O> partial -> e_part[sample][tile].
 __device__ __forceinline__ void emit_e(float e, float *lds_stat, float *e_part, const TileCtx &c, int T)
 {
     e = row_sum16(e);
@@ -743,7 +754,7 @@ __device__ __forceinline__ void fwd_ops(Tile &t, const TilePassArgs &a, const Ti
         }
     }
     if (a.diag < 0 && (a.rotA >= 0 || a.rotB >= 0)) scale_tile(t, sigma);
-    if (a.flags & PF_EMIT_E) emit_e(z0_partial(t, z0_mask_l1(c)), lds_stat, a.e_part, c, a.T);
+    if (a.flags & PF_EMIT_E) emit_e(z0_partial(t, obs_mask_l1(c, a.obs)), lds_stat, a.e_part, c, a.T);
     if (a.flags & PF_STORE) store_l1<ST>(t, a.psi_out, c, nelem);
 }
 
@@ -813,7 +824,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_tile_bwd(TilePassArgs a)
 
     if constexpr (SHAPE == BW_FUSED_INIT) {
         init_l1(p, a.init_u, c, a.n);
-        const uint32_t zm = z0_mask_l1(c);
+        const uint32_t zm = obs_mask_l1(c, a.obs);
         emit_e(z0_partial(p, zm), lds_stat, a.e_part, c, a.T);
         seed_lambda(l, p, zm);
         stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, 1.f);
@@ -829,7 +840,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_tile_bwd(TilePassArgs a)
         transpose(p, lds, c.a1, c.a2, true);
         rot_layer<false>(p, r2);
         const float fa = r1.F * r2.F;          // psi (and the seeded lambda) carry scale fa
-        const uint32_t zm = z0_mask_l2(c);
+        const uint32_t zm = obs_mask_l2(c, a.obs);
         emit_e(z0_partial(p, zm) * (fa * fa), lds_stat, a.e_part, c, a.T);
         seed_lambda(l, p, zm);
         stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, fa * fa);
@@ -846,7 +857,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_tile_bwd(TilePassArgs a)
         else
             load_l1<ST>(p, a.psi_in, c, nelem);
         if (a.flags & PF_SEED)
-            seed_lambda(l, p, z0_mask_l1(c));
+            seed_lambda(l, p, obs_mask_l1(c, a.obs));
         else
             load_l1<0>(l, a.lam, c, nelem);
         if constexpr (SHAPE == BW_GENERAL || SHAPE == BW_INIT_GENERAL) {
@@ -970,12 +981,12 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
                 __syncthreads();
             }
         }
-        // <Z_0>
+        // <O>
         float e = 0.f;
         for (uint32_t i = tid; i < N; i += kThreads) {
             const float2 v = psi[i];
             const float pr = v.x * v.x + v.y * v.y;
-            e += (i & 1u) ? -pr : pr;
+            e += (__builtin_popcount(i & a.obs) & 1) ? -pr : pr;
         }
         e = row_sum16(e);
         if ((lane & 15) == 15) red[w * 4 + (lane >> 4)] = e;
@@ -995,10 +1006,10 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
         __syncthreads();
     }
 
-    // Adjoint sweep: lambda = Z_0 psi at P_{L-1}; statistics at every P_l; uncompute.
+    // Adjoint sweep: lambda = O psi at P_{L-1}; statistics at every P_l; uncompute.
     for (uint32_t i = tid; i < N; i += kThreads) {
         const float2 v = psi[i];
-        lam[i] = (i & 1u) ? make_float2(-v.x, -v.y) : v;
+        lam[i] = (__builtin_popcount(i & a.obs) & 1) ? make_float2(-v.x, -v.y) : v;
     }
     __syncthreads();
     for (int l = L - 1; l >= 0; --l) {
@@ -1249,7 +1260,7 @@ __global__ void k_prep_init(const float *x, const double *zyz, const unsigned ch
 // ------------------------------------------------------------------ reductions (fixed order)
 
 // E_b = sum over tiles (fp64); with y: loss = mean (E - y)^2 and dLdE = 2 (E - y) / B.
-// First stage for samples with many tiles: out[b][ch] = sum of the <Z_0> partials of
+// First stage for samples with many tiles: out[b][ch] = sum of the <O> partials of
 // tiles ch*kTileChunk .. (ch+1)*kTileChunk-1 of sample b, by a fixed-order tree.
 // Grid (T / kTileChunk, B), kTileChunk threads.
 __global__ void __launch_bounds__(kTileChunk) k_ez_chunks(const float *e_part, int T, double *out)

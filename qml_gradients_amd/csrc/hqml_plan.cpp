@@ -280,7 +280,7 @@ Workspace size_workspace_gbg(int n, int L, int max_batch)
     w.part_bytes = n_params * B * nblk * 8;
     w.tile_chunks = nblk > (size_t)kTileChunk ? (int)(nblk / kTileChunk) : 0;
     w.epart2_bytes = B * (size_t)w.tile_chunks * 8;
-    // theta copy, dL/dE, E scratch, loss, per-block <Z_0> partials
+    // theta copy, dL/dE, E scratch, loss, per-block <O> partials
     w.tables_bytes = n_params * 4 + B * 16 + 64 + B * nblk * 4;
     w.total = w.state_bytes + w.lam_bytes + w.part_bytes + w.epart2_bytes + w.tables_bytes;
     return w;

@@ -57,7 +57,7 @@ struct Workspace {
     size_t part_bytes = 0;
     int tile_chunks = 0;        // first-stage reduction blocks per sample (0: tiles summed directly)
     size_t part2_bytes = 0;     // first-stage sums of the statistics partials, fp64
-    size_t epart2_bytes = 0;    // first-stage sums of the <Z_0> partials, fp64
+    size_t epart2_bytes = 0;    // first-stage sums of the <O> partials, fp64
     size_t tables_bytes = 0;
     size_t total = 0;
 };
@@ -66,7 +66,7 @@ Workspace size_workspace(const Plan &p, int max_batch, int storage);
 
 // Gate-by-gate comparator: workgroups per sample of one gate kernel, and its
 // workspace (psi and lambda as fp32 states, per-gate fp64 block sums of the
-// gradient terms in part_bytes, per-block <Z_0> partials, a copy of theta).
+// gradient terms in part_bytes, per-block <O> partials, a copy of theta).
 int gbg_blocks_per_sample(int n);
 Workspace size_workspace_gbg(int n, int L, int max_batch);
 

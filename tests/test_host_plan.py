@@ -42,12 +42,14 @@ def test_workspace_and_validation_host_only():
     assert hq.hqml_workspace_bytes(hq.make_config(20, 100, 32)) > 100 * 32 * (1 << 20) * 8
     for bad in (hq.make_config(0, 1, 1), hq.make_config(30, 1, 1), hq.make_config(4, 0, 1),
                 hq.make_config(4, 1, 0), hq.make_config(4, 1, 1, storage=7),
-                hq.make_config(4, 1, 1, ckpt_block=-1)):
+                hq.make_config(4, 1, 1, ckpt_block=-1), hq.make_config(4, 1, 1, obs_mask=16),
+                hq.make_config(4, 1, 1, obs_mask=-1)):
         assert hq.hqml_workspace_bytes(bad) == 0
         with pytest.raises(hq.HqmlError) as e:
             hq.hqml_create(bad)
         assert e.value.status == hq.HQML_ERR_ARG
     assert hq.load().hqml_status_str(hq.HQML_ERR_STATE) == b"call out of order"
+    assert hq.hqml_workspace_bytes(hq.make_config(4, 1, 1, obs_mask=15)) > 0
 
 
 def test_gate_by_gate_config_host_only():
