@@ -54,9 +54,18 @@ typedef enum {
 
 typedef enum {
     HQML_STORE_FP32 = 0,        /* saved states as complex fp32 (8 bytes per amplitude) */
-    HQML_STORE_BF16 = 1         /* saved states as bf16 (re, im) pairs, round to nearest even;
+    HQML_STORE_BF16 = 1,        /* saved states as bf16 (re, im) pairs, round to nearest even;
                                    arithmetic stays fp32 (the pages' mem-save mode, section 2.3) */
+    HQML_STORE_FP64 = 2         /* saved states as complex fp64 (16 bytes per amplitude);
+                                   needs HQML_COMPUTE_FP64 (full complex128 mode) */
 } hqml_storage;
+
+typedef enum {
+    HQML_COMPUTE_FP32 = 0,      /* arithmetic, lambda and partial sums in fp32 (fp64 reductions) */
+    HQML_COMPUTE_FP64 = 1       /* arithmetic, lambda and partial sums in fp64, with fp32 or fp64
+                                   saved states (the pages' higher-precision modes; n_qubits 13
+                                   is not supported in this mode) */
+} hqml_compute;
 
 typedef enum {
     HQML_FUSED = 0,             /* fused forward and adjoint passes (the method itself) */
@@ -78,6 +87,7 @@ typedef struct {
     int device;        /* HIP device ordinal */
     void *stream;      /* hipStream_t to queue work on; NULL = the null stream */
     int fusion;        /* hqml_fusion; 0 = HQML_FUSED */
+    int compute;       /* hqml_compute; 0 = HQML_COMPUTE_FP32 */
     int obs_mask;      /* observable O = product of Z_q over the qubits q whose bit is set
                           (bit q = qubit q, only qubits 0..n_qubits-1); 0 = Z on qubit 0.
                           A diagonal case of the general O of section 1.2 */
@@ -116,6 +126,15 @@ int hqml_backward(hqml_ctx *ctx, const float *dL_dE, float *grad);
  * first of the backward sweep run as one kernel. */
 int hqml_train_step(hqml_ctx *ctx, int B, const float *x, const float *theta, const float *y,
                     float *expz, float *loss, float *grad);
+
+/* The same three calls with fp64 arrays (x, theta, y, dL_dE in; expz, loss, grad out),
+ * for contexts whose results are wanted in fp64 (normally HQML_COMPUTE_FP64; any fused
+ * context accepts them).  HQML_ERR_UNSUPPORTED on a HQML_GATE_BY_GATE context. */
+int hqml_forward_f64(hqml_ctx *ctx, int B, const double *x, const double *theta, double *expz,
+                     int save_for_backward);
+int hqml_backward_f64(hqml_ctx *ctx, const double *dL_dE, double *grad);
+int hqml_train_step_f64(hqml_ctx *ctx, int B, const double *x, const double *theta, const double *y,
+                        double *expz, double *loss, double *grad);
 
 /* Static text for a status code. */
 const char *hqml_status_str(int status);

@@ -23,6 +23,9 @@ HQML_ERR_STATE = -4
 HQML_ERR_UNSUPPORTED = -5
 HQML_STORE_FP32 = 0
 HQML_STORE_BF16 = 1
+HQML_STORE_FP64 = 2
+HQML_COMPUTE_FP32 = 0
+HQML_COMPUTE_FP64 = 1
 HQML_FUSED = 0
 HQML_GATE_BY_GATE = 1
 HQML_K_FWD_PASS, HQML_K_BWD_PASS, HQML_K_SMALL, HQML_K_OTHER, HQML_K_GATE, HQML_K_COUNT = range(6)
@@ -38,6 +41,7 @@ class hqml_config(ctypes.Structure):
         ("device", ctypes.c_int),
         ("stream", ctypes.c_void_p),
         ("fusion", ctypes.c_int),
+        ("compute", ctypes.c_int),
         ("obs_mask", ctypes.c_int),
     ]
 
@@ -70,6 +74,9 @@ def load() -> ctypes.CDLL:
         "hqml_forward": (i, [P, i, P, P, P, i]),
         "hqml_backward": (i, [P, P, P]),
         "hqml_train_step": (i, [P, i, P, P, P, P, P, P]),
+        "hqml_forward_f64": (i, [P, i, P, P, P, i]),
+        "hqml_backward_f64": (i, [P, P, P]),
+        "hqml_train_step_f64": (i, [P, i, P, P, P, P, P, P]),
         "hqml_status_str": (ctypes.c_char_p, [i]),
         "hqml_last_error": (ctypes.c_char_p, [P]),
         "hqml_set_timing": (i, [P, i]),
@@ -88,16 +95,17 @@ def load() -> ctypes.CDLL:
 
 
 EXPORTED = ("hqml_workspace_bytes", "hqml_create", "hqml_destroy", "hqml_forward", "hqml_backward",
-            "hqml_train_step", "hqml_status_str", "hqml_last_error", "hqml_set_timing",
+            "hqml_train_step", "hqml_forward_f64", "hqml_backward_f64", "hqml_train_step_f64", "hqml_status_str", "hqml_last_error", "hqml_set_timing",
             "hqml_set_overlap", "hqml_kernel_times", "hqml_plan_info", "hqml_describe_plan")
 
 
 def make_config(n_qubits, n_layers, max_batch, storage="fp32", ckpt_block=0, device=0, stream=None,
-                fusion="fused", obs_mask=0):
-    st = {"fp32": HQML_STORE_FP32, "bf16": HQML_STORE_BF16}.get(storage, storage)
+                fusion="fused", obs_mask=0, compute="fp32"):
+    st = {"fp32": HQML_STORE_FP32, "bf16": HQML_STORE_BF16, "fp64": HQML_STORE_FP64}.get(storage, storage)
     fu = {"fused": HQML_FUSED, "gate_by_gate": HQML_GATE_BY_GATE}.get(fusion, fusion)
+    co = {"fp32": HQML_COMPUTE_FP32, "fp64": HQML_COMPUTE_FP64}.get(compute, compute)
     return hqml_config(int(n_qubits), int(n_layers), int(max_batch), int(st), int(ckpt_block),
-                       int(device), ctypes.c_void_p(stream or 0), int(fu), int(obs_mask))
+                       int(device), ctypes.c_void_p(stream or 0), int(fu), int(co), int(obs_mask))
 
 
 # ---- the C entry points, same names, argument marshalling only ----
@@ -146,6 +154,18 @@ def hqml_train_step(ctx, B, x_ptr, theta_ptr, y_ptr, expz_ptr, loss_ptr, grad_pt
     _check(ctx, load().hqml_train_step(ctx, int(B), x_ptr, theta_ptr, y_ptr, expz_ptr, loss_ptr, grad_ptr))
 
 
+def hqml_forward_f64(ctx, B, x_ptr, theta_ptr, expz_ptr, save_for_backward) -> None:
+    _check(ctx, load().hqml_forward_f64(ctx, int(B), x_ptr, theta_ptr, expz_ptr, int(save_for_backward)))
+
+
+def hqml_backward_f64(ctx, dlde_ptr, grad_ptr) -> None:
+    _check(ctx, load().hqml_backward_f64(ctx, dlde_ptr, grad_ptr))
+
+
+def hqml_train_step_f64(ctx, B, x_ptr, theta_ptr, y_ptr, expz_ptr, loss_ptr, grad_ptr) -> None:
+    _check(ctx, load().hqml_train_step_f64(ctx, int(B), x_ptr, theta_ptr, y_ptr, expz_ptr, loss_ptr, grad_ptr))
+
+
 def hqml_set_timing(ctx, enable: bool) -> None:
     _check(ctx, load().hqml_set_timing(ctx, int(bool(enable))))
 
@@ -174,12 +194,13 @@ def hqml_plan_info(ctx):
 class Context:
     """One hqml context on the current torch device and stream.
 
-    Inputs and outputs are torch float32 CUDA tensors; the library reads and
-    writes them in place through their device pointers.
+    Inputs and outputs are torch CUDA tensors (float32; float64 for a context with
+    compute="fp64", through the *_f64 entry points); the library reads and writes
+    them in place through their device pointers.
     """
 
     def __init__(self, n_qubits, n_layers, max_batch, storage="fp32", ckpt_block=0, device=None,
-                 stream=None, fusion="fused", obs_mask=0):
+                 stream=None, fusion="fused", obs_mask=0, compute="fp32"):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("hqml needs a GPU (torch.cuda.is_available() is False)")
@@ -190,7 +211,9 @@ class Context:
         self.device = torch.device("cuda", dev)
         self.n, self.L, self.max_batch = int(n_qubits), int(n_layers), int(max_batch)
         self.cfg = make_config(n_qubits, n_layers, max_batch, storage, ckpt_block, dev, stream, fusion,
-                               obs_mask)
+                               obs_mask, compute)
+        self.f64 = compute == "fp64" or compute == HQML_COMPUTE_FP64
+        self.dtype = torch.float64 if self.f64 else torch.float32
         self.handle = hqml_create(self.cfg)
 
     def close(self):
@@ -206,7 +229,7 @@ class Context:
 
     def _dev(self, a, shape):
         t = self.torch
-        a = t.as_tensor(a, dtype=t.float32, device=self.device).contiguous()
+        a = t.as_tensor(a, dtype=self.dtype, device=self.device).contiguous()
         if tuple(a.shape) != tuple(shape):
             raise ValueError(f"expected shape {tuple(shape)}, got {tuple(a.shape)}")
         return a
@@ -215,15 +238,17 @@ class Context:
         B = int(x.shape[0])
         x = self._dev(x, (B, self.n))
         theta = self._dev(theta, (self.L, self.n, 3))
-        expz = self.torch.empty(B, dtype=self.torch.float32, device=self.device)
-        hqml_forward(self.handle, B, x.data_ptr(), theta.data_ptr(), expz.data_ptr(), save_for_backward)
+        expz = self.torch.empty(B, dtype=self.dtype, device=self.device)
+        fwd = hqml_forward_f64 if self.f64 else hqml_forward
+        fwd(self.handle, B, x.data_ptr(), theta.data_ptr(), expz.data_ptr(), save_for_backward)
         self._keep = (x, theta)
         return expz
 
     def backward(self, dlde):
         dlde = self._dev(dlde, (int(dlde.shape[0]),))
-        grad = self.torch.empty((self.L, self.n, 3), dtype=self.torch.float32, device=self.device)
-        hqml_backward(self.handle, dlde.data_ptr(), grad.data_ptr())
+        grad = self.torch.empty((self.L, self.n, 3), dtype=self.dtype, device=self.device)
+        bwd = hqml_backward_f64 if self.f64 else hqml_backward
+        bwd(self.handle, dlde.data_ptr(), grad.data_ptr())
         self._keep_b = dlde
         return grad
 
@@ -233,11 +258,12 @@ class Context:
         theta = self._dev(theta, (self.L, self.n, 3))
         y = self._dev(y, (B,))
         t = self.torch
-        expz = t.empty(B, dtype=t.float32, device=self.device)
-        loss = t.empty(1, dtype=t.float32, device=self.device)
-        grad = t.empty((self.L, self.n, 3), dtype=t.float32, device=self.device)
-        hqml_train_step(self.handle, B, x.data_ptr(), theta.data_ptr(), y.data_ptr(), expz.data_ptr(),
-                        loss.data_ptr(), grad.data_ptr())
+        expz = t.empty(B, dtype=self.dtype, device=self.device)
+        loss = t.empty(1, dtype=self.dtype, device=self.device)
+        grad = t.empty((self.L, self.n, 3), dtype=self.dtype, device=self.device)
+        step = hqml_train_step_f64 if self.f64 else hqml_train_step
+        step(self.handle, B, x.data_ptr(), theta.data_ptr(), y.data_ptr(), expz.data_ptr(), loss.data_ptr(),
+             grad.data_ptr())
         self._keep = (x, theta, y)
         return expz, loss, grad
 

@@ -21,19 +21,21 @@
 #include "hqml_plan.hpp"
 
 namespace hqml {
-hipError_t launch_prep(const float *theta, const float *x, int L, int n, int B, double *zyz, unsigned char *G,
-                       float *rot_tf, float *dw, double *H, float *init_u, hipStream_t s);
-hipError_t launch_tile_fwd(const TilePassArgs &a, int B, int storage, hipStream_t s);
-hipError_t launch_tile_bwd(const TilePassArgs &a, int B, int storage, hipStream_t s);
-hipError_t launch_small(const SmallArgs &a, int B, hipStream_t s);
-hipError_t configure_small(size_t shm_bytes);
-hipError_t launch_ez_reduce(const float *e_part, int B, int T, const float *y, float *e_out, float *loss,
-                            double *dlde, double *e_work, double *chunks, hipStream_t s);
-hipError_t launch_copy_dlde(const float *src, int B, double *dlde, hipStream_t s);
-hipError_t launch_stats_reduce(const float *part, const int2 *map, int Bs, int b0, int Bc, int L, int n, int T,
-                               int pass_lo, int pass_hi, double *S, double *chunks, hipStream_t s);
+// Type codes: io64 = caller arrays are double; r64 = compute in double; storage 0/1/2 =
+// fp32 / bf16 / fp64 saved states.
+hipError_t launch_prep(const void *theta, const void *x, int io64, int L, int n, int B, double *zyz,
+                       unsigned char *G, void *rot_tf, void *dw, double *H, void *init_u, int r64, hipStream_t s);
+hipError_t launch_tile_fwd(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s);
+hipError_t launch_tile_bwd(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s);
+hipError_t launch_small(const SmallArgs &a, int B, int r64, hipStream_t s);
+hipError_t configure_small(size_t shm_bytes, int r64);
+hipError_t launch_ez_reduce(const void *e_part, int r64, int B, int T, const void *y, void *e_out, void *loss,
+                            int io64, double *dlde, double *e_work, double *chunks, hipStream_t s);
+hipError_t launch_copy_dlde(const void *src, int io64, int B, double *dlde, hipStream_t s);
+hipError_t launch_stats_reduce(const void *part, int r64, const int2 *map, int Bs, int b0, int Bc, int L, int n,
+                               int T, int pass_lo, int pass_hi, double *S, double *chunks, hipStream_t s);
 hipError_t launch_grad_reduce(const double *S, const double *H, const double *dlde, int B, int L, int n,
-                              float *grad, hipStream_t s);
+                              void *grad, int io64, hipStream_t s);
 // gate-by-gate comparator (hqml_gbg.hip)
 hipError_t launch_gbg_zero(float2 *psi, int n, int B, hipStream_t s);
 hipError_t launch_gbg_rot(int gate, float2 *psi, int n, int B, int q, const float *ang, int ang_stride,
@@ -64,17 +66,19 @@ struct hqml_ctx {
     int chunks = 0;              // 0: automatic
     std::vector<void *> allocs;
     // device buffers
+    int r64 = 0;                 // compute type: 0 float, 1 double
+    size_t rb = 4;               // bytes of the compute type
     char *saved = nullptr;       // saved states (n_saved buffers of max_batch samples)
-    float *lam = nullptr;
-    float *part = nullptr;
-    float *e_part = nullptr;
+    void *lam = nullptr;         // arrays below in the compute type
+    char *part = nullptr;
+    void *e_part = nullptr;
     double *S = nullptr;
     double *zyz = nullptr;
     unsigned char *frame = nullptr;
-    float *rot_tf = nullptr;
-    float *dw = nullptr;
+    void *rot_tf = nullptr;
+    void *dw = nullptr;
     double *H = nullptr;
-    float *init_u = nullptr;
+    void *init_u = nullptr;
     ViewDev *views = nullptr;
     int2 *statmap = nullptr;
     double *dlde = nullptr;
@@ -120,7 +124,10 @@ int hip_fail(hqml_ctx *c, hipError_t e, const char *what)
     return fail(c, HQML_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-size_t elem_bytes(const hqml_ctx *c) { return c->cfg.storage == HQML_STORE_BF16 ? 4 : 8; }
+size_t elem_bytes(const hqml_ctx *c)
+{
+    return c->cfg.storage == HQML_STORE_BF16 ? 4 : c->cfg.storage == HQML_STORE_FP64 ? 16 : 8;
+}
 
 hipEvent_t take_event(hqml_ctx *c)
 {
@@ -209,16 +216,16 @@ int fwd_pass(hqml_ctx *c, hipStream_t st, Span sp, int p, int extra_flags)
     a.flags = (pp.init ? PF_INIT : 0) | PF_STORE | extra_flags;
     a.sample0 = sp.b0;
     return run_on(c, st, HQML_K_FWD_PASS, "forward pass launch",
-                  [&] { return launch_tile_fwd(a, sp.bc, c->cfg.storage, st); });
+                  [&] { return launch_tile_fwd(a, sp.bc, c->cfg.storage, c->r64, st); });
 }
 
 // Backward pass k (forward pass index, or n_fwd + i for the i-th layer-0 stats-only pass).
-int bwd_pass(hqml_ctx *c, hipStream_t st, Span sp, int k, int part_lo, float *part_base, int extra_flags)
+int bwd_pass(hqml_ctx *c, hipStream_t st, Span sp, int k, int part_lo, char *part_base, int extra_flags)
 {
     const Plan &pl = c->plan;
     const int P = pl.n_fwd();
     TilePassArgs a = base_args(c);
-    a.stat_part = part_base + (size_t)(k - part_lo) * sp.bs * pl.T * kSlots;
+    a.stat_part = part_base + (size_t)(k - part_lo) * sp.bs * pl.T * kSlots * c->rb;
     a.sample0 = sp.b0;
     if (k >= P) {
         a.view = c->views + pl.stats_only[k - P];
@@ -237,14 +244,14 @@ int bwd_pass(hqml_ctx *c, hipStream_t st, Span sp, int k, int part_lo, float *pa
             a.psi_in = pass_out(c, k);
     }
     return run_on(c, st, HQML_K_BWD_PASS, "backward pass launch",
-                  [&] { return launch_tile_bwd(a, sp.bc, c->cfg.storage, st); });
+                  [&] { return launch_tile_bwd(a, sp.bc, c->cfg.storage, c->r64, st); });
 }
 
-int prep(hqml_ctx *c, int B, const float *x, const float *theta)
+int prep(hqml_ctx *c, int B, const void *x, const void *theta, int io64)
 {
     return run(c, HQML_K_OTHER, "table preparation", [&] {
-        return launch_prep(theta, x, c->plan.L, c->plan.n, B, c->zyz, c->frame, c->rot_tf, c->dw, c->H,
-                           c->init_u, c->stream);
+        return launch_prep(theta, x, io64, c->plan.L, c->plan.n, B, c->zyz, c->frame, c->rot_tf, c->dw, c->H,
+                           c->init_u, c->r64, c->stream);
     });
 }
 
@@ -258,9 +265,22 @@ int check_config(const hqml_config *cfg, Plan *plan, std::string *err)
         *err = "max_batch must be >= 1";
         return HQML_ERR_ARG;
     }
-    if (cfg->storage != HQML_STORE_FP32 && cfg->storage != HQML_STORE_BF16) {
-        *err = "storage must be HQML_STORE_FP32 or HQML_STORE_BF16";
+    if (cfg->storage != HQML_STORE_FP32 && cfg->storage != HQML_STORE_BF16 && cfg->storage != HQML_STORE_FP64) {
+        *err = "storage must be HQML_STORE_FP32, HQML_STORE_BF16 or HQML_STORE_FP64";
         return HQML_ERR_ARG;
+    }
+    if (cfg->compute != HQML_COMPUTE_FP32 && cfg->compute != HQML_COMPUTE_FP64) {
+        *err = "compute must be HQML_COMPUTE_FP32 or HQML_COMPUTE_FP64";
+        return HQML_ERR_ARG;
+    }
+    if ((cfg->storage == HQML_STORE_FP64 && cfg->compute != HQML_COMPUTE_FP64) ||
+        (cfg->storage == HQML_STORE_BF16 && cfg->compute != HQML_COMPUTE_FP32)) {
+        *err = "fp64 storage needs fp64 compute; bf16 storage needs fp32 compute";
+        return HQML_ERR_UNSUPPORTED;
+    }
+    if (cfg->compute == HQML_COMPUTE_FP64 && cfg->n_qubits == 13) {
+        *err = "fp64 compute supports n_qubits <= 12 (whole circuit per workgroup) or >= 14 (tiles)";
+        return HQML_ERR_UNSUPPORTED;
     }
     if (cfg->obs_mask < 0 || (cfg->n_qubits >= 1 && cfg->n_qubits < 31 && (cfg->obs_mask >> cfg->n_qubits) != 0)) {
         *err = "obs_mask may only name qubits 0..n_qubits-1";
@@ -274,8 +294,9 @@ int check_config(const hqml_config *cfg, Plan *plan, std::string *err)
         *err = "the gate-by-gate comparator takes at most 65535 samples";
         return HQML_ERR_ARG;
     }
-    if (cfg->fusion == HQML_GATE_BY_GATE && (cfg->storage != HQML_STORE_FP32 || cfg->ckpt_block != 0)) {
-        *err = "the gate-by-gate comparator supports fp32 storage without checkpointing only";
+    if (cfg->fusion == HQML_GATE_BY_GATE &&
+        (cfg->storage != HQML_STORE_FP32 || cfg->compute != HQML_COMPUTE_FP32 || cfg->ckpt_block != 0)) {
+        *err = "the gate-by-gate comparator supports fp32 storage and compute without checkpointing only";
         return HQML_ERR_UNSUPPORTED;
     }
     if (!make_plan(cfg->n_qubits, cfg->n_layers, cfg->ckpt_block, plan, err)) return HQML_ERR_ARG;
@@ -310,9 +331,10 @@ int tile_backward_sweep(hqml_ctx *c, hipStream_t st, Span sp, bool fused_last)
     const int nso = (int)pl.stats_only.size();
     int rc;
     const int2 *map = c->statmap;
-    auto reduce = [&](const float *base, int lo, int hi) {
+    auto reduce = [&](const char *base, int lo, int hi) {
         return run_on(c, st, HQML_K_OTHER, "statistics reduction", [&] {
-            return launch_stats_reduce(base, map, sp.bs, sp.b0, sp.bc, pl.L, pl.n, pl.T, lo, hi, c->S, c->part2, st);
+            return launch_stats_reduce(base, c->r64, map, sp.bs, sp.b0, sp.bc, pl.L, pl.n, pl.T, lo, hi, c->S,
+                                       c->part2, st);
         });
     };
     if (pl.c == 0) {
@@ -338,7 +360,7 @@ int tile_backward_sweep(hqml_ctx *c, hipStream_t st, Span sp, bool fused_last)
         }
         if ((rc = reduce(c->part, lo, hi))) return rc;
     }
-    float *so_base = c->part + (size_t)pl.c * sp.bs * pl.T * kSlots;
+    char *so_base = c->part + (size_t)pl.c * sp.bs * pl.T * kSlots * c->rb;
     for (int i = 0; i < nso; ++i)
         if ((rc = bwd_pass(c, st, sp, P + i, P, so_base, 0))) return rc;
     if (nso > 0) return reduce(so_base, P, P + nso);
@@ -377,7 +399,7 @@ SmallArgs small_args(hqml_ctx *c, int mode)
 Workspace workspace_for(const hqml_config *cfg, const Plan &plan)
 {
     if (cfg->fusion == HQML_GATE_BY_GATE) return size_workspace_gbg(plan.n, plan.L, cfg->max_batch);
-    return size_workspace(plan, cfg->max_batch, cfg->storage);
+    return size_workspace(plan, cfg->max_batch, cfg->storage, cfg->compute == HQML_COMPUTE_FP64);
 }
 
 int gbg_forward_sweep(hqml_ctx *c, int B, const float *x, const float *theta)
@@ -406,7 +428,7 @@ int gbg_forward_sweep(hqml_ctx *c, int B, const float *x, const float *theta)
                 return rc;
     }
     return run(c, HQML_K_GATE, "<O> partials",
-               [&] { return launch_gbg_expz(psi, n, B, c->obs, c->e_part, c->stream); });
+               [&] { return launch_gbg_expz(psi, n, B, c->obs, static_cast<float *>(c->e_part), c->stream); });
 }
 
 // Adjoint sweep from the final state left in gbg_psi; leaves the gradient block sums
@@ -492,6 +514,8 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     c->cfg = *cfg;
     c->plan = plan;
     c->gbg = cfg->fusion == HQML_GATE_BY_GATE;
+    c->r64 = cfg->compute == HQML_COMPUTE_FP64 ? 1 : 0;
+    c->rb = c->r64 ? 8 : 4;
     c->obs = cfg->obs_mask ? (uint32_t)cfg->obs_mask : 1u;
     c->ws = workspace_for(cfg, plan);
     c->stream = reinterpret_cast<hipStream_t>(cfg->stream);
@@ -532,7 +556,7 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
         c->gbg_lam = static_cast<float *>(grab(c->ws.lam_bytes));
         c->gbg_part = static_cast<double *>(grab(c->ws.part_bytes));
         c->gbg_theta = static_cast<float *>(grab(Ln * 3 * 4));
-        c->e_part = static_cast<float *>(grab((size_t)B * nblk * 4));
+        c->e_part = grab((size_t)B * nblk * 4);
         c->dlde = static_cast<double *>(grab((size_t)B * 8));
         c->e_work = static_cast<double *>(grab((size_t)B * 8));
         c->epart2 = static_cast<double *>(grab(c->ws.epart2_bytes));
@@ -545,16 +569,16 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
         return HQML_OK;
     }
     c->saved = static_cast<char *>(grab((size_t)c->ws.n_saved * c->ws.state_bytes));
-    c->lam = static_cast<float *>(grab(c->ws.lam_bytes));
-    c->part = static_cast<float *>(grab(c->ws.part_bytes));
-    c->e_part = static_cast<float *>(grab((size_t)B * plan.T * 4));
+    c->lam = grab(c->ws.lam_bytes);
+    c->part = static_cast<char *>(grab(c->ws.part_bytes));
+    c->e_part = grab((size_t)B * plan.T * c->rb);
     c->S = static_cast<double *>(grab((size_t)B * Ln * 3 * 8));
     c->zyz = static_cast<double *>(grab(Ln * 6 * 8));
     c->frame = static_cast<unsigned char *>(grab(Ln));
-    c->rot_tf = static_cast<float *>(grab(Ln * 2 * 4));
-    c->dw = static_cast<float *>(grab(Ln * 4 * 4));
+    c->rot_tf = grab(Ln * 2 * c->rb);
+    c->dw = grab(Ln * 4 * c->rb);
     c->H = static_cast<double *>(grab(Ln * 9 * 8));
-    c->init_u = static_cast<float *>(grab((size_t)B * plan.n * 16));
+    c->init_u = grab((size_t)B * plan.n * 4 * c->rb);
     if (!plan.small) c->views = static_cast<ViewDev *>(grab(plan.views.size() * sizeof(ViewDev)));
     c->statmap = static_cast<int2 *>(grab(Ln * sizeof(int2)));
     c->dlde = static_cast<double *>(grab((size_t)B * 8));
@@ -571,7 +595,7 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     e = hipMemcpy(c->statmap, sm.data(), Ln * sizeof(int2), hipMemcpyHostToDevice);
     if (e == hipSuccess && !plan.small)
         e = hipMemcpy(c->views, plan.views.data(), plan.views.size() * sizeof(ViewDev), hipMemcpyHostToDevice);
-    if (e == hipSuccess && plan.small) e = configure_small((size_t)2 * ((size_t)1 << plan.n) * 8);
+    if (e == hipSuccess && plan.small) e = configure_small((size_t)2 * ((size_t)1 << plan.n) * 2 * c->rb, c->r64);
     if (e != hipSuccess) {
         const std::string m = std::string("workspace set-up: ") + hipGetErrorString(e);
         hqml_destroy(c);
@@ -609,7 +633,11 @@ int hqml_destroy(hqml_ctx *c)
     return HQML_OK;
 }
 
-int hqml_forward(hqml_ctx *c, int B, const float *x, const float *theta, float *expz, int save_for_backward)
+}  // extern "C"
+
+namespace {
+
+int forward_impl(hqml_ctx *c, int B, const void *x, const void *theta, void *expz, int save_for_backward, int io64)
 {
     if (!c) return HQML_ERR_ARG;
     c->err.clear();
@@ -624,29 +652,31 @@ int hqml_forward(hqml_ctx *c, int B, const float *x, const float *theta, float *
     if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
     int rc;
     if (c->gbg) {
-        if ((rc = gbg_forward_sweep(c, B, x, theta))) return rc;
+        if ((rc = gbg_forward_sweep(c, B, static_cast<const float *>(x), static_cast<const float *>(theta)))) return rc;
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {
-            return launch_ez_reduce(c->e_part, B, c->gbg_blocks, nullptr, expz, nullptr, nullptr, c->e_work,
-                                    c->epart2, c->stream);
+            return launch_ez_reduce(c->e_part, 0, B, c->gbg_blocks, nullptr, expz, nullptr, io64, nullptr,
+                                    c->e_work, c->epart2, c->stream);
         });
         if (rc) return rc;
         if (save_for_backward) c->saved_B = B;
         return HQML_OK;
     }
-    rc = prep(c, B, x, theta);
+    rc = prep(c, B, x, theta, io64);
     if (rc) return rc;
     const Plan &pl = c->plan;
     if (pl.small) {
         const SmallArgs a = small_args(c, 0);
-        if ((rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->stream); })))
+        if ((rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->r64, c->stream); })))
             return rc;
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {
-            return launch_ez_reduce(c->e_part, B, 1, nullptr, expz, nullptr, nullptr, c->e_work, c->epart2, c->stream);
+            return launch_ez_reduce(c->e_part, c->r64, B, 1, nullptr, expz, nullptr, io64, nullptr, c->e_work,
+                                    c->epart2, c->stream);
         });
     } else {
         if ((rc = tile_forward_sweep(c, c->stream, Span{0, B, B}, false))) return rc;
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {
-            return launch_ez_reduce(c->e_part, B, pl.T, nullptr, expz, nullptr, nullptr, c->e_work, c->epart2, c->stream);
+            return launch_ez_reduce(c->e_part, c->r64, B, pl.T, nullptr, expz, nullptr, io64, nullptr, c->e_work,
+                                    c->epart2, c->stream);
         });
     }
     if (rc) return rc;
@@ -654,7 +684,7 @@ int hqml_forward(hqml_ctx *c, int B, const float *x, const float *theta, float *
     return HQML_OK;
 }
 
-int hqml_backward(hqml_ctx *c, const float *dL_dE, float *grad)
+int backward_impl(hqml_ctx *c, const void *dL_dE, void *grad, int io64)
 {
     if (!c) return HQML_ERR_ARG;
     c->err.clear();
@@ -665,33 +695,33 @@ int hqml_backward(hqml_ctx *c, const float *dL_dE, float *grad)
     if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
     const Plan &pl = c->plan;
     if (B == 0) {  // empty batch: the gradient is zero (the reduction over no samples)
-        if (c->gbg) return gbg_grad(c, 0, grad);
+        if (c->gbg) return gbg_grad(c, 0, static_cast<float *>(grad));
         return run(c, HQML_K_OTHER, "gradient reduction", [&] {
-            return launch_grad_reduce(c->S, c->H, c->dlde, 0, pl.L, pl.n, grad, c->stream);
+            return launch_grad_reduce(c->S, c->H, c->dlde, 0, pl.L, pl.n, grad, io64, c->stream);
         });
     }
     if (!dL_dE) return fail(c, HQML_ERR_ARG, "dL_dE must be a device pointer");
-    int rc = run(c, HQML_K_OTHER, "dL/dE copy", [&] { return launch_copy_dlde(dL_dE, B, c->dlde, c->stream); });
+    int rc = run(c, HQML_K_OTHER, "dL/dE copy", [&] { return launch_copy_dlde(dL_dE, io64, B, c->dlde, c->stream); });
     if (rc) return rc;
     if (c->gbg) {
         c->saved_B = -1;   // the adjoint sweep un-computes the saved state in place
         if ((rc = gbg_backward_sweep(c, B))) return rc;
-        return gbg_grad(c, B, grad);
+        return gbg_grad(c, B, static_cast<float *>(grad));
     }
     if (pl.small) {
         const SmallArgs a = small_args(c, 1);
-        rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->stream); });
+        rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->r64, c->stream); });
     } else {
         rc = tile_backward_sweep(c, c->stream, Span{0, B, B}, false);
     }
     if (rc) return rc;
     return run(c, HQML_K_OTHER, "gradient reduction", [&] {
-        return launch_grad_reduce(c->S, c->H, c->dlde, B, pl.L, pl.n, grad, c->stream);
+        return launch_grad_reduce(c->S, c->H, c->dlde, B, pl.L, pl.n, grad, io64, c->stream);
     });
 }
 
-int hqml_train_step(hqml_ctx *c, int B, const float *x, const float *theta, const float *y, float *expz,
-                    float *loss, float *grad)
+int train_impl(hqml_ctx *c, int B, const void *x, const void *theta, const void *y, void *expz, void *loss,
+               void *grad, int io64)
 {
     if (!c) return HQML_ERR_ARG;
     c->err.clear();
@@ -703,24 +733,25 @@ int hqml_train_step(hqml_ctx *c, int B, const float *x, const float *theta, cons
     c->saved_B = -1;
     int rc;
     if (c->gbg) {
-        if ((rc = gbg_forward_sweep(c, B, x, theta))) return rc;
+        if ((rc = gbg_forward_sweep(c, B, static_cast<const float *>(x), static_cast<const float *>(theta)))) return rc;
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {
-            return launch_ez_reduce(c->e_part, B, c->gbg_blocks, y, expz, loss, c->dlde, c->e_work, c->epart2,
-                                    c->stream);
+            return launch_ez_reduce(c->e_part, 0, B, c->gbg_blocks, y, expz, loss, io64, c->dlde, c->e_work,
+                                    c->epart2, c->stream);
         });
         if (rc) return rc;
         if ((rc = gbg_backward_sweep(c, B))) return rc;
-        return gbg_grad(c, B, grad);
+        return gbg_grad(c, B, static_cast<float *>(grad));
     }
-    rc = prep(c, B, x, theta);
+    rc = prep(c, B, x, theta, io64);
     if (rc) return rc;
     const Plan &pl = c->plan;
     if (pl.small) {
         const SmallArgs a = small_args(c, 2);
-        if ((rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->stream); })))
+        if ((rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->r64, c->stream); })))
             return rc;
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {
-            return launch_ez_reduce(c->e_part, B, 1, y, expz, loss, c->dlde, c->e_work, c->epart2, c->stream);
+            return launch_ez_reduce(c->e_part, c->r64, B, 1, y, expz, loss, io64, c->dlde, c->e_work, c->epart2,
+                                    c->stream);
         });
         if (rc) return rc;
     } else {
@@ -751,13 +782,53 @@ int hqml_train_step(hqml_ctx *c, int B, const float *x, const float *theta, cons
             }
         }
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {
-            return launch_ez_reduce(c->e_part, B, pl.T, y, expz, loss, c->dlde, c->e_work, c->epart2, c->stream);
+            return launch_ez_reduce(c->e_part, c->r64, B, pl.T, y, expz, loss, io64, c->dlde, c->e_work,
+                                    c->epart2, c->stream);
         });
         if (rc) return rc;
     }
     return run(c, HQML_K_OTHER, "gradient reduction", [&] {
-        return launch_grad_reduce(c->S, c->H, c->dlde, B, pl.L, pl.n, grad, c->stream);
+        return launch_grad_reduce(c->S, c->H, c->dlde, B, pl.L, pl.n, grad, io64, c->stream);
     });
+}
+
+}  // namespace
+
+extern "C" {
+
+int hqml_forward(hqml_ctx *c, int B, const float *x, const float *theta, float *expz, int save_for_backward)
+{
+    return forward_impl(c, B, x, theta, expz, save_for_backward, 0);
+}
+
+int hqml_backward(hqml_ctx *c, const float *dL_dE, float *grad)
+{
+    return backward_impl(c, dL_dE, grad, 0);
+}
+
+int hqml_train_step(hqml_ctx *c, int B, const float *x, const float *theta, const float *y, float *expz,
+                    float *loss, float *grad)
+{
+    return train_impl(c, B, x, theta, y, expz, loss, grad, 0);
+}
+
+int hqml_forward_f64(hqml_ctx *c, int B, const double *x, const double *theta, double *expz, int save_for_backward)
+{
+    if (c && c->gbg) return fail(c, HQML_ERR_UNSUPPORTED, "the gate-by-gate comparator takes fp32 arrays");
+    return forward_impl(c, B, x, theta, expz, save_for_backward, 1);
+}
+
+int hqml_backward_f64(hqml_ctx *c, const double *dL_dE, double *grad)
+{
+    if (c && c->gbg) return fail(c, HQML_ERR_UNSUPPORTED, "the gate-by-gate comparator takes fp32 arrays");
+    return backward_impl(c, dL_dE, grad, 1);
+}
+
+int hqml_train_step_f64(hqml_ctx *c, int B, const double *x, const double *theta, const double *y, double *expz,
+                        double *loss, double *grad)
+{
+    if (c && c->gbg) return fail(c, HQML_ERR_UNSUPPORTED, "the gate-by-gate comparator takes fp32 arrays");
+    return train_impl(c, B, x, theta, y, expz, loss, grad, 1);
 }
 
 const char *hqml_status_str(int s)

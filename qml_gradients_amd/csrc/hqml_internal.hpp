@@ -79,12 +79,13 @@ enum PassFlags : int {
 struct TilePassArgs {
     const void *psi_in;     // fwd: input state (previous pass output); bwd: saved output of this pass
     void *psi_out;          // fwd: output state
-    float *lam;             // bwd: adjoint state, fp32 complex, updated in place
-    float *e_part;          // [B][T] per-tile <O> partial sums
-    float *stat_part;       // [B][T][kSlots] per-tile gradient statistics of this pass
-    const float *rot_tf;    // [L][n][2]: tan form (k, f) of the real rotation
-    const float *dw;        // [L][n][4]: factors (f0, f1) of qubit q in D_l
-    const float *init_u;    // [B][n][4]: (u0.re, u0.im, u1.re, u1.im) layer-0 product factors
+    // Arrays below hold the compute type R of the kernel (float or double).
+    void *lam;              // bwd: adjoint state, complex R, updated in place
+    void *e_part;           // [B][T] per-tile <O> partial sums
+    void *stat_part;        // [B][T][kSlots] per-tile gradient statistics of this pass
+    const void *rot_tf;     // [L][n][2]: tan form (k, f) of the real rotation
+    const void *dw;         // [L][n][4]: factors (f0, f1) of qubit q in D_l
+    const void *init_u;     // [B][n][4]: (u0.re, u0.im, u1.re, u1.im) layer-0 product factors
     const ViewDev *view;
     int n;
     int L;
@@ -98,11 +99,12 @@ struct TilePassArgs {
 };
 
 struct SmallArgs {
-    const float *init_u;    // [B][n][4]
-    const float *rot_tf;    // [L][n][2]
-    const float *dw;        // [L][n][4]
-    float *psi_save;        // [B][2^n][2]: final state (forward mode writes, backward mode reads)
-    float *e_out;           // [B] per-sample <O> (fp32, from an fp64 in-block sum)
+    // Arrays hold the compute type R of the kernel (float or double).
+    const void *init_u;     // [B][n][4]
+    const void *rot_tf;     // [L][n][2]
+    const void *dw;         // [L][n][4]
+    void *psi_save;         // [B][2^n][2]: final state (forward mode writes, backward mode reads)
+    void *e_out;            // [B] per-sample <O> (R, from an fp64 in-block sum)
     double *stats;          // [B][L][n][3] per-sample statistics S_s at point P_l
     int n;
     int L;

@@ -51,6 +51,45 @@ __device__ __forceinline__ float4 ldu4(const float *p)
     return make_float4(ldu(p), ldu(p + 1), ldu(p + 2), ldu(p + 3));
 }
 
+__device__ __forceinline__ double ldu(const double *p)
+{
+    return *(const __attribute__((address_space(4))) double *)(p);
+}
+
+__device__ __forceinline__ double2 ldu2(const double *p)
+{
+    return make_double2(ldu(p), ldu(p + 1));
+}
+
+__device__ __forceinline__ double4 ldu4(const double *p)
+{
+    return make_double4(ldu(p), ldu(p + 1), ldu(p + 2), ldu(p + 3));
+}
+
+// The kernels are written once for the compute type R (float: the fp32 path; double:
+// the fp64-compute path).  V2<R> / V4<R> are the matching vector types.
+template <typename R>
+struct Vec;
+template <>
+struct Vec<float> {
+    using v2 = float2;
+    using v4 = float4;
+};
+template <>
+struct Vec<double> {
+    using v2 = double2;
+    using v4 = double4;
+};
+template <typename R>
+using V2 = typename Vec<R>::v2;
+template <typename R>
+using V4 = typename Vec<R>::v4;
+
+__device__ __forceinline__ float2 mk2(float a, float b) { return make_float2(a, b); }
+__device__ __forceinline__ double2 mk2(double a, double b) { return make_double2(a, b); }
+__device__ __forceinline__ float fmar(float a, float b, float c) { return fmaf(a, b, c); }
+__device__ __forceinline__ double fmar(double a, double b, double c) { return fma(a, b, c); }
+
 template <int CTRL>
 __device__ __forceinline__ float dppf(float v)
 {
@@ -58,8 +97,19 @@ __device__ __forceinline__ float dppf(float v)
                                                                   0xF, 0xF, false));
 }
 
+// The same lane permutation on a double (its two 32-bit halves moved alike).
+template <int CTRL>
+__device__ __forceinline__ double dppf(double v)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, (uint64_t)(uint32_t)lo | ((uint64_t)(uint32_t)hi << 32));
+}
+
 // Sum over the 16 lanes of a DPP row; every lane of the row ends with the row sum.
-__device__ __forceinline__ float row_sum16(float v)
+template <typename R>
+__device__ __forceinline__ R row_sum16(R v)
 {
     v += dppf<0xB1>(v);   // quad_perm [1,0,3,2]
     v += dppf<0x4E>(v);   // quad_perm [2,3,0,1]
@@ -80,36 +130,65 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h)
     return __builtin_bit_cast(float, h << 16);
 }
 
-// Storage element of a state: ST = 0 -> float2 (re, im); ST = 1 -> packed bf16 (re low, im high).
+// Storage element of a state: ST = 0 -> float2 (re, im); ST = 1 -> packed bf16 (re low,
+// im high); ST = 2 -> double2.  Loads widen to, stores round from, the compute type R.
 template <int ST>
 struct StateIO;
 
 template <>
 struct StateIO<0> {
     using elem = float2;
-    __device__ static __forceinline__ void load(const elem *p, float &re, float &im)
+    template <typename R>
+    __device__ static __forceinline__ void load(const elem *p, R &re, R &im)
     {
         const float2 v = *p;
-        re = v.x;
-        im = v.y;
+        re = (R)v.x;
+        im = (R)v.y;
     }
-    __device__ static __forceinline__ void store(elem *p, float re, float im) { *p = make_float2(re, im); }
+    template <typename R>
+    __device__ static __forceinline__ void store(elem *p, R re, R im)
+    {
+        *p = make_float2((float)re, (float)im);
+    }
 };
 
 template <>
 struct StateIO<1> {
     using elem = uint32_t;
-    __device__ static __forceinline__ void load(const elem *p, float &re, float &im)
+    template <typename R>
+    __device__ static __forceinline__ void load(const elem *p, R &re, R &im)
     {
         const uint32_t v = *p;
-        re = bf16_to_f32(v & 0xFFFFu);
-        im = bf16_to_f32(v >> 16);
+        re = (R)bf16_to_f32(v & 0xFFFFu);
+        im = (R)bf16_to_f32(v >> 16);
     }
-    __device__ static __forceinline__ void store(elem *p, float re, float im)
+    template <typename R>
+    __device__ static __forceinline__ void store(elem *p, R re, R im)
     {
-        *p = f32_to_bf16_rne(re) | (f32_to_bf16_rne(im) << 16);
+        *p = f32_to_bf16_rne((float)re) | (f32_to_bf16_rne((float)im) << 16);
     }
 };
+
+template <>
+struct StateIO<2> {
+    using elem = double2;
+    template <typename R>
+    __device__ static __forceinline__ void load(const elem *p, R &re, R &im)
+    {
+        const double2 v = *p;
+        re = (R)v.x;
+        im = (R)v.y;
+    }
+    template <typename R>
+    __device__ static __forceinline__ void store(elem *p, R re, R im)
+    {
+        *p = make_double2((double)re, (double)im);
+    }
+};
+
+// Storage element type of the adjoint state lambda: the compute type.
+template <typename R>
+constexpr int kLamIO = sizeof(R) == 4 ? 0 : 2;
 
 // ------------------------------------------------------------------ tile layouts
 
@@ -125,9 +204,10 @@ __host__ __device__ constexpr uint32_t swz(uint32_t l)
 __host__ __device__ constexpr uint32_t l1_reg(int j) { return (uint32_t)j << 4; }
 __host__ __device__ constexpr uint32_t l2_reg(int j) { return ((uint32_t)j & 3u) | (((uint32_t)j >> 2) << 9); }
 
+template <typename R>
 struct Tile {
-    float re[kRegs];
-    float im[kRegs];
+    R re[kRegs];
+    R im[kRegs];
 };
 
 __device__ __forceinline__ uint32_t l1_thread_local(int lane, int w)
@@ -140,29 +220,30 @@ __device__ __forceinline__ uint32_t l2_thread_local(int lane, int w)
     return ((uint32_t)lane << 2) | ((uint32_t)(w & 1) << 8) | ((uint32_t)(w >> 1) << 12);
 }
 
-// Move a tile between layouts through LDS (64 KB).  'from_l1' selects direction.
-__device__ __forceinline__ void transpose(Tile &t, float2 *lds, uint32_t a1, uint32_t a2, bool from_l1)
+// Move a tile between layouts through LDS (2^13 amplitudes).  'from_l1' selects direction.
+template <typename R>
+__device__ __forceinline__ void transpose(Tile<R> &t, V2<R> *lds, uint32_t a1, uint32_t a2, bool from_l1)
 {
     __syncthreads();
     if (from_l1) {
 #pragma unroll
-        for (int j = 0; j < kRegs; ++j) lds[a1 ^ swz(l1_reg(j))] = make_float2(t.re[j], t.im[j]);
+        for (int j = 0; j < kRegs; ++j) lds[a1 ^ swz(l1_reg(j))] = mk2(t.re[j], t.im[j]);
     } else {
 #pragma unroll
-        for (int j = 0; j < kRegs; ++j) lds[a2 ^ swz(l2_reg(j))] = make_float2(t.re[j], t.im[j]);
+        for (int j = 0; j < kRegs; ++j) lds[a2 ^ swz(l2_reg(j))] = mk2(t.re[j], t.im[j]);
     }
     __syncthreads();
     if (from_l1) {
 #pragma unroll
         for (int j = 0; j < kRegs; ++j) {
-            const float2 v = lds[a2 ^ swz(l2_reg(j))];
+            const V2<R> v = lds[a2 ^ swz(l2_reg(j))];
             t.re[j] = v.x;
             t.im[j] = v.y;
         }
     } else {
 #pragma unroll
         for (int j = 0; j < kRegs; ++j) {
-            const float2 v = lds[a1 ^ swz(l1_reg(j))];
+            const V2<R> v = lds[a1 ^ swz(l1_reg(j))];
             t.re[j] = v.x;
             t.im[j] = v.y;
         }
@@ -172,7 +253,8 @@ __device__ __forceinline__ void transpose(Tile &t, float2 *lds, uint32_t a1, uin
 // The same move through a 32 KB buffer.  Local position 12 is wave bit 1 in both
 // layouts, so waves 0-1 and waves 2-3 hold disjoint halves of the tile in both and
 // never exchange data; the two halves take turns in the buffer.  (swz keeps bit 12.)
-__device__ __forceinline__ void transpose_half(Tile &t, float2 *lds, uint32_t a1, uint32_t a2, bool from_l1,
+template <typename R>
+__device__ __forceinline__ void transpose_half(Tile<R> &t, V2<R> *lds, uint32_t a1, uint32_t a2, bool from_l1,
                                                int w)
 {
     constexpr uint32_t kHalf = (1u << (kTileBits - 1)) - 1u;
@@ -182,10 +264,10 @@ __device__ __forceinline__ void transpose_half(Tile &t, float2 *lds, uint32_t a1
         if ((w >> 1) == h) {
             if (from_l1) {
 #pragma unroll
-                for (int j = 0; j < kRegs; ++j) lds[(a1 ^ swz(l1_reg(j))) & kHalf] = make_float2(t.re[j], t.im[j]);
+                for (int j = 0; j < kRegs; ++j) lds[(a1 ^ swz(l1_reg(j))) & kHalf] = mk2(t.re[j], t.im[j]);
             } else {
 #pragma unroll
-                for (int j = 0; j < kRegs; ++j) lds[(a2 ^ swz(l2_reg(j))) & kHalf] = make_float2(t.re[j], t.im[j]);
+                for (int j = 0; j < kRegs; ++j) lds[(a2 ^ swz(l2_reg(j))) & kHalf] = mk2(t.re[j], t.im[j]);
             }
         }
         __syncthreads();
@@ -193,14 +275,14 @@ __device__ __forceinline__ void transpose_half(Tile &t, float2 *lds, uint32_t a1
             if (from_l1) {
 #pragma unroll
                 for (int j = 0; j < kRegs; ++j) {
-                    const float2 v = lds[(a2 ^ swz(l2_reg(j))) & kHalf];
+                    const V2<R> v = lds[(a2 ^ swz(l2_reg(j))) & kHalf];
                     t.re[j] = v.x;
                     t.im[j] = v.y;
                 }
             } else {
 #pragma unroll
                 for (int j = 0; j < kRegs; ++j) {
-                    const float2 v = lds[(a1 ^ swz(l1_reg(j))) & kHalf];
+                    const V2<R> v = lds[(a1 ^ swz(l1_reg(j))) & kHalf];
                     t.re[j] = v.x;
                     t.im[j] = v.y;
                 }
@@ -215,40 +297,42 @@ __device__ __forceinline__ void transpose_half(Tile &t, float2 *lds, uint32_t a1
 // it as a uniform scalar and fold it into the next diagonal, a statistics correction
 // or the final store.  k = 0 is the identity (used for register bits a view does not
 // rotate), so the code has no data-dependent branches.
-template <int M, bool INV>
-__device__ __forceinline__ void rot_bit(Tile &t, float k)
+template <int M, bool INV, typename R>
+__device__ __forceinline__ void rot_bit(Tile<R> &t, R k)
 {
-    const float kk = INV ? -k : k;
+    const R kk = INV ? -k : k;
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
         if (j & (1 << M)) continue;
         const int o = j | (1 << M);
-        const float ar = t.re[j], ai = t.im[j], br = t.re[o], bi = t.im[o];
-        t.re[j] = fmaf(-kk, br, ar);
-        t.im[j] = fmaf(-kk, bi, ai);
-        t.re[o] = fmaf(kk, ar, br);
-        t.im[o] = fmaf(kk, ai, bi);
+        const R ar = t.re[j], ai = t.im[j], br = t.re[o], bi = t.im[o];
+        t.re[j] = fmar(-kk, br, ar);
+        t.im[j] = fmar(-kk, bi, ai);
+        t.re[o] = fmar(kk, ar, br);
+        t.im[o] = fmar(kk, ai, bi);
     }
 }
 
 // Rotation coefficients of the register bits for one layer.
+template <typename R>
 struct RotCoef {
-    float k[5];
-    float F;         // product of the scale factors of the rotated bits
+    R k[5];
+    R F;         // product of the scale factors of the rotated bits
 };
 
 // rot_tf[l][q] = (k, f).  Bits outside regmask get k = 0, f = 1 (identity).
-__device__ __forceinline__ RotCoef load_coef(const float *rot_tf, int n, int layer, const int *qpos_to_q,
-                                             uint32_t regmask)
+template <typename R>
+__device__ __forceinline__ RotCoef<R> load_coef(const R *rot_tf, int n, int layer, const int *qpos_to_q,
+                                                uint32_t regmask)
 {
-    RotCoef rc;
-    rc.F = 1.f;
+    RotCoef<R> rc;
+    rc.F = (R)1;
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
-        rc.k[m] = 0.f;
+        rc.k[m] = (R)0;
         if (regmask & (1u << m)) {
             const int q = qpos_to_q[m];
-            const float2 kf = ldu2(rot_tf + ((size_t)layer * n + q) * 2);
+            const V2<R> kf = ldu2(rot_tf + ((size_t)layer * n + q) * 2);
             rc.k[m] = kf.x;
             rc.F *= kf.y;
         }
@@ -256,8 +340,8 @@ __device__ __forceinline__ RotCoef load_coef(const float *rot_tf, int n, int lay
     return rc;
 }
 
-template <bool INV>
-__device__ __forceinline__ void rot_layer(Tile &t, const RotCoef &rc)
+template <bool INV, typename R>
+__device__ __forceinline__ void rot_layer(Tile<R> &t, const RotCoef<R> &rc)
 {
     rot_bit<0, INV>(t, rc.k[0]);
     rot_bit<1, INV>(t, rc.k[1]);
@@ -266,14 +350,15 @@ __device__ __forceinline__ void rot_layer(Tile &t, const RotCoef &rc)
     rot_bit<4, INV>(t, rc.k[4]);
 }
 
-template <bool INV>
-__device__ __forceinline__ void rot_layer2(Tile &a, Tile &b, const RotCoef &rc)
+template <bool INV, typename R>
+__device__ __forceinline__ void rot_layer2(Tile<R> &a, Tile<R> &b, const RotCoef<R> &rc)
 {
     rot_layer<INV>(a, rc);
     rot_layer<INV>(b, rc);
 }
 
-__device__ __forceinline__ void scale_tile(Tile &t, float s)
+template <typename R>
+__device__ __forceinline__ void scale_tile(Tile<R> &t, R s)
 {
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
@@ -287,22 +372,22 @@ __device__ __forceinline__ void scale_tile(Tile &t, float s)
 //   Im<lam|Y_q|psi> = sum Re(conj(l_o) p_j) - Re(conj(l_j) p_o)
 // written as chains of plain FMAs into separate positive / negative accumulators
 // (no negated operand copies).
-template <int M>
-__device__ __forceinline__ void xy_stats(const Tile &p, const Tile &l, float &sx, float &sy)
+template <int M, typename R>
+__device__ __forceinline__ void xy_stats(const Tile<R> &p, const Tile<R> &l, R &sx, R &sy)
 {
-    float xp = 0.f, xn = 0.f, yp = 0.f, yn = 0.f;
+    R xp = 0, xn = 0, yp = 0, yn = 0;
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
         if (j & (1 << M)) continue;
         const int o = j | (1 << M);
-        xp = fmaf(l.re[j], p.im[o], xp);
-        xp = fmaf(l.re[o], p.im[j], xp);
-        xn = fmaf(l.im[j], p.re[o], xn);
-        xn = fmaf(l.im[o], p.re[j], xn);
-        yp = fmaf(l.re[o], p.re[j], yp);
-        yp = fmaf(l.im[o], p.im[j], yp);
-        yn = fmaf(l.re[j], p.re[o], yn);
-        yn = fmaf(l.im[j], p.im[o], yn);
+        xp = fmar(l.re[j], p.im[o], xp);
+        xp = fmar(l.re[o], p.im[j], xp);
+        xn = fmar(l.im[j], p.re[o], xn);
+        xn = fmar(l.im[o], p.re[j], xn);
+        yp = fmar(l.re[o], p.re[j], yp);
+        yp = fmar(l.im[o], p.im[j], yp);
+        yn = fmar(l.re[j], p.re[o], yn);
+        yn = fmar(l.im[j], p.im[o], yn);
     }
     sx = xp - xn;
     sy = yp - yn;
@@ -310,7 +395,8 @@ __device__ __forceinline__ void xy_stats(const Tile &p, const Tile &l, float &sx
 
 // Row sums of three independent values, interleaved so that no DPP step waits on
 // the one just before it.
-__device__ __forceinline__ void row_sum16x3(float &a, float &b, float &c)
+template <typename R>
+__device__ __forceinline__ void row_sum16x3(R &a, R &b, R &c)
 {
     a += dppf<0xB1>(a);
     b += dppf<0xB1>(b);
@@ -328,7 +414,8 @@ __device__ __forceinline__ void row_sum16x3(float &a, float &b, float &c)
 
 // Reduce the three statistics of one qubit over the workgroup into the LDS stat
 // area (16 row partials per slot, slots base .. base+2).
-__device__ __forceinline__ void stat_out3(float x, float y, float z, float *lds_stat, int base, int lane, int w)
+template <typename R>
+__device__ __forceinline__ void stat_out3(R x, R y, R z, R *lds_stat, int base, int lane, int w)
 {
     row_sum16x3(x, y, z);
     if ((lane & 15) == 15) {
@@ -345,11 +432,11 @@ __host__ __device__ constexpr int l2_pos(int m) { return m < 2 ? m : 7 + m; }
 
 // Z statistics of register bits LEVEL..4 from the pairwise sums left by the
 // previous level: d_m = sum_j (-1)^{bit m of j} w_j with w_j = Im(conj(l_j) p_j).
-template <int LEVEL>
-__device__ __forceinline__ void z_fold(float *wv, float *dz)
+template <int LEVEL, typename R>
+__device__ __forceinline__ void z_fold(R *wv, R *dz)
 {
     constexpr int cnt = kRegs >> LEVEL;
-    float d = 0.f;
+    R d = 0;
 #pragma unroll
     for (int k = 0; k < cnt / 2; ++k) {
         d += wv[2 * k] - wv[2 * k + 1];
@@ -363,24 +450,24 @@ __device__ __forceinline__ void z_fold(float *wv, float *dz)
 // view does not rotate land in slots nobody reads.  'corr' is the uniform factor
 // (product of the tracked scales of psi and lambda) that turns the stored-state
 // statistics into those of the true states.
-template <bool L2>
-__device__ __forceinline__ void stats_visit(const Tile &p, const Tile &l, int sel, float *lds_stat, int lane,
-                                            int w, float corr)
+template <bool L2, typename R>
+__device__ __forceinline__ void stats_visit(const Tile<R> &p, const Tile<R> &l, int sel, R *lds_stat, int lane,
+                                            int w, R corr)
 {
     // level 0 folded while forming w, so only 16 partial sums are live
-    float wv[kRegs / 2];
-    float dz[5];
-    float d0 = 0.f;
+    R wv[kRegs / 2];
+    R dz[5];
+    R d0 = 0;
 #pragma unroll
     for (int k = 0; k < kRegs / 2; ++k) {
-        const float w0 = fmaf(l.re[2 * k], p.im[2 * k], -l.im[2 * k] * p.re[2 * k]);
-        const float w1 = fmaf(l.re[2 * k + 1], p.im[2 * k + 1], -l.im[2 * k + 1] * p.re[2 * k + 1]);
+        const R w0 = fmar(l.re[2 * k], p.im[2 * k], -l.im[2 * k] * p.re[2 * k]);
+        const R w1 = fmar(l.re[2 * k + 1], p.im[2 * k + 1], -l.im[2 * k + 1] * p.re[2 * k + 1]);
         d0 += w0 - w1;
         wv[k] = w0 + w1;
     }
     dz[0] = d0;
     z_fold<1>(wv, dz);
-    float sx, sy;
+    R sx, sy;
 #define HQML_STAT_BIT(M)                                                        \
     {                                                                           \
         xy_stats<M>(p, l, sx, sy);                                              \
@@ -400,42 +487,49 @@ __device__ __forceinline__ float2 cmul(float2 a, float2 b)
     return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
 }
 
+__device__ __forceinline__ double2 cmul(double2 a, double2 b)
+{
+    return make_double2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+
 // Per-thread factor tables of the diagonal D_l in layout L2:
 // D(i) = Plo[j & 3] * Phi[j >> 2] for register j of this thread.  dw[l][q] holds the
 // factor (f0, f1) of qubit q for bit value 0 / 1; CZ signs between register and
 // fixed qubits are folded into the register factors, signs between two register
 // qubits of the same table into its entries (the planner keeps the two tables'
 // qubits non-adjacent).
+template <typename R>
 struct DiagTables {
-    float2 lo[4];
-    float2 hi[8];
+    V2<R> lo[4];
+    V2<R> hi[8];
 };
 
-__device__ __forceinline__ DiagTables diag_tables(const float *dw, int n, int layer, const int *rq,
-                                                  uint32_t fixed_bits)
+template <typename R>
+__device__ __forceinline__ DiagTables<R> diag_tables(const R *dw, int n, int layer, const int *rq,
+                                                     uint32_t fixed_bits)
 {
-    const float4 *wl = reinterpret_cast<const float4 *>(dw) + (size_t)layer * n;
+    const V4<R> *wl = reinterpret_cast<const V4<R> *>(dw) + (size_t)layer * n;
     uint32_t regq = 0;
 #pragma unroll
     for (int m = 0; m < 5; ++m) regq |= 1u << rq[m];
     // Thread constant: product over fixed qubits, CZ signs among fixed neighbours.
-    float2 c = make_float2(1.f, 0.f);
+    V2<R> c = mk2((R)1, (R)0);
     for (int q = 0; q < n; ++q) {
         if (regq & (1u << q)) continue;
-        const float4 f = ldu4(reinterpret_cast<const float *>(wl + q));
-        c = cmul(c, ((fixed_bits >> q) & 1u) ? make_float2(f.z, f.w) : make_float2(f.x, f.y));
+        const V4<R> f = ldu4(reinterpret_cast<const R *>(wl + q));
+        c = cmul(c, ((fixed_bits >> q) & 1u) ? mk2(f.z, f.w) : mk2(f.x, f.y));
     }
     if (__builtin_popcount(fixed_bits & (fixed_bits >> 1)) & 1) {
         c.x = -c.x;
         c.y = -c.y;
     }
-    float2 g0[5], g1[5];
+    V2<R> g0[5], g1[5];
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
         const int q = rq[m];
-        const float4 f = ldu4(reinterpret_cast<const float *>(wl + q));
-        g0[m] = make_float2(f.x, f.y);
-        g1[m] = make_float2(f.z, f.w);
+        const V4<R> f = ldu4(reinterpret_cast<const R *>(wl + q));
+        g0[m] = mk2(f.x, f.y);
+        g1[m] = mk2(f.z, f.w);
         uint32_t nb = (fixed_bits >> (q + 1)) & 1u;
         if (q > 0) nb += (fixed_bits >> (q - 1)) & 1u;
         if (nb & 1u) {
@@ -444,16 +538,16 @@ __device__ __forceinline__ DiagTables diag_tables(const float *dw, int n, int la
         }
     }
     auto adj = [&](int a, int b) { const int d = rq[a] - rq[b]; return d == 1 || d == -1; };
-    DiagTables t;
+    DiagTables<R> t;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-        float2 v = cmul(c, cmul((a & 1) ? g1[0] : g0[0], (a & 2) ? g1[1] : g0[1]));
+        V2<R> v = cmul(c, cmul((a & 1) ? g1[0] : g0[0], (a & 2) ? g1[1] : g0[1]));
         if (a == 3 && adj(0, 1)) { v.x = -v.x; v.y = -v.y; }
         t.lo[a] = v;
     }
 #pragma unroll
     for (int h = 0; h < 8; ++h) {
-        float2 v = cmul(cmul((h & 1) ? g1[2] : g0[2], (h & 2) ? g1[3] : g0[3]), (h & 4) ? g1[4] : g0[4]);
+        V2<R> v = cmul(cmul((h & 1) ? g1[2] : g0[2], (h & 2) ? g1[3] : g0[3]), (h & 4) ? g1[4] : g0[4]);
         int flips = 0;
         if ((h & 3) == 3 && adj(2, 3)) ++flips;
         if ((h & 6) == 6 && adj(3, 4)) ++flips;
@@ -464,7 +558,8 @@ __device__ __forceinline__ DiagTables diag_tables(const float *dw, int n, int la
     return t;
 }
 
-__device__ __forceinline__ void scale_lo(DiagTables &d, float s)
+template <typename R>
+__device__ __forceinline__ void scale_lo(DiagTables<R> &d, R s)
 {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -474,27 +569,29 @@ __device__ __forceinline__ void scale_lo(DiagTables &d, float s)
 }
 
 // Apply s * D in layout L2 (s folded into the thread's factor table).
-__device__ __forceinline__ void apply_diag(Tile &t, DiagTables d, float s)
+template <typename R>
+__device__ __forceinline__ void apply_diag(Tile<R> &t, DiagTables<R> d, R s)
 {
     scale_lo(d, s);
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
-        const float2 f = cmul(d.lo[j & 3], d.hi[j >> 2]);
-        const float r = t.re[j], i = t.im[j];
+        const V2<R> f = cmul(d.lo[j & 3], d.hi[j >> 2]);
+        const R r = t.re[j], i = t.im[j];
         t.re[j] = r * f.x - i * f.y;
         t.im[j] = r * f.y + i * f.x;
     }
 }
 
 // Apply s * D^dagger to two tiles in layout L2.
-__device__ __forceinline__ void apply_diag2(Tile &a, Tile &b, DiagTables d, float s)
+template <typename R>
+__device__ __forceinline__ void apply_diag2(Tile<R> &a, Tile<R> &b, DiagTables<R> d, R s)
 {
     scale_lo(d, s);
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
-        float2 f = cmul(d.lo[j & 3], d.hi[j >> 2]);
+        V2<R> f = cmul(d.lo[j & 3], d.hi[j >> 2]);
         f.y = -f.y;
-        float r = a.re[j], i = a.im[j];
+        R r = a.re[j], i = a.im[j];
         a.re[j] = r * f.x - i * f.y;
         a.im[j] = r * f.y + i * f.x;
         r = b.re[j];
@@ -590,8 +687,8 @@ __device__ __forceinline__ uint32_t roff(const TileCtx &c, int j)
 // Global-memory access of a tile in layout L1: a workgroup-uniform 64-bit tile
 // origin plus a 32-bit byte offset (thread part + register part), which maps onto
 // the scalar-base + vector-offset addressing form.
-template <int ST>
-__device__ __forceinline__ void load_l1(Tile &t, const void *state, const TileCtx &c, uint64_t nelem)
+template <int ST, typename R>
+__device__ __forceinline__ void load_l1(Tile<R> &t, const void *state, const TileCtx &c, uint64_t nelem)
 {
     using IO = StateIO<ST>;
     constexpr uint32_t esz = sizeof(typename IO::elem);
@@ -604,8 +701,8 @@ __device__ __forceinline__ void load_l1(Tile &t, const void *state, const TileCt
     }
 }
 
-template <int ST>
-__device__ __forceinline__ void store_l1(const Tile &t, void *state, const TileCtx &c, uint64_t nelem)
+template <int ST, typename R>
+__device__ __forceinline__ void store_l1(const Tile<R> &t, void *state, const TileCtx &c, uint64_t nelem)
 {
     using IO = StateIO<ST>;
     constexpr uint32_t esz = sizeof(typename IO::elem);
@@ -619,30 +716,31 @@ __device__ __forceinline__ void store_l1(const Tile &t, void *state, const TileC
 }
 
 // Layer-0 product state in layout L1: psi(i) = prod_q u_q[bit_q(i)].
-__device__ __forceinline__ void init_l1(Tile &t, const float *init_u, const TileCtx &c, int n)
+template <typename R>
+__device__ __forceinline__ void init_l1(Tile<R> &t, const R *init_u, const TileCtx &c, int n)
 {
-    const float4 *u = reinterpret_cast<const float4 *>(init_u) + (size_t)c.sample * n;
+    const V4<R> *u = reinterpret_cast<const V4<R> *>(init_u) + (size_t)c.sample * n;
     uint32_t regq = 0;
 #pragma unroll
     for (int m = 0; m < 5; ++m) regq |= 1u << c.q1[m];
-    float2 cst = make_float2(1.f, 0.f);
+    V2<R> cst = mk2((R)1, (R)0);
     for (int q = 0; q < n; ++q) {
         if (regq & (1u << q)) continue;
-        const float4 f = ldu4(reinterpret_cast<const float *>(u + q));
-        const float2 g = ((c.fixed1 >> q) & 1u) ? make_float2(f.z, f.w) : make_float2(f.x, f.y);
+        const V4<R> f = ldu4(reinterpret_cast<const R *>(u + q));
+        const V2<R> g = ((c.fixed1 >> q) & 1u) ? mk2(f.z, f.w) : mk2(f.x, f.y);
         cst = cmul(cst, g);
     }
     t.re[0] = cst.x;
     t.im[0] = cst.y;
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
-        const float4 f = ldu4(reinterpret_cast<const float *>(u + c.q1[m]));
-        const float2 g0 = make_float2(f.x, f.y), g1 = make_float2(f.z, f.w);
+        const V4<R> f = ldu4(reinterpret_cast<const R *>(u + c.q1[m]));
+        const V2<R> g0 = mk2(f.x, f.y), g1 = mk2(f.z, f.w);
         const int half = 1 << m;
 #pragma unroll
         for (int k = 0; k < half; ++k) {
-            const float2 v = make_float2(t.re[k], t.im[k]);
-            const float2 a = cmul(v, g0), b = cmul(v, g1);
+            const V2<R> v = mk2(t.re[k], t.im[k]);
+            const V2<R> a = cmul(v, g0), b = cmul(v, g1);
             t.re[k] = a.x;
             t.im[k] = a.y;
             t.re[k + half] = b.x;
@@ -676,31 +774,34 @@ __device__ __forceinline__ uint32_t obs_mask_l2(const TileCtx &c, uint32_t S)
 }
 
 // Workgroup sum of the per-thread <O> partial -> e_part[sample][tile].
-__device__ __forceinline__ void emit_e(float e, float *lds_stat, float *e_part, const TileCtx &c, int T)
+template <typename R>
+__device__ __forceinline__ void emit_e(R e, R *lds_stat, R *e_part, const TileCtx &c, int T)
 {
     e = row_sum16(e);
     __syncthreads();
     if ((c.lane & 15) == 15) lds_stat[kSlots * 16 + c.w * 4 + (c.lane >> 4)] = e;
     __syncthreads();
     if (threadIdx.x == 0) {
-        float s = 0.f;
+        R s = 0;
         for (int k = 0; k < 16; ++k) s += lds_stat[kSlots * 16 + k];
         e_part[(size_t)c.sample * T + c.tile] = s;
     }
 }
 
-__device__ __forceinline__ float z0_partial(const Tile &t, uint32_t zmask)
+template <typename R>
+__device__ __forceinline__ R z0_partial(const Tile<R> &t, uint32_t zmask)
 {
-    float e = 0.f;
+    R e = 0;
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
-        const float p = t.re[j] * t.re[j] + t.im[j] * t.im[j];
+        const R p = t.re[j] * t.re[j] + t.im[j] * t.im[j];
         e += ((zmask >> j) & 1u) ? -p : p;
     }
     return e;
 }
 
-__device__ __forceinline__ void seed_lambda(Tile &l, const Tile &p, uint32_t zmask)
+template <typename R>
+__device__ __forceinline__ void seed_lambda(Tile<R> &l, const Tile<R> &p, uint32_t zmask)
 {
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
@@ -713,35 +814,36 @@ __device__ __forceinline__ void seed_lambda(Tile &l, const Tile &p, uint32_t zma
 // ------------------------------------------------------------------ forward tile pass
 
 // Forward ops of one pass on a tile held in layout L1; stores the pass output.
-template <int ST>
-__device__ __forceinline__ void fwd_ops(Tile &t, const TilePassArgs &a, const TileCtx &c, float2 *lds,
-                                        float *lds_stat, uint64_t nelem)
+template <int ST, typename R>
+__device__ __forceinline__ void fwd_ops(Tile<R> &t, const TilePassArgs &a, const TileCtx &c, V2<R> *lds,
+                                        R *lds_stat, uint64_t nelem)
 {
+    const R *rot_tf = static_cast<const R *>(a.rot_tf);
     // true state = stored tile * sigma (uniform), see rot_bit
-    float sigma = 1.f;
+    R sigma = 1;
     const bool need_l2 = (a.rotA >= 0) || (a.diag >= 0) || (a.rotB >= 0);
     if (a.rotA >= 0) {
-        const RotCoef r = load_coef(a.rot_tf, a.n, a.rotA, c.q1, c.gm1);
+        const RotCoef<R> r = load_coef(rot_tf, a.n, a.rotA, c.q1, c.gm1);
         rot_layer<false>(t, r);
         sigma *= r.F;
     }
     if (need_l2) {
         transpose_half(t, lds, c.a1, c.a2, true, c.w);
         if (a.rotA >= 0) {
-            const RotCoef r = load_coef(a.rot_tf, a.n, a.rotA, c.q2, c.gm2);
+            const RotCoef<R> r = load_coef(rot_tf, a.n, a.rotA, c.q2, c.gm2);
             rot_layer<false>(t, r);
             sigma *= r.F;
         }
-        RotCoef rb1, rb2;
+        RotCoef<R> rb1, rb2;
         if (a.rotB >= 0) {
-            rb1 = load_coef(a.rot_tf, a.n, a.rotB, c.q1, c.gm1);
-            rb2 = load_coef(a.rot_tf, a.n, a.rotB, c.q2, c.gm2);
+            rb1 = load_coef(rot_tf, a.n, a.rotB, c.q1, c.gm1);
+            rb2 = load_coef(rot_tf, a.n, a.rotB, c.q2, c.gm2);
         }
         if (a.diag >= 0) {
             // fold the pending scale and the scale of the rotations that follow into D
-            const float fb = a.rotB >= 0 ? rb1.F * rb2.F : 1.f;
-            apply_diag(t, diag_tables(a.dw, a.n, a.diag, c.q2, c.fixed2), sigma * fb);
-            sigma = 1.f / fb;
+            const R fb = a.rotB >= 0 ? rb1.F * rb2.F : (R)1;
+            apply_diag(t, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2), sigma * fb);
+            sigma = (R)1 / fb;
         }
         if (a.rotB >= 0) {
             rot_layer<false>(t, rb2);
@@ -754,24 +856,25 @@ __device__ __forceinline__ void fwd_ops(Tile &t, const TilePassArgs &a, const Ti
         }
     }
     if (a.diag < 0 && (a.rotA >= 0 || a.rotB >= 0)) scale_tile(t, sigma);
-    if (a.flags & PF_EMIT_E) emit_e(z0_partial(t, obs_mask_l1(c, a.obs)), lds_stat, a.e_part, c, a.T);
+    if (a.flags & PF_EMIT_E)
+        emit_e(z0_partial(t, obs_mask_l1(c, a.obs)), lds_stat, static_cast<R *>(a.e_part), c, a.T);
     if (a.flags & PF_STORE) store_l1<ST>(t, a.psi_out, c, nelem);
 }
 
 // 37 KB of LDS and 128 VGPRs: four workgroups (16 waves) per compute unit, so one
 // workgroup's loads overlap another's rotations.
-template <int ST>
-__global__ __launch_bounds__(kThreads, 4) void k_tile_fwd(TilePassArgs a)
+template <int ST, typename R>
+__global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 4 : 2) void k_tile_fwd(TilePassArgs a)
 {
-    __shared__ float2 lds[1 << (kTileBits - 1)];
-    __shared__ float lds_stat[kSlots * 16 + 16];
+    __shared__ V2<R> lds[1 << (kTileBits - 1)];
+    __shared__ R lds_stat[kSlots * 16 + 16];
     const ViewDev &v = *a.view;
     TileCtx c;
     tile_ctx(c, v, a.T, blockIdx.x, a.sample0);
     const uint64_t nelem = 1ull << a.n;
-    Tile t;
+    Tile<R> t;
     if (a.flags & PF_INIT)
-        init_l1(t, a.init_u, c, a.n);
+        init_l1(t, static_cast<const R *>(a.init_u), c, a.n);
     else
         load_l1<ST>(t, a.psi_in, c, nelem);
     fwd_ops<ST>(t, a, c, lds, lds_stat, nelem);
@@ -779,16 +882,18 @@ __global__ __launch_bounds__(kThreads, 4) void k_tile_fwd(TilePassArgs a)
 
 // ------------------------------------------------------------------ backward tile pass
 
-__device__ __forceinline__ void zero_stats(float *lds_stat)
+template <typename R>
+__device__ __forceinline__ void zero_stats(R *lds_stat)
 {
-    for (int i = threadIdx.x; i < kSlots * 16 + 16; i += kThreads) lds_stat[i] = 0.f;
+    for (int i = threadIdx.x; i < kSlots * 16 + 16; i += kThreads) lds_stat[i] = 0;
 }
 
-__device__ __forceinline__ void flush_stats(const float *lds_stat, float *stat_part, const TileCtx &c, int T)
+template <typename R>
+__device__ __forceinline__ void flush_stats(const R *lds_stat, R *stat_part, const TileCtx &c, int T)
 {
     __syncthreads();
     if (threadIdx.x < kSlots) {
-        float s = 0.f;
+        R s = 0;
 #pragma unroll
         for (int k = 0; k < 16; ++k) s += lds_stat[threadIdx.x * 16 + k];
         stat_part[((size_t)c.sample * T + c.tile) * kSlots + threadIdx.x] = s;
@@ -805,11 +910,15 @@ enum BwdShape : int {
     BW_FUSED_INIT = 4    // one-layer circuit: product state + E + seed + layer-0 statistics
 };
 
-template <int ST, int SHAPE>
-__global__ __launch_bounds__(kThreads, 2) void k_tile_bwd(TilePassArgs a)
+template <int ST, int SHAPE, typename R>
+__global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(TilePassArgs a)
 {
-    __shared__ float2 lds[1 << kTileBits];
-    __shared__ float lds_stat[kSlots * 16 + 16];
+    __shared__ V2<R> lds[1 << kTileBits];
+    __shared__ R lds_stat[kSlots * 16 + 16];
+    const R *rot_tf = static_cast<const R *>(a.rot_tf);
+    const R *init_u = static_cast<const R *>(a.init_u);
+    R *e_part = static_cast<R *>(a.e_part);
+    constexpr int LIO = kLamIO<R>;
     const ViewDev &v = *a.view;
     TileCtx c;
     tile_ctx(c, v, a.T, blockIdx.x, a.sample0);
@@ -818,80 +927,80 @@ __global__ __launch_bounds__(kThreads, 2) void k_tile_bwd(TilePassArgs a)
     const uint64_t nelem = 1ull << a.n;
     const bool init = (a.flags & PF_INIT) != 0;
     const int la = init ? 0 : a.rotA;   // layer of the A-side statistics
-    Tile p, l;
+    Tile<R> p, l;
     // Scales: true psi = stored psi * sp, true lambda = stored lambda * sl (uniform).
-    float sl = 1.f;
+    R sl = 1;
 
     if constexpr (SHAPE == BW_FUSED_INIT) {
-        init_l1(p, a.init_u, c, a.n);
+        init_l1(p, init_u, c, a.n);
         const uint32_t zm = obs_mask_l1(c, a.obs);
-        emit_e(z0_partial(p, zm), lds_stat, a.e_part, c, a.T);
+        emit_e(z0_partial(p, zm), lds_stat, e_part, c, a.T);
         seed_lambda(l, p, zm);
-        stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, 1.f);
+        stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
         transpose(p, lds, c.a1, c.a2, true);
         transpose(l, lds, c.a1, c.a2, true);
-        stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, 1.f);
+        stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
         transpose(l, lds, c.a1, c.a2, false);
     } else if constexpr (SHAPE == BW_FUSED_LAST) {
         load_l1<ST>(p, a.psi_in, c, nelem);
-        const RotCoef r1 = load_coef(a.rot_tf, a.n, la, c.q1, c.gm1);
-        const RotCoef r2 = load_coef(a.rot_tf, a.n, la, c.q2, c.gm2);
+        const RotCoef<R> r1 = load_coef(rot_tf, a.n, la, c.q1, c.gm1);
+        const RotCoef<R> r2 = load_coef(rot_tf, a.n, la, c.q2, c.gm2);
         rot_layer<false>(p, r1);
         transpose(p, lds, c.a1, c.a2, true);
         rot_layer<false>(p, r2);
-        const float fa = r1.F * r2.F;          // psi (and the seeded lambda) carry scale fa
+        const R fa = r1.F * r2.F;              // psi (and the seeded lambda) carry scale fa
         const uint32_t zm = obs_mask_l2(c, a.obs);
-        emit_e(z0_partial(p, zm) * (fa * fa), lds_stat, a.e_part, c, a.T);
+        emit_e(z0_partial(p, zm) * (fa * fa), lds_stat, e_part, c, a.T);
         seed_lambda(l, p, zm);
         stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, fa * fa);
         rot_layer2<true>(p, l, r2);
         transpose(p, lds, c.a1, c.a2, false);
         transpose(l, lds, c.a1, c.a2, false);
-        const float s2 = fa * r2.F;
+        const R s2 = fa * r2.F;
         stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, s2 * s2);
         rot_layer<true>(l, r1);
         sl = s2 * r1.F;
     } else {
         if (a.flags & PF_STATS_ONLY)
-            init_l1(p, a.init_u, c, a.n);
+            init_l1(p, init_u, c, a.n);
         else
             load_l1<ST>(p, a.psi_in, c, nelem);
         if (a.flags & PF_SEED)
             seed_lambda(l, p, obs_mask_l1(c, a.obs));
         else
-            load_l1<0>(l, a.lam, c, nelem);
+            load_l1<LIO>(l, a.lam, c, nelem);
         if constexpr (SHAPE == BW_GENERAL || SHAPE == BW_INIT_GENERAL) {
-            const RotCoef b1 = load_coef(a.rot_tf, a.n, a.rotB, c.q1, c.gm1);
-            stats_visit<false>(p, l, 1, lds_stat, c.lane, c.w, 1.f);
+            const RotCoef<R> b1 = load_coef(rot_tf, a.n, a.rotB, c.q1, c.gm1);
+            stats_visit<false>(p, l, 1, lds_stat, c.lane, c.w, (R)1);
             rot_layer2<true>(p, l, b1);
-            const float fb1 = b1.F;
+            const R fb1 = b1.F;
             transpose(p, lds, c.a1, c.a2, true);
             transpose(l, lds, c.a1, c.a2, true);
             stats_visit<true>(p, l, 1, lds_stat, c.lane, c.w, fb1 * fb1);
-            const RotCoef b2 = load_coef(a.rot_tf, a.n, a.rotB, c.q2, c.gm2);
+            const RotCoef<R> b2 = load_coef(rot_tf, a.n, a.rotB, c.q2, c.gm2);
             rot_layer2<true>(p, l, b2);
             // both states carry scale fb = fb1 * b2.F; D^dagger removes it
-            apply_diag2(p, l, diag_tables(a.dw, a.n, a.diag, c.q2, c.fixed2), fb1 * b2.F);
-            stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, 1.f);
+            apply_diag2(p, l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2), fb1 * b2.F);
+            stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
             if constexpr (SHAPE == BW_GENERAL) {
-                const RotCoef a2 = load_coef(a.rot_tf, a.n, la, c.q2, c.gm2);
+                const RotCoef<R> a2 = load_coef(rot_tf, a.n, la, c.q2, c.gm2);
                 rot_layer2<true>(p, l, a2);
-                const float fa2 = a2.F;
+                const R fa2 = a2.F;
                 transpose(p, lds, c.a1, c.a2, false);
                 transpose(l, lds, c.a1, c.a2, false);
                 stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, fa2 * fa2);
-                const RotCoef a1 = load_coef(a.rot_tf, a.n, la, c.q1, c.gm1);
+                const RotCoef<R> a1 = load_coef(rot_tf, a.n, la, c.q1, c.gm1);
                 rot_layer<true>(l, a1);
                 sl = fa2 * a1.F;
             } else {
                 transpose(p, lds, c.a1, c.a2, false);
                 transpose(l, lds, c.a1, c.a2, false);
-                stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, 1.f);
+                stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
             }
         } else if constexpr (SHAPE == BW_ROTA) {
-            const RotCoef a1 = load_coef(a.rot_tf, a.n, la, c.q1, c.gm1);
-            const RotCoef a2 = load_coef(a.rot_tf, a.n, la, c.q2, c.gm2);
-            stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, 1.f);
+            const RotCoef<R> a1 = load_coef(rot_tf, a.n, la, c.q1, c.gm1);
+            const RotCoef<R> a2 = load_coef(rot_tf, a.n, la, c.q2, c.gm2);
+            stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
             rot_layer2<true>(p, l, a1);
             transpose(p, lds, c.a1, c.a2, true);
             transpose(l, lds, c.a1, c.a2, true);
@@ -900,34 +1009,32 @@ __global__ __launch_bounds__(kThreads, 2) void k_tile_bwd(TilePassArgs a)
             transpose(l, lds, c.a1, c.a2, false);
             sl = a1.F * a2.F;
         } else {   // BW_L0
-            stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, 1.f);
+            stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
             transpose(p, lds, c.a1, c.a2, true);
             transpose(l, lds, c.a1, c.a2, true);
-            stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, 1.f);
+            stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
             if (a.flags & PF_STATS_ONLY) {
-                flush_stats(lds_stat, a.stat_part, c, a.T);
+                flush_stats(lds_stat, static_cast<R *>(a.stat_part), c, a.T);
                 return;
             }
             transpose(l, lds, c.a1, c.a2, false);
         }
     }
-    if (sl != 1.f) scale_tile(l, sl);
-    store_l1<0>(l, a.lam, c, nelem);
-    flush_stats(lds_stat, a.stat_part, c, a.T);
+    if (sl != (R)1) scale_tile(l, sl);
+    store_l1<LIO>(l, a.lam, c, nelem);
+    flush_stats(lds_stat, static_cast<R *>(a.stat_part), c, a.T);
 }
-
-template __global__ void k_tile_fwd<0>(TilePassArgs);
-template __global__ void k_tile_fwd<1>(TilePassArgs);
 
 // ------------------------------------------------------------------ small circuits (n <= 13)
 
 // D_l of amplitude i: CZ-chain sign times the per-qubit factors f0 / f1.
-__device__ __forceinline__ float2 small_diag(const float4 *wl, int n, uint32_t i)
+template <typename R>
+__device__ __forceinline__ V2<R> small_diag(const V4<R> *wl, int n, uint32_t i)
 {
-    float2 f = make_float2(1.f, 0.f);
+    V2<R> f = mk2((R)1, (R)0);
     for (int q = 0; q < n; ++q) {
-        const float4 g = wl[q];
-        f = cmul(f, ((i >> q) & 1u) ? make_float2(g.z, g.w) : make_float2(g.x, g.y));
+        const V4<R> g = wl[q];
+        f = cmul(f, ((i >> q) & 1u) ? mk2(g.z, g.w) : mk2(g.x, g.y));
     }
     if (__builtin_popcount(i & (i >> 1)) & 1) {
         f.x = -f.x;
@@ -941,51 +1048,52 @@ __device__ __forceinline__ uint32_t pair_index(uint32_t k, int q)
     return ((k >> q) << (q + 1)) | (k & ((1u << q) - 1u));
 }
 
+template <typename R>
 __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
 {
-    extern __shared__ float2 sm[];
-    __shared__ float red[3 * kSmallMaxQubits * 16 + 16];
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ R red[3 * kSmallMaxQubits * 16 + 16];
     const int n = a.n, L = a.L;
     const uint32_t N = 1u << n;
-    float2 *psi = sm;
-    float2 *lam = sm + N;
+    V2<R> *psi = reinterpret_cast<V2<R> *>(smem);
+    V2<R> *lam = psi + N;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const float2 *rtf = reinterpret_cast<const float2 *>(a.rot_tf);
-    const float4 *dw = reinterpret_cast<const float4 *>(a.dw);
-    float2 *save = reinterpret_cast<float2 *>(a.psi_save) + (size_t)b * N;
+    const V2<R> *rtf = reinterpret_cast<const V2<R> *>(a.rot_tf);
+    const V4<R> *dw = reinterpret_cast<const V4<R> *>(a.dw);
+    V2<R> *save = reinterpret_cast<V2<R> *>(a.psi_save) + (size_t)b * N;
 
     if (a.mode != 1) {
-        const float4 *u = reinterpret_cast<const float4 *>(a.init_u) + (size_t)b * n;
+        const V4<R> *u = reinterpret_cast<const V4<R> *>(a.init_u) + (size_t)b * n;
         for (uint32_t i = tid; i < N; i += kThreads) {
-            float2 v = make_float2(1.f, 0.f);
+            V2<R> v = mk2((R)1, (R)0);
             for (int q = 0; q < n; ++q) {
-                const float4 f = u[q];
-                v = cmul(v, ((i >> q) & 1u) ? make_float2(f.z, f.w) : make_float2(f.x, f.y));
+                const V4<R> f = u[q];
+                v = cmul(v, ((i >> q) & 1u) ? mk2(f.z, f.w) : mk2(f.x, f.y));
             }
             psi[i] = v;
         }
         __syncthreads();
         for (int l = 0; l + 1 < L; ++l) {
-            const float4 *wl = dw + (size_t)l * n;
-            for (uint32_t i = tid; i < N; i += kThreads) psi[i] = cmul(psi[i], small_diag(wl, n, i));
+            const V4<R> *wl = dw + (size_t)l * n;
+            for (uint32_t i = tid; i < N; i += kThreads) psi[i] = cmul(psi[i], small_diag<R>(wl, n, i));
             __syncthreads();
             for (int q = 0; q < n; ++q) {
-                const float2 tf = rtf[(size_t)(l + 1) * n + q];
-                const float2 cs = make_float2(tf.y, tf.x * tf.y);   // (cos, sin) of the rotation
+                const V2<R> tf = rtf[(size_t)(l + 1) * n + q];
+                const V2<R> cs = mk2(tf.y, tf.x * tf.y);   // (cos, sin) of the rotation
                 for (uint32_t k = tid; k < N / 2; k += kThreads) {
                     const uint32_t i = pair_index(k, q), j = i | (1u << q);
-                    const float2 x = psi[i], y = psi[j];
-                    psi[i] = make_float2(cs.x * x.x - cs.y * y.x, cs.x * x.y - cs.y * y.y);
-                    psi[j] = make_float2(cs.y * x.x + cs.x * y.x, cs.y * x.y + cs.x * y.y);
+                    const V2<R> x = psi[i], y = psi[j];
+                    psi[i] = mk2(cs.x * x.x - cs.y * y.x, cs.x * x.y - cs.y * y.y);
+                    psi[j] = mk2(cs.y * x.x + cs.x * y.x, cs.y * x.y + cs.x * y.y);
                 }
                 __syncthreads();
             }
         }
         // <O>
-        float e = 0.f;
+        R e = 0;
         for (uint32_t i = tid; i < N; i += kThreads) {
-            const float2 v = psi[i];
-            const float pr = v.x * v.x + v.y * v.y;
+            const V2<R> v = psi[i];
+            const R pr = v.x * v.x + v.y * v.y;
             e += (__builtin_popcount(i & a.obs) & 1) ? -pr : pr;
         }
         e = row_sum16(e);
@@ -994,7 +1102,7 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
         if (tid == 0) {
             double s = 0.0;
             for (int k = 0; k < 16; ++k) s += (double)red[k];
-            a.e_out[b] = (float)s;
+            static_cast<R *>(a.e_out)[b] = (R)s;
         }
         if (a.mode == 0) {
             for (uint32_t i = tid; i < N; i += kThreads) save[i] = psi[i];
@@ -1008,16 +1116,16 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
 
     // Adjoint sweep: lambda = O psi at P_{L-1}; statistics at every P_l; uncompute.
     for (uint32_t i = tid; i < N; i += kThreads) {
-        const float2 v = psi[i];
-        lam[i] = (__builtin_popcount(i & a.obs) & 1) ? make_float2(-v.x, -v.y) : v;
+        const V2<R> v = psi[i];
+        lam[i] = (__builtin_popcount(i & a.obs) & 1) ? mk2(-v.x, -v.y) : v;
     }
     __syncthreads();
     for (int l = L - 1; l >= 0; --l) {
         for (int q = 0; q < n; ++q) {
-            float sx = 0.f, sy = 0.f, sz = 0.f;
+            R sx = 0, sy = 0, sz = 0;
             for (uint32_t k = tid; k < N / 2; k += kThreads) {
                 const uint32_t i = pair_index(k, q), j = i | (1u << q);
-                const float2 pi_ = psi[i], pj = psi[j], li = lam[i], lj = lam[j];
+                const V2<R> pi_ = psi[i], pj = psi[j], li = lam[i], lj = lam[j];
                 sx += li.x * pj.y - li.y * pj.x + lj.x * pi_.y - lj.y * pi_.x;
                 sy += lj.x * pi_.x + lj.y * pi_.y - li.x * pj.x - li.y * pj.y;
                 sz += (li.x * pi_.y - li.y * pi_.x) - (lj.x * pj.y - lj.y * pj.x);
@@ -1041,23 +1149,23 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
         if (l == 0) break;
         // uncompute Ry-layer l and D_{l-1} on psi and lambda
         for (int q = 0; q < n; ++q) {
-            const float2 tf = rtf[(size_t)l * n + q];
-            const float2 cs = make_float2(tf.y, tf.x * tf.y);
+            const V2<R> tf = rtf[(size_t)l * n + q];
+            const V2<R> cs = mk2(tf.y, tf.x * tf.y);
             for (uint32_t k = tid; k < N / 2; k += kThreads) {
                 const uint32_t i = pair_index(k, q), j = i | (1u << q);
-                float2 x = psi[i], y = psi[j];
-                psi[i] = make_float2(cs.x * x.x + cs.y * y.x, cs.x * x.y + cs.y * y.y);
-                psi[j] = make_float2(-cs.y * x.x + cs.x * y.x, -cs.y * x.y + cs.x * y.y);
+                V2<R> x = psi[i], y = psi[j];
+                psi[i] = mk2(cs.x * x.x + cs.y * y.x, cs.x * x.y + cs.y * y.y);
+                psi[j] = mk2(-cs.y * x.x + cs.x * y.x, -cs.y * x.y + cs.x * y.y);
                 x = lam[i];
                 y = lam[j];
-                lam[i] = make_float2(cs.x * x.x + cs.y * y.x, cs.x * x.y + cs.y * y.y);
-                lam[j] = make_float2(-cs.y * x.x + cs.x * y.x, -cs.y * x.y + cs.x * y.y);
+                lam[i] = mk2(cs.x * x.x + cs.y * y.x, cs.x * x.y + cs.y * y.y);
+                lam[j] = mk2(-cs.y * x.x + cs.x * y.x, -cs.y * x.y + cs.x * y.y);
             }
             __syncthreads();
         }
-        const float4 *wl = dw + (size_t)(l - 1) * n;
+        const V4<R> *wl = dw + (size_t)(l - 1) * n;
         for (uint32_t i = tid; i < N; i += kThreads) {
-            float2 f = small_diag(wl, n, i);
+            V2<R> f = small_diag<R>(wl, n, i);
             f.y = -f.y;
             psi[i] = cmul(psi[i], f);
             lam[i] = cmul(lam[i], f);
@@ -1117,7 +1225,8 @@ __device__ __forceinline__ m2 m_rz(double t)
 }
 
 // zyz[(l*n+q)*6]: cos(beta/2), sin(beta/2), p.re, p.im, r.re, r.im
-__global__ void k_prep_zyz(const float *theta, int L, int n, double *zyz)
+template <typename TI>
+__global__ void k_prep_zyz(const TI *theta, int L, int n, double *zyz)
 {
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= L * n) return;
@@ -1174,8 +1283,9 @@ __global__ void k_prep_frame(const double *zyz, int L, int n, unsigned char *G)
 // H[l][q][a][s]: Pauli coefficients of diag(p)^dag G_a diag(p), G_a the generator of
 //   theta[l][q][a] moved to just after U_{l,q} (G_z = Z, G_y = Rz Y Rz^dag,
 //   G_x = Rz Ry X Ry^dag Rz^dag), with the Y and Z coefficients negated where G[l][q].
-__global__ void k_prep_tables(const float *theta, const double *zyz, const unsigned char *G, int L, int n,
-                              float *rot_tf, float *dw, double *H)
+template <typename TI, typename R>
+__global__ void k_prep_tables(const TI *theta, const double *zyz, const unsigned char *G, int L, int n,
+                              R *rot_tf, R *dw, double *H)
 {
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= L * n) return;
@@ -1186,9 +1296,9 @@ __global__ void k_prep_tables(const float *theta, const double *zyz, const unsig
     double k = x_here ? -z[0] / z[1] : z[1] / z[0];
     const double f = x_here ? z[1] : z[0];
     if (gq) k = -k;
-    rot_tf[idx * 2 + 0] = (float)k;
-    rot_tf[idx * 2 + 1] = (float)f;
-    float *d = dw + (size_t)idx * 4;
+    rot_tf[idx * 2 + 0] = (R)k;
+    rot_tf[idx * 2 + 1] = (R)f;
+    R *d = dw + (size_t)idx * 4;
     if (l + 1 < L) {
         const double *zn = zyz + (size_t)(idx + n) * 6;
         const cd w = cmk(z[2], z[3]) * cmk(zn[4], zn[5]);
@@ -1202,15 +1312,15 @@ __global__ void k_prep_tables(const float *theta, const double *zyz, const unsig
         if (q > 0) sflip ^= G[idx - 1];                 // CZ(q-1, q) conjugated by X on q-1
         if (q + 1 < n) sflip ^= G[idx + 1];             // CZ(q, q+1) conjugated by X on q+1
         if (sflip) f1 = cmk(-f1.re, -f1.im);
-        d[0] = (float)f0.re;
-        d[1] = (float)f0.im;
-        d[2] = (float)f1.re;
-        d[3] = (float)f1.im;
+        d[0] = (R)f0.re;
+        d[1] = (R)f0.im;
+        d[2] = (R)f1.re;
+        d[3] = (R)f1.im;
     } else {
-        d[0] = 1.f;
-        d[1] = 0.f;
-        d[2] = 1.f;
-        d[3] = 0.f;
+        d[0] = 1;
+        d[1] = 0;
+        d[2] = 1;
+        d[3] = 0;
     }
     const double ay = theta[idx * 3 + 1], az = theta[idx * 3 + 2];
     const m2 X = m2{{cmk(0, 0), cmk(1, 0), cmk(1, 0), cmk(0, 0)}};
@@ -1234,8 +1344,8 @@ __global__ void k_prep_tables(const float *theta, const double *zyz, const unsig
 
 // u[b][q] = Ry(beta_{0,q}) diag(r, conj r) (cos x/2, sin x/2): the layer-0 product
 // factor, with its two components swapped where the frame has an X on qubit q.
-__global__ void k_prep_init(const float *x, const double *zyz, const unsigned char *G, int B, int n,
-                            float *init_u)
+template <typename TI, typename R>
+__global__ void k_prep_init(const TI *x, const double *zyz, const unsigned char *G, int B, int n, R *init_u)
 {
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= B * n) return;
@@ -1250,11 +1360,11 @@ __global__ void k_prep_init(const float *x, const double *zyz, const unsigned ch
     const cd u0 = cmk(cb * a0.re - sb * a1.re, cb * a0.im - sb * a1.im);
     const cd u1 = cmk(sb * a0.re + cb * a1.re, sb * a0.im + cb * a1.im);
     const bool sw = G[q] != 0;
-    float *o = init_u + (size_t)idx * 4;
-    o[0] = (float)(sw ? u1.re : u0.re);
-    o[1] = (float)(sw ? u1.im : u0.im);
-    o[2] = (float)(sw ? u0.re : u1.re);
-    o[3] = (float)(sw ? u0.im : u1.im);
+    R *o = init_u + (size_t)idx * 4;
+    o[0] = (R)(sw ? u1.re : u0.re);
+    o[1] = (R)(sw ? u1.im : u0.im);
+    o[2] = (R)(sw ? u0.re : u1.re);
+    o[3] = (R)(sw ? u0.im : u1.im);
 }
 
 // ------------------------------------------------------------------ reductions (fixed order)
@@ -1263,7 +1373,8 @@ __global__ void k_prep_init(const float *x, const double *zyz, const unsigned ch
 // First stage for samples with many tiles: out[b][ch] = sum of the <O> partials of
 // tiles ch*kTileChunk .. (ch+1)*kTileChunk-1 of sample b, by a fixed-order tree.
 // Grid (T / kTileChunk, B), kTileChunk threads.
-__global__ void __launch_bounds__(kTileChunk) k_ez_chunks(const float *e_part, int T, double *out)
+template <typename P>
+__global__ void __launch_bounds__(kTileChunk) k_ez_chunks(const P *e_part, int T, double *out)
 {
     __shared__ double red[kTileChunk];
     const int nch = gridDim.x, ch = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
@@ -1277,16 +1388,17 @@ __global__ void __launch_bounds__(kTileChunk) k_ez_chunks(const float *e_part, i
 }
 
 // E_b = sum over the T per-tile (or per-chunk) partials of sample b in order; with
-// labels y also the MSE loss and dL/dE_b = 2 (E_b - y_b) / B.
-template <typename P>
-__global__ void k_ez_reduce(const P *e_part, int B, int T, const float *y, float *e_out, float *loss,
-                            double *dlde, double *e_work)
+// labels y also the MSE loss and dL/dE_b = 2 (E_b - y_b) / B.  IO is the caller's
+// array type (float or double).
+template <typename P, typename IO>
+__global__ void k_ez_reduce(const P *e_part, int B, int T, const IO *y, IO *e_out, IO *loss, double *dlde,
+                            double *e_work)
 {
     for (int b = threadIdx.x; b < B; b += blockDim.x) {
         double s = 0.0;
         for (int t = 0; t < T; ++t) s += (double)e_part[(size_t)b * T + t];
         e_work[b] = s;
-        e_out[b] = (float)s;
+        e_out[b] = (IO)s;
         if (y) dlde[b] = 2.0 * (s - (double)y[b]) / (double)B;
     }
     __syncthreads();
@@ -1296,11 +1408,12 @@ __global__ void k_ez_reduce(const P *e_part, int B, int T, const float *y, float
             const double d = e_work[b] - (double)y[b];
             acc += d * d;
         }
-        *loss = (float)(acc / (double)B);
+        *loss = (IO)(acc / (double)B);
     }
 }
 
-__global__ void k_copy_dlde(const float *src, int B, double *dlde)
+template <typename IO>
+__global__ void k_copy_dlde(const IO *src, int B, double *dlde)
 {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b < B) dlde[b] = (double)src[b];
@@ -1312,12 +1425,13 @@ __global__ void k_copy_dlde(const float *src, int B, double *dlde)
 // every fourth tile starting at i / kSlots (consecutive threads read consecutive
 // floats); the four lanes are then added in a fixed order.
 // Grid (T / kTileChunk, Bc, passes), 4 * kSlots threads.
-__global__ void __launch_bounds__(4 * kSlots) k_stats_chunks(const float *part, int Bs, int b0, int T, double *out)
+template <typename P>
+__global__ void __launch_bounds__(4 * kSlots) k_stats_chunks(const P *part, int Bs, int b0, int T, double *out)
 {
     __shared__ double red[4 * kSlots];
     const int nch = gridDim.x, ch = blockIdx.x, bi = blockIdx.y, p = blockIdx.z, Bc = gridDim.y;
     const int i = threadIdx.x, slot = i % kSlots, lane = i / kSlots;
-    const float *src = part + (((size_t)p * Bs + b0 + bi) * T + (size_t)ch * kTileChunk) * kSlots + slot;
+    const P *src = part + (((size_t)p * Bs + b0 + bi) * T + (size_t)ch * kTileChunk) * kSlots + slot;
     double acc = 0.0;
     for (int t = lane; t < kTileChunk; t += 4) acc += (double)src[(size_t)t * kSlots];
     red[i] = acc;
@@ -1349,8 +1463,8 @@ __global__ void k_stats_reduce(const P *part, const int2 *map, int Bs, int bofs,
 }
 
 // grad[l][q][a] = sum_b dLdE_b * sum_s H[l][q][a][s] * S[b][l][q][s]
-__global__ void k_grad_reduce(const double *S, const double *H, const double *dlde, int B, int L, int n,
-                              float *grad)
+template <typename IO>
+__global__ void k_grad_reduce(const double *S, const double *H, const double *dlde, int B, int L, int n, IO *grad)
 {
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= L * n * 3) return;
@@ -1361,119 +1475,197 @@ __global__ void k_grad_reduce(const double *S, const double *H, const double *dl
         const double *sb = S + ((size_t)b * L * n + lq) * 3;
         acc += dlde[b] * (h[0] * sb[0] + h[1] * sb[1] + h[2] * sb[2]);
     }
-    grad[idx] = (float)acc;
+    grad[idx] = (IO)acc;
 }
 
 }  // namespace hqml
 
 // ------------------------------------------------------------------ launch wrappers (host)
+//
+// Type codes: io64 = the caller's arrays are double (else float); r64 = compute in
+// double (else float); storage 0 = float2, 1 = bf16 pair, 2 = double2 states.
 
 namespace hqml {
 
-hipError_t launch_prep(const float *theta, const float *x, int L, int n, int B, double *zyz, unsigned char *G,
-                       float *rot_tf, float *dw, double *H, float *init_u, hipStream_t s)
+template <typename TI, typename R>
+static void prep_typed(const void *theta, const void *x, int L, int n, int B, double *zyz, unsigned char *G,
+                       void *rot_tf, void *dw, double *H, void *init_u, hipStream_t s)
 {
     const int ln = L * n;
-    k_prep_zyz<<<(ln + 127) / 128, 128, 0, s>>>(theta, L, n, zyz);
+    k_prep_zyz<TI><<<(ln + 127) / 128, 128, 0, s>>>(static_cast<const TI *>(theta), L, n, zyz);
     k_prep_frame<<<1, 64, 0, s>>>(zyz, L, n, G);
-    k_prep_tables<<<(ln + 127) / 128, 128, 0, s>>>(theta, zyz, G, L, n, rot_tf, dw, H);
-    if (B > 0) k_prep_init<<<(B * n + 127) / 128, 128, 0, s>>>(x, zyz, G, B, n, init_u);
+    k_prep_tables<TI, R><<<(ln + 127) / 128, 128, 0, s>>>(static_cast<const TI *>(theta), zyz, G, L, n,
+                                                           static_cast<R *>(rot_tf), static_cast<R *>(dw), H);
+    if (B > 0)
+        k_prep_init<TI, R><<<(B * n + 127) / 128, 128, 0, s>>>(static_cast<const TI *>(x), zyz, G, B, n,
+                                                               static_cast<R *>(init_u));
+}
+
+hipError_t launch_prep(const void *theta, const void *x, int io64, int L, int n, int B, double *zyz,
+                       unsigned char *G, void *rot_tf, void *dw, double *H, void *init_u, int r64, hipStream_t s)
+{
+    if (io64) {
+        if (r64)
+            prep_typed<double, double>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, s);
+        else
+            prep_typed<double, float>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, s);
+    } else {
+        if (r64)
+            prep_typed<float, double>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, s);
+        else
+            prep_typed<float, float>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, s);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_tile_fwd(const TilePassArgs &a, int B, int storage, hipStream_t s)
+hipError_t launch_tile_fwd(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s)
 {
     const dim3 grid((unsigned)(B * a.T));
-    if (storage == 1)
-        k_tile_fwd<1><<<grid, kThreads, 0, s>>>(a);
-    else
-        k_tile_fwd<0><<<grid, kThreads, 0, s>>>(a);
+    if (r64) {
+        if (storage == 2)
+            k_tile_fwd<2, double><<<grid, kThreads, 0, s>>>(a);
+        else
+            k_tile_fwd<0, double><<<grid, kThreads, 0, s>>>(a);
+    } else {
+        if (storage == 1)
+            k_tile_fwd<1, float><<<grid, kThreads, 0, s>>>(a);
+        else
+            k_tile_fwd<0, float><<<grid, kThreads, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
-template <int ST>
+template <int ST, typename R>
 static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s)
 {
     if (a.flags & PF_FUSED) {
         if (a.flags & PF_INIT)
-            k_tile_bwd<ST, BW_FUSED_INIT><<<grid, kThreads, 0, s>>>(a);
+            k_tile_bwd<ST, BW_FUSED_INIT, R><<<grid, kThreads, 0, s>>>(a);
         else
-            k_tile_bwd<ST, BW_FUSED_LAST><<<grid, kThreads, 0, s>>>(a);
+            k_tile_bwd<ST, BW_FUSED_LAST, R><<<grid, kThreads, 0, s>>>(a);
     } else if (a.rotB >= 0) {
         if (a.flags & PF_INIT)
-            k_tile_bwd<ST, BW_INIT_GENERAL><<<grid, kThreads, 0, s>>>(a);
+            k_tile_bwd<ST, BW_INIT_GENERAL, R><<<grid, kThreads, 0, s>>>(a);
         else
-            k_tile_bwd<ST, BW_GENERAL><<<grid, kThreads, 0, s>>>(a);
+            k_tile_bwd<ST, BW_GENERAL, R><<<grid, kThreads, 0, s>>>(a);
     } else if (a.rotA >= 0 && !(a.flags & (PF_INIT | PF_STATS_ONLY))) {
-        k_tile_bwd<ST, BW_ROTA><<<grid, kThreads, 0, s>>>(a);
+        k_tile_bwd<ST, BW_ROTA, R><<<grid, kThreads, 0, s>>>(a);
     } else {
-        k_tile_bwd<ST, BW_L0><<<grid, kThreads, 0, s>>>(a);
+        k_tile_bwd<ST, BW_L0, R><<<grid, kThreads, 0, s>>>(a);
     }
 }
 
-hipError_t launch_tile_bwd(const TilePassArgs &a, int B, int storage, hipStream_t s)
+hipError_t launch_tile_bwd(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s)
 {
     const dim3 grid((unsigned)(B * a.T));
-    if (storage == 1)
-        launch_bwd_shape<1>(a, grid, s);
-    else
-        launch_bwd_shape<0>(a, grid, s);
-    return hipGetLastError();
-}
-
-hipError_t configure_small(size_t shm_bytes)
-{
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_small), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)shm_bytes);
-}
-
-hipError_t launch_small(const SmallArgs &a, int B, hipStream_t s)
-{
-    const size_t shm = (size_t)2 * ((size_t)1 << a.n) * sizeof(float2);
-    k_small<<<B, kThreads, shm, s>>>(a);
-    return hipGetLastError();
-}
-
-hipError_t launch_ez_reduce(const float *e_part, int B, int T, const float *y, float *e_out, float *loss,
-                            double *dlde, double *e_work, double *chunks, hipStream_t s)
-{
-    if (T > kTileChunk) {
-        const int nch = T / kTileChunk;
-        k_ez_chunks<<<dim3((unsigned)nch, (unsigned)B), kTileChunk, 0, s>>>(e_part, T, chunks);
-        k_ez_reduce<double><<<1, 256, 0, s>>>(chunks, B, nch, y, e_out, loss, dlde, e_work);
+    if (r64) {
+        if (storage == 2)
+            launch_bwd_shape<2, double>(a, grid, s);
+        else
+            launch_bwd_shape<0, double>(a, grid, s);
     } else {
-        k_ez_reduce<float><<<1, 256, 0, s>>>(e_part, B, T, y, e_out, loss, dlde, e_work);
+        if (storage == 1)
+            launch_bwd_shape<1, float>(a, grid, s);
+        else
+            launch_bwd_shape<0, float>(a, grid, s);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_copy_dlde(const float *src, int B, double *dlde, hipStream_t s)
+hipError_t configure_small(size_t shm_bytes, int r64)
 {
-    k_copy_dlde<<<(B + 255) / 256, 256, 0, s>>>(src, B, dlde);
+    const void *f = r64 ? reinterpret_cast<const void *>(&k_small<double>)
+                        : reinterpret_cast<const void *>(&k_small<float>);
+    return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm_bytes);
+}
+
+hipError_t launch_small(const SmallArgs &a, int B, int r64, hipStream_t s)
+{
+    const size_t shm = (size_t)2 * ((size_t)1 << a.n) * (r64 ? sizeof(double2) : sizeof(float2));
+    if (r64)
+        k_small<double><<<B, kThreads, shm, s>>>(a);
+    else
+        k_small<float><<<B, kThreads, shm, s>>>(a);
     return hipGetLastError();
 }
 
-hipError_t launch_stats_reduce(const float *part, const int2 *map, int Bs, int b0, int Bc, int L, int n, int T,
-                               int pass_lo, int pass_hi, double *S, double *chunks, hipStream_t s)
+template <typename P, typename IO>
+static void ez_typed(const void *e_part, int B, int T, const void *y, void *e_out, void *loss, double *dlde,
+                     double *e_work, double *chunks, hipStream_t s)
+{
+    const IO *yy = static_cast<const IO *>(y);
+    IO *eo = static_cast<IO *>(e_out), *lo = static_cast<IO *>(loss);
+    if (T > kTileChunk) {
+        const int nch = T / kTileChunk;
+        k_ez_chunks<P><<<dim3((unsigned)nch, (unsigned)B), kTileChunk, 0, s>>>(static_cast<const P *>(e_part), T,
+                                                                               chunks);
+        k_ez_reduce<double, IO><<<1, 256, 0, s>>>(chunks, B, nch, yy, eo, lo, dlde, e_work);
+    } else {
+        k_ez_reduce<P, IO><<<1, 256, 0, s>>>(static_cast<const P *>(e_part), B, T, yy, eo, lo, dlde, e_work);
+    }
+}
+
+hipError_t launch_ez_reduce(const void *e_part, int r64, int B, int T, const void *y, void *e_out, void *loss,
+                            int io64, double *dlde, double *e_work, double *chunks, hipStream_t s)
+{
+    if (r64) {
+        if (io64)
+            ez_typed<double, double>(e_part, B, T, y, e_out, loss, dlde, e_work, chunks, s);
+        else
+            ez_typed<double, float>(e_part, B, T, y, e_out, loss, dlde, e_work, chunks, s);
+    } else {
+        if (io64)
+            ez_typed<float, double>(e_part, B, T, y, e_out, loss, dlde, e_work, chunks, s);
+        else
+            ez_typed<float, float>(e_part, B, T, y, e_out, loss, dlde, e_work, chunks, s);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_dlde(const void *src, int io64, int B, double *dlde, hipStream_t s)
+{
+    if (io64)
+        k_copy_dlde<double><<<(B + 255) / 256, 256, 0, s>>>(static_cast<const double *>(src), B, dlde);
+    else
+        k_copy_dlde<float><<<(B + 255) / 256, 256, 0, s>>>(static_cast<const float *>(src), B, dlde);
+    return hipGetLastError();
+}
+
+template <typename P>
+static void stats_typed(const void *part, const int2 *map, int Bs, int b0, int Bc, int L, int n, int T,
+                        int pass_lo, int pass_hi, double *S, double *chunks, hipStream_t s)
 {
     const size_t total = (size_t)Bc * L * n * 3;
     const unsigned grid = (unsigned)((total + 255) / 256);
     if (T > kTileChunk) {
         const int nch = T / kTileChunk;
-        k_stats_chunks<<<dim3((unsigned)nch, (unsigned)Bc, (unsigned)(pass_hi - pass_lo)), 4 * kSlots, 0, s>>>(
-            part, Bs, b0, T, chunks);
+        k_stats_chunks<P><<<dim3((unsigned)nch, (unsigned)Bc, (unsigned)(pass_hi - pass_lo)), 4 * kSlots, 0, s>>>(
+            static_cast<const P *>(part), Bs, b0, T, chunks);
         k_stats_reduce<double><<<grid, 256, 0, s>>>(chunks, map, Bc, b0, b0, Bc, L, n, nch, pass_lo, pass_hi, S);
     } else {
-        k_stats_reduce<float><<<grid, 256, 0, s>>>(part, map, Bs, 0, b0, Bc, L, n, T, pass_lo, pass_hi, S);
+        k_stats_reduce<P><<<grid, 256, 0, s>>>(static_cast<const P *>(part), map, Bs, 0, b0, Bc, L, n, T, pass_lo,
+                                               pass_hi, S);
     }
+}
+
+hipError_t launch_stats_reduce(const void *part, int r64, const int2 *map, int Bs, int b0, int Bc, int L, int n,
+                               int T, int pass_lo, int pass_hi, double *S, double *chunks, hipStream_t s)
+{
+    if (r64)
+        stats_typed<double>(part, map, Bs, b0, Bc, L, n, T, pass_lo, pass_hi, S, chunks, s);
+    else
+        stats_typed<float>(part, map, Bs, b0, Bc, L, n, T, pass_lo, pass_hi, S, chunks, s);
     return hipGetLastError();
 }
 
 hipError_t launch_grad_reduce(const double *S, const double *H, const double *dlde, int B, int L, int n,
-                              float *grad, hipStream_t s)
+                              void *grad, int io64, hipStream_t s)
 {
     const int total = L * n * 3;
-    k_grad_reduce<<<(total + 255) / 256, 256, 0, s>>>(S, H, dlde, B, L, n, grad);
+    if (io64)
+        k_grad_reduce<double><<<(total + 255) / 256, 256, 0, s>>>(S, H, dlde, B, L, n, static_cast<double *>(grad));
+    else
+        k_grad_reduce<float><<<(total + 255) / 256, 256, 0, s>>>(S, H, dlde, B, L, n, static_cast<float *>(grad));
     return hipGetLastError();
 }
 

@@ -215,30 +215,31 @@ bool make_plan(int n, int L, int ckpt_block, Plan *out, std::string *err)
     return true;
 }
 
-Workspace size_workspace(const Plan &p, int max_batch, int storage)
+Workspace size_workspace(const Plan &p, int max_batch, int storage, int compute64)
 {
     Workspace w;
     const size_t B = (size_t)std::max(max_batch, 0);
+    const size_t r = compute64 ? 8 : 4;           // bytes of the compute type
     w.state_elems = (size_t)1 << p.n;
-    const size_t elem = storage == 1 ? 4 : 8;
+    const size_t elem = storage == 1 ? 4 : storage == 2 ? 16 : 8;
     w.state_bytes = B * w.state_elems * elem;
     const size_t Ln = (size_t)p.L * p.n;
-    // tables: zyz (6 doubles), frame (1 byte), rot_tf (2 floats), dw (4 floats), H (9 doubles), statmap (int2),
-    // init_u (4 floats per sample and qubit), views, per-sample E / dL/dE / scratch, loss.
-    w.tables_bytes = Ln * (6 * 8 + 1 + 2 * 4 + 4 * 4 + 9 * 8 + 8) + B * p.n * 16 +
+    // tables: zyz (6 doubles), frame (1 byte), rot_tf (2 reals), dw (4 reals), H (9 doubles), statmap (int2),
+    // init_u (4 reals per sample and qubit), views, per-sample E / dL/dE / scratch, loss.
+    w.tables_bytes = Ln * (6 * 8 + 1 + 2 * r + 4 * r + 9 * 8 + 8) + B * p.n * 4 * r +
                      (size_t)std::max(p.V, 1) * sizeof(ViewDev) + B * (8 * 3 + 4) + 64;
     const size_t S_bytes = B * Ln * 3 * 8;
     if (p.small) {
         w.n_saved = 1;
         w.lam_bytes = 0;
-        w.state_bytes = B * w.state_elems * 8;   // final state, fp32 (on-chip path)
+        w.state_bytes = B * w.state_elems * 2 * r;   // final state in the compute type (on-chip path)
         w.part_passes = 0;
         w.part_bytes = 0;
-        w.total = w.state_bytes + w.tables_bytes + S_bytes + B * 4;
+        w.total = w.state_bytes + w.tables_bytes + S_bytes + B * r;
         return w;
     }
     const int P = p.n_fwd();
-    w.lam_bytes = B * w.state_elems * 8;
+    w.lam_bytes = B * w.state_elems * 2 * r;
     if (p.c == 0) {
         w.n_saved = P;
         w.n_ckpt = 0;
@@ -248,8 +249,8 @@ Workspace size_workspace(const Plan &p, int max_batch, int storage)
         w.n_saved = p.c + w.n_ckpt;
         w.part_passes = p.c + (int)p.stats_only.size();
     }
-    w.part_bytes = (size_t)w.part_passes * B * p.T * kSlots * 4;
-    const size_t epart = B * p.T * 4;
+    w.part_bytes = (size_t)w.part_passes * B * p.T * kSlots * r;
+    const size_t epart = B * p.T * r;
     if (p.T > kTileChunk) {
         w.tile_chunks = p.T / kTileChunk;
         w.part2_bytes = (size_t)w.part_passes * B * w.tile_chunks * kSlots * 8;

@@ -62,7 +62,9 @@ struct Workspace {
     size_t total = 0;
 };
 
-Workspace size_workspace(const Plan &p, int max_batch, int storage);
+// storage: 0 fp32, 1 bf16, 2 fp64 saved states; compute64: arithmetic (and lambda,
+// tables, partial sums) in fp64.
+Workspace size_workspace(const Plan &p, int max_batch, int storage, int compute64);
 
 // Gate-by-gate comparator: workgroups per sample of one gate kernel, and its
 // workspace (psi and lambda as fp32 states, per-gate fp64 block sums of the

@@ -1,0 +1,114 @@
+"""fp64-compute modes on the GPU vs the fp64 oracle.
+
+HQML_COMPUTE_FP64 runs the same fused kernels with double arithmetic, a double
+adjoint state and double partial sums; saved states are complex fp64 (storage
+"fp64", the full complex128 mode) or complex fp32 ("fp32", rounded once per fused
+pass).  Arrays cross the ABI as fp64 (the *_f64 entry points).
+
+Bounds: full fp64 mode, |dE| <= 1e-10 and |d grad| <= 1e-10 (absolute), six orders
+below the fp32 bounds and far above fp64 rounding over these circuit depths;
+fp32-storage mode, the fp32 bounds (its states are rounded to fp32 every pass).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import hqml_inputs
+import oracle
+from gpu_util import assert_e_close, assert_grad_close, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TOL64 = 1e-10
+
+
+def _ctx(n, L, B, **kw):
+    import qml_gradients_amd as hq
+    return hq.Context(n, L, B, compute="fp64", **kw)
+
+
+def _check64(e, g, e_ref, g_ref):
+    assert np.max(np.abs(np.asarray(e) - e_ref)) <= TOL64, np.max(np.abs(np.asarray(e) - e_ref))
+    assert np.max(np.abs(np.asarray(g) - g_ref)) <= TOL64, np.max(np.abs(np.asarray(g) - g_ref))
+
+
+@pytest.mark.parametrize("n,L,B,ckpt,mask", [(1, 1, 3, 0, 0), (4, 2, 8, 0, 0), (7, 3, 2, 0, 0b1010101),
+                                             (12, 4, 3, 0, 0), (14, 1, 2, 0, 0), (14, 3, 2, 0, 0),
+                                             (15, 4, 2, 2, 0), (16, 3, 2, 0, (1 << 15) | 3), (17, 5, 2, 0, 0),
+                                             (21, 2, 1, 0, 0)])
+def test_fp64_train_step(n, L, B, ckpt, mask):
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=800 + n + L)
+    say(f"[gpu] fp64 train_step n={n} L={L} B={B} ckpt={ckpt} mask={mask:#x}")
+    ctx = _ctx(n, L, B, storage="fp64", ckpt_block=ckpt, obs_mask=mask)
+    X, TH, Y = (torch.from_numpy(a.astype(np.float64)) for a in (x, th, y))
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(X, TH, Y))
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, mask or 1)
+    _check64(e, g, e_ref, g_ref)
+    assert abs(float(loss[0]) - loss_ref) <= TOL64
+    # forward / backward split with an arbitrary upstream derivative
+    w = np.linspace(-1.0, 1.0, B)
+    e2 = ctx.forward(X, TH).cpu().numpy()
+    g2 = ctx.backward(torch.from_numpy(w)).cpu().numpy()
+    g2_ref, _ = oracle.backward(x, th, w, mask or 1)
+    _check64(e2, g2, e_ref, g2_ref)
+    ctx.close()
+
+
+@pytest.mark.parametrize("n,L,B", [(5, 3, 2), (16, 4, 2)])
+def test_fp32_storage_fp64_compute(n, L, B):
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=900 + n)
+    say(f"[gpu] fp32 storage / fp64 compute n={n}")
+    ctx = _ctx(n, L, B, storage="fp32")
+    X, TH, Y = (torch.from_numpy(a.astype(np.float64)) for a in (x, th, y))
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(X, TH, Y))
+    ctx.close()
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
+    assert_e_close(e, e_ref, n)
+    assert_grad_close(g, g_ref)
+
+
+def test_fp64_headline_workload_sampled():
+    """hea20q100l (batch 32) in full fp64: samples 0 and 31 vs the stored oracle values."""
+    name = "hea20q100l"
+    w = hqml_inputs.WORKLOADS[name]
+    x, th, y = hqml_inputs.workload_inputs(name)
+    B = w.batch
+    X, TH = (torch.from_numpy(a.astype(np.float64)) for a in (x, th))
+    say(f"[gpu] {name} fp64 sampled")
+    ctx = _ctx(w.n_qubits, w.n_layers, B, storage="fp64")
+    e = ctx.forward(X, TH).cpu().numpy()
+    for b in (0, 31):
+        path = os.path.join(GOLDEN, f"{name}_b0_s{b}.npz")
+        if not os.path.exists(path):
+            pytest.skip("golden values not generated (python tests/golden/make_golden.py full)")
+        ref = np.load(path)
+        oh = np.zeros(B)
+        oh[b] = 1.0
+        g = ctx.backward(torch.from_numpy(oh)).cpu().numpy()
+        _check64(e[b:b + 1], g, ref["expz"], ref["grad"])
+    ctx.close()
+
+
+def test_fp64_is_deterministic_and_fp32_arrays_accepted():
+    import qml_gradients_amd as hq
+    n, L, B = 15, 3, 3
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=31)
+    X, TH, Y = (torch.from_numpy(a.astype(np.float64)) for a in (x, th, y))
+    ctx = _ctx(n, L, B, storage="fp64")
+    r1 = [t.cpu().numpy() for t in ctx.train_step(X, TH, Y)]
+    r2 = [t.cpu().numpy() for t in ctx.train_step(X, TH, Y)]
+    for a, b in zip(r1, r2):
+        assert np.array_equal(a, b)
+    # the fp32 entry point on an fp64 context: same fp64 arithmetic, fp32 results
+    e32 = torch.empty(B, device="cuda")
+    l32 = torch.empty(1, device="cuda")
+    g32 = torch.empty((L, n, 3), device="cuda")
+    xs, ts, ys = (torch.from_numpy(a).cuda() for a in (x, th, y))
+    hq.hqml_train_step(ctx.handle, B, xs.data_ptr(), ts.data_ptr(), ys.data_ptr(), e32.data_ptr(), l32.data_ptr(),
+                       g32.data_ptr())
+    assert np.array_equal(e32.cpu().numpy(), r1[0].astype(np.float32))
+    assert np.array_equal(g32.cpu().numpy(), r1[2].astype(np.float32))
+    ctx.close()

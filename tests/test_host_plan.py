@@ -31,7 +31,7 @@ def _lib():
 def test_exports_every_declared_function():
     lib = _lib()
     header = open(os.path.join(ROOT, "include", "hqml.h")).read()
-    declared = set(re.findall(r"\b(hqml_[a-z_]+)\s*\(", header))
+    declared = set(re.findall(r"\b(hqml_[a-z_0-9]+)\s*\(", header))
     assert declared == set(hq.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
@@ -70,6 +70,26 @@ def test_gate_by_gate_config_host_only():
         assert e.value.status == hq.HQML_ERR_UNSUPPORTED
     for bad in (hq.make_config(4, 1, 1, fusion=2), hq.make_config(4, 1, 70000, fusion="gate_by_gate")):
         assert hq.hqml_workspace_bytes(bad) == 0
+
+
+def test_fp64_config_host_only():
+    _lib()
+    ws32 = hq.hqml_workspace_bytes(hq.make_config(20, 10, 4))
+    ws64c = hq.hqml_workspace_bytes(hq.make_config(20, 10, 4, compute="fp64"))
+    ws64 = hq.hqml_workspace_bytes(hq.make_config(20, 10, 4, storage="fp64", compute="fp64"))
+    st = 4 * (1 << 20) * 8
+    # fp64 compute doubles lambda; fp64 storage doubles the 10 saved states
+    assert ws64c - ws32 >= st
+    assert ws64 - ws64c >= 10 * st
+    assert hq.hqml_workspace_bytes(hq.make_config(12, 3, 2, storage="fp64", compute="fp64")) > 0
+    for bad in (hq.make_config(16, 2, 1, storage="fp64"), hq.make_config(16, 2, 1, storage="bf16", compute="fp64"),
+                hq.make_config(13, 2, 1, compute="fp64"),
+                hq.make_config(16, 2, 1, compute="fp64", fusion="gate_by_gate")):
+        assert hq.hqml_workspace_bytes(bad) == 0
+        with pytest.raises(hq.HqmlError) as e:
+            hq.hqml_create(bad)
+        assert e.value.status == hq.HQML_ERR_UNSUPPORTED
+    assert hq.hqml_workspace_bytes(hq.make_config(16, 2, 1, compute=2)) == 0
 
 
 def test_workspace_scaling_checkpoint_and_bf16():
