@@ -49,27 +49,29 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(plan: dict, B: int, storage: str):
+def algorithmic_bytes(plan: dict, B: int, storage: str, compute: str = "fp32"):
     """Bytes of state each fused kernel must move at minimum (per train step).
 
     Per amplitude and sample: forward pass = read input + write output (no read
     for the product-state pass); adjoint pass = read the saved pass output + read
     lambda + write lambda (the fused last pass reads the previous output and writes
-    lambda; a layer-0 statistics pass reads lambda only).  lambda is fp32 complex
-    (8 B); saved states are 8 B (fp32) or 4 B (bf16).
+    lambda; a layer-0 statistics pass reads lambda only).  lambda is complex in the
+    compute type (8 B fp32, 16 B fp64); saved states are 8 B (fp32), 4 B (bf16) or
+    16 B (fp64).
     """
     N = 1 << plan["n"]
-    s = 4 if storage == "bf16" else 8
+    s = {"bf16": 4, "fp32": 8, "fp64": 16}[storage]
+    lb = 16 if compute == "fp64" else 8
     P = len(plan["passes"])
     fwd = bwd = 0
     for k, ps in enumerate(plan["passes"]):
         if k == P - 1:
             # fused forward+adjoint of the last pass: counted with the adjoint kernels
-            bwd += ((0 if ps["init"] else s) + 8) * N * B
+            bwd += ((0 if ps["init"] else s) + lb) * N * B
             continue
         fwd += ((0 if ps["init"] else s) + s) * N * B
-        bwd += (s + 8 + 8) * N * B
-    bwd += 8 * N * B * len(plan["stats_only"])
+        bwd += (s + lb + lb) * N * B
+    bwd += lb * N * B * len(plan["stats_only"])
     # checkpointing: every block but the last is recomputed from its checkpoint
     # (the block's last output is itself the next checkpoint, kept from the forward)
     c = plan["c"]
@@ -222,6 +224,10 @@ def main():
                     help="deep model only: time one epoch over its 1000-sample set, applying "
                          "theta -= lr * grad between steps (lr = --lr)")
     ap.add_argument("--lr", type=float, default=0.01)
+    ap.add_argument("--compute", choices=["fp32", "fp64"], default="fp32",
+                    help="arithmetic type (fp64: the fp64-compute mode, fp64 arrays)")
+    ap.add_argument("--storage", choices=["fp32", "bf16", "fp64"], default=None,
+                    help="saved-state storage (default: the workload's)")
     ap.add_argument("--gbg-steps", type=int, default=2,
                     help="timed steps of the gate-by-gate comparator on the same workload (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -249,15 +255,21 @@ def main():
         return
 
     w = hqml_inputs.WORKLOADS[args.workload]
+    if args.storage is not None or args.compute != "fp32":
+        import dataclasses
+        st = args.storage or ("fp64" if args.compute == "fp64" else w.storage)
+        w = dataclasses.replace(w, storage=st)
+    f64 = args.compute == "fp64"
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    dt = torch.float64 if f64 else torch.float32
     x, th, y = hqml_inputs.workload_inputs(args.workload)
-    X = torch.from_numpy(x).to(dev)
-    TH = torch.from_numpy(th).to(dev)
-    Y = torch.from_numpy(y).to(dev)
+    X = torch.from_numpy(x).to(dev, dt)
+    TH = torch.from_numpy(th).to(dev, dt)
+    Y = torch.from_numpy(y).to(dev, dt)
     B = X.shape[0]
     free0 = torch.cuda.mem_get_info(0)[0]
-    ctx = hq.Context(w.n_qubits, w.n_layers, B, storage=w.storage, ckpt_block=w.ckpt_block)
+    ctx = hq.Context(w.n_qubits, w.n_layers, B, storage=w.storage, ckpt_block=w.ckpt_block, compute=args.compute)
     torch.cuda.synchronize()
     memory = {"workspace_bytes": hq.hqml_workspace_bytes(ctx.cfg),
               "device_mem_delta_bytes": int(free0 - torch.cuda.mem_get_info(0)[0])}
@@ -267,13 +279,14 @@ def main():
         return
     ctx.set_overlap(args.overlap)
     plan = json.loads(hq.hqml_describe_plan(ctx.cfg))
-    expz = torch.empty(B, device=dev)
-    loss = torch.empty(1, device=dev)
-    grad = torch.empty((w.n_layers, w.n_qubits, 3), device=dev)
+    expz = torch.empty(B, device=dev, dtype=dt)
+    loss = torch.empty(1, device=dev, dtype=dt)
+    grad = torch.empty((w.n_layers, w.n_qubits, 3), device=dev, dtype=dt)
+    train = hq.hqml_train_step_f64 if f64 else hq.hqml_train_step
 
     def step():
-        hq.hqml_train_step(ctx.handle, B, X.data_ptr(), TH.data_ptr(), Y.data_ptr(), expz.data_ptr(),
-                           loss.data_ptr(), grad.data_ptr())
+        train(ctx.handle, B, X.data_ptr(), TH.data_ptr(), Y.data_ptr(), expz.data_ptr(), loss.data_ptr(),
+              grad.data_ptr())
 
     for _ in range(args.warmup):
         step()
@@ -297,7 +310,7 @@ def main():
         step()
     ms_k, cnt_k = ctx.kernel_times(reset=True)
     ctx.set_timing(False)
-    fwd_b, bwd_b = algorithmic_bytes(plan, B, w.storage)
+    fwd_b, bwd_b = algorithmic_bytes(plan, B, w.storage, args.compute)
     n_steps = args.instrumented_steps
 
     bwd_flops = algorithmic_flops_bwd(plan, B)
@@ -349,10 +362,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f64" if f64 else "f32",
         "data": "synthetic (seeded x~U[0,pi), theta~U[0,2pi), y in {-1,+1})",
         "config": {"workload": args.workload, "n_qubits": w.n_qubits, "n_layers": w.n_layers,
-                   "batch": B, "state_storage": w.storage, "ckpt_block": w.ckpt_block,
+                   "batch": B, "state_storage": w.storage, "compute": args.compute, "ckpt_block": w.ckpt_block,
                    "overlap_chunks": args.overlap, "parallelism": "single GPU"},
         "memory": memory,
         "step_state_bytes": step_bytes,
@@ -366,7 +379,7 @@ def main():
                                enumerate(["fwd_pass", "bwd_pass", "small", "other"])},
     }
     ctx.close()
-    if args.gbg_steps > 0 and w.storage == "fp32" and w.ckpt_block == 0:
+    if args.gbg_steps > 0 and w.storage == "fp32" and w.ckpt_block == 0 and not f64:
         g = gate_by_gate(w, X, TH, Y, args.gbg_steps)
         g["fused_speedup"] = round(value / g["value"], 2)
         out["gate_by_gate"] = g
