@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "hqml_internal.hpp"
 
 namespace hqml {
@@ -685,18 +687,24 @@ __device__ __forceinline__ uint32_t roff(const TileCtx &c, int j)
 }
 
 // Global-memory access of a tile in layout L1: a workgroup-uniform 64-bit tile
-// origin plus a 32-bit byte offset (thread part + register part), which maps onto
-// the scalar-base + vector-offset addressing form.
+// origin plus a byte offset (thread part + register part).  The amplitude offset
+// within a sample is below 2^29 (n <= 29), so for elements of at most 8 bytes the
+// byte offset fits 32 bits and maps onto the scalar-base + vector-offset addressing
+// form; 16-byte (fp64) elements need a 64-bit offset.
+template <uint32_t ESZ>
+using TileOff = typename std::conditional<(ESZ <= 8), uint32_t, uint64_t>::type;
+
 template <int ST, typename R>
 __device__ __forceinline__ void load_l1(Tile<R> &t, const void *state, const TileCtx &c, uint64_t nelem)
 {
     using IO = StateIO<ST>;
     constexpr uint32_t esz = sizeof(typename IO::elem);
+    using Off = TileOff<esz>;
     const char *base = reinterpret_cast<const char *>(state) + ((uint64_t)c.sample * nelem + c.tile_off) * esz;
-    const uint32_t tb = c.t1 * esz;
+    const Off tb = (Off)c.t1 * esz;
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
-        const uint32_t off = tb + roff(c, j) * esz;      // < 2^32 for n <= 29
+        const Off off = tb + (Off)roff(c, j) * esz;
         IO::load(reinterpret_cast<const typename IO::elem *>(base + off), t.re[j], t.im[j]);
     }
 }
@@ -706,11 +714,12 @@ __device__ __forceinline__ void store_l1(const Tile<R> &t, void *state, const Ti
 {
     using IO = StateIO<ST>;
     constexpr uint32_t esz = sizeof(typename IO::elem);
+    using Off = TileOff<esz>;
     char *base = reinterpret_cast<char *>(state) + ((uint64_t)c.sample * nelem + c.tile_off) * esz;
-    const uint32_t tb = c.t1 * esz;
+    const Off tb = (Off)c.t1 * esz;
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
-        const uint32_t off = tb + roff(c, j) * esz;
+        const Off off = tb + (Off)roff(c, j) * esz;
         IO::store(reinterpret_cast<typename IO::elem *>(base + off), t.re[j], t.im[j]);
     }
 }

@@ -185,3 +185,40 @@ def test_chunked_overlap_is_bitwise_identical(storage, ckpt):
         assert_e_close(outs[0][0], e_ref, n)
         assert_grad_close(outs[0][2], g_ref)
     ctx.close()
+
+
+@pytest.mark.parametrize("ckpt", [0, 2])
+def test_ragged_batches_on_one_context(ckpt):
+    """A context sized for 7 samples trains on batches of 7, 5 and 2 (the last batch
+    of an epoch is smaller); each step matches the oracle on exactly its samples."""
+    n, L, maxB = 16, 5, 7
+    x, th, y = hqml_inputs.make_inputs(n, L, maxB, seed=123)
+    ctx = _ctx(n, L, maxB, ckpt_block=ckpt)
+    for B in (7, 5, 2):
+        say(f"[gpu] ragged batch B={B} of {maxB} ckpt={ckpt}")
+        out = ctx.train_step(torch.from_numpy(x[:B]), torch.from_numpy(th), torch.from_numpy(y[:B]))
+        e, loss, g = (t.cpu().numpy() for t in out)
+        e_ref, loss_ref, g_ref = oracle.train_step(x[:B], th, y[:B])
+        assert_e_close(e, e_ref, n)
+        assert abs(float(loss[0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
+        assert_grad_close(g, g_ref)
+    ctx.close()
+
+
+def test_wide_29_qubits_fp64_light_cone():
+    """hea29q4l in full fp64 (8 GiB states, per-layer checkpoints): E and every
+    derivative equal the 4-qubit oracle's within 1e-10."""
+    name = "hea29q4l"
+    w = hqml_inputs.WORKLOADS[name]
+    x, th, y = hqml_inputs.workload_inputs(name)
+    n, L = w.n_qubits, w.n_layers
+    e_ref, loss_ref, g4 = oracle.train_step(x[:, :L], th[:, :L, :], y)
+    g_ref = np.zeros((L, n, 3))
+    g_ref[:, :L, :] = g4
+    say(f"[gpu] {name} fp64")
+    ctx = _ctx(n, L, w.batch, storage="fp64", compute="fp64", ckpt_block=w.ckpt_block)
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(*(torch.from_numpy(a.astype(np.float64))
+                                                            for a in (x, th, y))))
+    assert np.max(np.abs(e - e_ref)) <= 1e-10
+    assert np.max(np.abs(g - g_ref)) <= 1e-10
+    ctx.close()
