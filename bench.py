@@ -228,6 +228,8 @@ def main():
                     help="arithmetic type (fp64: the fp64-compute mode, fp64 arrays)")
     ap.add_argument("--storage", choices=["fp32", "bf16", "fp64"], default=None,
                     help="saved-state storage (default: the workload's)")
+    ap.add_argument("--ckpt-block", type=int, default=None,
+                    help="layers per checkpoint block (default: the workload's; 0 = keep every pass output)")
     ap.add_argument("--gbg-steps", type=int, default=2,
                     help="timed steps of the gate-by-gate comparator on the same workload (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -255,10 +257,11 @@ def main():
         return
 
     w = hqml_inputs.WORKLOADS[args.workload]
-    if args.storage is not None or args.compute != "fp32":
+    if args.storage is not None or args.compute != "fp32" or args.ckpt_block is not None:
         import dataclasses
         st = args.storage or ("fp64" if args.compute == "fp64" else w.storage)
-        w = dataclasses.replace(w, storage=st)
+        ck = w.ckpt_block if args.ckpt_block is None else args.ckpt_block
+        w = dataclasses.replace(w, storage=st, ckpt_block=ck)
     f64 = args.compute == "fp64"
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
