@@ -58,9 +58,9 @@ class Oracle:
         d = ctypes.POINTER(ctypes.c_double)
         i = ctypes.c_int
         u = ctypes.c_uint32
-        lib.oracle_forward.argtypes = [i, i, i, u, d, d, d]
-        lib.oracle_backward.argtypes = [i, i, i, u, d, d, d, d, d]
-        lib.oracle_train_step.argtypes = [i, i, i, u, d, d, d, d, d, d]
+        lib.oracle_forward.argtypes = [i, i, i, u, u, d, d, d]
+        lib.oracle_backward.argtypes = [i, i, i, u, u, d, d, d, d, d]
+        lib.oracle_train_step.argtypes = [i, i, i, u, u, d, d, d, d, d, d]
         lib.oracle_state.argtypes = [i, i, d, d, d]
         lib.oracle_max_norm_drift.argtypes = [i, i, d, d]
         lib.oracle_max_norm_drift.restype = ctypes.c_double
@@ -89,19 +89,20 @@ class Oracle:
             raise ValueError("oracle_state rejected its arguments")
         return out.view(np.complex128)
 
-    def forward(self, x, theta, zmask: int = 1) -> np.ndarray:
-        """E_b = <O> per sample, fp64 [B], O = product of Z over the qubits of zmask
-        (default Z_0).  x: [B][n], theta: [L][n][3]."""
+    def forward(self, x, theta, zmask: int = 1, xmask: int = 0) -> np.ndarray:
+        """E_b = <O> per sample, fp64 [B].  O is the Pauli string with factor Z on the
+        qubits of zmask only, X on those of xmask only and Y on those of both (default
+        Z_0).  x: [B][n], theta: [L][n][3]."""
         x = _f64(x)
         B, n = x.shape
         theta = np.ascontiguousarray(_f64(theta).reshape(-1, n, 3))
         out = np.zeros(B, dtype=np.float64)
-        rc = self.lib.oracle_forward(n, theta.shape[0], B, int(zmask), _d(x), _d(theta), _d(out))
+        rc = self.lib.oracle_forward(n, theta.shape[0], B, int(zmask), int(xmask), _d(x), _d(theta), _d(out))
         if rc != 0:
             raise ValueError("oracle_forward rejected its arguments")
         return out
 
-    def backward(self, x, theta, dLdE, zmask: int = 1):
+    def backward(self, x, theta, dLdE, zmask: int = 1, xmask: int = 0):
         """(grad [L][n][3], E [B]) for upstream derivatives dLdE [B]."""
         x = _f64(x)
         B, n = x.shape
@@ -110,12 +111,12 @@ class Oracle:
         g = _f64(dLdE).ravel()
         grad = np.zeros((L, n, 3), dtype=np.float64)
         e = np.zeros(B, dtype=np.float64)
-        rc = self.lib.oracle_backward(n, L, B, int(zmask), _d(x), _d(theta), _d(g), _d(grad), _d(e))
+        rc = self.lib.oracle_backward(n, L, B, int(zmask), int(xmask), _d(x), _d(theta), _d(g), _d(grad), _d(e))
         if rc != 0:
             raise ValueError("oracle_backward rejected its arguments")
         return grad, e
 
-    def train_step(self, x, theta, y, zmask: int = 1):
+    def train_step(self, x, theta, y, zmask: int = 1, xmask: int = 0):
         """(E [B], loss, grad [L][n][3]) for the mean-squared-error loss on <O>."""
         x = _f64(x)
         B, n = x.shape
@@ -125,8 +126,8 @@ class Oracle:
         e = np.zeros(B, dtype=np.float64)
         loss = np.zeros(1, dtype=np.float64)
         grad = np.zeros((L, n, 3), dtype=np.float64)
-        rc = self.lib.oracle_train_step(n, L, B, int(zmask), _d(x), _d(theta), _d(y), _d(e), _d(loss),
-                                        _d(grad))
+        rc = self.lib.oracle_train_step(n, L, B, int(zmask), int(xmask), _d(x), _d(theta), _d(y), _d(e),
+                                        _d(loss), _d(grad))
         if rc != 0:
             raise ValueError("oracle_train_step rejected its arguments")
         return e, float(loss[0]), grad
@@ -159,16 +160,16 @@ def state(x, theta) -> np.ndarray:
     return default().state(x, theta)
 
 
-def forward(x, theta, zmask: int = 1) -> np.ndarray:
-    return default().forward(x, theta, zmask)
+def forward(x, theta, zmask: int = 1, xmask: int = 0) -> np.ndarray:
+    return default().forward(x, theta, zmask, xmask)
 
 
-def backward(x, theta, dLdE, zmask: int = 1):
-    return default().backward(x, theta, dLdE, zmask)
+def backward(x, theta, dLdE, zmask: int = 1, xmask: int = 0):
+    return default().backward(x, theta, dLdE, zmask, xmask)
 
 
-def train_step(x, theta, y, zmask: int = 1):
-    return default().train_step(x, theta, y, zmask)
+def train_step(x, theta, y, zmask: int = 1, xmask: int = 0):
+    return default().train_step(x, theta, y, zmask, xmask)
 
 
 def max_norm_drift(x, theta) -> float:

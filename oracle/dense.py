@@ -11,7 +11,8 @@ Conventions are the same readings as the gate-by-gate oracle: qubit q is bit q
 of the amplitude index, so in a Kronecker product the factor for qubit 0 is the
 rightmost one; R_s(t) = exp(-i t s/2); encoding Ry(x_q) on |0...0>; each layer
 applies Rx, Ry, Rz to every qubit, then CZ(q, q+1) for q = 0..n-2; O = the
-Kronecker product of Z on the qubits of a mask (default: Z_0) and identities.
+Kronecker product of one Pauli matrix per qubit: Z where only the z mask has the
+qubit, X where only the x mask has it, Y where both do, I elsewhere (default Z_0).
 """
 from __future__ import annotations
 
@@ -80,23 +81,25 @@ def state(x, theta) -> np.ndarray:
     return U @ psi0
 
 
-def observable(n: int, zmask: int = 1) -> np.ndarray:
-    """Full matrix of prod_{q in zmask} Z_q."""
+def observable(n: int, zmask: int = 1, xmask: int = 0) -> np.ndarray:
+    """Full matrix of the Pauli string given by the two masks."""
     out = np.array([[1.0 + 0j]])
     for k in range(n - 1, -1, -1):
-        out = np.kron(out, PAULI["Z"] if (zmask >> k) & 1 else np.eye(2))
+        z, xb = (zmask >> k) & 1, (xmask >> k) & 1
+        f = PAULI["Y"] if (z and xb) else PAULI["Z"] if z else PAULI["X"] if xb else np.eye(2)
+        out = np.kron(out, f)
     return out
 
 
-def expz(x, theta, zmask: int = 1) -> float:
+def expz(x, theta, zmask: int = 1, xmask: int = 0) -> float:
     x = np.asarray(x, dtype=np.float64).ravel()
     n = x.size
     psi = state(x, theta)
-    O = observable(n, zmask)
+    O = observable(n, zmask, xmask)
     return float(np.real(np.vdot(psi, O @ psi)))
 
 
-def grad_expz(x, theta, zmask: int = 1) -> np.ndarray:
+def grad_expz(x, theta, zmask: int = 1, xmask: int = 0) -> np.ndarray:
     """dE/dtheta [L][n][3] by the product rule on the dense circuit unitary."""
     x = np.asarray(x, dtype=np.float64).ravel()
     n = x.size
@@ -104,7 +107,7 @@ def grad_expz(x, theta, zmask: int = 1) -> np.ndarray:
     gates = gate_list(x, theta, n)
     psi0 = np.zeros(1 << n, dtype=np.complex128)
     psi0[0] = 1.0
-    O = observable(n, zmask)
+    O = observable(n, zmask, xmask)
     # prefix[k] = G_{k-1} ... G_0 psi0 ; suffix[k] = G_{m-1} ... G_{k+1}
     prefix = [psi0]
     for g, _, _ in gates:

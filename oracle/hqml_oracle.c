@@ -24,9 +24,10 @@
  *   - encoding: Ry(x_q)|0> on every qubit, once;
  *   - layer l: on every qubit q apply Rx(theta[l][q][0]), then Ry(theta[l][q][1]),
  *     then Rz(theta[l][q][2]); then CZ(q, q+1) for q = 0..n-2 (open chain);
- *   - observable O = product of Z over the qubits in a bit mask S (bit q =
- *     qubit q; the default is S = {0}, i.e. Z on qubit 0), a diagonal case of
- *     the general O of section 1.2; loss = mean over the batch of (E_b - y_b)^2;
+ *   - observable O = a Pauli string, the general O of section 1.2 restricted to
+ *     tensor products of I, X, Y, Z: two bit masks (bit q = qubit q) give qubit
+ *     q the factor I (in neither), Z (z only), X (x only) or Y (both); the default
+ *     is z = {0}, x = {} (Z on qubit 0); loss = mean over the batch of (E_b - y_b)^2;
  *   - the factor 2 of d<psi|O|psi> is carried by the adjoint seed:
  *     lambda_M = 2 (dL/dE) O psi_M, so the section-1.2 gradient formula holds
  *     literally.
@@ -145,23 +146,36 @@ static double re_braket_1q(const cplx *lam, const cplx *phi, int n, int q, gate2
     return acc;
 }
 
-/* Eigenvalue of O = prod_{q in S} Z_q on basis state i: (-1)^(number of qubits of S set in i). */
+/* (-1)^(number of qubits of S set in basis state i): the eigenvalue of prod_{q in S} Z_q. */
 static double zs_sign(int64_t i, uint32_t zmask)
 {
     return (__builtin_popcountll((uint64_t)i & zmask) & 1) ? -1.0 : 1.0;
 }
 
-/* <O> = sum_i sign_S(i) |psi_i|^2. */
-static double expect_zs(const cplx *psi, int n, uint32_t zmask, int par)
+/* out = O psi for the Pauli string (zmask, xmask).  Each Y is i X Z on its qubit, so
+ * O = i^(#Y) X^xmask Z^zmask, and
+ *   (O psi)_i = i^(#Y) (-1)^|(i ^ xmask) & zmask| psi_(i ^ xmask). */
+static void apply_observable(const cplx *psi, cplx *out, int n, uint32_t zmask, uint32_t xmask, int par)
 {
     const int64_t dim = (int64_t)1 << n;
-    double acc = 0.0;
+    static const double _Complex ipow[4] = {1.0, I, -1.0, -I};
+    const cplx ph = ipow[__builtin_popcount(zmask & xmask) & 3];
     (void)par;
-#pragma omp parallel for if (par) schedule(static) reduction(+ : acc)
+#pragma omp parallel for if (par) schedule(static)
     for (int64_t i = 0; i < dim; ++i) {
-        const double p = creal(psi[i]) * creal(psi[i]) + cimag(psi[i]) * cimag(psi[i]);
-        acc += zs_sign(i, zmask) * p;
+        const int64_t j = i ^ (int64_t)xmask;
+        out[i] = ph * zs_sign(j, zmask) * psi[j];
     }
+}
+
+/* <psi|O|psi> (real: O is Hermitian).  scratch holds 2^n amplitudes. */
+static double expect_obs(const cplx *psi, cplx *scratch, int n, uint32_t zmask, uint32_t xmask, int par)
+{
+    const int64_t dim = (int64_t)1 << n;
+    apply_observable(psi, scratch, n, zmask, xmask, par);
+    double acc = 0.0;
+#pragma omp parallel for if (par) schedule(static) reduction(+ : acc)
+    for (int64_t i = 0; i < dim; ++i) acc += creal(conj(psi[i]) * scratch[i]);
     return acc;
 }
 
@@ -184,11 +198,12 @@ static void run_circuit(cplx *psi, int n, int L, const double *x, const double *
  * gate by gate), lam is scratch.  grad[(l*n+q)*3+a] receives dL/dtheta for
  * upstream derivative g = dL/dE. */
 static void adjoint_sample(cplx *psi, cplx *lam, int n, int L, const double *theta, uint32_t zmask,
-                           double g, double *grad, int par)
+                           uint32_t xmask, double g, double *grad, int par)
 {
     const int64_t dim = (int64_t)1 << n;
     /* lambda_M = 2 g O psi_M */
-    for (int64_t i = 0; i < dim; ++i) lam[i] = 2.0 * g * zs_sign(i, zmask) * psi[i];
+    apply_observable(psi, lam, n, zmask, xmask, par);
+    for (int64_t i = 0; i < dim; ++i) lam[i] *= 2.0 * g;
     for (int l = L - 1; l >= 0; --l) {
         /* CZ chain, in reverse order (the CZs commute; order kept for clarity). */
         for (int q = n - 2; q >= 0; --q) { apply_cz(psi, n, q, par); apply_cz(lam, n, q, par); }
@@ -275,16 +290,18 @@ double oracle_max_norm_drift(int n, int L, const double *x, const double *theta)
     return worst;
 }
 
-/* Observable masks must name qubits of the circuit; 0 is rejected. */
-static int bad_mask(int n, uint32_t zmask)
+/* Observable masks must name qubits of the circuit; the identity string is rejected. */
+static int bad_mask(int n, uint32_t zmask, uint32_t xmask)
 {
-    return zmask == 0 || (n < 32 && (zmask >> n) != 0);
+    return (zmask | xmask) == 0 || (n < 32 && ((zmask | xmask) >> n) != 0);
 }
 
 /* E_b = <psi_M|O|psi_M> for every sample.  x: [B][n], theta: [L][n][3]. */
-int oracle_forward(int n, int L, int B, uint32_t zmask, const double *x, const double *theta, double *expz)
+int oracle_forward(int n, int L, int B, uint32_t zmask, uint32_t xmask, const double *x, const double *theta,
+                   double *expz)
 {
-    if (n < 1 || n > 30 || L < 0 || B < 0 || (B > 0 && (!x || !expz)) || (L > 0 && !theta) || bad_mask(n, zmask))
+    if (n < 1 || n > 30 || L < 0 || B < 0 || (B > 0 && (!x || !expz)) || (L > 0 && !theta) ||
+        bad_mask(n, zmask, xmask))
         return -1;
     const int par = choose_par(n, B);
     const int64_t dim = (int64_t)1 << n;
@@ -292,10 +309,12 @@ int oracle_forward(int n, int L, int B, uint32_t zmask, const double *x, const d
 #pragma omp parallel for if (!par) schedule(dynamic, 1) reduction(| : err)
     for (int b = 0; b < B; ++b) {
         cplx *psi = (cplx *)malloc(sizeof(cplx) * (size_t)dim);
-        if (!psi) { err |= 1; continue; }
+        cplx *tmp = (cplx *)malloc(sizeof(cplx) * (size_t)dim);
+        if (!psi || !tmp) { free(psi); free(tmp); err |= 1; continue; }
         run_circuit(psi, n, L, x + (size_t)b * n, theta, par);
-        expz[b] = expect_zs(psi, n, zmask, par);
+        expz[b] = expect_obs(psi, tmp, n, zmask, xmask, par);
         free(psi);
+        free(tmp);
     }
     return err ? -1 : 0;
 }
@@ -303,11 +322,11 @@ int oracle_forward(int n, int L, int B, uint32_t zmask, const double *x, const d
 /* Adjoint gradient for an arbitrary upstream derivative dLdE[b]:
  * grad[(l*n+q)*3+a] = sum_b (per-sample adjoint gradient), summed in sample
  * order.  expz (optional) receives E_b. */
-int oracle_backward(int n, int L, int B, uint32_t zmask, const double *x, const double *theta,
+int oracle_backward(int n, int L, int B, uint32_t zmask, uint32_t xmask, const double *x, const double *theta,
                     const double *dLdE, double *grad, double *expz)
 {
     if (n < 1 || n > 30 || L < 0 || B < 0 || (B > 0 && (!x || !dLdE)) || (L > 0 && (!theta || !grad)) ||
-        bad_mask(n, zmask))
+        bad_mask(n, zmask, xmask))
         return -1;
     const size_t P = (size_t)L * n * 3;
     const int par = choose_par(n, B);
@@ -321,8 +340,8 @@ int oracle_backward(int n, int L, int B, uint32_t zmask, const double *x, const 
         cplx *lam = (cplx *)malloc(sizeof(cplx) * (size_t)dim);
         if (!psi || !lam) { free(psi); free(lam); err |= 1; continue; }
         run_circuit(psi, n, L, x + (size_t)b * n, theta, par);
-        if (expz) expz[b] = expect_zs(psi, n, zmask, par);
-        adjoint_sample(psi, lam, n, L, theta, zmask, dLdE[b], per + (size_t)b * P, par);
+        if (expz) expz[b] = expect_obs(psi, lam, n, zmask, xmask, par);
+        adjoint_sample(psi, lam, n, L, theta, zmask, xmask, dLdE[b], per + (size_t)b * P, par);
         free(psi);
         free(lam);
     }
@@ -338,11 +357,11 @@ int oracle_backward(int n, int L, int B, uint32_t zmask, const double *x, const 
 /* One training step with the mean-squared-error loss on <O>:
  * loss = (1/B) sum_b (E_b - y_b)^2, dL/dE_b = 2 (E_b - y_b) / B.
  * Each sample is simulated once: forward, E_b, then its adjoint sweep. */
-int oracle_train_step(int n, int L, int B, uint32_t zmask, const double *x, const double *theta,
+int oracle_train_step(int n, int L, int B, uint32_t zmask, uint32_t xmask, const double *x, const double *theta,
                       const double *y, double *expz, double *loss, double *grad)
 {
     if (n < 1 || n > 30 || L < 0 || B < 1 || !x || !y || !expz || !loss || (L > 0 && (!theta || !grad)) ||
-        bad_mask(n, zmask))
+        bad_mask(n, zmask, xmask))
         return -1;
     const size_t P = (size_t)L * n * 3;
     const int par = choose_par(n, B);
@@ -356,9 +375,9 @@ int oracle_train_step(int n, int L, int B, uint32_t zmask, const double *x, cons
         cplx *lam = (cplx *)malloc(sizeof(cplx) * (size_t)dim);
         if (!psi || !lam) { free(psi); free(lam); err |= 1; continue; }
         run_circuit(psi, n, L, x + (size_t)b * n, theta, par);
-        expz[b] = expect_zs(psi, n, zmask, par);
+        expz[b] = expect_obs(psi, lam, n, zmask, xmask, par);
         const double g = 2.0 * (expz[b] - y[b]) / (double)B;
-        adjoint_sample(psi, lam, n, L, theta, zmask, g, per + (size_t)b * P, par);
+        adjoint_sample(psi, lam, n, L, theta, zmask, xmask, g, per + (size_t)b * P, par);
         free(psi);
         free(lam);
     }

@@ -218,6 +218,47 @@ def pin_zstring_dense_and_parameter_shift(o):
     assert np.max(np.abs(gt - gb)) < 1e-13
 
 
+def pin_pauli_product_state(o):
+    """No layers, O a Pauli string: on Ry(x)|0> a qubit has <Z> = cos x, <X> = sin x
+    and <Y> = 0, and the product state makes E the product of the factors."""
+    n = 4
+    x, _ = _rand(n, 0, 3, 1000)
+    f = {"Z": np.cos, "X": np.sin, "Y": lambda v: 0.0 * v}
+    for zm, xm in ((0, 1), (0, 0b0110), (0b1001, 0b0110), (0b0001, 0b0001), (0b0100, 0b1011)):
+        ref = np.ones(x.shape[0])
+        for q in range(n):
+            z, xb = (zm >> q) & 1, (xm >> q) & 1
+            if z or xb:
+                ref = ref * f["Y" if (z and xb) else "Z" if z else "X"](x[:, q])
+        e = o.forward(x, np.zeros((0, n, 3)), zm, xm)
+        assert np.max(np.abs(e - ref)) < 1e-14, (zm, xm, e, ref)
+
+
+def pin_pauli_dense_and_parameter_shift(o):
+    """Pauli strings with X and Y factors: E and the adjoint gradient equal the dense
+    checker's (n <= 4) and the exact parameter-shift derivative (n = 5)."""
+    for n, L, zm, xm in ((1, 2, 1, 1), (2, 2, 0, 3), (3, 2, 0b101, 0b011), (4, 2, 0b0110, 0b1100)):
+        x, th = _rand(n, L, 2, 1100 + n)
+        e = o.forward(x, th, zm, xm)
+        ed = np.array([dense.expz(x[b], th, zm, xm) for b in range(2)])
+        assert np.max(np.abs(e - ed)) < 1e-12, (n, zm, xm)
+        w = np.array([0.9, -0.4])
+        g, _ = o.backward(x, th, w, zm, xm)
+        gd = sum(w[b] * dense.grad_expz(x[b], th, zm, xm) for b in range(2))
+        assert np.max(np.abs(g - gd)) < 1e-12, (n, zm, xm)
+    n, L, zm, xm = 5, 2, 0b01010, 0b11000
+    x, th = _rand(n, L, 2, 1150)
+    w = np.array([1.0, -0.7])
+    g, _ = o.backward(x, th, w, zm, xm)
+    ref = np.zeros_like(th)
+    for idx in np.ndindex(th.shape):
+        tp, tm = th.copy(), th.copy()
+        tp[idx] += math.pi / 2
+        tm[idx] -= math.pi / 2
+        ref[idx] = np.sum(w * (o.forward(x, tp, zm, xm) - o.forward(x, tm, zm, xm)) / 2)
+    assert np.max(np.abs(g - ref)) < 1e-12, np.max(np.abs(g - ref))
+
+
 ALL_PINS = [
     pin_ry_closed_form,
     pin_one_layer_closed_form,
@@ -231,4 +272,6 @@ ALL_PINS = [
     pin_train_step_is_mse,
     pin_zstring_product_state,
     pin_zstring_dense_and_parameter_shift,
+    pin_pauli_product_state,
+    pin_pauli_dense_and_parameter_shift,
 ]

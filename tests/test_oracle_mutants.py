@@ -33,11 +33,16 @@ MUTANTS = [
      "apply_1q(psi, n, q, rotation(AX_X, x[q]), par);", 0),
     ("observable_shifted_qubit", "return (__builtin_popcountll((uint64_t)i & zmask) & 1) ? -1.0 : 1.0;",
      "return (__builtin_popcountll(((uint64_t)i << 1) & zmask) & 1) ? -1.0 : 1.0;", 0),
-    ("observable_ignores_mask", "acc += zs_sign(i, zmask) * p;", "acc += zs_sign(i, 1u) * p;", 0),
-    ("seed_no_factor2", "lam[i] = 2.0 * g * zs_sign(i, zmask) * psi[i];",
-     "lam[i] = g * zs_sign(i, zmask) * psi[i];", 0),
-    ("seed_ignores_mask", "lam[i] = 2.0 * g * zs_sign(i, zmask) * psi[i];",
-     "lam[i] = 2.0 * g * zs_sign(i, 1u) * psi[i];", 0),
+    ("observable_ignores_z_mask", "out[i] = ph * zs_sign(j, zmask) * psi[j];", "out[i] = ph * zs_sign(j, 1u) * psi[j];", 0),
+    ("observable_sign_before_flip", "out[i] = ph * zs_sign(j, zmask) * psi[j];",
+     "out[i] = ph * zs_sign(i, zmask) * psi[j];", 0),
+    ("observable_no_flip", "const int64_t j = i ^ (int64_t)xmask;", "const int64_t j = i;", 0),
+    ("observable_y_phase_dropped", "const cplx ph = ipow[__builtin_popcount(zmask & xmask) & 3];",
+     "const cplx ph = 1.0;", 0),
+    ("expectation_conjugate_dropped", "acc += creal(conj(psi[i]) * scratch[i]);",
+     "acc += creal(psi[i] * scratch[i]);", 0),
+    ("seed_no_factor2", "for (int64_t i = 0; i < dim; ++i) lam[i] *= 2.0 * g;",
+     "for (int64_t i = 0; i < dim; ++i) lam[i] *= g;", 0),
     ("no_uncompute", "apply_1q(psi, n, q, dagger(u), par);", "(void)u;", 0),
     ("lambda_not_propagated", "apply_1q(lam, n, q, dagger(u), par);", "(void)u;", 0),
     ("ry_derivative_sign", "g.m[0] = -0.5 * s; g.m[1] = -0.5 * c; g.m[2] = 0.5 * c;",
