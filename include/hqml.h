@@ -88,9 +88,13 @@ typedef struct {
     void *stream;      /* hipStream_t to queue work on; NULL = the null stream */
     int fusion;        /* hqml_fusion; 0 = HQML_FUSED */
     int compute;       /* hqml_compute; 0 = HQML_COMPUTE_FP32 */
-    int obs_mask;      /* observable O = product of Z_q over the qubits q whose bit is set
-                          (bit q = qubit q, only qubits 0..n_qubits-1); 0 = Z on qubit 0.
-                          A diagonal case of the general O of section 1.2 */
+    int obs_mask;      /* observable O, a Pauli string (the general O of section 1.2 restricted
+                          to tensor products of I, X, Y, Z): qubit q (bit q) carries Z if only
+                          obs_mask has it, X if only obs_x_mask has it, Y if both do, I if
+                          neither.  Both 0 = Z on qubit 0 (the default).  Only qubits
+                          0..n_qubits-1.  With X/Y factors and n_qubits >= 14, at most 9 of
+                          them may sit on qubits >= 4 (they must fit one tile view) */
+    int obs_x_mask;
 } hqml_config;
 
 /* Device bytes hqml_create would reserve for cfg.  Host-only: makes no HIP call.

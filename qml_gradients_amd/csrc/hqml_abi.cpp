@@ -26,6 +26,7 @@ namespace hqml {
 hipError_t launch_prep(const void *theta, const void *x, int io64, int L, int n, int B, double *zyz,
                        unsigned char *G, void *rot_tf, void *dw, double *H, void *init_u, int r64, hipStream_t s);
 hipError_t launch_tile_fwd(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s);
+hipError_t launch_tile_obs(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s);
 hipError_t launch_tile_bwd(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s);
 hipError_t launch_small(const SmallArgs &a, int B, int r64, hipStream_t s);
 hipError_t configure_small(size_t shm_bytes, int r64);
@@ -41,8 +42,10 @@ hipError_t launch_gbg_zero(float2 *psi, int n, int B, hipStream_t s);
 hipError_t launch_gbg_rot(int gate, float2 *psi, int n, int B, int q, const float *ang, int ang_stride,
                           hipStream_t s);
 hipError_t launch_gbg_cz(float2 *psi, float2 *lam, int n, int B, int q, hipStream_t s);
-hipError_t launch_gbg_expz(const float2 *psi, int n, int B, uint32_t obs, float *e_part, hipStream_t s);
-hipError_t launch_gbg_seed(const float2 *psi, float2 *lam, int n, int B, uint32_t obs, hipStream_t s);
+hipError_t launch_gbg_expz(const float2 *psi, int n, int B, uint32_t obs, uint32_t obs_x, float *e_part,
+                           hipStream_t s);
+hipError_t launch_gbg_seed(const float2 *psi, float2 *lam, int n, int B, uint32_t obs, uint32_t obs_x,
+                           hipStream_t s);
 hipError_t launch_gbg_rot_adj(int gate, float2 *psi, float2 *lam, int n, int B, int q, const float *ang,
                               double *gpart, hipStream_t s);
 hipError_t launch_gbg_grad(const double *gpart, const double *dlde, int B, int n, int n_params, float *grad,
@@ -86,7 +89,8 @@ struct hqml_ctx {
     double *part2 = nullptr;    // first-stage statistics sums (samples with many tiles)
     double *epart2 = nullptr;   // first-stage <O> sums
     float *loss_tmp = nullptr;
-    uint32_t obs = 1;            // observable: product of Z over the qubits of this mask
+    uint32_t obs = 1;            // observable: Z part of the Pauli string
+    uint32_t obs_x = 0;          // observable: X part (Y where both); nonzero adds an observable pass
     // gate-by-gate comparator
     bool gbg = false;
     float *gbg_psi = nullptr;    // [B][2^n] complex fp32
@@ -200,6 +204,7 @@ TilePassArgs base_args(hqml_ctx *c)
     a.L = c->plan.L;
     a.T = c->plan.T;
     a.obs = c->obs;
+    a.obs_x = c->obs_x;
     return a;
 }
 
@@ -282,8 +287,9 @@ int check_config(const hqml_config *cfg, Plan *plan, std::string *err)
         *err = "fp64 compute supports n_qubits <= 12 (whole circuit per workgroup) or >= 14 (tiles)";
         return HQML_ERR_UNSUPPORTED;
     }
-    if (cfg->obs_mask < 0 || (cfg->n_qubits >= 1 && cfg->n_qubits < 31 && (cfg->obs_mask >> cfg->n_qubits) != 0)) {
-        *err = "obs_mask may only name qubits 0..n_qubits-1";
+    if (cfg->obs_mask < 0 || cfg->obs_x_mask < 0 ||
+        (cfg->n_qubits >= 1 && cfg->n_qubits < 31 && ((cfg->obs_mask | cfg->obs_x_mask) >> cfg->n_qubits) != 0)) {
+        *err = "obs_mask and obs_x_mask may only name qubits 0..n_qubits-1";
         return HQML_ERR_ARG;
     }
     if (cfg->fusion != HQML_FUSED && cfg->fusion != HQML_GATE_BY_GATE) {
@@ -300,6 +306,10 @@ int check_config(const hqml_config *cfg, Plan *plan, std::string *err)
         return HQML_ERR_UNSUPPORTED;
     }
     if (!make_plan(cfg->n_qubits, cfg->n_layers, cfg->ckpt_block, plan, err)) return HQML_ERR_ARG;
+    if (cfg->obs_x_mask != 0 && !plan->small && cfg->fusion == HQML_FUSED) {
+        ViewDev ov;
+        if (!make_obs_view(cfg->n_qubits, (uint32_t)cfg->obs_x_mask, &ov, err)) return HQML_ERR_UNSUPPORTED;
+    }
     if (!plan->small && (size_t)cfg->max_batch * plan->T > 0x7FFFFFFFull) {
         *err = "max_batch * tiles per sample exceeds the grid limit";
         return HQML_ERR_ARG;
@@ -315,7 +325,7 @@ int tile_forward_sweep(hqml_ctx *c, hipStream_t st, Span sp, bool fuse_last)
     const int P = pl.n_fwd();
     const int last = fuse_last ? P - 1 : P;
     for (int p = 0; p < last; ++p) {
-        const int rc = fwd_pass(c, st, sp, p, (!fuse_last && p == P - 1) ? PF_EMIT_E : 0);
+        const int rc = fwd_pass(c, st, sp, p, (!fuse_last && p == P - 1 && !c->obs_x) ? PF_EMIT_E : 0);
         if (rc) return rc;
     }
     return HQML_OK;
@@ -324,8 +334,30 @@ int tile_forward_sweep(hqml_ctx *c, hipStream_t st, Span sp, bool fuse_last)
 // Backward sweep of the tile path for one chunk.  The last forward pass is either
 // fused here (train_step: forward ops, E, seed, adjoint ops in one kernel) or seeded
 // from its saved output.  Ends with the per-sample statistics of the chunk in S.
-int tile_backward_sweep(hqml_ctx *c, hipStream_t st, Span sp, bool fused_last)
+// How the backward sweep starts.
+enum LastPass {
+    SEED_FROM_SAVED = 0,   // lambda = O psi formed in the first adjoint pass from the saved final state
+    FUSED_LAST = 1,        // last forward pass, E, seed and first adjoint pass in one kernel
+    LAMBDA_READY = 2       // lambda already holds O psi (written by the observable pass)
+};
+
+// Observable pass of a Pauli string with X/Y factors on the final state of a chunk.
+int obs_pass(hqml_ctx *c, hipStream_t st, Span sp, int flags)
 {
+    const Plan &pl = c->plan;
+    TilePassArgs a = base_args(c);
+    a.view = c->views + pl.V;
+    a.psi_in = pass_out(c, pl.n_fwd() - 1);
+    a.rotA = a.diag = a.rotB = -1;
+    a.flags = flags;
+    a.sample0 = sp.b0;
+    return run_on(c, st, HQML_K_OTHER, "observable pass launch",
+                  [&] { return launch_tile_obs(a, sp.bc, c->cfg.storage, c->r64, st); });
+}
+
+int tile_backward_sweep(hqml_ctx *c, hipStream_t st, Span sp, int start)
+{
+    const int last_flags = start == FUSED_LAST ? (PF_FUSED | PF_EMIT_E) : start == SEED_FROM_SAVED ? PF_SEED : 0;
     const Plan &pl = c->plan;
     const int P = pl.n_fwd();
     const int nso = (int)pl.stats_only.size();
@@ -340,7 +372,7 @@ int tile_backward_sweep(hqml_ctx *c, hipStream_t st, Span sp, bool fused_last)
     if (pl.c == 0) {
         for (int k = P - 1; k >= 0; --k) {
             int fl = 0;
-            if (k == P - 1) fl = fused_last ? (PF_FUSED | PF_EMIT_E) : PF_SEED;
+            if (k == P - 1) fl = last_flags;
             if ((rc = bwd_pass(c, st, sp, k, 0, c->part, fl))) return rc;
         }
         for (int i = 0; i < nso; ++i)
@@ -355,7 +387,7 @@ int tile_backward_sweep(hqml_ctx *c, hipStream_t st, Span sp, bool fused_last)
         }
         for (int p = hi - 1; p >= lo; --p) {
             int fl = 0;
-            if (p == P - 1) fl = fused_last ? (PF_FUSED | PF_EMIT_E) : PF_SEED;
+            if (p == P - 1) fl = last_flags;
             if ((rc = bwd_pass(c, st, sp, p, lo, c->part, fl))) return rc;
         }
         if ((rc = reduce(c->part, lo, hi))) return rc;
@@ -391,6 +423,7 @@ SmallArgs small_args(hqml_ctx *c, int mode)
     a.L = c->plan.L;
     a.mode = mode;
     a.obs = c->obs;
+    a.obs_x = c->obs_x;
     return a;
 }
 
@@ -428,7 +461,7 @@ int gbg_forward_sweep(hqml_ctx *c, int B, const float *x, const float *theta)
                 return rc;
     }
     return run(c, HQML_K_GATE, "<O> partials",
-               [&] { return launch_gbg_expz(psi, n, B, c->obs, static_cast<float *>(c->e_part), c->stream); });
+               [&] { return launch_gbg_expz(psi, n, B, c->obs, c->obs_x, static_cast<float *>(c->e_part), c->stream); });
 }
 
 // Adjoint sweep from the final state left in gbg_psi; leaves the gradient block sums
@@ -439,7 +472,8 @@ int gbg_backward_sweep(hqml_ctx *c, int B)
     float2 *psi = reinterpret_cast<float2 *>(c->gbg_psi);
     float2 *lam = reinterpret_cast<float2 *>(c->gbg_lam);
     const size_t per_gate = (size_t)B * c->gbg_blocks;
-    int rc = run(c, HQML_K_GATE, "adjoint seed", [&] { return launch_gbg_seed(psi, lam, n, B, c->obs, c->stream); });
+    int rc = run(c, HQML_K_GATE, "adjoint seed",
+                 [&] { return launch_gbg_seed(psi, lam, n, B, c->obs, c->obs_x, c->stream); });
     if (rc) return rc;
     for (int l = L - 1; l >= 0; --l) {
         for (int q = n - 2; q >= 0; --q)
@@ -516,7 +550,8 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     c->gbg = cfg->fusion == HQML_GATE_BY_GATE;
     c->r64 = cfg->compute == HQML_COMPUTE_FP64 ? 1 : 0;
     c->rb = c->r64 ? 8 : 4;
-    c->obs = cfg->obs_mask ? (uint32_t)cfg->obs_mask : 1u;
+    c->obs = (cfg->obs_mask | cfg->obs_x_mask) ? (uint32_t)cfg->obs_mask : 1u;
+    c->obs_x = (uint32_t)cfg->obs_x_mask;
     c->ws = workspace_for(cfg, plan);
     c->stream = reinterpret_cast<hipStream_t>(cfg->stream);
     hipError_t e = hipSetDevice(cfg->device);
@@ -579,7 +614,7 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     c->dw = grab(Ln * 4 * c->rb);
     c->H = static_cast<double *>(grab(Ln * 9 * 8));
     c->init_u = grab((size_t)B * plan.n * 4 * c->rb);
-    if (!plan.small) c->views = static_cast<ViewDev *>(grab(plan.views.size() * sizeof(ViewDev)));
+    if (!plan.small) c->views = static_cast<ViewDev *>(grab((plan.views.size() + 1) * sizeof(ViewDev)));
     c->statmap = static_cast<int2 *>(grab(Ln * sizeof(int2)));
     c->dlde = static_cast<double *>(grab((size_t)B * 8));
     c->e_work = static_cast<double *>(grab((size_t)B * 8));
@@ -593,8 +628,18 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     std::vector<int2> sm(Ln);
     for (size_t i = 0; i < Ln; ++i) sm[i] = make_int2(plan.statmap[i].pass, plan.statmap[i].slot);
     e = hipMemcpy(c->statmap, sm.data(), Ln * sizeof(int2), hipMemcpyHostToDevice);
-    if (e == hipSuccess && !plan.small)
-        e = hipMemcpy(c->views, plan.views.data(), plan.views.size() * sizeof(ViewDev), hipMemcpyHostToDevice);
+    if (e == hipSuccess && !plan.small) {
+        std::vector<ViewDev> vs(plan.views);
+        ViewDev ov;
+        std::memset(&ov, 0, sizeof(ov));
+        std::string verr;
+        if (c->obs_x && !make_obs_view(plan.n, c->obs_x, &ov, &verr)) {
+            hqml_destroy(c);
+            return fail(nullptr, HQML_ERR_UNSUPPORTED, verr);
+        }
+        vs.push_back(ov);   // views[V]: the observable pass (unused without X/Y factors)
+        e = hipMemcpy(c->views, vs.data(), vs.size() * sizeof(ViewDev), hipMemcpyHostToDevice);
+    }
     if (e == hipSuccess && plan.small) e = configure_small((size_t)2 * ((size_t)1 << plan.n) * 2 * c->rb, c->r64);
     if (e != hipSuccess) {
         const std::string m = std::string("workspace set-up: ") + hipGetErrorString(e);
@@ -674,6 +719,7 @@ int forward_impl(hqml_ctx *c, int B, const void *x, const void *theta, void *exp
         });
     } else {
         if ((rc = tile_forward_sweep(c, c->stream, Span{0, B, B}, false))) return rc;
+        if (c->obs_x && (rc = obs_pass(c, c->stream, Span{0, B, B}, PF_EMIT_E))) return rc;
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {
             return launch_ez_reduce(c->e_part, c->r64, B, pl.T, nullptr, expz, nullptr, io64, nullptr, c->e_work,
                                     c->epart2, c->stream);
@@ -712,7 +758,8 @@ int backward_impl(hqml_ctx *c, const void *dL_dE, void *grad, int io64)
         const SmallArgs a = small_args(c, 1);
         rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->r64, c->stream); });
     } else {
-        rc = tile_backward_sweep(c, c->stream, Span{0, B, B}, false);
+        if (c->obs_x && (rc = obs_pass(c, c->stream, Span{0, B, B}, PF_SEED))) return rc;
+        rc = tile_backward_sweep(c, c->stream, Span{0, B, B}, c->obs_x ? LAMBDA_READY : SEED_FROM_SAVED);
     }
     if (rc) return rc;
     return run(c, HQML_K_OTHER, "gradient reduction", [&] {
@@ -759,8 +806,10 @@ int train_impl(hqml_ctx *c, int B, const void *x, const void *theta, const void 
         // gradient reduction, so the E reduction runs after the backward sweeps.
         const int C = chunk_count(c, B);
         if (C == 1) {
-            if ((rc = tile_forward_sweep(c, c->stream, Span{0, B, B}, true))) return rc;
-            if ((rc = tile_backward_sweep(c, c->stream, Span{0, B, B}, true))) return rc;
+            if ((rc = tile_forward_sweep(c, c->stream, Span{0, B, B}, !c->obs_x))) return rc;
+            if (c->obs_x && (rc = obs_pass(c, c->stream, Span{0, B, B}, PF_EMIT_E | PF_SEED))) return rc;
+            if ((rc = tile_backward_sweep(c, c->stream, Span{0, B, B}, c->obs_x ? LAMBDA_READY : FUSED_LAST)))
+                return rc;
         } else {
             hipError_t he = hipEventRecord(c->ev_start, c->stream);
             if (he == hipSuccess) he = hipStreamWaitEvent(c->aux, c->ev_start, 0);
@@ -771,14 +820,16 @@ int train_impl(hqml_ctx *c, int B, const void *x, const void *theta, const void 
                 spans.push_back(Span{b0, b1 - b0, B});
             }
             for (int k = 0; k < C; ++k) {
-                if ((rc = tile_forward_sweep(c, c->aux, spans[k], true))) return rc;
+                if ((rc = tile_forward_sweep(c, c->aux, spans[k], !c->obs_x))) return rc;
+                if (c->obs_x && (rc = obs_pass(c, c->aux, spans[k], PF_EMIT_E | PF_SEED))) return rc;
                 he = hipEventRecord(c->ev_fwd[k], c->aux);
                 if (he != hipSuccess) return hip_fail(c, he, "stream ordering");
             }
             for (int k = 0; k < C; ++k) {
                 he = hipStreamWaitEvent(c->stream, c->ev_fwd[k], 0);
                 if (he != hipSuccess) return hip_fail(c, he, "stream ordering");
-                if ((rc = tile_backward_sweep(c, c->stream, spans[k], true))) return rc;
+                if ((rc = tile_backward_sweep(c, c->stream, spans[k], c->obs_x ? LAMBDA_READY : FUSED_LAST)))
+                    return rc;
             }
         }
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {

@@ -120,10 +120,25 @@ __global__ void __launch_bounds__(kGbgThreads) k_gbg_cz(float2 *psi, float2 *lam
     }
 }
 
-// Per-block <O> partials, O = prod of Z over the qubits of obs: e_part[b][blk] = sum over
-// the block's amplitude pairs (2k, 2k+1) of sign_O |psi|^2.  Grid (nblk, B).
+// (O psi)_i for the Pauli string with Z part zm and X part xm (Y = iXZ):
+// i^(#Y) (-1)^|(i ^ xm) & zm| psi_(i ^ xm).
+__device__ __forceinline__ float2 gbg_obs(const float2 *s, uint32_t i, uint32_t zm, uint32_t xm)
+{
+    const uint32_t j = i ^ xm;
+    float2 w = s[j];
+    if (__builtin_popcount(j & zm) & 1) w = make_float2(-w.x, -w.y);
+    switch (__builtin_popcount(zm & xm) & 3) {
+    case 1: return make_float2(-w.y, w.x);
+    case 2: return make_float2(-w.x, -w.y);
+    case 3: return make_float2(w.y, -w.x);
+    default: return w;
+    }
+}
+
+// Per-block <O> partials: e_part[b][blk] = sum over the block's amplitudes i (two per
+// pair slot) of Re(conj(psi_i) (O psi)_i).  Grid (nblk, B).
 __global__ void __launch_bounds__(kGbgThreads) k_gbg_expz(const float2 *psi, uint32_t N, uint32_t obs,
-                                                           float *e_part)
+                                                           uint32_t obs_x, float *e_part)
 {
     __shared__ double red[kGbgThreads];
     const int b = blockIdx.y;
@@ -134,9 +149,8 @@ __global__ void __launch_bounds__(kGbgThreads) k_gbg_expz(const float2 *psi, uin
         const uint32_t k = blockIdx.x * kGbgPairsPerBlock + j * kGbgThreads + threadIdx.x;
         if (k >= half) break;
         const float2 a = s[2 * k], c = s[2 * k + 1];
-        const float pa = a.x * a.x + a.y * a.y, pc = c.x * c.x + c.y * c.y;
-        acc += (__builtin_popcount((2 * k) & obs) & 1) ? -pa : pa;
-        acc += (__builtin_popcount((2 * k + 1) & obs) & 1) ? -pc : pc;
+        const float2 oa = gbg_obs(s, 2 * k, obs, obs_x), oc = gbg_obs(s, 2 * k + 1, obs, obs_x);
+        acc += (a.x * oa.x + a.y * oa.y) + (c.x * oc.x + c.y * oc.y);
     }
     const double t = gbg_block_sum((double)acc, red);
     if (threadIdx.x == 0) e_part[(size_t)b * gridDim.x + blockIdx.x] = (float)t;
@@ -144,14 +158,14 @@ __global__ void __launch_bounds__(kGbgThreads) k_gbg_expz(const float2 *psi, uin
 
 // lambda = 2 O psi (the upstream dL/dE_b is applied in the final reduction).
 // Grid (ceil(N / 256), B).
-__global__ void __launch_bounds__(kGbgThreads) k_gbg_seed(const float2 *psi, float2 *lam, uint32_t N, uint32_t obs)
+__global__ void __launch_bounds__(kGbgThreads) k_gbg_seed(const float2 *psi, float2 *lam, uint32_t N, uint32_t obs,
+                                                           uint32_t obs_x)
 {
     const uint32_t i = blockIdx.x * kGbgThreads + threadIdx.x;
     if (i >= N) return;
-    const size_t o = (size_t)blockIdx.y * N + i;
-    const float f = (__builtin_popcount(i & obs) & 1) ? -2.f : 2.f;
-    const float2 v = psi[o];
-    lam[o] = make_float2(f * v.x, f * v.y);
+    const size_t base = (size_t)blockIdx.y * N;
+    const float2 v = gbg_obs(psi + base, i, obs, obs_x);
+    lam[base + i] = make_float2(2.f * v.x, 2.f * v.y);
 }
 
 // Adjoint step of one rotation exp(-i t sigma_G / 2) on qubit q, with psi and lambda
@@ -251,16 +265,19 @@ hipError_t launch_gbg_cz(float2 *psi, float2 *lam, int n, int B, int q, hipStrea
     return hipGetLastError();
 }
 
-hipError_t launch_gbg_expz(const float2 *psi, int n, int B, uint32_t obs, float *e_part, hipStream_t s)
+hipError_t launch_gbg_expz(const float2 *psi, int n, int B, uint32_t obs, uint32_t obs_x, float *e_part,
+                           hipStream_t s)
 {
-    k_gbg_expz<<<dim3((unsigned)gbg_blocks(n), (unsigned)B), kGbgThreads, 0, s>>>(psi, 1u << n, obs, e_part);
+    k_gbg_expz<<<dim3((unsigned)gbg_blocks(n), (unsigned)B), kGbgThreads, 0, s>>>(psi, 1u << n, obs, obs_x, e_part);
     return hipGetLastError();
 }
 
-hipError_t launch_gbg_seed(const float2 *psi, float2 *lam, int n, int B, uint32_t obs, hipStream_t s)
+hipError_t launch_gbg_seed(const float2 *psi, float2 *lam, int n, int B, uint32_t obs, uint32_t obs_x,
+                           hipStream_t s)
 {
     const uint32_t N = 1u << n;
-    k_gbg_seed<<<dim3((N + kGbgThreads - 1) / kGbgThreads, (unsigned)B), kGbgThreads, 0, s>>>(psi, lam, N, obs);
+    k_gbg_seed<<<dim3((N + kGbgThreads - 1) / kGbgThreads, (unsigned)B), kGbgThreads, 0, s>>>(psi, lam, N, obs,
+                                                                                              obs_x);
     return hipGetLastError();
 }
 

@@ -95,7 +95,8 @@ struct TilePassArgs {
     int rotB;               // second rotation layer (-1: none)
     int flags;
     int sample0;            // first sample of this launch (the grid covers samples sample0 ..)
-    uint32_t obs;           // observable O = prod of Z over the qubits of this mask
+    uint32_t obs;           // observable: Z part of the Pauli string (qubit mask)
+    uint32_t obs_x;         // observable: X part (qubits in both masks carry Y = iXZ)
 };
 
 struct SmallArgs {
@@ -109,7 +110,8 @@ struct SmallArgs {
     int n;
     int L;
     int mode;               // 0: forward only; 1: backward only (from psi_save); 2: both
-    uint32_t obs;           // observable O = prod of Z over the qubits of this mask
+    uint32_t obs;           // observable: Z part of the Pauli string (qubit mask)
+    uint32_t obs_x;         // observable: X part (qubits in both masks carry Y = iXZ)
 };
 
 }  // namespace hqml

@@ -889,6 +889,103 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 4 : 2) void k_tile_fwd(T
     fwd_ops<ST>(t, a, c, lds, lds_stat, nelem);
 }
 
+// ------------------------------------------------------------------ observable pass
+
+// Multiply by i^ph (ph = 0..3).
+template <typename R>
+__device__ __forceinline__ void mul_ipow(R &re, R &im, int ph)
+{
+    const R a = re, b = im;
+    if (ph == 1) { re = -b; im = a; }
+    else if (ph == 2) { re = -a; im = -b; }
+    else if (ph == 3) { re = b; im = -a; }
+}
+
+// Pauli-string observable with X or Y factors, O = i^(#Y) X^xm Z^zm (Y = iXZ), on the
+// final state: (O psi)_i = i^(#Y) (-1)^|(i ^ xm) & zm| psi_(i ^ xm).  The pass's view
+// keeps every qubit of xm on chip, so the partner amplitude i ^ xm is in the same
+// tile: the tile goes to LDS and each thread reads its partners.  Emits the per-tile
+// <O> partials (PF_EMIT_E) and/or writes lambda = O psi (PF_SEED).
+template <int ST, typename R>
+__global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_obs(TilePassArgs a)
+{
+    __shared__ V2<R> lds[1 << kTileBits];
+    __shared__ R lds_stat[kSlots * 16 + 16];
+    const ViewDev &v = *a.view;
+    TileCtx c;
+    tile_ctx(c, v, a.T, blockIdx.x, a.sample0);
+    const uint64_t nelem = 1ull << a.n;
+    Tile<R> p;
+    load_l1<ST>(p, a.psi_in, c, nelem);
+    // phi = D_trail psi, D_trail(i) = CZ-chain sign x prod_q f_q(bit q of i) (layer L-1's
+    // left factors): the true final state.  D_trail commutes with Z but not with X or Y.
+    const V4<R> *wl = reinterpret_cast<const V4<R> *>(a.dw) + (size_t)(a.L - 1) * a.n;
+    uint32_t regq = 0;
+#pragma unroll
+    for (int m = 0; m < 5; ++m) regq |= 1u << c.q1[m];
+    V2<R> cst = mk2((R)1, (R)0);
+    for (int q = 0; q < a.n; ++q) {
+        if ((regq >> q) & 1u) continue;
+        const V4<R> f = ldu4(reinterpret_cast<const R *>(wl + q));
+        cst = cmul(cst, ((c.fixed1 >> q) & 1u) ? mk2(f.z, f.w) : mk2(f.x, f.y));
+    }
+    V2<R> dj[kRegs];
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+        uint32_t g = c.fixed1;
+        V2<R> f = cst;
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+            const V4<R> w = ldu4(reinterpret_cast<const R *>(wl + c.q1[m]));
+            if ((j >> m) & 1) {
+                g |= 1u << c.q1[m];
+                f = cmul(f, mk2(w.z, w.w));
+            } else {
+                f = cmul(f, mk2(w.x, w.y));
+            }
+        }
+        if (__builtin_popcount(g & (g >> 1)) & 1) f = mk2(-f.x, -f.y);
+        dj[j] = f;
+        const R r = p.re[j], i = p.im[j];
+        p.re[j] = r * f.x - i * f.y;
+        p.im[j] = r * f.y + i * f.x;
+    }
+    uint32_t xl = 0;   // local positions of the X part
+    for (int q = 0; q < a.n; ++q)
+        if ((a.obs_x >> q) & 1u) xl |= 1u << ldu(&v.inv[q]);
+    const uint32_t sx = swz(xl);
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) lds[c.a1 ^ swz(l1_reg(j))] = mk2(p.re[j], p.im[j]);
+    __syncthreads();
+    // sign of Z^zm at the partner: parity((i ^ xm) & zm) = parity(i & zm) ^ parity(xm & zm)
+    uint32_t neg = obs_mask_l1(c, a.obs);
+    if (__builtin_popcount(a.obs & a.obs_x) & 1) neg = ~neg;
+    const int ph = __builtin_popcount(a.obs & a.obs_x) & 3;
+    Tile<R> o;
+    R e = 0;
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+        const V2<R> w = lds[(c.a1 ^ swz(l1_reg(j))) ^ sx];
+        R re = ((neg >> j) & 1u) ? -w.x : w.x;
+        R im = ((neg >> j) & 1u) ? -w.y : w.y;
+        mul_ipow(re, im, ph);
+        o.re[j] = re;
+        o.im[j] = im;
+        e = fmar(p.re[j], re, fmar(p.im[j], im, e));
+    }
+    if (a.flags & PF_EMIT_E) emit_e(e, lds_stat, static_cast<R *>(a.e_part), c, a.T);
+    if (a.flags & PF_SEED) {
+        // lambda at the last Ry layer = D_trail^dagger O phi
+#pragma unroll
+        for (int j = 0; j < kRegs; ++j) {
+            const R r = o.re[j], i = o.im[j];
+            o.re[j] = r * dj[j].x + i * dj[j].y;
+            o.im[j] = i * dj[j].x - r * dj[j].y;
+        }
+        store_l1<kLamIO<R>>(o, a.lam, c, nelem);
+    }
+}
+
 // ------------------------------------------------------------------ backward tile pass
 
 template <typename R>
@@ -1052,6 +1149,22 @@ __device__ __forceinline__ V2<R> small_diag(const V4<R> *wl, int n, uint32_t i)
     return f;
 }
 
+// (O phi)_i for the Pauli string (zm, xm), phi = D_trail psi the true final state
+// (wl: the trailing diagonal's factors; applied only when xm != 0, since D_trail
+// commutes with Z):  i^(#Y) (-1)^|(i ^ xm) & zm| phi_(i ^ xm).
+template <typename R>
+__device__ __forceinline__ V2<R> small_obs(const V2<R> *psi, uint32_t i, uint32_t zm, uint32_t xm, const V4<R> *wl,
+                                           int n)
+{
+    const uint32_t j = i ^ xm;
+    V2<R> w = psi[j];
+    if (xm) w = cmul(w, small_diag<R>(wl, n, j));
+    R re = (__builtin_popcount(j & zm) & 1) ? -w.x : w.x;
+    R im = (__builtin_popcount(j & zm) & 1) ? -w.y : w.y;
+    mul_ipow(re, im, __builtin_popcount(zm & xm) & 3);
+    return mk2(re, im);
+}
+
 __device__ __forceinline__ uint32_t pair_index(uint32_t k, int q)
 {
     return ((k >> q) << (q + 1)) | (k & ((1u << q) - 1u));
@@ -1098,12 +1211,13 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
                 __syncthreads();
             }
         }
-        // <O>
+        // <O> = sum_i Re(conj(psi_i) (O psi)_i)
         R e = 0;
         for (uint32_t i = tid; i < N; i += kThreads) {
-            const V2<R> v = psi[i];
-            const R pr = v.x * v.x + v.y * v.y;
-            e += (__builtin_popcount(i & a.obs) & 1) ? -pr : pr;
+            V2<R> v = psi[i];
+            if (a.obs_x) v = cmul(v, small_diag<R>(dw + (size_t)(L - 1) * n, n, i));
+            const V2<R> o = small_obs<R>(psi, i, a.obs, a.obs_x, dw + (size_t)(L - 1) * n, n);
+            e += v.x * o.x + v.y * o.y;
         }
         e = row_sum16(e);
         if ((lane & 15) == 15) red[w * 4 + (lane >> 4)] = e;
@@ -1124,9 +1238,15 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
     }
 
     // Adjoint sweep: lambda = O psi at P_{L-1}; statistics at every P_l; uncompute.
+    // lambda at the last Ry layer = D_trail^dagger O D_trail psi (= O psi for a Z-string)
     for (uint32_t i = tid; i < N; i += kThreads) {
-        const V2<R> v = psi[i];
-        lam[i] = (__builtin_popcount(i & a.obs) & 1) ? mk2(-v.x, -v.y) : v;
+        V2<R> o = small_obs<R>(psi, i, a.obs, a.obs_x, dw + (size_t)(L - 1) * n, n);
+        if (a.obs_x) {
+            V2<R> f = small_diag<R>(dw + (size_t)(L - 1) * n, n, i);
+            f.y = -f.y;
+            o = cmul(o, f);
+        }
+        lam[i] = o;
     }
     __syncthreads();
     for (int l = L - 1; l >= 0; --l) {
@@ -1326,10 +1446,14 @@ __global__ void k_prep_tables(const TI *theta, const double *zyz, const unsigned
         d[2] = (R)f1.re;
         d[3] = (R)f1.im;
     } else {
-        d[0] = 1;
-        d[1] = 0;
-        d[2] = 1;
-        d[3] = 0;
+        // the trailing diagonal (layer L-1's left factors; with the CZ chain it follows the
+        // last Ry layer): never applied by the passes, which drop it since it commutes
+        // with a Z-string observable; Pauli strings with X/Y factors apply it.  No frame
+        // bit reaches past the last layer.
+        d[0] = (R)z[2];
+        d[1] = (R)z[3];
+        d[2] = (R)z[2];
+        d[3] = (R)-z[3];
     }
     const double ay = theta[idx * 3 + 1], az = theta[idx * 3 + 2];
     const m2 X = m2{{cmk(0, 0), cmk(1, 0), cmk(1, 0), cmk(0, 0)}};
@@ -1523,6 +1647,23 @@ hipError_t launch_prep(const void *theta, const void *x, int io64, int L, int n,
             prep_typed<float, double>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, s);
         else
             prep_typed<float, float>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, s);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_obs(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s)
+{
+    const dim3 grid((unsigned)(B * a.T));
+    if (r64) {
+        if (storage == 2)
+            k_tile_obs<2, double><<<grid, kThreads, 0, s>>>(a);
+        else
+            k_tile_obs<0, double><<<grid, kThreads, 0, s>>>(a);
+    } else {
+        if (storage == 1)
+            k_tile_obs<1, float><<<grid, kThreads, 0, s>>>(a);
+        else
+            k_tile_obs<0, float><<<grid, kThreads, 0, s>>>(a);
     }
     return hipGetLastError();
 }

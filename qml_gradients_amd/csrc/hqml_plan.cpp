@@ -119,6 +119,37 @@ bool build_views(int n, Plan &p, std::string *err)
 
 }  // namespace
 
+bool make_obs_view(int n, uint32_t xmask, ViewDev *out, std::string *err)
+{
+    if (n <= kSmallMaxQubits) {
+        if (err) *err = "observable views are for the tile path";
+        return false;
+    }
+    ViewDev d;
+    std::memset(&d, 0, sizeof(d));
+    for (int i = 0; i < 32; ++i) d.inv[i] = -1;
+    int pos = 0;
+    for (int q = 0; q < kLowQubits; ++q) d.perm[pos++] = q;
+    for (int q = kLowQubits; q < n; ++q)   // every high qubit of the X part on chip
+        if ((xmask >> q) & 1u) {
+            if (pos == kTileBits) {
+                if (err) *err = "the X/Y factors of the observable span more than 9 qubits above qubit 3";
+                return false;
+            }
+            d.perm[pos++] = q;
+        }
+    for (int q = kLowQubits; q < n && pos < kTileBits; ++q)
+        if (!((xmask >> q) & 1u)) d.perm[pos++] = q;
+    for (int i = 0; i < kTileBits; ++i) d.inv[d.perm[i]] = i;
+    int nt = 0;
+    for (int q = 0; q < n; ++q)
+        if (d.inv[q] < 0) d.tile_q[nt++] = q;
+    d.n_tile = nt;
+    d.group_mask = 0;
+    *out = d;
+    return true;
+}
+
 bool make_plan(int n, int L, int ckpt_block, Plan *out, std::string *err)
 {
     Plan p;
@@ -227,7 +258,7 @@ Workspace size_workspace(const Plan &p, int max_batch, int storage, int compute6
     // tables: zyz (6 doubles), frame (1 byte), rot_tf (2 reals), dw (4 reals), H (9 doubles), statmap (int2),
     // init_u (4 reals per sample and qubit), views, per-sample E / dL/dE / scratch, loss.
     w.tables_bytes = Ln * (6 * 8 + 1 + 2 * r + 4 * r + 9 * 8 + 8) + B * p.n * 4 * r +
-                     (size_t)std::max(p.V, 1) * sizeof(ViewDev) + B * (8 * 3 + 4) + 64;
+                     (size_t)(std::max(p.V, 1) + 1) * sizeof(ViewDev) + B * (8 * 3 + 4) + 64;
     const size_t S_bytes = B * Ln * 3 * 8;
     if (p.small) {
         w.n_saved = 1;

@@ -46,6 +46,11 @@ struct Plan {
 // message in *err for unsupported sizes.
 bool make_plan(int n, int L, int ckpt_block, Plan *plan, std::string *err);
 
+// View for the observable pass of a Pauli string whose X part is xmask: qubits 0..3
+// and every higher qubit of xmask on chip (at most 9), the rest as tile bits.
+// Returns false with a message for n <= 13 or too many X/Y qubits.
+bool make_obs_view(int n, uint32_t xmask, ViewDev *out, std::string *err);
+
 // Device memory layout of a context.
 struct Workspace {
     size_t state_elems = 0;     // amplitudes per sample

@@ -92,6 +92,22 @@ def test_fp64_config_host_only():
     assert hq.hqml_workspace_bytes(hq.make_config(16, 2, 1, compute=2)) == 0
 
 
+def test_pauli_observable_config_host_only():
+    _lib()
+    ok = hq.make_config(20, 3, 2, obs_mask=0, obs_x_mask=sum(1 << q for q in range(11, 20)))   # 9 high X
+    assert hq.hqml_workspace_bytes(ok) > 0
+    too_many = hq.make_config(20, 3, 2, obs_x_mask=sum(1 << q for q in range(10, 20)))         # 10 high X
+    assert hq.hqml_workspace_bytes(too_many) == 0
+    with pytest.raises(hq.HqmlError) as e:
+        hq.hqml_create(too_many)
+    assert e.value.status == hq.HQML_ERR_UNSUPPORTED
+    # the whole-circuit path and the gate-by-gate comparator take any Pauli string
+    assert hq.hqml_workspace_bytes(hq.make_config(13, 3, 2, obs_x_mask=(1 << 13) - 1)) > 0
+    assert hq.hqml_workspace_bytes(hq.make_config(20, 3, 2, obs_x_mask=(1 << 20) - 1, fusion="gate_by_gate")) > 0
+    for bad in (hq.make_config(4, 1, 1, obs_x_mask=16), hq.make_config(4, 1, 1, obs_x_mask=-2)):
+        assert hq.hqml_workspace_bytes(bad) == 0
+
+
 def test_workspace_scaling_checkpoint_and_bf16():
     _lib()
     full = hq.hqml_workspace_bytes(hq.make_config(20, 1000, 60))
