@@ -217,6 +217,7 @@ class Context:
         self.f64 = compute == "fp64" or compute == HQML_COMPUTE_FP64
         self.dtype = torch.float64 if self.f64 else torch.float32
         self.handle = hqml_create(self.cfg)
+        self.fwd_id = 0          # counts forwards (the saved states belong to the latest one)
 
     def close(self):
         if self.handle is not None:
@@ -243,6 +244,7 @@ class Context:
         expz = self.torch.empty(B, dtype=self.dtype, device=self.device)
         fwd = hqml_forward_f64 if self.f64 else hqml_forward
         fwd(self.handle, B, x.data_ptr(), theta.data_ptr(), expz.data_ptr(), save_for_backward)
+        self.fwd_id += 1
         self._keep = (x, theta)
         return expz
 
@@ -266,6 +268,7 @@ class Context:
         step = hqml_train_step_f64 if self.f64 else hqml_train_step
         step(self.handle, B, x.data_ptr(), theta.data_ptr(), y.data_ptr(), expz.data_ptr(), loss.data_ptr(),
              grad.data_ptr())
+        self.fwd_id += 1
         self._keep = (x, theta, y)
         return expz, loss, grad
 
