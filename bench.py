@@ -236,8 +236,9 @@ def main():
                     help="only run a 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                                   "(the data-parallel sharding over GPUs is described in DESIGN.md)"}))
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 (samples shard over "
+                                   "GPUs by batch with an all-gather of the per-rank fp64 gradient; "
+                                   "that multi-GPU layer is not implemented)"}))
         sys.exit(2)
 
     import torch

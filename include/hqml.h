@@ -49,7 +49,7 @@ typedef enum {
     HQML_ERR_OOM = -2,          /* device memory could not be reserved */
     HQML_ERR_HIP = -3,          /* a HIP runtime call or kernel launch failed */
     HQML_ERR_STATE = -4,        /* call out of order (e.g. backward without a saved forward) */
-    HQML_ERR_UNSUPPORTED = -5   /* valid request this build does not implement */
+    HQML_ERR_UNSUPPORTED = -5   /* valid request the library does not implement */
 } hqml_status;
 
 typedef enum {
