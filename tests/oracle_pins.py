@@ -44,8 +44,8 @@ def pin_one_layer_closed_form(o):
         E = cos x0 cos a cos b - sin x0 sin b,
         dE/da = -cos x0 sin a cos b,  dE/db = -cos x0 cos a sin b - sin x0 cos b,
     and every other derivative is 0."""
-    for n in (1, 3, 7):
-        x, th = _rand(n, 1, 5, 10 + n)
+    for n in (1, 3, 7, 20):
+        x, th = _rand(n, 1, 5 if n < 20 else 2, 10 + n)
         a, b = th[0, 0, 0], th[0, 0, 1]
         x0 = x[:, 0]
         e_ref = np.cos(x0) * np.cos(a) * np.cos(b) - np.sin(x0) * np.sin(b)

@@ -143,3 +143,62 @@ def test_error_paths():
     torch.cuda.synchronize()
     assert float(g[:2].abs().max()) == 0.0
     ctx.close()
+
+
+@pytest.mark.parametrize("n", [20, 29])
+def test_one_layer_closed_form_full_width(n):
+    """L = 1 at full width: E = cos x0 cos a cos b - sin x0 sin b, with (a, b) the Rx and Ry
+    angles of qubit 0; dE/da, dE/db in closed form; every other derivative is 0 (the CZ
+    chain and the Rz gates commute with Z_0)."""
+    import qml_gradients_amd as hq
+    B = 2 if n == 20 else 1
+    x, th, _ = hqml_inputs.make_inputs(n, 1, B, seed=77)
+    say(f"[gpu] one-layer closed form n={n}")
+    ctx = _ctx(n, 1, B, ckpt_block=1 if n == 29 else 0)
+    w = np.linspace(0.5, 1.5, B).astype(np.float32)
+    e = ctx.forward(torch.from_numpy(x), torch.from_numpy(th)).cpu().numpy().astype(np.float64)
+    g = ctx.backward(torch.from_numpy(w)).cpu().numpy().astype(np.float64)
+    ctx.close()
+    x0 = x[:, 0].astype(np.float64)
+    a, b = float(th[0, 0, 0]), float(th[0, 0, 1])
+    e_ref = np.cos(x0) * np.cos(a) * np.cos(b) - np.sin(x0) * np.sin(b)
+    assert_e_close(e, e_ref, n)
+    g_ref = np.zeros((1, n, 3))
+    g_ref[0, 0, 0] = np.sum(w * (-np.cos(x0) * np.sin(a) * np.cos(b)))
+    g_ref[0, 0, 1] = np.sum(w * (-np.cos(x0) * np.cos(a) * np.sin(b) - np.sin(x0) * np.cos(b)))
+    assert_grad_close(g, g_ref)
+
+
+def test_nan_inputs_propagate_and_oom_precheck():
+    """A NaN angle gives NaN results without a fault; a workspace larger than the free
+    device memory is refused before any allocation."""
+    import qml_gradients_amd as hq
+    n, L, B = 15, 2, 2
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=9)
+    th[1, 3, 1] = np.nan
+    say("[gpu] NaN inputs")
+    ctx = _ctx(n, L, B)
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(*(torch.from_numpy(a) for a in (x, th, y))))
+    ctx.close()
+    assert np.isnan(loss[0]) or np.isnan(e).any() or np.isnan(g).any()
+    say("[gpu] OOM pre-check")
+    with pytest.raises(hq.HqmlError) as err:
+        _ctx(29, 200, 8)        # ~200 saved 32 GiB states
+    assert err.value.status == hq.HQML_ERR_OOM
+    ok = _ctx(14, 1, 1)        # the device is still usable afterwards
+    ok.close()
+
+
+def test_null_pointer_arguments():
+    import qml_gradients_amd as hq
+    ctx = _ctx(14, 2, 2)
+    buf = torch.zeros(1024, device="cuda")
+    p = buf.data_ptr()
+    for args in ((2, 0, p, p, p, p, p), (2, p, 0, p, p, p, p), (2, p, p, 0, p, p, p), (2, p, p, p, p, p, 0)):
+        with pytest.raises(hq.HqmlError) as e:
+            hq.hqml_train_step(ctx.handle, *args)
+        assert e.value.status == hq.HQML_ERR_ARG
+    with pytest.raises(hq.HqmlError) as e:
+        hq.hqml_train_step(ctx.handle, 3, p, p, p, p, p, p)      # B > max_batch
+    assert e.value.status == hq.HQML_ERR_ARG
+    ctx.close()
