@@ -297,15 +297,19 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     ev0.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
+        marks[i + 1].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
     value = B / (ms_per_step / 1e3)
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
 
     # Instrumented loop: HIP events around every launch (same workload).
     ctx.set_timing(True)
@@ -363,6 +367,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(per_step[len(per_step) // 2], 4) if per_step else None,
+        "ms_per_step_min": round(per_step[0], 4) if per_step else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
