@@ -10,7 +10,9 @@ adjoint state at all.  Used to check the gate-by-gate oracle in
 Conventions are the same readings as the gate-by-gate oracle: qubit q is bit q
 of the amplitude index, so in a Kronecker product the factor for qubit 0 is the
 rightmost one; R_s(t) = exp(-i t s/2); encoding Ry(x_q) on |0...0>; each layer
-applies Rx, Ry, Rz to every qubit, then CZ(q, q+1) for q = 0..n-2; O = the
+applies Rx, Ry, Rz to every qubit, then CZ(q, q+1) for q = 0..n-2 (entangler 0)
+or CNOT(q, q+1), control q, for q = 0, 1, ..., n-2 in that order (entangler 1),
+each CNOT built as the sum of two Kronecker products; O = the
 Kronecker product of one Pauli matrix per qubit: Z where only the z mask has the
 qubit, X where only the x mask has it, Y where both do, I elsewhere (default Z_0).
 """
@@ -54,7 +56,21 @@ def cz(q: int, n: int) -> np.ndarray:
     return np.diag(d)
 
 
-def gate_list(x, theta, n):
+def cnot(c: int, t: int, n: int) -> np.ndarray:
+    """Full matrix of CNOT(c, t) = |0><0|_c (x) I + |1><1|_c (x) X_t."""
+    p0 = np.array([[1, 0], [0, 0]], dtype=np.complex128)
+    p1 = np.array([[0, 0], [0, 1]], dtype=np.complex128)
+
+    def kron_all(factors):
+        out = np.array([[1.0 + 0j]])
+        for k in range(n - 1, -1, -1):
+            out = np.kron(out, factors.get(k, np.eye(2)))
+        return out
+
+    return kron_all({c: p0}) + kron_all({c: p1, t: PAULI["X"]})
+
+
+def gate_list(x, theta, n, entangler: int = 0):
     """The circuit as a list of (matrix, parameter index or None, derivative)."""
     theta = np.asarray(theta, dtype=np.float64).reshape(-1, n, 3)
     gates = []
@@ -66,17 +82,17 @@ def gate_list(x, theta, n):
                 t = theta[l, q, a]
                 gates.append((embed(rot(ax, t), q, n), (l, q, a), embed(rot_deriv(ax, t), q, n)))
         for q in range(n - 1):
-            gates.append((cz(q, n), None, None))
+            gates.append((cnot(q, q + 1, n) if entangler else cz(q, n), None, None))
     return gates
 
 
-def state(x, theta) -> np.ndarray:
+def state(x, theta, entangler: int = 0) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64).ravel()
     n = x.size
     psi0 = np.zeros(1 << n, dtype=np.complex128)
     psi0[0] = 1.0
     U = np.eye(1 << n, dtype=np.complex128)
-    for g, _, _ in gate_list(x, theta, n):
+    for g, _, _ in gate_list(x, theta, n, entangler):
         U = g @ U
     return U @ psi0
 
@@ -91,20 +107,20 @@ def observable(n: int, zmask: int = 1, xmask: int = 0) -> np.ndarray:
     return out
 
 
-def expz(x, theta, zmask: int = 1, xmask: int = 0) -> float:
+def expz(x, theta, zmask: int = 1, xmask: int = 0, entangler: int = 0) -> float:
     x = np.asarray(x, dtype=np.float64).ravel()
     n = x.size
-    psi = state(x, theta)
+    psi = state(x, theta, entangler)
     O = observable(n, zmask, xmask)
     return float(np.real(np.vdot(psi, O @ psi)))
 
 
-def grad_expz(x, theta, zmask: int = 1, xmask: int = 0) -> np.ndarray:
+def grad_expz(x, theta, zmask: int = 1, xmask: int = 0, entangler: int = 0) -> np.ndarray:
     """dE/dtheta [L][n][3] by the product rule on the dense circuit unitary."""
     x = np.asarray(x, dtype=np.float64).ravel()
     n = x.size
     theta = np.asarray(theta, dtype=np.float64).reshape(-1, n, 3)
-    gates = gate_list(x, theta, n)
+    gates = gate_list(x, theta, n, entangler)
     psi0 = np.zeros(1 << n, dtype=np.complex128)
     psi0[0] = 1.0
     O = observable(n, zmask, xmask)

@@ -16,14 +16,17 @@
  *     the adjoint gradient is dL/dtheta_j = Re<lambda_j| dU_j/dtheta_j |psi_{j-1}>
  *     with lambda_{j-1} = U_j^dagger lambda_j;
  *   section 2.1: the HEA uses single-qubit Rx, Ry, Rz rotations and CZ gates;
- *   section 3.2: CZ is a sign flip when both qubit bits are set.
+ *   section 3.2: CZ is a sign flip when both qubit bits are set; CNOT gates are
+ *     fused by recomputing amplitude indices (a CNOT permutes basis states).
  * Circuit details the pages leave open are fixed as follows (each is a reading,
  * listed with its reason in the design notes):
  *   - qubit q is bit q of the amplitude index (qubit 0 = least significant);
  *   - R_s(t) = exp(-i t s / 2) for s in {X, Y, Z};
  *   - encoding: Ry(x_q)|0> on every qubit, once;
  *   - layer l: on every qubit q apply Rx(theta[l][q][0]), then Ry(theta[l][q][1]),
- *     then Rz(theta[l][q][2]); then CZ(q, q+1) for q = 0..n-2 (open chain);
+ *     then Rz(theta[l][q][2]); then the entangler: CZ(q, q+1) for q = 0..n-2 (open
+ *     chain, the default), or, as the second entangler, CNOT(q, q+1) (control q,
+ *     target q+1) for q = 0, 1, ..., n-2 in that order;
  *   - observable O = a Pauli string, the general O of section 1.2 restricted to
  *     tensor products of I, X, Y, Z: two bit masks (bit q = qubit q) give qubit
  *     q the factor I (in neither), Z (z only), X (x only) or Y (both); the default
@@ -128,6 +131,45 @@ static void apply_cz(cplx *psi, int n, int q, int par)
         if ((i & both) == both) psi[i] = -psi[i];
 }
 
+/* CNOT(c, t): swap the amplitudes of i and i ^ 2^t wherever bit c of i is set. */
+static void apply_cnot(cplx *psi, int n, int c, int t, int par)
+{
+    const int64_t dim = (int64_t)1 << n;
+    const int64_t cb = (int64_t)1 << c, tb = (int64_t)1 << t;
+    (void)par;
+#pragma omp parallel for if (par) schedule(static)
+    for (int64_t i = 0; i < dim; ++i) {
+        if (!(i & cb) || (i & tb)) continue;
+        const cplx a = psi[i];
+        psi[i] = psi[i | tb];
+        psi[i | tb] = a;
+    }
+}
+
+enum { ENT_CZ = 0, ENT_CNOT = 1 };
+
+/* The entangling block that ends every layer, in circuit order. */
+static void apply_entangler(cplx *psi, int n, int ent, int par)
+{
+    for (int q = 0; q + 1 < n; ++q) {
+        if (ent == ENT_CNOT)
+            apply_cnot(psi, n, q, q + 1, par);
+        else
+            apply_cz(psi, n, q, par);
+    }
+}
+
+/* Its inverse: the same self-inverse gates in reverse order. */
+static void undo_entangler(cplx *psi, int n, int ent, int par)
+{
+    for (int q = n - 2; q >= 0; --q) {
+        if (ent == ENT_CNOT)
+            apply_cnot(psi, n, q, q + 1, par);
+        else
+            apply_cz(psi, n, q, par);
+    }
+}
+
 /* Re<lam| D_q |phi>, D a 2x2 matrix on qubit q (summed in index order). */
 static double re_braket_1q(const cplx *lam, const cplx *phi, int n, int q, gate2 d, int par)
 {
@@ -180,7 +222,7 @@ static double expect_obs(const cplx *psi, cplx *scratch, int n, uint32_t zmask, 
 }
 
 /* psi <- encoding followed by all L layers; |psi| must hold 2^n amplitudes. */
-static void run_circuit(cplx *psi, int n, int L, const double *x, const double *theta, int par)
+static void run_circuit(cplx *psi, int n, int L, const double *x, const double *theta, int ent, int par)
 {
     const int64_t dim = (int64_t)1 << n;
     memset(psi, 0, sizeof(cplx) * (size_t)dim);
@@ -190,7 +232,7 @@ static void run_circuit(cplx *psi, int n, int L, const double *x, const double *
         for (int q = 0; q < n; ++q)
             for (int a = 0; a < 3; ++a)
                 apply_1q(psi, n, q, rotation(a, theta[((size_t)l * n + q) * 3 + a]), par);
-        for (int q = 0; q + 1 < n; ++q) apply_cz(psi, n, q, par);
+        apply_entangler(psi, n, ent, par);
     }
 }
 
@@ -198,15 +240,16 @@ static void run_circuit(cplx *psi, int n, int L, const double *x, const double *
  * gate by gate), lam is scratch.  grad[(l*n+q)*3+a] receives dL/dtheta for
  * upstream derivative g = dL/dE. */
 static void adjoint_sample(cplx *psi, cplx *lam, int n, int L, const double *theta, uint32_t zmask,
-                           uint32_t xmask, double g, double *grad, int par)
+                           uint32_t xmask, int ent, double g, double *grad, int par)
 {
     const int64_t dim = (int64_t)1 << n;
     /* lambda_M = 2 g O psi_M */
     apply_observable(psi, lam, n, zmask, xmask, par);
     for (int64_t i = 0; i < dim; ++i) lam[i] *= 2.0 * g;
     for (int l = L - 1; l >= 0; --l) {
-        /* CZ chain, in reverse order (the CZs commute; order kept for clarity). */
-        for (int q = n - 2; q >= 0; --q) { apply_cz(psi, n, q, par); apply_cz(lam, n, q, par); }
+        /* the entangler, gate by gate in reverse order, on both states */
+        undo_entangler(psi, n, ent, par);
+        undo_entangler(lam, n, ent, par);
         for (int q = n - 1; q >= 0; --q) {
             for (int a = 2; a >= 0; --a) {
                 const double t = theta[((size_t)l * n + q) * 3 + a];
@@ -253,17 +296,18 @@ int oracle_get_max_threads(void)
 
 /* Final state of one sample after encoding and all L layers (psi: 2^n
  * interleaved (re, im) doubles).  Returns 0, or -1 on bad arguments / memory. */
-int oracle_state(int n, int L, const double *x, const double *theta, double *psi_out)
+int oracle_state(int n, int L, int ent, const double *x, const double *theta, double *psi_out)
 {
-    if (n < 1 || n > 30 || L < 0 || !x || (L > 0 && !theta) || !psi_out) return -1;
-    run_circuit((cplx *)psi_out, n, L, x, theta, n >= 14);
+    if (n < 1 || n > 30 || L < 0 || (ent != ENT_CZ && ent != ENT_CNOT) || !x || (L > 0 && !theta) || !psi_out)
+        return -1;
+    run_circuit((cplx *)psi_out, n, L, x, theta, ent, n >= 14);
     return 0;
 }
 
 /* Largest |1 - ||psi||^2| after any single gate of the circuit (unitarity check). */
-double oracle_max_norm_drift(int n, int L, const double *x, const double *theta)
+double oracle_max_norm_drift(int n, int L, int ent, const double *x, const double *theta)
 {
-    if (n < 1 || n > 24 || L < 0) return -1.0;
+    if (n < 1 || n > 24 || L < 0 || (ent != ENT_CZ && ent != ENT_CNOT)) return -1.0;
     const int64_t dim = (int64_t)1 << n;
     cplx *psi = (cplx *)calloc((size_t)dim, sizeof(cplx));
     if (!psi) return -1.0;
@@ -283,7 +327,13 @@ double oracle_max_norm_drift(int n, int L, const double *x, const double *theta)
                 apply_1q(psi, n, q, rotation(a, theta[((size_t)l * n + q) * 3 + a]), 0);
                 HQML_ORACLE_TRACK();
             }
-        for (int q = 0; q + 1 < n; ++q) { apply_cz(psi, n, q, 0); HQML_ORACLE_TRACK(); }
+        for (int q = 0; q + 1 < n; ++q) {
+            if (ent == ENT_CNOT)
+                apply_cnot(psi, n, q, q + 1, 0);
+            else
+                apply_cz(psi, n, q, 0);
+            HQML_ORACLE_TRACK();
+        }
     }
 #undef HQML_ORACLE_TRACK
     free(psi);
@@ -296,12 +346,14 @@ static int bad_mask(int n, uint32_t zmask, uint32_t xmask)
     return (zmask | xmask) == 0 || (n < 32 && ((zmask | xmask) >> n) != 0);
 }
 
+static int bad_ent(int ent) { return ent != ENT_CZ && ent != ENT_CNOT; }
+
 /* E_b = <psi_M|O|psi_M> for every sample.  x: [B][n], theta: [L][n][3]. */
-int oracle_forward(int n, int L, int B, uint32_t zmask, uint32_t xmask, const double *x, const double *theta,
-                   double *expz)
+int oracle_forward(int n, int L, int B, uint32_t zmask, uint32_t xmask, int ent, const double *x,
+                   const double *theta, double *expz)
 {
     if (n < 1 || n > 30 || L < 0 || B < 0 || (B > 0 && (!x || !expz)) || (L > 0 && !theta) ||
-        bad_mask(n, zmask, xmask))
+        bad_mask(n, zmask, xmask) || bad_ent(ent))
         return -1;
     const int par = choose_par(n, B);
     const int64_t dim = (int64_t)1 << n;
@@ -311,7 +363,7 @@ int oracle_forward(int n, int L, int B, uint32_t zmask, uint32_t xmask, const do
         cplx *psi = (cplx *)malloc(sizeof(cplx) * (size_t)dim);
         cplx *tmp = (cplx *)malloc(sizeof(cplx) * (size_t)dim);
         if (!psi || !tmp) { free(psi); free(tmp); err |= 1; continue; }
-        run_circuit(psi, n, L, x + (size_t)b * n, theta, par);
+        run_circuit(psi, n, L, x + (size_t)b * n, theta, ent, par);
         expz[b] = expect_obs(psi, tmp, n, zmask, xmask, par);
         free(psi);
         free(tmp);
@@ -322,11 +374,11 @@ int oracle_forward(int n, int L, int B, uint32_t zmask, uint32_t xmask, const do
 /* Adjoint gradient for an arbitrary upstream derivative dLdE[b]:
  * grad[(l*n+q)*3+a] = sum_b (per-sample adjoint gradient), summed in sample
  * order.  expz (optional) receives E_b. */
-int oracle_backward(int n, int L, int B, uint32_t zmask, uint32_t xmask, const double *x, const double *theta,
-                    const double *dLdE, double *grad, double *expz)
+int oracle_backward(int n, int L, int B, uint32_t zmask, uint32_t xmask, int ent, const double *x,
+                    const double *theta, const double *dLdE, double *grad, double *expz)
 {
     if (n < 1 || n > 30 || L < 0 || B < 0 || (B > 0 && (!x || !dLdE)) || (L > 0 && (!theta || !grad)) ||
-        bad_mask(n, zmask, xmask))
+        bad_mask(n, zmask, xmask) || bad_ent(ent))
         return -1;
     const size_t P = (size_t)L * n * 3;
     const int par = choose_par(n, B);
@@ -339,9 +391,9 @@ int oracle_backward(int n, int L, int B, uint32_t zmask, uint32_t xmask, const d
         cplx *psi = (cplx *)malloc(sizeof(cplx) * (size_t)dim);
         cplx *lam = (cplx *)malloc(sizeof(cplx) * (size_t)dim);
         if (!psi || !lam) { free(psi); free(lam); err |= 1; continue; }
-        run_circuit(psi, n, L, x + (size_t)b * n, theta, par);
+        run_circuit(psi, n, L, x + (size_t)b * n, theta, ent, par);
         if (expz) expz[b] = expect_obs(psi, lam, n, zmask, xmask, par);
-        adjoint_sample(psi, lam, n, L, theta, zmask, xmask, dLdE[b], per + (size_t)b * P, par);
+        adjoint_sample(psi, lam, n, L, theta, zmask, xmask, ent, dLdE[b], per + (size_t)b * P, par);
         free(psi);
         free(lam);
     }
@@ -357,11 +409,11 @@ int oracle_backward(int n, int L, int B, uint32_t zmask, uint32_t xmask, const d
 /* One training step with the mean-squared-error loss on <O>:
  * loss = (1/B) sum_b (E_b - y_b)^2, dL/dE_b = 2 (E_b - y_b) / B.
  * Each sample is simulated once: forward, E_b, then its adjoint sweep. */
-int oracle_train_step(int n, int L, int B, uint32_t zmask, uint32_t xmask, const double *x, const double *theta,
-                      const double *y, double *expz, double *loss, double *grad)
+int oracle_train_step(int n, int L, int B, uint32_t zmask, uint32_t xmask, int ent, const double *x,
+                      const double *theta, const double *y, double *expz, double *loss, double *grad)
 {
     if (n < 1 || n > 30 || L < 0 || B < 1 || !x || !y || !expz || !loss || (L > 0 && (!theta || !grad)) ||
-        bad_mask(n, zmask, xmask))
+        bad_mask(n, zmask, xmask) || bad_ent(ent))
         return -1;
     const size_t P = (size_t)L * n * 3;
     const int par = choose_par(n, B);
@@ -374,10 +426,10 @@ int oracle_train_step(int n, int L, int B, uint32_t zmask, uint32_t xmask, const
         cplx *psi = (cplx *)malloc(sizeof(cplx) * (size_t)dim);
         cplx *lam = (cplx *)malloc(sizeof(cplx) * (size_t)dim);
         if (!psi || !lam) { free(psi); free(lam); err |= 1; continue; }
-        run_circuit(psi, n, L, x + (size_t)b * n, theta, par);
+        run_circuit(psi, n, L, x + (size_t)b * n, theta, ent, par);
         expz[b] = expect_obs(psi, lam, n, zmask, xmask, par);
         const double g = 2.0 * (expz[b] - y[b]) / (double)B;
-        adjoint_sample(psi, lam, n, L, theta, zmask, xmask, g, per + (size_t)b * P, par);
+        adjoint_sample(psi, lam, n, L, theta, zmask, xmask, ent, g, per + (size_t)b * P, par);
         free(psi);
         free(lam);
     }

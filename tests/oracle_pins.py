@@ -13,6 +13,11 @@ Sources of the facts:
     1.1, citing Mitarai et al. 2018): for a gate exp(-i t s/2) the exact
     derivative is [E(t + pi/2) - E(t - pi/2)] / 2.
   * Ry(t)|0> has <Z> = cos t (textbook).
+  * CNOT entangler (same page, section 3.2: CNOT gates permute amplitude indices):
+    the chain CNOT(0,1), CNOT(1,2), ..., CNOT(n-2,n-1) maps |i> to |P(i)>, bit k of
+    P(i) being the parity of bits 0..k of i.  Conjugating Pauli strings by it
+    (textbook Clifford algebra): P^dag Z_k P = Z_0 Z_1 ... Z_k and
+    P^dag X_q P = X_q X_(q+1) (q < n-1), P^dag X_(n-1) P = X_(n-1).
 """
 from __future__ import annotations
 
@@ -259,6 +264,78 @@ def pin_pauli_dense_and_parameter_shift(o):
     assert np.max(np.abs(g - ref)) < 1e-12, np.max(np.abs(g - ref))
 
 
+def _single_qubit_bloch(xq, th_q):
+    """<X>, <Y>, <Z> of Rz Ry Rx Ry(xq)|0> (one qubit, gates from the matrix exponential)."""
+    v = dense.rot("Y", xq) @ np.array([1.0, 0.0], dtype=np.complex128)
+    for a, ax in enumerate(dense.AXES):
+        v = dense.rot(ax, th_q[a]) @ v
+    return {s: float(np.real(np.vdot(v, dense.PAULI[s] @ v))) for s in dense.AXES}
+
+
+def pin_cnot_one_layer_product_closed_form(o):
+    """One layer with the CNOT chain: the state is P applied to a product state, so
+    for a Pauli string O, E = <prod| P^dag O P |prod> factors into single-qubit
+    expectations: <Z_k> = prod_{q <= k} <Z>_q, <X_q> = <X>_q <X>_(q+1), <X_(n-1)> =
+    <X>_(n-1), <Y_0> = <Y>_0 <X>_1 (Y_0 = i X_0 Z_0).  A reversed chain, swapped
+    control and target or a missing gate gives different products."""
+    n = 4
+    x, th = _rand(n, 1, 3, 1200)
+    for b in range(x.shape[0]):
+        bl = [_single_qubit_bloch(x[b, q], th[0, q]) for q in range(n)]
+        cases = [(1 << k, 0, np.prod([bl[q]["Z"] for q in range(k + 1)])) for k in range(n)]
+        cases += [(0, 1 << q, bl[q]["X"] * bl[q + 1]["X"]) for q in range(n - 1)]
+        cases += [(0, 1 << (n - 1), bl[n - 1]["X"]), (1, 1, bl[0]["Y"] * bl[1]["X"])]
+        for zm, xm, ref in cases:
+            e = o.forward(x[b:b + 1], th, zm, xm, entangler=1)[0]
+            assert abs(e - ref) < 1e-13, (b, zm, xm, e, ref)
+
+
+def pin_cnot_dense_and_parameter_shift(o):
+    """CNOT entangler: state, E and the adjoint gradient equal the dense checker's
+    (n <= 4; CNOT there is |0><0| x I + |1><1| x X), and the exact parameter-shift
+    derivative (n = 5); every gate stays unitary."""
+    for n, L, zm, xm in ((2, 2, 1, 0), (3, 2, 0b100, 0), (3, 3, 0b101, 0b011), (4, 2, 0b0110, 0b1100), (4, 3, 1, 0)):
+        x, th = _rand(n, L, 2, 1300 + 10 * n + L)
+        s = o.state(x[0], th, entangler=1)
+        assert np.max(np.abs(s - dense.state(x[0], th, entangler=1))) < 1e-12, (n, L)
+        e = o.forward(x, th, zm, xm, entangler=1)
+        ed = np.array([dense.expz(x[b], th, zm, xm, entangler=1) for b in range(2)])
+        assert np.max(np.abs(e - ed)) < 1e-12, (n, L, zm, xm)
+        w = np.array([0.8, -1.2])
+        g, _ = o.backward(x, th, w, zm, xm, entangler=1)
+        gd = sum(w[b] * dense.grad_expz(x[b], th, zm, xm, entangler=1) for b in range(2))
+        assert np.max(np.abs(g - gd)) < 1e-12, (n, L, zm, xm)
+    n, L, zm, xm = 5, 2, 0b00100, 0b00001
+    x, th = _rand(n, L, 2, 1350)
+    w = np.array([1.0, -0.6])
+    g, _ = o.backward(x, th, w, zm, xm, entangler=1)
+    ref = np.zeros_like(th)
+    for idx in np.ndindex(th.shape):
+        tp, tm = th.copy(), th.copy()
+        tp[idx] += math.pi / 2
+        tm[idx] -= math.pi / 2
+        ref[idx] = np.sum(w * (o.forward(x, tp, zm, xm, entangler=1) - o.forward(x, tm, zm, xm, entangler=1)) / 2)
+    assert np.max(np.abs(g - ref)) < 1e-12, np.max(np.abs(g - ref))
+    assert o.max_norm_drift(x[0], th, entangler=1) < 1e-13
+
+
+def pin_cnot_light_cone(o):
+    """CNOT entangler, O = Z_0: qubit 0 is only ever a control, so Z_0 passes the last
+    chain unchanged, and each earlier chain widens the cone by one qubit upward
+    (X_q -> X_q X_(q+1)): for L < n, E and the gradient only involve qubits 0..L-1."""
+    n, L = 8, 3
+    x, th = _rand(n, L, 2, 1400)
+    e = o.forward(x, th, entangler=1)
+    assert np.max(np.abs(e - o.forward(x[:, :L], th[:, :L, :], entangler=1))) < 1e-13
+    g, _ = o.backward(x, th, np.array([0.6, -1.0]), entangler=1)
+    for l in range(L):
+        for q in range(n):
+            if q > L - 1 - l:
+                assert np.max(np.abs(g[l, q])) < 1e-14, (l, q, g[l, q])
+    g_small, _ = o.backward(x[:, :L], th[:, :L, :], np.array([0.6, -1.0]), entangler=1)
+    assert np.max(np.abs(g[:, :L, :] - g_small)) < 1e-13
+
+
 ALL_PINS = [
     pin_ry_closed_form,
     pin_one_layer_closed_form,
@@ -274,4 +351,7 @@ ALL_PINS = [
     pin_zstring_dense_and_parameter_shift,
     pin_pauli_product_state,
     pin_pauli_dense_and_parameter_shift,
+    pin_cnot_one_layer_product_closed_form,
+    pin_cnot_dense_and_parameter_shift,
+    pin_cnot_light_cone,
 ]

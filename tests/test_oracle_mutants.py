@@ -23,8 +23,8 @@ MUTANTS = [
      "g.m[0] = c + I * s; g.m[1] = 0; g.m[2] = 0; g.m[3] = c - I * s;", 0),
     ("full_angle", "const double c = cos(0.5 * t), s = sin(0.5 * t);",
      "const double c = cos(t), s = sin(t);", 0),
-    ("cz_chain_short", "for (int q = 0; q + 1 < n; ++q) apply_cz(psi, n, q, par);",
-     "for (int q = 0; q + 2 < n; ++q) apply_cz(psi, n, q, par);", 0),
+    ("entangler_chain_short", "for (int q = 0; q + 1 < n; ++q) {\n        if (ent == ENT_CNOT)",
+     "for (int q = 0; q + 2 < n; ++q) {\n        if (ent == ENT_CNOT)", 0),
     ("cz_wrong_pair", "const int64_t both = ((int64_t)1 << q) | ((int64_t)1 << (q + 1));",
      "const int64_t both = ((int64_t)1 << q) | ((int64_t)1 << ((q + 2) % n));", 0),
     ("gate_order_zyx", "for (int a = 0; a < 3; ++a)\n                apply_1q(psi, n, q, rotation(a,",
@@ -51,6 +51,13 @@ MUTANTS = [
      "acc += creal(lam[i] * di) + creal(lam[j] * dj);", 0),
     ("mse_no_mean", "const double g = 2.0 * (expz[b] - y[b]) / (double)B;",
      "const double g = 2.0 * (expz[b] - y[b]);", 0),
+    ("cnot_control_target_swapped", "apply_cnot(psi, n, q, q + 1, par);",
+     "apply_cnot(psi, n, q + 1, q, par);", 0),
+    ("cnot_chain_reversed", "apply_cnot(psi, n, q, q + 1, par);",
+     "apply_cnot(psi, n, n - 2 - q, n - 1 - q, par);", 0),
+    ("cnot_undo_in_circuit_order", "for (int q = n - 2; q >= 0; --q) {\n        if (ent == ENT_CNOT)",
+     "for (int q = 0; q + 1 < n; ++q) {\n        if (ent == ENT_CNOT)", 0),
+    ("cnot_swaps_every_pair", "if (!(i & cb) || (i & tb)) continue;", "if (i & tb) continue;", 0),
     ("theta_index_transposed", "rotation(a, theta[((size_t)l * n + q) * 3 + a]), par);",
      "rotation(a, theta[((size_t)q * (L > 0 ? L : 1) + (l % (n > 0 ? n : 1))) * 3 + a]), par);", 0),
 ]
