@@ -75,6 +75,18 @@ typedef enum {
                                    only, no checkpointing */
 } hqml_fusion;
 
+typedef enum {
+    HQML_ENT_CZ = 0,            /* every layer ends with CZ(q, q+1), q = 0..n-2 (section 2.1) */
+    HQML_ENT_CNOT = 1           /* every layer ends with CNOT(q, q+1) (control q, target q+1) for
+                                   q = 0, 1, ..., n-2 in that order, a permutation of the amplitude
+                                   indices (section 3.2 fuses CNOTs by recomputing indices).
+                                   Offered where a sample's whole state is on chip (n_qubits <= 13,
+                                   the index map is applied in local memory) and by the
+                                   HQML_GATE_BY_GATE comparator at any width; a fused context with
+                                   n_qubits >= 14 returns HQML_ERR_UNSUPPORTED (the map mixes every
+                                   index bit, so it cannot be applied inside a tile pass) */
+} hqml_entangler;
+
 typedef struct {
     int n_qubits;      /* 1..29 */
     int n_layers;      /* >= 1 */
@@ -95,6 +107,7 @@ typedef struct {
                           0..n_qubits-1.  With X/Y factors and n_qubits >= 14, at most 9 of
                           them may sit on qubits >= 4 (they must fit one tile view) */
     int obs_x_mask;
+    int entangler;     /* hqml_entangler; 0 = HQML_ENT_CZ */
 } hqml_config;
 
 /* Device bytes hqml_create would reserve for cfg.  Host-only: makes no HIP call.

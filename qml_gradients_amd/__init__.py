@@ -28,6 +28,8 @@ HQML_COMPUTE_FP32 = 0
 HQML_COMPUTE_FP64 = 1
 HQML_FUSED = 0
 HQML_GATE_BY_GATE = 1
+HQML_ENT_CZ = 0
+HQML_ENT_CNOT = 1
 HQML_K_FWD_PASS, HQML_K_BWD_PASS, HQML_K_SMALL, HQML_K_OTHER, HQML_K_GATE, HQML_K_COUNT = range(6)
 
 
@@ -44,6 +46,7 @@ class hqml_config(ctypes.Structure):
         ("compute", ctypes.c_int),
         ("obs_mask", ctypes.c_int),
         ("obs_x_mask", ctypes.c_int),
+        ("entangler", ctypes.c_int),
     ]
 
 
@@ -101,13 +104,14 @@ EXPORTED = ("hqml_workspace_bytes", "hqml_create", "hqml_destroy", "hqml_forward
 
 
 def make_config(n_qubits, n_layers, max_batch, storage="fp32", ckpt_block=0, device=0, stream=None,
-                fusion="fused", obs_mask=0, compute="fp32", obs_x_mask=0):
+                fusion="fused", obs_mask=0, compute="fp32", obs_x_mask=0, entangler="cz"):
     st = {"fp32": HQML_STORE_FP32, "bf16": HQML_STORE_BF16, "fp64": HQML_STORE_FP64}.get(storage, storage)
     fu = {"fused": HQML_FUSED, "gate_by_gate": HQML_GATE_BY_GATE}.get(fusion, fusion)
     co = {"fp32": HQML_COMPUTE_FP32, "fp64": HQML_COMPUTE_FP64}.get(compute, compute)
+    en = {"cz": HQML_ENT_CZ, "cnot": HQML_ENT_CNOT}.get(entangler, entangler)
     return hqml_config(int(n_qubits), int(n_layers), int(max_batch), int(st), int(ckpt_block),
                        int(device), ctypes.c_void_p(stream or 0), int(fu), int(co), int(obs_mask),
-                       int(obs_x_mask))
+                       int(obs_x_mask), int(en))
 
 
 # ---- the C entry points, same names, argument marshalling only ----
@@ -202,7 +206,7 @@ class Context:
     """
 
     def __init__(self, n_qubits, n_layers, max_batch, storage="fp32", ckpt_block=0, device=None,
-                 stream=None, fusion="fused", obs_mask=0, compute="fp32", obs_x_mask=0):
+                 stream=None, fusion="fused", obs_mask=0, compute="fp32", obs_x_mask=0, entangler="cz"):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("hqml needs a GPU (torch.cuda.is_available() is False)")
@@ -213,7 +217,7 @@ class Context:
         self.device = torch.device("cuda", dev)
         self.n, self.L, self.max_batch = int(n_qubits), int(n_layers), int(max_batch)
         self.cfg = make_config(n_qubits, n_layers, max_batch, storage, ckpt_block, dev, stream, fusion,
-                               obs_mask, compute, obs_x_mask)
+                               obs_mask, compute, obs_x_mask, entangler)
         self.f64 = compute == "fp64" or compute == HQML_COMPUTE_FP64
         self.dtype = torch.float64 if self.f64 else torch.float32
         self.handle = hqml_create(self.cfg)

@@ -24,7 +24,8 @@ namespace hqml {
 // Type codes: io64 = caller arrays are double; r64 = compute in double; storage 0/1/2 =
 // fp32 / bf16 / fp64 saved states.
 hipError_t launch_prep(const void *theta, const void *x, int io64, int L, int n, int B, double *zyz,
-                       unsigned char *G, void *rot_tf, void *dw, double *H, void *init_u, int r64, hipStream_t s);
+                       unsigned char *G, void *rot_tf, void *dw, double *H, void *init_u, int cnot, int r64,
+                       hipStream_t s);
 hipError_t launch_tile_fwd(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s);
 hipError_t launch_tile_obs(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s);
 hipError_t launch_tile_bwd(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s);
@@ -42,6 +43,7 @@ hipError_t launch_gbg_zero(float2 *psi, int n, int B, hipStream_t s);
 hipError_t launch_gbg_rot(int gate, float2 *psi, int n, int B, int q, const float *ang, int ang_stride,
                           hipStream_t s);
 hipError_t launch_gbg_cz(float2 *psi, float2 *lam, int n, int B, int q, hipStream_t s);
+hipError_t launch_gbg_cnot(float2 *psi, float2 *lam, int n, int B, int q, hipStream_t s);
 hipError_t launch_gbg_expz(const float2 *psi, int n, int B, uint32_t obs, uint32_t obs_x, float *e_part,
                            hipStream_t s);
 hipError_t launch_gbg_seed(const float2 *psi, float2 *lam, int n, int B, uint32_t obs, uint32_t obs_x,
@@ -256,7 +258,7 @@ int prep(hqml_ctx *c, int B, const void *x, const void *theta, int io64)
 {
     return run(c, HQML_K_OTHER, "table preparation", [&] {
         return launch_prep(theta, x, io64, c->plan.L, c->plan.n, B, c->zyz, c->frame, c->rot_tf, c->dw, c->H,
-                           c->init_u, c->r64, c->stream);
+                           c->init_u, c->cfg.entangler == HQML_ENT_CNOT, c->r64, c->stream);
     });
 }
 
@@ -305,7 +307,15 @@ int check_config(const hqml_config *cfg, Plan *plan, std::string *err)
         *err = "the gate-by-gate comparator supports fp32 storage and compute without checkpointing only";
         return HQML_ERR_UNSUPPORTED;
     }
+    if (cfg->entangler != HQML_ENT_CZ && cfg->entangler != HQML_ENT_CNOT) {
+        *err = "entangler must be HQML_ENT_CZ or HQML_ENT_CNOT";
+        return HQML_ERR_ARG;
+    }
     if (!make_plan(cfg->n_qubits, cfg->n_layers, cfg->ckpt_block, plan, err)) return HQML_ERR_ARG;
+    if (cfg->entangler == HQML_ENT_CNOT && !plan->small && cfg->fusion == HQML_FUSED) {
+        *err = "the CNOT entangler is offered for n_qubits <= 13 and by the gate-by-gate comparator";
+        return HQML_ERR_UNSUPPORTED;
+    }
     if (cfg->obs_x_mask != 0 && !plan->small && cfg->fusion == HQML_FUSED) {
         ViewDev ov;
         if (!make_obs_view(cfg->n_qubits, (uint32_t)cfg->obs_x_mask, &ov, err)) return HQML_ERR_UNSUPPORTED;
@@ -422,6 +432,7 @@ SmallArgs small_args(hqml_ctx *c, int mode)
     a.n = c->plan.n;
     a.L = c->plan.L;
     a.mode = mode;
+    a.ent = c->cfg.entangler;
     a.obs = c->obs;
     a.obs_x = c->obs_x;
     return a;
@@ -438,6 +449,7 @@ Workspace workspace_for(const hqml_config *cfg, const Plan &plan)
 int gbg_forward_sweep(hqml_ctx *c, int B, const float *x, const float *theta)
 {
     const int n = c->plan.n, L = c->plan.L;
+    const bool cnot = c->cfg.entangler == HQML_ENT_CNOT;
     float2 *psi = reinterpret_cast<float2 *>(c->gbg_psi);
     int rc = run(c, HQML_K_OTHER, "theta copy",
                  [&] { return launch_gbg_copy(theta, L * n * 3, c->gbg_theta, c->stream); });
@@ -457,7 +469,10 @@ int gbg_forward_sweep(hqml_ctx *c, int B, const float *x, const float *theta)
                      })))
                     return rc;
         for (int q = 0; q + 1 < n; ++q)
-            if ((rc = run(c, HQML_K_GATE, "CZ gate", [&] { return launch_gbg_cz(psi, nullptr, n, B, q, c->stream); })))
+            if ((rc = run(c, HQML_K_GATE, "entangling gate", [&] {
+                     return cnot ? launch_gbg_cnot(psi, nullptr, n, B, q, c->stream)
+                                 : launch_gbg_cz(psi, nullptr, n, B, q, c->stream);
+                 })))
                 return rc;
     }
     return run(c, HQML_K_GATE, "<O> partials",
@@ -469,6 +484,7 @@ int gbg_forward_sweep(hqml_ctx *c, int B, const float *x, const float *theta)
 int gbg_backward_sweep(hqml_ctx *c, int B)
 {
     const int n = c->plan.n, L = c->plan.L;
+    const bool cnot = c->cfg.entangler == HQML_ENT_CNOT;
     float2 *psi = reinterpret_cast<float2 *>(c->gbg_psi);
     float2 *lam = reinterpret_cast<float2 *>(c->gbg_lam);
     const size_t per_gate = (size_t)B * c->gbg_blocks;
@@ -476,8 +492,10 @@ int gbg_backward_sweep(hqml_ctx *c, int B)
                  [&] { return launch_gbg_seed(psi, lam, n, B, c->obs, c->obs_x, c->stream); });
     if (rc) return rc;
     for (int l = L - 1; l >= 0; --l) {
-        for (int q = n - 2; q >= 0; --q)
-            if ((rc = run(c, HQML_K_GATE, "CZ adjoint", [&] { return launch_gbg_cz(psi, lam, n, B, q, c->stream); })))
+        for (int q = n - 2; q >= 0; --q)   // self-inverse gates, undone in reverse order
+            if ((rc = run(c, HQML_K_GATE, "entangling gate adjoint", [&] {
+                     return cnot ? launch_gbg_cnot(psi, lam, n, B, q, c->stream) : launch_gbg_cz(psi, lam, n, B, q, c->stream);
+                 })))
                 return rc;
         for (int q = n - 1; q >= 0; --q)
             for (int g = 2; g >= 0; --g) {

@@ -4,7 +4,8 @@
 // backward pass visits the gates one at a time, as an unfused adjoint simulator
 // does (the comparison of fused against gate-by-gate execution in the hugo-pages
 // summary, sections 2.1 and 2.2):
-//   forward   psi <- U psi for every encoding gate, rotation and CZ in circuit order;
+//   forward   psi <- U psi for every encoding gate, rotation and entangling gate (CZ or
+//             CNOT) in circuit order;
 //   adjoint   for every gate in reverse order, with psi and lambda at the point just
 //             after the gate: grad += (1/2) Im<lambda| sigma |psi> for a rotation
 //             exp(-i t sigma / 2) (the gate's term Re<lambda| dU/dt |psi_prev>), then
@@ -117,6 +118,24 @@ __global__ void __launch_bounds__(kGbgThreads) k_gbg_cz(float2 *psi, float2 *lam
     if (lam) {
         v = lam[o];
         lam[o] = make_float2(-v.x, -v.y);
+    }
+}
+
+// CNOT(q, q+1) (control q, target q+1): swap the amplitudes whose bit q is set and whose
+// bit q+1 differs, in psi and (if given) lambda.  Grid (ceil((N / 4) / 256), B).
+__global__ void __launch_bounds__(kGbgThreads) k_gbg_cnot(float2 *psi, float2 *lam, uint32_t N, int q)
+{
+    const uint32_t k = blockIdx.x * kGbgThreads + threadIdx.x;
+    if (k >= (N >> 2)) return;
+    const uint32_t i = ((k >> q) << (q + 2)) | (1u << q) | (k & ((1u << q) - 1u));
+    const size_t o0 = (size_t)blockIdx.y * N + i, o1 = o0 + ((size_t)1 << (q + 1));
+    float2 v = psi[o0];
+    psi[o0] = psi[o1];
+    psi[o1] = v;
+    if (lam) {
+        v = lam[o0];
+        lam[o0] = lam[o1];
+        lam[o1] = v;
     }
 }
 
@@ -262,6 +281,13 @@ hipError_t launch_gbg_cz(float2 *psi, float2 *lam, int n, int B, int q, hipStrea
 {
     const uint32_t N = 1u << n, quarter = N >> 2;
     k_gbg_cz<<<dim3((quarter + kGbgThreads - 1) / kGbgThreads, (unsigned)B), kGbgThreads, 0, s>>>(psi, lam, N, q);
+    return hipGetLastError();
+}
+
+hipError_t launch_gbg_cnot(float2 *psi, float2 *lam, int n, int B, int q, hipStream_t s)
+{
+    const uint32_t N = 1u << n, quarter = N >> 2;
+    k_gbg_cnot<<<dim3((quarter + kGbgThreads - 1) / kGbgThreads, (unsigned)B), kGbgThreads, 0, s>>>(psi, lam, N, q);
     return hipGetLastError();
 }
 

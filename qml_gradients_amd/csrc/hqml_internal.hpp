@@ -110,6 +110,7 @@ struct SmallArgs {
     int n;
     int L;
     int mode;               // 0: forward only; 1: backward only (from psi_save); 2: both
+    int ent;                // entangler closing each layer: 0 CZ chain, 1 CNOT chain
     uint32_t obs;           // observable: Z part of the Pauli string (qubit mask)
     uint32_t obs_x;         // observable: X part (qubits in both masks carry Y = iXZ)
 };

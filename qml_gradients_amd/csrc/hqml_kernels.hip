@@ -1170,7 +1170,217 @@ __device__ __forceinline__ uint32_t pair_index(uint32_t k, int q)
     return ((k >> q) << (q + 1)) | (k & ((1u << q) - 1u));
 }
 
+// X, Y, Z statistics S = Im<lambda|sigma_q|psi> of every qubit at the current point,
+// reduced over the workgroup (fp64 sum of 16 row partials), into a.stats[b][l][q][*].
 template <typename R>
+__device__ __forceinline__ void small_stats(const V2<R> *psi, const V2<R> *lam, const SmallArgs &a, int l, R *red)
+{
+    const int n = a.n, L = a.L;
+    const uint32_t N = 1u << n;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int q = 0; q < n; ++q) {
+        R sx = 0, sy = 0, sz = 0;
+        for (uint32_t k = tid; k < N / 2; k += kThreads) {
+            const uint32_t i = pair_index(k, q), j = i | (1u << q);
+            const V2<R> pi_ = psi[i], pj = psi[j], li = lam[i], lj = lam[j];
+            sx += li.x * pj.y - li.y * pj.x + lj.x * pi_.y - lj.y * pi_.x;
+            sy += lj.x * pi_.x + lj.y * pi_.y - li.x * pj.x - li.y * pj.y;
+            sz += (li.x * pi_.y - li.y * pi_.x) - (lj.x * pj.y - lj.y * pj.x);
+        }
+        sx = row_sum16(sx);
+        sy = row_sum16(sy);
+        sz = row_sum16(sz);
+        if ((lane & 15) == 15) {
+            const int r = w * 4 + (lane >> 4);
+            red[(q * 3 + 0) * 16 + r] = sx;
+            red[(q * 3 + 1) * 16 + r] = sy;
+            red[(q * 3 + 2) * 16 + r] = sz;
+        }
+    }
+    __syncthreads();
+    if (tid < 3 * n) {
+        double s = 0.0;
+        for (int k = 0; k < 16; ++k) s += (double)red[tid * 16 + k];
+        a.stats[(((size_t)b * L + l) * n) * 3 + tid] = s;
+    }
+}
+
+// ---- CNOT entangler (whole state in local memory)
+//
+// The chain CNOT(0,1), CNOT(1,2), ..., CNOT(n-2,n-1), applied in that order, sends basis
+// state |i> to |P(i)> where bit k of P(i) is the parity of bits 0..k of i; its inverse
+// is P^-1(j) = j ^ (j << 1).  The chain is applied by moving amplitudes to their new
+// indices (the hugo-pages summary, section 3.2, fuses CNOTs by recomputing indices).
+__device__ __forceinline__ uint32_t cnot_chain(uint32_t i, uint32_t mask)
+{
+    i ^= i << 1;
+    i ^= i << 2;
+    i ^= i << 4;
+    i ^= i << 8;   // parities of up to 16 low bits; n <= 13 here
+    return i & mask;
+}
+
+__device__ __forceinline__ uint32_t cnot_chain_inv(uint32_t j, uint32_t mask) { return (j ^ (j << 1)) & mask; }
+
+// In-place permutation of a state in local memory: INV = false applies the chain
+// (buf[j] <- buf[P^-1(j)]), INV = true its inverse (buf[i] <- buf[P(i)]).  Every thread
+// reads all its sources into registers before any thread writes.
+template <bool INV, typename R>
+__device__ __forceinline__ void small_permute(V2<R> *buf, uint32_t N)
+{
+    constexpr int kPer = (1 << kSmallMaxQubits) / kThreads;
+    const uint32_t mask = N - 1, tid = threadIdx.x;
+    V2<R> tmp[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const uint32_t i = tid + (uint32_t)r * kThreads;
+        if (i < N) tmp[r] = buf[INV ? cnot_chain(i, mask) : cnot_chain_inv(i, mask)];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const uint32_t i = tid + (uint32_t)r * kThreads;
+        if (i < N) buf[i] = tmp[r];
+    }
+    __syncthreads();
+}
+
+// Factor of amplitude i in prod_q diag(f_q, conj f_q); f_q = (x, y) of wl[q] (SECOND =
+// false) or (z, w) (SECOND = true).
+template <bool SECOND, typename R>
+__device__ __forceinline__ V2<R> small_phase(const V4<R> *wl, int n, uint32_t i)
+{
+    V2<R> f = mk2((R)1, (R)0);
+    for (int q = 0; q < n; ++q) {
+        const V4<R> g = wl[q];
+        V2<R> h = SECOND ? mk2(g.z, g.w) : mk2(g.x, g.y);
+        if ((i >> q) & 1u) h.y = -h.y;
+        f = cmul(f, h);
+    }
+    return f;
+}
+
+// Real rotation layer Ry(beta_{l,q}) on every qubit (INV: its inverse) of one state;
+// cs[l][q] = (sin, cos) of beta/2.
+template <bool INV, typename R>
+__device__ __forceinline__ void small_ry_layer(V2<R> *st, const V2<R> *cs, int n, uint32_t N)
+{
+    for (int q = 0; q < n; ++q) {
+        const R s = INV ? -cs[q].x : cs[q].x, c = cs[q].y;
+        for (uint32_t k = threadIdx.x; k < N / 2; k += kThreads) {
+            const uint32_t i = pair_index(k, q), j = i | (1u << q);
+            const V2<R> x = st[i], y = st[j];
+            st[i] = mk2(c * x.x - s * y.x, c * x.y - s * y.y);
+            st[j] = mk2(s * x.x + c * y.x, s * x.y + c * y.y);
+        }
+        __syncthreads();
+    }
+}
+
+// Whole circuit of one sample with the CNOT entangler.  Per layer l the simulated
+// sequence is diag(r_l), Ry-layer l, diag(p_l), then the chain (U_{l,q} =
+// diag(p) Ry(beta) diag(r); layer 0 up to Ry is the product state init_u).  The
+// statistics are taken at P_l, just after Ry-layer l, as on the CZ path, so the same
+// gradient map applies (with no Pauli frame).  lambda at P_{L-1} is
+// D^dag P^dag O P D psi with D = diag(p_{L-1}):
+//   lambda_i = conj(D_i) c(P(i)) D_(i^x') psi_(i^x'),  x' = P^-1(xm),
+//   c(j) = i^(#Y) (-1)^|(j ^ xm) & zm|,
+// and E = Re <psi|lambda>.
+template <typename R>
+__device__ void small_cnot_circuit(const SmallArgs &a, V2<R> *psi, V2<R> *lam, R *red)
+{
+    const int n = a.n, L = a.L;
+    const uint32_t N = 1u << n, mask = N - 1;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const V2<R> *rcs = reinterpret_cast<const V2<R> *>(a.rot_tf);
+    const V4<R> *dw = reinterpret_cast<const V4<R> *>(a.dw);
+    V2<R> *save = reinterpret_cast<V2<R> *>(a.psi_save) + (size_t)b * N;
+
+    if (a.mode != 1) {
+        const V4<R> *u = reinterpret_cast<const V4<R> *>(a.init_u) + (size_t)b * n;
+        for (uint32_t i = tid; i < N; i += kThreads) {
+            V2<R> v = mk2((R)1, (R)0);
+            for (int q = 0; q < n; ++q) {
+                const V4<R> f = u[q];
+                v = cmul(v, ((i >> q) & 1u) ? mk2(f.z, f.w) : mk2(f.x, f.y));
+            }
+            psi[i] = v;
+        }
+        __syncthreads();
+        for (int l = 0; l + 1 < L; ++l) {
+            const V4<R> *wl = dw + (size_t)l * n, *wn = wl + n;
+            for (uint32_t i = tid; i < N; i += kThreads) psi[i] = cmul(psi[i], small_phase<false, R>(wl, n, i));
+            __syncthreads();
+            small_permute<false, R>(psi, N);
+            for (uint32_t i = tid; i < N; i += kThreads) psi[i] = cmul(psi[i], small_phase<true, R>(wn, n, i));
+            __syncthreads();
+            small_ry_layer<false, R>(psi, rcs + (size_t)(l + 1) * n, n, N);
+        }
+    } else {
+        for (uint32_t i = tid; i < N; i += kThreads) psi[i] = save[i];
+        __syncthreads();
+    }
+
+    const V4<R> *wt = dw + (size_t)(L - 1) * n;
+    const uint32_t zm = a.obs, xm = a.obs_x, xs = cnot_chain_inv(xm, mask);
+    const int yph = __builtin_popcount(zm & xm) & 3;
+    R e = 0;
+    for (uint32_t i = tid; i < N; i += kThreads) {
+        const uint32_t j = i ^ xs;
+        V2<R> v = cmul(small_phase<false, R>(wt, n, j), psi[j]);
+        if (__builtin_popcount((cnot_chain(i, mask) ^ xm) & zm) & 1) v = mk2(-v.x, -v.y);
+        mul_ipow(v.x, v.y, yph);
+        V2<R> d = small_phase<false, R>(wt, n, i);
+        d.y = -d.y;
+        const V2<R> li = cmul(d, v);
+        lam[i] = li;
+        e += psi[i].x * li.x + psi[i].y * li.y;
+    }
+    if (a.mode != 1) {
+        e = row_sum16(e);
+        if ((lane & 15) == 15) red[w * 4 + (lane >> 4)] = e;
+        __syncthreads();
+        if (tid == 0) {
+            double s = 0.0;
+            for (int k = 0; k < 16; ++k) s += (double)red[k];
+            static_cast<R *>(a.e_out)[b] = (R)s;
+        }
+        if (a.mode == 0) {
+            for (uint32_t i = tid; i < N; i += kThreads) save[i] = psi[i];
+            return;
+        }
+    }
+    __syncthreads();
+
+    for (int l = L - 1; l >= 0; --l) {
+        small_stats<R>(psi, lam, a, l, red);
+        if (l == 0) break;
+        __syncthreads();
+        small_ry_layer<true, R>(psi, rcs + (size_t)l * n, n, N);
+        small_ry_layer<true, R>(lam, rcs + (size_t)l * n, n, N);
+        const V4<R> *wl = dw + (size_t)l * n, *wp = wl - n;
+        for (uint32_t i = tid; i < N; i += kThreads) {
+            V2<R> f = small_phase<true, R>(wl, n, i);
+            f.y = -f.y;
+            psi[i] = cmul(psi[i], f);
+            lam[i] = cmul(lam[i], f);
+        }
+        __syncthreads();
+        small_permute<true, R>(psi, N);
+        small_permute<true, R>(lam, N);
+        for (uint32_t i = tid; i < N; i += kThreads) {
+            V2<R> f = small_phase<false, R>(wp, n, i);
+            f.y = -f.y;
+            psi[i] = cmul(psi[i], f);
+            lam[i] = cmul(lam[i], f);
+        }
+        __syncthreads();
+    }
+}
+
+// ENT: the entangler (0 CZ chain, 1 CNOT chain), one instance each so that the CZ
+// kernel keeps its own register budget.
+template <typename R, int ENT>
 __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -1183,6 +1393,10 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
     const V2<R> *rtf = reinterpret_cast<const V2<R> *>(a.rot_tf);
     const V4<R> *dw = reinterpret_cast<const V4<R> *>(a.dw);
     V2<R> *save = reinterpret_cast<V2<R> *>(a.psi_save) + (size_t)b * N;
+    if constexpr (ENT != 0) {
+        small_cnot_circuit<R>(a, psi, lam, red);
+        return;
+    }
 
     if (a.mode != 1) {
         const V4<R> *u = reinterpret_cast<const V4<R> *>(a.init_u) + (size_t)b * n;
@@ -1250,31 +1464,7 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
     }
     __syncthreads();
     for (int l = L - 1; l >= 0; --l) {
-        for (int q = 0; q < n; ++q) {
-            R sx = 0, sy = 0, sz = 0;
-            for (uint32_t k = tid; k < N / 2; k += kThreads) {
-                const uint32_t i = pair_index(k, q), j = i | (1u << q);
-                const V2<R> pi_ = psi[i], pj = psi[j], li = lam[i], lj = lam[j];
-                sx += li.x * pj.y - li.y * pj.x + lj.x * pi_.y - lj.y * pi_.x;
-                sy += lj.x * pi_.x + lj.y * pi_.y - li.x * pj.x - li.y * pj.y;
-                sz += (li.x * pi_.y - li.y * pi_.x) - (lj.x * pj.y - lj.y * pj.x);
-            }
-            sx = row_sum16(sx);
-            sy = row_sum16(sy);
-            sz = row_sum16(sz);
-            if ((lane & 15) == 15) {
-                const int r = w * 4 + (lane >> 4);
-                red[(q * 3 + 0) * 16 + r] = sx;
-                red[(q * 3 + 1) * 16 + r] = sy;
-                red[(q * 3 + 2) * 16 + r] = sz;
-            }
-        }
-        __syncthreads();
-        if (tid < 3 * n) {
-            double s = 0.0;
-            for (int k = 0; k < 16; ++k) s += (double)red[tid * 16 + k];
-            a.stats[(((size_t)b * L + l) * n) * 3 + tid] = s;
-        }
+        small_stats<R>(psi, lam, a, l, red);
         if (l == 0) break;
         // uncompute Ry-layer l and D_{l-1} on psi and lambda
         for (int q = 0; q < n; ++q) {
@@ -1393,7 +1583,8 @@ __global__ void k_prep_zyz(const TI *theta, int L, int n, double *zyz)
 // every gradient statistic).  G[l][q] = parity of the X's from layers after l; the
 // simulated state at P_l is X^G times the original one, so the Y and Z statistics
 // of such qubits change sign, which the gradient map H absorbs.
-__global__ void k_prep_frame(const double *zyz, int L, int n, unsigned char *G)
+// With the CNOT entangler (cnot != 0) no frame is used: G = 0 everywhere.
+__global__ void k_prep_frame(const double *zyz, int L, int n, int cnot, unsigned char *G)
 {
     const int q = blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= n) return;
@@ -1401,7 +1592,7 @@ __global__ void k_prep_frame(const double *zyz, int L, int n, unsigned char *G)
     for (int l = L - 1; l >= 0; --l) {
         G[(size_t)l * n + q] = g;
         const double *z = zyz + ((size_t)l * n + q) * 6;
-        if (l >= 1 && z[1] > z[0]) g ^= 1;
+        if (!cnot && l >= 1 && z[1] > z[0]) g ^= 1;
     }
 }
 
@@ -1412,8 +1603,11 @@ __global__ void k_prep_frame(const double *zyz, int L, int n, unsigned char *G)
 // H[l][q][a][s]: Pauli coefficients of diag(p)^dag G_a diag(p), G_a the generator of
 //   theta[l][q][a] moved to just after U_{l,q} (G_z = Z, G_y = Rz Y Rz^dag,
 //   G_x = Rz Ry X Ry^dag Rz^dag), with the Y and Z coefficients negated where G[l][q].
+// With the CNOT entangler the diagonals cannot merge across the chain (a permutation)
+// and no frame is used: rot_tf[l][q] = (sin(beta/2), cos(beta/2)) and dw[l][q] =
+// (p, r), the factors of diag(p, conj p) after and diag(r, conj r) before Ry(beta).
 template <typename TI, typename R>
-__global__ void k_prep_tables(const TI *theta, const double *zyz, const unsigned char *G, int L, int n,
+__global__ void k_prep_tables(const TI *theta, const double *zyz, const unsigned char *G, int L, int n, int cnot,
                               R *rot_tf, R *dw, double *H)
 {
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
@@ -1421,39 +1615,45 @@ __global__ void k_prep_tables(const TI *theta, const double *zyz, const unsigned
     const int l = idx / n, q = idx - l * n;
     const double *z = zyz + (size_t)idx * 6;
     const bool gq = G[idx] != 0;
-    const bool x_here = l >= 1 && z[1] > z[0];
-    double k = x_here ? -z[0] / z[1] : z[1] / z[0];
-    const double f = x_here ? z[1] : z[0];
-    if (gq) k = -k;
-    rot_tf[idx * 2 + 0] = (R)k;
-    rot_tf[idx * 2 + 1] = (R)f;
-    R *d = dw + (size_t)idx * 4;
-    if (l + 1 < L) {
-        const double *zn = zyz + (size_t)(idx + n) * 6;
-        const cd w = cmk(z[2], z[3]) * cmk(zn[4], zn[5]);
-        cd f0 = w, f1 = cconj(w);
-        if (gq) {
-            const cd t = f0;
-            f0 = f1;
-            f1 = t;
-        }
-        int sflip = (zn[1] > zn[0]) ? 1 : 0;            // Z from the next layer's rewrite
-        if (q > 0) sflip ^= G[idx - 1];                 // CZ(q-1, q) conjugated by X on q-1
-        if (q + 1 < n) sflip ^= G[idx + 1];             // CZ(q, q+1) conjugated by X on q+1
-        if (sflip) f1 = cmk(-f1.re, -f1.im);
-        d[0] = (R)f0.re;
-        d[1] = (R)f0.im;
-        d[2] = (R)f1.re;
-        d[3] = (R)f1.im;
+    if (cnot) {
+        rot_tf[idx * 2 + 0] = (R)z[1];
+        rot_tf[idx * 2 + 1] = (R)z[0];
+        for (int k = 0; k < 4; ++k) dw[(size_t)idx * 4 + k] = (R)z[2 + k];
     } else {
-        // the trailing diagonal (layer L-1's left factors; with the CZ chain it follows the
-        // last Ry layer): never applied by the passes, which drop it since it commutes
-        // with a Z-string observable; Pauli strings with X/Y factors apply it.  No frame
-        // bit reaches past the last layer.
-        d[0] = (R)z[2];
-        d[1] = (R)z[3];
-        d[2] = (R)z[2];
-        d[3] = (R)-z[3];
+        const bool x_here = l >= 1 && z[1] > z[0];
+        double k = x_here ? -z[0] / z[1] : z[1] / z[0];
+        const double f = x_here ? z[1] : z[0];
+        if (gq) k = -k;
+        rot_tf[idx * 2 + 0] = (R)k;
+        rot_tf[idx * 2 + 1] = (R)f;
+        R *d = dw + (size_t)idx * 4;
+        if (l + 1 < L) {
+            const double *zn = zyz + (size_t)(idx + n) * 6;
+            const cd w = cmk(z[2], z[3]) * cmk(zn[4], zn[5]);
+            cd f0 = w, f1 = cconj(w);
+            if (gq) {
+                const cd t = f0;
+                f0 = f1;
+                f1 = t;
+            }
+            int sflip = (zn[1] > zn[0]) ? 1 : 0;            // Z from the next layer's rewrite
+            if (q > 0) sflip ^= G[idx - 1];                 // CZ(q-1, q) conjugated by X on q-1
+            if (q + 1 < n) sflip ^= G[idx + 1];             // CZ(q, q+1) conjugated by X on q+1
+            if (sflip) f1 = cmk(-f1.re, -f1.im);
+            d[0] = (R)f0.re;
+            d[1] = (R)f0.im;
+            d[2] = (R)f1.re;
+            d[3] = (R)f1.im;
+        } else {
+            // the trailing diagonal (layer L-1's left factors; with the CZ chain it follows the
+            // last Ry layer): never applied by the passes, which drop it since it commutes
+            // with a Z-string observable; Pauli strings with X/Y factors apply it.  No frame
+            // bit reaches past the last layer.
+            d[0] = (R)z[2];
+            d[1] = (R)z[3];
+            d[2] = (R)z[2];
+            d[3] = (R)-z[3];
+        }
     }
     const double ay = theta[idx * 3 + 1], az = theta[idx * 3 + 2];
     const m2 X = m2{{cmk(0, 0), cmk(1, 0), cmk(1, 0), cmk(0, 0)}};
@@ -1622,12 +1822,12 @@ namespace hqml {
 
 template <typename TI, typename R>
 static void prep_typed(const void *theta, const void *x, int L, int n, int B, double *zyz, unsigned char *G,
-                       void *rot_tf, void *dw, double *H, void *init_u, hipStream_t s)
+                       void *rot_tf, void *dw, double *H, void *init_u, int cnot, hipStream_t s)
 {
     const int ln = L * n;
     k_prep_zyz<TI><<<(ln + 127) / 128, 128, 0, s>>>(static_cast<const TI *>(theta), L, n, zyz);
-    k_prep_frame<<<1, 64, 0, s>>>(zyz, L, n, G);
-    k_prep_tables<TI, R><<<(ln + 127) / 128, 128, 0, s>>>(static_cast<const TI *>(theta), zyz, G, L, n,
+    k_prep_frame<<<1, 64, 0, s>>>(zyz, L, n, cnot, G);
+    k_prep_tables<TI, R><<<(ln + 127) / 128, 128, 0, s>>>(static_cast<const TI *>(theta), zyz, G, L, n, cnot,
                                                            static_cast<R *>(rot_tf), static_cast<R *>(dw), H);
     if (B > 0)
         k_prep_init<TI, R><<<(B * n + 127) / 128, 128, 0, s>>>(static_cast<const TI *>(x), zyz, G, B, n,
@@ -1635,18 +1835,19 @@ static void prep_typed(const void *theta, const void *x, int L, int n, int B, do
 }
 
 hipError_t launch_prep(const void *theta, const void *x, int io64, int L, int n, int B, double *zyz,
-                       unsigned char *G, void *rot_tf, void *dw, double *H, void *init_u, int r64, hipStream_t s)
+                       unsigned char *G, void *rot_tf, void *dw, double *H, void *init_u, int cnot, int r64,
+                       hipStream_t s)
 {
     if (io64) {
         if (r64)
-            prep_typed<double, double>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, s);
+            prep_typed<double, double>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, cnot, s);
         else
-            prep_typed<double, float>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, s);
+            prep_typed<double, float>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, cnot, s);
     } else {
         if (r64)
-            prep_typed<float, double>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, s);
+            prep_typed<float, double>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, cnot, s);
         else
-            prep_typed<float, float>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, s);
+            prep_typed<float, float>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, cnot, s);
     }
     return hipGetLastError();
 }
@@ -1724,18 +1925,31 @@ hipError_t launch_tile_bwd(const TilePassArgs &a, int B, int storage, int r64, h
 
 hipError_t configure_small(size_t shm_bytes, int r64)
 {
-    const void *f = r64 ? reinterpret_cast<const void *>(&k_small<double>)
-                        : reinterpret_cast<const void *>(&k_small<float>);
-    return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm_bytes);
+    const void *f[2] = {r64 ? reinterpret_cast<const void *>(&k_small<double, 0>)
+                            : reinterpret_cast<const void *>(&k_small<float, 0>),
+                        r64 ? reinterpret_cast<const void *>(&k_small<double, 1>)
+                            : reinterpret_cast<const void *>(&k_small<float, 1>)};
+    for (const void *k : f) {
+        const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm_bytes);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_small(const SmallArgs &a, int B, int r64, hipStream_t s)
 {
     const size_t shm = (size_t)2 * ((size_t)1 << a.n) * (r64 ? sizeof(double2) : sizeof(float2));
-    if (r64)
-        k_small<double><<<B, kThreads, shm, s>>>(a);
-    else
-        k_small<float><<<B, kThreads, shm, s>>>(a);
+    if (r64) {
+        if (a.ent)
+            k_small<double, 1><<<B, kThreads, shm, s>>>(a);
+        else
+            k_small<double, 0><<<B, kThreads, shm, s>>>(a);
+    } else {
+        if (a.ent)
+            k_small<float, 1><<<B, kThreads, shm, s>>>(a);
+        else
+            k_small<float, 0><<<B, kThreads, shm, s>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -1,0 +1,121 @@
+"""CNOT-chain entangler on the GPU vs the oracle (entangler=1).
+
+Every layer ends with CNOT(q, q+1), control q, for q = 0..n-2 in that order.  The
+whole-circuit kernel (n <= 13) applies the chain as a permutation of the amplitude
+indices in local memory; the gate-by-gate comparator runs one kernel per CNOT at any
+width.  Tolerances as for the CZ chain: <O> within 1e-5 relative to
+max(|E|, 2^(-n/2)), gradients within 1e-4 absolute (fp32), 1e-10 (fp64).
+"""
+import numpy as np
+import pytest
+
+import hqml_inputs
+import oracle
+from gpu_util import assert_e_close, assert_grad_close, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+# (n, L, B, z mask, x mask); (0, 0) = Z_0
+SMALL = [
+    (1, 2, 3, 0, 0),
+    (2, 1, 3, 0, 0),
+    (2, 3, 2, 0b10, 0b01),
+    (3, 2, 4, 0b100, 0),
+    (4, 3, 3, 0, 0b0011),
+    (5, 2, 3, 0b10010, 0b00101),
+    (8, 3, 2, 0, 0),
+    (9, 2, 2, 1 << 8, 1 << 3),
+    (12, 3, 2, 0, 0),
+    (13, 2, 2, (1 << 12) | 1, 0),
+    (13, 2, 2, 0b1, (1 << 11) | (1 << 6)),
+]
+
+
+def _masks(zm, xm):
+    return (1, 0) if (zm | xm) == 0 else (zm, xm)
+
+
+def _ctx(n, L, B, zm, xm, **kw):
+    import qml_gradients_amd as hq
+    return hq.Context(n, L, B, obs_mask=zm, obs_x_mask=xm, entangler="cnot", **kw)
+
+
+@pytest.mark.parametrize("n,L,B,zm,xm", SMALL)
+def test_cnot_whole_circuit(n, L, B, zm, xm):
+    say(f"[gpu] CNOT whole circuit n={n} L={L} B={B} z={zm:#x} x={xm:#x}")
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=1600 + 7 * n + L)
+    X, TH, Y = (torch.from_numpy(a) for a in (x, th, y))
+    ctx = _ctx(n, L, B, zm, xm)
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(X, TH, Y))
+    e2 = ctx.forward(X, TH).cpu().numpy()
+    w = np.linspace(-1.0, 1.0, B).astype(np.float32)
+    g2 = ctx.backward(torch.from_numpy(w)).cpu().numpy()
+    ctx.close()
+    oz, ox = _masks(zm, xm)
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, oz, ox, entangler=1)
+    assert_e_close(e, e_ref, n)
+    assert abs(float(loss[0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
+    assert_grad_close(g, g_ref)
+    g2_ref, _ = oracle.backward(x, th, w.astype(np.float64), oz, ox, entangler=1)
+    assert_e_close(e2, e_ref, n)
+    assert_grad_close(g2, g2_ref)
+
+
+def test_cnot_differs_from_cz():
+    """The entangler is really switched: the same inputs give different results."""
+    import qml_gradients_amd as hq
+    n, L, B = 6, 3, 2
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=1700)
+    X, TH = torch.from_numpy(x), torch.from_numpy(th)
+    outs = []
+    for ent in ("cz", "cnot"):
+        ctx = hq.Context(n, L, B, obs_mask=0b100, entangler=ent)
+        outs.append(ctx.forward(X, TH).cpu().numpy())
+        ctx.close()
+    assert_e_close(outs[0], oracle.forward(x, th, 0b100), n)
+    assert_e_close(outs[1], oracle.forward(x, th, 0b100, entangler=1), n)
+    assert np.max(np.abs(outs[0] - outs[1])) > 1e-3
+
+
+def test_cnot_whole_circuit_fp64():
+    n, L, B, zm, xm = 7, 3, 2, 0b0100001, 0b0000110
+    say(f"[gpu] CNOT whole circuit fp64 n={n}")
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=1800)
+    ctx = _ctx(n, L, B, zm, xm, compute="fp64", storage="fp64")
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(*(torch.from_numpy(a).double() for a in (x, th, y))))
+    ctx.close()
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, zm, xm, entangler=1)
+    assert np.max(np.abs(e - e_ref)) < 1e-12
+    assert abs(float(loss[0]) - loss_ref) < 1e-12
+    assert np.max(np.abs(g - g_ref)) < 1e-10
+
+
+def test_cnot_hea12q20l_full():
+    """The 12-qubit, 20-layer, batch-64 shape with the CNOT chain, every sample."""
+    w = hqml_inputs.WORKLOADS["hea12q20l"]
+    x, th, y = hqml_inputs.workload_inputs("hea12q20l")
+    say("[gpu] CNOT hea12q20l")
+    ctx = _ctx(w.n_qubits, w.n_layers, x.shape[0], 0, 0)
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(*(torch.from_numpy(a) for a in (x, th, y))))
+    ctx.close()
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, entangler=1)
+    assert_e_close(e, e_ref, w.n_qubits)
+    assert abs(float(loss[0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
+    assert_grad_close(g, g_ref)
+
+
+@pytest.mark.parametrize("n,L,B,zm,xm", [(2, 2, 3, 0, 0), (5, 2, 2, 0b10010, 0b00101), (13, 2, 2, 0, 0),
+                                         (14, 2, 2, 0, 0), (17, 2, 2, 1 << 16, 1 << 2)])
+def test_cnot_gate_by_gate(n, L, B, zm, xm):
+    say(f"[gpu] CNOT gate-by-gate n={n} L={L}")
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=1900 + n)
+    ctx = _ctx(n, L, B, zm, xm, fusion="gate_by_gate")
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(*(torch.from_numpy(a) for a in (x, th, y))))
+    ctx.close()
+    oz, ox = _masks(zm, xm)
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, oz, ox, entangler=1)
+    assert_e_close(e, e_ref, n)
+    assert abs(float(loss[0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
+    assert_grad_close(g, g_ref)

@@ -108,6 +108,24 @@ def test_pauli_observable_config_host_only():
         assert hq.hqml_workspace_bytes(bad) == 0
 
 
+def test_entangler_config_host_only():
+    _lib()
+    assert hq.hqml_workspace_bytes(hq.make_config(12, 3, 2, entangler="cnot")) > 0
+    assert hq.hqml_workspace_bytes(hq.make_config(13, 3, 2, entangler="cnot", obs_x_mask=0b101)) > 0
+    assert hq.hqml_workspace_bytes(hq.make_config(20, 3, 2, entangler="cnot", fusion="gate_by_gate")) > 0
+    # the tile path applies the chain nowhere: a fused context with n >= 14 is refused
+    tile = hq.make_config(14, 3, 2, entangler="cnot")
+    assert hq.hqml_workspace_bytes(tile) == 0
+    with pytest.raises(hq.HqmlError) as e:
+        hq.hqml_create(tile)
+    assert e.value.status == hq.HQML_ERR_UNSUPPORTED
+    for bad in (hq.make_config(4, 1, 1, entangler=2), hq.make_config(4, 1, 1, entangler=-1)):
+        assert hq.hqml_workspace_bytes(bad) == 0
+        with pytest.raises(hq.HqmlError) as e:
+            hq.hqml_create(bad)
+        assert e.value.status == hq.HQML_ERR_ARG
+
+
 def test_workspace_scaling_checkpoint_and_bf16():
     _lib()
     full = hq.hqml_workspace_bytes(hq.make_config(20, 1000, 60))
