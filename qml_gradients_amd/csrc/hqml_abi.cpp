@@ -23,8 +23,9 @@
 namespace hqml {
 // Type codes: io64 = caller arrays are double; r64 = compute in double; storage 0/1/2 =
 // fp32 / bf16 / fp64 saved states.
+// ent: 0 CZ chain; 1 CNOT chain, whole-circuit tables; 2 CNOT chain, tile tables
 hipError_t launch_prep(const void *theta, const void *x, int io64, int L, int n, int B, double *zyz,
-                       unsigned char *G, void *rot_tf, void *dw, double *H, void *init_u, int cnot, int r64,
+                       unsigned char *G, void *rot_tf, void *dw, double *H, void *init_u, int ent, int r64,
                        hipStream_t s);
 hipError_t launch_tile_fwd(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s);
 hipError_t launch_tile_obs(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s);
@@ -75,6 +76,7 @@ struct hqml_ctx {
     size_t rb = 4;               // bytes of the compute type
     char *saved = nullptr;       // saved states (n_saved buffers of max_batch samples)
     void *lam = nullptr;         // arrays below in the compute type
+    void *lam_alt = nullptr;     // CNOT plan: second lambda buffer for the passes that scatter it
     char *part = nullptr;
     void *e_part = nullptr;
     double *S = nullptr;
@@ -221,6 +223,7 @@ int fwd_pass(hqml_ctx *c, hipStream_t st, Span sp, int p, int extra_flags)
     a.diag = pp.diag;
     a.rotB = pp.rotB;
     a.flags = (pp.init ? PF_INIT : 0) | PF_STORE | extra_flags;
+    if (c->plan.cnot) a.flags |= PF_CNOT | (pp.gather ? PF_GATHER : 0);
     a.sample0 = sp.b0;
     return run_on(c, st, HQML_K_FWD_PASS, "forward pass launch",
                   [&] { return launch_tile_fwd(a, sp.bc, c->cfg.storage, c->r64, st); });
@@ -238,6 +241,15 @@ int bwd_pass(hqml_ctx *c, hipStream_t st, Span sp, int k, int part_lo, char *par
         a.view = c->views + pl.stats_only[k - P];
         a.rotA = a.diag = a.rotB = -1;
         a.flags = PF_STATS_ONLY | PF_INIT;
+        if (pl.cnot) {   // lambda is taken back through diag(p_0) first
+            a.diag = 0;
+            a.flags |= PF_CNOT;
+        }
+    } else if (pl.cnot && k == 0) {   // the product-state pass: its backward is layer-0 statistics
+        a.view = c->views;
+        a.rotA = a.rotB = -1;
+        a.diag = 0;
+        a.flags = PF_STATS_ONLY | PF_INIT | PF_CNOT | (extra_flags & PF_SEED);
     } else {
         const PassPlan &pp = pl.fwd[k];
         a.view = c->views + pp.view;
@@ -245,20 +257,27 @@ int bwd_pass(hqml_ctx *c, hipStream_t st, Span sp, int k, int part_lo, char *par
         a.diag = pp.diag;
         a.rotB = pp.rotB;
         a.flags = (pp.init ? PF_INIT : 0) | extra_flags;
+        if (pl.cnot) a.flags |= PF_CNOT | (pp.gather ? PF_GATHER : 0);
         if (extra_flags & PF_FUSED)
             a.psi_in = k == 0 ? nullptr : pass_out(c, k - 1);
         else
             a.psi_in = pass_out(c, k);
+        // lambda goes back through the chain's index map: other tiles still read the
+        // old lambda, so the pass writes the second buffer and the two swap roles
+        if (pl.cnot && pp.gather) a.psi_out = c->lam_alt;
     }
-    return run_on(c, st, HQML_K_BWD_PASS, "backward pass launch",
-                  [&] { return launch_tile_bwd(a, sp.bc, c->cfg.storage, c->r64, st); });
+    const int rc = run_on(c, st, HQML_K_BWD_PASS, "backward pass launch",
+                          [&] { return launch_tile_bwd(a, sp.bc, c->cfg.storage, c->r64, st); });
+    if (rc == HQML_OK && (a.flags & PF_GATHER)) std::swap(c->lam, c->lam_alt);
+    return rc;
 }
 
 int prep(hqml_ctx *c, int B, const void *x, const void *theta, int io64)
 {
     return run(c, HQML_K_OTHER, "table preparation", [&] {
+        const int ent = c->cfg.entangler != HQML_ENT_CNOT ? 0 : c->plan.small ? 1 : 2;
         return launch_prep(theta, x, io64, c->plan.L, c->plan.n, B, c->zyz, c->frame, c->rot_tf, c->dw, c->H,
-                           c->init_u, c->cfg.entangler == HQML_ENT_CNOT, c->r64, c->stream);
+                           c->init_u, ent, c->r64, c->stream);
     });
 }
 
@@ -311,9 +330,10 @@ int check_config(const hqml_config *cfg, Plan *plan, std::string *err)
         *err = "entangler must be HQML_ENT_CZ or HQML_ENT_CNOT";
         return HQML_ERR_ARG;
     }
-    if (!make_plan(cfg->n_qubits, cfg->n_layers, cfg->ckpt_block, plan, err)) return HQML_ERR_ARG;
-    if (cfg->entangler == HQML_ENT_CNOT && !plan->small && cfg->fusion == HQML_FUSED) {
-        *err = "the CNOT entangler is offered for n_qubits <= 13 and by the gate-by-gate comparator";
+    const bool cnot_tiles = cfg->entangler == HQML_ENT_CNOT && cfg->fusion == HQML_FUSED;
+    if (!make_plan(cfg->n_qubits, cfg->n_layers, cfg->ckpt_block, plan, err, cnot_tiles)) return HQML_ERR_ARG;
+    if (plan->cnot && cfg->obs_x_mask != 0) {
+        *err = "with the CNOT entangler and n_qubits >= 14 the observable must be a Z-string (obs_x_mask = 0)";
         return HQML_ERR_UNSUPPORTED;
     }
     if (cfg->obs_x_mask != 0 && !plan->small && cfg->fusion == HQML_FUSED) {
@@ -570,6 +590,13 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     c->rb = c->r64 ? 8 : 4;
     c->obs = (cfg->obs_mask | cfg->obs_x_mask) ? (uint32_t)cfg->obs_mask : 1u;
     c->obs_x = (uint32_t)cfg->obs_x_mask;
+    if (plan.cnot) {
+        // The tile passes stop before the last layer's CNOT chain P, so they measure
+        // P^dag Z_S P = Z_S' with bit k of S' the parity of the bits k.. of S.
+        uint32_t z = c->obs;
+        for (int sh = 1; sh < 32; sh <<= 1) z ^= z >> sh;
+        c->obs = z;
+    }
     c->ws = workspace_for(cfg, plan);
     c->stream = reinterpret_cast<hipStream_t>(cfg->stream);
     hipError_t e = hipSetDevice(cfg->device);
@@ -623,13 +650,14 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     }
     c->saved = static_cast<char *>(grab((size_t)c->ws.n_saved * c->ws.state_bytes));
     c->lam = grab(c->ws.lam_bytes);
+    if (plan.cnot) c->lam_alt = grab(c->ws.lam_bytes);
     c->part = static_cast<char *>(grab(c->ws.part_bytes));
     c->e_part = grab((size_t)B * plan.T * c->rb);
     c->S = static_cast<double *>(grab((size_t)B * Ln * 3 * 8));
     c->zyz = static_cast<double *>(grab(Ln * 6 * 8));
     c->frame = static_cast<unsigned char *>(grab(Ln));
     c->rot_tf = grab(Ln * 2 * c->rb);
-    c->dw = grab(Ln * 4 * c->rb);
+    c->dw = grab(Ln * 4 * c->rb * (plan.cnot ? 2 : 1));   // CNOT tiles: diag(p_l) and diag(r_l) rows
     c->H = static_cast<double *>(grab(Ln * 9 * 8));
     c->init_u = grab((size_t)B * plan.n * 4 * c->rb);
     if (!plan.small) c->views = static_cast<ViewDev *>(grab((plan.views.size() + 1) * sizeof(ViewDev)));
@@ -823,11 +851,14 @@ int train_impl(hqml_ctx *c, int B, const void *x, const void *theta, const void 
         // The fused last pass emits E; the loss and dL/dE are needed only by the final
         // gradient reduction, so the E reduction runs after the backward sweeps.
         const int C = chunk_count(c, B);
+        // the last forward pass is fused with the first backward pass unless lambda comes
+        // from the observable pass or the plan has no fused-last shape (CNOT chain)
+        const bool fuse = !c->obs_x && !pl.cnot;
+        const int start = c->obs_x ? LAMBDA_READY : fuse ? FUSED_LAST : SEED_FROM_SAVED;
         if (C == 1) {
-            if ((rc = tile_forward_sweep(c, c->stream, Span{0, B, B}, !c->obs_x))) return rc;
+            if ((rc = tile_forward_sweep(c, c->stream, Span{0, B, B}, fuse))) return rc;
             if (c->obs_x && (rc = obs_pass(c, c->stream, Span{0, B, B}, PF_EMIT_E | PF_SEED))) return rc;
-            if ((rc = tile_backward_sweep(c, c->stream, Span{0, B, B}, c->obs_x ? LAMBDA_READY : FUSED_LAST)))
-                return rc;
+            if ((rc = tile_backward_sweep(c, c->stream, Span{0, B, B}, start))) return rc;
         } else {
             hipError_t he = hipEventRecord(c->ev_start, c->stream);
             if (he == hipSuccess) he = hipStreamWaitEvent(c->aux, c->ev_start, 0);
@@ -838,7 +869,7 @@ int train_impl(hqml_ctx *c, int B, const void *x, const void *theta, const void 
                 spans.push_back(Span{b0, b1 - b0, B});
             }
             for (int k = 0; k < C; ++k) {
-                if ((rc = tile_forward_sweep(c, c->aux, spans[k], !c->obs_x))) return rc;
+                if ((rc = tile_forward_sweep(c, c->aux, spans[k], fuse))) return rc;
                 if (c->obs_x && (rc = obs_pass(c, c->aux, spans[k], PF_EMIT_E | PF_SEED))) return rc;
                 he = hipEventRecord(c->ev_fwd[k], c->aux);
                 if (he != hipSuccess) return hip_fail(c, he, "stream ordering");
@@ -846,8 +877,7 @@ int train_impl(hqml_ctx *c, int B, const void *x, const void *theta, const void 
             for (int k = 0; k < C; ++k) {
                 he = hipStreamWaitEvent(c->stream, c->ev_fwd[k], 0);
                 if (he != hipSuccess) return hip_fail(c, he, "stream ordering");
-                if ((rc = tile_backward_sweep(c, c->stream, spans[k], c->obs_x ? LAMBDA_READY : FUSED_LAST)))
-                    return rc;
+                if ((rc = tile_backward_sweep(c, c->stream, spans[k], start))) return rc;
             }
         }
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {

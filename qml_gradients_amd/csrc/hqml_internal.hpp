@@ -73,7 +73,11 @@ enum PassFlags : int {
     PF_STORE = 4,        // forward: write the pass output
     PF_FUSED = 8,        // forward ops of the (last) pass followed by its backward ops
     PF_STATS_ONLY = 16,  // backward: layer-0 statistics of this view only (no state update)
-    PF_SEED = 32         // backward: lambda = O psi formed from the pass output (last pass)
+    PF_SEED = 32,        // backward: lambda = O psi formed from the pass output (last pass)
+    PF_CNOT = 64,        // CNOT-chain plan: diagonals are plain single-qubit factors (no CZ
+                         // signs); backward shapes of that plan
+    PF_GATHER = 128      // forward: read the input at P^-1(i) (the CNOT chain);
+                         // backward: write lambda back to P^-1(i)
 };
 
 struct TilePassArgs {

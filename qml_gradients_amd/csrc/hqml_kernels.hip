@@ -506,9 +506,10 @@ struct DiagTables {
     V2<R> hi[8];
 };
 
+// cz = false (CNOT-chain plan): a plain product of single-qubit factors, no CZ signs.
 template <typename R>
 __device__ __forceinline__ DiagTables<R> diag_tables(const R *dw, int n, int layer, const int *rq,
-                                                     uint32_t fixed_bits)
+                                                     uint32_t fixed_bits, bool cz = true)
 {
     const V4<R> *wl = reinterpret_cast<const V4<R> *>(dw) + (size_t)layer * n;
     uint32_t regq = 0;
@@ -521,7 +522,7 @@ __device__ __forceinline__ DiagTables<R> diag_tables(const R *dw, int n, int lay
         const V4<R> f = ldu4(reinterpret_cast<const R *>(wl + q));
         c = cmul(c, ((fixed_bits >> q) & 1u) ? mk2(f.z, f.w) : mk2(f.x, f.y));
     }
-    if (__builtin_popcount(fixed_bits & (fixed_bits >> 1)) & 1) {
+    if (cz && (__builtin_popcount(fixed_bits & (fixed_bits >> 1)) & 1)) {
         c.x = -c.x;
         c.y = -c.y;
     }
@@ -534,12 +535,12 @@ __device__ __forceinline__ DiagTables<R> diag_tables(const R *dw, int n, int lay
         g1[m] = mk2(f.z, f.w);
         uint32_t nb = (fixed_bits >> (q + 1)) & 1u;
         if (q > 0) nb += (fixed_bits >> (q - 1)) & 1u;
-        if (nb & 1u) {
+        if (cz && (nb & 1u)) {
             g1[m].x = -g1[m].x;
             g1[m].y = -g1[m].y;
         }
     }
-    auto adj = [&](int a, int b) { const int d = rq[a] - rq[b]; return d == 1 || d == -1; };
+    auto adj = [&](int a, int b) { const int d = rq[a] - rq[b]; return cz && (d == 1 || d == -1); };
     DiagTables<R> t;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -600,6 +601,21 @@ __device__ __forceinline__ void apply_diag2(Tile<R> &a, Tile<R> &b, DiagTables<R
         i = b.im[j];
         b.re[j] = r * f.x - i * f.y;
         b.im[j] = r * f.y + i * f.x;
+    }
+}
+
+// Apply s * D^dagger to one tile in layout L2.
+template <typename R>
+__device__ __forceinline__ void apply_diag_dag(Tile<R> &t, DiagTables<R> d, R s)
+{
+    scale_lo(d, s);
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+        V2<R> f = cmul(d.lo[j & 3], d.hi[j >> 2]);
+        f.y = -f.y;
+        const R r = t.re[j], i = t.im[j];
+        t.re[j] = r * f.x - i * f.y;
+        t.im[j] = r * f.y + i * f.x;
     }
 }
 
@@ -720,6 +736,46 @@ __device__ __forceinline__ void store_l1(const Tile<R> &t, void *state, const Ti
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
         const Off off = tb + (Off)roff(c, j) * esz;
+        IO::store(reinterpret_cast<typename IO::elem *>(base + off), t.re[j], t.im[j]);
+    }
+}
+
+// The CNOT chain CNOT(0,1), ..., CNOT(n-2,n-1) sends basis state i to P(i), bit k of
+// P(i) = parity of bits 0..k of i; P^-1(j) = j ^ (j << 1), linear over XOR.  A pass that
+// follows a chain reads its tile (amplitude indices j) from P^-1(j) of the previous
+// output, and its adjoint writes lambda back to P^-1(j).  The tile's index bits (tile,
+// thread, register parts) are disjoint, so P^-1 of the index is the XOR of P^-1 of the
+// parts: one per-thread value and one uniform value per register.
+__device__ __forceinline__ uint32_t chain_inv(uint32_t i, uint32_t mask) { return (i ^ (i << 1)) & mask; }
+
+template <int ST, typename R>
+__device__ __forceinline__ void load_l1_chain(Tile<R> &t, const void *state, const TileCtx &c, uint64_t nelem)
+{
+    using IO = StateIO<ST>;
+    constexpr uint32_t esz = sizeof(typename IO::elem);
+    using Off = TileOff<esz>;
+    const uint32_t mask = (uint32_t)(nelem - 1);
+    const char *base = reinterpret_cast<const char *>(state) + (uint64_t)c.sample * nelem * esz;
+    const uint32_t pt = chain_inv((uint32_t)c.tile_off | c.t1, mask);
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+        const Off off = (Off)(pt ^ chain_inv(roff(c, j), mask)) * esz;
+        IO::load(reinterpret_cast<const typename IO::elem *>(base + off), t.re[j], t.im[j]);
+    }
+}
+
+template <int ST, typename R>
+__device__ __forceinline__ void store_l1_chain(const Tile<R> &t, void *state, const TileCtx &c, uint64_t nelem)
+{
+    using IO = StateIO<ST>;
+    constexpr uint32_t esz = sizeof(typename IO::elem);
+    using Off = TileOff<esz>;
+    const uint32_t mask = (uint32_t)(nelem - 1);
+    char *base = reinterpret_cast<char *>(state) + (uint64_t)c.sample * nelem * esz;
+    const uint32_t pt = chain_inv((uint32_t)c.tile_off | c.t1, mask);
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+        const Off off = (Off)(pt ^ chain_inv(roff(c, j), mask)) * esz;
         IO::store(reinterpret_cast<typename IO::elem *>(base + off), t.re[j], t.im[j]);
     }
 }
@@ -851,7 +907,8 @@ __device__ __forceinline__ void fwd_ops(Tile<R> &t, const TilePassArgs &a, const
         if (a.diag >= 0) {
             // fold the pending scale and the scale of the rotations that follow into D
             const R fb = a.rotB >= 0 ? rb1.F * rb2.F : (R)1;
-            apply_diag(t, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2), sigma * fb);
+            apply_diag(t, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2, !(a.flags & PF_CNOT)),
+                       sigma * fb);
             sigma = (R)1 / fb;
         }
         if (a.rotB >= 0) {
@@ -884,6 +941,8 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 4 : 2) void k_tile_fwd(T
     Tile<R> t;
     if (a.flags & PF_INIT)
         init_l1(t, static_cast<const R *>(a.init_u), c, a.n);
+    else if (a.flags & PF_GATHER)
+        load_l1_chain<ST>(t, a.psi_in, c, nelem);
     else
         load_l1<ST>(t, a.psi_in, c, nelem);
     fwd_ops<ST>(t, a, c, lds, lds_stat, nelem);
@@ -1013,7 +1072,12 @@ enum BwdShape : int {
     BW_ROTA = 1,         // [rotA(la)]
     BW_L0 = 2,           // layer-0 statistics only (one-layer circuit, or stats-only view)
     BW_FUSED_LAST = 3,   // forward [rotA(la)] + E + seed + its backward
-    BW_FUSED_INIT = 4    // one-layer circuit: product state + E + seed + layer-0 statistics
+    BW_FUSED_INIT = 4,   // one-layer circuit: product state + E + seed + layer-0 statistics
+    // CNOT-chain plan (no merged diagonals; see the plan builder):
+    BW_DROTB = 6,        // [diag(r_l), rotB(l)] read through the chain; lambda written back through it
+    BW_ROTAD = 7,        // [rotA(l), diag(p_l)]
+    BW_L0D = 8,          // layer-0 statistics, lambda taken back through diag(p_0)
+    BW_L0D_SEED = 9      // one-layer circuit: seed, layer-0 statistics of view 0, diag(p_0) lambda stored
 };
 
 template <int ST, int SHAPE, typename R>
@@ -1103,6 +1167,59 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
                 transpose(l, lds, c.a1, c.a2, false);
                 stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
             }
+        } else if constexpr (SHAPE == BW_DROTB) {
+            const RotCoef<R> b1 = load_coef(rot_tf, a.n, a.rotB, c.q1, c.gm1);
+            stats_visit<false>(p, l, 1, lds_stat, c.lane, c.w, (R)1);
+            rot_layer2<true>(p, l, b1);
+            const R fb1 = b1.F;
+            transpose(p, lds, c.a1, c.a2, true);
+            transpose(l, lds, c.a1, c.a2, true);
+            stats_visit<true>(p, l, 1, lds_stat, c.lane, c.w, fb1 * fb1);
+            const RotCoef<R> b2 = load_coef(rot_tf, a.n, a.rotB, c.q2, c.gm2);
+            rot_layer<true>(l, b2);
+            // lambda carries scale fb1 * b2.F; diag(r_l)^dagger removes it
+            apply_diag_dag(l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2, false),
+                           fb1 * b2.F);
+            transpose(l, lds, c.a1, c.a2, false);
+        } else if constexpr (SHAPE == BW_ROTAD) {
+            transpose(p, lds, c.a1, c.a2, true);
+            transpose(l, lds, c.a1, c.a2, true);
+            apply_diag2(p, l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2, false), (R)1);
+            stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
+            const RotCoef<R> a2 = load_coef(rot_tf, a.n, la, c.q2, c.gm2);
+            rot_layer2<true>(p, l, a2);
+            const R fa2 = a2.F;
+            transpose(p, lds, c.a1, c.a2, false);
+            transpose(l, lds, c.a1, c.a2, false);
+            stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, fa2 * fa2);
+            const RotCoef<R> a1 = load_coef(rot_tf, a.n, la, c.q1, c.gm1);
+            rot_layer<true>(l, a1);
+            sl = fa2 * a1.F;
+        } else if constexpr (SHAPE == BW_L0D) {
+            // psi = the layer-0 product state; lambda (at the output of the product-state
+            // pass, after diag(p_0)) is taken back through diag(p_0).
+            transpose(p, lds, c.a1, c.a2, true);
+            transpose(l, lds, c.a1, c.a2, true);
+            apply_diag_dag(l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2, false), (R)1);
+            stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
+            transpose(p, lds, c.a1, c.a2, false);
+            transpose(l, lds, c.a1, c.a2, false);
+            stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
+            flush_stats(lds_stat, static_cast<R *>(a.stat_part), c, a.T);
+            return;
+        } else if constexpr (SHAPE == BW_L0D_SEED) {
+            // One-layer circuit: the seeded lambda = O psi is already at the statistics point
+            // (O is diagonal and commutes with diag(p_0)).  The other views' passes read
+            // lambda at the pass output, so diag(p_0) lambda is stored for them.
+            stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
+            transpose(p, lds, c.a1, c.a2, true);
+            transpose(l, lds, c.a1, c.a2, true);
+            stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
+            apply_diag(l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2, false), (R)1);
+            transpose(l, lds, c.a1, c.a2, false);
+            store_l1<LIO>(l, a.lam, c, nelem);
+            flush_stats(lds_stat, static_cast<R *>(a.stat_part), c, a.T);
+            return;
         } else if constexpr (SHAPE == BW_ROTA) {
             const RotCoef<R> a1 = load_coef(rot_tf, a.n, la, c.q1, c.gm1);
             const RotCoef<R> a2 = load_coef(rot_tf, a.n, la, c.q2, c.gm2);
@@ -1127,7 +1244,10 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
         }
     }
     if (sl != (R)1) scale_tile(l, sl);
-    store_l1<LIO>(l, a.lam, c, nelem);
+    if constexpr (SHAPE == BW_DROTB)
+        store_l1_chain<LIO>(l, a.psi_out, c, nelem);   // the second lambda buffer (others read a.lam)
+    else
+        store_l1<LIO>(l, a.lam, c, nelem);
     flush_stats(lds_stat, static_cast<R *>(a.stat_part), c, a.T);
 }
 
@@ -1583,16 +1703,36 @@ __global__ void k_prep_zyz(const TI *theta, int L, int n, double *zyz)
 // every gradient statistic).  G[l][q] = parity of the X's from layers after l; the
 // simulated state at P_l is X^G times the original one, so the Y and Z statistics
 // of such qubits change sign, which the gradient map H absorbs.
-// With the CNOT entangler (cnot != 0) no frame is used: G = 0 everywhere.
-__global__ void k_prep_frame(const double *zyz, int L, int n, int cnot, unsigned char *G)
+// ent = 1 (CNOT chain, whole-circuit kernel): no frame, G = 0.  ent = 2 (CNOT chain,
+// tile passes): the same rewrite, but an X^g moved left through the chain P becomes
+// X^(P^-1 g), P^-1 g = g ^ (g << 1) (no Z appears), so the frame is a qubit mask carried
+// from layer to layer by one thread.
+__global__ void k_prep_frame(const double *zyz, int L, int n, int ent, unsigned char *G)
 {
     const int q = blockIdx.x * blockDim.x + threadIdx.x;
+    if (ent == 2) {
+        if (q != 0) return;
+        const uint32_t full = (uint32_t)((1ull << n) - 1ull);
+        uint32_t g = 0;
+        for (int l = L - 1; l >= 0; --l) {
+            for (int k = 0; k < n; ++k) G[(size_t)l * n + k] = (unsigned char)((g >> k) & 1u);
+            if (l == 0) break;
+            uint32_t rw = 0;   // qubits rewritten at layer l: their X enters before Ry, after diag(r_l)
+            for (int k = 0; k < n; ++k) {
+                const double *z = zyz + ((size_t)l * n + k) * 6;
+                if (z[1] > z[0]) rw |= 1u << k;
+            }
+            const uint32_t gb = g ^ rw;
+            g = (gb ^ (gb << 1)) & full;
+        }
+        return;
+    }
     if (q >= n) return;
     unsigned char g = 0;
     for (int l = L - 1; l >= 0; --l) {
         G[(size_t)l * n + q] = g;
         const double *z = zyz + ((size_t)l * n + q) * 6;
-        if (!cnot && l >= 1 && z[1] > z[0]) g ^= 1;
+        if (ent == 0 && l >= 1 && z[1] > z[0]) g ^= 1;
     }
 }
 
@@ -1603,11 +1743,14 @@ __global__ void k_prep_frame(const double *zyz, int L, int n, int cnot, unsigned
 // H[l][q][a][s]: Pauli coefficients of diag(p)^dag G_a diag(p), G_a the generator of
 //   theta[l][q][a] moved to just after U_{l,q} (G_z = Z, G_y = Rz Y Rz^dag,
 //   G_x = Rz Ry X Ry^dag Rz^dag), with the Y and Z coefficients negated where G[l][q].
-// With the CNOT entangler the diagonals cannot merge across the chain (a permutation)
-// and no frame is used: rot_tf[l][q] = (sin(beta/2), cos(beta/2)) and dw[l][q] =
-// (p, r), the factors of diag(p, conj p) after and diag(r, conj r) before Ry(beta).
+// With the CNOT entangler the diagonals cannot merge across the chain (a permutation).
+// ent = 1 (whole-circuit kernel, no frame): rot_tf[l][q] = (sin(beta/2), cos(beta/2)) and
+// dw[l][q] = (p, r), the factors of diag(p, conj p) after and diag(r, conj r) before
+// Ry(beta).  ent = 2 (tile passes): rot_tf in the tan form with the frame, dw row l =
+// (f0, f1) of diag(p_l) and row L + l of diag(r_l) (times the rewrite's Z), the two
+// factors swapped where an X of the frame passes them.
 template <typename TI, typename R>
-__global__ void k_prep_tables(const TI *theta, const double *zyz, const unsigned char *G, int L, int n, int cnot,
+__global__ void k_prep_tables(const TI *theta, const double *zyz, const unsigned char *G, int L, int n, int ent,
                               R *rot_tf, R *dw, double *H)
 {
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
@@ -1615,10 +1758,32 @@ __global__ void k_prep_tables(const TI *theta, const double *zyz, const unsigned
     const int l = idx / n, q = idx - l * n;
     const double *z = zyz + (size_t)idx * 6;
     const bool gq = G[idx] != 0;
-    if (cnot) {
+    if (ent == 1) {
         rot_tf[idx * 2 + 0] = (R)z[1];
         rot_tf[idx * 2 + 1] = (R)z[0];
         for (int k = 0; k < 4; ++k) dw[(size_t)idx * 4 + k] = (R)z[2 + k];
+    } else if (ent == 2) {
+        const bool x_here = l >= 1 && z[1] > z[0];
+        double k = x_here ? -z[0] / z[1] : z[1] / z[0];
+        if (gq) k = -k;
+        rot_tf[idx * 2 + 0] = (R)k;
+        rot_tf[idx * 2 + 1] = (R)(x_here ? z[1] : z[0]);
+        const cd p = cmk(z[2], z[3]), r = cmk(z[4], z[5]);
+        const cd p0 = gq ? cconj(p) : p, p1 = gq ? p : cconj(p);
+        R *dp = dw + (size_t)idx * 4;
+        dp[0] = (R)p0.re;
+        dp[1] = (R)p0.im;
+        dp[2] = (R)p1.re;
+        dp[3] = (R)p1.im;
+        cd r1 = cconj(r);
+        if (x_here) r1 = cmk(-r1.re, -r1.im);   // the rewrite's Z, applied after diag(r_l)
+        const bool sw = gq != x_here;           // the X's at the point before Ry(beta')
+        const cd f0 = sw ? r1 : r, f1 = sw ? r : r1;
+        R *dr = dw + ((size_t)L * n + idx) * 4;
+        dr[0] = (R)f0.re;
+        dr[1] = (R)f0.im;
+        dr[2] = (R)f1.re;
+        dr[3] = (R)f1.im;
     } else {
         const bool x_here = l >= 1 && z[1] > z[0];
         double k = x_here ? -z[0] / z[1] : z[1] / z[0];
@@ -1822,12 +1987,12 @@ namespace hqml {
 
 template <typename TI, typename R>
 static void prep_typed(const void *theta, const void *x, int L, int n, int B, double *zyz, unsigned char *G,
-                       void *rot_tf, void *dw, double *H, void *init_u, int cnot, hipStream_t s)
+                       void *rot_tf, void *dw, double *H, void *init_u, int ent, hipStream_t s)
 {
     const int ln = L * n;
     k_prep_zyz<TI><<<(ln + 127) / 128, 128, 0, s>>>(static_cast<const TI *>(theta), L, n, zyz);
-    k_prep_frame<<<1, 64, 0, s>>>(zyz, L, n, cnot, G);
-    k_prep_tables<TI, R><<<(ln + 127) / 128, 128, 0, s>>>(static_cast<const TI *>(theta), zyz, G, L, n, cnot,
+    k_prep_frame<<<1, 64, 0, s>>>(zyz, L, n, ent, G);
+    k_prep_tables<TI, R><<<(ln + 127) / 128, 128, 0, s>>>(static_cast<const TI *>(theta), zyz, G, L, n, ent,
                                                            static_cast<R *>(rot_tf), static_cast<R *>(dw), H);
     if (B > 0)
         k_prep_init<TI, R><<<(B * n + 127) / 128, 128, 0, s>>>(static_cast<const TI *>(x), zyz, G, B, n,
@@ -1835,19 +2000,19 @@ static void prep_typed(const void *theta, const void *x, int L, int n, int B, do
 }
 
 hipError_t launch_prep(const void *theta, const void *x, int io64, int L, int n, int B, double *zyz,
-                       unsigned char *G, void *rot_tf, void *dw, double *H, void *init_u, int cnot, int r64,
+                       unsigned char *G, void *rot_tf, void *dw, double *H, void *init_u, int ent, int r64,
                        hipStream_t s)
 {
     if (io64) {
         if (r64)
-            prep_typed<double, double>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, cnot, s);
+            prep_typed<double, double>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, ent, s);
         else
-            prep_typed<double, float>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, cnot, s);
+            prep_typed<double, float>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, ent, s);
     } else {
         if (r64)
-            prep_typed<float, double>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, cnot, s);
+            prep_typed<float, double>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, ent, s);
         else
-            prep_typed<float, float>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, cnot, s);
+            prep_typed<float, float>(theta, x, L, n, B, zyz, G, rot_tf, dw, H, init_u, ent, s);
     }
     return hipGetLastError();
 }
@@ -1889,6 +2054,19 @@ hipError_t launch_tile_fwd(const TilePassArgs &a, int B, int storage, int r64, h
 template <int ST, typename R>
 static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s)
 {
+    if (a.flags & PF_CNOT) {
+        if ((a.flags & PF_STATS_ONLY) && (a.flags & PF_SEED))
+            k_tile_bwd<ST, BW_L0D_SEED, R><<<grid, kThreads, 0, s>>>(a);
+        else if (a.flags & PF_STATS_ONLY)
+            k_tile_bwd<ST, BW_L0D, R><<<grid, kThreads, 0, s>>>(a);
+        else if (a.rotA < 0)
+            k_tile_bwd<ST, BW_DROTB, R><<<grid, kThreads, 0, s>>>(a);
+        else if (a.diag >= 0)
+            k_tile_bwd<ST, BW_ROTAD, R><<<grid, kThreads, 0, s>>>(a);
+        else
+            k_tile_bwd<ST, BW_ROTA, R><<<grid, kThreads, 0, s>>>(a);
+        return;
+    }
     if (a.flags & PF_FUSED) {
         if (a.flags & PF_INIT)
             k_tile_bwd<ST, BW_FUSED_INIT, R><<<grid, kThreads, 0, s>>>(a);

@@ -150,7 +150,58 @@ bool make_obs_view(int n, uint32_t xmask, ViewDev *out, std::string *err)
     return true;
 }
 
-bool make_plan(int n, int L, int ckpt_block, Plan *out, std::string *err)
+// CNOT-chain plan.  The chain maps basis state i to P(i) (bit k = parity of bits 0..k
+// of i); it mixes every index bit, so it cannot be applied inside a tile and the
+// diagonals of consecutive layers do not merge across it.  Per layer l >= 1 there is
+// one pass per view: view 0 reads its input through P^-1 (the previous layer's chain),
+// applies diag(r_l) and its group of Ry-layer l; middle views their group; the last
+// view its group and diag(p_l).  Pass 0 forms the layer-0 product state and applies
+// diag(p_0).  Diagonal table rows: l = diag(p_l), L + l = diag(r_l).  Layer-0
+// statistics come from stats-only passes, one per view (pass 0's own backward is one).
+static bool make_plan_cnot(Plan &p, int ckpt_block, std::string *err)
+{
+    const int n = p.n, L = p.L, V = p.V;
+    auto slot_of = [&](int v, int q, int sel) { return (sel * 13 + p.views[v].inv[q]) * 3; };
+    p.cnot = true;
+    p.fwd.push_back(PassPlan{0, true, -1, 0, -1});
+    for (int l = 1; l < L; ++l)
+        for (int v = 0; v < V; ++v) {
+            PassPlan pp{v, false, -1, -1, -1};
+            if (v == 0) {
+                pp.gather = true;
+                pp.diag = L + l;
+                pp.rotB = l;
+            } else {
+                pp.rotA = l;
+            }
+            if (v == V - 1) pp.diag = l;
+            p.fwd.push_back(pp);
+        }
+    const int P = (int)p.fwd.size();
+    for (int v = 1; v < V; ++v) p.stats_only.push_back(v);
+    for (int q = 0; q < n; ++q) {
+        int v0 = -1;
+        for (int v = 0; v < V; ++v) {
+            const int pos = p.views[v].inv[q];
+            if (pos >= 0 && ((p.views[v].group_mask >> pos) & 1)) v0 = v;
+        }
+        if (v0 < 0) {
+            if (err) *err = "a qubit is rotated by no view";
+            return false;
+        }
+        p.statmap[q] = v0 == 0 ? StatLoc{0, slot_of(0, q, 0)} : StatLoc{P + (v0 - 1), slot_of(v0, q, 0)};
+        for (int l = 1; l < L; ++l)
+            p.statmap[(size_t)l * n + q] = StatLoc{1 + (l - 1) * V + v0, slot_of(v0, q, v0 == 0 ? 1 : 0)};
+    }
+    if (ckpt_block > 0) {
+        p.c = std::max(1, ckpt_block * V);
+        if (p.c >= P) p.c = 0;
+    }
+    p.nblocks = p.c > 0 ? (P + p.c - 1) / p.c : 1;
+    return true;
+}
+
+bool make_plan(int n, int L, int ckpt_block, Plan *out, std::string *err, bool cnot)
 {
     Plan p;
     p.n = n;
@@ -176,6 +227,11 @@ bool make_plan(int n, int L, int ckpt_block, Plan *out, std::string *err)
         return true;
     }
     if (!build_views(n, p, err)) return false;
+    if (cnot) {
+        if (!make_plan_cnot(p, ckpt_block, err)) return false;
+        *out = p;
+        return true;
+    }
     const int V = p.V;
     auto group_has = [&](int v, int q) {
         const int pos = p.views[v].inv[q];
@@ -255,9 +311,10 @@ Workspace size_workspace(const Plan &p, int max_batch, int storage, int compute6
     const size_t elem = storage == 1 ? 4 : storage == 2 ? 16 : 8;
     w.state_bytes = B * w.state_elems * elem;
     const size_t Ln = (size_t)p.L * p.n;
-    // tables: zyz (6 doubles), frame (1 byte), rot_tf (2 reals), dw (4 reals), H (9 doubles), statmap (int2),
+    // tables: zyz (6 doubles), frame (1 byte), rot_tf (2 reals), dw (4 reals; 8 with the CNOT plan), H (9
+    // doubles), statmap (int2),
     // init_u (4 reals per sample and qubit), views, per-sample E / dL/dE / scratch, loss.
-    w.tables_bytes = Ln * (6 * 8 + 1 + 2 * r + 4 * r + 9 * 8 + 8) + B * p.n * 4 * r +
+    w.tables_bytes = Ln * (6 * 8 + 1 + 2 * r + 4 * r * (p.cnot ? 2 : 1) + 9 * 8 + 8) + B * p.n * 4 * r +
                      (size_t)(std::max(p.V, 1) + 1) * sizeof(ViewDev) + B * (8 * 3 + 4) + 64;
     const size_t S_bytes = B * Ln * 3 * 8;
     if (p.small) {
@@ -287,8 +344,9 @@ Workspace size_workspace(const Plan &p, int max_batch, int storage, int compute6
         w.part2_bytes = (size_t)w.part_passes * B * w.tile_chunks * kSlots * 8;
         w.epart2_bytes = B * (size_t)w.tile_chunks * 8;
     }
-    w.total = (size_t)w.n_saved * w.state_bytes + w.lam_bytes + w.part_bytes + w.tables_bytes + S_bytes + epart +
-              w.part2_bytes + w.epart2_bytes;
+    // the CNOT plan keeps a second lambda buffer (passes that write lambda through the chain)
+    w.total = (size_t)w.n_saved * w.state_bytes + w.lam_bytes * (p.cnot ? 2 : 1) + w.part_bytes + w.tables_bytes +
+              S_bytes + epart + w.part2_bytes + w.epart2_bytes;
     return w;
 }
 
@@ -322,8 +380,9 @@ std::string describe_plan(const Plan &p)
 {
     std::string s = "{";
     char buf[256];
-    std::snprintf(buf, sizeof buf, "\"n\":%d,\"L\":%d,\"small\":%s,\"V\":%d,\"T\":%d,\"c\":%d,\"nblocks\":%d,",
-                  p.n, p.L, p.small ? "true" : "false", p.V, p.T, p.c, p.nblocks);
+    std::snprintf(buf, sizeof buf,
+                  "\"n\":%d,\"L\":%d,\"small\":%s,\"cnot\":%s,\"V\":%d,\"T\":%d,\"c\":%d,\"nblocks\":%d,", p.n, p.L,
+                  p.small ? "true" : "false", p.cnot ? "true" : "false", p.V, p.T, p.c, p.nblocks);
     s += buf;
     s += "\"views\":[";
     for (size_t v = 0; v < p.views.size(); ++v) {
@@ -345,8 +404,9 @@ std::string describe_plan(const Plan &p)
     s += "],\"passes\":[";
     for (size_t i = 0; i < p.fwd.size(); ++i) {
         const PassPlan &q = p.fwd[i];
-        std::snprintf(buf, sizeof buf, "%s{\"view\":%d,\"init\":%s,\"rotA\":%d,\"diag\":%d,\"rotB\":%d}", i ? "," : "",
-                      q.view, q.init ? "true" : "false", q.rotA, q.diag, q.rotB);
+        std::snprintf(buf, sizeof buf,
+                      "%s{\"view\":%d,\"init\":%s,\"rotA\":%d,\"diag\":%d,\"rotB\":%d,\"gather\":%s}", i ? "," : "",
+                      q.view, q.init ? "true" : "false", q.rotA, q.diag, q.rotB, q.gather ? "true" : "false");
         s += buf;
     }
     s += "],\"stats_only\":[";

@@ -15,8 +15,10 @@ struct PassPlan {
     int view;
     bool init;    // generates the layer-0 product state (all of Ry-layer 0)
     int rotA;     // Ry-layer applied to the view's group first (-1: none)
-    int diag;     // diagonal D_l applied next (-1: none)
+    int diag;     // row of the diagonal table applied next (-1: none)
     int rotB;     // Ry-layer applied to the view's group last (-1: none)
+    bool gather = false;   // CNOT chain: the input is read through the chain's index map
+                           // (and the backward pass writes lambda back through it)
 };
 
 struct StatLoc {
@@ -27,6 +29,7 @@ struct StatLoc {
 struct Plan {
     int n = 0, L = 0;
     bool small = false;                  // n <= 13: whole circuit in one workgroup per sample
+    bool cnot = false;                   // tile path with the CNOT-chain entangler
     int V = 0;                           // views (tile path)
     int T = 1;                           // tiles per sample
     std::vector<ViewDev> views;
@@ -42,9 +45,10 @@ struct Plan {
 };
 
 // Build the plan for an n-qubit, L-layer circuit; ckpt_block = layers per
-// checkpoint block (0 = keep every fused-pass output).  Returns false with a
-// message in *err for unsupported sizes.
-bool make_plan(int n, int L, int ckpt_block, Plan *plan, std::string *err);
+// checkpoint block (0 = keep every fused-pass output).  cnot: layers end with the
+// CNOT chain instead of the CZ chain (tile path: one pass per view and layer).
+// Returns false with a message in *err for unsupported sizes.
+bool make_plan(int n, int L, int ckpt_block, Plan *plan, std::string *err, bool cnot = false);
 
 // View for the observable pass of a Pauli string whose X part is xmask: qubits 0..3
 // and every higher qubit of xmask on chip (at most 9), the rest as tile bits.

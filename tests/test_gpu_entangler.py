@@ -2,9 +2,11 @@
 
 Every layer ends with CNOT(q, q+1), control q, for q = 0..n-2 in that order.  The
 whole-circuit kernel (n <= 13) applies the chain as a permutation of the amplitude
-indices in local memory; the gate-by-gate comparator runs one kernel per CNOT at any
-width.  Tolerances as for the CZ chain: <O> within 1e-5 relative to
-max(|E|, 2^(-n/2)), gradients within 1e-4 absolute (fp32), 1e-10 (fp64).
+indices in local memory; the tile path (n >= 14) runs one pass per view and layer, the
+first reading its input through the chain's index map and its adjoint writing lambda
+back through it; the gate-by-gate comparator runs one kernel per CNOT at any width.
+Tolerances as for the CZ chain: <O> within 1e-5 relative to max(|E|, 2^(-n/2)),
+gradients within 1e-4 absolute (fp32), 2e-2 (bf16 storage), 1e-10 (fp64).
 """
 import numpy as np
 import pytest
@@ -55,11 +57,11 @@ def test_cnot_whole_circuit(n, L, B, zm, xm):
     ctx.close()
     oz, ox = _masks(zm, xm)
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, oz, ox, entangler=1)
-    assert_e_close(e, e_ref, n)
+    assert_e_close(e, e_ref, n, L)
     assert abs(float(loss[0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
     assert_grad_close(g, g_ref)
     g2_ref, _ = oracle.backward(x, th, w.astype(np.float64), oz, ox, entangler=1)
-    assert_e_close(e2, e_ref, n)
+    assert_e_close(e2, e_ref, n, L)
     assert_grad_close(g2, g2_ref)
 
 
@@ -74,8 +76,8 @@ def test_cnot_differs_from_cz():
         ctx = hq.Context(n, L, B, obs_mask=0b100, entangler=ent)
         outs.append(ctx.forward(X, TH).cpu().numpy())
         ctx.close()
-    assert_e_close(outs[0], oracle.forward(x, th, 0b100), n)
-    assert_e_close(outs[1], oracle.forward(x, th, 0b100, entangler=1), n)
+    assert_e_close(outs[0], oracle.forward(x, th, 0b100), n, L)
+    assert_e_close(outs[1], oracle.forward(x, th, 0b100, entangler=1), n, L)
     assert np.max(np.abs(outs[0] - outs[1])) > 1e-3
 
 
@@ -101,7 +103,7 @@ def test_cnot_hea12q20l_full():
     e, loss, g = (t.cpu().numpy() for t in ctx.train_step(*(torch.from_numpy(a) for a in (x, th, y))))
     ctx.close()
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, entangler=1)
-    assert_e_close(e, e_ref, w.n_qubits)
+    assert_e_close(e, e_ref, w.n_qubits, w.n_layers)
     assert abs(float(loss[0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
     assert_grad_close(g, g_ref)
 
@@ -116,6 +118,106 @@ def test_cnot_gate_by_gate(n, L, B, zm, xm):
     ctx.close()
     oz, ox = _masks(zm, xm)
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, oz, ox, entangler=1)
-    assert_e_close(e, e_ref, n)
+    assert_e_close(e, e_ref, n, L)
     assert abs(float(loss[0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
     assert_grad_close(g, g_ref)
+
+
+TILE = [
+    (14, 1, 2, 0),
+    (14, 2, 2, 0),
+    (14, 3, 3, 0b10000000000100),
+    (15, 4, 2, 0),
+    (16, 3, 2, (1 << 15) | (1 << 6)),
+    (17, 2, 2, 0),
+    (21, 2, 1, (1 << 20) | 1),
+]
+
+
+def _tile_run(n, L, B, zm, seed, **kw):
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=seed)
+    X, TH, Y = (torch.from_numpy(a) for a in (x, th, y))
+    ctx = _ctx(n, L, B, zm, 0, **kw)
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(X, TH, Y))
+    e2 = ctx.forward(X, TH).cpu().numpy()
+    w = np.linspace(-1.0, 1.0, B).astype(np.float32)
+    g2 = ctx.backward(torch.from_numpy(w)).cpu().numpy()
+    ctx.close()
+    return (x, th, y, w), (e, float(loss[0]), g, e2, g2)
+
+
+@pytest.mark.parametrize("n,L,B,zm", TILE)
+def test_cnot_tile_path(n, L, B, zm):
+    say(f"[gpu] CNOT tile path n={n} L={L} B={B} z={zm:#x}")
+    (x, th, y, w), (e, loss, g, e2, g2) = _tile_run(n, L, B, zm, seed=2000 + 3 * n + L)
+    oz = zm or 1
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, oz, entangler=1)
+    assert_e_close(e, e_ref, n, L)
+    assert abs(loss - loss_ref) <= 1e-5 * max(1.0, loss_ref)
+    assert_grad_close(g, g_ref)
+    g2_ref, _ = oracle.backward(x, th, w.astype(np.float64), oz, entangler=1)
+    assert_e_close(e2, e_ref, n, L)
+    assert_grad_close(g2, g2_ref)
+
+
+def test_cnot_tile_checkpoints_and_chunks_are_bitwise_identical():
+    """Checkpoint blocks (recomputed passes, including the chain reads) and batch chunks
+    change nothing in the CNOT plan's results."""
+    import qml_gradients_amd as hq
+    n, L, B = 15, 5, 4
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=2100)
+    X, TH, Y = (torch.from_numpy(a) for a in (x, th, y))
+    outs = []
+    for ckpt, chunks in ((0, 1), (1, 1), (2, 1), (0, 3)):
+        say(f"[gpu] CNOT tile ckpt={ckpt} chunks={chunks}")
+        ctx = hq.Context(n, L, B, ckpt_block=ckpt, entangler="cnot")
+        ctx.set_overlap(chunks)
+        outs.append([t.cpu().numpy() for t in ctx.train_step(X, TH, Y)])
+        ctx.close()
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b)
+    e_ref, _, g_ref = oracle.train_step(x, th, y, entangler=1)
+    assert_e_close(outs[0][0], e_ref, n, L)
+    assert_grad_close(outs[0][2], g_ref)
+
+
+def test_cnot_tile_bf16_storage():
+    n, L, B = 16, 4, 2
+    say("[gpu] CNOT tile bf16")
+    (x, th, y, w), (e, loss, g, e2, g2) = _tile_run(n, L, B, 0, seed=2200, storage="bf16")
+    e_ref, _, g_ref = oracle.train_step(x, th, y, entangler=1)
+    assert np.max(np.abs(e - e_ref)) < 2e-2
+    assert_grad_close(g, g_ref, atol=2e-2)
+
+
+def test_cnot_tile_fp64():
+    import qml_gradients_amd as hq
+    n, L, B = 14, 3, 2
+    say("[gpu] CNOT tile fp64")
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=2300)
+    ctx = hq.Context(n, L, B, obs_mask=0b100, compute="fp64", storage="fp64", entangler="cnot")
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(*(torch.from_numpy(a).double() for a in (x, th, y))))
+    ctx.close()
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, 0b100, entangler=1)
+    assert np.max(np.abs(e - e_ref)) < 1e-12
+    assert np.max(np.abs(g - g_ref)) < 1e-10
+
+
+def test_cnot_tile_20_qubits_sampled():
+    """20 qubits, 12 layers, batch 4: samples 0 and 3 against the oracle one by one."""
+    import qml_gradients_amd as hq
+    n, L, B = 20, 12, 4
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=2400)
+    X, TH = torch.from_numpy(x), torch.from_numpy(th)
+    say("[gpu] CNOT tile 20 qubits")
+    ctx = hq.Context(n, L, B, entangler="cnot")
+    e = ctx.forward(X, TH).cpu().numpy()
+    for b in (0, 3):
+        oh = np.zeros(B, dtype=np.float32)
+        oh[b] = 1.0
+        g = ctx.backward(torch.from_numpy(oh)).cpu().numpy()
+        g_ref, e_ref = oracle.backward(x[b:b + 1], th, np.ones(1), entangler=1)
+        assert_e_close(e[b:b + 1], e_ref, n, L)
+        assert_grad_close(g, g_ref)
+    ctx.close()

@@ -35,7 +35,7 @@ def test_gate_by_gate_train_step(n, L, B):
     e, loss, g = e.cpu().numpy(), float(loss.cpu()[0]), g.cpu().numpy()
     ctx.close()
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
-    assert_e_close(e, e_ref, n)
+    assert_e_close(e, e_ref, n, L)
     assert abs(loss - loss_ref) <= 1e-5 * max(1.0, loss_ref)
     assert_grad_close(g, g_ref)
 
@@ -55,7 +55,7 @@ def test_gate_by_gate_backward_consumes_the_saved_state():
     ctx.close()
     e_ref = oracle.forward(x, th)
     g_ref, _ = oracle.backward(x, th, dl.numpy().astype(np.float64))
-    assert_e_close(e, e_ref, n)
+    assert_e_close(e, e_ref, n, L)
     assert_grad_close(g, g_ref)
 
 
@@ -76,7 +76,7 @@ def test_gate_by_gate_headline_matches_fused_and_oracle():
     e, loss, g = (t.cpu().numpy() for t in ctx.train_step(X, TH, Y))
     # two fp32 results, each within the parity bound of the exact one: their
     # difference is within twice the bound
-    assert_e_close(e.astype(np.float64), e_f.astype(np.float64), n, scale=2.0)
+    assert_e_close(e.astype(np.float64), e_f.astype(np.float64), n, L, scale=2.0)
     assert abs(float(loss[0]) - float(loss_f[0])) <= 1e-5
     assert_grad_close(g, g_f.astype(np.float64), atol=2e-4)
     for b in (0, 31):
@@ -85,7 +85,7 @@ def test_gate_by_gate_headline_matches_fused_and_oracle():
             pytest.skip("golden values not generated (python tests/golden/make_golden.py full)")
         ref = np.load(path)
         eb = ctx.forward(X, TH).cpu().numpy().astype(np.float64)
-        assert_e_close(eb[b:b + 1], ref["expz"], n)
+        assert_e_close(eb[b:b + 1], ref["expz"], n, L)
         oh = np.zeros(B, dtype=np.float32)
         oh[b] = 1.0
         gb = ctx.backward(torch.from_numpy(oh)).cpu().numpy()

@@ -52,12 +52,12 @@ def test_zstring_fused(n, L, B, mask):
     (x, th, y), out = _run(n, L, B, mask, seed=500 + n)
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, mask)
     e, loss, g = out["train"]
-    assert_e_close(e, e_ref, n)
+    assert_e_close(e, e_ref, n, L)
     assert abs(loss - loss_ref) <= 1e-5 * max(1.0, loss_ref)
     assert_grad_close(g, g_ref)
     e2, w, g2 = out["split"]
     g2_ref, _ = oracle.backward(x, th, w.astype(np.float64), mask)
-    assert_e_close(e2, e_ref, n)
+    assert_e_close(e2, e_ref, n, L)
     assert_grad_close(g2, g2_ref)
 
 
@@ -67,7 +67,7 @@ def test_zstring_gate_by_gate(n, L, B, mask):
     (x, th, y), out = _run(n, L, B, mask, seed=600 + n, fusion="gate_by_gate")
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, mask)
     e, loss, g = out["train"]
-    assert_e_close(e, e_ref, n)
+    assert_e_close(e, e_ref, n, L)
     assert_grad_close(g, g_ref)
 
 
@@ -79,7 +79,7 @@ def test_zstring_checkpoint_and_bf16(storage, ckpt):
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, mask)
     e, loss, g = out["train"]
     if storage == "fp32":
-        assert_e_close(e, e_ref, n)
+        assert_e_close(e, e_ref, n, L)
         assert_grad_close(g, g_ref)
     else:
         assert np.max(np.abs(e - e_ref)) <= 2e-2
@@ -108,14 +108,14 @@ def test_pauli_string_fused(n, L, B, zm, xm):
     ctx = hq.Context(n, L, B, obs_mask=zm, obs_x_mask=xm)
     e, loss, g = (t.cpu().numpy() for t in ctx.train_step(X, TH, Y))
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, zm, xm)
-    assert_e_close(e, e_ref, n)
+    assert_e_close(e, e_ref, n, L)
     assert abs(float(loss[0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
     assert_grad_close(g, g_ref)
     w = np.linspace(-1.0, 1.0, B).astype(np.float32)
     e2 = ctx.forward(X, TH).cpu().numpy()
     g2 = ctx.backward(torch.from_numpy(w)).cpu().numpy()
     g2_ref, _ = oracle.backward(x, th, w.astype(np.float64), zm, xm)
-    assert_e_close(e2, e_ref, n)
+    assert_e_close(e2, e_ref, n, L)
     assert_grad_close(g2, g2_ref)
     ctx.close()
 
@@ -143,5 +143,5 @@ def test_pauli_string_modes(mode):
         assert np.max(np.abs(e - e_ref)) <= 1e-10
         assert np.max(np.abs(g - g_ref)) <= 1e-10
     else:
-        assert_e_close(e, e_ref, n)
+        assert_e_close(e, e_ref, n, L)
         assert_grad_close(g, g_ref)

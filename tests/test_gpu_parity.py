@@ -36,7 +36,7 @@ def _run_train(n, L, B, seed, **kw):
 def test_small_path_train_step(n, L, B):
     (x, th, y), (e, loss, g) = _run_train(n, L, B, seed=10 + n)
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
-    assert_e_close(e, e_ref, n)
+    assert_e_close(e, e_ref, n, L)
     assert abs(loss - loss_ref) <= 1e-5 * max(1.0, loss_ref)
     assert_grad_close(g, g_ref)
 
@@ -45,7 +45,7 @@ def test_small_path_train_step(n, L, B):
 def test_tile_path_train_step(n, L, B):
     (x, th, y), (e, loss, g) = _run_train(n, L, B, seed=20 + n + L)
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
-    assert_e_close(e, e_ref, n)
+    assert_e_close(e, e_ref, n, L)
     assert abs(loss - loss_ref) <= 1e-5 * max(1.0, loss_ref)
     assert_grad_close(g, g_ref)
 
@@ -54,7 +54,7 @@ def test_tile_path_three_views():
     n, L, B = 21, 3, 1
     (x, th, y), (e, loss, g) = _run_train(n, L, B, seed=5)
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
-    assert_e_close(e, e_ref, n)
+    assert_e_close(e, e_ref, n, L)
     assert_grad_close(g, g_ref)
 
 
@@ -66,14 +66,14 @@ def test_two_stage_reductions(ckpt):
     n, L, B = 22, 3, 3
     (x, th, y), (e, loss, g) = _run_train(n, L, B, seed=42, ckpt_block=ckpt)
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
-    assert_e_close(e, e_ref, n)
+    assert_e_close(e, e_ref, n, L)
     assert abs(loss - loss_ref) <= 1e-5 * max(1.0, loss_ref)
     assert_grad_close(g, g_ref)
     ctx = _ctx(n, L, B, ckpt_block=ckpt)
     e2 = ctx.forward(torch.from_numpy(x), torch.from_numpy(th)).cpu().numpy()
     g2 = ctx.backward(torch.from_numpy((2.0 * (e2 - y) / B).astype(np.float32))).cpu().numpy()
     ctx.close()
-    assert_e_close(e2, e_ref, n)
+    assert_e_close(e2, e_ref, n, L)
     assert_grad_close(g2, g_ref)
 
 
@@ -87,7 +87,7 @@ def test_forward_backward_split(n, L, B):
     g = ctx.backward(torch.from_numpy(w))
     torch.cuda.synchronize()
     g_ref, e_ref = oracle.backward(x, th, w)
-    assert_e_close(e.cpu().numpy(), e_ref, n)
+    assert_e_close(e.cpu().numpy(), e_ref, n, L)
     assert_grad_close(g.cpu().numpy(), g_ref)
     ctx.close()
 
@@ -101,7 +101,7 @@ def test_named_workload_full(name):
     e, loss, g = ctx.train_step(torch.from_numpy(x), torch.from_numpy(th), torch.from_numpy(y))
     torch.cuda.synchronize()
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
-    assert_e_close(e.cpu().numpy(), e_ref, w.n_qubits)
+    assert_e_close(e.cpu().numpy(), e_ref, w.n_qubits, w.n_layers)
     assert_grad_close(g.cpu().numpy(), g_ref)
     ctx.close()
 
@@ -162,7 +162,7 @@ def test_one_layer_closed_form_full_width(n):
     x0 = x[:, 0].astype(np.float64)
     a, b = float(th[0, 0, 0]), float(th[0, 0, 1])
     e_ref = np.cos(x0) * np.cos(a) * np.cos(b) - np.sin(x0) * np.sin(b)
-    assert_e_close(e, e_ref, n)
+    assert_e_close(e, e_ref, n, 1)
     g_ref = np.zeros((1, n, 3))
     g_ref[0, 0, 0] = np.sum(w * (-np.cos(x0) * np.sin(a) * np.cos(b)))
     g_ref[0, 0, 1] = np.sum(w * (-np.cos(x0) * np.cos(a) * np.sin(b) - np.sin(x0) * np.cos(b)))

@@ -30,7 +30,7 @@ def test_layer_backward_matches_oracle(n, L, B, compute):
         assert np.max(np.abs(e.detach().cpu().numpy() - e_ref)) <= 1e-10
         assert np.max(np.abs(g - g_ref)) <= 1e-10
     else:
-        assert_e_close(e.detach().cpu().numpy(), e_ref, n)
+        assert_e_close(e.detach().cpu().numpy(), e_ref, n, L)
         assert_grad_close(g, g_ref)
 
 

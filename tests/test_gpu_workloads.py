@@ -52,7 +52,7 @@ def test_headline_workload_sampled_parity():
     e = ctx.forward(X, TH).cpu().numpy().astype(np.float64)
     for b in (0, 31):
         ref = _golden(f"{name}_b0_s{b}.npz")
-        assert_e_close(e[b:b + 1], ref["expz"], n)
+        assert_e_close(e[b:b + 1], ref["expz"], n, L)
         g = ctx.backward(_one_hot(B, b)).cpu().numpy()
         assert_grad_close(g, ref["grad"])
     e2, loss, g_ts = ctx.train_step(X, TH, Y)
@@ -75,7 +75,7 @@ def test_deep_checkpointed_workload_sampled_parity():
     say(f"[gpu] {name} checkpointed sampled parity")
     ctx = _ctx(w.n_qubits, w.n_layers, w.batch, ckpt_block=w.ckpt_block)
     e = ctx.forward(torch.from_numpy(x), torch.from_numpy(th)).cpu().numpy().astype(np.float64)
-    assert_e_close(e[:1], ref["expz"], w.n_qubits)
+    assert_e_close(e[:1], ref["expz"], w.n_qubits, w.n_layers)
     g = ctx.backward(_one_hot(w.batch, 0)).cpu().numpy()
     assert_grad_close(g, ref["grad"])
     ctx.close()
@@ -143,7 +143,7 @@ def test_wide_29_qubits_light_cone(storage):
     e, loss, g = ctx.train_step(*(torch.from_numpy(a) for a in (x, th, y)))
     e, g = e.cpu().numpy(), g.cpu().numpy()
     if storage == "fp32":
-        assert_e_close(e, e_ref, n)
+        assert_e_close(e, e_ref, n, L)
         assert_grad_close(g, g_ref)
     else:
         assert np.max(np.abs(e - e_ref)) <= 2e-2
@@ -182,7 +182,7 @@ def test_chunked_overlap_is_bitwise_identical(storage, ckpt):
             assert np.array_equal(a, b)
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
     if storage == "fp32":
-        assert_e_close(outs[0][0], e_ref, n)
+        assert_e_close(outs[0][0], e_ref, n, L)
         assert_grad_close(outs[0][2], g_ref)
     ctx.close()
 
@@ -199,7 +199,7 @@ def test_ragged_batches_on_one_context(ckpt):
         out = ctx.train_step(torch.from_numpy(x[:B]), torch.from_numpy(th), torch.from_numpy(y[:B]))
         e, loss, g = (t.cpu().numpy() for t in out)
         e_ref, loss_ref, g_ref = oracle.train_step(x[:B], th, y[:B])
-        assert_e_close(e, e_ref, n)
+        assert_e_close(e, e_ref, n, L)
         assert abs(float(loss[0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
         assert_grad_close(g, g_ref)
     ctx.close()

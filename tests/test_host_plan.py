@@ -113,8 +113,12 @@ def test_entangler_config_host_only():
     assert hq.hqml_workspace_bytes(hq.make_config(12, 3, 2, entangler="cnot")) > 0
     assert hq.hqml_workspace_bytes(hq.make_config(13, 3, 2, entangler="cnot", obs_x_mask=0b101)) > 0
     assert hq.hqml_workspace_bytes(hq.make_config(20, 3, 2, entangler="cnot", fusion="gate_by_gate")) > 0
-    # the tile path applies the chain nowhere: a fused context with n >= 14 is refused
-    tile = hq.make_config(14, 3, 2, entangler="cnot")
+    # tile path: one pass per view and layer, Z-string observables only, a second lambda buffer
+    cz = hq.hqml_workspace_bytes(hq.make_config(20, 10, 4))
+    cn = hq.hqml_workspace_bytes(hq.make_config(20, 10, 4, entangler="cnot"))
+    st = 4 * (1 << 20) * 8
+    assert cn - cz >= 10 * st   # 19 saved pass outputs instead of 10, plus lambda
+    tile = hq.make_config(14, 3, 2, entangler="cnot", obs_x_mask=1)
     assert hq.hqml_workspace_bytes(tile) == 0
     with pytest.raises(hq.HqmlError) as e:
         hq.hqml_create(tile)
@@ -190,6 +194,37 @@ def test_model_of_kernel_algebra_matches_oracle(n, L, B):
     w = np.linspace(0.5, -1.0, B)
     e, g = m.backward(w)
     g_ref, e_ref = oracle.backward(x, th, w)
+    assert np.max(np.abs(e - e_ref)) < 1e-10
+    assert np.max(np.abs(g - g_ref)) < 1e-10
+
+
+@pytest.mark.parametrize("n", [14, 16, 21, 29])
+def test_cnot_plan_invariants(n):
+    """CNOT plan: pass 0 forms the product state and diag(p_0); then per layer one pass
+    per view in view order, the first reading through the chain (diag(r_l) row L + l),
+    the last applying diag(p_l) (row l); every (layer, qubit) has one statistics slot."""
+    _lib()
+    for L in (1, 2, 4):
+        p = json.loads(hq.hqml_describe_plan(hq.make_config(n, L, 1, entangler="cnot")))
+        V = p["V"]
+        assert p["cnot"] and len(p["passes"]) == 1 + (L - 1) * V
+        assert p["passes"][0] == {"view": 0, "init": True, "rotA": -1, "diag": 0, "rotB": -1, "gather": False}
+        for l in range(1, L):
+            for v in range(V):
+                ps = p["passes"][1 + (l - 1) * V + v]
+                assert ps["view"] == v and ps["gather"] == (v == 0) and not ps["init"]
+                assert (ps["rotA"], ps["rotB"]) == ((-1, l) if v == 0 else (l, -1))
+                assert ps["diag"] == (L + l if v == 0 else l if v == V - 1 else -1)
+        assert len({tuple(sm) for sm in p["statmap"]}) == L * n
+
+
+@pytest.mark.parametrize("n,L,B", [(14, 1, 2), (14, 3, 2), (15, 4, 1), (17, 3, 1)])
+def test_model_of_cnot_plan_matches_oracle(n, L, B):
+    x, th, _ = hqml_inputs.make_inputs(n, L, B, seed=200 + n + L)
+    m = Model(hq.hqml_describe_plan(hq.make_config(n, L, B, entangler="cnot")), x, th)
+    w = np.linspace(0.5, -1.0, B)
+    e, g = m.backward(w)
+    g_ref, e_ref = oracle.backward(x, th, w, entangler=1)
     assert np.max(np.abs(e - e_ref)) < 1e-10
     assert np.max(np.abs(g - g_ref)) < 1e-10
 

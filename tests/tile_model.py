@@ -92,6 +92,39 @@ def pauli_frame(cb, sb, p, r, H):
     return c, s, f0, f1, G, H2
 
 
+def cnot_frame(cb, sb, p, r, H):
+    """The same rewrite with the CNOT chain P (|i> -> |P(i)>, bit k of P(i) = parity of
+    bits 0..k).  Moving X^g left through P gives X^(P^-1 g), P^-1 g = g ^ (g << 1): no Z
+    appears.  Per layer the simulated sequence is diag(r_l), Ry(beta'_l), diag(p_l), P;
+    the rewrite's Z merges into diag(r_l).  Returns (c, s), the diagonal rows
+    (dP[l], dR[l]) as (f0, f1) pairs, G at the statistics points and the adjusted map."""
+    L, n = cb.shape
+    x = np.zeros((L, n), dtype=bool)
+    x[1:] = sb[1:] > cb[1:]
+    G = np.zeros((L, n), dtype=bool)
+    g = 0
+    full = (1 << n) - 1
+    for l in range(L - 1, -1, -1):
+        G[l] = [(g >> q) & 1 for q in range(n)]
+        if l == 0:
+            break
+        gb = g ^ sum(1 << q for q in range(n) if x[l, q])
+        g = (gb ^ (gb << 1)) & full
+    c = np.where(x, sb, cb)
+    s = np.where(x, -cb, sb)
+    s = np.where(G, -s, s)
+    dP0 = np.where(G, np.conj(p), p)
+    dP1 = np.where(G, p, np.conj(p))
+    r0, r1 = r.copy(), np.where(x, -np.conj(r), np.conj(r))
+    sw = G ^ x
+    dR0 = np.where(sw, r1, r0)
+    dR1 = np.where(sw, r0, r1)
+    H2 = H.copy()
+    H2[..., 1] = np.where(G[..., None], -H[..., 1], H[..., 1])
+    H2[..., 2] = np.where(G[..., None], -H[..., 2], H[..., 2])
+    return c, s, (dP0, dP1), (dR0, dR1), G, H2
+
+
 class Model:
     def __init__(self, plan_json: str, x, theta):
         self.plan = json.loads(plan_json)
@@ -99,7 +132,14 @@ class Model:
         self.theta = np.asarray(theta, dtype=np.float64)
         self.L, self.n = self.theta.shape[0], self.theta.shape[1]
         self.cb, self.sb, self.p, self.r, H0 = factorise(self.theta)
-        self.c, self.s, self.f0, self.f1, self.G, self.H = pauli_frame(self.cb, self.sb, self.p, self.r, H0)
+        self.cnot = bool(self.plan.get("cnot", False))
+        if self.cnot:
+            self.c, self.s, dP, dR, self.G, self.H = cnot_frame(self.cb, self.sb, self.p, self.r, H0)
+            # table rows: l = diag(p_l), L + l = diag(r_l)
+            self.f0 = np.concatenate([dP[0], dR[0]])
+            self.f1 = np.concatenate([dP[1], dR[1]])
+        else:
+            self.c, self.s, self.f0, self.f1, self.G, self.H = pauli_frame(self.cb, self.sb, self.p, self.r, H0)
         n = self.n
         self.idx = np.arange(1 << n, dtype=np.int64)
         self.bits = [((self.idx >> q) & 1).astype(bool) for q in range(n)]
@@ -133,7 +173,7 @@ class Model:
         return psi
 
     def diag(self, l):
-        d = self.cz.astype(complex)
+        d = np.ones(1 << self.n, dtype=complex) if self.cnot else self.cz.astype(complex)
         for q in range(self.n):
             d = d * np.where(self.bits[q], self.f1[l, q], self.f0[l, q])
         return d
@@ -149,9 +189,20 @@ class Model:
         return np.array([sx, sy, sz])
 
     # --- fused passes -------------------------------------------------
+    def chain(self, i):
+        """P(i): bit k = parity of bits 0..k of i."""
+        for sh in (1, 2, 4, 8, 16):
+            i = i ^ (i << sh)
+        return i & ((1 << self.n) - 1)
+
+    def chain_inv(self, j):
+        return (j ^ (j << 1)) & ((1 << self.n) - 1)
+
     def forward_pass(self, k, psi, b):
         ps = self.plan["passes"][k]
         g = self.groups[ps["view"]]
+        if ps.get("gather"):
+            psi = psi[self.chain_inv(self.idx)]
         if ps["init"]:
             psi = self.init_state(b)
         if ps["rotA"] >= 0:
@@ -163,6 +214,8 @@ class Model:
         return psi
 
     def run_sample(self, b):
+        if self.cnot:
+            return self.run_sample_cnot(b)
         P = len(self.plan["passes"])
         outs = []
         psi = None
@@ -202,6 +255,60 @@ class Model:
             inv = {q: pos for pos, q in enumerate(v["perm"])}
             for q in self.groups[vi]:
                 part[(P + i, inv[q] * 3)] = self.stats(psi0, lam, q)
+        S = np.zeros((self.L, self.n, 3))
+        for l in range(self.L):
+            for q in range(self.n):
+                pk, slot = self.plan["statmap"][l * self.n + q]
+                S[l, q] = part[(pk, slot)]
+        return e, S
+
+    def run_sample_cnot(self, b, zmask=1):
+        P = len(self.plan["passes"])
+        outs = []
+        psi = None
+        for k in range(P):
+            psi = self.forward_pass(k, psi, b)
+            outs.append(psi)
+        # the passes stop before the last chain: measure P^dag Z_S P = Z_S'
+        zs = zmask
+        for sh in (1, 2, 4, 8, 16):
+            zs ^= zs >> sh
+        sign = np.where(np.bitwise_count(self.idx & zs) & 1, -1.0, 1.0)
+        e = float(np.sum(sign * np.abs(psi) ** 2))
+        lam = sign * psi
+        part = {}
+        psi0 = self.init_state(b)
+
+        def inv_of(vi):
+            return {q: pos for pos, q in enumerate(self.plan["views"][vi]["perm"])}
+
+        for k in range(P - 1, -1, -1):
+            ps = self.plan["passes"][k]
+            g = self.groups[ps["view"]]
+            inv = inv_of(ps["view"])
+            psi = outs[k]
+            if ps["init"]:
+                l0 = lam * np.conj(self.diag(ps["diag"]))
+                for q in g:
+                    part[(k, inv[q] * 3)] = self.stats(psi0, l0, q)
+            elif ps["rotB"] >= 0:          # [diag(r_l), rot] read through P^-1
+                for q in g:
+                    part[(k, (13 + inv[q]) * 3)] = self.stats(psi, lam, q)
+                lam = self.rot(lam, ps["rotB"], g, inverse=True)
+                lam = lam * np.conj(self.diag(ps["diag"]))
+                lam = lam[self.chain(self.idx)]
+            else:                           # [rot] or [rot, diag(p_l)]
+                if ps["diag"] >= 0:
+                    d = np.conj(self.diag(ps["diag"]))
+                    psi, lam = psi * d, lam * d
+                for q in g:
+                    part[(k, inv[q] * 3)] = self.stats(psi, lam, q)
+                lam = self.rot(lam, ps["rotA"], g, inverse=True)
+        l0 = lam * np.conj(self.diag(0))
+        for i, vi in enumerate(self.plan["stats_only"]):
+            inv = inv_of(vi)
+            for q in self.groups[vi]:
+                part[(P + i, inv[q] * 3)] = self.stats(psi0, l0, q)
         S = np.zeros((self.L, self.n, 3))
         for l in range(self.L):
             for q in range(self.n):
