@@ -65,6 +65,12 @@ def algorithmic_bytes(plan: dict, B: int, storage: str, compute: str = "fp32"):
     P = len(plan["passes"])
     fwd = bwd = 0
     for k, ps in enumerate(plan["passes"]):
+        if plan.get("cnot"):
+            # CNOT-chain plan: no fused last pass; pass 0's backward reads lambda only
+            # (and writes it once for a one-layer circuit)
+            fwd += ((0 if ps["init"] else s) + s) * N * B
+            bwd += (lb * (2 if P == 1 else 1) if ps["init"] else s + lb + lb) * N * B
+            continue
         if k == P - 1:
             # fused forward+adjoint of the last pass: counted with the adjoint kernels
             bwd += ((0 if ps["init"] else s) + lb) * N * B
@@ -114,7 +120,10 @@ def algorithmic_flops_bwd(plan: dict, B: int):
     return total
 
 
-def traffic_record(kernel: str, workload: str):
+def traffic_record(kernel: str, workload: str, entangler: str = "cz"):
+    """Counter-measured HBM bytes per launch (CZ-chain plan), while the source matches."""
+    if entangler != "cz":
+        return None
     path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -124,7 +133,7 @@ def traffic_record(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(workload: str, timeout_s: float = 60.0):
+def cpu_baseline(workload: str, timeout_s: float = 60.0, entangler: str = "cz"):
     import numpy as np  # noqa: F401
 
     import hqml_inputs
@@ -133,21 +142,21 @@ def cpu_baseline(workload: str, timeout_s: float = 60.0):
     o = oracle.default()
     threads = o.max_threads()
     t0 = time.perf_counter()
-    o.train_step(x[:1], th, y[:1])
+    o.train_step(x[:1], th, y[:1], entangler=1 if entangler == "cnot" else 0)
     dt = time.perf_counter() - t0
     return {"value": 1.0 / dt, "unit": "samples/s", "cores": threads, "kind": "oracle",
             "sample": f"1 of the {x.shape[0]} samples of {workload} (full circuit, fp64 train step), "
                       f"{dt:.1f} s on {threads} OpenMP threads"}
 
 
-def gate_by_gate(w, X, TH, Y, steps):
+def gate_by_gate(w, X, TH, Y, steps, entangler="cz"):
     """The same train step on the comparator without fusion (one kernel per gate,
     gate-by-gate adjoint): one untimed step, then `steps` timed ones."""
     import torch
 
     import qml_gradients_amd as hq
     B = X.shape[0]
-    ctx = hq.Context(w.n_qubits, w.n_layers, B, fusion="gate_by_gate")
+    ctx = hq.Context(w.n_qubits, w.n_layers, B, fusion="gate_by_gate", entangler=entangler)
     info = ctx.plan_info()
     ctx.train_step(X, TH, Y)
     torch.cuda.synchronize()
@@ -232,6 +241,8 @@ def main():
                     help="layers per checkpoint block (default: the workload's; 0 = keep every pass output)")
     ap.add_argument("--gbg-steps", type=int, default=2,
                     help="timed steps of the gate-by-gate comparator on the same workload (0 = skip)")
+    ap.add_argument("--entangler", choices=["cz", "cnot"], default="cz",
+                    help="the block ending each layer: the CZ chain (the pages' ansatz) or the CNOT chain")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -273,7 +284,8 @@ def main():
     Y = torch.from_numpy(y).to(dev, dt)
     B = X.shape[0]
     free0 = torch.cuda.mem_get_info(0)[0]
-    ctx = hq.Context(w.n_qubits, w.n_layers, B, storage=w.storage, ckpt_block=w.ckpt_block, compute=args.compute)
+    ctx = hq.Context(w.n_qubits, w.n_layers, B, storage=w.storage, ckpt_block=w.ckpt_block, compute=args.compute,
+                     entangler=args.entangler)
     torch.cuda.synchronize()
     memory = {"workspace_bytes": hq.hqml_workspace_bytes(ctx.cfg),
               "device_mem_delta_bytes": int(free0 - torch.cuda.mem_get_info(0)[0])}
@@ -336,7 +348,7 @@ def main():
         achieved = per_launch_bytes / (avg_ms / 1e3) / 1e9
         return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic_record(kernel_name, args.workload),
+                "traffic": traffic_record(kernel_name, args.workload, args.entangler),
                 "kernel": kernel_name, "avg_launch_ms": round(avg_ms, 4),
                 "launches_per_step": launches, "algorithmic_bytes_per_launch": int(per_launch_bytes)}
 
@@ -349,14 +361,17 @@ def main():
         hbm = bytes_per_step / launches / (avg_ms / 1e3) / 1e9
         return {"bound": "alu", "achieved": round(achieved, 2), "peak": round(ALU_PEAK_TFLOPS, 1),
                 "unit": "TFLOP/s", "frac": round(achieved / ALU_PEAK_TFLOPS, 4),
-                "traffic": traffic_record(kernel_name, args.workload),
+                "traffic": traffic_record(kernel_name, args.workload, args.entangler),
                 "kernel": kernel_name, "avg_launch_ms": round(avg_ms, 4), "launches_per_step": launches,
                 "algorithmic_flops_per_launch": int(per_launch),
                 "algorithmic_bytes_per_launch": int(bytes_per_step / launches),
                 "hbm_achieved_GBps": round(hbm, 1), "hbm_frac": round(hbm / HBM_PEAK_GBPS, 4),
                 "frac_of_published_fp32_peak": round(achieved / FP32_PUBLISHED_TFLOPS, 4)}
 
-    roof_bwd = roof_alu(hq.HQML_K_BWD_PASS, bwd_flops, bwd_b, "k_tile_bwd")
+    # the CNOT plan's adjoint passes each rotate one qubit group (half the ALU work of a
+    # merged pass for the same bytes): reported against the HBM peak
+    roof_bwd = (roof_hbm(hq.HQML_K_BWD_PASS, bwd_b, "k_tile_bwd") if plan.get("cnot")
+                else roof_alu(hq.HQML_K_BWD_PASS, bwd_flops, bwd_b, "k_tile_bwd"))
     roof_fwd = roof_hbm(hq.HQML_K_FWD_PASS, fwd_b, "k_tile_fwd")
     step_bytes = fwd_b + bwd_b
     out = {
@@ -376,6 +391,7 @@ def main():
         "data": "synthetic (seeded x~U[0,pi), theta~U[0,2pi), y in {-1,+1})",
         "config": {"workload": args.workload, "n_qubits": w.n_qubits, "n_layers": w.n_layers,
                    "batch": B, "state_storage": w.storage, "compute": args.compute, "ckpt_block": w.ckpt_block,
+                   "entangler": args.entangler,
                    "overlap_chunks": args.overlap, "parallelism": "single GPU"},
         "memory": memory,
         "step_state_bytes": step_bytes,
@@ -390,11 +406,11 @@ def main():
     }
     ctx.close()
     if args.gbg_steps > 0 and w.storage == "fp32" and w.ckpt_block == 0 and not f64:
-        g = gate_by_gate(w, X, TH, Y, args.gbg_steps)
+        g = gate_by_gate(w, X, TH, Y, args.gbg_steps, args.entangler)
         g["fused_speedup"] = round(value / g["value"], 2)
         out["gate_by_gate"] = g
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.workload)
+        out["cpu_baseline"] = cpu_baseline(args.workload, entangler=args.entangler)
     print(json.dumps(out), flush=True)
 
 

@@ -79,12 +79,14 @@ typedef enum {
     HQML_ENT_CZ = 0,            /* every layer ends with CZ(q, q+1), q = 0..n-2 (section 2.1) */
     HQML_ENT_CNOT = 1           /* every layer ends with CNOT(q, q+1) (control q, target q+1) for
                                    q = 0, 1, ..., n-2 in that order, a permutation of the amplitude
-                                   indices (section 3.2 fuses CNOTs by recomputing indices).
-                                   Offered where a sample's whole state is on chip (n_qubits <= 13,
-                                   the index map is applied in local memory) and by the
-                                   HQML_GATE_BY_GATE comparator at any width; a fused context with
-                                   n_qubits >= 14 returns HQML_ERR_UNSUPPORTED (the map mixes every
-                                   index bit, so it cannot be applied inside a tile pass) */
+                                   indices (section 3.2 fuses CNOTs by recomputing indices).  With
+                                   n_qubits <= 13 the index map is applied in local memory; with
+                                   n_qubits >= 14 it mixes every index bit, so the fused passes run
+                                   one per qubit group and layer (twice the CZ chain's state traffic
+                                   at 20 qubits) and read each layer's input through the map; there
+                                   the observable must be a Z-string (obs_x_mask = 0, else
+                                   HQML_ERR_UNSUPPORTED).  The HQML_GATE_BY_GATE comparator applies
+                                   one kernel per CNOT at any width */
 } hqml_entangler;
 
 typedef struct {
