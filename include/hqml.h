@@ -83,10 +83,11 @@ typedef enum {
                                    n_qubits <= 13 the index map is applied in local memory; with
                                    n_qubits >= 14 it mixes every index bit, so the fused passes run
                                    one per qubit group and layer (twice the CZ chain's state traffic
-                                   at 20 qubits) and read each layer's input through the map; there
-                                   the observable must be a Z-string (obs_x_mask = 0, else
-                                   HQML_ERR_UNSUPPORTED).  The HQML_GATE_BY_GATE comparator applies
-                                   one kernel per CNOT at any width */
+                                   at 20 qubits) and read each layer's input through the map; they
+                                   measure the string conjugated by the last chain, whose X/Y part
+                                   covers qubits q and q+1 for each X/Y factor on q (the limit of 9
+                                   such qubits above qubit 3 applies to it).  The HQML_GATE_BY_GATE
+                                   comparator applies one kernel per CNOT at any width */
 } hqml_entangler;
 
 typedef struct {

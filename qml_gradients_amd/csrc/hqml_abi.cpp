@@ -95,6 +95,7 @@ struct hqml_ctx {
     float *loss_tmp = nullptr;
     uint32_t obs = 1;            // observable: Z part of the Pauli string
     uint32_t obs_x = 0;          // observable: X part (Y where both); nonzero adds an observable pass
+    bool obs_neg = false;        // CNOT-chain plan: the conjugated string carries a sign -1
     // gate-by-gate comparator
     bool gbg = false;
     float *gbg_psi = nullptr;    // [B][2^n] complex fp32
@@ -281,6 +282,33 @@ int prep(hqml_ctx *c, int B, const void *x, const void *theta, int io64)
     });
 }
 
+// The Pauli string the tile passes measure.  The CNOT-chain plan stops before the last
+// chain P, so it measures P^dag O P: X^x -> X^(x ^ (x << 1)) and Z^z -> Z^z' (bit k of z'
+// = parity of bits k.. of z), and O = i^|x & z| X^x Z^z becomes s i^|x' & z'| X^x' Z^z'
+// with the sign s = i^(|x & z| - |x' & z'|) = +-1.
+struct ObsString {
+    uint32_t z, x;
+    bool neg;
+};
+
+ObsString tile_observable(const hqml_config *cfg, const Plan &plan)
+{
+    ObsString o;
+    o.z = (cfg->obs_mask | cfg->obs_x_mask) ? (uint32_t)cfg->obs_mask : 1u;
+    o.x = (uint32_t)cfg->obs_x_mask;
+    o.neg = false;
+    if (!plan.cnot) return o;
+    const uint32_t full = (uint32_t)((1ull << plan.n) - 1ull);
+    const int d0 = __builtin_popcount(o.z & o.x);
+    uint32_t z = o.z;
+    for (int sh = 1; sh < 32; sh <<= 1) z ^= z >> sh;
+    o.z = z;
+    o.x = (o.x ^ (o.x << 1)) & full;
+    const int d = d0 - __builtin_popcount(o.z & o.x);
+    o.neg = (((d % 4) + 4) % 4) == 2;
+    return o;
+}
+
 int check_config(const hqml_config *cfg, Plan *plan, std::string *err)
 {
     if (!cfg) {
@@ -332,13 +360,10 @@ int check_config(const hqml_config *cfg, Plan *plan, std::string *err)
     }
     const bool cnot_tiles = cfg->entangler == HQML_ENT_CNOT && cfg->fusion == HQML_FUSED;
     if (!make_plan(cfg->n_qubits, cfg->n_layers, cfg->ckpt_block, plan, err, cnot_tiles)) return HQML_ERR_ARG;
-    if (plan->cnot && cfg->obs_x_mask != 0) {
-        *err = "with the CNOT entangler and n_qubits >= 14 the observable must be a Z-string (obs_x_mask = 0)";
-        return HQML_ERR_UNSUPPORTED;
-    }
     if (cfg->obs_x_mask != 0 && !plan->small && cfg->fusion == HQML_FUSED) {
+        const ObsString o = tile_observable(cfg, *plan);
         ViewDev ov;
-        if (!make_obs_view(cfg->n_qubits, (uint32_t)cfg->obs_x_mask, &ov, err)) return HQML_ERR_UNSUPPORTED;
+        if (!make_obs_view(cfg->n_qubits, o.x, &ov, err)) return HQML_ERR_UNSUPPORTED;
     }
     if (!plan->small && (size_t)cfg->max_batch * plan->T > 0x7FFFFFFFull) {
         *err = "max_batch * tiles per sample exceeds the grid limit";
@@ -379,7 +404,7 @@ int obs_pass(hqml_ctx *c, hipStream_t st, Span sp, int flags)
     a.view = c->views + pl.V;
     a.psi_in = pass_out(c, pl.n_fwd() - 1);
     a.rotA = a.diag = a.rotB = -1;
-    a.flags = flags;
+    a.flags = flags | (pl.cnot ? PF_CNOT : 0) | (c->obs_neg ? PF_OBS_NEG : 0);
     a.sample0 = sp.b0;
     return run_on(c, st, HQML_K_OTHER, "observable pass launch",
                   [&] { return launch_tile_obs(a, sp.bc, c->cfg.storage, c->r64, st); });
@@ -588,14 +613,11 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     c->gbg = cfg->fusion == HQML_GATE_BY_GATE;
     c->r64 = cfg->compute == HQML_COMPUTE_FP64 ? 1 : 0;
     c->rb = c->r64 ? 8 : 4;
-    c->obs = (cfg->obs_mask | cfg->obs_x_mask) ? (uint32_t)cfg->obs_mask : 1u;
-    c->obs_x = (uint32_t)cfg->obs_x_mask;
-    if (plan.cnot) {
-        // The tile passes stop before the last layer's CNOT chain P, so they measure
-        // P^dag Z_S P = Z_S' with bit k of S' the parity of the bits k.. of S.
-        uint32_t z = c->obs;
-        for (int sh = 1; sh < 32; sh <<= 1) z ^= z >> sh;
-        c->obs = z;
+    {
+        const ObsString o = tile_observable(cfg, plan);
+        c->obs = o.z;
+        c->obs_x = o.x;
+        c->obs_neg = o.neg;
     }
     c->ws = workspace_for(cfg, plan);
     c->stream = reinterpret_cast<hipStream_t>(cfg->stream);

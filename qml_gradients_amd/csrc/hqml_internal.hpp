@@ -76,8 +76,9 @@ enum PassFlags : int {
     PF_SEED = 32,        // backward: lambda = O psi formed from the pass output (last pass)
     PF_CNOT = 64,        // CNOT-chain plan: diagonals are plain single-qubit factors (no CZ
                          // signs); backward shapes of that plan
-    PF_GATHER = 128      // forward: read the input at P^-1(i) (the CNOT chain);
+    PF_GATHER = 128,     // forward: read the input at P^-1(i) (the CNOT chain);
                          // backward: write lambda back to P^-1(i)
+    PF_OBS_NEG = 256     // observable pass: the Pauli string carries an extra sign -1
 };
 
 struct TilePassArgs {

@@ -978,12 +978,15 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_obs(T
     load_l1<ST>(p, a.psi_in, c, nelem);
     // phi = D_trail psi, D_trail(i) = CZ-chain sign x prod_q f_q(bit q of i) (layer L-1's
     // left factors): the true final state.  D_trail commutes with Z but not with X or Y.
+    // The CNOT-chain plan has applied diag(p_(L-1)) in its last pass (PF_CNOT: no D_trail;
+    // the string is the chain-conjugated one, possibly with a sign, PF_OBS_NEG).
+    const bool trail = !(a.flags & PF_CNOT);
     const V4<R> *wl = reinterpret_cast<const V4<R> *>(a.dw) + (size_t)(a.L - 1) * a.n;
     uint32_t regq = 0;
 #pragma unroll
     for (int m = 0; m < 5; ++m) regq |= 1u << c.q1[m];
     V2<R> cst = mk2((R)1, (R)0);
-    for (int q = 0; q < a.n; ++q) {
+    for (int q = 0; trail && q < a.n; ++q) {
         if ((regq >> q) & 1u) continue;
         const V4<R> f = ldu4(reinterpret_cast<const R *>(wl + q));
         cst = cmul(cst, ((c.fixed1 >> q) & 1u) ? mk2(f.z, f.w) : mk2(f.x, f.y));
@@ -991,6 +994,10 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_obs(T
     V2<R> dj[kRegs];
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
+        if (!trail) {
+            dj[j] = mk2((R)1, (R)0);
+            continue;
+        }
         uint32_t g = c.fixed1;
         V2<R> f = cst;
 #pragma unroll
@@ -1019,7 +1026,7 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_obs(T
     // sign of Z^zm at the partner: parity((i ^ xm) & zm) = parity(i & zm) ^ parity(xm & zm)
     uint32_t neg = obs_mask_l1(c, a.obs);
     if (__builtin_popcount(a.obs & a.obs_x) & 1) neg = ~neg;
-    const int ph = __builtin_popcount(a.obs & a.obs_x) & 3;
+    const int ph = (__builtin_popcount(a.obs & a.obs_x) + ((a.flags & PF_OBS_NEG) ? 2 : 0)) & 3;
     Tile<R> o;
     R e = 0;
 #pragma unroll

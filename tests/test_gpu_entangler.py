@@ -160,6 +160,37 @@ def test_cnot_tile_path(n, L, B, zm):
     assert_grad_close(g2, g2_ref)
 
 
+# Pauli strings with X / Y factors on the tile path: the passes measure the string
+# conjugated by the last chain (X on q -> X on q and q+1), with its sign
+TILE_PAULI = [
+    (14, 2, 2, 0b1, 0b10),
+    (15, 3, 2, 1 << 5, (1 << 5) | 1),
+    (16, 2, 2, 1 << 15, (1 << 15) | (1 << 3)),
+    (17, 3, 1, 0, (1 << 12) | (1 << 2)),
+    (16, 3, 2, 0b11, 0b11),
+]
+
+
+@pytest.mark.parametrize("n,L,B,zm,xm", TILE_PAULI)
+def test_cnot_tile_pauli_strings(n, L, B, zm, xm):
+    say(f"[gpu] CNOT tile Pauli n={n} L={L} z={zm:#x} x={xm:#x}")
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=2050 + n + L)
+    X, TH, Y = (torch.from_numpy(a) for a in (x, th, y))
+    ctx = _ctx(n, L, B, zm, xm)
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(X, TH, Y))
+    e2 = ctx.forward(X, TH).cpu().numpy()
+    w = np.linspace(-1.0, 1.0, B).astype(np.float32)
+    g2 = ctx.backward(torch.from_numpy(w)).cpu().numpy()
+    ctx.close()
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, zm, xm, entangler=1)
+    assert_e_close(e, e_ref, n, L)
+    assert abs(float(loss[0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
+    assert_grad_close(g, g_ref)
+    g2_ref, _ = oracle.backward(x, th, w.astype(np.float64), zm, xm, entangler=1)
+    assert_e_close(e2, e_ref, n, L)
+    assert_grad_close(g2, g2_ref)
+
+
 def test_cnot_tile_checkpoints_and_chunks_are_bitwise_identical():
     """Checkpoint blocks (recomputed passes, including the chain reads) and batch chunks
     change nothing in the CNOT plan's results."""

@@ -118,10 +118,14 @@ def test_entangler_config_host_only():
     cn = hq.hqml_workspace_bytes(hq.make_config(20, 10, 4, entangler="cnot"))
     st = 4 * (1 << 20) * 8
     assert cn - cz >= 10 * st   # 19 saved pass outputs instead of 10, plus lambda
-    tile = hq.make_config(14, 3, 2, entangler="cnot", obs_x_mask=1)
-    assert hq.hqml_workspace_bytes(tile) == 0
+    # X/Y factors: the chain-conjugated string has X on q and q+1 for each X/Y on q; it
+    # must fit the observable view (at most 9 such qubits above qubit 3)
+    assert hq.hqml_workspace_bytes(hq.make_config(20, 3, 2, entangler="cnot", obs_x_mask=0b1010 << 4)) > 0
+    wide = hq.make_config(20, 3, 2, entangler="cnot", obs_x_mask=0b1010101010 << 4)   # 10 qubits after
+    assert hq.hqml_workspace_bytes(wide) == 0
+    assert hq.hqml_workspace_bytes(hq.make_config(20, 3, 2, obs_x_mask=0b1010101010 << 4)) > 0   # CZ: 5
     with pytest.raises(hq.HqmlError) as e:
-        hq.hqml_create(tile)
+        hq.hqml_create(wide)
     assert e.value.status == hq.HQML_ERR_UNSUPPORTED
     for bad in (hq.make_config(4, 1, 1, entangler=2), hq.make_config(4, 1, 1, entangler=-1)):
         assert hq.hqml_workspace_bytes(bad) == 0
