@@ -1014,7 +1014,7 @@ int hqml_plan_info(const hqml_ctx *c, int *fwd_passes, int *bwd_passes, int *til
     if (!c) return HQML_ERR_ARG;
     const Plan &pl = c->plan;
     if (c->gbg) {
-        const int gates = pl.L * (4 * pl.n - 1);   // 3n rotations and n-1 CZ per layer
+        const int gates = pl.L * (4 * pl.n - 1);   // 3n rotations and n-1 entangling gates per layer
         if (fwd_passes) *fwd_passes = gates + pl.n;
         if (bwd_passes) *bwd_passes = gates;
         if (tiles_per_sample) *tiles_per_sample = c->gbg_blocks;

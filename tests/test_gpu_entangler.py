@@ -252,3 +252,25 @@ def test_cnot_tile_20_qubits_sampled():
         assert_e_close(e[b:b + 1], e_ref, n, L)
         assert_grad_close(g, g_ref)
     ctx.close()
+
+
+def test_cnot_tile_29_qubits_light_cone():
+    """hea29q4l with the CNOT chain (four views, 13 passes, per-layer checkpoints, 4 GiB
+    state): Z_0 passes each chain unchanged and an X on q widens to q, q+1 per earlier
+    chain, so with 4 layers E and the gradient equal those of the 4-qubit circuit on the
+    same angles, and every other derivative is 0."""
+    import qml_gradients_amd as hq
+    name = "hea29q4l"
+    w = hqml_inputs.WORKLOADS[name]
+    x, th, y = hqml_inputs.workload_inputs(name)
+    n, L = w.n_qubits, w.n_layers
+    e_ref, loss_ref, g4 = oracle.train_step(x[:, :L], th[:, :L, :], y, entangler=1)
+    g_ref = np.zeros((L, n, 3))
+    g_ref[:, :L, :] = g4
+    say(f"[gpu] {name} CNOT")
+    ctx = hq.Context(n, L, w.batch, ckpt_block=w.ckpt_block, entangler="cnot")
+    assert ctx.plan_info()["fwd_passes"] == 1 + (L - 1) * 4
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(*(torch.from_numpy(a) for a in (x, th, y))))
+    ctx.close()
+    assert_e_close(e, e_ref, n, L)
+    assert_grad_close(g, g_ref)
