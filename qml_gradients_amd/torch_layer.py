@@ -37,13 +37,14 @@ class HEAExpectation(torch.autograd.Function):
 
 class HEALayer(torch.nn.Module):
     """Hardware-efficient ansatz layer: angle encoding Ry(x_q), n_layers of Rx, Ry, Rz on
-    every qubit plus the CZ chain, output <O> per sample (O = Z_0 unless obs_mask /
-    obs_x_mask say otherwise).  theta [n_layers][n_qubits][3] is the trainable parameter.
+    every qubit plus the CZ chain (or the CNOT chain, entangler="cnot"), output <O> per
+    sample (O = Z_0 unless obs_mask / obs_x_mask say otherwise).  theta
+    [n_layers][n_qubits][3] is the trainable parameter.
     The remaining arguments are those of the C ABI's hqml_config; storage defaults to
     the compute type's (complex128 states with compute="fp64")."""
 
     def __init__(self, n_qubits, n_layers, max_batch, storage=None, ckpt_block=0, compute="fp32",
-                 obs_mask=0, obs_x_mask=0, theta=None, device=None):
+                 obs_mask=0, obs_x_mask=0, theta=None, device=None, entangler="cz"):
         super().__init__()
         if storage is None:
             storage = "fp64" if compute == "fp64" else "fp32"
@@ -53,7 +54,8 @@ class HEALayer(torch.nn.Module):
             theta = torch.rand(n_layers, n_qubits, 3, dtype=torch.float64) * (2.0 * math.pi)
         self.theta = torch.nn.Parameter(torch.as_tensor(theta).to(dev, dtype).contiguous())
         self.hq = Context(n_qubits, n_layers, max_batch, storage=storage, ckpt_block=ckpt_block,
-                          device=dev.index, compute=compute, obs_mask=obs_mask, obs_x_mask=obs_x_mask)
+                          device=dev.index, compute=compute, obs_mask=obs_mask, obs_x_mask=obs_x_mask,
+                          entangler=entangler)
 
     def forward(self, x):
         return HEAExpectation.apply(self.theta, x, self.hq)

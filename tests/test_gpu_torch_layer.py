@@ -12,19 +12,21 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 
-@pytest.mark.parametrize("n,L,B,compute", [(5, 3, 4, "fp32"), (16, 3, 3, "fp32"), (16, 2, 2, "fp64")])
-def test_layer_backward_matches_oracle(n, L, B, compute):
+@pytest.mark.parametrize("n,L,B,compute,ent", [(5, 3, 4, "fp32", "cz"), (16, 3, 3, "fp32", "cz"),
+                                               (16, 2, 2, "fp64", "cz"), (6, 3, 2, "fp32", "cnot"),
+                                               (15, 3, 2, "fp32", "cnot")])
+def test_layer_backward_matches_oracle(n, L, B, compute, ent):
     from qml_gradients_amd.torch_layer import HEALayer
     x, th, y = hqml_inputs.make_inputs(n, L, B, seed=1400 + n)
-    say(f"[gpu] HEALayer n={n} L={L} {compute}")
-    layer = HEALayer(n, L, B, compute=compute, theta=torch.from_numpy(th))
+    say(f"[gpu] HEALayer n={n} L={L} {compute} {ent}")
+    layer = HEALayer(n, L, B, compute=compute, theta=torch.from_numpy(th), entangler=ent)
     dt = layer.theta.dtype
     X = torch.from_numpy(x).cuda().to(dt)
     Y = torch.from_numpy(y).cuda().to(dt)
     e = layer(X)
     loss = torch.mean((e - Y) ** 2)
     loss.backward()
-    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, entangler=1 if ent == "cnot" else 0)
     g = layer.theta.grad.cpu().numpy()
     if compute == "fp64":
         assert np.max(np.abs(e.detach().cpu().numpy() - e_ref)) <= 1e-10
