@@ -163,6 +163,7 @@ def test_cnot_tile_path(n, L, B, zm):
 # Pauli strings with X / Y factors on the tile path: the passes measure the string
 # conjugated by the last chain (X on q -> X on q and q+1), with its sign
 TILE_PAULI = [
+    (14, 1, 2, 0b1, 0b110),
     (14, 2, 2, 0b1, 0b10),
     (15, 3, 2, 1 << 5, (1 << 5) | 1),
     (16, 2, 2, 1 << 15, (1 << 15) | (1 << 3)),
