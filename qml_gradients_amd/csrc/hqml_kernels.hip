@@ -1718,17 +1718,19 @@ __global__ void k_prep_frame(const double *zyz, int L, int n, int ent, unsigned 
 {
     const int q = blockIdx.x * blockDim.x + threadIdx.x;
     if (ent == 2) {
-        if (q != 0) return;
+        // one wave, lane q = qubit q (n <= 29 < 64); the mask g is the same in every lane
         const uint32_t full = (uint32_t)((1ull << n) - 1ull);
         uint32_t g = 0;
         for (int l = L - 1; l >= 0; --l) {
-            for (int k = 0; k < n; ++k) G[(size_t)l * n + k] = (unsigned char)((g >> k) & 1u);
+            if (q < n) G[(size_t)l * n + q] = (unsigned char)((g >> q) & 1u);
             if (l == 0) break;
-            uint32_t rw = 0;   // qubits rewritten at layer l: their X enters before Ry, after diag(r_l)
-            for (int k = 0; k < n; ++k) {
-                const double *z = zyz + ((size_t)l * n + k) * 6;
-                if (z[1] > z[0]) rw |= 1u << k;
+            // qubits rewritten at layer l: their X enters before Ry, after diag(r_l)
+            bool rwq = false;
+            if (q < n) {
+                const double *z = zyz + ((size_t)l * n + q) * 6;
+                rwq = z[1] > z[0];
             }
+            const uint32_t rw = (uint32_t)__ballot(rwq) & full;
             const uint32_t gb = g ^ rw;
             g = (gb ^ (gb << 1)) & full;
         }
