@@ -214,6 +214,27 @@ def test_cnot_tile_checkpoints_and_chunks_are_bitwise_identical():
     assert_grad_close(outs[0][2], g_ref)
 
 
+def test_cnot_tile_pauli_checkpoints_and_ragged_batch():
+    """X/Y observable with checkpoint blocks, and a smaller batch on the same context:
+    bitwise equal to the stored-output run, and equal to the oracle."""
+    import qml_gradients_amd as hq
+    n, L, maxB, zm, xm = 15, 4, 4, 0b1, (1 << 9) | 0b10
+    x, th, y = hqml_inputs.make_inputs(n, L, maxB, seed=2150)
+    outs = []
+    for ckpt in (0, 1):
+        say(f"[gpu] CNOT tile Pauli ckpt={ckpt}")
+        ctx = hq.Context(n, L, maxB, ckpt_block=ckpt, obs_mask=zm, obs_x_mask=xm, entangler="cnot")
+        full = [t.cpu().numpy() for t in ctx.train_step(*(torch.from_numpy(a) for a in (x, th, y)))]
+        part = [t.cpu().numpy() for t in ctx.train_step(*(torch.from_numpy(a) for a in (x[:3], th, y[:3])))]
+        ctx.close()
+        outs.append((full, part))
+    for a, b in zip(outs[0][0] + outs[0][1], outs[1][0] + outs[1][1]):
+        assert np.array_equal(a, b)
+    e_ref, _, g_ref = oracle.train_step(x[:3], th, y[:3], zm, xm, entangler=1)
+    assert_e_close(outs[0][1][0], e_ref, n, L)
+    assert_grad_close(outs[0][1][2], g_ref)
+
+
 def test_cnot_tile_bf16_storage():
     n, L, B = 16, 4, 2
     say("[gpu] CNOT tile bf16")
