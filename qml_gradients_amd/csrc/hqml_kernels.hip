@@ -1276,15 +1276,20 @@ __device__ __forceinline__ V2<R> small_diag(const V4<R> *wl, int n, uint32_t i)
     return f;
 }
 
-// (O phi)_i for the Pauli string (zm, xm), phi = D_trail psi the true final state
-// (wl: the trailing diagonal's factors; applied only when xm != 0, since D_trail
-// commutes with Z):  i^(#Y) (-1)^|(i ^ xm) & zm| phi_(i ^ xm).
+// LDS slot of amplitude i on the CZ small path: bits 0..4 XOR bits 4..8 (a bijection: bits 5 and up are
+// unchanged).  With it the rounds on qubits 0..3 (consecutive lanes step bit 4), 4..7
+// and 8..11 give every 32 consecutive lanes distinct 8-byte slots modulo 256 bytes.
+__device__ __forceinline__ uint32_t sslot(uint32_t i) { return i ^ ((i >> 4) & 31u); }
+
+// (O phi)_i for the Pauli string (zm, xm), phi = D_trail psi the true final state held
+// at slots sslot(i) (wl: the trailing diagonal's factors; applied only when xm != 0,
+// since D_trail commutes with Z):  i^(#Y) (-1)^|(i ^ xm) & zm| phi_(i ^ xm).
 template <typename R>
 __device__ __forceinline__ V2<R> small_obs(const V2<R> *psi, uint32_t i, uint32_t zm, uint32_t xm, const V4<R> *wl,
                                            int n)
 {
     const uint32_t j = i ^ xm;
-    V2<R> w = psi[j];
+    V2<R> w = psi[sslot(j)];
     if (xm) w = cmul(w, small_diag<R>(wl, n, j));
     R re = (__builtin_popcount(j & zm) & 1) ? -w.x : w.x;
     R im = (__builtin_popcount(j & zm) & 1) ? -w.y : w.y;
@@ -1505,13 +1510,315 @@ __device__ void small_cnot_circuit(const SmallArgs &a, V2<R> *psi, V2<R> *lam, R
     }
 }
 
+// ---- whole circuit per workgroup with the CZ chain: register rounds
+//
+// The state of one sample lives in LDS.  A "round" on qubits s .. s+G-1 (G <= 4) hands
+// every thread whole groups of 2^G amplitudes {base + (j << s)}, gathers a group into
+// registers, applies the round's work there and writes it back, so each LDS round trip
+// covers four qubits.  Round 0 (qubits 0 .. G0-1) also applies the merged diagonal D_l,
+// factored as T[j] (qubits below G0 and the CZ signs among them: uniform, built once per
+// layer) times a per-group factor over the other qubits (with their CZ signs and the
+// CZ between qubits G0-1 and G0).  Rotations use the scaled tangent form of rot_bit;
+// the uniform scale is carried along and folded into the next diagonal.
+
+template <typename R>
+__device__ __forceinline__ R lane_bcast(R v, int lane);
+
+template <>
+__device__ __forceinline__ float lane_bcast<float>(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+template <>
+__device__ __forceinline__ double lane_bcast<double>(double v, int lane)
+{
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), lane);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// Factor of the low qubits: prod_{q < G0} f_q(bit q of j) for j = lane & 15, with the CZ
+// signs among those qubits if cz.  f_q = (x, y) for bit value 0, (z, w) for 1.
+template <typename R>
+__device__ __forceinline__ V2<R> low_factor(const V4<R> *f, int G0, bool cz, int lane)
+{
+    const uint32_t j = (uint32_t)lane & 15u;
+    V2<R> t = mk2((R)1, (R)0);
+    for (int q = 0; q < G0; ++q) {
+        const V4<R> g = f[q];
+        t = cmul(t, ((j >> q) & 1u) ? mk2(g.z, g.w) : mk2(g.x, g.y));
+    }
+    if (cz && (__builtin_popcount(j & (j >> 1) & ((1u << G0) - 1u)) & 1)) t = mk2(-t.x, -t.y);
+    return t;
+}
+
+// Factor of the high qubits of group g of round 0: prod_{q >= G0} f_q(bit q - G0 of g),
+// with the CZ signs among them if cz.
+template <typename R>
+__device__ __forceinline__ V2<R> high_factor(const V4<R> *f, int G0, int n, uint32_t g, bool cz)
+{
+    V2<R> h = mk2((R)1, (R)0);
+    for (int q = G0; q < n; ++q) {
+        const V4<R> w = f[q];
+        h = cmul(h, ((g >> (q - G0)) & 1u) ? mk2(w.z, w.w) : mk2(w.x, w.y));
+    }
+    if (cz && (__builtin_popcount(g & (g >> 1)) & 1)) h = mk2(-h.x, -h.y);
+    return h;
+}
+
+template <int G, typename R>
+struct SmallGroup {
+    R re[1 << G], im[1 << G];
+};
+
+template <int G, typename R>
+__device__ __forceinline__ void sg_load(SmallGroup<G, R> &v, const V2<R> *st, uint32_t base, int s)
+{
+#pragma unroll
+    for (int j = 0; j < (1 << G); ++j) {
+        const V2<R> a = st[sslot(base | ((uint32_t)j << s))];
+        v.re[j] = a.x;
+        v.im[j] = a.y;
+    }
+}
+
+template <int G, typename R>
+__device__ __forceinline__ void sg_store(const SmallGroup<G, R> &v, V2<R> *st, uint32_t base, int s)
+{
+#pragma unroll
+    for (int j = 0; j < (1 << G); ++j) st[sslot(base | ((uint32_t)j << s))] = mk2(v.re[j], v.im[j]);
+}
+
+// Tangent-form rotation of register bit m of a group (INV: the inverse); see rot_bit.
+template <int G, bool INV, typename R>
+__device__ __forceinline__ void sg_rot(SmallGroup<G, R> &v, int m, R k)
+{
+    const R kk = INV ? -k : k;
+#pragma unroll
+    for (int j = 0; j < (1 << G); ++j) {
+        if ((j >> m) & 1) continue;
+        const int o = j | (1 << m);
+        const R ar = v.re[j], ai = v.im[j], br = v.re[o], bi = v.im[o];
+        v.re[j] = fmar(-kk, br, ar);
+        v.im[j] = fmar(-kk, bi, ai);
+        v.re[o] = fmar(kk, ar, br);
+        v.im[o] = fmar(kk, ai, bi);
+    }
+}
+
+// The 16 entries T[j] of the low-qubit factor, held by lanes j = lane & 15, as uniform
+// values.  Called with every lane of the wave active (readlane reads a lane whether or
+// not it is active, so the entries must be computed outside divergent code).
+template <int G, typename R>
+__device__ __forceinline__ void bcast_low(V2<R> (&t)[1 << G], V2<R> tl)
+{
+#pragma unroll
+    for (int j = 0; j < (1 << G); ++j) t[j] = mk2(lane_bcast<R>(tl.x, j), lane_bcast<R>(tl.y, j));
+}
+
+// Multiply a round-0 group by its diagonal D_j = T[j] * (h or hx), hx for j with bit G-1
+// set (the CZ between qubits G-1 and G).  CONJ: by conj(D).
+template <int G, bool CONJ, typename R>
+__device__ __forceinline__ void sg_diag(SmallGroup<G, R> &v, const V2<R> (&t)[1 << G], V2<R> h, V2<R> hx)
+{
+#pragma unroll
+    for (int j = 0; j < (1 << G); ++j) {
+        V2<R> d = cmul(t[j], ((j >> (G - 1)) & 1) ? hx : h);
+        if (CONJ) d.y = -d.y;
+        const R re = v.re[j] * d.x - v.im[j] * d.y;
+        const R im = v.re[j] * d.y + v.im[j] * d.x;
+        v.re[j] = re;
+        v.im[j] = im;
+    }
+}
+
+// X, Y, Z statistics of register bit m of a group pair (psi p, lambda l), added to
+// sx, sy, sz (the same sums as xy_stats and the Z fold of stats_visit).
+template <int G, typename R>
+__device__ __forceinline__ void sg_stats(const SmallGroup<G, R> &p, const SmallGroup<G, R> &l, int m, R &sx, R &sy,
+                                         R &sz)
+{
+    R xp = 0, xn = 0, yp = 0, yn = 0, zp = 0, zn = 0;
+#pragma unroll
+    for (int j = 0; j < (1 << G); ++j) {
+        if ((j >> m) & 1) continue;
+        const int o = j | (1 << m);
+        xp = fmar(l.re[j], p.im[o], xp);
+        xp = fmar(l.re[o], p.im[j], xp);
+        xn = fmar(l.im[j], p.re[o], xn);
+        xn = fmar(l.im[o], p.re[j], xn);
+        yp = fmar(l.re[o], p.re[j], yp);
+        yp = fmar(l.im[o], p.im[j], yp);
+        yn = fmar(l.re[j], p.re[o], yn);
+        yn = fmar(l.im[j], p.im[o], yn);
+        zp = fmar(l.re[j], p.im[j], zp);
+        zp = fmar(l.im[o], p.re[o], zp);
+        zn = fmar(l.im[j], p.re[j], zn);
+        zn = fmar(l.re[o], p.im[o], zn);
+    }
+    sx += xp - xn;
+    sy += yp - yn;
+    sz += zp - zn;
+}
+
+struct SmallRound {
+    int s, G;          // qubits s .. s+G-1
+    uint32_t groups;   // 2^(n - G)
+};
+
+__device__ __forceinline__ uint32_t sg_base(uint32_t g, int s, int G)
+{
+    return ((g >> s) << (s + G)) | (g & ((1u << s) - 1u));
+}
+
+// Forward round: [round 0: init from the product-state factors (INIT) or multiply by
+// scale * D], rotations of the round's qubits with layer lr's coefficients (lr < 0:
+// none), [LAST: multiply by fin].
+template <int G, typename R>
+__device__ __forceinline__ void small_fwd_round(V2<R> *psi, const SmallArgs &a, SmallRound rd, int lr, bool init,
+                                                bool diag, const V4<R> *f, V2<R> tl, R scale, bool last, R fin)
+{
+    const V2<R> *rtf = reinterpret_cast<const V2<R> *>(a.rot_tf);
+    R k[G];
+#pragma unroll
+    for (int m = 0; m < G; ++m) k[m] = lr >= 0 ? rtf[(size_t)lr * a.n + rd.s + m].x : (R)0;
+    V2<R> t[1 << G];
+    bcast_low<G, R>(t, tl);
+    for (uint32_t g = threadIdx.x; g < rd.groups; g += kThreads) {
+        const uint32_t base = sg_base(g, rd.s, G);
+        SmallGroup<G, R> v;
+        if (init || diag) {
+            V2<R> h = high_factor<R>(f, G, a.n, g, !init);
+            h = mk2(h.x * scale, h.y * scale);
+            const V2<R> hx = (!init && G < a.n && (g & 1u)) ? mk2(-h.x, -h.y) : h;
+            if (init) {   // the product state: T[j] * h
+#pragma unroll
+                for (int j = 0; j < (1 << G); ++j) {
+                    v.re[j] = (R)1;
+                    v.im[j] = (R)0;
+                }
+            } else {
+                sg_load<G>(v, psi, base, rd.s);
+            }
+            sg_diag<G, false>(v, t, h, hx);
+        } else {
+            sg_load<G>(v, psi, base, rd.s);
+        }
+        if (lr >= 0) {
+#pragma unroll
+            for (int m = 0; m < G; ++m) sg_rot<G, false>(v, m, k[m]);
+        }
+        if (last) {
+#pragma unroll
+            for (int j = 0; j < (1 << G); ++j) {
+                v.re[j] *= fin;
+                v.im[j] *= fin;
+            }
+        }
+        sg_store<G>(v, psi, base, rd.s);
+    }
+}
+
+// Adjoint round at layer l: [round 0 and D: multiply psi and lambda by scale * conj(D)],
+// statistics of the round's qubits (scaled by corr) into red, then, if urot, the inverse
+// rotations of layer l on both states; the groups are written back if anything changed.
+template <int G, typename R>
+__device__ __forceinline__ void small_adj_round(V2<R> *psi, V2<R> *lam, const SmallArgs &a, SmallRound rd, int l,
+                                                bool diag, const V4<R> *f, V2<R> tl, R scale, R corr, bool urot,
+                                                R *red)
+{
+    const V2<R> *rtf = reinterpret_cast<const V2<R> *>(a.rot_tf);
+    R k[G], sx[G], sy[G], sz[G];
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+        k[m] = rtf[(size_t)l * a.n + rd.s + m].x;
+        sx[m] = sy[m] = sz[m] = (R)0;
+    }
+    V2<R> t[1 << G];
+    bcast_low<G, R>(t, tl);
+    for (uint32_t g = threadIdx.x; g < rd.groups; g += kThreads) {
+        const uint32_t base = sg_base(g, rd.s, G);
+        SmallGroup<G, R> p, q;
+        sg_load<G>(p, psi, base, rd.s);
+        sg_load<G>(q, lam, base, rd.s);
+        if (diag) {
+            V2<R> h = high_factor<R>(f, G, a.n, g, true);
+            h = mk2(h.x * scale, h.y * scale);
+            const V2<R> hx = (G < a.n && (g & 1u)) ? mk2(-h.x, -h.y) : h;
+            sg_diag<G, true>(p, t, h, hx);
+            sg_diag<G, true>(q, t, h, hx);
+        }
+#pragma unroll
+        for (int m = 0; m < G; ++m) sg_stats<G>(p, q, m, sx[m], sy[m], sz[m]);
+        if (urot) {
+#pragma unroll
+            for (int m = 0; m < G; ++m) {
+                sg_rot<G, true>(p, m, k[m]);
+                sg_rot<G, true>(q, m, k[m]);
+            }
+        }
+        if (urot || diag) {   // at l = 0 the later rounds still need D_0^dagger applied
+            sg_store<G>(p, psi, base, rd.s);
+            sg_store<G>(q, lam, base, rd.s);
+        }
+    }
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+        R x = sx[m] * corr, y = sy[m] * corr, z = sz[m] * corr;
+        row_sum16x3(x, y, z);
+        if ((lane & 15) == 15) {
+            const int r = w * 4 + (lane >> 4), q = rd.s + m;
+            red[(q * 3 + 0) * 16 + r] = x;
+            red[(q * 3 + 1) * 16 + r] = y;
+            red[(q * 3 + 2) * 16 + r] = z;
+        }
+    }
+}
+
+__device__ __forceinline__ SmallRound small_round(int n, int r)
+{
+    SmallRound rd;
+    rd.s = 4 * r;
+    rd.G = n - rd.s < 4 ? n - rd.s : 4;
+    rd.groups = (1u << n) >> rd.G;
+    return rd;
+}
+
+template <typename R>
+__device__ __forceinline__ void small_fwd_round_g(V2<R> *psi, const SmallArgs &a, SmallRound rd, int lr, bool init,
+                                                  bool diag, const V4<R> *f, V2<R> tl, R scale, bool last, R fin)
+{
+    switch (rd.G) {
+    case 1: small_fwd_round<1, R>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
+    case 2: small_fwd_round<2, R>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
+    case 3: small_fwd_round<3, R>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
+    default: small_fwd_round<4, R>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
+    }
+}
+
+template <typename R>
+__device__ __forceinline__ void small_adj_round_g(V2<R> *psi, V2<R> *lam, const SmallArgs &a, SmallRound rd, int l,
+                                                  bool diag, const V4<R> *f, V2<R> tl, R scale, R corr, bool urot,
+                                                  R *red)
+{
+    switch (rd.G) {
+    case 1: small_adj_round<1, R>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
+    case 2: small_adj_round<2, R>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
+    case 3: small_adj_round<3, R>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
+    default: small_adj_round<4, R>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
+    }
+}
+
 // ENT: the entangler (0 CZ chain, 1 CNOT chain), one instance each so that the CZ
 // kernel keeps its own register budget.
 template <typename R, int ENT>
 __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ R red[3 * kSmallMaxQubits * 16 + 16];
+    __shared__ R red[2 * 3 * kSmallMaxQubits * 16 + 16];
     const int n = a.n, L = a.L;
     const uint32_t N = 1u << n;
     V2<R> *psi = reinterpret_cast<V2<R> *>(smem);
@@ -1525,37 +1832,32 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
         return;
     }
 
+    const int G0 = n < 4 ? n : 4;
+    const int nr = (n + 3) / 4;   // rounds per layer: qubits 0..3, 4..7, 8..11, 12
     if (a.mode != 1) {
         const V4<R> *u = reinterpret_cast<const V4<R> *>(a.init_u) + (size_t)b * n;
-        for (uint32_t i = tid; i < N; i += kThreads) {
-            V2<R> v = mk2((R)1, (R)0);
-            for (int q = 0; q < n; ++q) {
-                const V4<R> f = u[q];
-                v = cmul(v, ((i >> q) & 1u) ? mk2(f.z, f.w) : mk2(f.x, f.y));
-            }
-            psi[i] = v;
-        }
+        small_fwd_round_g<R>(psi, a, small_round(n, 0), -1, true, false, u, low_factor<R>(u, G0, false, lane), (R)1,
+                             false, (R)1);
         __syncthreads();
+        R c = 1;   // true state = stored state * c
         for (int l = 0; l + 1 < L; ++l) {
+            // D_l (with the pending scale c), then Ry-layer l+1 round by round
             const V4<R> *wl = dw + (size_t)l * n;
-            for (uint32_t i = tid; i < N; i += kThreads) psi[i] = cmul(psi[i], small_diag<R>(wl, n, i));
-            __syncthreads();
-            for (int q = 0; q < n; ++q) {
-                const V2<R> tf = rtf[(size_t)(l + 1) * n + q];
-                const V2<R> cs = mk2(tf.y, tf.x * tf.y);   // (cos, sin) of the rotation
-                for (uint32_t k = tid; k < N / 2; k += kThreads) {
-                    const uint32_t i = pair_index(k, q), j = i | (1u << q);
-                    const V2<R> x = psi[i], y = psi[j];
-                    psi[i] = mk2(cs.x * x.x - cs.y * y.x, cs.x * x.y - cs.y * y.y);
-                    psi[j] = mk2(cs.y * x.x + cs.x * y.x, cs.y * x.y + cs.x * y.y);
-                }
+            const V2<R> tl = low_factor<R>(wl, G0, true, lane);
+            R cn = 1;
+            for (int r = 0; r < nr; ++r) {
+                const SmallRound rd = small_round(n, r);
+                for (int m = 0; m < rd.G; ++m) cn *= rtf[(size_t)(l + 1) * n + rd.s + m].y;
+                const bool last = l + 2 == L && r + 1 == nr;
+                small_fwd_round_g<R>(psi, a, rd, l + 1, false, r == 0, wl, tl, c, last, cn);
                 __syncthreads();
             }
+            c = cn;
         }
         // <O> = sum_i Re(conj(psi_i) (O psi)_i)
         R e = 0;
         for (uint32_t i = tid; i < N; i += kThreads) {
-            V2<R> v = psi[i];
+            V2<R> v = psi[sslot(i)];
             if (a.obs_x) v = cmul(v, small_diag<R>(dw + (size_t)(L - 1) * n, n, i));
             const V2<R> o = small_obs<R>(psi, i, a.obs, a.obs_x, dw + (size_t)(L - 1) * n, n);
             e += v.x * o.x + v.y * o.y;
@@ -1569,12 +1871,12 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
             static_cast<R *>(a.e_out)[b] = (R)s;
         }
         if (a.mode == 0) {
-            for (uint32_t i = tid; i < N; i += kThreads) save[i] = psi[i];
+            for (uint32_t i = tid; i < N; i += kThreads) save[i] = psi[sslot(i)];
             return;
         }
         __syncthreads();
     } else {
-        for (uint32_t i = tid; i < N; i += kThreads) psi[i] = save[i];
+        for (uint32_t i = tid; i < N; i += kThreads) psi[sslot(i)] = save[i];
         __syncthreads();
     }
 
@@ -1587,36 +1889,32 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
             f.y = -f.y;
             o = cmul(o, f);
         }
-        lam[i] = o;
+        lam[sslot(i)] = o;
     }
     __syncthreads();
+    // Layer l: [D_l^dagger with the pending scale], then per round the statistics of its
+    // qubits at P_l and the inverse rotations of Ry-layer l (none at l = 0).  The
+    // statistics partials alternate between two halves of red, so the sums of layer l
+    // are read while layer l-1 writes the other half.
+    R c = 1;
     for (int l = L - 1; l >= 0; --l) {
-        small_stats<R>(psi, lam, a, l, red);
-        if (l == 0) break;
-        // uncompute Ry-layer l and D_{l-1} on psi and lambda
-        for (int q = 0; q < n; ++q) {
-            const V2<R> tf = rtf[(size_t)l * n + q];
-            const V2<R> cs = mk2(tf.y, tf.x * tf.y);
-            for (uint32_t k = tid; k < N / 2; k += kThreads) {
-                const uint32_t i = pair_index(k, q), j = i | (1u << q);
-                V2<R> x = psi[i], y = psi[j];
-                psi[i] = mk2(cs.x * x.x + cs.y * y.x, cs.x * x.y + cs.y * y.y);
-                psi[j] = mk2(-cs.y * x.x + cs.x * y.x, -cs.y * x.y + cs.x * y.y);
-                x = lam[i];
-                y = lam[j];
-                lam[i] = mk2(cs.x * x.x + cs.y * y.x, cs.x * x.y + cs.y * y.y);
-                lam[j] = mk2(-cs.y * x.x + cs.x * y.x, -cs.y * x.y + cs.x * y.y);
-            }
+        R *rl = red + (l & 1) * (3 * kSmallMaxQubits * 16);
+        const bool diag = l + 1 < L;
+        const V4<R> *wl = dw + (size_t)l * n;
+        const V2<R> tl = low_factor<R>(wl, G0, true, lane);
+        R cc = 1;
+        for (int r = 0; r < nr; ++r) {
+            const SmallRound rd = small_round(n, r);
+            small_adj_round_g<R>(psi, lam, a, rd, l, diag && r == 0, wl, tl, c, cc * cc, l > 0, rl);
+            for (int m = 0; l > 0 && m < rd.G; ++m) cc *= rtf[(size_t)l * n + rd.s + m].y;   // scales of the rotations undone
             __syncthreads();
         }
-        const V4<R> *wl = dw + (size_t)(l - 1) * n;
-        for (uint32_t i = tid; i < N; i += kThreads) {
-            V2<R> f = small_diag<R>(wl, n, i);
-            f.y = -f.y;
-            psi[i] = cmul(psi[i], f);
-            lam[i] = cmul(lam[i], f);
+        if (tid < 3 * n) {
+            double s = 0.0;
+            for (int k = 0; k < 16; ++k) s += (double)rl[tid * 16 + k];
+            a.stats[(((size_t)b * L + l) * n) * 3 + tid] = s;
         }
-        __syncthreads();
+        c = cc;
     }
 }
 
