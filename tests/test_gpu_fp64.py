@@ -136,3 +136,18 @@ def test_fp32_noise_floor_of_e(ent):
     # proportional to |E| (an additive floor near 2^(-n/2) eps32 sqrt(L (n + 2)))
     sigma = 2.0 * np.sqrt(2.0) * 2.0 ** -24 * np.sqrt(L * (n + 2)) * 2.0 ** (-n / 2)
     assert 0.1 * sigma < np.median(err) < 3.0 * sigma, (np.median(err), sigma)
+
+
+@pytest.mark.parametrize("n", [2, 3, 5, 6, 8, 9, 10, 11, 12])
+def test_fp64_whole_circuit_widths(n):
+    """fp64 whole-circuit kernel at the widths the train-step cases above skip (round
+    remainders of 1..3 qubits, the CZ between qubits 3 and 4), L = 3."""
+    L, B = 3, 2
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=3300 + n)
+    say(f"[gpu] fp64 whole circuit n={n}")
+    ctx = _ctx(n, L, B, storage="fp64")
+    X, TH, Y = (torch.from_numpy(a.astype(np.float64)) for a in (x, th, y))
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(X, TH, Y))
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
+    _check64(e, g, e_ref, g_ref)
+    ctx.close()

@@ -202,3 +202,41 @@ def test_null_pointer_arguments():
         hq.hqml_train_step(ctx.handle, 3, p, p, p, p, p, p)      # B > max_batch
     assert e.value.status == hq.HQML_ERR_ARG
     ctx.close()
+
+
+def _whole_circuit_obs(n):
+    """A Pauli string for width n: Z_0 alone on even widths, else Z_0 Y_(n-1) with an X
+    on qubit n // 2 (X/Y factors read partner amplitudes across the swizzled slots)."""
+    if n % 2 == 0 or n == 1:
+        return 1, 0
+    top, mid = 1 << (n - 1), 1 << (n // 2)
+    return 1 | top, top | mid
+
+
+@pytest.mark.parametrize("L", [1, 4])
+@pytest.mark.parametrize("n", list(range(1, 14)))
+def test_whole_circuit_every_width(n, L):
+    """Whole-circuit kernel at every width 1..13: the register rounds cover qubits
+    0..3, 4..7, 8..11, 12 and so leave remainders of 1..3 qubits; the diagonal's CZ
+    between qubits 3 and 4 exists only for n > 4; small n leaves most threads idle.
+    Train step and forward/backward split, a smaller batch on the same context."""
+    import qml_gradients_amd as hq
+    zm, xm = _whole_circuit_obs(n)
+    maxB = 3
+    x, th, y = hqml_inputs.make_inputs(n, L, maxB, seed=3100 + 17 * n + L)
+    say(f"[gpu] whole circuit n={n} L={L} z={zm:#x} x={xm:#x}")
+    ctx = hq.Context(n, L, maxB, obs_mask=zm, obs_x_mask=xm)
+    for B in (maxB, 2):
+        X, TH, Y = (torch.from_numpy(a) for a in (x[:B], th, y[:B]))
+        e, loss, g = (t.cpu().numpy() for t in ctx.train_step(X, TH, Y))
+        e_ref, loss_ref, g_ref = oracle.train_step(x[:B], th, y[:B], zm, xm)
+        assert_e_close(e, e_ref, n, L)
+        assert abs(float(loss[0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
+        assert_grad_close(g, g_ref)
+    w = np.linspace(-0.5, 1.5, 2).astype(np.float32)
+    e2 = ctx.forward(torch.from_numpy(x[:2]), torch.from_numpy(th)).cpu().numpy()
+    g2 = ctx.backward(torch.from_numpy(w)).cpu().numpy()
+    g2_ref, e2_ref = oracle.backward(x[:2], th, w.astype(np.float64), zm, xm)
+    assert_e_close(e2, e2_ref, n, L)
+    assert_grad_close(g2, g2_ref)
+    ctx.close()
