@@ -1297,46 +1297,6 @@ __device__ __forceinline__ V2<R> small_obs(const V2<R> *psi, uint32_t i, uint32_
     return mk2(re, im);
 }
 
-__device__ __forceinline__ uint32_t pair_index(uint32_t k, int q)
-{
-    return ((k >> q) << (q + 1)) | (k & ((1u << q) - 1u));
-}
-
-// X, Y, Z statistics S = Im<lambda|sigma_q|psi> of every qubit at the current point,
-// reduced over the workgroup (fp64 sum of 16 row partials), into a.stats[b][l][q][*].
-template <typename R>
-__device__ __forceinline__ void small_stats(const V2<R> *psi, const V2<R> *lam, const SmallArgs &a, int l, R *red)
-{
-    const int n = a.n, L = a.L;
-    const uint32_t N = 1u << n;
-    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    for (int q = 0; q < n; ++q) {
-        R sx = 0, sy = 0, sz = 0;
-        for (uint32_t k = tid; k < N / 2; k += kThreads) {
-            const uint32_t i = pair_index(k, q), j = i | (1u << q);
-            const V2<R> pi_ = psi[i], pj = psi[j], li = lam[i], lj = lam[j];
-            sx += li.x * pj.y - li.y * pj.x + lj.x * pi_.y - lj.y * pi_.x;
-            sy += lj.x * pi_.x + lj.y * pi_.y - li.x * pj.x - li.y * pj.y;
-            sz += (li.x * pi_.y - li.y * pi_.x) - (lj.x * pj.y - lj.y * pj.x);
-        }
-        sx = row_sum16(sx);
-        sy = row_sum16(sy);
-        sz = row_sum16(sz);
-        if ((lane & 15) == 15) {
-            const int r = w * 4 + (lane >> 4);
-            red[(q * 3 + 0) * 16 + r] = sx;
-            red[(q * 3 + 1) * 16 + r] = sy;
-            red[(q * 3 + 2) * 16 + r] = sz;
-        }
-    }
-    __syncthreads();
-    if (tid < 3 * n) {
-        double s = 0.0;
-        for (int k = 0; k < 16; ++k) s += (double)red[tid * 16 + k];
-        a.stats[(((size_t)b * L + l) * n) * 3 + tid] = s;
-    }
-}
-
 // ---- CNOT entangler (whole state in local memory)
 //
 // The chain CNOT(0,1), CNOT(1,2), ..., CNOT(n-2,n-1), applied in that order, sends basis
@@ -1354,29 +1314,6 @@ __device__ __forceinline__ uint32_t cnot_chain(uint32_t i, uint32_t mask)
 
 __device__ __forceinline__ uint32_t cnot_chain_inv(uint32_t j, uint32_t mask) { return (j ^ (j << 1)) & mask; }
 
-// In-place permutation of a state in local memory: INV = false applies the chain
-// (buf[j] <- buf[P^-1(j)]), INV = true its inverse (buf[i] <- buf[P(i)]).  Every thread
-// reads all its sources into registers before any thread writes.
-template <bool INV, typename R>
-__device__ __forceinline__ void small_permute(V2<R> *buf, uint32_t N)
-{
-    constexpr int kPer = (1 << kSmallMaxQubits) / kThreads;
-    const uint32_t mask = N - 1, tid = threadIdx.x;
-    V2<R> tmp[kPer];
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-        const uint32_t i = tid + (uint32_t)r * kThreads;
-        if (i < N) tmp[r] = buf[INV ? cnot_chain(i, mask) : cnot_chain_inv(i, mask)];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-        const uint32_t i = tid + (uint32_t)r * kThreads;
-        if (i < N) buf[i] = tmp[r];
-    }
-    __syncthreads();
-}
-
 // Factor of amplitude i in prod_q diag(f_q, conj f_q); f_q = (x, y) of wl[q] (SECOND =
 // false) or (z, w) (SECOND = true).
 template <bool SECOND, typename R>
@@ -1390,124 +1327,6 @@ __device__ __forceinline__ V2<R> small_phase(const V4<R> *wl, int n, uint32_t i)
         f = cmul(f, h);
     }
     return f;
-}
-
-// Real rotation layer Ry(beta_{l,q}) on every qubit (INV: its inverse) of one state;
-// cs[l][q] = (sin, cos) of beta/2.
-template <bool INV, typename R>
-__device__ __forceinline__ void small_ry_layer(V2<R> *st, const V2<R> *cs, int n, uint32_t N)
-{
-    for (int q = 0; q < n; ++q) {
-        const R s = INV ? -cs[q].x : cs[q].x, c = cs[q].y;
-        for (uint32_t k = threadIdx.x; k < N / 2; k += kThreads) {
-            const uint32_t i = pair_index(k, q), j = i | (1u << q);
-            const V2<R> x = st[i], y = st[j];
-            st[i] = mk2(c * x.x - s * y.x, c * x.y - s * y.y);
-            st[j] = mk2(s * x.x + c * y.x, s * x.y + c * y.y);
-        }
-        __syncthreads();
-    }
-}
-
-// Whole circuit of one sample with the CNOT entangler.  Per layer l the simulated
-// sequence is diag(r_l), Ry-layer l, diag(p_l), then the chain (U_{l,q} =
-// diag(p) Ry(beta) diag(r); layer 0 up to Ry is the product state init_u).  The
-// statistics are taken at P_l, just after Ry-layer l, as on the CZ path, so the same
-// gradient map applies (with no Pauli frame).  lambda at P_{L-1} is
-// D^dag P^dag O P D psi with D = diag(p_{L-1}):
-//   lambda_i = conj(D_i) c(P(i)) D_(i^x') psi_(i^x'),  x' = P^-1(xm),
-//   c(j) = i^(#Y) (-1)^|(j ^ xm) & zm|,
-// and E = Re <psi|lambda>.
-template <typename R>
-__device__ void small_cnot_circuit(const SmallArgs &a, V2<R> *psi, V2<R> *lam, R *red)
-{
-    const int n = a.n, L = a.L;
-    const uint32_t N = 1u << n, mask = N - 1;
-    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const V2<R> *rcs = reinterpret_cast<const V2<R> *>(a.rot_tf);
-    const V4<R> *dw = reinterpret_cast<const V4<R> *>(a.dw);
-    V2<R> *save = reinterpret_cast<V2<R> *>(a.psi_save) + (size_t)b * N;
-
-    if (a.mode != 1) {
-        const V4<R> *u = reinterpret_cast<const V4<R> *>(a.init_u) + (size_t)b * n;
-        for (uint32_t i = tid; i < N; i += kThreads) {
-            V2<R> v = mk2((R)1, (R)0);
-            for (int q = 0; q < n; ++q) {
-                const V4<R> f = u[q];
-                v = cmul(v, ((i >> q) & 1u) ? mk2(f.z, f.w) : mk2(f.x, f.y));
-            }
-            psi[i] = v;
-        }
-        __syncthreads();
-        for (int l = 0; l + 1 < L; ++l) {
-            const V4<R> *wl = dw + (size_t)l * n, *wn = wl + n;
-            for (uint32_t i = tid; i < N; i += kThreads) psi[i] = cmul(psi[i], small_phase<false, R>(wl, n, i));
-            __syncthreads();
-            small_permute<false, R>(psi, N);
-            for (uint32_t i = tid; i < N; i += kThreads) psi[i] = cmul(psi[i], small_phase<true, R>(wn, n, i));
-            __syncthreads();
-            small_ry_layer<false, R>(psi, rcs + (size_t)(l + 1) * n, n, N);
-        }
-    } else {
-        for (uint32_t i = tid; i < N; i += kThreads) psi[i] = save[i];
-        __syncthreads();
-    }
-
-    const V4<R> *wt = dw + (size_t)(L - 1) * n;
-    const uint32_t zm = a.obs, xm = a.obs_x, xs = cnot_chain_inv(xm, mask);
-    const int yph = __builtin_popcount(zm & xm) & 3;
-    R e = 0;
-    for (uint32_t i = tid; i < N; i += kThreads) {
-        const uint32_t j = i ^ xs;
-        V2<R> v = cmul(small_phase<false, R>(wt, n, j), psi[j]);
-        if (__builtin_popcount((cnot_chain(i, mask) ^ xm) & zm) & 1) v = mk2(-v.x, -v.y);
-        mul_ipow(v.x, v.y, yph);
-        V2<R> d = small_phase<false, R>(wt, n, i);
-        d.y = -d.y;
-        const V2<R> li = cmul(d, v);
-        lam[i] = li;
-        e += psi[i].x * li.x + psi[i].y * li.y;
-    }
-    if (a.mode != 1) {
-        e = row_sum16(e);
-        if ((lane & 15) == 15) red[w * 4 + (lane >> 4)] = e;
-        __syncthreads();
-        if (tid == 0) {
-            double s = 0.0;
-            for (int k = 0; k < 16; ++k) s += (double)red[k];
-            static_cast<R *>(a.e_out)[b] = (R)s;
-        }
-        if (a.mode == 0) {
-            for (uint32_t i = tid; i < N; i += kThreads) save[i] = psi[i];
-            return;
-        }
-    }
-    __syncthreads();
-
-    for (int l = L - 1; l >= 0; --l) {
-        small_stats<R>(psi, lam, a, l, red);
-        if (l == 0) break;
-        __syncthreads();
-        small_ry_layer<true, R>(psi, rcs + (size_t)l * n, n, N);
-        small_ry_layer<true, R>(lam, rcs + (size_t)l * n, n, N);
-        const V4<R> *wl = dw + (size_t)l * n, *wp = wl - n;
-        for (uint32_t i = tid; i < N; i += kThreads) {
-            V2<R> f = small_phase<true, R>(wl, n, i);
-            f.y = -f.y;
-            psi[i] = cmul(psi[i], f);
-            lam[i] = cmul(lam[i], f);
-        }
-        __syncthreads();
-        small_permute<true, R>(psi, N);
-        small_permute<true, R>(lam, N);
-        for (uint32_t i = tid; i < N; i += kThreads) {
-            V2<R> f = small_phase<false, R>(wp, n, i);
-            f.y = -f.y;
-            psi[i] = cmul(psi[i], f);
-            lam[i] = cmul(lam[i], f);
-        }
-        __syncthreads();
-    }
 }
 
 // ---- whole circuit per workgroup with the CZ chain: register rounds
@@ -1618,19 +1437,39 @@ __device__ __forceinline__ void bcast_low(V2<R> (&t)[1 << G], V2<R> tl)
     for (int j = 0; j < (1 << G); ++j) t[j] = mk2(lane_bcast<R>(tl.x, j), lane_bcast<R>(tl.y, j));
 }
 
-// Multiply a round-0 group by its diagonal D_j = T[j] * (h or hx), hx for j with bit G-1
-// set (the CZ between qubits G-1 and G).  CONJ: by conj(D).
-template <int G, bool CONJ, typename R>
+// Multiply a round-0 group by its diagonal D_j = T[j] * (h or hx).  SEL = 0: hx for j with
+// bit G-1 set (the CZ chain's CZ between qubits G-1 and G, or, through the CNOT chain's
+// inverse map, bit G of the source index); SEL = 1: hx for j of odd parity (every bit of
+// the CNOT chain's image above G flips with it).  CONJ: by conj(D).
+template <int G, bool CONJ, int SEL = 0, typename R>
 __device__ __forceinline__ void sg_diag(SmallGroup<G, R> &v, const V2<R> (&t)[1 << G], V2<R> h, V2<R> hx)
 {
 #pragma unroll
     for (int j = 0; j < (1 << G); ++j) {
-        V2<R> d = cmul(t[j], ((j >> (G - 1)) & 1) ? hx : h);
+        const bool x = SEL == 0 ? ((j >> (G - 1)) & 1) != 0 : (__builtin_popcount(j) & 1) != 0;
+        V2<R> d = cmul(t[j], x ? hx : h);
         if (CONJ) d.y = -d.y;
         const R re = v.re[j] * d.x - v.im[j] * d.y;
         const R im = v.re[j] * d.y + v.im[j] * d.x;
         v.re[j] = re;
         v.im[j] = im;
+    }
+}
+
+// Rotation Ry on register bit m of a group in (sin, cos) form (INV: its inverse).
+template <int G, bool INV, typename R>
+__device__ __forceinline__ void sg_rot_cs(SmallGroup<G, R> &v, int m, R sn, R cs)
+{
+    const R ss = INV ? -sn : sn;
+#pragma unroll
+    for (int j = 0; j < (1 << G); ++j) {
+        if ((j >> m) & 1) continue;
+        const int o = j | (1 << m);
+        const R ar = v.re[j], ai = v.im[j], br = v.re[o], bi = v.im[o];
+        v.re[j] = fmar(cs, ar, -ss * br);
+        v.im[j] = fmar(cs, ai, -ss * bi);
+        v.re[o] = fmar(ss, ar, cs * br);
+        v.im[o] = fmar(ss, ai, cs * bi);
     }
 }
 
@@ -1663,6 +1502,25 @@ __device__ __forceinline__ void sg_stats(const SmallGroup<G, R> &p, const SmallG
     sz += zp - zn;
 }
 
+// Row partials (16 per workgroup) of the statistics of qubits s .. s+G-1 into red.
+template <int G, typename R>
+__device__ __forceinline__ void round_stats_out(const R (&sx)[G], const R (&sy)[G], const R (&sz)[G], R corr, int s,
+                                                R *red)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+        R x = sx[m] * corr, y = sy[m] * corr, z = sz[m] * corr;
+        row_sum16x3(x, y, z);
+        if ((lane & 15) == 15) {
+            const int r = w * 4 + (lane >> 4), q = s + m;
+            red[(q * 3 + 0) * 16 + r] = x;
+            red[(q * 3 + 1) * 16 + r] = y;
+            red[(q * 3 + 2) * 16 + r] = z;
+        }
+    }
+}
+
 struct SmallRound {
     int s, G;          // qubits s .. s+G-1
     uint32_t groups;   // 2^(n - G)
@@ -1675,15 +1533,19 @@ __device__ __forceinline__ uint32_t sg_base(uint32_t g, int s, int G)
 
 // Forward round: [round 0: init from the product-state factors (INIT) or multiply by
 // scale * D], rotations of the round's qubits with layer lr's coefficients (lr < 0:
-// none), [LAST: multiply by fin].
-template <int G, typename R>
+// none; CS: (sin, cos) form, else tangent form), [LAST: multiply by fin].
+template <int G, typename R, bool CS>
 __device__ __forceinline__ void small_fwd_round(V2<R> *psi, const SmallArgs &a, SmallRound rd, int lr, bool init,
                                                 bool diag, const V4<R> *f, V2<R> tl, R scale, bool last, R fin)
 {
     const V2<R> *rtf = reinterpret_cast<const V2<R> *>(a.rot_tf);
-    R k[G];
+    R k[G], c[G];
 #pragma unroll
-    for (int m = 0; m < G; ++m) k[m] = lr >= 0 ? rtf[(size_t)lr * a.n + rd.s + m].x : (R)0;
+    for (int m = 0; m < G; ++m) {
+        const V2<R> kf = lr >= 0 ? rtf[(size_t)lr * a.n + rd.s + m] : mk2((R)0, (R)1);
+        k[m] = kf.x;
+        c[m] = kf.y;
+    }
     V2<R> t[1 << G];
     bcast_low<G, R>(t, tl);
     for (uint32_t g = threadIdx.x; g < rd.groups; g += kThreads) {
@@ -1708,7 +1570,12 @@ __device__ __forceinline__ void small_fwd_round(V2<R> *psi, const SmallArgs &a, 
         }
         if (lr >= 0) {
 #pragma unroll
-            for (int m = 0; m < G; ++m) sg_rot<G, false>(v, m, k[m]);
+            for (int m = 0; m < G; ++m) {
+                if constexpr (CS)
+                    sg_rot_cs<G, false>(v, m, k[m], c[m]);
+                else
+                    sg_rot<G, false>(v, m, k[m]);
+            }
         }
         if (last) {
 #pragma unroll
@@ -1724,16 +1591,18 @@ __device__ __forceinline__ void small_fwd_round(V2<R> *psi, const SmallArgs &a, 
 // Adjoint round at layer l: [round 0 and D: multiply psi and lambda by scale * conj(D)],
 // statistics of the round's qubits (scaled by corr) into red, then, if urot, the inverse
 // rotations of layer l on both states; the groups are written back if anything changed.
-template <int G, typename R>
+template <int G, typename R, bool CS>
 __device__ __forceinline__ void small_adj_round(V2<R> *psi, V2<R> *lam, const SmallArgs &a, SmallRound rd, int l,
                                                 bool diag, const V4<R> *f, V2<R> tl, R scale, R corr, bool urot,
                                                 R *red)
 {
     const V2<R> *rtf = reinterpret_cast<const V2<R> *>(a.rot_tf);
-    R k[G], sx[G], sy[G], sz[G];
+    R k[G], c[G], sx[G], sy[G], sz[G];
 #pragma unroll
     for (int m = 0; m < G; ++m) {
-        k[m] = rtf[(size_t)l * a.n + rd.s + m].x;
+        const V2<R> kf = rtf[(size_t)l * a.n + rd.s + m];
+        k[m] = kf.x;
+        c[m] = kf.y;
         sx[m] = sy[m] = sz[m] = (R)0;
     }
     V2<R> t[1 << G];
@@ -1755,8 +1624,13 @@ __device__ __forceinline__ void small_adj_round(V2<R> *psi, V2<R> *lam, const Sm
         if (urot) {
 #pragma unroll
             for (int m = 0; m < G; ++m) {
-                sg_rot<G, true>(p, m, k[m]);
-                sg_rot<G, true>(q, m, k[m]);
+                if constexpr (CS) {
+                    sg_rot_cs<G, true>(p, m, k[m], c[m]);
+                    sg_rot_cs<G, true>(q, m, k[m], c[m]);
+                } else {
+                    sg_rot<G, true>(p, m, k[m]);
+                    sg_rot<G, true>(q, m, k[m]);
+                }
             }
         }
         if (urot || diag) {   // at l = 0 the later rounds still need D_0^dagger applied
@@ -1764,18 +1638,7 @@ __device__ __forceinline__ void small_adj_round(V2<R> *psi, V2<R> *lam, const Sm
             sg_store<G>(q, lam, base, rd.s);
         }
     }
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-    for (int m = 0; m < G; ++m) {
-        R x = sx[m] * corr, y = sy[m] * corr, z = sz[m] * corr;
-        row_sum16x3(x, y, z);
-        if ((lane & 15) == 15) {
-            const int r = w * 4 + (lane >> 4), q = rd.s + m;
-            red[(q * 3 + 0) * 16 + r] = x;
-            red[(q * 3 + 1) * 16 + r] = y;
-            red[(q * 3 + 2) * 16 + r] = z;
-        }
-    }
+    round_stats_out<G>(sx, sy, sz, corr, rd.s, red);
 }
 
 __device__ __forceinline__ SmallRound small_round(int n, int r)
@@ -1787,28 +1650,320 @@ __device__ __forceinline__ SmallRound small_round(int n, int r)
     return rd;
 }
 
-template <typename R>
+template <typename R, bool CS = false>
 __device__ __forceinline__ void small_fwd_round_g(V2<R> *psi, const SmallArgs &a, SmallRound rd, int lr, bool init,
                                                   bool diag, const V4<R> *f, V2<R> tl, R scale, bool last, R fin)
 {
     switch (rd.G) {
-    case 1: small_fwd_round<1, R>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
-    case 2: small_fwd_round<2, R>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
-    case 3: small_fwd_round<3, R>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
-    default: small_fwd_round<4, R>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
+    case 1: small_fwd_round<1, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
+    case 2: small_fwd_round<2, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
+    case 3: small_fwd_round<3, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
+    default: small_fwd_round<4, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
     }
 }
 
-template <typename R>
+template <typename R, bool CS = false>
 __device__ __forceinline__ void small_adj_round_g(V2<R> *psi, V2<R> *lam, const SmallArgs &a, SmallRound rd, int l,
                                                   bool diag, const V4<R> *f, V2<R> tl, R scale, R corr, bool urot,
                                                   R *red)
 {
     switch (rd.G) {
-    case 1: small_adj_round<1, R>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
-    case 2: small_adj_round<2, R>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
-    case 3: small_adj_round<3, R>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
-    default: small_adj_round<4, R>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
+    case 1: small_adj_round<1, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
+    case 2: small_adj_round<2, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
+    case 3: small_adj_round<3, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
+    default: small_adj_round<4, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
+    }
+}
+
+// ---- whole circuit per workgroup with the CNOT chain: the same register rounds
+//
+// Per layer l the simulated sequence is diag(r_l), Ry-layer l, diag(p_l), then the chain P
+// (bit k of P(i) = parity of bits 0..k of i; P^-1(j) = j ^ (j << 1)); layer 0 up to Ry is
+// the product state.  The statistics are taken at P_l, just after Ry-layer l.  A forward
+// step l -> l+1 gathers in round 0 amplitude J of the new state from i = P^-1(J), times
+// p_l(i) r_{l+1}(J); an adjoint step back to P_l gathers amplitude i from P(i), times
+// conj(r_{l+1}(P(i)) p_l(i)).  Both factors split into T[j] over qubits 0..G-1 (uniform)
+// and a per-group factor with two variants: in the forward, bit G of i also depends on
+// bit G-1 of j; in the adjoint, every bit of P(i) from G up flips with the parity of j.
+// A gather reads all sources of a thread's groups before the workgroup barrier and writes
+// after it, so it runs in place: at most two groups per thread (2^(n-4) <= 512 for n <= 13;
+// fp64 compute is limited to n <= 12 by the host, so one).  The rotations
+// use the (sin, cos) form: these tables carry no Pauli frame.
+
+template <typename R>
+constexpr int kGatherGroups = sizeof(R) == 4 ? 2 : 1;
+
+// Factor diag(h, conj h) of qubit q at bit value b; h = (x, y) of f[q], or (z, w) (SECOND).
+template <bool SECOND, typename R>
+__device__ __forceinline__ V2<R> cphase(const V4<R> *f, int q, uint32_t b)
+{
+    const V4<R> g = f[q];
+    const R im = SECOND ? g.w : g.y;
+    return mk2(SECOND ? g.z : g.x, b ? -im : im);
+}
+
+// T[j] (j = lane & 15) of a forward step l -> l+1: p_l (wl) over the low bits of
+// P^-1(j) times r_{l+1} (wn) over the bits of j.
+template <typename R>
+__device__ __forceinline__ V2<R> cnot_low_fwd(const V4<R> *wl, const V4<R> *wn, int G, int lane)
+{
+    const uint32_t j = (uint32_t)lane & 15u, ji = (j ^ (j << 1)) & ((1u << G) - 1u);
+    V2<R> t = mk2((R)1, (R)0);
+    for (int q = 0; q < G; ++q) {
+        t = cmul(t, cphase<false, R>(wl, q, (ji >> q) & 1u));
+        t = cmul(t, cphase<true, R>(wn, q, (j >> q) & 1u));
+    }
+    return t;
+}
+
+// T[j] of an adjoint step back to P_l: conj(r_{l+1} over the low bits of P(j) times p_l
+// over the bits of j).
+template <typename R>
+__device__ __forceinline__ V2<R> cnot_low_adj(const V4<R> *wl, const V4<R> *wn, int G, int lane)
+{
+    const uint32_t lm = (1u << G) - 1u, j = (uint32_t)lane & lm & 15u, jp = cnot_chain(j, lm);
+    V2<R> t = mk2((R)1, (R)0);
+    for (int q = 0; q < G; ++q) {
+        t = cmul(t, cphase<true, R>(wn, q, (jp >> q) & 1u));
+        t = cmul(t, cphase<false, R>(wl, q, (j >> q) & 1u));
+    }
+    return mk2(t.x, -t.y);
+}
+
+// Round 0 of a forward step l -> l+1 (G = qubits of round 0): gather through P^-1 with
+// the two diagonals, then Ry-layer l+1 on qubits 0..G-1.
+template <int G, typename R>
+__device__ __forceinline__ void cnot_fwd_gather(V2<R> *psi, const SmallArgs &a, int l, V2<R> tl)
+{
+    const int n = a.n;
+    const uint32_t groups = (1u << n) >> G, hmask = groups - 1u, lmask = (1u << G) - 1u;
+    const V4<R> *wl = reinterpret_cast<const V4<R> *>(a.dw) + (size_t)l * n, *wn = wl + n;
+    const V2<R> *rcs = reinterpret_cast<const V2<R> *>(a.rot_tf) + (size_t)(l + 1) * n;
+    V2<R> t[1 << G];
+    bcast_low<G, R>(t, tl);
+    constexpr int KG = kGatherGroups<R>;
+    SmallGroup<G, R> v[KG];
+    V2<R> h[KG], hx[KG];
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+        const uint32_t g = threadIdx.x + (uint32_t)k * kThreads;
+        if (g >= groups) continue;
+        // high bits of the source index i = P^-1((g << G) | j): (g ^ (g << 1)), with bit 0
+        // flipped when bit G-1 of j is set
+        const uint32_t ih0 = (g ^ (g << 1)) & hmask, ih1 = ih0 ^ (hmask & 1u);
+        V2<R> hr = mk2((R)1, (R)0), hp0 = hr, hp1 = hr;
+        for (int q = G; q < n; ++q) {
+            hr = cmul(hr, cphase<true, R>(wn, q, (g >> (q - G)) & 1u));
+            hp0 = cmul(hp0, cphase<false, R>(wl, q, (ih0 >> (q - G)) & 1u));
+            hp1 = cmul(hp1, cphase<false, R>(wl, q, (ih1 >> (q - G)) & 1u));
+        }
+        h[k] = cmul(hp0, hr);
+        hx[k] = cmul(hp1, hr);
+#pragma unroll
+        for (int j = 0; j < (1 << G); ++j) {
+            const uint32_t hi = ((j >> (G - 1)) & 1) ? ih1 : ih0;
+            const V2<R> x = psi[sslot((hi << G) | (((uint32_t)j ^ ((uint32_t)j << 1)) & lmask))];
+            v[k].re[j] = x.x;
+            v[k].im[j] = x.y;
+        }
+    }
+    __syncthreads();   // every source read before any amplitude is overwritten
+    R sn[G], cs[G];
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+        sn[m] = rcs[m].x;
+        cs[m] = rcs[m].y;
+    }
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+        const uint32_t g = threadIdx.x + (uint32_t)k * kThreads;
+        if (g >= groups) continue;
+        sg_diag<G, false, 0>(v[k], t, h[k], hx[k]);
+#pragma unroll
+        for (int m = 0; m < G; ++m) sg_rot_cs<G, false>(v[k], m, sn[m], cs[m]);
+        sg_store<G>(v[k], psi, g << G, 0);
+    }
+}
+
+// Round 0 of an adjoint step back to P_l: gather psi and lambda through P with the
+// conjugate diagonals, the statistics of qubits 0..G-1 at P_l, then (urot) the inverse
+// rotations of Ry-layer l.
+template <int G, typename R>
+__device__ __forceinline__ void cnot_adj_gather(V2<R> *psi, V2<R> *lam, const SmallArgs &a, int l, V2<R> tl,
+                                                bool urot, R *red)
+{
+    const int n = a.n;
+    const uint32_t groups = (1u << n) >> G, hmask = groups - 1u, lmask = (1u << G) - 1u;
+    const V4<R> *wl = reinterpret_cast<const V4<R> *>(a.dw) + (size_t)l * n, *wn = wl + n;
+    const V2<R> *rcs = reinterpret_cast<const V2<R> *>(a.rot_tf) + (size_t)l * n;
+    V2<R> t[1 << G];
+    bcast_low<G, R>(t, tl);
+    constexpr int KG = kGatherGroups<R>;
+    SmallGroup<G, R> p[KG], q[KG];
+    V2<R> h[KG], hx[KG];
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+        const uint32_t g = threadIdx.x + (uint32_t)k * kThreads;
+        if (g >= groups) continue;
+        // high bits of P((g << G) | j): the prefix parities of g, all flipped for odd j
+        const uint32_t pb0 = cnot_chain(g, hmask), pb1 = pb0 ^ hmask;
+        V2<R> hp = mk2((R)1, (R)0), hr0 = hp, hr1 = hp;
+        for (int qq = G; qq < n; ++qq) {
+            hp = cmul(hp, cphase<false, R>(wl, qq, (g >> (qq - G)) & 1u));
+            hr0 = cmul(hr0, cphase<true, R>(wn, qq, (pb0 >> (qq - G)) & 1u));
+            hr1 = cmul(hr1, cphase<true, R>(wn, qq, (pb1 >> (qq - G)) & 1u));
+        }
+        const V2<R> d0 = cmul(hp, hr0), d1 = cmul(hp, hr1);
+        h[k] = mk2(d0.x, -d0.y);
+        hx[k] = mk2(d1.x, -d1.y);
+#pragma unroll
+        for (int j = 0; j < (1 << G); ++j) {
+            const uint32_t hi = (__builtin_popcount(j) & 1) ? pb1 : pb0;
+            const uint32_t src = sslot((hi << G) | cnot_chain((uint32_t)j, lmask));
+            const V2<R> x = psi[src], y = lam[src];
+            p[k].re[j] = x.x;
+            p[k].im[j] = x.y;
+            q[k].re[j] = y.x;
+            q[k].im[j] = y.y;
+        }
+    }
+    __syncthreads();   // every source read before any amplitude is overwritten
+    R sn[G], cs[G], sx[G], sy[G], sz[G];
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+        sn[m] = rcs[m].x;
+        cs[m] = rcs[m].y;
+        sx[m] = sy[m] = sz[m] = (R)0;
+    }
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+        const uint32_t g = threadIdx.x + (uint32_t)k * kThreads;
+        if (g >= groups) continue;
+        sg_diag<G, false, 1>(p[k], t, h[k], hx[k]);
+        sg_diag<G, false, 1>(q[k], t, h[k], hx[k]);
+#pragma unroll
+        for (int m = 0; m < G; ++m) sg_stats<G>(p[k], q[k], m, sx[m], sy[m], sz[m]);
+        if (urot) {
+#pragma unroll
+            for (int m = 0; m < G; ++m) {
+                sg_rot_cs<G, true>(p[k], m, sn[m], cs[m]);
+                sg_rot_cs<G, true>(q[k], m, sn[m], cs[m]);
+            }
+        }
+        sg_store<G>(p[k], psi, g << G, 0);
+        sg_store<G>(q[k], lam, g << G, 0);
+    }
+    round_stats_out<G>(sx, sy, sz, (R)1, 0, red);
+}
+
+template <typename R>
+__device__ __forceinline__ void cnot_fwd_gather_g(V2<R> *psi, const SmallArgs &a, int G, int l, V2<R> tl)
+{
+    switch (G) {
+    case 1: cnot_fwd_gather<1, R>(psi, a, l, tl); break;
+    case 2: cnot_fwd_gather<2, R>(psi, a, l, tl); break;
+    case 3: cnot_fwd_gather<3, R>(psi, a, l, tl); break;
+    default: cnot_fwd_gather<4, R>(psi, a, l, tl); break;
+    }
+}
+
+template <typename R>
+__device__ __forceinline__ void cnot_adj_gather_g(V2<R> *psi, V2<R> *lam, const SmallArgs &a, int G, int l,
+                                                  V2<R> tl, bool urot, R *red)
+{
+    switch (G) {
+    case 1: cnot_adj_gather<1, R>(psi, lam, a, l, tl, urot, red); break;
+    case 2: cnot_adj_gather<2, R>(psi, lam, a, l, tl, urot, red); break;
+    case 3: cnot_adj_gather<3, R>(psi, lam, a, l, tl, urot, red); break;
+    default: cnot_adj_gather<4, R>(psi, lam, a, l, tl, urot, red); break;
+    }
+}
+
+// Whole circuit of one sample with the CNOT entangler.  lambda at P_{L-1} is
+// D^dag P^dag O P D psi with D = diag(p_{L-1}):
+//   lambda_i = conj(D_i) c(P(i)) D_(i^x') psi_(i^x'),  x' = P^-1(xm),
+//   c(j) = i^(#Y) (-1)^|(j ^ xm) & zm|,
+// and E = Re <psi|lambda>.
+template <typename R>
+__device__ void small_cnot_rounds(const SmallArgs &a, V2<R> *psi, V2<R> *lam, R *red)
+{
+    const int n = a.n, L = a.L;
+    const uint32_t N = 1u << n, mask = N - 1;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const V4<R> *dw = reinterpret_cast<const V4<R> *>(a.dw);
+    V2<R> *save = reinterpret_cast<V2<R> *>(a.psi_save) + (size_t)b * N;
+    const int G0 = n < 4 ? n : 4;
+    const int nr = (n + 3) / 4;
+    const V2<R> one = mk2((R)1, (R)0);
+
+    if (a.mode != 1) {
+        const V4<R> *u = reinterpret_cast<const V4<R> *>(a.init_u) + (size_t)b * n;
+        small_fwd_round_g<R>(psi, a, small_round(n, 0), -1, true, false, u, low_factor<R>(u, G0, false, lane), (R)1,
+                             false, (R)1);
+        __syncthreads();
+        for (int l = 0; l + 1 < L; ++l) {
+            const V4<R> *wl = dw + (size_t)l * n;
+            cnot_fwd_gather_g<R>(psi, a, G0, l, cnot_low_fwd<R>(wl, wl + n, G0, lane));
+            __syncthreads();
+            for (int r = 1; r < nr; ++r) {
+                small_fwd_round_g<R, true>(psi, a, small_round(n, r), l + 1, false, false, wl, one, (R)1, false,
+                                           (R)1);
+                __syncthreads();
+            }
+        }
+    } else {
+        for (uint32_t i = tid; i < N; i += kThreads) psi[sslot(i)] = save[i];
+        __syncthreads();
+    }
+
+    const V4<R> *wt = dw + (size_t)(L - 1) * n;
+    const uint32_t zm = a.obs, xm = a.obs_x, xs = cnot_chain_inv(xm, mask);
+    const int yph = __builtin_popcount(zm & xm) & 3;
+    R e = 0;
+    for (uint32_t i = tid; i < N; i += kThreads) {
+        const uint32_t j = i ^ xs;
+        V2<R> v = cmul(small_phase<false, R>(wt, n, j), psi[sslot(j)]);
+        if (__builtin_popcount((cnot_chain(i, mask) ^ xm) & zm) & 1) v = mk2(-v.x, -v.y);
+        mul_ipow(v.x, v.y, yph);
+        V2<R> d = small_phase<false, R>(wt, n, i);
+        d.y = -d.y;
+        const V2<R> li = cmul(d, v), pi = psi[sslot(i)];
+        lam[sslot(i)] = li;
+        e += pi.x * li.x + pi.y * li.y;
+    }
+    if (a.mode != 1) {
+        e = row_sum16(e);
+        if ((lane & 15) == 15) red[w * 4 + (lane >> 4)] = e;
+        __syncthreads();
+        if (tid == 0) {
+            double s = 0.0;
+            for (int k = 0; k < 16; ++k) s += (double)red[k];
+            static_cast<R *>(a.e_out)[b] = (R)s;
+        }
+        if (a.mode == 0) {
+            for (uint32_t i = tid; i < N; i += kThreads) save[i] = psi[sslot(i)];
+            return;
+        }
+    }
+    __syncthreads();
+
+    for (int l = L - 1; l >= 0; --l) {
+        R *rl = red + (l & 1) * (3 * kSmallMaxQubits * 16);
+        const V4<R> *wl = dw + (size_t)l * n;
+        if (l + 1 < L)
+            cnot_adj_gather_g<R>(psi, lam, a, G0, l, cnot_low_adj<R>(wl, wl + n, G0, lane), l > 0, rl);
+        else
+            small_adj_round_g<R, true>(psi, lam, a, small_round(n, 0), l, false, wl, one, (R)1, (R)1, l > 0, rl);
+        __syncthreads();
+        for (int r = 1; r < nr; ++r) {
+            small_adj_round_g<R, true>(psi, lam, a, small_round(n, r), l, false, wl, one, (R)1, (R)1, l > 0, rl);
+            __syncthreads();
+        }
+        if (tid < 3 * n) {
+            double s = 0.0;
+            for (int k = 0; k < 16; ++k) s += (double)rl[tid * 16 + k];
+            a.stats[(((size_t)b * L + l) * n) * 3 + tid] = s;
+        }
     }
 }
 
@@ -1828,7 +1983,7 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
     const V4<R> *dw = reinterpret_cast<const V4<R> *>(a.dw);
     V2<R> *save = reinterpret_cast<V2<R> *>(a.psi_save) + (size_t)b * N;
     if constexpr (ENT != 0) {
-        small_cnot_circuit<R>(a, psi, lam, red);
+        small_cnot_rounds<R>(a, psi, lam, red);
         return;
     }
 

@@ -1,8 +1,8 @@
 """CNOT-chain entangler on the GPU vs the oracle (entangler=1).
 
 Every layer ends with CNOT(q, q+1), control q, for q = 0..n-2 in that order.  The
-whole-circuit kernel (n <= 13) applies the chain as a permutation of the amplitude
-indices in local memory; the tile path (n >= 14) runs one pass per view and layer, the
+whole-circuit kernel (n <= 13) applies the chain as a gather of the amplitude indices in
+local memory (round 0 of each step); the tile path (n >= 14) runs one pass per view and layer, the
 first reading its input through the chain's index map and its adjoint writing lambda
 back through it; the gate-by-gate comparator runs one kernel per CNOT at any width.
 Tolerances as for the CZ chain: <O> within 1e-5 relative to max(|E|, 2^(-n/2)),
@@ -107,6 +107,27 @@ def test_cnot_hea12q20l_full():
     assert abs(float(loss[0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
     assert_grad_close(g, g_ref)
 
+
+
+@pytest.mark.parametrize("L", [1, 4])
+@pytest.mark.parametrize("n", list(range(1, 14)))
+def test_cnot_whole_circuit_every_width(n, L):
+    """Every width 1..13: the gather of round 0 covers qubits 0..min(n, 4)-1 and its
+    high part the rest (none for n <= 4; two groups per thread at n = 13); ragged batch
+    on one context; an X/Y string on odd widths."""
+    zm, xm = (1, 0) if n % 2 == 0 or n == 1 else ((1 << (n - 1)) | 1, (1 << (n - 1)) | (1 << (n // 2)))
+    maxB = 3
+    x, th, y = hqml_inputs.make_inputs(n, L, maxB, seed=3500 + 13 * n + L)
+    say(f"[gpu] CNOT whole circuit every width n={n} L={L}")
+    ctx = _ctx(n, L, maxB, zm, xm)
+    for B in (maxB, 2):
+        X, TH, Y = (torch.from_numpy(a) for a in (x[:B], th, y[:B]))
+        e, loss, g = (t.cpu().numpy() for t in ctx.train_step(X, TH, Y))
+        e_ref, loss_ref, g_ref = oracle.train_step(x[:B], th, y[:B], zm, xm, entangler=1)
+        assert_e_close(e, e_ref, n, L)
+        assert abs(float(loss[0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
+        assert_grad_close(g, g_ref)
+    ctx.close()
 
 @pytest.mark.parametrize("n,L,B,zm,xm", [(2, 2, 3, 0, 0), (5, 2, 2, 0b10010, 0b00101), (13, 2, 2, 0, 0),
                                          (14, 2, 2, 0, 0), (17, 2, 2, 1 << 16, 1 << 2)])
