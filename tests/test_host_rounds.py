@@ -1,0 +1,103 @@
+"""Host checks of the index algebra of the whole-circuit kernel (n <= 13).
+
+The kernel keeps a sample's state in LDS at slot sslot(i) = i ^ ((i >> 4) & 31) and
+works in rounds: a round on qubits s .. s+G-1 gives thread g (consecutive lanes =
+consecutive g) the amplitudes base(g) | (j << s).  With the CNOT chain, round 0 of a
+forward step reads amplitude J from P^-1(J) and round 0 of an adjoint step reads
+amplitude i from P(i) (bit k of P(i) = parity of bits 0..k of i), with the source index
+assembled from a per-group high part and a per-j low part.  These tests restate those
+formulas in Python and check them exhaustively against their definitions: the slot map
+is a bijection with no LDS bank conflicts in any round shape, and the assembled sources
+are exactly P^-1(J) and P(i).
+"""
+import numpy as np
+import pytest
+
+
+def sslot(i):
+    return i ^ ((i >> 4) & 31)
+
+
+def rounds(n):
+    out, s = [], 0
+    while s < n:
+        G = min(4, n - s)
+        out.append((s, G))
+        s += G
+    return out
+
+
+def base(g, s, G):
+    return ((g >> s) << (s + G)) | (g & ((1 << s) - 1))
+
+
+def chain(i, n):
+    """P(i): bit k = parity of bits 0..k of i."""
+    out, par = 0, 0
+    for k in range(n):
+        par ^= (i >> k) & 1
+        out |= par << k
+    return out
+
+
+def chain_inv(j, n):
+    return (j ^ (j << 1)) & ((1 << n) - 1)
+
+
+@pytest.mark.parametrize("n", range(1, 14))
+def test_slot_map_is_a_bijection(n):
+    N = 1 << n
+    slots = sslot(np.arange(N))
+    assert slots.max() < N
+    assert len(np.unique(slots)) == N
+
+
+@pytest.mark.parametrize("n", [9, 12, 13])
+def test_rounds_cover_every_amplitude_once(n):
+    N = 1 << n
+    for s, G in rounds(n):
+        seen = np.zeros(N, dtype=int)
+        for g in range(N >> G):
+            for j in range(1 << G):
+                seen[base(g, s, G) | (j << s)] += 1
+        assert (seen == 1).all()
+
+
+@pytest.mark.parametrize("n", range(1, 14))
+def test_rounds_are_bank_conflict_free(n):
+    """For every round, amplitude j and block of 32 consecutive threads, the 8-byte slots
+    read or written are distinct modulo 32 slots (256 bytes = the 64 four-byte banks)."""
+    for s, G in rounds(n):
+        groups = (1 << n) >> G
+        for j in range(1 << G):
+            for start in range(0, groups, 32):
+                gs = range(start, min(start + 32, groups))
+                banks = {sslot(base(g, s, G) | (j << s)) % 32 for g in gs}
+                assert len(banks) == len(gs), (n, s, G, j, start)
+
+
+@pytest.mark.parametrize("n", range(1, 14))
+def test_cnot_forward_gather_source_is_the_inverse_chain(n):
+    G = min(4, n)
+    hmask, lmask = (1 << (n - G)) - 1, (1 << G) - 1
+    for g in range(1 << (n - G)):
+        ih0 = (g ^ (g << 1)) & hmask
+        ih1 = ih0 ^ (hmask & 1)
+        for j in range(1 << G):
+            hi = ih1 if (j >> (G - 1)) & 1 else ih0
+            src = (hi << G) | ((j ^ (j << 1)) & lmask)
+            assert src == chain_inv((g << G) | j, n)
+
+
+@pytest.mark.parametrize("n", range(1, 14))
+def test_cnot_adjoint_gather_source_is_the_chain(n):
+    G = min(4, n)
+    hmask, lmask = (1 << (n - G)) - 1, (1 << G) - 1
+    for g in range(1 << (n - G)):
+        pb0 = chain(g, n - G)
+        pb1 = pb0 ^ hmask
+        for j in range(1 << G):
+            hi = pb1 if bin(j).count("1") & 1 else pb0
+            src = (hi << G) | chain(j, G)
+            assert src == chain((g << G) | j, n)
+            assert chain_inv(src, n) == (g << G) | j
