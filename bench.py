@@ -43,7 +43,7 @@ L2_POSITIONS = (0, 1, 9, 10, 11)
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("hqml_kernels.hip", "hqml_internal.hpp"):
+    for f in ("hqml_kernels.hip", "hqml_device.hpp", "hqml_internal.hpp"):   # what the tile kernels are built from
         with open(os.path.join(ROOT, "qml_gradients_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libhqml.so")
-SOURCES = ["hqml_kernels.hip", "hqml_gbg.hip", "hqml_abi.cpp", "hqml_plan.cpp"]
+SOURCES = ["hqml_kernels.hip", "hqml_small.hip", "hqml_gbg.hip", "hqml_abi.cpp", "hqml_plan.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("HQML_OFFLOAD_ARCH", "gfx950")
 
