@@ -15,13 +15,24 @@ namespace hqml {
 
 // ------------------------------------------------------------------ small circuits (n <= 13)
 
+// Table entry (factor for bit value 0 in x, y; for 1 in z, w) as a uniform value held in
+// scalar registers.  Without the pin the compiler may turn a per-lane choice between the
+// two factors into a per-lane load address: one vector load, waited on, per use.
+template <typename R>
+__device__ __forceinline__ V4<R> uniform_v4(const V4<R> *p)
+{
+    V4<R> f = ldu4(reinterpret_cast<const R *>(p));
+    asm volatile("" : "+s"(f.x), "+s"(f.y), "+s"(f.z), "+s"(f.w));
+    return f;
+}
+
 // D_l of amplitude i: CZ-chain sign times the per-qubit factors f0 / f1.
 template <typename R>
 __device__ __forceinline__ V2<R> small_diag(const V4<R> *wl, int n, uint32_t i)
 {
     V2<R> f = mk2((R)1, (R)0);
     for (int q = 0; q < n; ++q) {
-        const V4<R> g = wl[q];
+        const V4<R> g = uniform_v4<R>(wl + q);
         f = cmul(f, ((i >> q) & 1u) ? mk2(g.z, g.w) : mk2(g.x, g.y));
     }
     if (__builtin_popcount(i & (i >> 1)) & 1) {
@@ -76,7 +87,7 @@ __device__ __forceinline__ V2<R> small_phase(const V4<R> *wl, int n, uint32_t i)
 {
     V2<R> f = mk2((R)1, (R)0);
     for (int q = 0; q < n; ++q) {
-        const V4<R> g = wl[q];
+        const V4<R> g = uniform_v4<R>(wl + q);
         V2<R> h = SECOND ? mk2(g.z, g.w) : mk2(g.x, g.y);
         if ((i >> q) & 1u) h.y = -h.y;
         f = cmul(f, h);
@@ -121,7 +132,7 @@ __device__ __forceinline__ V2<R> low_factor(const V4<R> *f, int G0, bool cz, int
     const uint32_t j = (uint32_t)lane & 15u;
     V2<R> t = mk2((R)1, (R)0);
     for (int q = 0; q < G0; ++q) {
-        const V4<R> g = f[q];
+        const V4<R> g = uniform_v4<R>(f + q);
         t = cmul(t, ((j >> q) & 1u) ? mk2(g.z, g.w) : mk2(g.x, g.y));
     }
     if (cz && (__builtin_popcount(j & (j >> 1) & ((1u << G0) - 1u)) & 1)) t = mk2(-t.x, -t.y);
@@ -130,12 +141,12 @@ __device__ __forceinline__ V2<R> low_factor(const V4<R> *f, int G0, bool cz, int
 
 // Factor of the high qubits of group g of round 0: prod_{q >= G0} f_q(bit q - G0 of g),
 // with the CZ signs among them if cz.
-template <typename R>
-__device__ __forceinline__ V2<R> high_factor(const V4<R> *f, int G0, int n, uint32_t g, bool cz)
+template <int G0, typename R>
+__device__ __forceinline__ V2<R> high_factor(const V4<R> *f, int n, uint32_t g, bool cz)
 {
     V2<R> h = mk2((R)1, (R)0);
     for (int q = G0; q < n; ++q) {
-        const V4<R> w = f[q];
+        const V4<R> w = uniform_v4<R>(f + q);
         h = cmul(h, ((g >> (q - G0)) & 1u) ? mk2(w.z, w.w) : mk2(w.x, w.y));
     }
     if (cz && (__builtin_popcount(g & (g >> 1)) & 1)) h = mk2(-h.x, -h.y);
@@ -288,26 +299,32 @@ __device__ __forceinline__ uint32_t sg_base(uint32_t g, int s, int G)
 
 // Forward round: [round 0: init from the product-state factors (INIT) or multiply by
 // scale * D], rotations of the round's qubits with layer lr's coefficients (lr < 0:
-// none; CS: (sin, cos) form, else tangent form), [LAST: multiply by fin].
+// none; CS: (sin, cos) form, else tangent form), [LAST: multiply by fin times this
+// round's own scale].  Returns the product of the scales of its tangent-form rotations
+// (1 in the (sin, cos) form), so the caller needs no second read of the table.
 template <int G, typename R, bool CS>
-__device__ __forceinline__ void small_fwd_round(V2<R> *psi, const SmallArgs &a, SmallRound rd, int lr, bool init,
+__device__ __forceinline__ R small_fwd_round(V2<R> *psi, const SmallArgs &a, SmallRound rd, int lr, bool init,
                                                 bool diag, const V4<R> *f, V2<R> tl, R scale, bool last, R fin)
 {
     const V2<R> *rtf = reinterpret_cast<const V2<R> *>(a.rot_tf);
     R k[G], c[G];
 #pragma unroll
     for (int m = 0; m < G; ++m) {
-        const V2<R> kf = lr >= 0 ? rtf[(size_t)lr * a.n + rd.s + m] : mk2((R)0, (R)1);
+        const V2<R> kf = lr >= 0 ? ldu2(reinterpret_cast<const R *>(rtf + (size_t)lr * a.n + rd.s + m)) : mk2((R)0, (R)1);
         k[m] = kf.x;
         c[m] = kf.y;
     }
+    R own = 1;
+#pragma unroll
+    for (int m = 0; m < G; ++m) own *= (CS || lr < 0) ? (R)1 : c[m];
+    fin *= own;
     V2<R> t[1 << G];
     bcast_low<G, R>(t, tl);
     for (uint32_t g = threadIdx.x; g < rd.groups; g += kThreads) {
         const uint32_t base = sg_base(g, rd.s, G);
         SmallGroup<G, R> v;
         if (init || diag) {
-            V2<R> h = high_factor<R>(f, G, a.n, g, !init);
+            V2<R> h = high_factor<G, R>(f, a.n, g, !init);
             h = mk2(h.x * scale, h.y * scale);
             const V2<R> hx = (!init && G < a.n && (g & 1u)) ? mk2(-h.x, -h.y) : h;
             if (init) {   // the product state: T[j] * h
@@ -341,13 +358,15 @@ __device__ __forceinline__ void small_fwd_round(V2<R> *psi, const SmallArgs &a, 
         }
         sg_store<G>(v, psi, base, rd.s);
     }
+    return own;
 }
 
 // Adjoint round at layer l: [round 0 and D: multiply psi and lambda by scale * conj(D)],
 // statistics of the round's qubits (scaled by corr) into red, then, if urot, the inverse
 // rotations of layer l on both states; the groups are written back if anything changed.
+// Returns the product of the scales of its tangent-form inverse rotations (1 if none).
 template <int G, typename R, bool CS>
-__device__ __forceinline__ void small_adj_round(V2<R> *psi, V2<R> *lam, const SmallArgs &a, SmallRound rd, int l,
+__device__ __forceinline__ R small_adj_round(V2<R> *psi, V2<R> *lam, const SmallArgs &a, SmallRound rd, int l,
                                                 bool diag, const V4<R> *f, V2<R> tl, R scale, R corr, bool urot,
                                                 R *red)
 {
@@ -355,7 +374,7 @@ __device__ __forceinline__ void small_adj_round(V2<R> *psi, V2<R> *lam, const Sm
     R k[G], c[G], sx[G], sy[G], sz[G];
 #pragma unroll
     for (int m = 0; m < G; ++m) {
-        const V2<R> kf = rtf[(size_t)l * a.n + rd.s + m];
+        const V2<R> kf = ldu2(reinterpret_cast<const R *>(rtf + (size_t)l * a.n + rd.s + m));
         k[m] = kf.x;
         c[m] = kf.y;
         sx[m] = sy[m] = sz[m] = (R)0;
@@ -368,7 +387,7 @@ __device__ __forceinline__ void small_adj_round(V2<R> *psi, V2<R> *lam, const Sm
         sg_load<G>(p, psi, base, rd.s);
         sg_load<G>(q, lam, base, rd.s);
         if (diag) {
-            V2<R> h = high_factor<R>(f, G, a.n, g, true);
+            V2<R> h = high_factor<G, R>(f, a.n, g, true);
             h = mk2(h.x * scale, h.y * scale);
             const V2<R> hx = (G < a.n && (g & 1u)) ? mk2(-h.x, -h.y) : h;
             sg_diag<G, true>(p, t, h, hx);
@@ -394,6 +413,10 @@ __device__ __forceinline__ void small_adj_round(V2<R> *psi, V2<R> *lam, const Sm
         }
     }
     round_stats_out<G>(sx, sy, sz, corr, rd.s, red);
+    R own = 1;
+#pragma unroll
+    for (int m = 0; m < G; ++m) own *= (CS || !urot) ? (R)1 : c[m];
+    return own;
 }
 
 __device__ __forceinline__ SmallRound small_round(int n, int r)
@@ -406,27 +429,27 @@ __device__ __forceinline__ SmallRound small_round(int n, int r)
 }
 
 template <typename R, bool CS = false>
-__device__ __forceinline__ void small_fwd_round_g(V2<R> *psi, const SmallArgs &a, SmallRound rd, int lr, bool init,
+__device__ __forceinline__ R small_fwd_round_g(V2<R> *psi, const SmallArgs &a, SmallRound rd, int lr, bool init,
                                                   bool diag, const V4<R> *f, V2<R> tl, R scale, bool last, R fin)
 {
     switch (rd.G) {
-    case 1: small_fwd_round<1, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
-    case 2: small_fwd_round<2, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
-    case 3: small_fwd_round<3, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
-    default: small_fwd_round<4, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin); break;
+    case 1: return small_fwd_round<1, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin);
+    case 2: return small_fwd_round<2, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin);
+    case 3: return small_fwd_round<3, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin);
+    default: return small_fwd_round<4, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin);
     }
 }
 
 template <typename R, bool CS = false>
-__device__ __forceinline__ void small_adj_round_g(V2<R> *psi, V2<R> *lam, const SmallArgs &a, SmallRound rd, int l,
+__device__ __forceinline__ R small_adj_round_g(V2<R> *psi, V2<R> *lam, const SmallArgs &a, SmallRound rd, int l,
                                                   bool diag, const V4<R> *f, V2<R> tl, R scale, R corr, bool urot,
                                                   R *red)
 {
     switch (rd.G) {
-    case 1: small_adj_round<1, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
-    case 2: small_adj_round<2, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
-    case 3: small_adj_round<3, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
-    default: small_adj_round<4, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red); break;
+    case 1: return small_adj_round<1, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red);
+    case 2: return small_adj_round<2, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red);
+    case 3: return small_adj_round<3, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red);
+    default: return small_adj_round<4, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red);
     }
 }
 
@@ -452,7 +475,7 @@ constexpr int kGatherGroups = sizeof(R) == 4 ? 2 : 1;
 template <bool SECOND, typename R>
 __device__ __forceinline__ V2<R> cphase(const V4<R> *f, int q, uint32_t b)
 {
-    const V4<R> g = f[q];
+    const V4<R> g = uniform_v4<R>(f + q);
     const R im = SECOND ? g.w : g.y;
     return mk2(SECOND ? g.z : g.x, b ? -im : im);
 }
@@ -526,8 +549,9 @@ __device__ __forceinline__ void cnot_fwd_gather(V2<R> *psi, const SmallArgs &a, 
     R sn[G], cs[G];
 #pragma unroll
     for (int m = 0; m < G; ++m) {
-        sn[m] = rcs[m].x;
-        cs[m] = rcs[m].y;
+        const V2<R> sc = ldu2(reinterpret_cast<const R *>(rcs + m));
+        sn[m] = sc.x;
+        cs[m] = sc.y;
     }
 #pragma unroll
     for (int k = 0; k < KG; ++k) {
@@ -586,8 +610,9 @@ __device__ __forceinline__ void cnot_adj_gather(V2<R> *psi, V2<R> *lam, const Sm
     R sn[G], cs[G], sx[G], sy[G], sz[G];
 #pragma unroll
     for (int m = 0; m < G; ++m) {
-        sn[m] = rcs[m].x;
-        cs[m] = rcs[m].y;
+        const V2<R> sc = ldu2(reinterpret_cast<const R *>(rcs + m));
+        sn[m] = sc.x;
+        cs[m] = sc.y;
         sx[m] = sy[m] = sz[m] = (R)0;
     }
 #pragma unroll
@@ -734,7 +759,6 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
     V2<R> *psi = reinterpret_cast<V2<R> *>(smem);
     V2<R> *lam = psi + N;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const V2<R> *rtf = reinterpret_cast<const V2<R> *>(a.rot_tf);
     const V4<R> *dw = reinterpret_cast<const V4<R> *>(a.dw);
     V2<R> *save = reinterpret_cast<V2<R> *>(a.psi_save) + (size_t)b * N;
     if constexpr (ENT != 0) {
@@ -756,10 +780,8 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
             const V2<R> tl = low_factor<R>(wl, G0, true, lane);
             R cn = 1;
             for (int r = 0; r < nr; ++r) {
-                const SmallRound rd = small_round(n, r);
-                for (int m = 0; m < rd.G; ++m) cn *= rtf[(size_t)(l + 1) * n + rd.s + m].y;
                 const bool last = l + 2 == L && r + 1 == nr;
-                small_fwd_round_g<R>(psi, a, rd, l + 1, false, r == 0, wl, tl, c, last, cn);
+                cn *= small_fwd_round_g<R>(psi, a, small_round(n, r), l + 1, false, r == 0, wl, tl, c, last, cn);
                 __syncthreads();
             }
             c = cn;
@@ -814,9 +836,7 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
         const V2<R> tl = low_factor<R>(wl, G0, true, lane);
         R cc = 1;
         for (int r = 0; r < nr; ++r) {
-            const SmallRound rd = small_round(n, r);
-            small_adj_round_g<R>(psi, lam, a, rd, l, diag && r == 0, wl, tl, c, cc * cc, l > 0, rl);
-            for (int m = 0; l > 0 && m < rd.G; ++m) cc *= rtf[(size_t)l * n + rd.s + m].y;   // scales of the rotations undone
+            cc *= small_adj_round_g<R>(psi, lam, a, small_round(n, r), l, diag && r == 0, wl, tl, c, cc * cc, l > 0, rl);
             __syncthreads();
         }
         if (tid < 3 * n) {
