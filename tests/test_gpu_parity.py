@@ -240,3 +240,21 @@ def test_whole_circuit_every_width(n, L):
     assert_e_close(e2, e2_ref, n, L)
     assert_grad_close(g2, g2_ref)
     ctx.close()
+
+
+@pytest.mark.parametrize("entangler", ["cz", "cnot"])
+def test_whole_circuit_deep(entangler):
+    """600 layers on the whole-circuit kernel (n = 9: a 4-qubit remainder round plus a
+    1-qubit one): the rotation scales carried from round to round and folded into each
+    layer's diagonal must not drift; the bounds grow with depth as derived for <O>."""
+    import qml_gradients_amd as hq
+    n, L, B = 9, 600, 2
+    ent = 1 if entangler == "cnot" else 0
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=3700 + ent)
+    say(f"[gpu] whole circuit deep n={n} L={L} {entangler}")
+    ctx = hq.Context(n, L, B, entangler=entangler)
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(*(torch.from_numpy(a) for a in (x, th, y))))
+    ctx.close()
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, entangler=ent)
+    assert_e_close(e, e_ref, n, L)
+    assert_grad_close(g, g_ref)
