@@ -15,6 +15,10 @@ namespace hqml {
 
 // ------------------------------------------------------------------ small circuits (n <= 13)
 
+constexpr int kSmallThreads = 512;               // eight waves: two per SIMD hide each other's latency
+constexpr int kRoundBits = 3;                    // qubits per register round
+constexpr int kSmallRows = kSmallThreads / 16;   // DPP row partials per workgroup
+
 // Table entry (factor for bit value 0 in x, y; for 1 in z, w) as a uniform value held in
 // scalar registers.  Without the pin the compiler may turn a per-lane choice between the
 // two factors into a per-lane load address: one vector load, waited on, per use.
@@ -42,10 +46,11 @@ __device__ __forceinline__ V2<R> small_diag(const V4<R> *wl, int n, uint32_t i)
     return f;
 }
 
-// LDS slot of amplitude i on the CZ small path: bits 0..4 XOR bits 4..8 (a bijection: bits 5 and up are
-// unchanged).  With it the rounds on qubits 0..3 (consecutive lanes step bit 4), 4..7
-// and 8..11 give every 32 consecutive lanes distinct 8-byte slots modulo 256 bytes.
-__device__ __forceinline__ uint32_t sslot(uint32_t i) { return i ^ ((i >> 4) & 31u); }
+// LDS slot of amplitude i: bits 0..4 XOR bits 3..7 (a bijection: bits 5 and up are
+// unchanged, which then fix bits 4, 3 and 0..2 in turn).  With it every round shape
+// (qubits 0..2, 3..5, 6..8, 9..11, 12 in registers) gives each 32 consecutive lanes
+// distinct 8-byte slots modulo 256 bytes, so the LDS accesses are free of bank conflicts.
+__device__ __forceinline__ uint32_t sslot(uint32_t i) { return i ^ ((i >> 3) & 31u); }
 
 // (O phi)_i for the Pauli string (zm, xm), phi = D_trail psi the true final state held
 // at slots sslot(i) (wl: the trailing diagonal's factors; applied only when xm != 0,
@@ -97,10 +102,12 @@ __device__ __forceinline__ V2<R> small_phase(const V4<R> *wl, int n, uint32_t i)
 
 // ---- whole circuit per workgroup with the CZ chain: register rounds
 //
-// The state of one sample lives in LDS.  A "round" on qubits s .. s+G-1 (G <= 4) hands
+// The state of one sample lives in LDS.  A "round" on qubits s .. s+G-1 (G <= 3) hands
 // every thread whole groups of 2^G amplitudes {base + (j << s)}, gathers a group into
 // registers, applies the round's work there and writes it back, so each LDS round trip
-// covers four qubits.  Round 0 (qubits 0 .. G0-1) also applies the merged diagonal D_l,
+// covers three qubits (eight amplitudes per thread and 512 threads keep two waves on
+// each SIMD; four-qubit rounds with one wave per SIMD, and two-qubit rounds with four,
+// were slower).  Round 0 (qubits 0 .. G0-1) also applies the merged diagonal D_l,
 // factored as T[j] (qubits below G0 and the CZ signs among them: uniform, built once per
 // layer) times a per-group factor over the other qubits (with their CZ signs and the
 // CZ between qubits G0-1 and G0).  Rotations use the scaled tangent form of rot_bit;
@@ -193,7 +200,7 @@ __device__ __forceinline__ void sg_rot(SmallGroup<G, R> &v, int m, R k)
     }
 }
 
-// The 16 entries T[j] of the low-qubit factor, held by lanes j = lane & 15, as uniform
+// The entries T[j] of the low-qubit factor, held by lanes j = lane & 15, as uniform
 // values.  Called with every lane of the wave active (readlane reads a lane whether or
 // not it is active, so the entries must be computed outside divergent code).
 template <int G, typename R>
@@ -280,9 +287,9 @@ __device__ __forceinline__ void round_stats_out(const R (&sx)[G], const R (&sy)[
         row_sum16x3(x, y, z);
         if ((lane & 15) == 15) {
             const int r = w * 4 + (lane >> 4), q = s + m;
-            red[(q * 3 + 0) * 16 + r] = x;
-            red[(q * 3 + 1) * 16 + r] = y;
-            red[(q * 3 + 2) * 16 + r] = z;
+            red[(q * 3 + 0) * kSmallRows + r] = x;
+            red[(q * 3 + 1) * kSmallRows + r] = y;
+            red[(q * 3 + 2) * kSmallRows + r] = z;
         }
     }
 }
@@ -320,7 +327,7 @@ __device__ __forceinline__ R small_fwd_round(V2<R> *psi, const SmallArgs &a, Sma
     fin *= own;
     V2<R> t[1 << G];
     bcast_low<G, R>(t, tl);
-    for (uint32_t g = threadIdx.x; g < rd.groups; g += kThreads) {
+    for (uint32_t g = threadIdx.x; g < rd.groups; g += kSmallThreads) {
         const uint32_t base = sg_base(g, rd.s, G);
         SmallGroup<G, R> v;
         if (init || diag) {
@@ -381,7 +388,7 @@ __device__ __forceinline__ R small_adj_round(V2<R> *psi, V2<R> *lam, const Small
     }
     V2<R> t[1 << G];
     bcast_low<G, R>(t, tl);
-    for (uint32_t g = threadIdx.x; g < rd.groups; g += kThreads) {
+    for (uint32_t g = threadIdx.x; g < rd.groups; g += kSmallThreads) {
         const uint32_t base = sg_base(g, rd.s, G);
         SmallGroup<G, R> p, q;
         sg_load<G>(p, psi, base, rd.s);
@@ -422,8 +429,8 @@ __device__ __forceinline__ R small_adj_round(V2<R> *psi, V2<R> *lam, const Small
 __device__ __forceinline__ SmallRound small_round(int n, int r)
 {
     SmallRound rd;
-    rd.s = 4 * r;
-    rd.G = n - rd.s < 4 ? n - rd.s : 4;
+    rd.s = kRoundBits * r;
+    rd.G = n - rd.s < kRoundBits ? n - rd.s : kRoundBits;
     rd.groups = (1u << n) >> rd.G;
     return rd;
 }
@@ -435,8 +442,7 @@ __device__ __forceinline__ R small_fwd_round_g(V2<R> *psi, const SmallArgs &a, S
     switch (rd.G) {
     case 1: return small_fwd_round<1, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin);
     case 2: return small_fwd_round<2, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin);
-    case 3: return small_fwd_round<3, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin);
-    default: return small_fwd_round<4, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin);
+    default: return small_fwd_round<3, R, CS>(psi, a, rd, lr, init, diag, f, tl, scale, last, fin);
     }
 }
 
@@ -448,8 +454,7 @@ __device__ __forceinline__ R small_adj_round_g(V2<R> *psi, V2<R> *lam, const Sma
     switch (rd.G) {
     case 1: return small_adj_round<1, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red);
     case 2: return small_adj_round<2, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red);
-    case 3: return small_adj_round<3, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red);
-    default: return small_adj_round<4, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red);
+    default: return small_adj_round<3, R, CS>(psi, lam, a, rd, l, diag, f, tl, scale, corr, urot, red);
     }
 }
 
@@ -524,7 +529,7 @@ __device__ __forceinline__ void cnot_fwd_gather(V2<R> *psi, const SmallArgs &a, 
     V2<R> h[KG], hx[KG];
 #pragma unroll
     for (int k = 0; k < KG; ++k) {
-        const uint32_t g = threadIdx.x + (uint32_t)k * kThreads;
+        const uint32_t g = threadIdx.x + (uint32_t)k * kSmallThreads;
         if (g >= groups) continue;
         // high bits of the source index i = P^-1((g << G) | j): (g ^ (g << 1)), with bit 0
         // flipped when bit G-1 of j is set
@@ -555,7 +560,7 @@ __device__ __forceinline__ void cnot_fwd_gather(V2<R> *psi, const SmallArgs &a, 
     }
 #pragma unroll
     for (int k = 0; k < KG; ++k) {
-        const uint32_t g = threadIdx.x + (uint32_t)k * kThreads;
+        const uint32_t g = threadIdx.x + (uint32_t)k * kSmallThreads;
         if (g >= groups) continue;
         sg_diag<G, false, 0>(v[k], t, h[k], hx[k]);
 #pragma unroll
@@ -582,7 +587,7 @@ __device__ __forceinline__ void cnot_adj_gather(V2<R> *psi, V2<R> *lam, const Sm
     V2<R> h[KG], hx[KG];
 #pragma unroll
     for (int k = 0; k < KG; ++k) {
-        const uint32_t g = threadIdx.x + (uint32_t)k * kThreads;
+        const uint32_t g = threadIdx.x + (uint32_t)k * kSmallThreads;
         if (g >= groups) continue;
         // high bits of P((g << G) | j): the prefix parities of g, all flipped for odd j
         const uint32_t pb0 = cnot_chain(g, hmask), pb1 = pb0 ^ hmask;
@@ -617,7 +622,7 @@ __device__ __forceinline__ void cnot_adj_gather(V2<R> *psi, V2<R> *lam, const Sm
     }
 #pragma unroll
     for (int k = 0; k < KG; ++k) {
-        const uint32_t g = threadIdx.x + (uint32_t)k * kThreads;
+        const uint32_t g = threadIdx.x + (uint32_t)k * kSmallThreads;
         if (g >= groups) continue;
         sg_diag<G, false, 1>(p[k], t, h[k], hx[k]);
         sg_diag<G, false, 1>(q[k], t, h[k], hx[k]);
@@ -642,8 +647,7 @@ __device__ __forceinline__ void cnot_fwd_gather_g(V2<R> *psi, const SmallArgs &a
     switch (G) {
     case 1: cnot_fwd_gather<1, R>(psi, a, l, tl); break;
     case 2: cnot_fwd_gather<2, R>(psi, a, l, tl); break;
-    case 3: cnot_fwd_gather<3, R>(psi, a, l, tl); break;
-    default: cnot_fwd_gather<4, R>(psi, a, l, tl); break;
+    default: cnot_fwd_gather<3, R>(psi, a, l, tl); break;
     }
 }
 
@@ -654,8 +658,7 @@ __device__ __forceinline__ void cnot_adj_gather_g(V2<R> *psi, V2<R> *lam, const 
     switch (G) {
     case 1: cnot_adj_gather<1, R>(psi, lam, a, l, tl, urot, red); break;
     case 2: cnot_adj_gather<2, R>(psi, lam, a, l, tl, urot, red); break;
-    case 3: cnot_adj_gather<3, R>(psi, lam, a, l, tl, urot, red); break;
-    default: cnot_adj_gather<4, R>(psi, lam, a, l, tl, urot, red); break;
+    default: cnot_adj_gather<3, R>(psi, lam, a, l, tl, urot, red); break;
     }
 }
 
@@ -672,8 +675,8 @@ __device__ void small_cnot_rounds(const SmallArgs &a, V2<R> *psi, V2<R> *lam, R 
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const V4<R> *dw = reinterpret_cast<const V4<R> *>(a.dw);
     V2<R> *save = reinterpret_cast<V2<R> *>(a.psi_save) + (size_t)b * N;
-    const int G0 = n < 4 ? n : 4;
-    const int nr = (n + 3) / 4;
+    const int G0 = n < kRoundBits ? n : kRoundBits;
+    const int nr = (n + kRoundBits - 1) / kRoundBits;
     const V2<R> one = mk2((R)1, (R)0);
 
     if (a.mode != 1) {
@@ -692,7 +695,7 @@ __device__ void small_cnot_rounds(const SmallArgs &a, V2<R> *psi, V2<R> *lam, R 
             }
         }
     } else {
-        for (uint32_t i = tid; i < N; i += kThreads) psi[sslot(i)] = save[i];
+        for (uint32_t i = tid; i < N; i += kSmallThreads) psi[sslot(i)] = save[i];
         __syncthreads();
     }
 
@@ -700,7 +703,7 @@ __device__ void small_cnot_rounds(const SmallArgs &a, V2<R> *psi, V2<R> *lam, R 
     const uint32_t zm = a.obs, xm = a.obs_x, xs = cnot_chain_inv(xm, mask);
     const int yph = __builtin_popcount(zm & xm) & 3;
     R e = 0;
-    for (uint32_t i = tid; i < N; i += kThreads) {
+    for (uint32_t i = tid; i < N; i += kSmallThreads) {
         const uint32_t j = i ^ xs;
         V2<R> v = cmul(small_phase<false, R>(wt, n, j), psi[sslot(j)]);
         if (__builtin_popcount((cnot_chain(i, mask) ^ xm) & zm) & 1) v = mk2(-v.x, -v.y);
@@ -717,18 +720,18 @@ __device__ void small_cnot_rounds(const SmallArgs &a, V2<R> *psi, V2<R> *lam, R 
         __syncthreads();
         if (tid == 0) {
             double s = 0.0;
-            for (int k = 0; k < 16; ++k) s += (double)red[k];
+            for (int k = 0; k < kSmallRows; ++k) s += (double)red[k];
             static_cast<R *>(a.e_out)[b] = (R)s;
         }
         if (a.mode == 0) {
-            for (uint32_t i = tid; i < N; i += kThreads) save[i] = psi[sslot(i)];
+            for (uint32_t i = tid; i < N; i += kSmallThreads) save[i] = psi[sslot(i)];
             return;
         }
     }
     __syncthreads();
 
     for (int l = L - 1; l >= 0; --l) {
-        R *rl = red + (l & 1) * (3 * kSmallMaxQubits * 16);
+        R *rl = red + (l & 1) * (3 * kSmallMaxQubits * kSmallRows);
         const V4<R> *wl = dw + (size_t)l * n;
         if (l + 1 < L)
             cnot_adj_gather_g<R>(psi, lam, a, G0, l, cnot_low_adj<R>(wl, wl + n, G0, lane), l > 0, rl);
@@ -741,7 +744,7 @@ __device__ void small_cnot_rounds(const SmallArgs &a, V2<R> *psi, V2<R> *lam, R 
         }
         if (tid < 3 * n) {
             double s = 0.0;
-            for (int k = 0; k < 16; ++k) s += (double)rl[tid * 16 + k];
+            for (int k = 0; k < kSmallRows; ++k) s += (double)rl[tid * kSmallRows + k];
             a.stats[(((size_t)b * L + l) * n) * 3 + tid] = s;
         }
     }
@@ -750,10 +753,10 @@ __device__ void small_cnot_rounds(const SmallArgs &a, V2<R> *psi, V2<R> *lam, R 
 // ENT: the entangler (0 CZ chain, 1 CNOT chain), one instance each so that the CZ
 // kernel keeps its own register budget.
 template <typename R, int ENT>
-__global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
+__global__ __launch_bounds__(kSmallThreads) void k_small(SmallArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ R red[2 * 3 * kSmallMaxQubits * 16 + 16];
+    __shared__ R red[2 * 3 * kSmallMaxQubits * kSmallRows + kSmallRows];
     const int n = a.n, L = a.L;
     const uint32_t N = 1u << n;
     V2<R> *psi = reinterpret_cast<V2<R> *>(smem);
@@ -766,8 +769,8 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
         return;
     }
 
-    const int G0 = n < 4 ? n : 4;
-    const int nr = (n + 3) / 4;   // rounds per layer: qubits 0..3, 4..7, 8..11, 12
+    const int G0 = n < kRoundBits ? n : kRoundBits;
+    const int nr = (n + kRoundBits - 1) / kRoundBits;   // rounds per layer: qubits 0..2, 3..5, 6..8, 9..11, 12
     if (a.mode != 1) {
         const V4<R> *u = reinterpret_cast<const V4<R> *>(a.init_u) + (size_t)b * n;
         small_fwd_round_g<R>(psi, a, small_round(n, 0), -1, true, false, u, low_factor<R>(u, G0, false, lane), (R)1,
@@ -788,7 +791,7 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
         }
         // <O> = sum_i Re(conj(psi_i) (O psi)_i)
         R e = 0;
-        for (uint32_t i = tid; i < N; i += kThreads) {
+        for (uint32_t i = tid; i < N; i += kSmallThreads) {
             V2<R> v = psi[sslot(i)];
             if (a.obs_x) v = cmul(v, small_diag<R>(dw + (size_t)(L - 1) * n, n, i));
             const V2<R> o = small_obs<R>(psi, i, a.obs, a.obs_x, dw + (size_t)(L - 1) * n, n);
@@ -799,22 +802,22 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
         __syncthreads();
         if (tid == 0) {
             double s = 0.0;
-            for (int k = 0; k < 16; ++k) s += (double)red[k];
+            for (int k = 0; k < kSmallRows; ++k) s += (double)red[k];
             static_cast<R *>(a.e_out)[b] = (R)s;
         }
         if (a.mode == 0) {
-            for (uint32_t i = tid; i < N; i += kThreads) save[i] = psi[sslot(i)];
+            for (uint32_t i = tid; i < N; i += kSmallThreads) save[i] = psi[sslot(i)];
             return;
         }
         __syncthreads();
     } else {
-        for (uint32_t i = tid; i < N; i += kThreads) psi[sslot(i)] = save[i];
+        for (uint32_t i = tid; i < N; i += kSmallThreads) psi[sslot(i)] = save[i];
         __syncthreads();
     }
 
     // Adjoint sweep: lambda = O psi at P_{L-1}; statistics at every P_l; uncompute.
     // lambda at the last Ry layer = D_trail^dagger O D_trail psi (= O psi for a Z-string)
-    for (uint32_t i = tid; i < N; i += kThreads) {
+    for (uint32_t i = tid; i < N; i += kSmallThreads) {
         V2<R> o = small_obs<R>(psi, i, a.obs, a.obs_x, dw + (size_t)(L - 1) * n, n);
         if (a.obs_x) {
             V2<R> f = small_diag<R>(dw + (size_t)(L - 1) * n, n, i);
@@ -830,7 +833,7 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
     // are read while layer l-1 writes the other half.
     R c = 1;
     for (int l = L - 1; l >= 0; --l) {
-        R *rl = red + (l & 1) * (3 * kSmallMaxQubits * 16);
+        R *rl = red + (l & 1) * (3 * kSmallMaxQubits * kSmallRows);
         const bool diag = l + 1 < L;
         const V4<R> *wl = dw + (size_t)l * n;
         const V2<R> tl = low_factor<R>(wl, G0, true, lane);
@@ -841,7 +844,7 @@ __global__ __launch_bounds__(kThreads) void k_small(SmallArgs a)
         }
         if (tid < 3 * n) {
             double s = 0.0;
-            for (int k = 0; k < 16; ++k) s += (double)rl[tid * 16 + k];
+            for (int k = 0; k < kSmallRows; ++k) s += (double)rl[tid * kSmallRows + k];
             a.stats[(((size_t)b * L + l) * n) * 3 + tid] = s;
         }
         c = cc;
@@ -872,14 +875,14 @@ hipError_t launch_small(const SmallArgs &a, int B, int r64, hipStream_t s)
     const size_t shm = (size_t)2 * ((size_t)1 << a.n) * (r64 ? sizeof(double2) : sizeof(float2));
     if (r64) {
         if (a.ent)
-            k_small<double, 1><<<B, kThreads, shm, s>>>(a);
+            k_small<double, 1><<<B, kSmallThreads, shm, s>>>(a);
         else
-            k_small<double, 0><<<B, kThreads, shm, s>>>(a);
+            k_small<double, 0><<<B, kSmallThreads, shm, s>>>(a);
     } else {
         if (a.ent)
-            k_small<float, 1><<<B, kThreads, shm, s>>>(a);
+            k_small<float, 1><<<B, kSmallThreads, shm, s>>>(a);
         else
-            k_small<float, 0><<<B, kThreads, shm, s>>>(a);
+            k_small<float, 0><<<B, kSmallThreads, shm, s>>>(a);
     }
     return hipGetLastError();
 }

@@ -1,8 +1,8 @@
 """Host checks of the index algebra of the whole-circuit kernel (n <= 13).
 
-The kernel keeps a sample's state in LDS at slot sslot(i) = i ^ ((i >> 4) & 31) and
-works in rounds: a round on qubits s .. s+G-1 gives thread g (consecutive lanes =
-consecutive g) the amplitudes base(g) | (j << s).  With the CNOT chain, round 0 of a
+The kernel keeps a sample's state in LDS at slot sslot(i) = i ^ ((i >> 3) & 31) and
+works in rounds of up to three qubits: a round on qubits s .. s+G-1 gives thread g
+(consecutive lanes = consecutive g) the amplitudes base(g) | (j << s).  With the CNOT chain, round 0 of a
 forward step reads amplitude J from P^-1(J) and round 0 of an adjoint step reads
 amplitude i from P(i) (bit k of P(i) = parity of bits 0..k of i), with the source index
 assembled from a per-group high part and a per-j low part.  These tests restate those
@@ -14,14 +14,17 @@ import numpy as np
 import pytest
 
 
+ROUND_BITS = 3
+
+
 def sslot(i):
-    return i ^ ((i >> 4) & 31)
+    return i ^ ((i >> 3) & 31)
 
 
 def rounds(n):
     out, s = [], 0
     while s < n:
-        G = min(4, n - s)
+        G = min(ROUND_BITS, n - s)
         out.append((s, G))
         s += G
     return out
@@ -78,7 +81,7 @@ def test_rounds_are_bank_conflict_free(n):
 
 @pytest.mark.parametrize("n", range(1, 14))
 def test_cnot_forward_gather_source_is_the_inverse_chain(n):
-    G = min(4, n)
+    G = min(ROUND_BITS, n)
     hmask, lmask = (1 << (n - G)) - 1, (1 << G) - 1
     for g in range(1 << (n - G)):
         ih0 = (g ^ (g << 1)) & hmask
@@ -91,7 +94,7 @@ def test_cnot_forward_gather_source_is_the_inverse_chain(n):
 
 @pytest.mark.parametrize("n", range(1, 14))
 def test_cnot_adjoint_gather_source_is_the_chain(n):
-    G = min(4, n)
+    G = min(ROUND_BITS, n)
     hmask, lmask = (1 << (n - G)) - 1, (1 << G) - 1
     for g in range(1 << (n - G)):
         pb0 = chain(g, n - G)
