@@ -1463,20 +1463,26 @@ __global__ void k_stats_reduce(const P *part, const int2 *map, int Bs, int bofs,
     S[((size_t)b * L * n + lq) * 3 + s] = acc;
 }
 
-// grad[l][q][a] = sum_b dLdE_b * sum_s H[l][q][a][s] * S[b][l][q][s]
+// grad[l][q][a] = sum_b dLdE_b * sum_s H[l][q][a][s] * S[b][l][q][s].  One wave per
+// output: lane t sums samples t, t + 64, ... in order, then the lanes combine in a fixed
+// butterfly, so every run adds in the same order.
 template <typename IO>
-__global__ void k_grad_reduce(const double *S, const double *H, const double *dlde, int B, int L, int n, IO *grad)
+__global__ void __launch_bounds__(256) k_grad_reduce(const double *S, const double *H, const double *dlde, int B, int L,
+                                                      int n, IO *grad)
 {
-    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= L * n * 3) return;
+    const int idx = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (idx >= L * n * 3) return;   // whole waves leave together
     const int lq = idx / 3;
     const double *h = H + (size_t)idx * 3;
+    const double h0 = h[0], h1 = h[1], h2 = h[2];
     double acc = 0.0;
-    for (int b = 0; b < B; ++b) {
+    for (int b = lane; b < B; b += 64) {
         const double *sb = S + ((size_t)b * L * n + lq) * 3;
-        acc += dlde[b] * (h[0] * sb[0] + h[1] * sb[1] + h[2] * sb[2]);
+        acc += dlde[b] * (h0 * sb[0] + h1 * sb[1] + h2 * sb[2]);
     }
-    grad[idx] = (IO)acc;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    if (lane == 0) grad[idx] = (IO)acc;
 }
 
 }  // namespace hqml
@@ -1676,11 +1682,11 @@ hipError_t launch_stats_reduce(const void *part, int r64, const int2 *map, int B
 hipError_t launch_grad_reduce(const double *S, const double *H, const double *dlde, int B, int L, int n,
                               void *grad, int io64, hipStream_t s)
 {
-    const int total = L * n * 3;
+    const int total = L * n * 3, blocks = (total + 3) / 4;   // four outputs (waves) per block
     if (io64)
-        k_grad_reduce<double><<<(total + 255) / 256, 256, 0, s>>>(S, H, dlde, B, L, n, static_cast<double *>(grad));
+        k_grad_reduce<double><<<blocks, 256, 0, s>>>(S, H, dlde, B, L, n, static_cast<double *>(grad));
     else
-        k_grad_reduce<float><<<(total + 255) / 256, 256, 0, s>>>(S, H, dlde, B, L, n, static_cast<float *>(grad));
+        k_grad_reduce<float><<<blocks, 256, 0, s>>>(S, H, dlde, B, L, n, static_cast<float *>(grad));
     return hipGetLastError();
 }
 
