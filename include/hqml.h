@@ -187,8 +187,9 @@ int hqml_kernel_times(hqml_ctx *ctx, double *ms, long long *count, int reset);
 /* Number of batch chunks a training step on the tile path (n >= 14) pipelines: chunk
  * k+1's forward sweep runs on a second stream of the context while chunk k's adjoint
  * sweep runs on the context's stream.  Samples are independent, so results are
- * bitwise the same for every chunk count.  0 = automatic (2), 1 = no overlap,
- * at most 8.  Per-launch timing (hqml_set_timing) also disables the overlap. */
+ * bitwise the same for every chunk count.  0 = automatic (2 when ckpt_block > 0, else
+ * 1), 1 = no overlap, at most 8; a chunk keeps at least 256 tiles.  Per-launch timing
+ * (hqml_set_timing) also disables the overlap. */
 int hqml_set_overlap(hqml_ctx *ctx, int chunks);
 
 /* Plan facts for reporting: fused forward passes per training step, backward

@@ -64,7 +64,13 @@ def test_two_stage_reductions(ckpt):
     first summed in 256-tile chunks.  Batch 3 in two pipelined chunks (the second one
     starting at sample 1) and a forward/backward split."""
     n, L, B = 22, 3, 3
-    (x, th, y), (e, loss, g) = _run_train(n, L, B, seed=42, ckpt_block=ckpt)
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=42)
+    say(f"[gpu] two-stage reductions n={n} ckpt={ckpt}, two chunks")
+    ctx = _ctx(n, L, B, ckpt_block=ckpt)
+    ctx.set_overlap(2)
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(*(torch.from_numpy(a) for a in (x, th, y))))
+    loss = float(loss[0])
+    ctx.close()
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
     assert_e_close(e, e_ref, n, L)
     assert abs(loss - loss_ref) <= 1e-5 * max(1.0, loss_ref)
