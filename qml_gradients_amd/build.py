@@ -16,6 +16,11 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libhqml.so")
 SOURCES = ["hqml_kernels.hip", "hqml_small.hip", "hqml_gbg.hip", "hqml_abi.cpp", "hqml_plan.cpp"]
+# Compilation units: (source, extra flags).  hqml_kernels.hip is compiled a second time
+# for the fp32 adjoint launches alone, with the backend's max-ilp instruction schedule.
+UNITS = [(s, []) for s in SOURCES] + [
+    ("hqml_kernels.hip", ["-DHQML_BWD32_UNIT=1", "-mllvm", "--amdgpu-sched-strategy=max-ilp"]),
+]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("HQML_OFFLOAD_ARCH", "gfx950")
 
@@ -31,10 +36,31 @@ FLAGS = [
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, *FLAGS, "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
+    objdir = os.path.join(HERE, f"_obj{os.getpid()}")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    procs, objs = [], []
+    try:
+        for k, (src, extra) in enumerate(UNITS):
+            obj = os.path.join(objdir, f"{k}_{os.path.splitext(src)[0]}.o")
+            cmd = [HIPCC, *compile_flags, *extra, "-c", "-o", obj, os.path.join(CSRC, src)]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((cmd, subprocess.Popen(cmd)))
+            objs.append(obj)
+        for cmd, p in procs:
+            if p.wait() != 0:
+                raise subprocess.CalledProcessError(p.returncode, cmd)
+        link = [HIPCC, *FLAGS, "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(link), flush=True)
+        subprocess.check_call(link)
+    finally:
+        for obj in objs:
+            if os.path.exists(obj):
+                os.remove(obj)
+        if os.path.isdir(objdir):
+            os.rmdir(objdir)
     os.replace(tmp, LIB)
     return LIB
 

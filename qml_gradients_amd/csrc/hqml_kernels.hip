@@ -27,6 +27,11 @@
 #include "hqml_device.hpp"
 #include "hqml_internal.hpp"
 
+// 1: the compilation unit of the fp32 adjoint launches (see the launch wrappers below).
+#ifndef HQML_BWD32_UNIT
+#define HQML_BWD32_UNIT 0
+#endif
+
 namespace hqml {
 
 // Element access of a stored state.  Every state read is a streaming read (each pass
@@ -1224,6 +1229,7 @@ __global__ void k_prep_zyz(const TI *theta, int L, int n, double *zyz)
 // tile passes): the same rewrite, but an X^g moved left through the chain P becomes
 // X^(P^-1 g), P^-1 g = g ^ (g << 1) (no Z appears), so the frame is a qubit mask carried
 // from layer to layer by one thread.
+#if HQML_BWD32_UNIT == 0   // a non-template kernel: defined in one compilation unit only
 __global__ void k_prep_frame(const double *zyz, int L, int n, int ent, unsigned char *G)
 {
     const int q = blockIdx.x * blockDim.x + threadIdx.x;
@@ -1254,6 +1260,7 @@ __global__ void k_prep_frame(const double *zyz, int L, int n, int ent, unsigned 
         if (ent == 0 && l >= 1 && z[1] > z[0]) g ^= 1;
     }
 }
+#endif
 
 // rot_tf[l][q] = (k, f): the simulated rotation is Ry(beta') = f [[1, -k], [k, 1]],
 //   f = cos(beta'/2) >= 1/sqrt 2, k = tan(beta'/2) in [-1, 1] (frame sign included);
@@ -1507,8 +1514,21 @@ __global__ void __launch_bounds__(256) k_grad_reduce(const double *S, const doub
 //
 // Type codes: io64 = the caller's arrays are double (else float); r64 = compute in
 // double (else float); storage 0 = float2, 1 = bf16 pair, 2 = double2 states.
-
+//
+// This file is compiled twice.  HQML_BWD32_UNIT = 1 builds only the fp32 adjoint
+// launches (and so the only instances of k_tile_bwd<*, *, float>), with the backend's
+// max-ilp instruction schedule: measured 4 % faster for that kernel at 20 qubits, but
+// slower for the fp64 adjoint (+7 %) and the bf16 forward pass (+5 %), which the default
+// build (HQML_BWD32_UNIT = 0) compiles with the default schedule.
 namespace hqml {
+
+template <int ST, typename R>
+static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s);
+
+// The fp32 adjoint launches (the other compilation unit).
+void launch_tile_bwd_f32(const TilePassArgs &a, dim3 grid, int storage, hipStream_t s);
+
+#if HQML_BWD32_UNIT == 0
 
 template <typename TI, typename R>
 static void prep_typed(const void *theta, const void *x, int L, int n, int B, double *zyz, unsigned char *G,
@@ -1576,6 +1596,8 @@ hipError_t launch_tile_fwd(const TilePassArgs &a, int B, int storage, int r64, h
     return hipGetLastError();
 }
 
+#endif  // HQML_BWD32_UNIT == 0
+
 template <int ST, typename R>
 static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s)
 {
@@ -1609,6 +1631,15 @@ static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s)
     }
 }
 
+#if HQML_BWD32_UNIT == 1
+void launch_tile_bwd_f32(const TilePassArgs &a, dim3 grid, int storage, hipStream_t s)
+{
+    if (storage == 1)
+        launch_bwd_shape<1, float>(a, grid, s);
+    else
+        launch_bwd_shape<0, float>(a, grid, s);
+}
+#else
 hipError_t launch_tile_bwd(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s)
 {
     const dim3 grid((unsigned)(B * a.T));
@@ -1618,10 +1649,7 @@ hipError_t launch_tile_bwd(const TilePassArgs &a, int B, int storage, int r64, h
         else
             launch_bwd_shape<0, double>(a, grid, s);
     } else {
-        if (storage == 1)
-            launch_bwd_shape<1, float>(a, grid, s);
-        else
-            launch_bwd_shape<0, float>(a, grid, s);
+        launch_tile_bwd_f32(a, grid, storage, s);
     }
     return hipGetLastError();
 }
@@ -1705,5 +1733,6 @@ hipError_t launch_grad_reduce(const double *S, const double *H, const double *dl
         k_grad_reduce<float><<<blocks, 256, 0, s>>>(S, H, dlde, B, L, n, static_cast<float *>(grad));
     return hipGetLastError();
 }
+#endif  // HQML_BWD32_UNIT
 
 }  // namespace hqml
