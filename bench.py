@@ -44,9 +44,11 @@ L2_POSITIONS = (0, 1, 9, 10, 11)
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     # what the tile kernels are built from: their sources and the build's compile flags
-    for f in ("csrc/hqml_kernels.hip", "csrc/hqml_device.hpp", "csrc/hqml_internal.hpp", "build.py"):
-        with open(os.path.join(ROOT, "qml_gradients_amd", f), "rb") as fh:
+    for f in ("hqml_kernels.hip", "hqml_device.hpp", "hqml_internal.hpp"):
+        with open(os.path.join(ROOT, "qml_gradients_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    from qml_gradients_amd import build as hq_build
+    h.update(repr((hq_build.FLAGS[:-1], hq_build.UNITS)).encode())   # FLAGS[-1]: the include path
     return h.hexdigest()[:16]
 
 

@@ -54,7 +54,7 @@ def build(verbose: bool = False) -> str:
         for cmd, p in procs:
             if p.wait() != 0:
                 raise subprocess.CalledProcessError(p.returncode, cmd)
-        link = [HIPCC, *FLAGS, "-o", tmp, *objs]
+        link = [HIPCC, *FLAGS, "-Wl,--no-undefined", "-o", tmp, *objs]   # every unit present
         if verbose:
             print(" ".join(link), flush=True)
         subprocess.check_call(link)
