@@ -20,7 +20,11 @@
  *     arrays owned by the caller; the library never frees or keeps them.
  *     x: [B][n] encoding angles; theta: [L][n][3] (Rx, Ry, Rz angle of qubit q
  *     in layer l); y: [B] labels; expz: [B]; loss: [1]; grad: [L][n][3];
- *     dL_dE: [B].
+ *     dL_dE: [B].  Each array must be device memory of the context's device
+ *     (pinned host memory mapped into it also works) and fit inside its
+ *     allocation; otherwise the call returns HQML_ERR_ARG before queuing
+ *     anything (a NULL, pageable-host or too-short array).  A pointer that
+ *     passed is remembered per argument, so only new buffers are queried.
  *   - Work is queued on the context's stream and is asynchronous: outputs are
  *     valid once that stream has synchronised.  Argument errors are detected
  *     on the host before anything is queued.

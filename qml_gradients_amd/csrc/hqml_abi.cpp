@@ -106,6 +106,12 @@ struct hqml_ctx {
     // saved-forward bookkeeping
     int saved_B = -1;
     std::string err;
+    // caller arrays already found device-accessible and large enough, one slot per argument
+    struct Checked {
+        const void *p = nullptr;
+        size_t bytes = 0;
+    };
+    Checked checked[8];
     // instrumentation
     bool timing = false;
     struct Rec {
@@ -131,6 +137,41 @@ int fail(hqml_ctx *c, int code, const std::string &msg)
 int hip_fail(hqml_ctx *c, hipError_t e, const char *what)
 {
     return fail(c, HQML_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Caller array argument `slot` (its index in the table above) must be memory this
+// context's kernels can read or write: device memory of its device, managed memory, or
+// pinned host memory mapped into the device; pageable host memory is refused, as is an
+// array that runs past the end of its allocation.  A pointer that passed is remembered
+// per slot, so a loop that reuses its buffers queries the runtime once.
+int check_array(hqml_ctx *c, int slot, const void *p, size_t bytes, const char *name)
+{
+    hqml_ctx::Checked &k = c->checked[slot];
+    if (p && p == k.p && bytes <= k.bytes) return HQML_OK;
+    if (!p) return fail(c, HQML_ERR_ARG, std::string(name) + " is NULL");
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();   // the failed query leaves its error behind
+        return fail(c, HQML_ERR_ARG, std::string(name) + " is not memory known to HIP");
+    }
+    const bool on_device = at.type == hipMemoryTypeDevice && at.device == c->cfg.device;
+    const bool mapped = (at.type == hipMemoryTypeHost || at.type == hipMemoryTypeManaged) && at.devicePointer == p;
+    if (!on_device && !mapped)
+        return fail(c, HQML_ERR_ARG, std::string(name) + " must be device memory of the context's device "
+                                     "(or pinned host memory), not pageable host memory");
+    void *base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void *>(p)) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(c, HQML_ERR_ARG, std::string(name) + ": allocation range unknown");
+    }
+    const size_t room = static_cast<size_t>(static_cast<const char *>(base) + size - static_cast<const char *>(p));
+    if (bytes > room)
+        return fail(c, HQML_ERR_ARG, std::string(name) + " needs " + std::to_string(bytes) + " bytes, its allocation has " +
+                                         std::to_string(room) + " from that address");
+    k.p = p;
+    k.bytes = bytes;
+    return HQML_OK;
 }
 
 size_t elem_bytes(const hqml_ctx *c)
@@ -764,10 +805,14 @@ int forward_impl(hqml_ctx *c, int B, const void *x, const void *theta, void *exp
         if (save_for_backward) c->saved_B = 0;
         return HQML_OK;
     }
-    if (!x || !theta || !expz) return fail(c, HQML_ERR_ARG, "x, theta and expz must be device pointers");
     hipError_t e = hipSetDevice(c->cfg.device);
     if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
+    const size_t io = io64 ? sizeof(double) : sizeof(float), nq = (size_t)c->cfg.n_qubits;
     int rc;
+    if ((rc = check_array(c, 0, x, (size_t)B * nq * io, "x")) ||
+        (rc = check_array(c, 1, theta, (size_t)c->cfg.n_layers * nq * 3 * io, "theta")) ||
+        (rc = check_array(c, 3, expz, (size_t)B * io, "expz")))
+        return rc;
     if (c->gbg) {
         if ((rc = gbg_forward_sweep(c, B, static_cast<const float *>(x), static_cast<const float *>(theta)))) return rc;
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {
@@ -806,11 +851,13 @@ int backward_impl(hqml_ctx *c, const void *dL_dE, void *grad, int io64)
 {
     if (!c) return HQML_ERR_ARG;
     c->err.clear();
-    if (c->saved_B < 0) return fail(c, HQML_ERR_STATE, "no saved forward pass on this context");
-    if (!grad) return fail(c, HQML_ERR_ARG, "grad must be a device pointer");
-    const int B = c->saved_B;
     hipError_t e = hipSetDevice(c->cfg.device);
     if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
+    const size_t io = io64 ? sizeof(double) : sizeof(float);
+    int rc = check_array(c, 5, grad, (size_t)c->cfg.n_layers * c->cfg.n_qubits * 3 * io, "grad");
+    if (rc) return rc;
+    if (c->saved_B < 0) return fail(c, HQML_ERR_STATE, "no saved forward pass on this context");
+    const int B = c->saved_B;
     const Plan &pl = c->plan;
     if (B == 0) {  // empty batch: the gradient is zero (the reduction over no samples)
         if (c->gbg) return gbg_grad(c, 0, static_cast<float *>(grad));
@@ -818,8 +865,8 @@ int backward_impl(hqml_ctx *c, const void *dL_dE, void *grad, int io64)
             return launch_grad_reduce(c->S, c->H, c->dlde, 0, pl.L, pl.n, grad, io64, c->stream);
         });
     }
-    if (!dL_dE) return fail(c, HQML_ERR_ARG, "dL_dE must be a device pointer");
-    int rc = run(c, HQML_K_OTHER, "dL/dE copy", [&] { return launch_copy_dlde(dL_dE, io64, B, c->dlde, c->stream); });
+    if ((rc = check_array(c, 6, dL_dE, (size_t)B * io, "dL_dE"))) return rc;
+    rc = run(c, HQML_K_OTHER, "dL/dE copy", [&] { return launch_copy_dlde(dL_dE, io64, B, c->dlde, c->stream); });
     if (rc) return rc;
     if (c->gbg) {
         c->saved_B = -1;   // the adjoint sweep un-computes the saved state in place
@@ -845,12 +892,16 @@ int train_impl(hqml_ctx *c, int B, const void *x, const void *theta, const void 
     if (!c) return HQML_ERR_ARG;
     c->err.clear();
     if (B < 1 || B > c->cfg.max_batch) return fail(c, HQML_ERR_ARG, "B must be in 1..max_batch");
-    if (!x || !theta || !y || !expz || !loss || !grad)
-        return fail(c, HQML_ERR_ARG, "x, theta, y, expz, loss and grad must be device pointers");
     hipError_t e = hipSetDevice(c->cfg.device);
     if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
-    c->saved_B = -1;
+    const size_t io = io64 ? sizeof(double) : sizeof(float), nq = (size_t)c->cfg.n_qubits;
+    const size_t np = (size_t)c->cfg.n_layers * nq * 3 * io;
     int rc;
+    if ((rc = check_array(c, 0, x, (size_t)B * nq * io, "x")) || (rc = check_array(c, 1, theta, np, "theta")) ||
+        (rc = check_array(c, 2, y, (size_t)B * io, "y")) || (rc = check_array(c, 3, expz, (size_t)B * io, "expz")) ||
+        (rc = check_array(c, 4, loss, io, "loss")) || (rc = check_array(c, 5, grad, np, "grad")))
+        return rc;
+    c->saved_B = -1;
     if (c->gbg) {
         if ((rc = gbg_forward_sweep(c, B, static_cast<const float *>(x), static_cast<const float *>(theta)))) return rc;
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {

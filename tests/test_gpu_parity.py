@@ -210,6 +210,42 @@ def test_null_pointer_arguments():
     ctx.close()
 
 
+def test_unusable_array_arguments():
+    """Arrays the kernels could not use are refused on the host with HQML_ERR_ARG:
+    pageable host memory, and an array running past the end of its allocation.  Each
+    case is a backward call before any forward, so a check that let the array through
+    would still queue nothing (the call then fails with HQML_ERR_STATE instead)."""
+    import ctypes
+    import qml_gradients_amd as hq
+    say("[gpu] unusable array arguments")
+    ctx = _ctx(14, 2, 2)
+    g = torch.zeros((2, 14, 3), device="cuda")
+    host = np.zeros((2, 14, 3), dtype=np.float32)
+    with pytest.raises(hq.HqmlError) as e:
+        hq.hqml_backward(ctx.handle, g.data_ptr(), host.ctypes.data)
+    assert e.value.status == hq.HQML_ERR_ARG and "pageable" in str(e.value)
+    # the last 8 bytes of an allocation cannot hold the 336-byte gradient
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipMemGetAddressRange.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_size_t),
+                                          ctypes.c_void_p]
+    blk = torch.empty(1 << 21, dtype=torch.uint8, device="cuda")
+    base, size = ctypes.c_void_p(), ctypes.c_size_t()
+    assert hip.hipMemGetAddressRange(ctypes.byref(base), ctypes.byref(size), ctypes.c_void_p(blk.data_ptr())) == 0
+    with pytest.raises(hq.HqmlError) as e:
+        hq.hqml_backward(ctx.handle, g.data_ptr(), base.value + size.value - 8)
+    assert e.value.status == hq.HQML_ERR_ARG and "needs 336 bytes" in str(e.value)
+    # pinned host memory passes the check (the call then stops at the missing forward)
+    pinned = torch.zeros((2, 14, 3)).pin_memory()
+    with pytest.raises(hq.HqmlError) as e:
+        hq.hqml_backward(ctx.handle, g.data_ptr(), pinned.data_ptr())
+    assert e.value.status == hq.HQML_ERR_STATE
+    # the context is still usable, with no error left behind by the refused calls
+    x, th, y = hqml_inputs.make_inputs(14, 2, 2, seed=5)
+    e_, loss, grad = (t.cpu().numpy() for t in ctx.train_step(*(torch.from_numpy(a) for a in (x, th, y))))
+    assert np.isfinite(loss).all() and np.isfinite(grad).all()
+    ctx.close()
+
+
 def _whole_circuit_obs(n):
     """A Pauli string for width n: Z_0 alone on even widths, else Z_0 Y_(n-1) with an X
     on qubit n // 2 (X/Y factors read partner amplitudes across the swizzled slots)."""
