@@ -57,6 +57,13 @@ struct StateIO<0> {
         *p = make_float2((float)re, (float)im);
     }
     template <typename R>
+    __device__ static __forceinline__ void load_temporal(const elem *p, R &re, R &im)
+    {
+        const float2 v = *p;
+        re = (R)v.x;
+        im = (R)v.y;
+    }
+    template <typename R>
     __device__ static __forceinline__ void store_nt(elem *p, R re, R im)
     {
         const unsigned long long u =
@@ -538,6 +545,19 @@ __device__ __forceinline__ void tile_retarget(TileCtx &c, const ViewDev &v, int 
     c.fixed2 = c.fx2t | tb;
 }
 
+// Grid slot of workgroup blk renumbered so that each XCD works on one contiguous range of
+// the grid's (sample, tile) pairs: the dispatcher places workgroup blk on XCD blk % 8, so
+// slot (blk % 8) * (G / 8) + blk / 8 keeps a sample on the same XCD from pass to pass and
+// part of a pass's output is read back from that XCD's L2 by the next pass.  A bijection
+// of 0..G-1 when 8 divides G; otherwise the plain order.  Used by the fp32 forward pass
+// and by the adjoint shapes of the CZ-chain plan (there with lambda loaded and stored
+// through L2); the CNOT-chain adjoint shapes, whose lambda moves through the chain's
+// index map, and the fp64 forward run slower with it and keep the plain order.
+__device__ __forceinline__ int xcd_slot(int blk, int G)
+{
+    return (G & 7) ? blk : (blk & 7) * (G >> 3) + (blk >> 3);
+}
+
 __device__ __forceinline__ void tile_ctx(TileCtx &c, const ViewDev &v, int T, int blk, int sample0)
 {
     const int tid = threadIdx.x;
@@ -593,7 +613,9 @@ __device__ __forceinline__ uint32_t roff(const TileCtx &c, int j)
 template <uint32_t ESZ>
 using TileOff = typename std::conditional<(ESZ <= 8), uint32_t, uint64_t>::type;
 
-template <int ST, typename R>
+// NT = false: ordinary loads (fp32 only), for lambda where the previous pass's output is
+// partly still in this XCD's L2.
+template <int ST, typename R, bool NT = true>
 __device__ __forceinline__ void load_l1(Tile<R> &t, const void *state, const TileCtx &c, uint64_t nelem)
 {
     using IO = StateIO<ST>;
@@ -604,12 +626,15 @@ __device__ __forceinline__ void load_l1(Tile<R> &t, const void *state, const Til
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
         const Off off = tb + (Off)roff(c, j) * esz;
-        IO::load(reinterpret_cast<const typename IO::elem *>(base + off), t.re[j], t.im[j]);
+        if constexpr (NT)
+            IO::load(reinterpret_cast<const typename IO::elem *>(base + off), t.re[j], t.im[j]);
+        else
+            IO::load_temporal(reinterpret_cast<const typename IO::elem *>(base + off), t.re[j], t.im[j]);
     }
 }
 
-// NT: non-temporal stores (fp32 lambda only: measured 1 % faster for the adjoint pass,
-// while the forward pass outputs, read by the very next pass, are slower with them).
+// NT: non-temporal stores (fp32 lambda of the CNOT-chain adjoint shapes; the forward pass
+// outputs, read by the very next pass, are slower with them).
 template <int ST, typename R, bool NT = false>
 __device__ __forceinline__ void store_l1(const Tile<R> &t, void *state, const TileCtx &c, uint64_t nelem)
 {
@@ -824,7 +849,8 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 4 : 2) void k_tile_fwd(T
     __shared__ R lds_stat[kSlots * 16 + 16];
     const ViewDev &v = *a.view;
     TileCtx c;
-    tile_ctx(c, v, a.T, blockIdx.x, a.sample0);
+    // fp64 compute (twice the bytes per sample) streams faster in the plain order
+    tile_ctx(c, v, a.T, sizeof(R) == 4 ? xcd_slot((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x, a.sample0);
     const uint64_t nelem = 1ull << a.n;
     Tile<R> t;
     if (a.flags & PF_INIT)
@@ -975,8 +1001,12 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
     R *e_part = static_cast<R *>(a.e_part);
     constexpr int LIO = kLamIO<R>;
     const ViewDev &v = *a.view;
+    // CZ-chain plan shapes: XCD-contiguous tiles, fp32 lambda read and written through L2
+    constexpr bool kXcd = SHAPE == BW_GENERAL || SHAPE == BW_INIT_GENERAL || SHAPE == BW_FUSED_LAST ||
+                          SHAPE == BW_FUSED_INIT || SHAPE == BW_L0;
+    constexpr bool kLamNT = LIO == 0 && !kXcd;
     TileCtx c;
-    tile_ctx(c, v, a.T, blockIdx.x, a.sample0);
+    tile_ctx(c, v, a.T, kXcd ? xcd_slot((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x, a.sample0);
     zero_stats(lds_stat);
     __syncthreads();
     const uint64_t nelem = 1ull << a.n;
@@ -1023,7 +1053,7 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
         if (a.flags & PF_SEED)
             seed_lambda(l, p, obs_mask_l1(c, a.obs));
         else
-            load_l1<LIO>(l, a.lam, c, nelem);
+            load_l1<LIO, R, kLamNT || LIO != 0>(l, a.lam, c, nelem);
         if constexpr (SHAPE == BW_GENERAL || SHAPE == BW_INIT_GENERAL) {
             const RotCoef<R> b1 = load_coef(rot_tf, a.n, a.rotB, c.q1, c.gm1);
             stats_visit<false>(p, l, 1, lds_stat, c.lane, c.w, (R)1);
@@ -1132,7 +1162,7 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
     if constexpr (SHAPE == BW_DROTB)
         store_l1_chain<LIO>(l, a.psi_out, c, nelem);   // the second lambda buffer (others read a.lam)
     else
-        store_l1<LIO, R, LIO == 0>(l, a.lam, c, nelem);
+        store_l1<LIO, R, kLamNT>(l, a.lam, c, nelem);
     flush_stats(lds_stat, static_cast<R *>(a.stat_part), c, a.T);
 }
 
