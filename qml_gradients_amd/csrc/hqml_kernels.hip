@@ -547,9 +547,10 @@ __device__ __forceinline__ void tile_retarget(TileCtx &c, const ViewDev &v, int 
 
 // Grid slot of workgroup blk renumbered so that each XCD works on one contiguous range of
 // the grid's (sample, tile) pairs: the dispatcher places workgroup blk on XCD blk % 8, so
-// slot (blk % 8) * (G / 8) + blk / 8 keeps a sample on the same XCD from pass to pass and
-// part of a pass's output is read back from that XCD's L2 by the next pass.  A bijection
-// of 0..G-1 when 8 divides G; otherwise the plain order.  Used by the fp32 forward pass
+// slot (blk % 8) * (G / 8) + blk / 8 keeps each sample on one XCD from pass to pass.  The
+// passes below run faster so although their HBM byte counts do not change (the gain is in
+// access latency, not traffic).  A bijection of 0..G-1 when 8 divides G; otherwise the
+// plain order.  Used by the fp32 forward pass
 // and by the adjoint shapes of the CZ-chain plan (there with lambda loaded and stored
 // through L2); the CNOT-chain adjoint shapes, whose lambda moves through the chain's
 // index map, and the fp64 forward run slower with it and keep the plain order.
@@ -613,8 +614,8 @@ __device__ __forceinline__ uint32_t roff(const TileCtx &c, int j)
 template <uint32_t ESZ>
 using TileOff = typename std::conditional<(ESZ <= 8), uint32_t, uint64_t>::type;
 
-// NT = false: ordinary loads (fp32 only), for lambda where the previous pass's output is
-// partly still in this XCD's L2.
+// NT = false: ordinary loads (fp32 only), used for lambda in the XCD-contiguous order,
+// where they measured faster than non-temporal loads.
 template <int ST, typename R, bool NT = true>
 __device__ __forceinline__ void load_l1(Tile<R> &t, const void *state, const TileCtx &c, uint64_t nelem)
 {
