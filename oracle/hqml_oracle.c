@@ -37,9 +37,11 @@
  *
  * Numbers are fp64 throughout; fp32 inputs are promoted by the caller.
  * Samples are independent; OpenMP runs them in parallel (or, for a batch too
- * small to fill the threads, runs the amplitude loops in parallel).  Per-sample
- * results are summed over the batch in sample order, so results do not depend
- * on the thread count.
+ * small to fill the threads, runs the amplitude loops in parallel).  Every sum
+ * over amplitudes has one fixed order that depends only on the number of
+ * amplitudes (sum_blocks below), whether its blocks run on one thread or many,
+ * and per-sample results are summed over the batch in sample order, so results
+ * do not depend on the thread count.
  */
 #include <complex.h>
 #include <math.h>
@@ -170,22 +172,43 @@ static void undo_entangler(cplx *psi, int n, int ent, int par)
     }
 }
 
-/* Re<lam| D_q |phi>, D a 2x2 matrix on qubit q (summed in index order). */
+/* Summation order of every sum over the 2^n amplitude indices: the range is cut
+ * into SUM_BLOCKS equal blocks of consecutive indices (one block below 2^12
+ * indices), each block is summed in index order, and the block sums are added
+ * in block order.  The order depends on n only; 'par' only lets the blocks run
+ * on several threads. */
+enum { SUM_BLOCKS = 64 };
+
+static int64_t sum_blocks(int64_t dim) { return dim >= 4096 ? SUM_BLOCKS : 1; }
+
+static double add_blocks(const double *part, int64_t nb)
+{
+    double acc = 0.0;
+    for (int64_t c = 0; c < nb; ++c) acc += part[c];
+    return acc;
+}
+
+/* Re<lam| D_q |phi>, D a 2x2 matrix on qubit q (fixed order, see sum_blocks). */
 static double re_braket_1q(const cplx *lam, const cplx *phi, int n, int q, gate2 d, int par)
 {
     const int64_t dim = (int64_t)1 << n;
     const int64_t bit = (int64_t)1 << q;
-    double acc = 0.0;
+    const int64_t nb = sum_blocks(dim), len = dim / nb;
+    double part[SUM_BLOCKS];
     (void)par;
-#pragma omp parallel for if (par) schedule(static) reduction(+ : acc)
-    for (int64_t i = 0; i < dim; ++i) {
-        if (i & bit) continue;
-        const int64_t j = i | bit;
-        const cplx di = d.m[0] * phi[i] + d.m[1] * phi[j];
-        const cplx dj = d.m[2] * phi[i] + d.m[3] * phi[j];
-        acc += creal(conj(lam[i]) * di) + creal(conj(lam[j]) * dj);
+#pragma omp parallel for if (par) schedule(static)
+    for (int64_t c = 0; c < nb; ++c) {
+        double acc = 0.0;
+        for (int64_t i = c * len; i < (c + 1) * len; ++i) {
+            if (i & bit) continue;
+            const int64_t j = i | bit;
+            const cplx di = d.m[0] * phi[i] + d.m[1] * phi[j];
+            const cplx dj = d.m[2] * phi[i] + d.m[3] * phi[j];
+            acc += creal(conj(lam[i]) * di) + creal(conj(lam[j]) * dj);
+        }
+        part[c] = acc;
     }
-    return acc;
+    return add_blocks(part, nb);
 }
 
 /* (-1)^(number of qubits of S set in basis state i): the eigenvalue of prod_{q in S} Z_q. */
@@ -214,11 +237,16 @@ static void apply_observable(const cplx *psi, cplx *out, int n, uint32_t zmask, 
 static double expect_obs(const cplx *psi, cplx *scratch, int n, uint32_t zmask, uint32_t xmask, int par)
 {
     const int64_t dim = (int64_t)1 << n;
+    const int64_t nb = sum_blocks(dim), len = dim / nb;
+    double part[SUM_BLOCKS];
     apply_observable(psi, scratch, n, zmask, xmask, par);
-    double acc = 0.0;
-#pragma omp parallel for if (par) schedule(static) reduction(+ : acc)
-    for (int64_t i = 0; i < dim; ++i) acc += creal(conj(psi[i]) * scratch[i]);
-    return acc;
+#pragma omp parallel for if (par) schedule(static)
+    for (int64_t c = 0; c < nb; ++c) {
+        double acc = 0.0;
+        for (int64_t i = c * len; i < (c + 1) * len; ++i) acc += creal(conj(psi[i]) * scratch[i]);
+        part[c] = acc;
+    }
+    return add_blocks(part, nb);
 }
 
 /* psi <- encoding followed by all L layers; |psi| must hold 2^n amplitudes. */
