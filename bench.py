@@ -8,16 +8,22 @@ fused forward pass, the fused adjoint passes and all reductions, with inputs
 already resident in device memory.  Prints one JSON line.
 
 Besides the throughput, the line carries:
-  roofline      the dominant kernel (the fused adjoint tile pass, bound by plain
-                fp32 ALU work): algorithmic flops per launch / its mean launch time,
-                from HIP events recorded around every launch in a separate
-                instrumented loop (batch chunking off), against the plain fp32 FMA
-                peak; also its HBM rate (algorithmic bytes / time vs 8 TB/s) and
-                "traffic", the measured HBM bytes per launch from rocprofv3 counters
-                when the kernel source still matches them;
+  roofline      the dominant kernel (the fused adjoint tile pass) against the
+                published HBM peak of 8 TB/s: its algorithmic state bytes per launch
+                (read the saved pass output, read and write lambda: 24 B per
+                amplitude and sample in fp32) / its mean launch time, from HIP
+                events recorded on the launch stream around every launch in a
+                separate instrumented loop (batch chunking off); "traffic" is the
+                measured HBM bytes per launch from rocprofv3 counters while the
+                kernel source still matches them;
+  roofline_alu  the same kernel's arithmetic rate (algorithmic flops per launch /
+                time) against a plain (non-packed) fp32 FMA peak derived from the
+                unit counts and clock, and as a fraction of the published 157.3
+                TFLOP/s (which counts packed FP32, excluded from this build);
   roofline_fwd  the fused forward tile pass (memory-bound) against 8 TB/s;
   cpu_baseline  the CPU oracle (fp64, gate by gate) timed on this host for a
-                bounded sample of the same workload.
+                bounded sample of the same workload, with the host's CPU model,
+                logical and physical core counts and the threads it used.
 """
 from __future__ import annotations
 
@@ -136,9 +142,36 @@ def traffic_record(kernel: str, workload: str, entangler: str = "cz"):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(workload: str, timeout_s: float = 60.0, entangler: str = "cz"):
-    import numpy as np  # noqa: F401
+def host_cpu():
+    """CPU model, logical CPUs this process may use, and physical cores (distinct
+    (package, core) pairs in /proc/cpuinfo)."""
+    model, cores = None, set()
+    phys = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and model is None:
+                    model = v
+                elif k == "physical id":
+                    phys = v
+                elif k == "core id":
+                    cores.add((phys, v))
+    except OSError:
+        pass
+    try:
+        logical = len(os.sched_getaffinity(0))
+    except AttributeError:
+        logical = os.cpu_count()
+    return {"cpu_model": model, "nproc": logical, "logical_cpus_host": os.cpu_count(),
+            "physical_cores": len(cores) or None}
 
+
+def cpu_baseline(workload: str, entangler: str = "cz"):
+    """The oracle's train step on one sample of the workload (its full circuit, fp64).
+    With one sample the oracle runs its OpenMP threads over the amplitude loops; the
+    whole batch of the workload would take tens of minutes of host time."""
     import hqml_inputs
     import oracle
     x, th, y = hqml_inputs.workload_inputs(workload)
@@ -147,9 +180,13 @@ def cpu_baseline(workload: str, timeout_s: float = 60.0, entangler: str = "cz"):
     t0 = time.perf_counter()
     o.train_step(x[:1], th, y[:1], entangler=1 if entangler == "cnot" else 0)
     dt = time.perf_counter() - t0
-    return {"value": 1.0 / dt, "unit": "samples/s", "cores": threads, "kind": "oracle",
-            "sample": f"1 of the {x.shape[0]} samples of {workload} (full circuit, fp64 train step), "
-                      f"{dt:.1f} s on {threads} OpenMP threads"}
+    out = {"value": round(1.0 / dt, 5), "unit": "samples/s", "cores": threads, "kind": "oracle",
+           "sample": f"1 of the {x.shape[0]} samples of {workload}: its full fp64 forward, loss and "
+                     f"gate-by-gate adjoint, {dt:.1f} s with {threads} OpenMP threads over the "
+                     f"amplitude loops (threads over samples need a batch of at least {threads})",
+           "parallel_over": "amplitudes", "threads": threads}
+    out.update(host_cpu())
+    return out
 
 
 def gate_by_gate(w, X, TH, Y, steps, entangler="cz"):
@@ -371,10 +408,13 @@ def main():
                 "hbm_achieved_GBps": round(hbm, 1), "hbm_frac": round(hbm / HBM_PEAK_GBPS, 4),
                 "frac_of_published_fp32_peak": round(achieved / FP32_PUBLISHED_TFLOPS, 4)}
 
-    # the CNOT plan's adjoint passes each rotate one qubit group (half the ALU work of a
-    # merged pass for the same bytes): reported against the HBM peak
-    roof_bwd = (roof_hbm(hq.HQML_K_BWD_PASS, bwd_b, "k_tile_bwd") if plan.get("cnot")
-                else roof_alu(hq.HQML_K_BWD_PASS, bwd_flops, bwd_b, "k_tile_bwd"))
+    # dominant kernel against the published HBM peak; its arithmetic rate beside it (the
+    # CNOT plan's adjoint passes each rotate one qubit group, so no ALU figure there)
+    roof_bwd = roof_hbm(hq.HQML_K_BWD_PASS, bwd_b, "k_tile_bwd")
+    roof_bwd_alu = None if plan.get("cnot") else roof_alu(hq.HQML_K_BWD_PASS, bwd_flops, bwd_b, "k_tile_bwd")
+    if roof_bwd_alu:
+        roof_bwd_alu["peak_basis"] = ("non-packed fp32 FMA: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz "
+                                      "(self-derived; packed FP32 is excluded from the build)")
     roof_fwd = roof_hbm(hq.HQML_K_FWD_PASS, fwd_b, "k_tile_fwd")
     step_bytes = fwd_b + bwd_b
     out = {
@@ -403,6 +443,7 @@ def main():
         "passes": {"fwd": len(plan["passes"]), "bwd": len(plan["passes"]) + len(plan["stats_only"]),
                    "per_layer": round(len(plan["passes"]) / w.n_layers, 3)},
         "roofline": roof_bwd if roof_bwd else roof_fwd,
+        "roofline_alu": roof_bwd_alu,
         "roofline_fwd": roof_fwd,
         "kernel_ms_per_step": {k: round(ms_k[i] / max(n_steps, 1), 3) for i, k in
                                enumerate(["fwd_pass", "bwd_pass", "small", "other"])},

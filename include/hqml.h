@@ -10,7 +10,8 @@
  *   applying Rx(theta[l][q][0]), Ry(theta[l][q][1]), Rz(theta[l][q][2]) to every
  *   qubit q followed by CZ(q, q+1) for q = 0..n-2; R_s(t) = exp(-i t s/2);
  *   qubit q is bit q of the amplitude index.  E_b = <psi_M|O|psi_M> with
- *   O = Z_0 by default, or a product of Z over any set of qubits (obs_mask).
+ *   O = Z_0 by default, or any Pauli string: Z on the qubits of obs_mask only,
+ *   X on those of obs_x_mask only and Y on those in both masks.
  *   The gradient is the adjoint-method gradient of section 1.2:
  *   dL/dtheta_j = Re<lambda_j| dU_j/dtheta_j |psi_{j-1}>, lambda_{j-1} = U_j^dag lambda_j,
  *   seeded with lambda_M = 2 (dL/dE_b) O psi_M, summed over the batch.
@@ -21,10 +22,14 @@
  *     x: [B][n] encoding angles; theta: [L][n][3] (Rx, Ry, Rz angle of qubit q
  *     in layer l); y: [B] labels; expz: [B]; loss: [1]; grad: [L][n][3];
  *     dL_dE: [B].  Each array must be device memory of the context's device
- *     (pinned host memory mapped into it also works) and fit inside its
- *     allocation; otherwise the call returns HQML_ERR_ARG before queuing
- *     anything (a NULL, pageable-host or too-short array).  A pointer that
- *     passed is remembered per argument, so only new buffers are queried.
+ *     (pinned host memory mapped into it also works) and fit inside the HIP
+ *     allocation that holds it; otherwise the call returns HQML_ERR_ARG before
+ *     queuing anything (a NULL, pageable-host or too-short array).  The range
+ *     check sees the runtime's allocation, not a caller's sub-allocation: a
+ *     tensor inside a larger segment of a caching allocator is checked against
+ *     the end of that segment.  A pointer that passed is remembered per
+ *     argument with its allocation's base and size; a repeat call re-reads
+ *     only the allocation range.
  *   - Work is queued on the context's stream and is asynchronous: outputs are
  *     valid once that stream has synchronised.  Argument errors are detected
  *     on the host before anything is queued.

@@ -77,6 +77,10 @@ struct hqml_ctx {
     char *saved = nullptr;       // saved states (n_saved buffers of max_batch samples)
     void *lam = nullptr;         // arrays below in the compute type
     void *lam_alt = nullptr;     // CNOT plan: second lambda buffer for the passes that scatter it
+    // The two lambda allocations.  'lam' / 'lam_alt' swap roles after every pass that
+    // scatters lambda; each backward sweep starts from lam_buf[0], where the
+    // observable pass writes its seed.
+    void *lam_buf[2] = {nullptr, nullptr};
     char *part = nullptr;
     void *e_part = nullptr;
     double *S = nullptr;
@@ -110,6 +114,8 @@ struct hqml_ctx {
     struct Checked {
         const void *p = nullptr;
         size_t bytes = 0;
+        const void *base = nullptr;   // the allocation that held it
+        size_t size = 0;
     };
     Checked checked[8];
     // instrumentation
@@ -142,13 +148,24 @@ int hip_fail(hqml_ctx *c, hipError_t e, const char *what)
 // Caller array argument `slot` (its index in the table above) must be memory this
 // context's kernels can read or write: device memory of its device, managed memory, or
 // pinned host memory mapped into the device; pageable host memory is refused, as is an
-// array that runs past the end of its allocation.  A pointer that passed is remembered
-// per slot, so a loop that reuses its buffers queries the runtime once.
+// array that runs past the end of the allocation that holds it (for a sub-allocator such
+// as PyTorch's caching allocator, the runtime's allocation is the whole segment).  A
+// pointer that passed is remembered per slot together with its allocation's base and
+// size; a later call with the same pointer re-reads only the allocation range (a cheap
+// host-side lookup), so a buffer freed and replaced by a different allocation at the
+// same address is checked again in full.
 int check_array(hqml_ctx *c, int slot, const void *p, size_t bytes, const char *name)
 {
     hqml_ctx::Checked &k = c->checked[slot];
-    if (p && p == k.p && bytes <= k.bytes) return HQML_OK;
     if (!p) return fail(c, HQML_ERR_ARG, std::string(name) + " is NULL");
+    if (p == k.p && bytes <= k.bytes) {
+        void *b = nullptr;
+        size_t sz = 0;
+        if (hipMemGetAddressRange(&b, &sz, const_cast<void *>(p)) == hipSuccess && b == k.base && sz == k.size)
+            return HQML_OK;
+        (void)hipGetLastError();
+        k = hqml_ctx::Checked{};
+    }
     hipPointerAttribute_t at;
     if (hipPointerGetAttributes(&at, p) != hipSuccess) {
         (void)hipGetLastError();   // the failed query leaves its error behind
@@ -171,6 +188,8 @@ int check_array(hqml_ctx *c, int slot, const void *p, size_t bytes, const char *
                                          std::to_string(room) + " from that address");
     k.p = p;
     k.bytes = bytes;
+    k.base = base;
+    k.size = size;
     return HQML_OK;
 }
 
@@ -442,6 +461,7 @@ int obs_pass(hqml_ctx *c, hipStream_t st, Span sp, int flags)
 {
     const Plan &pl = c->plan;
     TilePassArgs a = base_args(c);
+    a.lam = c->lam_buf[0];   // the buffer every backward sweep starts from
     a.view = c->views + pl.V;
     a.psi_in = pass_out(c, pl.n_fwd() - 1);
     a.rotA = a.diag = a.rotB = -1;
@@ -453,6 +473,11 @@ int obs_pass(hqml_ctx *c, hipStream_t st, Span sp, int flags)
 
 int tile_backward_sweep(hqml_ctx *c, hipStream_t st, Span sp, int start)
 {
+    // A CNOT-plan sweep swaps the lambda buffers once per scattering pass; the next
+    // chunk's sweep (its seed written by an observable pass queued before this sweep)
+    // must start from lam_buf[0] again.
+    c->lam = c->lam_buf[0];
+    c->lam_alt = c->lam_buf[1];
     const int last_flags = start == FUSED_LAST ? (PF_FUSED | PF_EMIT_E) : start == SEED_FROM_SAVED ? PF_SEED : 0;
     const Plan &pl = c->plan;
     const int P = pl.n_fwd();
@@ -718,6 +743,8 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     c->saved = static_cast<char *>(grab((size_t)c->ws.n_saved * c->ws.state_bytes));
     c->lam = grab(c->ws.lam_bytes);
     if (plan.cnot) c->lam_alt = grab(c->ws.lam_bytes);
+    c->lam_buf[0] = c->lam;
+    c->lam_buf[1] = c->lam_alt;
     c->part = static_cast<char *>(grab(c->ws.part_bytes));
     c->e_part = grab((size_t)B * plan.T * c->rb);
     c->S = static_cast<double *>(grab((size_t)B * Ln * 3 * 8));

@@ -100,11 +100,14 @@ __device__ __forceinline__ R row_sum16(R v)
     return v;
 }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+// (re, im) -> packed bf16 (re in the low half), rounded to nearest even by gfx950's
+// packed conversion (one instruction for both halves); a NaN stays a NaN.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float re, float im)
 {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+    const f2v v = {re, im};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2v));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h)

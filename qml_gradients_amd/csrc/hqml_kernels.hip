@@ -85,7 +85,7 @@ struct StateIO<1> {
     template <typename R>
     __device__ static __forceinline__ void store(elem *p, R re, R im)
     {
-        *p = f32_to_bf16_rne((float)re) | (f32_to_bf16_rne((float)im) << 16);
+        *p = f32x2_to_bf16x2((float)re, (float)im);
     }
 };
 

@@ -256,6 +256,31 @@ def test_cnot_tile_pauli_checkpoints_and_ragged_batch():
     assert_grad_close(outs[0][1][2], g_ref)
 
 
+def test_cnot_tile_pauli_batch_chunks_20_qubits():
+    """X/Y observable, checkpoint every layer and two batch chunks (the default with
+    checkpoints at 20 qubits, batch 4): every chunk's adjoint sweep must start from the
+    lambda buffer its observable pass wrote, although the previous chunk's sweep swapped
+    the two buffers an odd number of times (L = 2).  Bitwise equal to one chunk, and
+    equal to the oracle."""
+    import qml_gradients_amd as hq
+    n, L, B, zm, xm = 20, 2, 4, 0b1, (1 << 9) | 0b10
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=2160)
+    ctx = hq.Context(n, L, B, ckpt_block=1, obs_mask=zm, obs_x_mask=xm, entangler="cnot")
+    outs = []
+    for chunks in (2, 1):
+        say(f"[gpu] CNOT tile Pauli 20 qubits, {chunks} chunk(s)")
+        ctx.set_overlap(chunks)
+        outs.append([t.cpu().numpy() for t in ctx.train_step(*(torch.from_numpy(a) for a in (x, th, y)))])
+    ctx.close()
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert np.array_equal(a, b)
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y, zm, xm, entangler=1)
+    assert_e_close(outs[0][0], e_ref, n, L)
+    assert abs(float(outs[0][1][0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
+    assert_grad_close(outs[0][2], g_ref)
+
+
 def test_cnot_tile_bf16_storage():
     n, L, B = 16, 4, 2
     say("[gpu] CNOT tile bf16")
