@@ -20,41 +20,7 @@
 #include "hqml_internal.hpp"
 #include "hqml_plan.hpp"
 
-namespace hqml {
-// Type codes: io64 = caller arrays are double; r64 = compute in double; storage 0/1/2 =
-// fp32 / bf16 / fp64 saved states.
-// ent: 0 CZ chain; 1 CNOT chain, whole-circuit tables; 2 CNOT chain, tile tables
-hipError_t launch_prep(const void *theta, const void *x, int io64, int L, int n, int B, double *zyz,
-                       unsigned char *G, void *rot_tf, void *dw, double *H, void *init_u, int ent, int r64,
-                       hipStream_t s);
-hipError_t launch_tile_fwd(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s);
-hipError_t launch_tile_obs(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s);
-hipError_t launch_tile_bwd(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s);
-hipError_t launch_small(const SmallArgs &a, int B, int r64, hipStream_t s);
-hipError_t configure_small(size_t shm_bytes, int r64);
-hipError_t launch_ez_reduce(const void *e_part, int r64, int B, int T, const void *y, void *e_out, void *loss,
-                            int io64, double *dlde, double *e_work, double *chunks, hipStream_t s);
-hipError_t launch_copy_dlde(const void *src, int io64, int B, double *dlde, hipStream_t s);
-hipError_t launch_stats_reduce(const void *part, int r64, const int2 *map, int Bs, int b0, int Bc, int L, int n,
-                               int T, int pass_lo, int pass_hi, double *S, double *chunks, hipStream_t s);
-hipError_t launch_grad_reduce(const double *S, const double *H, const double *dlde, int B, int L, int n,
-                              void *grad, int io64, hipStream_t s);
-// gate-by-gate comparator (hqml_gbg.hip)
-hipError_t launch_gbg_zero(float2 *psi, int n, int B, hipStream_t s);
-hipError_t launch_gbg_rot(int gate, float2 *psi, int n, int B, int q, const float *ang, int ang_stride,
-                          hipStream_t s);
-hipError_t launch_gbg_cz(float2 *psi, float2 *lam, int n, int B, int q, hipStream_t s);
-hipError_t launch_gbg_cnot(float2 *psi, float2 *lam, int n, int B, int q, hipStream_t s);
-hipError_t launch_gbg_expz(const float2 *psi, int n, int B, uint32_t obs, uint32_t obs_x, float *e_part,
-                           hipStream_t s);
-hipError_t launch_gbg_seed(const float2 *psi, float2 *lam, int n, int B, uint32_t obs, uint32_t obs_x,
-                           hipStream_t s);
-hipError_t launch_gbg_rot_adj(int gate, float2 *psi, float2 *lam, int n, int B, int q, const float *ang,
-                              double *gpart, hipStream_t s);
-hipError_t launch_gbg_grad(const double *gpart, const double *dlde, int B, int n, int n_params, float *grad,
-                           hipStream_t s);
-hipError_t launch_gbg_copy(const float *src, int count, float *dst, hipStream_t s);
-}  // namespace hqml
+#include "hqml_host.hpp"
 
 using namespace hqml;
 
@@ -145,20 +111,15 @@ int hip_fail(hqml_ctx *c, hipError_t e, const char *what)
     return fail(c, HQML_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// Caller array argument `slot` (its index in the table above) must be memory this
-// context's kernels can read or write: device memory of its device, managed memory, or
-// pinned host memory mapped into the device; pageable host memory is refused, as is an
-// array that runs past the end of the allocation that holds it (for a sub-allocator such
-// as PyTorch's caching allocator, the runtime's allocation is the whole segment).  A
-// pointer that passed is remembered per slot together with its allocation's base and
+// Caller array argument `slot` (its index in the table above): see check_device_array.
+// A pointer that passed is remembered per slot together with its allocation's base and
 // size; a later call with the same pointer re-reads only the allocation range (a cheap
 // host-side lookup), so a buffer freed and replaced by a different allocation at the
 // same address is checked again in full.
 int check_array(hqml_ctx *c, int slot, const void *p, size_t bytes, const char *name)
 {
     hqml_ctx::Checked &k = c->checked[slot];
-    if (!p) return fail(c, HQML_ERR_ARG, std::string(name) + " is NULL");
-    if (p == k.p && bytes <= k.bytes) {
+    if (p && p == k.p && bytes <= k.bytes) {
         void *b = nullptr;
         size_t sz = 0;
         if (hipMemGetAddressRange(&b, &sz, const_cast<void *>(p)) == hipSuccess && b == k.base && sz == k.size)
@@ -166,26 +127,11 @@ int check_array(hqml_ctx *c, int slot, const void *p, size_t bytes, const char *
         (void)hipGetLastError();
         k = hqml_ctx::Checked{};
     }
-    hipPointerAttribute_t at;
-    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
-        (void)hipGetLastError();   // the failed query leaves its error behind
-        return fail(c, HQML_ERR_ARG, std::string(name) + " is not memory known to HIP");
-    }
-    const bool on_device = at.type == hipMemoryTypeDevice && at.device == c->cfg.device;
-    const bool mapped = (at.type == hipMemoryTypeHost || at.type == hipMemoryTypeManaged) && at.devicePointer == p;
-    if (!on_device && !mapped)
-        return fail(c, HQML_ERR_ARG, std::string(name) + " must be device memory of the context's device "
-                                     "(or pinned host memory), not pageable host memory");
-    void *base = nullptr;
+    std::string err;
+    const void *base = nullptr;
     size_t size = 0;
-    if (hipMemGetAddressRange(&base, &size, const_cast<void *>(p)) != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(c, HQML_ERR_ARG, std::string(name) + ": allocation range unknown");
-    }
-    const size_t room = static_cast<size_t>(static_cast<const char *>(base) + size - static_cast<const char *>(p));
-    if (bytes > room)
-        return fail(c, HQML_ERR_ARG, std::string(name) + " needs " + std::to_string(bytes) + " bytes, its allocation has " +
-                                         std::to_string(room) + " from that address");
+    const int rc = check_device_array(c->cfg.device, p, bytes, name, &err, &base, &size);
+    if (rc != HQML_OK) return fail(c, rc, err);
     k.p = p;
     k.bytes = bytes;
     k.base = base;
@@ -635,6 +581,71 @@ int gbg_grad(hqml_ctx *c, int B, float *grad)
 
 }  // namespace
 
+namespace hqml {
+
+int validate_config(const hqml_config *cfg, Plan *plan, std::string *err)
+{
+    return check_config(cfg, plan, err);
+}
+
+// Memory this library's kernels can read or write: device memory of `device`, managed
+// memory, or pinned host memory mapped into the device; pageable host memory is
+// refused, as is an array that runs past the end of the allocation that holds it (for a
+// sub-allocator such as PyTorch's caching allocator, the runtime's allocation is the
+// whole segment).
+int check_device_array(int device, const void *p, size_t bytes, const char *name, std::string *err,
+                       const void **base_out, size_t *size_out)
+{
+    if (!p) {
+        *err = std::string(name) + " is NULL";
+        return HQML_ERR_ARG;
+    }
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();   // the failed query leaves its error behind
+        *err = std::string(name) + " is not memory known to HIP";
+        return HQML_ERR_ARG;
+    }
+    const bool on_device = at.type == hipMemoryTypeDevice && at.device == device;
+    const bool mapped = (at.type == hipMemoryTypeHost || at.type == hipMemoryTypeManaged) && at.devicePointer == p;
+    if (!on_device && !mapped) {
+        *err = std::string(name) + " must be device memory of the context's device "
+                                   "(or pinned host memory), not pageable host memory";
+        return HQML_ERR_ARG;
+    }
+    void *base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void *>(p)) != hipSuccess) {
+        (void)hipGetLastError();
+        *err = std::string(name) + ": allocation range unknown";
+        return HQML_ERR_ARG;
+    }
+    const size_t room = static_cast<size_t>(static_cast<const char *>(base) + size - static_cast<const char *>(p));
+    if (bytes > room) {
+        *err = std::string(name) + " needs " + std::to_string(bytes) + " bytes, its allocation has " +
+               std::to_string(room) + " from that address";
+        return HQML_ERR_ARG;
+    }
+    if (base_out) *base_out = base;
+    if (size_out) *size_out = size;
+    return HQML_OK;
+}
+
+void set_thread_error(const std::string &msg)
+{
+    g_create_err = msg;
+}
+
+void config_observable(const hqml_config *cfg, const Plan &plan, uint32_t *z, uint32_t *x, bool *neg)
+{
+    const ObsString o = tile_observable(cfg, plan);
+    *z = o.z;
+    *x = o.x;
+    *neg = o.neg;
+}
+
+}  // namespace hqml
+
 extern "C" {
 
 size_t hqml_workspace_bytes(const hqml_config *cfg)
@@ -780,7 +791,7 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
         vs.push_back(ov);   // views[V]: the observable pass (unused without X/Y factors)
         e = hipMemcpy(c->views, vs.data(), vs.size() * sizeof(ViewDev), hipMemcpyHostToDevice);
     }
-    if (e == hipSuccess && plan.small) e = configure_small((size_t)2 * ((size_t)1 << plan.n) * 2 * c->rb, c->r64);
+    if (e == hipSuccess && plan.small) e = configure_small();
     if (e != hipSuccess) {
         const std::string m = std::string("workspace set-up: ") + hipGetErrorString(e);
         hqml_destroy(c);

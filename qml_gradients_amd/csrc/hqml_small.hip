@@ -857,14 +857,15 @@ __global__ __launch_bounds__(kSmallThreads) void k_small(SmallArgs a)
 
 namespace hqml {
 
-hipError_t configure_small(size_t shm_bytes, int r64)
+hipError_t configure_small()
 {
-    const void *f[2] = {r64 ? reinterpret_cast<const void *>(&k_small<double, 0>)
-                            : reinterpret_cast<const void *>(&k_small<float, 0>),
-                        r64 ? reinterpret_cast<const void *>(&k_small<double, 1>)
-                            : reinterpret_cast<const void *>(&k_small<float, 1>)};
+    constexpr int kMaxShm = 2 * (1 << kSmallMaxQubits) * (int)sizeof(float2);   // = 2 * 2^12 * sizeof(double2)
+    const void *f[4] = {reinterpret_cast<const void *>(&k_small<float, 0>),
+                        reinterpret_cast<const void *>(&k_small<float, 1>),
+                        reinterpret_cast<const void *>(&k_small<double, 0>),
+                        reinterpret_cast<const void *>(&k_small<double, 1>)};
     for (const void *k : f) {
-        const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm_bytes);
+        const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxShm);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
