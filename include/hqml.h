@@ -165,11 +165,33 @@ int hqml_backward_f64(hqml_ctx *ctx, const double *dL_dE, double *grad);
 int hqml_train_step_f64(hqml_ctx *ctx, int B, const double *x, const double *theta, const double *y,
                         double *expz, double *loss, double *grad);
 
+/* Allocation-free training step, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * computes exactly what hqml_train_step computes on a context created from *cfg (same
+ * kernels, same order, bitwise the same results), for the fused whole-circuit sizes only
+ * (n_qubits <= 13), and needs no context.  The caller passes inputs and outputs as for
+ * hqml_train_step (fp32 device arrays of cfg->device; 1 <= B <= cfg->max_batch); work is
+ * queued on cfg->stream.  Every intermediate (rotation tables, per-sample gradient
+ * statistics, sums) lives in one library-owned device buffer of
+ * HQML_NOALLOC_SCRATCH_BYTES per GPU, reserved when the library's code is loaded on that
+ * GPU and held until the process ends; the call allocates nothing.  A step needs
+ * 24 B per sample, layer and qubit (fp64 statistics), 145 B (fp32 compute) or 169 B
+ * (fp64 compute) per layer and qubit (tables), 16 B or 32 B per sample and qubit plus
+ * 24 B per sample, each of its ten parts rounded up to 256 B; a batch beyond the buffer
+ * returns HQML_ERR_ARG.  HQML_ERR_UNSUPPORTED for n_qubits > 13 or
+ * HQML_GATE_BY_GATE.  Errors are reported by hqml_last_error(NULL).
+ * All calls on one GPU share its buffer, which keeps the last call's contents: calls
+ * that overlap on one GPU (from two host threads, or queued on two streams whose work
+ * runs concurrently) race and give wrong results. */
+#define HQML_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+int hqml_train_step_noalloc(const hqml_config *cfg, int B, const float *x, const float *theta,
+                            const float *y, float *expz, float *loss, float *grad);
+
 /* Static text for a status code. */
 const char *hqml_status_str(int status);
 
 /* Text of the last error on ctx ("" if none); with ctx == NULL, the last error of
- * hqml_create on this thread. */
+ * hqml_create or hqml_train_step_noalloc on this thread. */
 const char *hqml_last_error(const hqml_ctx *ctx);
 
 /* ---- instrumentation (benchmarking; not needed for training) ---- */

@@ -89,6 +89,7 @@ def load() -> ctypes.CDLL:
         "hqml_plan_info": (i, [P, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i),
                               ctypes.POINTER(ctypes.c_size_t)]),
         "hqml_describe_plan": (ctypes.c_longlong, [cfgp, ctypes.c_char_p, ctypes.c_size_t]),
+        "hqml_train_step_noalloc": (i, [cfgp, i, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -100,7 +101,8 @@ def load() -> ctypes.CDLL:
 
 EXPORTED = ("hqml_workspace_bytes", "hqml_create", "hqml_destroy", "hqml_forward", "hqml_backward",
             "hqml_train_step", "hqml_forward_f64", "hqml_backward_f64", "hqml_train_step_f64", "hqml_status_str", "hqml_last_error", "hqml_set_timing",
-            "hqml_set_overlap", "hqml_kernel_times", "hqml_plan_info", "hqml_describe_plan")
+            "hqml_set_overlap", "hqml_kernel_times", "hqml_plan_info", "hqml_describe_plan",
+            "hqml_train_step_noalloc")
 
 
 def make_config(n_qubits, n_layers, max_batch, storage="fp32", ckpt_block=0, device=0, stream=None,
@@ -170,6 +172,13 @@ def hqml_backward_f64(ctx, dlde_ptr, grad_ptr) -> None:
 
 def hqml_train_step_f64(ctx, B, x_ptr, theta_ptr, y_ptr, expz_ptr, loss_ptr, grad_ptr) -> None:
     _check(ctx, load().hqml_train_step_f64(ctx, int(B), x_ptr, theta_ptr, y_ptr, expz_ptr, loss_ptr, grad_ptr))
+
+
+def hqml_train_step_noalloc(cfg: hqml_config, B, x_ptr, theta_ptr, y_ptr, expz_ptr, loss_ptr, grad_ptr) -> None:
+    lib = load()
+    rc = lib.hqml_train_step_noalloc(ctypes.byref(cfg), int(B), x_ptr, theta_ptr, y_ptr, expz_ptr, loss_ptr, grad_ptr)
+    if rc != HQML_OK:
+        raise HqmlError(rc, lib.hqml_last_error(None).decode())
 
 
 def hqml_set_timing(ctx, enable: bool) -> None:
