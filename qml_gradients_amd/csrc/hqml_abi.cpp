@@ -75,6 +75,10 @@ struct hqml_ctx {
     int gbg_blocks = 0;
     // saved-forward bookkeeping
     int saved_B = -1;
+    // Checkpointed plans keep the last block's pass outputs in the block buffers, which
+    // a backward sweep's recomputation of the other blocks overwrites: false once that
+    // has happened, so a later backward on the same saved forward recomputes the block.
+    bool tail_valid = false;
     std::string err;
     // caller arrays already found device-accessible and large enough, one slot per argument
     struct Checked {
@@ -874,6 +878,7 @@ int forward_impl(hqml_ctx *c, int B, const void *x, const void *theta, void *exp
         });
     } else {
         if ((rc = tile_forward_sweep(c, c->stream, Span{0, B, B}, false))) return rc;
+        c->tail_valid = true;
         if (c->obs_x && (rc = obs_pass(c, c->stream, Span{0, B, B}, PF_EMIT_E))) return rc;
         rc = run(c, HQML_K_OTHER, "E reduction", [&] {
             return launch_ez_reduce(c->e_part, c->r64, B, pl.T, nullptr, expz, nullptr, io64, nullptr, c->e_work,
@@ -882,6 +887,21 @@ int forward_impl(hqml_ctx *c, int B, const void *x, const void *theta, void *exp
     }
     if (rc) return rc;
     if (save_for_backward) c->saved_B = B;
+    return HQML_OK;
+}
+
+// The last checkpoint block's forward passes again, from the checkpoint before it, when
+// an earlier backward sweep has overwritten their saved outputs.
+int restore_tail_block(hqml_ctx *c, Span sp)
+{
+    const Plan &pl = c->plan;
+    if (pl.c == 0 || pl.nblocks < 2 || c->tail_valid) return HQML_OK;
+    const int P = pl.n_fwd();
+    for (int p = (pl.nblocks - 1) * pl.c; p < P; ++p) {
+        const int rc = fwd_pass(c, c->stream, sp, p, 0);
+        if (rc) return rc;
+    }
+    c->tail_valid = true;
     return HQML_OK;
 }
 
@@ -915,8 +935,10 @@ int backward_impl(hqml_ctx *c, const void *dL_dE, void *grad, int io64)
         const SmallArgs a = small_args(c, 1);
         rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->r64, c->stream); });
     } else {
+        if ((rc = restore_tail_block(c, Span{0, B, B}))) return rc;
         if (c->obs_x && (rc = obs_pass(c, c->stream, Span{0, B, B}, PF_SEED))) return rc;
         rc = tile_backward_sweep(c, c->stream, Span{0, B, B}, c->obs_x ? LAMBDA_READY : SEED_FROM_SAVED);
+        if (pl.c > 0 && pl.nblocks > 1) c->tail_valid = false;   // the sweep recomputed other blocks
     }
     if (rc) return rc;
     return run(c, HQML_K_OTHER, "gradient reduction", [&] {

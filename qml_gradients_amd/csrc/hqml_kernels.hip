@@ -384,6 +384,69 @@ __device__ __forceinline__ void stats_visit(const Tile<R> &p, const Tile<R> &l, 
 #undef HQML_STAT_BIT
 }
 
+// Sign of Z_{q-1} Z_{q+1} for the qubit q[m] of each register bit m (bit m set: -1), on
+// this thread's amplitudes.  'fixed' holds the thread's lane, wave and tile qubit values;
+// the view keeps the chain neighbours of a rotated qubit off the register bits of its
+// layout, so for those qubits the sign is the same on all 32 registers of the thread.
+__device__ __forceinline__ uint32_t nb_sign_mask(uint32_t fixed, const int *q, int n)
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int r = 0; r < 5; ++r) {
+        const int qq = q[r];
+        uint32_t nb = qq + 1 < n ? 1u << (qq + 1) : 0u;
+        if (qq > 0) nb |= 1u << (qq - 1);
+        m |= (uint32_t)(__builtin_popcount(fixed & nb) & 1) << r;
+    }
+    return m;
+}
+
+// Merged statistics of the 5 register bits: one set of sums gives both rotation layers
+// of a pass [Ry-layer la, D_la, Ry-layer lb].  Taken where qubit q of the group is at the
+// point after Ry_q(lb) (the pass output, with at most other group qubits un-rotated on
+// both states), for register bit m (qubit q):
+//   slots (13 + pos)*3 + {X,Y,Z}: S_s = Im<lam|s_q|psi>, layer lb's statistics as they are;
+//   slots pos*3 + {X,Y,Z}: T_s = Im<lam|Z_{q-1} Z_{q+1} s_q|psi>, from which flush_merged
+//     forms layer la's statistics (the neighbours' Z is a per-thread sign, nb bit m).
+// Layer la's statistics at its own point need no un-rotated psi: the group holds no
+// two chain neighbours, so only D_la and Ry_q(lb) separate that point from this one, and
+//   D X_q D^dag = Z_{q-1} Z_{q+1} (Re rho X_q - Im rho Y_q),
+//   D Y_q D^dag = Z_{q-1} Z_{q+1} (Im rho X_q + Re rho Y_q),  D Z_q D^dag = Z_q,
+// rho = f0 conj(f1) of qubit q in D_la, then Ry X Ry^dag = cos b X - sin b Z and
+// Ry Z Ry^dag = cos b Z + sin b X.
+template <bool L2, typename R>
+__device__ __forceinline__ void stats_visit_merged(const Tile<R> &p, const Tile<R> &l, R *lds_stat, int lane, int w,
+                                                   R corr, uint32_t nb)
+{
+    R wv[kRegs / 2];
+    R dz[5];
+    R d0 = 0;
+#pragma unroll
+    for (int k = 0; k < kRegs / 2; ++k) {
+        const R w0 = fmar(l.re[2 * k], p.im[2 * k], -l.im[2 * k] * p.re[2 * k]);
+        const R w1 = fmar(l.re[2 * k + 1], p.im[2 * k + 1], -l.im[2 * k + 1] * p.re[2 * k + 1]);
+        d0 += w0 - w1;
+        wv[k] = w0 + w1;
+    }
+    dz[0] = d0;
+    z_fold<1>(wv, dz);
+    R sx, sy;
+#define HQML_STAT_BIT(M)                                                                           \
+    {                                                                                              \
+        xy_stats<M>(p, l, sx, sy);                                                                 \
+        const int pos = L2 ? l2_pos(M) : l1_pos(M);                                                \
+        const R sg = ((nb >> (M)) & 1u) ? -corr : corr;                                            \
+        stat_out3(sx * corr, sy * corr, dz[M] * corr, lds_stat, (13 + pos) * 3, lane, w);          \
+        stat_out3(sx * sg, sy * sg, dz[M] * sg, lds_stat, pos * 3, lane, w);                       \
+    }
+    HQML_STAT_BIT(0)
+    HQML_STAT_BIT(1)
+    HQML_STAT_BIT(2)
+    HQML_STAT_BIT(3)
+    HQML_STAT_BIT(4)
+#undef HQML_STAT_BIT
+}
+
 // Per-thread factor tables of the diagonal D_l in layout L2:
 // D(i) = Plo[j & 3] * Phi[j >> 2] for register j of this thread.  dw[l][q] holds the
 // factor (f0, f1) of qubit q for bit value 0 / 1; CZ signs between register and
@@ -977,6 +1040,45 @@ __device__ __forceinline__ void flush_stats(const R *lds_stat, R *stat_part, con
     }
 }
 
+// flush_stats for a pass whose statistics were taken by stats_visit_merged: the sums of
+// the slots of each group position are combined into layer la's statistics (see
+// stats_visit_merged) with rho = f0 conj(f1) of qubit q in D_la (dw row la) and
+// cos b, sin b of Ry_q(lb) from its tan form k = tan(b/2) (rot_tf row lb).  lds_stat row 0
+// of every slot receives the slot's workgroup sum first.
+template <typename R>
+__device__ __forceinline__ void flush_merged(R *lds_stat, R *stat_part, const TileCtx &c, int T, const ViewDev &v,
+                                             const R *rot_tf, const R *dw, int n, int la, int lb)
+{
+    __syncthreads();
+    const int t = threadIdx.x;
+    R sum = 0;
+    if (t < kSlots) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) sum += lds_stat[t * 16 + k];
+    }
+    __syncthreads();
+    if (t < kSlots) lds_stat[t * 16] = sum;
+    __syncthreads();
+    if (t < kSlots) {
+        R out = sum;
+        const int pos = (t / 3) % 13, sel = t / 39, sig = t % 3;
+        if (t < 78 && sel == 0 && ((ldu(&v.group_mask) >> pos) & 1)) {
+            const int q = ldu(&v.perm[pos]);
+            const V4<R> f = ldu4(dw + ((size_t)la * n + q) * 4);
+            const R rr = f.x * f.z + f.y * f.w, ri = f.y * f.z - f.x * f.w;   // rho = f0 conj(f1)
+            const R k = ldu(rot_tf + ((size_t)lb * n + q) * 2);
+            const R inv = (R)1 / ((R)1 + k * k);
+            const R cb = ((R)1 - k * k) * inv, sb = (R)2 * k * inv;
+            const R tx = lds_stat[(pos * 3 + 0) * 16], ty = lds_stat[(pos * 3 + 1) * 16];
+            const R tz = lds_stat[(pos * 3 + 2) * 16];
+            const R sxl = lds_stat[((13 + pos) * 3 + 0) * 16], szl = lds_stat[((13 + pos) * 3 + 2) * 16];
+            const R u = cb * tx - sb * tz;
+            out = sig == 0 ? rr * u - ri * ty : sig == 1 ? ri * u + rr * ty : cb * szl + sb * sxl;
+        }
+        stat_part[((size_t)c.sample * T + c.tile) * kSlots + t] = out;
+    }
+}
+
 // Backward pass shapes (one kernel instance each, to keep register use per shape low).
 enum BwdShape : int {
     BW_GENERAL = 0,      // [rotA(la), D_la, rotB(la+1)]
@@ -1056,33 +1158,38 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
         else
             load_l1<LIO, R, kLamNT || LIO != 0>(l, a.lam, c, nelem);
         if constexpr (SHAPE == BW_GENERAL || SHAPE == BW_INIT_GENERAL) {
+            // Backward gate fusion with merged statistics: both layers of the pass from one
+            // set of sums per layout (stats_visit_merged), so psi is only brought into L2
+            // (its L1 group qubits un-rotated alongside lambda to keep the two states at one
+            // point) and never through D_la; lambda goes back through the whole pass.
+            const uint32_t nb1 = nb_sign_mask(c.fixed1, c.q1, a.n);
+            const uint32_t nb2 = nb_sign_mask(c.fixed2, c.q2, a.n);
             const RotCoef<R> b1 = load_coef(rot_tf, a.n, a.rotB, c.q1, c.gm1);
-            stats_visit<false>(p, l, 1, lds_stat, c.lane, c.w, (R)1);
+            stats_visit_merged<false>(p, l, lds_stat, c.lane, c.w, (R)1, nb1);
             rot_layer2<true>(p, l, b1);
             const R fb1 = b1.F;
             transpose(p, lds, c.a1, c.a2, true);
             transpose(l, lds, c.a1, c.a2, true);
-            stats_visit<true>(p, l, 1, lds_stat, c.lane, c.w, fb1 * fb1);
+            stats_visit_merged<true>(p, l, lds_stat, c.lane, c.w, fb1 * fb1, nb2);
             const RotCoef<R> b2 = load_coef(rot_tf, a.n, a.rotB, c.q2, c.gm2);
-            rot_layer2<true>(p, l, b2);
-            // both states carry scale fb = fb1 * b2.F; D^dagger removes it
-            apply_diag2(p, l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2), fb1 * b2.F);
-            stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
+            rot_layer<true>(l, b2);
+            // lambda carries scale fb1 * b2.F; D^dagger removes it
+            apply_diag_dag(l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2), fb1 * b2.F);
             if constexpr (SHAPE == BW_GENERAL) {
                 const RotCoef<R> a2 = load_coef(rot_tf, a.n, la, c.q2, c.gm2);
-                rot_layer2<true>(p, l, a2);
-                const R fa2 = a2.F;
-                transpose(p, lds, c.a1, c.a2, false);
+                rot_layer<true>(l, a2);
                 transpose(l, lds, c.a1, c.a2, false);
-                stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, fa2 * fa2);
                 const RotCoef<R> a1 = load_coef(rot_tf, a.n, la, c.q1, c.gm1);
                 rot_layer<true>(l, a1);
-                sl = fa2 * a1.F;
+                sl = a2.F * a1.F;
             } else {
-                transpose(p, lds, c.a1, c.a2, false);
                 transpose(l, lds, c.a1, c.a2, false);
-                stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
             }
+            if (sl != (R)1) scale_tile(l, sl);
+            store_l1<LIO, R, kLamNT>(l, a.lam, c, nelem);
+            flush_merged(lds_stat, static_cast<R *>(a.stat_part), c, a.T, v, rot_tf, static_cast<const R *>(a.dw), a.n,
+                         a.diag, a.rotB);
+            return;
         } else if constexpr (SHAPE == BW_DROTB) {
             const RotCoef<R> b1 = load_coef(rot_tf, a.n, a.rotB, c.q1, c.gm1);
             stats_visit<false>(p, l, 1, lds_stat, c.lane, c.w, (R)1);
@@ -1137,15 +1244,16 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
             flush_stats(lds_stat, static_cast<R *>(a.stat_part), c, a.T);
             return;
         } else if constexpr (SHAPE == BW_ROTA) {
-            const RotCoef<R> a1 = load_coef(rot_tf, a.n, la, c.q1, c.gm1);
-            const RotCoef<R> a2 = load_coef(rot_tf, a.n, la, c.q2, c.gm2);
+            // statistics of both layouts at the pass output; psi is not un-rotated
             stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
-            rot_layer2<true>(p, l, a1);
             transpose(p, lds, c.a1, c.a2, true);
             transpose(l, lds, c.a1, c.a2, true);
-            stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, a1.F * a1.F);
+            stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
+            const RotCoef<R> a2 = load_coef(rot_tf, a.n, la, c.q2, c.gm2);
             rot_layer<true>(l, a2);
             transpose(l, lds, c.a1, c.a2, false);
+            const RotCoef<R> a1 = load_coef(rot_tf, a.n, la, c.q1, c.gm1);
+            rot_layer<true>(l, a1);
             sl = a1.F * a2.F;
         } else {   // BW_L0
             stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, (R)1);

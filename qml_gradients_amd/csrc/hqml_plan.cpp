@@ -19,87 +19,116 @@ namespace {
 
 constexpr int kLowQubits = 4;   // positions 0..3 always hold qubits 0..3 (128-byte runs)
 
-// Local positions a view may rotate, in fill order for a view's own high qubits.
-const int kHighRotPos[8] = {4, 5, 6, 7, 8, 9, 10, 11};
+// Register positions of the two layouts (see hqml_internal.hpp): L1 rotates positions
+// 4..8, L2 positions 0, 1, 9, 10, 11.
+constexpr uint32_t kL1Regs = 0x1F0u;
+constexpr uint32_t kL2Regs = 0xE03u;
 
+// Whether qubits a and b are neighbours in the CZ chain.
+bool adjacent(int a, int b) { return a >= 0 && b >= 0 && (a - b == 1 || b - a == 1); }
+
+// Check a view's placement: (a) no qubit at a register position of a layout is a chain
+// neighbour of a rotated qubit at a register position of the same layout (so the sign of
+// Z_{q-1} Z_{q+1} is constant over a thread's registers wherever the statistics of a
+// rotated qubit q are taken); (b) no qubit at L2 positions 0, 1 neighbours one at 9..11
+// (the diagonal's per-thread factor tables handle CZ signs within those two sets only).
+bool view_ok(const int *perm, uint32_t group)
+{
+    for (uint32_t regs : {kL1Regs, kL2Regs})
+        for (int a = 0; a < kTileBits; ++a) {
+            if (!((regs >> a) & 1u) || !((group >> a) & 1u)) continue;
+            for (int b = 0; b < kTileBits; ++b)
+                if (b != a && ((regs >> b) & 1u) && adjacent(perm[a], perm[b])) return false;
+        }
+    for (int a : {0, 1})
+        for (int b : {9, 10, 11})
+            if (adjacent(perm[a], perm[b])) return false;
+    return true;
+}
+
+// Views.  Qubit q is rotated by view q mod V, so no two chain neighbours share a view:
+// the rotations of a pass never touch the neighbours of the qubits it rotates, and the
+// backward pass can take both of its layers' statistics from one point (the merged
+// statistics of the adjoint kernel).  V = max(2, ceil((n - 4) / 8)) views keep at most
+// 8 high qubits (>= 4) and 2 low qubits per view on the 10 rotatable positions.  A
+// view's rotated low qubits sit at positions 0, 1 (the other low qubits at 2, 3 or as
+// fillers of 0, 1), its rotated high qubits at 4..8 (L1 registers) and 9..11 (L2
+// registers), and the remaining register positions, position 12 and the tile bits take
+// the other qubits, subject to view_ok.
 bool build_views(int n, Plan &p, std::string *err)
 {
     const int nhigh = n - kLowQubits;
-    int V = std::max(2, (nhigh + 7) / 8);
+    const int V = std::max(2, (nhigh + 7) / 8);
     p.V = V;
     p.T = 1 << (n - kTileBits);
-    // Balance rotations per view: views 0 and 1 also rotate two low qubits each.
-    std::vector<int> load(V, 0), hcount(V, 0);
-    load[0] = 2;
-    load[1] = 2;
-    for (int k = 0; k < nhigh; ++k) {
-        int best = -1;
-        for (int v = 0; v < V; ++v) {
-            if (hcount[v] >= 8) continue;
-            if (best < 0 || load[v] < load[best]) best = v;
-        }
-        if (best < 0) {
-            if (err) *err = "no view has room for another high qubit";
-            return false;
-        }
-        ++hcount[best];
-        ++load[best];
-    }
-    // Contiguous ranges of high qubits per view, in view order.
-    std::vector<std::vector<int>> own(V);
-    int next = kLowQubits;
-    for (int v = 0; v < V; ++v)
-        for (int k = 0; k < hcount[v]; ++k) own[v].push_back(next++);
-
     p.views.assign(V, ViewDev{});
     for (int v = 0; v < V; ++v) {
+        std::vector<int> rlow, rhigh, olow, ohigh;
+        for (int q = 0; q < n; ++q) {
+            const bool mine = q % V == v;
+            if (q < kLowQubits) (mine ? rlow : olow).push_back(q);
+            else (mine ? rhigh : ohigh).push_back(q);
+        }
+        if (rlow.size() > 2 || rhigh.size() > 8) {
+            if (err) *err = "a view has more rotated qubits than rotatable positions";
+            return false;
+        }
+        std::sort(ohigh.rbegin(), ohigh.rend());   // fillers: highest first
+        const int kh = (int)rhigh.size();
+        bool placed = false;
+        int perm[kTileBits];
+        uint32_t group = 0;
+        // Try every choice of the rotated high qubits that go to L2 (highest first), and
+        // every low filler order, until the placement passes view_ok.
+        const int nl2_min = std::max(0, kh - 5), nl2_max = std::min(3, kh);
+        for (int nl2 = nl2_min; nl2 <= nl2_max && !placed; ++nl2) {
+            std::vector<int> pick(kh, 0);
+            std::fill(pick.end() - nl2, pick.end(), 1);
+            do {
+                std::vector<int> lo2 = olow;
+                std::sort(lo2.begin(), lo2.end());
+                do {
+                    for (int i = 0; i < kTileBits; ++i) perm[i] = -1;
+                    group = 0;
+                    std::vector<int> low = rlow;
+                    for (int q : lo2) low.push_back(q);
+                    for (int i = 0; i < kLowQubits; ++i) perm[i] = low[i];
+                    for (size_t i = 0; i < rlow.size(); ++i) group |= 1u << i;
+                    int p1 = 4, p2 = 9;
+                    for (int k = 0; k < kh; ++k) {
+                        const int pos = pick[k] ? p2++ : p1++;
+                        perm[pos] = rhigh[k];
+                        group |= 1u << pos;
+                    }
+                    std::vector<int> cand = ohigh;
+                    bool ok = true;
+                    for (int pos = 4; pos < kTileBits && ok; ++pos) {
+                        if (perm[pos] >= 0) continue;
+                        const uint32_t regs = ((kL1Regs >> pos) & 1u) ? kL1Regs : ((kL2Regs >> pos) & 1u) ? kL2Regs : 0u;
+                        ok = false;
+                        for (size_t ci = 0; ci < cand.size(); ++ci) {
+                            bool clash = false;
+                            for (int b = 0; b < kTileBits && regs; ++b)
+                                if (((regs >> b) & 1u) && ((group >> b) & 1u) && adjacent(cand[ci], perm[b])) clash = true;
+                            if (!clash) {
+                                perm[pos] = cand[ci];
+                                cand.erase(cand.begin() + (long)ci);
+                                ok = true;
+                                break;
+                            }
+                        }
+                    }
+                    if (ok && view_ok(perm, group)) placed = true;
+                } while (!placed && std::next_permutation(lo2.begin(), lo2.end()));
+            } while (!placed && std::next_permutation(pick.begin(), pick.end()));
+        }
+        if (!placed) {
+            if (err) *err = "no tile view keeps the chain neighbours of its rotated qubits off its register positions";
+            return false;
+        }
         ViewDev &d = p.views[v];
         std::memset(&d, 0, sizeof(d));
         for (int i = 0; i < 32; ++i) d.inv[i] = -1;
-        int perm[kTileBits];
-        for (int i = 0; i < kTileBits; ++i) perm[i] = -1;
-        uint32_t group = 0;
-        // low positions
-        if (v == 1) {
-            perm[0] = 2; perm[1] = 3; perm[2] = 0; perm[3] = 1;
-        } else {
-            perm[0] = 0; perm[1] = 1; perm[2] = 2; perm[3] = 3;
-        }
-        if (v <= 1) group |= 0x3u;   // positions 0,1 rotated by views 0 and 1
-        // own high qubits at rotatable high positions
-        for (size_t k = 0; k < own[v].size(); ++k) {
-            perm[kHighRotPos[k]] = own[v][k];
-            group |= 1u << kHighRotPos[k];
-        }
-        // fillers: other high qubits, highest first (qubit 4 last)
-        std::vector<int> cand;
-        for (int q = n - 1; q >= kLowQubits; --q)
-            if (std::find(own[v].begin(), own[v].end(), q) == own[v].end()) cand.push_back(q);
-        size_t ci = 0;
-        for (int pos = 4; pos < kTileBits; ++pos) {
-            if (perm[pos] >= 0) continue;
-            if (ci >= cand.size()) {
-                if (err) *err = "not enough qubits to fill a tile view";
-                return false;
-            }
-            perm[pos] = cand[ci++];
-        }
-        // The diagonal's per-thread factor tables need: if qubit 3 sits at an L2 register
-        // position 0/1, qubit 4 is not at the other L2 register positions 9..11.
-        auto at = [&](int q) { for (int i = 0; i < kTileBits; ++i) if (perm[i] == q) return i; return -1; };
-        const int p3 = at(3), p4 = at(4);
-        if ((p3 == 0 || p3 == 1) && p4 >= 9 && p4 <= 11) {
-            const bool in_group = (group >> p4) & 1u;
-            int swap_with = -1;
-            for (int pos : {4, 5, 6, 7, 8, 12}) {
-                if (((group >> pos) & 1u) == (in_group ? 1u : 0u)) { swap_with = pos; break; }
-            }
-            if (swap_with < 0) {
-                if (err) *err = "cannot place qubit 4 away from the L2 register positions";
-                return false;
-            }
-            std::swap(perm[p4], perm[swap_with]);
-        }
         for (int i = 0; i < kTileBits; ++i) {
             d.perm[i] = perm[i];
             d.inv[perm[i]] = i;

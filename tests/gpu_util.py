@@ -1,9 +1,12 @@
-"""Helpers shared by the GPU parity tests."""
+"""Helpers shared by the GPU parity tests: parity bounds and the stored oracle values."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 def say(*a):
@@ -37,3 +40,55 @@ def assert_grad_close(g_gpu, g_ref, atol=1e-4):
     g_gpu = np.asarray(g_gpu, dtype=np.float64)
     err = np.abs(g_gpu - g_ref)
     assert err.max() <= atol, f"gradient mismatch: max abs err {err.max():.3e} (bound {atol})"
+
+
+def assert_grad_rel(g_gpu, g_ref, rel, what="gradient"):
+    """The bound that binds where gradients are small (deep random circuits): the
+    largest error is at most `rel` times the largest reference entry."""
+    g_gpu = np.asarray(g_gpu, dtype=np.float64)
+    err = np.abs(g_gpu - g_ref).max()
+    scale = np.abs(g_ref).max()
+    assert err <= rel * scale, f"{what}: max|dg| {err:.3e} > {rel:g} x max|g_ref| {scale:.3e}"
+    return err / scale
+
+
+# ---- bf16 storage: a bound from the rounding of the stored states ----
+
+BF16_HALF_ULP = 2.0 ** -9   # bf16 keeps 8 significant bits: round-to-nearest error <= 2^-9 relative
+
+
+def bf16_sigma(n, passes, grad=False):
+    """rms error of E (grad=False) or of a gradient entry (grad=True) caused by storing
+    every pass output in bf16.
+
+    E: each of the `passes` roundings multiplies every amplitude by (1 + e_i), e_i uniform
+    in [-2^-9, 2^-9] (rms 2^-9 / sqrt 3); carried to the end by the rest of the circuit,
+    a rounding moves E = <psi|O|psi> by 2 Re<phi|delta> with ||phi|| = 1, whose rms is
+    2 (2^-9 / sqrt 3) sqrt(sum_i |phi_i|^2 |psi_i|^2), about 2 (2^-9 / sqrt 3) 2^(-n/2)
+    for spread states; independent roundings add in quadrature.
+
+    Gradient entry: a statistic Im<lam|s|psi> (||lam|| = 2 for a one-hot dL/dE) sees the
+    same rounding twice, through the stored psi it reads and through lambda, which the
+    adjoint seeds from the rounded final state (a factor sqrt 2), and an entry combines
+    the three Pauli statistics of its qubit through the gradient map, |H| <= 1 (a factor
+    up to sqrt 3): sigma_grad = sqrt 6 sigma_E."""
+    s = 2.0 * BF16_HALF_ULP / np.sqrt(3.0) * np.sqrt(passes) * 2.0 ** (-n / 2)
+    return s * np.sqrt(6.0) if grad else s
+
+
+def bf16_bound(n, passes, k=5.0, grad=False):
+    """Absolute bound k sigma (k = 5) on E (or on every gradient entry, grad=True) in
+    bf16 storage, orders of magnitude inside the stated 2e-2 envelope at the full
+    workload sizes."""
+    return k * bf16_sigma(n, passes, grad)
+
+
+def golden_sample(name, b):
+    """Stored oracle values of sample b of a workload's first batch: (E [1], grad
+    [L][n][3]) for dL/dE_b = 1 (written by tests/golden/make_golden.py from the oracle)."""
+    path = os.path.join(GOLDEN, f"{name}_golden.npz")
+    if not os.path.exists(path):
+        return None
+    d = np.load(path)
+    k = int(np.nonzero(d["samples"] == b)[0][0])
+    return d["expz"][k:k + 1], d["grad"][k]

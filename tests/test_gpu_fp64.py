@@ -9,19 +9,17 @@ Bounds: full fp64 mode, |dE| <= 1e-10 and |d grad| <= 1e-10 (absolute), six orde
 below the fp32 bounds and far above fp64 rounding over these circuit depths;
 fp32-storage mode, the fp32 bounds (its states are rounded to fp32 every pass).
 """
-import os
 
 import numpy as np
 import pytest
 
 import hqml_inputs
 import oracle
-from gpu_util import assert_e_close, assert_grad_close, say
+from gpu_util import assert_e_close, assert_grad_close, golden_sample, say
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 TOL64 = 1e-10
 
 
@@ -81,14 +79,13 @@ def test_fp64_headline_workload_sampled():
     ctx = _ctx(w.n_qubits, w.n_layers, B, storage="fp64")
     e = ctx.forward(X, TH).cpu().numpy()
     for b in (0, 31):
-        path = os.path.join(GOLDEN, f"{name}_b0_s{b}.npz")
-        if not os.path.exists(path):
+        ref = golden_sample(name, b)
+        if ref is None:
             pytest.skip("golden values not generated (python tests/golden/make_golden.py full)")
-        ref = np.load(path)
         oh = np.zeros(B)
         oh[b] = 1.0
         g = ctx.backward(torch.from_numpy(oh)).cpu().numpy()
-        _check64(e[b:b + 1], g, ref["expz"], ref["grad"])
+        _check64(e[b:b + 1], g, ref[0], ref[1])
     ctx.close()
 
 

@@ -5,19 +5,17 @@ gate by gate, un-computing psi in place; it must give the same E, loss and
 gradient as the oracle (same tolerances as the fused path: <Z_0> within 1e-5
 relative to max(|E|, 2^(-n/2)), gradients within 1e-4 absolute).
 """
-import os
 
 import numpy as np
 import pytest
 
 import hqml_inputs
 import oracle
-from gpu_util import assert_e_close, assert_grad_close, say
+from gpu_util import assert_e_close, assert_grad_close, golden_sample, say
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 def _ctx(n, L, B, **kw):
@@ -80,14 +78,13 @@ def test_gate_by_gate_headline_matches_fused_and_oracle():
     assert abs(float(loss[0]) - float(loss_f[0])) <= 1e-5
     assert_grad_close(g, g_f.astype(np.float64), atol=2e-4)
     for b in (0, 31):
-        path = os.path.join(GOLDEN, f"{name}_b0_s{b}.npz")
-        if not os.path.exists(path):
+        ref = golden_sample(name, b)
+        if ref is None:
             pytest.skip("golden values not generated (python tests/golden/make_golden.py full)")
-        ref = np.load(path)
         eb = ctx.forward(X, TH).cpu().numpy().astype(np.float64)
-        assert_e_close(eb[b:b + 1], ref["expz"], n, L)
+        assert_e_close(eb[b:b + 1], ref[0], n, L)
         oh = np.zeros(B, dtype=np.float32)
         oh[b] = 1.0
         gb = ctx.backward(torch.from_numpy(oh)).cpu().numpy()
-        assert_grad_close(gb, ref["grad"])
+        assert_grad_close(gb, ref[1])
     ctx.close()

@@ -1,31 +1,38 @@
 """GPU parity at the full workload sizes, checkpointing, bf16 storage, 29 qubits.
 
-Full-size references are single samples computed by the CPU oracle and stored
-under tests/golden/ by ``tests/golden/make_golden.py full`` (it calls only the
-oracle).  The GPU runs the whole batch in the configuration the benchmark times;
-per-sample gradients are read back with a one-hot dL/dE, which the backward
-pass accepts for any upstream derivative.
-"""
-import os
+Full-size references are per-sample oracle values (E_b and the gradient of E_b
+alone) stored under tests/golden/ by ``tests/golden/make_golden.py full`` (it calls
+only the oracle): every sample of the 20-qubit 100-layer batch, and samples 0, 17,
+42, 59 and 84 of the 1000-layer set.  The GPU runs the whole batch in the
+configuration the benchmark times; a single sample's gradient is read back with a
+one-hot dL/dE, which the backward pass accepts for any upstream derivative.
 
+Bounds: <Z_0> within the 1e-5-relative bound (tol_e); gradients within 1e-4
+absolute and, where that does not bind (deep-circuit gradients are ~1e-3), within
+1e-3 of the largest reference entry; bf16 storage within 5 sigma of the rounding
+model bf16_sigma (and the stated 2e-2 envelope).  Each test prints the errors as
+ratios of its bounds.
+"""
 import numpy as np
 import pytest
 
 import hqml_inputs
 import oracle
-from gpu_util import assert_e_close, assert_grad_close, say
+from gpu_util import (assert_e_close, assert_grad_close, assert_grad_rel, bf16_bound, golden_sample, say,
+                      tol_e)
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+GRAD_REL = 1e-3   # fp32 storage: max|dg| <= GRAD_REL * max|g_ref|
 
 
-def _golden(name):
-    path = os.path.join(GOLDEN, name)
-    if not os.path.exists(path):
-        pytest.skip(f"{name} not generated (python tests/golden/make_golden.py full)")
-    return np.load(path)
+def _golden(name, b):
+    g = golden_sample(name, b)
+    if g is None:
+        pytest.skip(f"{name} golden values not generated (python tests/golden/make_golden.py full)")
+    return g
 
 
 def _ctx(n, L, B, **kw):
@@ -39,45 +46,81 @@ def _one_hot(B, b):
     return torch.from_numpy(w)
 
 
-def test_headline_workload_sampled_parity():
-    """hea20q100l, batch 32, every pass output kept: samples 0 and 31 vs the oracle;
-    train_step's gradient vs forward + backward with dL/dE = 2 (E - y) / B."""
+def test_headline_train_step_full_batch_parity():
+    """hea20q100l, batch 32, every pass output kept (the benchmark's configuration):
+    train_step's E for all 32 samples, the loss and the 6,000-entry batch gradient
+    against the oracle.  The reference batch gradient is sum_b 2 (E_b - y_b) / B
+    times the stored per-sample gradients; the reference loss is mean (E_b - y_b)^2."""
     name = "hea20q100l"
     w = hqml_inputs.WORKLOADS[name]
     x, th, y = hqml_inputs.workload_inputs(name)
     B, n, L = w.batch, w.n_qubits, w.n_layers
-    say(f"[gpu] {name} sampled parity")
+    refs = [_golden(name, b) for b in range(B)]
+    e_ref = np.concatenate([r[0] for r in refs])
+    G = np.stack([r[1] for r in refs])
+    yd = y.astype(np.float64)
+    dl = 2.0 * (e_ref - yd) / B
+    g_ref = np.tensordot(dl, G, axes=1)
+    loss_ref = float(np.mean((e_ref - yd) ** 2))
+    say(f"[gpu] {name} full-batch train step parity")
     ctx = _ctx(n, L, B)
-    X, TH, Y = (torch.from_numpy(a) for a in (x, th, y))
-    e = ctx.forward(X, TH).cpu().numpy().astype(np.float64)
-    for b in (0, 31):
-        ref = _golden(f"{name}_b0_s{b}.npz")
-        assert_e_close(e[b:b + 1], ref["expz"], n, L)
-        g = ctx.backward(_one_hot(B, b)).cpu().numpy()
-        assert_grad_close(g, ref["grad"])
-    e2, loss, g_ts = ctx.train_step(X, TH, Y)
-    e2 = e2.cpu().numpy().astype(np.float64)
-    assert np.max(np.abs(e2 - e)) <= 1e-6
-    dl = (2.0 * (e2 - y) / B).astype(np.float32)
-    ctx.forward(X, TH)
-    g_fb = ctx.backward(torch.from_numpy(dl)).cpu().numpy()
-    assert np.max(np.abs(g_ts.cpu().numpy() - g_fb)) <= 1e-6
-    assert abs(float(loss.cpu()[0]) - np.mean((e2 - y) ** 2)) <= 1e-6
+    e, loss, g = (t.cpu().numpy().astype(np.float64) for t in ctx.train_step(*(torch.from_numpy(a) for a in (x, th, y))))
+    te = tol_e(e_ref, n, L)
+    # d loss = (1/B) sum 2 (E - y) dE (+ dE^2): bounded through the E bounds
+    tl = float(np.sum(2.0 * np.abs(e_ref - yd) * te + te ** 2) / B) + 1e-7 * loss_ref
+    say(f"  E: max|dE| {np.abs(e - e_ref).max():.2e}, worst ratio to bound {np.max(np.abs(e - e_ref) / te):.3f}")
+    say(f"  loss: |dloss| {abs(loss[0] - loss_ref):.2e} (bound {tl:.2e})")
+    assert_e_close(e, e_ref, n, L)
+    assert abs(loss[0] - loss_ref) <= tl
+    assert_grad_close(g, g_ref)
+    r = assert_grad_rel(g, g_ref, GRAD_REL, "batch gradient")
+    say(f"  batch gradient: max|dg| {np.abs(g - g_ref).max():.2e}, max|g_ref| {np.abs(g_ref).max():.2e}, "
+        f"ratio {r:.2e} (bound {GRAD_REL:g})")
+    # the forward / backward split reads single samples back with a one-hot dL/dE
+    # (the forward-only sweep sums E in its own last pass, not in the fused one)
+    e2 = ctx.forward(*(torch.from_numpy(a) for a in (x, th))).cpu().numpy().astype(np.float64)
+    assert_e_close(e2, e_ref, n, L)
+    for b in (0, 13, 31):
+        gb = ctx.backward(_one_hot(B, b)).cpu().numpy()
+        assert_grad_close(gb, G[b])
+        r = assert_grad_rel(gb, G[b], GRAD_REL, f"sample {b} gradient")
+        say(f"  sample {b}: max|dg|/max|g_ref| {r:.2e}")
     ctx.close()
 
 
-def test_deep_checkpointed_workload_sampled_parity():
-    """hea20q1000l, batch 60, checkpoint every 20 layers: sample 0 of the first batch."""
-    name = "hea20q1000l"
+DEEP_SAMPLES = (0, 17, 42, 59, 84)
+
+
+@pytest.mark.parametrize("storage", ["fp32", "bf16"])
+def test_deep_checkpointed_workload_sampled_parity(storage):
+    """hea20q1000l (checkpoint every 20 layers): fp32 storage at batch 60, bf16 storage
+    at batch 85, each the first mini-batch of the 1000-sample set.  The sampled
+    entries (0, 17, 42, 59 and 84 where the batch holds them) against the oracle."""
+    name = "hea20q1000l" if storage == "fp32" else "hea20q1000l_bf16"
     w = hqml_inputs.WORKLOADS[name]
-    x, th, _ = hqml_inputs.workload_inputs(name)
-    ref = _golden(f"{name}_b0_s0.npz")
-    say(f"[gpu] {name} checkpointed sampled parity")
-    ctx = _ctx(w.n_qubits, w.n_layers, w.batch, ckpt_block=w.ckpt_block)
+    x, th, y = hqml_inputs.workload_inputs(name)
+    n, L, B = w.n_qubits, w.n_layers, w.batch
+    samples = [b for b in DEEP_SAMPLES if b < B]
+    refs = {b: _golden("hea20q1000l", b) for b in samples}
+    say(f"[gpu] {name} checkpointed sampled parity, samples {samples}")
+    ctx = _ctx(n, L, B, storage=storage, ckpt_block=w.ckpt_block)
     e = ctx.forward(torch.from_numpy(x), torch.from_numpy(th)).cpu().numpy().astype(np.float64)
-    assert_e_close(e[:1], ref["expz"], w.n_qubits, w.n_layers)
-    g = ctx.backward(_one_hot(w.batch, 0)).cpu().numpy()
-    assert_grad_close(g, ref["grad"])
+    bf, bfg = bf16_bound(n, L), bf16_bound(n, L, grad=True)
+    for b in samples:
+        e_ref, g_ref = refs[b]
+        g = ctx.backward(_one_hot(B, b)).cpu().numpy().astype(np.float64)
+        de, dg = abs(e[b] - e_ref[0]), np.abs(g - g_ref).max()
+        say(f"  sample {b}: E {e[b]:+.4e} (ref {e_ref[0]:+.4e}), |dE| {de:.2e}; max|dg| {dg:.2e}, "
+            f"max|g_ref| {np.abs(g_ref).max():.2e}")
+        if storage == "fp32":
+            assert_e_close(e[b:b + 1], e_ref, n, L)
+            assert_grad_close(g, g_ref)
+            assert_grad_rel(g, g_ref, GRAD_REL, f"sample {b} gradient")
+        else:
+            say(f"    bf16 bounds E {bf:.2e}, gradient {bfg:.2e}: |dE| ratio {de / bf:.3f}, "
+                f"max|dg| ratio {dg / bfg:.3f}")
+            assert de <= min(bf, 2e-2)
+            assert dg <= min(bfg, 2e-2)
     ctx.close()
 
 
@@ -99,6 +142,32 @@ def test_checkpointing_is_bitwise_identical(storage):
             assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("storage,ckpt,xm", [("fp32", 3, 0), ("bf16", 2, 0), ("fp32", 3, 0b101)])
+def test_repeated_backward_after_one_checkpointed_forward(storage, ckpt, xm):
+    """Several hqml_backward calls may follow one saved forward.  With checkpoints the
+    last block's saved outputs share the block buffers that a backward sweep's
+    recomputation overwrites, so a later backward rebuilds that block: every call equals
+    the same call right after a fresh forward, bit for bit (also with an X/Y observable,
+    whose observable pass reads the last block's output)."""
+    n, L, B = 16, 12, 3
+    x, th, _ = hqml_inputs.make_inputs(n, L, B, seed=66)
+    X, TH = torch.from_numpy(x), torch.from_numpy(th)
+    ws = [np.array(v, dtype=np.float32) for v in ([1, 0, 0], [0, 0, 1], [0.5, -1, 2])]
+    say(f"[gpu] repeated backward, storage {storage}, checkpoint {ckpt}, obs_x {xm}")
+    ctx = _ctx(n, L, B, storage=storage, ckpt_block=ckpt, obs_x_mask=xm)
+    ctx.forward(X, TH)
+    gs = [ctx.backward(torch.from_numpy(w_)).cpu().numpy() for w_ in ws + ws[:1]]
+    assert np.array_equal(gs[0], gs[3])
+    for w_, g in zip(ws, gs):
+        ctx.forward(X, TH)
+        assert np.array_equal(ctx.backward(torch.from_numpy(w_)).cpu().numpy(), g)
+    ctx.close()
+    if storage == "fp32":
+        # obs_mask 0 with an X part: the string has no Z factors (X on qubits 0 and 2)
+        g_ref, _ = oracle.backward(x, th, ws[1].astype(np.float64), 0 if xm else 1, xm)
+        assert_grad_close(gs[1], g_ref)
+
+
 def test_bf16_storage_parity_small():
     n, L, B = 16, 6, 3
     x, th, y = hqml_inputs.make_inputs(n, L, B, seed=71)
@@ -108,21 +177,6 @@ def test_bf16_storage_parity_small():
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
     assert np.max(np.abs(e.cpu().numpy() - e_ref)) <= 2e-2
     assert_grad_close(g.cpu().numpy(), g_ref, atol=2e-2)
-    ctx.close()
-
-
-def test_bf16_deep_workload_sampled_parity():
-    """hea20q1000l in bf16 storage (batch 85, checkpoint every 20 layers): sample 0."""
-    name = "hea20q1000l_bf16"
-    w = hqml_inputs.WORKLOADS[name]
-    x, th, _ = hqml_inputs.workload_inputs(name)
-    ref = _golden("hea20q1000l_b0_s0.npz")      # same circuit and first sample
-    say(f"[gpu] {name} sampled parity")
-    ctx = _ctx(w.n_qubits, w.n_layers, w.batch, storage="bf16", ckpt_block=w.ckpt_block)
-    e = ctx.forward(torch.from_numpy(x), torch.from_numpy(th)).cpu().numpy().astype(np.float64)
-    assert abs(e[0] - ref["expz"][0]) <= 2e-2
-    g = ctx.backward(_one_hot(w.batch, 0)).cpu().numpy()
-    assert_grad_close(g, ref["grad"], atol=2e-2)
     ctx.close()
 
 

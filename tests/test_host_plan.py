@@ -191,15 +191,36 @@ def test_plan_invariants(n):
                     last_layer[ps["view"]] = ps[key]
 
 
+@pytest.mark.parametrize("merged", [True, False], ids=["merged", "uncompute"])
 @pytest.mark.parametrize("n,L,B", [(14, 1, 2), (14, 3, 2), (15, 4, 2), (17, 2, 1), (16, 5, 1)])
-def test_model_of_kernel_algebra_matches_oracle(n, L, B):
+def test_model_of_kernel_algebra_matches_oracle(n, L, B, merged):
+    """The kernels' algebra on the library's schedule: with the merged statistics (both
+    layers of a pass from its output, the saved state never un-rotated) and with the
+    plain un-computation of psi to the earlier layer's point."""
     x, th, _ = hqml_inputs.make_inputs(n, L, B, seed=100 + n + L)
-    m = Model(hq.hqml_describe_plan(hq.make_config(n, L, B)), x, th)
+    m = Model(hq.hqml_describe_plan(hq.make_config(n, L, B)), x, th, merged=merged)
     w = np.linspace(0.5, -1.0, B)
     e, g = m.backward(w)
     g_ref, e_ref = oracle.backward(x, th, w)
     assert np.max(np.abs(e - e_ref)) < 1e-10
     assert np.max(np.abs(g - g_ref)) < 1e-10
+
+
+@pytest.mark.parametrize("n", list(range(14, 30)))
+def test_views_keep_chain_neighbours_apart(n):
+    """What the merged statistics rely on: no two qubits a view rotates are chain
+    neighbours, and no qubit at a register position of a layout neighbours a rotated
+    qubit at a register position of the same layout (L1: positions 4..8; L2: 0, 1,
+    9..11), so Z_{q-1} Z_{q+1} is constant over each thread's registers."""
+    p = _plan(n, 3)
+    for v in p["views"]:
+        perm, gm = v["perm"], v["group_mask"]
+        rot = {perm[i] for i in range(13) if (gm >> i) & 1}
+        assert not any(q + 1 in rot for q in rot)
+        for regs in ((4, 5, 6, 7, 8), (0, 1, 9, 10, 11)):
+            for a in regs:
+                if (gm >> a) & 1:
+                    assert all(abs(perm[a] - perm[b]) != 1 for b in regs if b != a)
 
 
 @pytest.mark.parametrize("n", [14, 16, 21, 29])

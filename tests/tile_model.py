@@ -126,8 +126,9 @@ def cnot_frame(cb, sb, p, r, H):
 
 
 class Model:
-    def __init__(self, plan_json: str, x, theta):
+    def __init__(self, plan_json: str, x, theta, merged: bool = True):
         self.plan = json.loads(plan_json)
+        self.merged = merged
         self.x = np.asarray(x, dtype=np.float64)
         self.theta = np.asarray(theta, dtype=np.float64)
         self.L, self.n = self.theta.shape[0], self.theta.shape[1]
@@ -178,15 +179,43 @@ class Model:
             d = d * np.where(self.bits[q], self.f1[l, q], self.f0[l, q])
         return d
 
-    def stats(self, psi, lam, q):
+    def stats(self, psi, lam, q, weight=None):
+        """Im<lam|s_q|psi> for s = X, Y, Z; with `weight` (a +-1 per amplitude that does
+        not depend on bit q), Im<lam|W s_q|psi> for the diagonal W."""
         b = self.bits[q]
         i0 = self.idx[~b]
         i1 = i0 | (1 << q)
         li, lj, pi, pj = lam[i0], lam[i1], psi[i0], psi[i1]
-        sx = np.sum(np.imag(np.conj(li) * pj) + np.imag(np.conj(lj) * pi))
-        sy = np.sum(np.real(np.conj(lj) * pi) - np.real(np.conj(li) * pj))
-        sz = np.sum(np.imag(np.conj(li) * pi) - np.imag(np.conj(lj) * pj))
+        wt = 1.0 if weight is None else weight[i0]
+        sx = np.sum(wt * (np.imag(np.conj(li) * pj) + np.imag(np.conj(lj) * pi)))
+        sy = np.sum(wt * (np.real(np.conj(lj) * pi) - np.real(np.conj(li) * pj)))
+        sz = np.sum(wt * (np.imag(np.conj(li) * pi) - np.imag(np.conj(lj) * pj)))
         return np.array([sx, sy, sz])
+
+    def neighbour_sign(self, q):
+        """The eigenvalue of Z_{q-1} Z_{q+1} (chain neighbours of q) on every basis state."""
+        s = np.ones(1 << self.n)
+        for r in (q - 1, q + 1):
+            if 0 <= r < self.n:
+                s = s * np.where(self.bits[r], -1.0, 1.0)
+        return s
+
+    def merged_stats(self, psi, lam, q, la, lb):
+        """Both layers' statistics of qubit q from one point: the output of a pass
+        [.., D_la, Ry-layer lb on q's group] (or any point after it that only other,
+        non-neighbouring group qubits' rotations separate from it).  Layer lb's are the
+        plain sums; layer la's follow from the sums weighted by Z_{q-1} Z_{q+1}:
+        D X_q D^dag = Z_{q-1} Z_{q+1} (Re rho X_q - Im rho Y_q), D Y_q D^dag =
+        Z_{q-1} Z_{q+1} (Im rho X_q + Re rho Y_q), rho = f0 conj(f1) of qubit q in D_la,
+        and Ry(b) X Ry(b)^dag = cos b X - sin b Z, Ry(b) Z Ry(b)^dag = cos b Z + sin b X."""
+        X, Y, Zs = self.stats(psi, lam, q)
+        sX, sY, sZ = self.stats(psi, lam, q, self.neighbour_sign(q))
+        rho = self.f0[la, q] * np.conj(self.f1[la, q])
+        c, s = self.c[lb, q], self.s[lb, q]
+        cb, sb = c * c - s * s, 2.0 * c * s
+        t = cb * sX - sb * sZ
+        early = np.array([rho.real * t - rho.imag * sY, rho.imag * t + rho.real * sY, cb * Zs + sb * X])
+        return np.array([X, Y, Zs]), early
 
     # --- fused passes -------------------------------------------------
     def chain(self, i):
@@ -231,7 +260,17 @@ class Model:
             v = self.plan["views"][ps["view"]]
             inv = {q: pos for pos, q in enumerate(v["perm"])}
             psi = outs[k]
-            if ps["rotB"] >= 0:
+            if ps["rotB"] >= 0 and self.merged:
+                # the adjoint kernel's form: both layers from the pass output, psi never
+                # un-rotated (the view's group has no two chain neighbours)
+                for q in g:
+                    late, early = self.merged_stats(psi, lam, q, ps["diag"], ps["rotB"])
+                    part[(k, (13 + inv[q]) * 3)] = late
+                    part[(k, inv[q] * 3)] = early
+                lam = self.rot(lam, ps["rotB"], g, inverse=True) * np.conj(self.diag(ps["diag"]))
+                if not ps["init"]:
+                    lam = self.rot(lam, ps["rotA"], g, inverse=True)
+            elif ps["rotB"] >= 0:
                 for q in g:
                     part[(k, (13 + inv[q]) * 3)] = self.stats(psi, lam, q)
                 psi = self.rot(psi, ps["rotB"], g, inverse=True)
