@@ -111,6 +111,15 @@ struct StateIO<2> {
 template <typename R>
 constexpr int kLamIO = sizeof(R) == 4 ? 0 : 2;
 
+// A copy of a per-thread value that the compiler cannot identify with earlier uses: values derived
+// from it (addresses of the stores of a tile, offsets inside a loop) are recomputed where
+// they are used instead of being kept live in registers.  (An empty asm: no instruction.)
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 // ------------------------------------------------------------------ tile layouts
 
 // LDS bank swizzle on the 8-byte amplitude index.  Linear over GF(2), so
@@ -241,7 +250,9 @@ struct RotCoef {
     R F;         // product of the scale factors of the rotated bits
 };
 
-// rot_tf[l][q] = (k, f).  Bits outside regmask get k = 0, f = 1 (identity).
+// rot_tf[l][q] = (k, f).  Bits outside regmask get k = 0, f = 1 (identity).  The table is
+// read for every bit (any qubit's entry is valid) and the mask selects, so the uniform
+// values stay in scalar registers without branches.
 template <typename R>
 __device__ __forceinline__ RotCoef<R> load_coef(const R *rot_tf, int n, int layer, const int *qpos_to_q,
                                                 uint32_t regmask)
@@ -250,13 +261,10 @@ __device__ __forceinline__ RotCoef<R> load_coef(const R *rot_tf, int n, int laye
     rc.F = (R)1;
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
-        rc.k[m] = (R)0;
-        if (regmask & (1u << m)) {
-            const int q = qpos_to_q[m];
-            const V2<R> kf = ldu2(rot_tf + ((size_t)layer * n + q) * 2);
-            rc.k[m] = kf.x;
-            rc.F *= kf.y;
-        }
+        const V2<R> kf = ldu2(rot_tf + ((size_t)layer * n + qpos_to_q[m]) * 2);
+        const bool on = (regmask >> m) & 1u;
+        rc.k[m] = on ? kf.x : (R)0;
+        rc.F *= on ? kf.y : (R)1;
     }
     return rc;
 }
@@ -332,20 +340,30 @@ __device__ __forceinline__ void stat_out3(R x, R y, R z, R *lds_stat, int base, 
 __host__ __device__ constexpr int l1_pos(int m) { return 4 + m; }
 __host__ __device__ constexpr int l2_pos(int m) { return m < 2 ? m : 7 + m; }
 
-// Z statistics of register bits LEVEL..4 from the pairwise sums left by the
-// previous level: d_m = sum_j (-1)^{bit m of j} w_j with w_j = Im(conj(l_j) p_j).
-template <int LEVEL, typename R>
-__device__ __forceinline__ void z_fold(R *wv, R *dz)
+// Z statistics of the register bits: d_m = sum_j (-1)^{bit m of j} w_j with
+// w_j = Im(conj(l_j) p_j).  zsum<K, LO> returns the sum of w over registers LO..LO+2^K-1
+// and adds the differences of its two halves to d_{K-1} (and recursively below), depth
+// first, so at most one pending half-sum per level is live (5 values, not 16).
+template <int J, typename R>
+__device__ __forceinline__ R zw(const Tile<R> &p, const Tile<R> &l)
 {
-    constexpr int cnt = kRegs >> LEVEL;
-    R d = 0;
-#pragma unroll
-    for (int k = 0; k < cnt / 2; ++k) {
-        d += wv[2 * k] - wv[2 * k + 1];
-        wv[k] = wv[2 * k] + wv[2 * k + 1];
+    return fmar(l.re[J], p.im[J], -l.im[J] * p.re[J]);
+}
+
+template <int K, int LO, typename R>
+__device__ __forceinline__ R zsum(const Tile<R> &p, const Tile<R> &l, R *dz)
+{
+    if constexpr (K == 0) {
+        return zw<LO>(p, l);
+    } else {
+        const R a = zsum<K - 1, LO>(p, l, dz);
+        const R b = zsum<K - 1, LO + (1 << (K - 1))>(p, l, dz);
+        if constexpr (LO == 0)
+            dz[K - 1] = a - b;
+        else
+            dz[K - 1] += a - b;
+        return a + b;
     }
-    dz[LEVEL] = d;
-    if constexpr (LEVEL < 4) z_fold<LEVEL + 1>(wv, dz);
 }
 
 // Statistics of the 5 register bits: slots ((sel*13 + pos)*3 + {X,Y,Z}).  Bits a
@@ -356,19 +374,8 @@ template <bool L2, typename R>
 __device__ __forceinline__ void stats_visit(const Tile<R> &p, const Tile<R> &l, int sel, R *lds_stat, int lane,
                                             int w, R corr)
 {
-    // level 0 folded while forming w, so only 16 partial sums are live
-    R wv[kRegs / 2];
     R dz[5];
-    R d0 = 0;
-#pragma unroll
-    for (int k = 0; k < kRegs / 2; ++k) {
-        const R w0 = fmar(l.re[2 * k], p.im[2 * k], -l.im[2 * k] * p.re[2 * k]);
-        const R w1 = fmar(l.re[2 * k + 1], p.im[2 * k + 1], -l.im[2 * k + 1] * p.re[2 * k + 1]);
-        d0 += w0 - w1;
-        wv[k] = w0 + w1;
-    }
-    dz[0] = d0;
-    z_fold<1>(wv, dz);
+    (void)zsum<5, 0>(p, l, dz);
     R sx, sy;
 #define HQML_STAT_BIT(M)                                                        \
     {                                                                           \
@@ -418,18 +425,8 @@ template <bool L2, typename R>
 __device__ __forceinline__ void stats_visit_merged(const Tile<R> &p, const Tile<R> &l, R *lds_stat, int lane, int w,
                                                    R corr, uint32_t nb)
 {
-    R wv[kRegs / 2];
     R dz[5];
-    R d0 = 0;
-#pragma unroll
-    for (int k = 0; k < kRegs / 2; ++k) {
-        const R w0 = fmar(l.re[2 * k], p.im[2 * k], -l.im[2 * k] * p.re[2 * k]);
-        const R w1 = fmar(l.re[2 * k + 1], p.im[2 * k + 1], -l.im[2 * k + 1] * p.re[2 * k + 1]);
-        d0 += w0 - w1;
-        wv[k] = w0 + w1;
-    }
-    dz[0] = d0;
-    z_fold<1>(wv, dz);
+    (void)zsum<5, 0>(p, l, dz);
     R sx, sy;
 #define HQML_STAT_BIT(M)                                                                           \
     {                                                                                              \
@@ -706,7 +703,7 @@ __device__ __forceinline__ void store_l1(const Tile<R> &t, void *state, const Ti
     constexpr uint32_t esz = sizeof(typename IO::elem);
     using Off = TileOff<esz>;
     char *base = reinterpret_cast<char *>(state) + ((uint64_t)c.sample * nelem + c.tile_off) * esz;
-    const Off tb = (Off)c.t1 * esz;
+    const Off tb = (Off)opaque_u32(c.t1) * esz;
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
         const Off off = tb + (Off)roff(c, j) * esz;
@@ -1703,10 +1700,10 @@ __global__ void __launch_bounds__(256) k_grad_reduce(const double *S, const doub
 namespace hqml {
 
 template <int ST, typename R>
-static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s);
+static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s, bool *bad);
 
 // The fp32 adjoint launches (the other compilation unit).
-void launch_tile_bwd_f32(const TilePassArgs &a, dim3 grid, int storage, hipStream_t s);
+void launch_tile_bwd_f32(const TilePassArgs &a, dim3 grid, int storage, hipStream_t s, bool *bad);
 
 #if HQML_BWD32_UNIT == 0
 
@@ -1786,7 +1783,7 @@ hipError_t launch_tile_fwd(const TilePassArgs &a, int B, int storage, int r64, h
 #endif  // HQML_BWD32_UNIT == 0
 
 template <int ST, typename R>
-static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s)
+static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s, bool *bad)
 {
     if (a.flags & PF_CNOT) {
         if ((a.flags & PF_STATS_ONLY) && (a.flags & PF_SEED))
@@ -1807,10 +1804,17 @@ static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s)
         else
             k_tile_bwd<ST, BW_FUSED_LAST, R><<<grid, kThreads, 0, s>>>(a);
     } else if (a.rotB >= 0) {
-        if (a.flags & PF_INIT)
+        // the plans end every sweep with a pass without rotB, so the general shapes are
+        // never seeded and never statistics-only (their kernels do not handle either)
+        if (a.flags & (PF_SEED | PF_STATS_ONLY)) {
+            *bad = true;
+            return;
+        }
+        if (a.flags & PF_INIT) {
             k_tile_bwd<ST, BW_INIT_GENERAL, R><<<grid, kThreads, 0, s>>>(a);
-        else
+        } else {
             k_tile_bwd<ST, BW_GENERAL, R><<<grid, kThreads, 0, s>>>(a);
+        }
     } else if (a.rotA >= 0 && !(a.flags & (PF_INIT | PF_STATS_ONLY))) {
         k_tile_bwd<ST, BW_ROTA, R><<<grid, kThreads, 0, s>>>(a);
     } else {
@@ -1819,25 +1823,27 @@ static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s)
 }
 
 #if HQML_BWD32_UNIT == 1
-void launch_tile_bwd_f32(const TilePassArgs &a, dim3 grid, int storage, hipStream_t s)
+void launch_tile_bwd_f32(const TilePassArgs &a, dim3 grid, int storage, hipStream_t s, bool *bad)
 {
     if (storage == 1)
-        launch_bwd_shape<1, float>(a, grid, s);
+        launch_bwd_shape<1, float>(a, grid, s, bad);
     else
-        launch_bwd_shape<0, float>(a, grid, s);
+        launch_bwd_shape<0, float>(a, grid, s, bad);
 }
 #else
 hipError_t launch_tile_bwd(const TilePassArgs &a, int B, int storage, int r64, hipStream_t s)
 {
     const dim3 grid((unsigned)(B * a.T));
+    bool bad = false;
     if (r64) {
         if (storage == 2)
-            launch_bwd_shape<2, double>(a, grid, s);
+            launch_bwd_shape<2, double>(a, grid, s, &bad);
         else
-            launch_bwd_shape<0, double>(a, grid, s);
+            launch_bwd_shape<0, double>(a, grid, s, &bad);
     } else {
-        launch_tile_bwd_f32(a, grid, storage, s);
+        launch_tile_bwd_f32(a, grid, storage, s, &bad);
     }
+    if (bad) return hipErrorInvalidValue;   // a pass the kernels have no shape for (nothing queued)
     return hipGetLastError();
 }
 
