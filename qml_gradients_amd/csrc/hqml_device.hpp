@@ -100,14 +100,22 @@ __device__ __forceinline__ R row_sum16(R v)
     return v;
 }
 
-// (re, im) -> packed bf16 (re in the low half), rounded to nearest even by gfx950's
-// packed conversion (one instruction for both halves); a NaN stays a NaN.
+// fp32 -> bf16 bits, round to nearest even on the bit pattern; a NaN becomes a quiet NaN
+// of the same sign (the rounding add would carry a NaN whose payload sits only in the low
+// 16 bits into the exponent and give an infinity).  gfx950's packed conversion
+// instruction (v_cvt_pk_bf16_f32) gives the same results but made the bf16 forward pass
+// 4.3x slower (0.959 against 0.224 ms per launch at 20 qubits, batch 85).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, f);
+    const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return (u & 0x7FFFFFFFu) > 0x7F800000u ? ((u >> 16) | 0x40u) : r;
+}
+
+// (re, im) -> packed bf16 (re in the low half).
 __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float re, float im)
 {
-    typedef float f2v __attribute__((ext_vector_type(2)));
-    typedef __bf16 b2v __attribute__((ext_vector_type(2)));
-    const f2v v = {re, im};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2v));
+    return f32_to_bf16_rne(re) | (f32_to_bf16_rne(im) << 16);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h)
