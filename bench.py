@@ -102,8 +102,10 @@ def algorithmic_flops_bwd(plan: dict, B: int):
     (FMA = 2, multiply or add = 1), per amplitude and sample of each launch:
       rotation (scaled tan form) on one state: 4 per qubit;
       X and Y statistics of one qubit: 8; Z statistics of a register layout: 5;
-      merged diagonal applied to psi and lambda: 18; final lambda scale: 2.
-    g = qubits the pass's view rotates, g2 = those at L2 register positions."""
+      merged diagonal applied to lambda: 9 (to psi and lambda: 18); final lambda scale: 2.
+    g = qubits the pass's view rotates, g1 / g2 = those at L1 / L2 register positions.
+    The general and product-state shapes take both layers' statistics from one set of
+    sums (merged statistics) and rotate psi only by the L1 half of the later layer."""
     N = 1 << plan["n"]
     P = len(plan["passes"])
     total = 0
@@ -111,15 +113,16 @@ def algorithmic_flops_bwd(plan: dict, B: int):
         gm = plan["views"][ps["view"]]["group_mask"]
         g = bin(gm).count("1")
         g2 = sum((gm >> p) & 1 for p in L2_POSITIONS)
+        g1 = g - g2
         if k == P - 1 and not ps["init"]:
             # forward rotations, E, seed, statistics, un-rotations, scale
             f = 4 * g + 3 + 8 * g + 10 + 4 * g2 + 4 * g + 2
         elif ps["rotB"] >= 0 and ps["init"]:
-            f = 8 * g + 16 * g + 20 + 18
+            f = 8 * g + 10 + 4 * g1 + 4 * g + 9 + 2
         elif ps["rotB"] >= 0:
-            f = 8 * g + 4 * (g + g2) + 16 * g + 20 + 18 + 2
+            f = 8 * g + 10 + 4 * g1 + 8 * g + 9 + 2
         elif ps["rotA"] >= 0:
-            f = 8 * g + 10 + 4 * g + 4 * g + 2
+            f = 8 * g + 10 + 4 * g + 2
         else:
             f = 8 * g + 10
         total += f * N * B
