@@ -57,6 +57,9 @@ struct hqml_ctx {
     double *H = nullptr;
     void *init_u = nullptr;
     ViewDev *views = nullptr;
+    ViewDevH *hviews = nullptr;  // half-tile views (general adjoint passes on half tiles)
+    bool half = false;           // fp32 CZ-chain tile plan whose views all have half views
+    int stat_mul = 1;            // statistics partials per full tile: 2 with half tiles
     int2 *statmap = nullptr;
     double *dlde = nullptr;
     double *e_work = nullptr;
@@ -220,6 +223,7 @@ TilePassArgs base_args(hqml_ctx *c)
     a.T = c->plan.T;
     a.obs = c->obs;
     a.obs_x = c->obs_x;
+    a.stat_mul = c->stat_mul;
     return a;
 }
 
@@ -246,7 +250,7 @@ int bwd_pass(hqml_ctx *c, hipStream_t st, Span sp, int k, int part_lo, char *par
     const Plan &pl = c->plan;
     const int P = pl.n_fwd();
     TilePassArgs a = base_args(c);
-    a.stat_part = part_base + (size_t)(k - part_lo) * sp.bs * pl.T * kSlots * c->rb;
+    a.stat_part = part_base + (size_t)(k - part_lo) * sp.bs * pl.T * c->stat_mul * kSlots * c->rb;
     a.sample0 = sp.b0;
     if (k >= P) {
         a.view = c->views + pl.stats_only[k - P];
@@ -273,6 +277,12 @@ int bwd_pass(hqml_ctx *c, hipStream_t st, Span sp, int k, int part_lo, char *par
             a.psi_in = k == 0 ? nullptr : pass_out(c, k - 1);
         else
             a.psi_in = pass_out(c, k);
+        // the general shape [rotA, D, rotB] on a saved output: half tiles when the context has them
+        if (c->half && !pp.init && pp.rotA >= 0 && pp.diag >= 0 && pp.rotB >= 0 &&
+            !(extra_flags & (PF_FUSED | PF_SEED))) {
+            a.flags |= PF_HALF;
+            a.hview = c->hviews + pp.view;
+        }
         // lambda goes back through the chain's index map: other tiles still read the
         // old lambda, so the pass writes the second buffer and the two swap roles
         if (pl.cnot && pp.gather) a.psi_out = c->lam_alt;
@@ -436,8 +446,8 @@ int tile_backward_sweep(hqml_ctx *c, hipStream_t st, Span sp, int start)
     const int2 *map = c->statmap;
     auto reduce = [&](const char *base, int lo, int hi) {
         return run_on(c, st, HQML_K_OTHER, "statistics reduction", [&] {
-            return launch_stats_reduce(base, c->r64, map, sp.bs, sp.b0, sp.bc, pl.L, pl.n, pl.T, lo, hi, c->S,
-                                       c->part2, st);
+            return launch_stats_reduce(base, c->r64, map, sp.bs, sp.b0, sp.bc, pl.L, pl.n, pl.T * c->stat_mul, lo,
+                                       hi, c->S, c->part2, st);
         });
     };
     if (pl.c == 0) {
@@ -463,7 +473,7 @@ int tile_backward_sweep(hqml_ctx *c, hipStream_t st, Span sp, int start)
         }
         if ((rc = reduce(c->part, lo, hi))) return rc;
     }
-    char *so_base = c->part + (size_t)pl.c * sp.bs * pl.T * kSlots * c->rb;
+    char *so_base = c->part + (size_t)pl.c * sp.bs * pl.T * c->stat_mul * kSlots * c->rb;
     for (int i = 0; i < nso; ++i)
         if ((rc = bwd_pass(c, st, sp, P + i, P, so_base, 0))) return rc;
     if (nso > 0) return reduce(so_base, P, P + nso);
@@ -770,6 +780,9 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     c->H = static_cast<double *>(grab(Ln * 9 * 8));
     c->init_u = grab((size_t)B * plan.n * 4 * c->rb);
     if (!plan.small) c->views = static_cast<ViewDev *>(grab((plan.views.size() + 1) * sizeof(ViewDev)));
+    c->half = !plan.small && !plan.cnot && plan.half && !c->r64;
+    c->stat_mul = plan.small ? 1 : stat_tiles(plan, c->r64) / plan.T;
+    if (c->half) c->hviews = static_cast<ViewDevH *>(grab(plan.hviews.size() * sizeof(ViewDevH)));
     c->statmap = static_cast<int2 *>(grab(Ln * sizeof(int2)));
     c->dlde = static_cast<double *>(grab((size_t)B * 8));
     c->e_work = static_cast<double *>(grab((size_t)B * 8));
@@ -794,6 +807,8 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
         }
         vs.push_back(ov);   // views[V]: the observable pass (unused without X/Y factors)
         e = hipMemcpy(c->views, vs.data(), vs.size() * sizeof(ViewDev), hipMemcpyHostToDevice);
+        if (e == hipSuccess && c->half)
+            e = hipMemcpy(c->hviews, plan.hviews.data(), plan.hviews.size() * sizeof(ViewDevH), hipMemcpyHostToDevice);
     }
     if (e == hipSuccess && plan.small) e = configure_small();
     if (e != hipSuccess) {

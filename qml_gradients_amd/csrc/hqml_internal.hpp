@@ -67,6 +67,32 @@ struct ViewDev {
     int32_t pad[3];
 };
 
+// Half tile of the fp32 adjoint pass (hqml_kernels.hip, k_tile_bwdh): 2^12 amplitudes,
+// 256 threads x 16 registers, so that four workgroups share a compute unit.
+// Layout H1 (global-memory layout): regs  <- positions 4..7
+//                                    lanes <- positions 0,1,2,3,8,9
+//                                    waves <- positions 10,11
+// Layout H2 (after one LDS transpose): regs  <- positions 8..11
+//                                    lanes <- positions 0..5
+//                                    waves <- positions 6,7
+// Positions 0 and 1 are lane bits 0 and 1 in both layouts; their rotations and
+// statistics take the partner lane's amplitude through a DPP quad permutation.  A half
+// view rotates the same group of qubits as the full view of the same index: its rotated
+// low qubits at 0, 1, the other low qubits at 2, 3, its rotated high qubits at 4..11.
+constexpr int kHalfBits = 12;
+constexpr int kHalfRegs = 16;
+
+struct ViewDevH {
+    int32_t perm[kHalfBits];       // global qubit held at local position
+    int32_t slot_pos[kHalfBits];   // statistics slot position of that qubit: its position in the
+                                   // full view (so the statistics land where the full-tile kernel
+                                   // puts them); 12 (a slot nobody reads) where it is not rotated
+    int32_t n_tile;                // number of tile-index bits (n - 12)
+    int32_t tile_q[32];            // global qubit of tile-index bit k
+    int32_t group_mask;            // local positions whose qubits this view rotates
+    int32_t pad[2];
+};
+
 enum PassFlags : int {
     PF_INIT = 1,         // generate the layer-0 product state instead of loading a state
     PF_EMIT_E = 2,       // write per-tile <O> partial sums
@@ -78,7 +104,8 @@ enum PassFlags : int {
                          // signs); backward shapes of that plan
     PF_GATHER = 128,     // forward: read the input at P^-1(i) (the CNOT chain);
                          // backward: write lambda back to P^-1(i)
-    PF_OBS_NEG = 256     // observable pass: the Pauli string carries an extra sign -1
+    PF_OBS_NEG = 256,    // observable pass: the Pauli string carries an extra sign -1
+    PF_HALF = 512        // backward: the general shape on half tiles (k_tile_bwdh, fp32)
 };
 
 struct TilePassArgs {
@@ -87,11 +114,12 @@ struct TilePassArgs {
     // Arrays below hold the compute type R of the kernel (float or double).
     void *lam;              // bwd: adjoint state, complex R, updated in place
     void *e_part;           // [B][T] per-tile <O> partial sums
-    void *stat_part;        // [B][T][kSlots] per-tile gradient statistics of this pass
+    void *stat_part;        // [B][T * stat_mul][kSlots] per-tile gradient statistics of this pass
     const void *rot_tf;     // [L][n][2]: tan form (k, f) of the real rotation
     const void *dw;         // [L][n][4]: factors (f0, f1) of qubit q in D_l
     const void *init_u;     // [B][n][4]: (u0.re, u0.im, u1.re, u1.im) layer-0 product factors
     const ViewDev *view;
+    const ViewDevH *hview;  // bwd with PF_HALF: the half view of the same group
     int n;
     int L;
     int T;                  // tiles per sample = 2^(n-13)
@@ -100,6 +128,8 @@ struct TilePassArgs {
     int rotB;               // second rotation layer (-1: none)
     int flags;
     int sample0;            // first sample of this launch (the grid covers samples sample0 ..)
+    int stat_mul;           // bwd: statistics partials per tile (2 when the context's adjoint
+                            // runs on half tiles: full-tile passes write theirs and a zero row)
     uint32_t obs;           // observable: Z part of the Pauli string (qubit mask)
     uint32_t obs_x;         // observable: X part (qubits in both masks carry Y = iXZ)
 };

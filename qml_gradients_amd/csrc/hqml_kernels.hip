@@ -1025,15 +1025,25 @@ __device__ __forceinline__ void zero_stats(R *lds_stat)
     for (int i = threadIdx.x; i < kSlots * 16 + 16; i += kThreads) lds_stat[i] = 0;
 }
 
+// Where a full tile's statistics partials go: row (sample * T + tile) * stat_mul of the
+// pass's partials; with stat_mul = 2 (the context's general passes run on half tiles, two
+// rows per full tile) the row after it is written with zeros.
 template <typename R>
-__device__ __forceinline__ void flush_stats(const R *lds_stat, R *stat_part, const TileCtx &c, int T)
+__device__ __forceinline__ R *stat_row(const TilePassArgs &a, const TileCtx &c)
+{
+    return static_cast<R *>(a.stat_part) + ((size_t)c.sample * a.T + c.tile) * (size_t)a.stat_mul * kSlots;
+}
+
+template <typename R>
+__device__ __forceinline__ void flush_stats(const R *lds_stat, R *dst, bool zero_next)
 {
     __syncthreads();
     if (threadIdx.x < kSlots) {
         R s = 0;
 #pragma unroll
         for (int k = 0; k < 16; ++k) s += lds_stat[threadIdx.x * 16 + k];
-        stat_part[((size_t)c.sample * T + c.tile) * kSlots + threadIdx.x] = s;
+        dst[threadIdx.x] = s;
+        if (zero_next) dst[kSlots + threadIdx.x] = 0;
     }
 }
 
@@ -1043,8 +1053,8 @@ __device__ __forceinline__ void flush_stats(const R *lds_stat, R *stat_part, con
 // cos b, sin b of Ry_q(lb) from its tan form k = tan(b/2) (rot_tf row lb).  lds_stat row 0
 // of every slot receives the slot's workgroup sum first.
 template <typename R>
-__device__ __forceinline__ void flush_merged(R *lds_stat, R *stat_part, const TileCtx &c, int T, const ViewDev &v,
-                                             const R *rot_tf, const R *dw, int n, int la, int lb)
+__device__ __forceinline__ void flush_merged(R *lds_stat, R *dst, bool zero_next, const ViewDev &v, const R *rot_tf,
+                                             const R *dw, int n, int la, int lb)
 {
     __syncthreads();
     const int t = threadIdx.x;
@@ -1072,7 +1082,8 @@ __device__ __forceinline__ void flush_merged(R *lds_stat, R *stat_part, const Ti
             const R u = cb * tx - sb * tz;
             out = sig == 0 ? rr * u - ri * ty : sig == 1 ? ri * u + rr * ty : cb * szl + sb * sxl;
         }
-        stat_part[((size_t)c.sample * T + c.tile) * kSlots + t] = out;
+        dst[t] = out;
+        if (zero_next) dst[kSlots + t] = 0;
     }
 }
 
@@ -1184,7 +1195,7 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
             }
             if (sl != (R)1) scale_tile(l, sl);
             store_l1<LIO, R, kLamNT>(l, a.lam, c, nelem);
-            flush_merged(lds_stat, static_cast<R *>(a.stat_part), c, a.T, v, rot_tf, static_cast<const R *>(a.dw), a.n,
+            flush_merged(lds_stat, stat_row<R>(a, c), a.stat_mul == 2, v, rot_tf, static_cast<const R *>(a.dw), a.n,
                          a.diag, a.rotB);
             return;
         } else if constexpr (SHAPE == BW_DROTB) {
@@ -1225,7 +1236,7 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
             transpose(p, lds, c.a1, c.a2, false);
             transpose(l, lds, c.a1, c.a2, false);
             stats_visit<false>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
-            flush_stats(lds_stat, static_cast<R *>(a.stat_part), c, a.T);
+            flush_stats(lds_stat, stat_row<R>(a, c), a.stat_mul == 2);
             return;
         } else if constexpr (SHAPE == BW_L0D_SEED) {
             // One-layer circuit: the seeded lambda = O psi is already at the statistics point
@@ -1238,7 +1249,7 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
             apply_diag(l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2, false), (R)1);
             transpose(l, lds, c.a1, c.a2, false);
             store_l1<LIO>(l, a.lam, c, nelem);
-            flush_stats(lds_stat, static_cast<R *>(a.stat_part), c, a.T);
+            flush_stats(lds_stat, stat_row<R>(a, c), a.stat_mul == 2);
             return;
         } else if constexpr (SHAPE == BW_ROTA) {
             // statistics of both layouts at the pass output; psi is not un-rotated
@@ -1258,7 +1269,7 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
             transpose(l, lds, c.a1, c.a2, true);
             stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
             if (a.flags & PF_STATS_ONLY) {
-                flush_stats(lds_stat, static_cast<R *>(a.stat_part), c, a.T);
+                flush_stats(lds_stat, stat_row<R>(a, c), a.stat_mul == 2);
                 return;
             }
             transpose(l, lds, c.a1, c.a2, false);
@@ -1269,7 +1280,495 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
         store_l1_chain<LIO>(l, a.psi_out, c, nelem);   // the second lambda buffer (others read a.lam)
     else
         store_l1<LIO, R, kLamNT>(l, a.lam, c, nelem);
-    flush_stats(lds_stat, static_cast<R *>(a.stat_part), c, a.T);
+    flush_stats(lds_stat, stat_row<R>(a, c), a.stat_mul == 2);
+}
+
+// ------------------------------------------------------------------ half-tile adjoint pass (fp32)
+//
+// The general adjoint shape [Ry-layer la on the group, D_la, Ry-layer lb on the group] on
+// half tiles: 2^12 amplitudes in 256 threads x 16 registers (layouts H1 / H2,
+// hqml_internal.hpp).  With half the registers of the full tile for the two states, four
+// workgroups share a compute unit instead of two, so the loads of some overlap the
+// arithmetic of others.  The arithmetic is that of the full-tile general shape (merged
+// statistics into the same slots), in this order: load psi and lambda (H1); merged
+// statistics of positions 0, 1 (lane bits: the partner lane's psi through a DPP quad
+// permutation) and 4..7 (register bits); un-rotate layer lb at 4..7 on both states;
+// transpose both; merged statistics of 8..11 (psi is then dead); on lambda: un-rotate lb at
+// 8..11 and at 0, 1, apply D_la^dagger, un-rotate la at 8..11 and at 0, 1; transpose;
+// un-rotate la at 4..7; store.
+
+struct HTile {
+    float re[kHalfRegs];
+    float im[kHalfRegs];
+};
+
+// LDS swizzle of the 12-bit local index: bit 4 ^= bit 8.  Linear over GF(2).  A half-wave
+// then touches 32 distinct 8-byte slots in both layouts: in H1 its lanes 16..31 differ from
+// lanes 0..15 in position 8, which moves them to the other half of the 32 slots; in H2
+// they differ in position 4 and the flip by register bit 0 (position 8) is uniform.
+__host__ __device__ constexpr uint32_t hswz(uint32_t i) { return i ^ (((i >> 8) & 1u) << 4); }
+
+struct HCtx {
+    int lane, w, sample, tile;
+    uint64_t tile_off;        // global amplitude offset of the tile's fixed (tile-index) bits
+    uint32_t t1;              // H1: thread's amplitude offset within the tile
+    uint32_t a1, a2;          // swizzled LDS bases of the thread in H1 / H2
+    uint32_t fixed1, fixed2;  // qubit bitmask of the thread's fixed bits (with the tile's) in H1 / H2
+    uint32_t rs[4];           // H1: amplitude stride of register bit m (uniform)
+    int q0[2], q1[4], q2[4];  // qubits at positions 0, 1 / 4..7 / 8..11
+    uint32_t gm0, gm1, gm2;   // rotated-group masks of those positions
+};
+
+__device__ __forceinline__ void hctx(HCtx &c, const ViewDevH &v, int T2, int blk, int sample0)
+{
+    const int tid = threadIdx.x;
+    c.lane = tid & 63;
+    c.w = tid >> 6;
+    const int lane = c.lane, w = c.w;
+    // thread bits (lane 0..5, wave 0..1): H1 -> positions 0,1,2,3,8,9,10,11; H2 -> 0..7
+    const int h1p[8] = {0, 1, 2, 3, 8, 9, 10, 11};
+    const uint32_t tv = (uint32_t)lane | ((uint32_t)w << 6);
+    uint32_t t1 = 0, t2 = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        if ((tv >> k) & 1u) {
+            t1 |= 1u << ldu(&v.perm[h1p[k]]);
+            t2 |= 1u << ldu(&v.perm[k]);
+        }
+    c.t1 = t1;
+    c.a1 = hswz((uint32_t)(lane & 15) | ((uint32_t)(lane >> 4) << 8) | ((uint32_t)w << 10));
+    c.a2 = hswz(tv);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        c.q1[m] = ldu(&v.perm[4 + m]);
+        c.q2[m] = ldu(&v.perm[8 + m]);
+        c.rs[m] = 1u << c.q1[m];
+    }
+    c.q0[0] = ldu(&v.perm[0]);
+    c.q0[1] = ldu(&v.perm[1]);
+    const uint32_t gm = (uint32_t)ldu(&v.group_mask);
+    c.gm0 = gm & 3u;
+    c.gm1 = (gm >> 4) & 15u;
+    c.gm2 = (gm >> 8) & 15u;
+    const int rel = blk / T2;
+    c.tile = blk - rel * T2;
+    c.sample = sample0 + rel;
+    uint64_t toff = 0;
+    uint32_t tb = 0;
+    const int nt = ldu(&v.n_tile);
+    for (int k = 0; k < nt; ++k)
+        if ((c.tile >> k) & 1) {
+            const int q = ldu(&v.tile_q[k]);
+            toff |= 1ull << q;
+            tb |= 1u << q;
+        }
+    c.tile_off = toff;
+    c.fixed1 = t1 | tb;
+    c.fixed2 = t2 | tb;
+}
+
+__device__ __forceinline__ uint32_t hroff(const HCtx &c, int j)
+{
+    uint32_t o = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        if (j & (1 << m)) o += c.rs[m];
+    return o;
+}
+
+// Global-memory access of a half tile in layout H1 (NT: non-temporal loads).
+template <int ST, bool NT>
+__device__ __forceinline__ void hload(HTile &t, const void *state, const HCtx &c, uint64_t nelem)
+{
+    using IO = StateIO<ST>;
+    constexpr uint32_t esz = sizeof(typename IO::elem);
+    const char *base = reinterpret_cast<const char *>(state) + ((uint64_t)c.sample * nelem + c.tile_off) * esz;
+    const uint32_t tb = c.t1 * esz;
+#pragma unroll
+    for (int j = 0; j < kHalfRegs; ++j) {
+        const uint32_t off = tb + hroff(c, j) * esz;
+        if constexpr (NT)
+            IO::load(reinterpret_cast<const typename IO::elem *>(base + off), t.re[j], t.im[j]);
+        else
+            IO::load_temporal(reinterpret_cast<const typename IO::elem *>(base + off), t.re[j], t.im[j]);
+    }
+}
+
+__device__ __forceinline__ void hstore(const HTile &t, void *state, const HCtx &c, uint64_t nelem)
+{
+    char *base = reinterpret_cast<char *>(state) + ((uint64_t)c.sample * nelem + c.tile_off) * 8u;
+    const uint32_t tb = opaque_u32(c.t1) * 8u;
+#pragma unroll
+    for (int j = 0; j < kHalfRegs; ++j) {
+        const uint32_t off = tb + hroff(c, j) * 8u;
+        StateIO<0>::store(reinterpret_cast<float2 *>(base + off), t.re[j], t.im[j]);
+    }
+}
+
+// Move a half tile between H1 and H2 through the 32 KB LDS buffer.
+__device__ __forceinline__ void htranspose(HTile &t, float2 *lds, uint32_t a1, uint32_t a2, bool from_h1)
+{
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kHalfRegs; ++j) {
+        const uint32_t i = from_h1 ? (a1 ^ ((uint32_t)j << 4)) : (a2 ^ hswz((uint32_t)j << 8));
+        lds[i] = make_float2(t.re[j], t.im[j]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kHalfRegs; ++j) {
+        const uint32_t i = from_h1 ? (a2 ^ hswz((uint32_t)j << 8)) : (a1 ^ ((uint32_t)j << 4));
+        const float2 v = lds[i];
+        t.re[j] = v.x;
+        t.im[j] = v.y;
+    }
+}
+
+// Ry (kk = k) or Ry^dagger (kk = -k) on register bit M, scale f left out (as rot_bit).
+template <int M>
+__device__ __forceinline__ void hrot_bit(HTile &t, float kk)
+{
+#pragma unroll
+    for (int j = 0; j < kHalfRegs; ++j) {
+        if (j & (1 << M)) continue;
+        const int o = j | (1 << M);
+        const float ar = t.re[j], ai = t.im[j], br = t.re[o], bi = t.im[o];
+        t.re[j] = fmaf(-kk, br, ar);
+        t.im[j] = fmaf(-kk, bi, ai);
+        t.re[o] = fmaf(kk, ar, br);
+        t.im[o] = fmaf(kk, ai, bi);
+    }
+}
+
+struct HCoef {
+    float k[4];
+    float F;      // product of the scale factors of the rotated bits
+};
+
+// Tan-form coefficients of NB positions (qubits q[m]); positions outside mask: identity.
+template <int NB>
+__device__ __forceinline__ HCoef hcoef(const float *rot_tf, int n, int layer, const int *q, uint32_t mask)
+{
+    HCoef rc;
+    rc.F = 1.f;
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+        const float2 kf = ldu2(rot_tf + ((size_t)layer * n + q[m]) * 2);
+        const bool on = (mask >> m) & 1u;
+        rc.k[m] = on ? kf.x : 0.f;
+        rc.F *= on ? kf.y : 1.f;
+    }
+    return rc;
+}
+
+__device__ __forceinline__ void hunrot_regs(HTile &t, const HCoef &rc)
+{
+    hrot_bit<0>(t, -rc.k[0]);
+    hrot_bit<1>(t, -rc.k[1]);
+    hrot_bit<2>(t, -rc.k[2]);
+    hrot_bit<3>(t, -rc.k[3]);
+}
+
+// DPP forms of a multiply-add with the partner lane's operand.  The compiler does not fold
+// a DPP move into v_fmac_f32, so these are written as instructions: a quad permutation of
+// src0 (lane index XOR 1 or XOR 2, so every lane's source is valid), no memory access.
+// Each block starts with two wait states (a VALU write of a VGPR followed by a DPP read of
+// it needs two on this hardware); inside a block no instruction reads through DPP a
+// register that an earlier one wrote.
+#define HQML_QP0 " quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+#define HQML_QP1 " quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+#define HQML_SELF8(QP)                                                                        \
+    asm("s_nop 1\n\t"                                                                         \
+        "v_fmac_f32_dpp %0, %0, %8" QP "\n\t"                                                 \
+        "v_fmac_f32_dpp %1, %1, %8" QP "\n\t"                                                 \
+        "v_fmac_f32_dpp %2, %2, %8" QP "\n\t"                                                 \
+        "v_fmac_f32_dpp %3, %3, %8" QP "\n\t"                                                 \
+        "v_fmac_f32_dpp %4, %4, %8" QP "\n\t"                                                 \
+        "v_fmac_f32_dpp %5, %5, %8" QP "\n\t"                                                 \
+        "v_fmac_f32_dpp %6, %6, %8" QP "\n\t"                                                 \
+        "v_fmac_f32_dpp %7, %7, %8" QP                                                        \
+        : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), \
+          "+v"(x[7])                                                                          \
+        : "v"(k))
+
+// x[i] += k * (x[i] of the partner lane), eight values, in place.
+template <int B>
+__device__ __forceinline__ void dpp_self8(float *x, float k)
+{
+    if constexpr (B == 0)
+        HQML_SELF8(HQML_QP0);
+    else
+        HQML_SELF8(HQML_QP1);
+}
+
+// Statistics of two registers with the partner lane's psi:
+//   xp += l.re * p.im', xn += l.im * p.re', rp += l.re * p.re', rq += l.im * p.im'
+// (primes: the partner lane's value), for registers j and j + 1.
+#define HQML_XY2(QP)                                                                         \
+    asm("s_nop 1\n\t"                                                                        \
+        "v_fmac_f32_dpp %0, %5, %4" QP "\n\t"                                                \
+        "v_fmac_f32_dpp %1, %6, %7" QP "\n\t"                                                \
+        "v_fmac_f32_dpp %2, %6, %4" QP "\n\t"                                                \
+        "v_fmac_f32_dpp %3, %5, %7" QP "\n\t"                                                \
+        "v_fmac_f32_dpp %0, %9, %8" QP "\n\t"                                                \
+        "v_fmac_f32_dpp %1, %10, %11" QP "\n\t"                                              \
+        "v_fmac_f32_dpp %2, %10, %8" QP "\n\t"                                               \
+        "v_fmac_f32_dpp %3, %9, %11" QP                                                      \
+        : "+v"(xp), "+v"(xn), "+v"(rp), "+v"(rq)                                             \
+        : "v"(l.re[j]), "v"(p.im[j]), "v"(p.re[j]), "v"(l.im[j]), "v"(l.re[j + 1]),          \
+          "v"(p.im[j + 1]), "v"(p.re[j + 1]), "v"(l.im[j + 1]))
+
+// Ry^dagger on the qubit at lane bit B (position B) in tan form, scale left out: the thread
+// holding bit value 0 computes a + k b, the one holding 1 computes b - k a, with the partner
+// lane's amplitude (every source is read before any lane writes, so the update is in place).
+template <int B>
+__device__ __forceinline__ void hunrot_lane(HTile &t, float k, int lane)
+{
+    const float ks = ((lane >> B) & 1) ? -k : k;
+    dpp_self8<B>(t.re, ks);
+    dpp_self8<B>(t.re + 8, ks);
+    dpp_self8<B>(t.im, ks);
+    dpp_self8<B>(t.im + 8, ks);
+}
+
+// X / Y statistics of register bit M (as xy_stats).
+template <int M>
+__device__ __forceinline__ void hxy_reg(const HTile &p, const HTile &l, float &sx, float &sy)
+{
+    float xp = 0, xn = 0, yp = 0, yn = 0;
+#pragma unroll
+    for (int j = 0; j < kHalfRegs; ++j) {
+        if (j & (1 << M)) continue;
+        const int o = j | (1 << M);
+        xp = fmaf(l.re[j], p.im[o], xp);
+        xp = fmaf(l.re[o], p.im[j], xp);
+        xn = fmaf(l.im[j], p.re[o], xn);
+        xn = fmaf(l.im[o], p.re[j], xn);
+        yp = fmaf(l.re[o], p.re[j], yp);
+        yp = fmaf(l.im[o], p.im[j], yp);
+        yn = fmaf(l.re[j], p.re[o], yn);
+        yn = fmaf(l.im[j], p.im[o], yn);
+    }
+    sx = xp - xn;
+    sy = yp - yn;
+}
+
+// X / Y statistics of the qubit at lane bit B: with c = conj(l_i) p_{i ^ 2^B} (the partner
+// lane's psi), Im<lam|X|psi> = sum Im c and Im<lam|Y|psi> = sum (bit ? Re c : -Re c), since
+// (Y psi)_i = -i psi_partner where bit B of i is 0 and +i psi_partner where it is 1.
+template <int B>
+__device__ __forceinline__ void hxy_lane(const HTile &p, const HTile &l, int lane, float &sx, float &sy)
+{
+    float xp = 0, xn = 0, rp = 0, rq = 0;
+#pragma unroll
+    for (int j = 0; j < kHalfRegs; j += 2) {
+        if constexpr (B == 0)
+            HQML_XY2(HQML_QP0);
+        else
+            HQML_XY2(HQML_QP1);
+    }
+    sx = xp - xn;
+    const float r = rp + rq;
+    sy = ((lane >> B) & 1) ? r : -r;
+}
+
+// Z statistics of the register bits (zsum on 16 registers): returns the sum of
+// w_j = Im(conj(l_j) p_j) over the registers, d_m = sum (-1)^{bit m of j} w_j.
+template <int J>
+__device__ __forceinline__ float hzw(const HTile &p, const HTile &l)
+{
+    return fmaf(l.re[J], p.im[J], -l.im[J] * p.re[J]);
+}
+
+template <int K, int LO>
+__device__ __forceinline__ float hzsum(const HTile &p, const HTile &l, float *dz)
+{
+    if constexpr (K == 0) {
+        return hzw<LO>(p, l);
+    } else {
+        const float a = hzsum<K - 1, LO>(p, l, dz);
+        const float b = hzsum<K - 1, LO + (1 << (K - 1))>(p, l, dz);
+        if constexpr (LO == 0)
+            dz[K - 1] = a - b;
+        else
+            dz[K - 1] += a - b;
+        return a + b;
+    }
+}
+
+// Parity of this thread's chain neighbours of qubit q (1: Z_{q-1} Z_{q+1} = -1).
+__device__ __forceinline__ bool nb_odd(uint32_t fixed, int q, int n)
+{
+    uint32_t nb = q + 1 < n ? 1u << (q + 1) : 0u;
+    if (q > 0) nb |= 1u << (q - 1);
+    return __builtin_popcount(fixed & nb) & 1;
+}
+
+// Plain (layer lb) and neighbour-signed (layer la, see stats_visit_merged) sums of one
+// position's statistics into its slots.
+__device__ __forceinline__ void hstat_out(float sx, float sy, float sz, float corr, bool odd, int sp, float *lds_stat,
+                                          int lane, int w)
+{
+    const float sg = odd ? -corr : corr;
+    stat_out3(sx * corr, sy * corr, sz * corr, lds_stat, (13 + sp) * 3, lane, w);
+    stat_out3(sx * sg, sy * sg, sz * sg, lds_stat, sp * 3, lane, w);
+}
+
+// Factor tables of D_l in layout H2: D(i) = lo[j & 3] * hi[j >> 2] for register j
+// (positions 8, 9 and 10, 11), thread constant and CZ signs with fixed qubits folded in
+// as in diag_tables; the half view keeps positions 8, 9 apart from 10, 11 in the chain.
+struct HDiag {
+    float2 lo[4];
+    float2 hi[4];
+};
+
+__device__ __forceinline__ HDiag hdiag_tables(const float *dw, int n, int layer, const int *rq, uint32_t fixed_bits)
+{
+    const float4 *wl = reinterpret_cast<const float4 *>(dw) + (size_t)layer * n;
+    uint32_t regq = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) regq |= 1u << rq[m];
+    float2 c = make_float2(1.f, 0.f);
+    for (int q = 0; q < n; ++q) {
+        if (regq & (1u << q)) continue;
+        const float4 f = ldu4(reinterpret_cast<const float *>(wl + q));
+        c = cmul(c, ((fixed_bits >> q) & 1u) ? make_float2(f.z, f.w) : make_float2(f.x, f.y));
+    }
+    if (__builtin_popcount(fixed_bits & (fixed_bits >> 1)) & 1) {
+        c.x = -c.x;
+        c.y = -c.y;
+    }
+    float2 g0[4], g1[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int q = rq[m];
+        const float4 f = ldu4(reinterpret_cast<const float *>(wl + q));
+        g0[m] = make_float2(f.x, f.y);
+        g1[m] = make_float2(f.z, f.w);
+        if (nb_odd(fixed_bits, q, n)) {
+            g1[m].x = -g1[m].x;
+            g1[m].y = -g1[m].y;
+        }
+    }
+    auto adj = [&](int a, int b) { const int d = rq[a] - rq[b]; return d == 1 || d == -1; };
+    HDiag t;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        float2 v = cmul(c, cmul((a & 1) ? g1[0] : g0[0], (a & 2) ? g1[1] : g0[1]));
+        if (a == 3 && adj(0, 1)) {
+            v.x = -v.x;
+            v.y = -v.y;
+        }
+        t.lo[a] = v;
+        float2 h = cmul((a & 1) ? g1[2] : g0[2], (a & 2) ? g1[3] : g0[3]);
+        if (a == 3 && adj(2, 3)) {
+            h.x = -h.x;
+            h.y = -h.y;
+        }
+        t.hi[a] = h;
+    }
+    return t;
+}
+
+// s * D^dagger on a half tile in H2.
+__device__ __forceinline__ void hdiag_dag(HTile &t, HDiag d, float s)
+{
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        d.lo[a].x *= s;
+        d.lo[a].y *= s;
+    }
+#pragma unroll
+    for (int j = 0; j < kHalfRegs; ++j) {
+        float2 f = cmul(d.lo[j & 3], d.hi[j >> 2]);
+        f.y = -f.y;
+        const float r = t.re[j], i = t.im[j];
+        t.re[j] = r * f.x - i * f.y;
+        t.im[j] = r * f.y + i * f.x;
+    }
+}
+
+template <int ST>
+__global__ __launch_bounds__(kThreads, 4) void k_tile_bwdh(TilePassArgs a)
+{
+    __shared__ float2 lds[1 << kHalfBits];
+    __shared__ float lds_stat[kSlots * 16 + 16];
+    const float *rot_tf = static_cast<const float *>(a.rot_tf);
+    const float *dw = static_cast<const float *>(a.dw);
+    const ViewDevH &v = *a.hview;
+    const int T2 = a.T * 2, n = a.n, la = a.rotA, lb = a.rotB;
+    HCtx c;
+    hctx(c, v, T2, xcd_slot((int)blockIdx.x, (int)gridDim.x), a.sample0);
+    zero_stats(lds_stat);
+    __syncthreads();
+    const uint64_t nelem = 1ull << n;
+    HTile p, l;
+    hload<ST, true>(p, a.psi_in, c, nelem);
+    hload<0, false>(l, a.lam, c, nelem);
+    {   // merged statistics at the pass output: positions 0, 1 and 4..7 (H1)
+        float dz[4];
+        const float W = hzsum<4, 0>(p, l, dz);
+        float sx, sy;
+        hxy_lane<0>(p, l, c.lane, sx, sy);
+        hstat_out(sx, sy, (c.lane & 1) ? -W : W, 1.f, nb_odd(c.fixed1, c.q0[0], n), ldu(&v.slot_pos[0]), lds_stat,
+                  c.lane, c.w);
+        hxy_lane<1>(p, l, c.lane, sx, sy);
+        hstat_out(sx, sy, (c.lane & 2) ? -W : W, 1.f, nb_odd(c.fixed1, c.q0[1], n), ldu(&v.slot_pos[1]), lds_stat,
+                  c.lane, c.w);
+#define HQML_HSTAT1(M)                                                                                      \
+    hxy_reg<M>(p, l, sx, sy);                                                                               \
+    hstat_out(sx, sy, dz[M], 1.f, nb_odd(c.fixed1, c.q1[M], n), ldu(&v.slot_pos[4 + M]), lds_stat, c.lane, c.w);
+        HQML_HSTAT1(0)
+        HQML_HSTAT1(1)
+        HQML_HSTAT1(2)
+        HQML_HSTAT1(3)
+#undef HQML_HSTAT1
+    }
+    const HCoef b1 = hcoef<4>(rot_tf, n, lb, c.q1, c.gm1);
+    hunrot_regs(p, b1);
+    hunrot_regs(l, b1);
+    htranspose(p, lds, c.a1, c.a2, true);
+    htranspose(l, lds, c.a1, c.a2, true);
+    {   // positions 8..11 (H2); both states carry scale 1 / b1.F
+        float dz[4];
+        (void)hzsum<4, 0>(p, l, dz);
+        const float corr = b1.F * b1.F;
+        float sx, sy;
+#define HQML_HSTAT2(M)                                                                                       \
+    hxy_reg<M>(p, l, sx, sy);                                                                                \
+    hstat_out(sx, sy, dz[M], corr, nb_odd(c.fixed2, c.q2[M], n), ldu(&v.slot_pos[8 + M]), lds_stat, c.lane, c.w);
+        HQML_HSTAT2(0)
+        HQML_HSTAT2(1)
+        HQML_HSTAT2(2)
+        HQML_HSTAT2(3)
+#undef HQML_HSTAT2
+    }
+    // lambda: the rest of layer lb, D_la^dagger (which removes the scales so far), layer la
+    const HCoef b2 = hcoef<4>(rot_tf, n, lb, c.q2, c.gm2);
+    hunrot_regs(l, b2);
+    const HCoef b0 = hcoef<2>(rot_tf, n, lb, c.q0, c.gm0);
+    hunrot_lane<0>(l, b0.k[0], c.lane);
+    hunrot_lane<1>(l, b0.k[1], c.lane);
+    hdiag_dag(l, hdiag_tables(dw, n, a.diag, c.q2, c.fixed2), b1.F * b2.F * b0.F);
+    const HCoef a2 = hcoef<4>(rot_tf, n, la, c.q2, c.gm2);
+    hunrot_regs(l, a2);
+    const HCoef a0 = hcoef<2>(rot_tf, n, la, c.q0, c.gm0);
+    hunrot_lane<0>(l, a0.k[0], c.lane);
+    hunrot_lane<1>(l, a0.k[1], c.lane);
+    htranspose(l, lds, c.a1, c.a2, false);
+    const HCoef a1 = hcoef<4>(rot_tf, n, la, c.q1, c.gm1);
+    hunrot_regs(l, a1);
+    const float sl = a2.F * a0.F * a1.F;
+    if (sl != 1.f) {
+#pragma unroll
+        for (int j = 0; j < kHalfRegs; ++j) {
+            l.re[j] *= sl;
+            l.im[j] *= sl;
+        }
+    }
+    hstore(l, a.lam, c, nelem);
+    flush_merged(lds_stat, static_cast<float *>(a.stat_part) + ((size_t)c.sample * T2 + c.tile) * kSlots, false,
+                 *a.view, rot_tf, dw, n, a.diag, lb);
 }
 
 // ------------------------------------------------------------------ table preparation (fp64)
@@ -1785,6 +2284,18 @@ hipError_t launch_tile_fwd(const TilePassArgs &a, int B, int storage, int r64, h
 template <int ST, typename R>
 static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s, bool *bad)
 {
+    if (a.flags & PF_HALF) {
+        // the general shape on half tiles (fp32 compute, fp32 or bf16 psi): two per full tile
+        if constexpr (std::is_same<R, float>::value && ST != 2) {
+            if (a.rotA >= 0 && a.diag >= 0 && a.rotB >= 0 && a.hview &&
+                !(a.flags & (PF_CNOT | PF_FUSED | PF_INIT | PF_SEED | PF_STATS_ONLY))) {
+                k_tile_bwdh<ST><<<dim3(grid.x * 2), kThreads, 0, s>>>(a);
+                return;
+            }
+        }
+        *bad = true;
+        return;
+    }
     if (a.flags & PF_CNOT) {
         if ((a.flags & PF_STATS_ONLY) && (a.flags & PF_SEED))
             k_tile_bwd<ST, BW_L0D_SEED, R><<<grid, kThreads, 0, s>>>(a);

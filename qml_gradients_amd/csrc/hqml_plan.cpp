@@ -146,7 +146,97 @@ bool build_views(int n, Plan &p, std::string *err)
     return true;
 }
 
+// Half-tile views (hqml_internal.hpp): the group of full view v on 12 positions.  Low
+// positions 0..3 as in the full view; the rotated high qubits split over H1 registers
+// (positions 4..7) and H2 registers (8..11); free register positions take other high
+// qubits.  Checked: (a) where the statistics of a rotated qubit are taken (H1 for
+// positions 0, 1, 4..7; H2 for 8..11) none of its chain neighbours sits at a register
+// position of that layout; (b) no qubit at positions 8, 9 neighbours one at 10, 11 (the
+// diagonal's two per-thread factor tables in H2).
+bool half_view_ok(const int *perm, uint32_t group)
+{
+    constexpr uint32_t kH1Stat = 0x0F3u, kH1Regs = 0x0F0u, kH2Regs = 0xF00u;
+    for (int a = 0; a < kHalfBits; ++a) {
+        if (!((group >> a) & 1u)) continue;
+        const uint32_t regs = ((kH1Stat >> a) & 1u) ? kH1Regs : kH2Regs;
+        for (int b = 0; b < kHalfBits; ++b)
+            if (b != a && ((regs >> b) & 1u) && adjacent(perm[a], perm[b])) return false;
+    }
+    for (int a : {8, 9})
+        for (int b : {10, 11})
+            if (adjacent(perm[a], perm[b])) return false;
+    return true;
+}
+
+bool build_half_view(int n, const ViewDev &full, ViewDevH *out)
+{
+    std::vector<int> rhigh, fill;
+    const uint32_t g = (uint32_t)full.group_mask;
+    for (int pos = 4; pos < kTileBits; ++pos)
+        if ((g >> pos) & 1u) rhigh.push_back(full.perm[pos]);
+    for (int q = kLowQubits; q < n; ++q)
+        if (full.inv[q] < 0 || !((g >> full.inv[q]) & 1u)) fill.push_back(q);
+    std::sort(fill.rbegin(), fill.rend());   // fillers: highest first
+    const int kh = (int)rhigh.size();
+    if (kh > 8) return false;
+    int perm[kHalfBits];
+    uint32_t group = 0;
+    for (int nl2 = std::max(0, kh - 4); nl2 <= std::min(4, kh); ++nl2) {
+        std::vector<int> pick(kh, 0);
+        std::fill(pick.end() - nl2, pick.end(), 1);
+        do {
+            for (int i = 0; i < kHalfBits; ++i) perm[i] = -1;
+            group = g & 3u;
+            for (int i = 0; i < kLowQubits; ++i) perm[i] = full.perm[i];
+            int p1 = 4, p2 = 8;
+            for (int k = 0; k < kh; ++k) {
+                const int pos = pick[k] ? p2++ : p1++;
+                perm[pos] = rhigh[k];
+                group |= 1u << pos;
+            }
+            std::vector<int> cand = fill;
+            bool ok = true;
+            for (int pos = 4; pos < kHalfBits && ok; ++pos) {
+                if (perm[pos] >= 0) continue;
+                ok = false;
+                for (size_t ci = 0; ci < cand.size(); ++ci) {
+                    perm[pos] = cand[ci];
+                    if (half_view_ok(perm, group)) {
+                        cand.erase(cand.begin() + (long)ci);
+                        ok = true;
+                        break;
+                    }
+                    perm[pos] = -1;
+                }
+            }
+            if (ok && half_view_ok(perm, group)) {
+                ViewDevH &d = *out;
+                std::memset(&d, 0, sizeof(d));
+                int inv[32];
+                for (int i = 0; i < 32; ++i) inv[i] = -1;
+                for (int i = 0; i < kHalfBits; ++i) {
+                    d.perm[i] = perm[i];
+                    inv[perm[i]] = i;
+                    d.slot_pos[i] = ((group >> i) & 1u) ? full.inv[perm[i]] : kTileBits - 1;
+                }
+                d.group_mask = (int32_t)group;
+                int nt = 0;
+                for (int q = 0; q < n; ++q)
+                    if (inv[q] < 0) d.tile_q[nt++] = q;
+                d.n_tile = nt;
+                return nt == n - kHalfBits;
+            }
+        } while (std::next_permutation(pick.begin(), pick.end()));
+    }
+    return false;
+}
+
 }  // namespace
+
+int stat_tiles(const Plan &p, int compute64)
+{
+    return (p.half && !compute64) ? 2 * p.T : p.T;
+}
 
 bool make_obs_view(int n, uint32_t xmask, ViewDev *out, std::string *err)
 {
@@ -262,6 +352,11 @@ bool make_plan(int n, int L, int ckpt_block, Plan *out, std::string *err, bool c
         return true;
     }
     const int V = p.V;
+    p.hviews.assign(V, ViewDevH{});
+    p.half = true;
+    for (int v = 0; v < V; ++v)
+        if (!build_half_view(n, p.views[v], &p.hviews[v])) p.half = false;
+    if (!p.half) p.hviews.clear();
     auto group_has = [&](int v, int q) {
         const int pos = p.views[v].inv[q];
         return pos >= 0 && ((p.views[v].group_mask >> pos) & 1);
@@ -344,7 +439,8 @@ Workspace size_workspace(const Plan &p, int max_batch, int storage, int compute6
     // doubles), statmap (int2),
     // init_u (4 reals per sample and qubit), views, per-sample E / dL/dE / scratch, loss.
     w.tables_bytes = Ln * (6 * 8 + 1 + 2 * r + 4 * r * (p.cnot ? 2 : 1) + 9 * 8 + 8) + B * p.n * 4 * r +
-                     (size_t)(std::max(p.V, 1) + 1) * sizeof(ViewDev) + B * (8 * 3 + 4) + 64;
+                     (size_t)(std::max(p.V, 1) + 1) * sizeof(ViewDev) + p.hviews.size() * sizeof(ViewDevH) +
+                     B * (8 * 3 + 4) + 64;
     const size_t S_bytes = B * Ln * 3 * 8;
     if (p.small) {
         w.n_saved = 1;
@@ -366,13 +462,14 @@ Workspace size_workspace(const Plan &p, int max_batch, int storage, int compute6
         w.n_saved = p.c + w.n_ckpt;
         w.part_passes = p.c + (int)p.stats_only.size();
     }
-    w.part_bytes = (size_t)w.part_passes * B * p.T * kSlots * r;
+    const int Ts = stat_tiles(p, compute64);
+    w.part_bytes = (size_t)w.part_passes * B * Ts * kSlots * r;
     const size_t epart = B * p.T * r;
-    if (p.T > kTileChunk) {
-        w.tile_chunks = p.T / kTileChunk;
+    if (Ts > kTileChunk) {
+        w.tile_chunks = Ts / kTileChunk;
         w.part2_bytes = (size_t)w.part_passes * B * w.tile_chunks * kSlots * 8;
-        w.epart2_bytes = B * (size_t)w.tile_chunks * 8;
     }
+    if (p.T > kTileChunk) w.epart2_bytes = B * (size_t)(p.T / kTileChunk) * 8;
     // the CNOT plan keeps a second lambda buffer (passes that write lambda through the chain)
     w.total = (size_t)w.n_saved * w.state_bytes + w.lam_bytes * (p.cnot ? 2 : 1) + w.part_bytes + w.tables_bytes +
               S_bytes + epart + w.part2_bytes + w.epart2_bytes;
@@ -420,6 +517,30 @@ std::string describe_plan(const Plan &p)
         s += "\"perm\":[";
         for (int i = 0; i < kTileBits; ++i) {
             std::snprintf(buf, sizeof buf, "%s%d", i ? "," : "", d.perm[i]);
+            s += buf;
+        }
+        s += "],\"tile_q\":[";
+        for (int i = 0; i < d.n_tile; ++i) {
+            std::snprintf(buf, sizeof buf, "%s%d", i ? "," : "", d.tile_q[i]);
+            s += buf;
+        }
+        std::snprintf(buf, sizeof buf, "],\"group_mask\":%d}", d.group_mask);
+        s += buf;
+    }
+    s += "],\"half\":";
+    s += p.half ? "true" : "false";
+    s += ",\"hviews\":[";
+    for (size_t v = 0; v < p.hviews.size(); ++v) {
+        const ViewDevH &d = p.hviews[v];
+        s += v ? ",{" : "{";
+        s += "\"perm\":[";
+        for (int i = 0; i < kHalfBits; ++i) {
+            std::snprintf(buf, sizeof buf, "%s%d", i ? "," : "", d.perm[i]);
+            s += buf;
+        }
+        s += "],\"slot_pos\":[";
+        for (int i = 0; i < kHalfBits; ++i) {
+            std::snprintf(buf, sizeof buf, "%s%d", i ? "," : "", d.slot_pos[i]);
             s += buf;
         }
         s += "],\"tile_q\":[";

@@ -33,6 +33,9 @@ struct Plan {
     int V = 0;                           // views (tile path)
     int T = 1;                           // tiles per sample
     std::vector<ViewDev> views;
+    std::vector<ViewDevH> hviews;        // half-tile views of the same groups (CZ-chain plan)
+    bool half = false;                   // every view has a half-tile view: the fp32 adjoint's
+                                         // general passes run on half tiles
     std::vector<PassPlan> fwd;           // forward passes in order
     std::vector<int> stats_only;         // views needing a layer-0 stats-only backward pass
     std::vector<StatLoc> statmap;        // [L*n]
@@ -70,6 +73,10 @@ struct Workspace {
     size_t tables_bytes = 0;
     size_t total = 0;
 };
+
+// Statistics partials per sample of a backward pass: 2T when the fp32 adjoint runs its
+// general passes on half tiles (p.half and fp32 compute), else T.
+int stat_tiles(const Plan &p, int compute64);
 
 // storage: 0 fp32, 1 bf16, 2 fp64 saved states; compute64: arithmetic (and lambda,
 // tables, partial sums) in fp64.

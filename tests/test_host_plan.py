@@ -117,7 +117,9 @@ def test_entangler_config_host_only():
     cz = hq.hqml_workspace_bytes(hq.make_config(20, 10, 4))
     cn = hq.hqml_workspace_bytes(hq.make_config(20, 10, 4, entangler="cnot"))
     st = 4 * (1 << 20) * 8
-    assert cn - cz >= 10 * st   # 19 saved pass outputs instead of 10, plus lambda
+    # 19 saved pass outputs instead of 10, plus lambda; the statistics partials differ by
+    # less than half a state (the CZ plan's general passes write two rows per tile)
+    assert cn - cz >= 9.5 * st
     # X/Y factors: the chain-conjugated string has X on q and q+1 for each X/Y on q; it
     # must fit the observable view (at most 9 such qubits above qubit 3)
     assert hq.hqml_workspace_bytes(hq.make_config(20, 3, 2, entangler="cnot", obs_x_mask=0b1010 << 4)) > 0
@@ -221,6 +223,33 @@ def test_views_keep_chain_neighbours_apart(n):
             for a in regs:
                 if (gm >> a) & 1:
                     assert all(abs(perm[a] - perm[b]) != 1 for b in regs if b != a)
+
+
+@pytest.mark.parametrize("n", list(range(14, 30)))
+def test_half_views_match_full_views(n):
+    """Half-tile views (the fp32 adjoint's general passes): each rotates exactly the group
+    of the full view with the same index, holds qubits 0..3 at positions 0..3 with the
+    rotated low qubits at 0, 1, keeps the chain neighbours of a rotated qubit off the
+    register positions of the layout where its statistics are taken (H1: positions 0, 1,
+    4..7 against registers 4..7; H2: 8..11 against 8..11) and positions 8, 9 apart from
+    10, 11, and sends each rotated qubit's statistics to its full-view slot."""
+    p = _plan(n, 3)
+    assert p["half"] and len(p["hviews"]) == len(p["views"])
+    for v, h in zip(p["views"], p["hviews"]):
+        perm, gm, hperm, hg = v["perm"], v["group_mask"], h["perm"], h["group_mask"]
+        rot = {perm[i] for i in range(13) if (gm >> i) & 1}
+        hrot = {hperm[i] for i in range(12) if (hg >> i) & 1}
+        assert hrot == rot
+        assert sorted(hperm[:4]) == [0, 1, 2, 3] and hg & 0b1100 == 0 and hg >> 12 == 0
+        assert sorted(hperm + h["tile_q"]) == list(range(n))
+        for a in range(12):
+            if not (hg >> a) & 1:
+                assert h["slot_pos"][a] == 12
+                continue
+            assert perm[h["slot_pos"][a]] == hperm[a]
+            regs = (4, 5, 6, 7) if a in (0, 1, 4, 5, 6, 7) else (8, 9, 10, 11)
+            assert all(abs(hperm[a] - hperm[b]) != 1 for b in regs if b != a)
+        assert all(abs(hperm[a] - hperm[b]) != 1 for a in (8, 9) for b in (10, 11))
 
 
 @pytest.mark.parametrize("n", [14, 16, 21, 29])
