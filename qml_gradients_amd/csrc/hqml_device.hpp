@@ -142,6 +142,10 @@ __device__ __forceinline__ void row_sum16x3(R &a, R &b, R &c)
     a += dppf<0x140>(a);
     b += dppf<0x140>(b);
     c += dppf<0x140>(c);
+    // The callers use the sums in one lane of the row only; without this the compiler
+    // moves the last add under that lane's branch, where it cannot take the DPP operand,
+    // and emits a separate DPP move (and the move's zero fill) instead of one DPP add.
+    asm volatile("" : "+v"(a), "+v"(b), "+v"(c));
 }
 
 __device__ __forceinline__ float2 cmul(float2 a, float2 b)

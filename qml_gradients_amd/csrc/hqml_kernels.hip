@@ -1605,13 +1605,30 @@ __device__ __forceinline__ bool nb_odd(uint32_t fixed, int q, int n)
 }
 
 // Plain (layer lb) and neighbour-signed (layer la, see stats_visit_merged) sums of one
-// position's statistics into its slots.
-__device__ __forceinline__ void hstat_out(float sx, float sy, float sz, float corr, bool odd, int sp, float *lds_stat,
-                                          int lane, int w)
+// position's statistics into its slots.  A DPP row is lane bits 0..3, i.e. positions 0..3,
+// which hold qubits 0..3: for a qubit q >= 5 neither chain neighbour is there, the
+// neighbours' sign is the same on the whole row, and the row leader forms the signed sums
+// from the plain ones (one reduction instead of two).  q is uniform, so is the branch.
+__device__ __forceinline__ void hstat_out(float sx, float sy, float sz, float corr, bool odd, int q, int sp,
+                                          float *lds_stat, int lane, int w)
 {
-    const float sg = odd ? -corr : corr;
-    stat_out3(sx * corr, sy * corr, sz * corr, lds_stat, (13 + sp) * 3, lane, w);
-    stat_out3(sx * sg, sy * sg, sz * sg, lds_stat, sp * 3, lane, w);
+    if (q >= 5) {
+        row_sum16x3(sx, sy, sz);
+        if ((lane & 15) == 15) {
+            const int r = w * 4 + (lane >> 4);
+            const float sg = odd ? -corr : corr;
+            lds_stat[((13 + sp) * 3 + 0) * 16 + r] = sx * corr;
+            lds_stat[((13 + sp) * 3 + 1) * 16 + r] = sy * corr;
+            lds_stat[((13 + sp) * 3 + 2) * 16 + r] = sz * corr;
+            lds_stat[(sp * 3 + 0) * 16 + r] = sx * sg;
+            lds_stat[(sp * 3 + 1) * 16 + r] = sy * sg;
+            lds_stat[(sp * 3 + 2) * 16 + r] = sz * sg;
+        }
+    } else {
+        const float sg = odd ? -corr : corr;
+        stat_out3(sx * corr, sy * corr, sz * corr, lds_stat, (13 + sp) * 3, lane, w);
+        stat_out3(sx * sg, sy * sg, sz * sg, lds_stat, sp * 3, lane, w);
+    }
 }
 
 // Factor tables of D_l in layout H2: D(i) = lo[j & 3] * hi[j >> 2] for register j
@@ -1622,30 +1639,50 @@ struct HDiag {
     float2 hi[4];
 };
 
-__device__ __forceinline__ HDiag hdiag_tables(const float *dw, int n, int layer, const int *rq, uint32_t fixed_bits)
+// Factor of qubit q in D_l for bit value 1 (sel) or 0, read as uniform values into scalar
+// registers before the per-lane choice (otherwise the compiler turns the choice into a
+// per-lane address and a vector load per qubit).
+__device__ __forceinline__ float rfl(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ float2 hfactor(const float4 *wl, int q, bool sel)
+{
+    const float4 f = ldu4(reinterpret_cast<const float *>(wl + __builtin_amdgcn_readfirstlane(q)));
+    const float x = rfl(f.x), y = rfl(f.y), z = rfl(f.z), w = rfl(f.w);
+    return sel ? make_float2(z, w) : make_float2(x, y);
+}
+
+// tv: the thread's lane and wave bits (H2 positions 0..7); tile_bits: the tile's qubits.
+__device__ __forceinline__ HDiag hdiag_tables(const float *dw, int n, int layer, const HCtx &c, const ViewDevH &v,
+                                              uint32_t tv)
 {
     const float4 *wl = reinterpret_cast<const float4 *>(dw) + (size_t)layer * n;
-    uint32_t regq = 0;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) regq |= 1u << rq[m];
-    float2 c = make_float2(1.f, 0.f);
-    for (int q = 0; q < n; ++q) {
-        if (regq & (1u << q)) continue;
-        const float4 f = ldu4(reinterpret_cast<const float *>(wl + q));
-        c = cmul(c, ((fixed_bits >> q) & 1u) ? make_float2(f.z, f.w) : make_float2(f.x, f.y));
+    const uint32_t fixed_bits = c.fixed2;
+    // thread constant: lane and wave qubits (per lane), then the tile's qubits (uniform)
+    float2 ct = make_float2(1.f, 0.f);
+#pragma unroll 1
+    for (int k = 0; k < 8; ++k) ct = cmul(ct, hfactor(wl, ldu(&v.perm[k]), (tv >> k) & 1u));
+    const int nt = ldu(&v.n_tile);
+    float2 cu = make_float2(1.f, 0.f);
+    for (int k = 0; k < nt; ++k) {
+        const int q = ldu(&v.tile_q[k]);
+        cu = cmul(cu, hfactor(wl, q, (c.tile >> k) & 1));
     }
-    if (__builtin_popcount(fixed_bits & (fixed_bits >> 1)) & 1) {
-        c.x = -c.x;
-        c.y = -c.y;
+    float2 cc = cmul(ct, cu);
+    if (__builtin_popcount(fixed_bits & (fixed_bits >> 1)) & 1) {   // CZ signs among fixed qubits
+        cc.x = -cc.x;
+        cc.y = -cc.y;
     }
+    const int *rq = c.q2;
     float2 g0[4], g1[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int q = rq[m];
-        const float4 f = ldu4(reinterpret_cast<const float *>(wl + q));
-        g0[m] = make_float2(f.x, f.y);
-        g1[m] = make_float2(f.z, f.w);
-        if (nb_odd(fixed_bits, q, n)) {
+        g0[m] = hfactor(wl, q, false);
+        g1[m] = hfactor(wl, q, true);
+        if (nb_odd(fixed_bits, q, n)) {   // CZ with a fixed neighbour at 1
             g1[m].x = -g1[m].x;
             g1[m].y = -g1[m].y;
         }
@@ -1654,12 +1691,12 @@ __device__ __forceinline__ HDiag hdiag_tables(const float *dw, int n, int layer,
     HDiag t;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-        float2 v = cmul(c, cmul((a & 1) ? g1[0] : g0[0], (a & 2) ? g1[1] : g0[1]));
+        float2 x = cmul(cc, cmul((a & 1) ? g1[0] : g0[0], (a & 2) ? g1[1] : g0[1]));
         if (a == 3 && adj(0, 1)) {
-            v.x = -v.x;
-            v.y = -v.y;
+            x.x = -x.x;
+            x.y = -x.y;
         }
-        t.lo[a] = v;
+        t.lo[a] = x;
         float2 h = cmul((a & 1) ? g1[2] : g0[2], (a & 2) ? g1[3] : g0[3]);
         if (a == 3 && adj(2, 3)) {
             h.x = -h.x;
@@ -1710,14 +1747,15 @@ __global__ __launch_bounds__(kThreads, 4) void k_tile_bwdh(TilePassArgs a)
         const float W = hzsum<4, 0>(p, l, dz);
         float sx, sy;
         hxy_lane<0>(p, l, c.lane, sx, sy);
-        hstat_out(sx, sy, (c.lane & 1) ? -W : W, 1.f, nb_odd(c.fixed1, c.q0[0], n), ldu(&v.slot_pos[0]), lds_stat,
-                  c.lane, c.w);
+        hstat_out(sx, sy, (c.lane & 1) ? -W : W, 1.f, nb_odd(c.fixed1, c.q0[0], n), c.q0[0], ldu(&v.slot_pos[0]),
+                  lds_stat, c.lane, c.w);
         hxy_lane<1>(p, l, c.lane, sx, sy);
-        hstat_out(sx, sy, (c.lane & 2) ? -W : W, 1.f, nb_odd(c.fixed1, c.q0[1], n), ldu(&v.slot_pos[1]), lds_stat,
-                  c.lane, c.w);
+        hstat_out(sx, sy, (c.lane & 2) ? -W : W, 1.f, nb_odd(c.fixed1, c.q0[1], n), c.q0[1], ldu(&v.slot_pos[1]),
+                  lds_stat, c.lane, c.w);
 #define HQML_HSTAT1(M)                                                                                      \
     hxy_reg<M>(p, l, sx, sy);                                                                               \
-    hstat_out(sx, sy, dz[M], 1.f, nb_odd(c.fixed1, c.q1[M], n), ldu(&v.slot_pos[4 + M]), lds_stat, c.lane, c.w);
+    hstat_out(sx, sy, dz[M], 1.f, nb_odd(c.fixed1, c.q1[M], n), c.q1[M], ldu(&v.slot_pos[4 + M]), lds_stat, c.lane,  \
+              c.w);
         HQML_HSTAT1(0)
         HQML_HSTAT1(1)
         HQML_HSTAT1(2)
@@ -1736,7 +1774,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_tile_bwdh(TilePassArgs a)
         float sx, sy;
 #define HQML_HSTAT2(M)                                                                                       \
     hxy_reg<M>(p, l, sx, sy);                                                                                \
-    hstat_out(sx, sy, dz[M], corr, nb_odd(c.fixed2, c.q2[M], n), ldu(&v.slot_pos[8 + M]), lds_stat, c.lane, c.w);
+    hstat_out(sx, sy, dz[M], corr, nb_odd(c.fixed2, c.q2[M], n), c.q2[M], ldu(&v.slot_pos[8 + M]), lds_stat, c.lane, \
+              c.w);
         HQML_HSTAT2(0)
         HQML_HSTAT2(1)
         HQML_HSTAT2(2)
@@ -1749,7 +1788,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_tile_bwdh(TilePassArgs a)
     const HCoef b0 = hcoef<2>(rot_tf, n, lb, c.q0, c.gm0);
     hunrot_lane<0>(l, b0.k[0], c.lane);
     hunrot_lane<1>(l, b0.k[1], c.lane);
-    hdiag_dag(l, hdiag_tables(dw, n, a.diag, c.q2, c.fixed2), b1.F * b2.F * b0.F);
+    hdiag_dag(l, hdiag_tables(dw, n, a.diag, c, v, (uint32_t)threadIdx.x), b1.F * b2.F * b0.F);
     const HCoef a2 = hcoef<4>(rot_tf, n, la, c.q2, c.gm2);
     hunrot_regs(l, a2);
     const HCoef a0 = hcoef<2>(rot_tf, n, la, c.q0, c.gm0);
