@@ -8,10 +8,12 @@ fused forward pass, the fused adjoint passes and all reductions, with inputs
 already resident in device memory.  Prints one JSON line.
 
 Besides the throughput, the line carries:
-  roofline      the dominant kernel (the fused adjoint tile pass) against the
-                published HBM peak of 8 TB/s: its algorithmic state bytes per launch
-                (read the saved pass output, read and write lambda: 24 B per
-                amplitude and sample in fp32) / its mean launch time, from HIP
+  roofline      the dominant kernel (the fused adjoint tile pass: k_tile_bwdh, the
+                half-tile general shape, for all adjoint launches but the fused last
+                pass and the product-state pass of the fp32 CZ-chain plan) against the
+                published HBM peak of 8 TB/s: the adjoint launches' algorithmic state
+                bytes per launch (read the saved pass output, read and write lambda: 24 B
+                per amplitude and sample in fp32) / their mean launch time, from HIP
                 events recorded on the launch stream around every launch in a
                 separate instrumented loop (batch chunking off); "traffic" is the
                 measured HBM bytes per launch from rocprofv3 counters while the
@@ -97,7 +99,13 @@ def algorithmic_bytes(plan: dict, B: int, storage: str, compute: str = "fp32"):
     return fwd, bwd
 
 
-def algorithmic_flops_bwd(plan: dict, B: int):
+def half_tiles(plan: dict, compute: str = "fp32") -> bool:
+    """Whether the general adjoint passes run on half tiles (k_tile_bwdh): fp32 compute,
+    CZ-chain plan, every view with a half view."""
+    return bool(plan.get("half")) and not plan.get("cnot") and compute == "fp32"
+
+
+def algorithmic_flops_bwd(plan: dict, B: int, compute: str = "fp32"):
     """Floating-point operations the fused adjoint kernels perform per train step
     (FMA = 2, multiply or add = 1), per amplitude and sample of each launch:
       rotation (scaled tan form) on one state: 4 per qubit;
@@ -105,15 +113,19 @@ def algorithmic_flops_bwd(plan: dict, B: int):
       merged diagonal applied to lambda: 9 (to psi and lambda: 18); final lambda scale: 2.
     g = qubits the pass's view rotates, g1 / g2 = those at L1 / L2 register positions.
     The general and product-state shapes take both layers' statistics from one set of
-    sums (merged statistics) and rotate psi only by the L1 half of the later layer."""
+    sums (merged statistics) and rotate psi only by the L1 half of the later layer; on
+    half tiles that is the group's qubits at H1 register positions 4..7."""
     N = 1 << plan["n"]
     P = len(plan["passes"])
+    half = half_tiles(plan, compute)
     total = 0
     for k, ps in enumerate(plan["passes"]):
         gm = plan["views"][ps["view"]]["group_mask"]
         g = bin(gm).count("1")
         g2 = sum((gm >> p) & 1 for p in L2_POSITIONS)
         g1 = g - g2
+        if half and k != P - 1 and ps["rotA"] >= 0 and ps["diag"] >= 0 and ps["rotB"] >= 0 and not ps["init"]:
+            g1 = bin(plan["hviews"][ps["view"]]["group_mask"] & 0xF0).count("1")
         if k == P - 1 and not ps["init"]:
             # forward rotations, E, seed, statistics, un-rotations, scale
             f = 4 * g + 3 + 8 * g + 10 + 4 * g2 + 4 * g + 2
@@ -376,7 +388,10 @@ def main():
     fwd_b, bwd_b = algorithmic_bytes(plan, B, w.storage, args.compute)
     n_steps = args.instrumented_steps
 
-    bwd_flops = algorithmic_flops_bwd(plan, B)
+    bwd_flops = algorithmic_flops_bwd(plan, B, args.compute)
+    # the adjoint launches: half-tile general passes (all but the fused last pass and the
+    # product-state pass) when the plan has them, else the full-tile kernel
+    bwd_kernel = "k_tile_bwdh" if half_tiles(plan, args.compute) else "k_tile_bwd"
 
     def launches_and_ms(kind):
         if n_steps == 0 or cnt_k[kind] == 0:
@@ -413,8 +428,8 @@ def main():
 
     # dominant kernel against the published HBM peak; its arithmetic rate beside it (the
     # CNOT plan's adjoint passes each rotate one qubit group, so no ALU figure there)
-    roof_bwd = roof_hbm(hq.HQML_K_BWD_PASS, bwd_b, "k_tile_bwd")
-    roof_bwd_alu = None if plan.get("cnot") else roof_alu(hq.HQML_K_BWD_PASS, bwd_flops, bwd_b, "k_tile_bwd")
+    roof_bwd = roof_hbm(hq.HQML_K_BWD_PASS, bwd_b, bwd_kernel)
+    roof_bwd_alu = None if plan.get("cnot") else roof_alu(hq.HQML_K_BWD_PASS, bwd_flops, bwd_b, bwd_kernel)
     if roof_bwd_alu:
         roof_bwd_alu["peak_basis"] = ("non-packed fp32 FMA: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz "
                                       "(self-derived; packed FP32 is excluded from the build)")
