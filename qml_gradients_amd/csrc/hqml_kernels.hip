@@ -1292,10 +1292,13 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
 // arithmetic of others.  The arithmetic is that of the full-tile general shape (merged
 // statistics into the same slots), in this order: load psi and lambda (H1); merged
 // statistics of positions 0, 1 (lane bits: the partner lane's psi through a DPP quad
-// permutation) and 4..7 (register bits); un-rotate layer lb at 4..7 on both states;
-// transpose both; merged statistics of 8..11 (psi is then dead); on lambda: un-rotate lb at
-// 8..11 and at 0, 1, apply D_la^dagger, un-rotate la at 8..11 and at 0, 1; transpose;
-// un-rotate la at 4..7; store.
+// permutation) and 4..7 (register bits); transpose both states; merged statistics of
+// 8..11.  All of them are taken at the pass output (a qubit's statistics do not change
+// under the rotations of the other group qubits, which are not its chain neighbours), so
+// psi is never rotated and is dead here.  On lambda: un-rotate layer lb at 8..11 and 0, 1;
+// transpose; un-rotate lb at 4..7, apply D_la^dagger, un-rotate layer la at 4..7 and 0, 1;
+// transpose; un-rotate la at 8..11; store from H2, whose lane bits 0..3 are positions 0..3
+// as in H1, so the stores stay 128-byte runs.
 
 struct HTile {
     float re[kHalfRegs];
@@ -1311,7 +1314,7 @@ __host__ __device__ constexpr uint32_t hswz(uint32_t i) { return i ^ (((i >> 8) 
 struct HCtx {
     int lane, w, sample, tile;
     uint64_t tile_off;        // global amplitude offset of the tile's fixed (tile-index) bits
-    uint32_t t1;              // H1: thread's amplitude offset within the tile
+    uint32_t t1, t2;          // H1 / H2: thread's amplitude offset within the tile
     uint32_t a1, a2;          // swizzled LDS bases of the thread in H1 / H2
     uint32_t fixed1, fixed2;  // qubit bitmask of the thread's fixed bits (with the tile's) in H1 / H2
     uint32_t rs[4];           // H1: amplitude stride of register bit m (uniform)
@@ -1336,6 +1339,7 @@ __device__ __forceinline__ void hctx(HCtx &c, const ViewDevH &v, int T2, int blk
             t2 |= 1u << ldu(&v.perm[k]);
         }
     c.t1 = t1;
+    c.t2 = t2;
     c.a1 = hswz((uint32_t)(lane & 15) | ((uint32_t)(lane >> 4) << 8) | ((uint32_t)w << 10));
     c.a2 = hswz(tv);
 #pragma unroll
@@ -1394,14 +1398,19 @@ __device__ __forceinline__ void hload(HTile &t, const void *state, const HCtx &c
     }
 }
 
-__device__ __forceinline__ void hstore(const HTile &t, void *state, const HCtx &c, uint64_t nelem)
+// Store lambda in layout H2 (positions 0..3 are lane bits 0..3 here as in H1, so a 16-lane
+// row writes 16 consecutive amplitudes).
+__device__ __forceinline__ void hstore2(const HTile &t, void *state, const HCtx &c, uint64_t nelem)
 {
     char *base = reinterpret_cast<char *>(state) + ((uint64_t)c.sample * nelem + c.tile_off) * 8u;
-    const uint32_t tb = opaque_u32(c.t1) * 8u;
+    const uint32_t tb = opaque_u32(c.t2) * 8u;
 #pragma unroll
     for (int j = 0; j < kHalfRegs; ++j) {
-        const uint32_t off = tb + hroff(c, j) * 8u;
-        StateIO<0>::store(reinterpret_cast<float2 *>(base + off), t.re[j], t.im[j]);
+        uint32_t o = 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            if (j & (1 << m)) o += 1u << c.q2[m];
+        StateIO<0>::store(reinterpret_cast<float2 *>(base + tb + o * 8u), t.re[j], t.im[j]);
     }
 }
 
@@ -1654,16 +1663,22 @@ __device__ __forceinline__ float2 hfactor(const float4 *wl, int q, bool sel)
     return sel ? make_float2(z, w) : make_float2(x, y);
 }
 
-// tv: the thread's lane and wave bits (H2 positions 0..7); tile_bits: the tile's qubits.
+// Factor tables of D_l in layout H1 (H1 = true: registers at positions 4..7, lo = 4, 5 and
+// hi = 6, 7) or H2 (registers at 8..11, lo = 8, 9 and hi = 10, 11).  tv: the thread's lane
+// and wave bits, at H1 positions 0,1,2,3,8,9,10,11 or H2 positions 0..7.
+template <bool H1>
 __device__ __forceinline__ HDiag hdiag_tables(const float *dw, int n, int layer, const HCtx &c, const ViewDevH &v,
                                               uint32_t tv)
 {
     const float4 *wl = reinterpret_cast<const float4 *>(dw) + (size_t)layer * n;
-    const uint32_t fixed_bits = c.fixed2;
+    const uint32_t fixed_bits = H1 ? c.fixed1 : c.fixed2;
     // thread constant: lane and wave qubits (per lane), then the tile's qubits (uniform)
     float2 ct = make_float2(1.f, 0.f);
 #pragma unroll 1
-    for (int k = 0; k < 8; ++k) ct = cmul(ct, hfactor(wl, ldu(&v.perm[k]), (tv >> k) & 1u));
+    for (int k = 0; k < 8; ++k) {
+        const int pos = H1 ? (k < 4 ? k : k + 4) : k;
+        ct = cmul(ct, hfactor(wl, ldu(&v.perm[pos]), (tv >> k) & 1u));
+    }
     const int nt = ldu(&v.n_tile);
     float2 cu = make_float2(1.f, 0.f);
     for (int k = 0; k < nt; ++k) {
@@ -1675,7 +1690,7 @@ __device__ __forceinline__ HDiag hdiag_tables(const float *dw, int n, int layer,
         cc.x = -cc.x;
         cc.y = -cc.y;
     }
-    const int *rq = c.q2;
+    const int *rq = H1 ? c.q1 : c.q2;
     float2 g0[4], g1[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -1707,7 +1722,7 @@ __device__ __forceinline__ HDiag hdiag_tables(const float *dw, int n, int layer,
     return t;
 }
 
-// s * D^dagger on a half tile in H2.
+// s * D^dagger on a half tile (the tables of its layout).
 __device__ __forceinline__ void hdiag_dag(HTile &t, HDiag d, float s)
 {
 #pragma unroll
@@ -1762,19 +1777,15 @@ __global__ __launch_bounds__(kThreads, 4) void k_tile_bwdh(TilePassArgs a)
         HQML_HSTAT1(3)
 #undef HQML_HSTAT1
     }
-    const HCoef b1 = hcoef<4>(rot_tf, n, lb, c.q1, c.gm1);
-    hunrot_regs(p, b1);
-    hunrot_regs(l, b1);
     htranspose(p, lds, c.a1, c.a2, true);
     htranspose(l, lds, c.a1, c.a2, true);
-    {   // positions 8..11 (H2); both states carry scale 1 / b1.F
+    {   // positions 8..11 (H2), also at the pass output
         float dz[4];
         (void)hzsum<4, 0>(p, l, dz);
-        const float corr = b1.F * b1.F;
         float sx, sy;
 #define HQML_HSTAT2(M)                                                                                       \
     hxy_reg<M>(p, l, sx, sy);                                                                                \
-    hstat_out(sx, sy, dz[M], corr, nb_odd(c.fixed2, c.q2[M], n), c.q2[M], ldu(&v.slot_pos[8 + M]), lds_stat, c.lane, \
+    hstat_out(sx, sy, dz[M], 1.f, nb_odd(c.fixed2, c.q2[M], n), c.q2[M], ldu(&v.slot_pos[8 + M]), lds_stat, c.lane, \
               c.w);
         HQML_HSTAT2(0)
         HQML_HSTAT2(1)
@@ -1782,21 +1793,25 @@ __global__ __launch_bounds__(kThreads, 4) void k_tile_bwdh(TilePassArgs a)
         HQML_HSTAT2(3)
 #undef HQML_HSTAT2
     }
-    // lambda: the rest of layer lb, D_la^dagger (which removes the scales so far), layer la
+    // lambda: layer lb at 8..11 and 0, 1 (H2), at 4..7 (H1); D_la^dagger (H1), which removes
+    // the scales so far; layer la at 4..7 and 0, 1 (H1), at 8..11 (H2); store from H2
     const HCoef b2 = hcoef<4>(rot_tf, n, lb, c.q2, c.gm2);
     hunrot_regs(l, b2);
     const HCoef b0 = hcoef<2>(rot_tf, n, lb, c.q0, c.gm0);
     hunrot_lane<0>(l, b0.k[0], c.lane);
     hunrot_lane<1>(l, b0.k[1], c.lane);
-    hdiag_dag(l, hdiag_tables(dw, n, a.diag, c, v, (uint32_t)threadIdx.x), b1.F * b2.F * b0.F);
-    const HCoef a2 = hcoef<4>(rot_tf, n, la, c.q2, c.gm2);
-    hunrot_regs(l, a2);
+    htranspose(l, lds, c.a1, c.a2, false);
+    const HCoef b1 = hcoef<4>(rot_tf, n, lb, c.q1, c.gm1);
+    hunrot_regs(l, b1);
+    hdiag_dag(l, hdiag_tables<true>(dw, n, a.diag, c, v, (uint32_t)threadIdx.x), b1.F * b2.F * b0.F);
+    const HCoef a1 = hcoef<4>(rot_tf, n, la, c.q1, c.gm1);
+    hunrot_regs(l, a1);
     const HCoef a0 = hcoef<2>(rot_tf, n, la, c.q0, c.gm0);
     hunrot_lane<0>(l, a0.k[0], c.lane);
     hunrot_lane<1>(l, a0.k[1], c.lane);
-    htranspose(l, lds, c.a1, c.a2, false);
-    const HCoef a1 = hcoef<4>(rot_tf, n, la, c.q1, c.gm1);
-    hunrot_regs(l, a1);
+    htranspose(l, lds, c.a1, c.a2, true);
+    const HCoef a2 = hcoef<4>(rot_tf, n, la, c.q2, c.gm2);
+    hunrot_regs(l, a2);
     const float sl = a2.F * a0.F * a1.F;
     if (sl != 1.f) {
 #pragma unroll
@@ -1805,7 +1820,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_tile_bwdh(TilePassArgs a)
             l.im[j] *= sl;
         }
     }
-    hstore(l, a.lam, c, nelem);
+    hstore2(l, a.lam, c, nelem);
     flush_merged(lds_stat, static_cast<float *>(a.stat_part) + ((size_t)c.sample * T2 + c.tile) * kSlots, false,
                  *a.view, rot_tf, dw, n, a.diag, lb);
 }

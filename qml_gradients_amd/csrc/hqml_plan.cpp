@@ -151,8 +151,8 @@ bool build_views(int n, Plan &p, std::string *err)
 // (positions 4..7) and H2 registers (8..11); free register positions take other high
 // qubits.  Checked: (a) where the statistics of a rotated qubit are taken (H1 for
 // positions 0, 1, 4..7; H2 for 8..11) none of its chain neighbours sits at a register
-// position of that layout; (b) no qubit at positions 8, 9 neighbours one at 10, 11 (the
-// diagonal's two per-thread factor tables in H2).
+// position of that layout; (b) no qubit at positions 8, 9 neighbours one at 10, 11, and
+// none at 4, 5 one at 6, 7 (the diagonal's two per-thread factor tables in H2 or H1).
 bool half_view_ok(const int *perm, uint32_t group)
 {
     constexpr uint32_t kH1Stat = 0x0F3u, kH1Regs = 0x0F0u, kH2Regs = 0xF00u;
@@ -164,6 +164,9 @@ bool half_view_ok(const int *perm, uint32_t group)
     }
     for (int a : {8, 9})
         for (int b : {10, 11})
+            if (adjacent(perm[a], perm[b])) return false;
+    for (int a : {4, 5})
+        for (int b : {6, 7})
             if (adjacent(perm[a], perm[b])) return false;
     return true;
 }

@@ -231,8 +231,9 @@ def test_half_views_match_full_views(n):
     of the full view with the same index, holds qubits 0..3 at positions 0..3 with the
     rotated low qubits at 0, 1, keeps the chain neighbours of a rotated qubit off the
     register positions of the layout where its statistics are taken (H1: positions 0, 1,
-    4..7 against registers 4..7; H2: 8..11 against 8..11) and positions 8, 9 apart from
-    10, 11, and sends each rotated qubit's statistics to its full-view slot."""
+    4..7 against registers 4..7; H2: 8..11 against 8..11), positions 8, 9 apart from 10, 11
+    and 4, 5 from 6, 7 (the diagonal's factor tables), and sends each rotated qubit's
+    statistics to its full-view slot."""
     p = _plan(n, 3)
     assert p["half"] and len(p["hviews"]) == len(p["views"])
     for v, h in zip(p["views"], p["hviews"]):
@@ -250,6 +251,7 @@ def test_half_views_match_full_views(n):
             regs = (4, 5, 6, 7) if a in (0, 1, 4, 5, 6, 7) else (8, 9, 10, 11)
             assert all(abs(hperm[a] - hperm[b]) != 1 for b in regs if b != a)
         assert all(abs(hperm[a] - hperm[b]) != 1 for a in (8, 9) for b in (10, 11))
+        assert all(abs(hperm[a] - hperm[b]) != 1 for a in (4, 5) for b in (6, 7))
 
 
 @pytest.mark.parametrize("n", [14, 16, 21, 29])
