@@ -100,9 +100,9 @@ def algorithmic_bytes(plan: dict, B: int, storage: str, compute: str = "fp32"):
 
 
 def half_tiles(plan: dict, compute: str = "fp32") -> bool:
-    """Whether the general adjoint passes run on half tiles (k_tile_bwdh): fp32 compute,
-    CZ-chain plan, every view with a half view."""
-    return bool(plan.get("half")) and not plan.get("cnot") and compute == "fp32"
+    """Whether the general adjoint passes run on half tiles (k_tile_bwdh): the CZ-chain
+    tile plan with a half view for every view (either compute type)."""
+    return bool(plan.get("half")) and not plan.get("cnot")
 
 
 def algorithmic_flops_bwd(plan: dict, B: int, compute: str = "fp32"):

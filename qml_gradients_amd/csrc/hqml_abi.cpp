@@ -58,7 +58,7 @@ struct hqml_ctx {
     void *init_u = nullptr;
     ViewDev *views = nullptr;
     ViewDevH *hviews = nullptr;  // half-tile views (general adjoint passes on half tiles)
-    bool half = false;           // fp32 CZ-chain tile plan whose views all have half views
+    bool half = false;           // CZ-chain tile plan whose views all have half views
     int stat_mul = 1;            // statistics partials per full tile: 2 with half tiles
     int2 *statmap = nullptr;
     double *dlde = nullptr;
@@ -780,7 +780,7 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     c->H = static_cast<double *>(grab(Ln * 9 * 8));
     c->init_u = grab((size_t)B * plan.n * 4 * c->rb);
     if (!plan.small) c->views = static_cast<ViewDev *>(grab((plan.views.size() + 1) * sizeof(ViewDev)));
-    c->half = !plan.small && !plan.cnot && plan.half && !c->r64;
+    c->half = !plan.small && !plan.cnot && plan.half;
     c->stat_mul = plan.small ? 1 : stat_tiles(plan, c->r64) / plan.T;
     if (c->half) c->hviews = static_cast<ViewDevH *>(grab(plan.hviews.size() * sizeof(ViewDevH)));
     c->statmap = static_cast<int2 *>(grab(Ln * sizeof(int2)));

@@ -67,8 +67,8 @@ struct ViewDev {
     int32_t pad[3];
 };
 
-// Half tile of the fp32 adjoint pass (hqml_kernels.hip, k_tile_bwdh): 2^12 amplitudes,
-// 256 threads x 16 registers, so that four workgroups share a compute unit.
+// Half tile of the adjoint pass (hqml_kernels.hip, k_tile_bwdh): 2^12 amplitudes, 256
+// threads x 16 registers, so that four workgroups share a compute unit (two in fp64).
 // Layout H1 (global-memory layout): regs  <- positions 4..7
 //                                    lanes <- positions 0,1,2,3,8,9
 //                                    waves <- positions 10,11
@@ -105,7 +105,7 @@ enum PassFlags : int {
     PF_GATHER = 128,     // forward: read the input at P^-1(i) (the CNOT chain);
                          // backward: write lambda back to P^-1(i)
     PF_OBS_NEG = 256,    // observable pass: the Pauli string carries an extra sign -1
-    PF_HALF = 512        // backward: the general shape on half tiles (k_tile_bwdh, fp32)
+    PF_HALF = 512        // backward: the general shape on half tiles (k_tile_bwdh)
 };
 
 struct TilePassArgs {

@@ -1283,7 +1283,7 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
     flush_stats(lds_stat, stat_row<R>(a, c), a.stat_mul == 2);
 }
 
-// ------------------------------------------------------------------ half-tile adjoint pass (fp32)
+// ------------------------------------------------------------------ half-tile adjoint pass
 //
 // The general adjoint shape [Ry-layer la on the group, D_la, Ry-layer lb on the group] on
 // half tiles: 2^12 amplitudes in 256 threads x 16 registers (layouts H1 / H2,
@@ -1298,11 +1298,13 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
 // psi is never rotated and is dead here.  On lambda: un-rotate layer lb at 8..11 and 0, 1;
 // transpose; un-rotate lb at 4..7, apply D_la^dagger, un-rotate layer la at 4..7 and 0, 1;
 // transpose; un-rotate la at 8..11; store from H2, whose lane bits 0..3 are positions 0..3
-// as in H1, so the stores stay 128-byte runs.
+// as in H1, so the stores stay 128-byte runs.  Written once for the compute type R: in fp64
+// (complex128 lambda) the two states take 128 VGPRs and two workgroups share a compute unit.
 
+template <typename R>
 struct HTile {
-    float re[kHalfRegs];
-    float im[kHalfRegs];
+    R re[kHalfRegs];
+    R im[kHalfRegs];
 };
 
 // LDS swizzle of the 12-bit local index: bit 4 ^= bit 8.  Linear over GF(2).  A half-wave
@@ -1381,16 +1383,17 @@ __device__ __forceinline__ uint32_t hroff(const HCtx &c, int j)
 }
 
 // Global-memory access of a half tile in layout H1 (NT: non-temporal loads).
-template <int ST, bool NT>
-__device__ __forceinline__ void hload(HTile &t, const void *state, const HCtx &c, uint64_t nelem)
+template <int ST, bool NT, typename R>
+__device__ __forceinline__ void hload(HTile<R> &t, const void *state, const HCtx &c, uint64_t nelem)
 {
     using IO = StateIO<ST>;
     constexpr uint32_t esz = sizeof(typename IO::elem);
+    using Off = TileOff<esz>;
     const char *base = reinterpret_cast<const char *>(state) + ((uint64_t)c.sample * nelem + c.tile_off) * esz;
-    const uint32_t tb = c.t1 * esz;
+    const Off tb = (Off)c.t1 * esz;
 #pragma unroll
     for (int j = 0; j < kHalfRegs; ++j) {
-        const uint32_t off = tb + hroff(c, j) * esz;
+        const Off off = tb + (Off)hroff(c, j) * esz;
         if constexpr (NT)
             IO::load(reinterpret_cast<const typename IO::elem *>(base + off), t.re[j], t.im[j]);
         else
@@ -1400,77 +1403,84 @@ __device__ __forceinline__ void hload(HTile &t, const void *state, const HCtx &c
 
 // Store lambda in layout H2 (positions 0..3 are lane bits 0..3 here as in H1, so a 16-lane
 // row writes 16 consecutive amplitudes).
-__device__ __forceinline__ void hstore2(const HTile &t, void *state, const HCtx &c, uint64_t nelem)
+template <typename R>
+__device__ __forceinline__ void hstore2(const HTile<R> &t, void *state, const HCtx &c, uint64_t nelem)
 {
-    char *base = reinterpret_cast<char *>(state) + ((uint64_t)c.sample * nelem + c.tile_off) * 8u;
-    const uint32_t tb = opaque_u32(c.t2) * 8u;
+    using IO = StateIO<kLamIO<R>>;
+    constexpr uint32_t esz = sizeof(typename IO::elem);
+    using Off = TileOff<esz>;
+    char *base = reinterpret_cast<char *>(state) + ((uint64_t)c.sample * nelem + c.tile_off) * esz;
+    const Off tb = (Off)opaque_u32(c.t2) * esz;
 #pragma unroll
     for (int j = 0; j < kHalfRegs; ++j) {
         uint32_t o = 0;
 #pragma unroll
         for (int m = 0; m < 4; ++m)
             if (j & (1 << m)) o += 1u << c.q2[m];
-        StateIO<0>::store(reinterpret_cast<float2 *>(base + tb + o * 8u), t.re[j], t.im[j]);
+        IO::store(reinterpret_cast<typename IO::elem *>(base + tb + (Off)o * esz), t.re[j], t.im[j]);
     }
 }
 
-// Move a half tile between H1 and H2 through the 32 KB LDS buffer.
-__device__ __forceinline__ void htranspose(HTile &t, float2 *lds, uint32_t a1, uint32_t a2, bool from_h1)
+// Move a half tile between H1 and H2 through the LDS buffer (32 KB in fp32, 64 KB in fp64).
+template <typename R>
+__device__ __forceinline__ void htranspose(HTile<R> &t, V2<R> *lds, uint32_t a1, uint32_t a2, bool from_h1)
 {
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kHalfRegs; ++j) {
         const uint32_t i = from_h1 ? (a1 ^ ((uint32_t)j << 4)) : (a2 ^ hswz((uint32_t)j << 8));
-        lds[i] = make_float2(t.re[j], t.im[j]);
+        lds[i] = mk2(t.re[j], t.im[j]);
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kHalfRegs; ++j) {
         const uint32_t i = from_h1 ? (a2 ^ hswz((uint32_t)j << 8)) : (a1 ^ ((uint32_t)j << 4));
-        const float2 v = lds[i];
+        const V2<R> v = lds[i];
         t.re[j] = v.x;
         t.im[j] = v.y;
     }
 }
 
 // Ry (kk = k) or Ry^dagger (kk = -k) on register bit M, scale f left out (as rot_bit).
-template <int M>
-__device__ __forceinline__ void hrot_bit(HTile &t, float kk)
+template <int M, typename R>
+__device__ __forceinline__ void hrot_bit(HTile<R> &t, R kk)
 {
 #pragma unroll
     for (int j = 0; j < kHalfRegs; ++j) {
         if (j & (1 << M)) continue;
         const int o = j | (1 << M);
-        const float ar = t.re[j], ai = t.im[j], br = t.re[o], bi = t.im[o];
-        t.re[j] = fmaf(-kk, br, ar);
-        t.im[j] = fmaf(-kk, bi, ai);
-        t.re[o] = fmaf(kk, ar, br);
-        t.im[o] = fmaf(kk, ai, bi);
+        const R ar = t.re[j], ai = t.im[j], br = t.re[o], bi = t.im[o];
+        t.re[j] = fmar(-kk, br, ar);
+        t.im[j] = fmar(-kk, bi, ai);
+        t.re[o] = fmar(kk, ar, br);
+        t.im[o] = fmar(kk, ai, bi);
     }
 }
 
+template <typename R>
 struct HCoef {
-    float k[4];
-    float F;      // product of the scale factors of the rotated bits
+    R k[4];
+    R F;      // product of the scale factors of the rotated bits
 };
 
 // Tan-form coefficients of NB positions (qubits q[m]); positions outside mask: identity.
-template <int NB>
-__device__ __forceinline__ HCoef hcoef(const float *rot_tf, int n, int layer, const int *q, uint32_t mask)
+template <int NB, typename R>
+__device__ __forceinline__ HCoef<R> hcoef(const R *rot_tf, int n, int layer, const int *q, uint32_t mask)
 {
-    HCoef rc;
-    rc.F = 1.f;
+    HCoef<R> rc;
+    rc.F = (R)1;
 #pragma unroll
     for (int m = 0; m < NB; ++m) {
-        const float2 kf = ldu2(rot_tf + ((size_t)layer * n + q[m]) * 2);
+        const V2<R> kf = ldu2(rot_tf + ((size_t)layer * n + q[m]) * 2);
         const bool on = (mask >> m) & 1u;
-        rc.k[m] = on ? kf.x : 0.f;
-        rc.F *= on ? kf.y : 1.f;
+        rc.k[m] = on ? kf.x : (R)0;
+        rc.F *= on ? kf.y : (R)1;
     }
     return rc;
 }
 
-__device__ __forceinline__ void hunrot_regs(HTile &t, const HCoef &rc)
+template <typename R>
+__device__ __forceinline__ void hunrot_regs(HTile<R> &t, const HCoef<R> &rc)
 {
     hrot_bit<0>(t, -rc.k[0]);
     hrot_bit<1>(t, -rc.k[1]);
@@ -1530,33 +1540,43 @@ __device__ __forceinline__ void dpp_self8(float *x, float k)
 // Ry^dagger on the qubit at lane bit B (position B) in tan form, scale left out: the thread
 // holding bit value 0 computes a + k b, the one holding 1 computes b - k a, with the partner
 // lane's amplitude (every source is read before any lane writes, so the update is in place).
-template <int B>
-__device__ __forceinline__ void hunrot_lane(HTile &t, float k, int lane)
+template <int B, typename R>
+__device__ __forceinline__ void hunrot_lane(HTile<R> &t, R k, int lane)
 {
-    const float ks = ((lane >> B) & 1) ? -k : k;
-    dpp_self8<B>(t.re, ks);
-    dpp_self8<B>(t.re + 8, ks);
-    dpp_self8<B>(t.im, ks);
-    dpp_self8<B>(t.im + 8, ks);
+    const R ks = ((lane >> B) & 1) ? -k : k;
+    if constexpr (std::is_same<R, float>::value) {
+        dpp_self8<B>(t.re, ks);
+        dpp_self8<B>(t.re + 8, ks);
+        dpp_self8<B>(t.im, ks);
+        dpp_self8<B>(t.im + 8, ks);
+    } else {   // fp64: no DPP form of the 64-bit multiply-add; move the partner's value first
+        constexpr int CTRL = B == 0 ? 0xB1 : 0x4E;
+#pragma unroll
+        for (int j = 0; j < kHalfRegs; ++j) {
+            const R pr = dppf<CTRL>(t.re[j]), pi = dppf<CTRL>(t.im[j]);
+            t.re[j] = fmar(ks, pr, t.re[j]);
+            t.im[j] = fmar(ks, pi, t.im[j]);
+        }
+    }
 }
 
 // X / Y statistics of register bit M (as xy_stats).
-template <int M>
-__device__ __forceinline__ void hxy_reg(const HTile &p, const HTile &l, float &sx, float &sy)
+template <int M, typename R>
+__device__ __forceinline__ void hxy_reg(const HTile<R> &p, const HTile<R> &l, R &sx, R &sy)
 {
-    float xp = 0, xn = 0, yp = 0, yn = 0;
+    R xp = 0, xn = 0, yp = 0, yn = 0;
 #pragma unroll
     for (int j = 0; j < kHalfRegs; ++j) {
         if (j & (1 << M)) continue;
         const int o = j | (1 << M);
-        xp = fmaf(l.re[j], p.im[o], xp);
-        xp = fmaf(l.re[o], p.im[j], xp);
-        xn = fmaf(l.im[j], p.re[o], xn);
-        xn = fmaf(l.im[o], p.re[j], xn);
-        yp = fmaf(l.re[o], p.re[j], yp);
-        yp = fmaf(l.im[o], p.im[j], yp);
-        yn = fmaf(l.re[j], p.re[o], yn);
-        yn = fmaf(l.im[j], p.im[o], yn);
+        xp = fmar(l.re[j], p.im[o], xp);
+        xp = fmar(l.re[o], p.im[j], xp);
+        xn = fmar(l.im[j], p.re[o], xn);
+        xn = fmar(l.im[o], p.re[j], xn);
+        yp = fmar(l.re[o], p.re[j], yp);
+        yp = fmar(l.im[o], p.im[j], yp);
+        yn = fmar(l.re[j], p.re[o], yn);
+        yn = fmar(l.im[j], p.im[o], yn);
     }
     sx = xp - xn;
     sy = yp - yn;
@@ -1565,38 +1585,50 @@ __device__ __forceinline__ void hxy_reg(const HTile &p, const HTile &l, float &s
 // X / Y statistics of the qubit at lane bit B: with c = conj(l_i) p_{i ^ 2^B} (the partner
 // lane's psi), Im<lam|X|psi> = sum Im c and Im<lam|Y|psi> = sum (bit ? Re c : -Re c), since
 // (Y psi)_i = -i psi_partner where bit B of i is 0 and +i psi_partner where it is 1.
-template <int B>
-__device__ __forceinline__ void hxy_lane(const HTile &p, const HTile &l, int lane, float &sx, float &sy)
+template <int B, typename R>
+__device__ __forceinline__ void hxy_lane(const HTile<R> &p, const HTile<R> &l, int lane, R &sx, R &sy)
 {
-    float xp = 0, xn = 0, rp = 0, rq = 0;
+    R xp = 0, xn = 0, rp = 0, rq = 0;
+    if constexpr (std::is_same<R, float>::value) {
 #pragma unroll
-    for (int j = 0; j < kHalfRegs; j += 2) {
-        if constexpr (B == 0)
-            HQML_XY2(HQML_QP0);
-        else
-            HQML_XY2(HQML_QP1);
+        for (int j = 0; j < kHalfRegs; j += 2) {
+            if constexpr (B == 0)
+                HQML_XY2(HQML_QP0);
+            else
+                HQML_XY2(HQML_QP1);
+        }
+    } else {
+        constexpr int CTRL = B == 0 ? 0xB1 : 0x4E;
+#pragma unroll
+        for (int j = 0; j < kHalfRegs; ++j) {
+            const R pr = dppf<CTRL>(p.re[j]), pi = dppf<CTRL>(p.im[j]);
+            xp = fmar(l.re[j], pi, xp);
+            xn = fmar(l.im[j], pr, xn);
+            rp = fmar(l.re[j], pr, rp);
+            rq = fmar(l.im[j], pi, rq);
+        }
     }
     sx = xp - xn;
-    const float r = rp + rq;
+    const R r = rp + rq;
     sy = ((lane >> B) & 1) ? r : -r;
 }
 
 // Z statistics of the register bits (zsum on 16 registers): returns the sum of
 // w_j = Im(conj(l_j) p_j) over the registers, d_m = sum (-1)^{bit m of j} w_j.
-template <int J>
-__device__ __forceinline__ float hzw(const HTile &p, const HTile &l)
+template <int J, typename R>
+__device__ __forceinline__ R hzw(const HTile<R> &p, const HTile<R> &l)
 {
-    return fmaf(l.re[J], p.im[J], -l.im[J] * p.re[J]);
+    return fmar(l.re[J], p.im[J], -l.im[J] * p.re[J]);
 }
 
-template <int K, int LO>
-__device__ __forceinline__ float hzsum(const HTile &p, const HTile &l, float *dz)
+template <int K, int LO, typename R>
+__device__ __forceinline__ R hzsum(const HTile<R> &p, const HTile<R> &l, R *dz)
 {
     if constexpr (K == 0) {
         return hzw<LO>(p, l);
     } else {
-        const float a = hzsum<K - 1, LO>(p, l, dz);
-        const float b = hzsum<K - 1, LO + (1 << (K - 1))>(p, l, dz);
+        const R a = hzsum<K - 1, LO>(p, l, dz);
+        const R b = hzsum<K - 1, LO + (1 << (K - 1))>(p, l, dz);
         if constexpr (LO == 0)
             dz[K - 1] = a - b;
         else
@@ -1618,14 +1650,15 @@ __device__ __forceinline__ bool nb_odd(uint32_t fixed, int q, int n)
 // which hold qubits 0..3: for a qubit q >= 5 neither chain neighbour is there, the
 // neighbours' sign is the same on the whole row, and the row leader forms the signed sums
 // from the plain ones (one reduction instead of two).  q is uniform, so is the branch.
-__device__ __forceinline__ void hstat_out(float sx, float sy, float sz, float corr, bool odd, int q, int sp,
-                                          float *lds_stat, int lane, int w)
+template <typename R>
+__device__ __forceinline__ void hstat_out(R sx, R sy, R sz, R corr, bool odd, int q, int sp, R *lds_stat, int lane,
+                                          int w)
 {
     if (q >= 5) {
         row_sum16x3(sx, sy, sz);
         if ((lane & 15) == 15) {
             const int r = w * 4 + (lane >> 4);
-            const float sg = odd ? -corr : corr;
+            const R sg = odd ? -corr : corr;
             lds_stat[((13 + sp) * 3 + 0) * 16 + r] = sx * corr;
             lds_stat[((13 + sp) * 3 + 1) * 16 + r] = sy * corr;
             lds_stat[((13 + sp) * 3 + 2) * 16 + r] = sz * corr;
@@ -1634,7 +1667,7 @@ __device__ __forceinline__ void hstat_out(float sx, float sy, float sz, float co
             lds_stat[(sp * 3 + 2) * 16 + r] = sz * sg;
         }
     } else {
-        const float sg = odd ? -corr : corr;
+        const R sg = odd ? -corr : corr;
         stat_out3(sx * corr, sy * corr, sz * corr, lds_stat, (13 + sp) * 3, lane, w);
         stat_out3(sx * sg, sy * sg, sz * sg, lds_stat, sp * 3, lane, w);
     }
@@ -1643,9 +1676,10 @@ __device__ __forceinline__ void hstat_out(float sx, float sy, float sz, float co
 // Factor tables of D_l in layout H2: D(i) = lo[j & 3] * hi[j >> 2] for register j
 // (positions 8, 9 and 10, 11), thread constant and CZ signs with fixed qubits folded in
 // as in diag_tables; the half view keeps positions 8, 9 apart from 10, 11 in the chain.
+template <typename R>
 struct HDiag {
-    float2 lo[4];
-    float2 hi[4];
+    V2<R> lo[4];
+    V2<R> hi[4];
 };
 
 // Factor of qubit q in D_l for bit value 1 (sel) or 0, read as uniform values into scalar
@@ -1656,63 +1690,72 @@ __device__ __forceinline__ float rfl(float x)
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
 
-__device__ __forceinline__ float2 hfactor(const float4 *wl, int q, bool sel)
+__device__ __forceinline__ double rfl(double x)
 {
-    const float4 f = ldu4(reinterpret_cast<const float *>(wl + __builtin_amdgcn_readfirstlane(q)));
-    const float x = rfl(f.x), y = rfl(f.y), z = rfl(f.z), w = rfl(f.w);
-    return sel ? make_float2(z, w) : make_float2(x, y);
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, (uint64_t)lo | ((uint64_t)hi << 32));
+}
+
+template <typename R>
+__device__ __forceinline__ V2<R> hfactor(const V4<R> *wl, int q, bool sel)
+{
+    const V4<R> f = ldu4(reinterpret_cast<const R *>(wl + __builtin_amdgcn_readfirstlane(q)));
+    const R x = rfl(f.x), y = rfl(f.y), z = rfl(f.z), w = rfl(f.w);
+    return sel ? mk2(z, w) : mk2(x, y);
 }
 
 // Factor tables of D_l in layout H1 (H1 = true: registers at positions 4..7, lo = 4, 5 and
 // hi = 6, 7) or H2 (registers at 8..11, lo = 8, 9 and hi = 10, 11).  tv: the thread's lane
 // and wave bits, at H1 positions 0,1,2,3,8,9,10,11 or H2 positions 0..7.
-template <bool H1>
-__device__ __forceinline__ HDiag hdiag_tables(const float *dw, int n, int layer, const HCtx &c, const ViewDevH &v,
-                                              uint32_t tv)
+template <bool H1, typename R>
+__device__ __forceinline__ HDiag<R> hdiag_tables(const R *dw, int n, int layer, const HCtx &c, const ViewDevH &v,
+                                                 uint32_t tv)
 {
-    const float4 *wl = reinterpret_cast<const float4 *>(dw) + (size_t)layer * n;
+    const V4<R> *wl = reinterpret_cast<const V4<R> *>(dw) + (size_t)layer * n;
     const uint32_t fixed_bits = H1 ? c.fixed1 : c.fixed2;
     // thread constant: lane and wave qubits (per lane), then the tile's qubits (uniform)
-    float2 ct = make_float2(1.f, 0.f);
+    V2<R> ct = mk2((R)1, (R)0);
 #pragma unroll 1
     for (int k = 0; k < 8; ++k) {
         const int pos = H1 ? (k < 4 ? k : k + 4) : k;
-        ct = cmul(ct, hfactor(wl, ldu(&v.perm[pos]), (tv >> k) & 1u));
+        ct = cmul(ct, hfactor<R>(wl, ldu(&v.perm[pos]), (tv >> k) & 1u));
     }
     const int nt = ldu(&v.n_tile);
-    float2 cu = make_float2(1.f, 0.f);
+    V2<R> cu = mk2((R)1, (R)0);
     for (int k = 0; k < nt; ++k) {
         const int q = ldu(&v.tile_q[k]);
-        cu = cmul(cu, hfactor(wl, q, (c.tile >> k) & 1));
+        cu = cmul(cu, hfactor<R>(wl, q, (c.tile >> k) & 1));
     }
-    float2 cc = cmul(ct, cu);
+    V2<R> cc = cmul(ct, cu);
     if (__builtin_popcount(fixed_bits & (fixed_bits >> 1)) & 1) {   // CZ signs among fixed qubits
         cc.x = -cc.x;
         cc.y = -cc.y;
     }
     const int *rq = H1 ? c.q1 : c.q2;
-    float2 g0[4], g1[4];
+    V2<R> g0[4], g1[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int q = rq[m];
-        g0[m] = hfactor(wl, q, false);
-        g1[m] = hfactor(wl, q, true);
+        g0[m] = hfactor<R>(wl, q, false);
+        g1[m] = hfactor<R>(wl, q, true);
         if (nb_odd(fixed_bits, q, n)) {   // CZ with a fixed neighbour at 1
             g1[m].x = -g1[m].x;
             g1[m].y = -g1[m].y;
         }
     }
     auto adj = [&](int a, int b) { const int d = rq[a] - rq[b]; return d == 1 || d == -1; };
-    HDiag t;
+    HDiag<R> t;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-        float2 x = cmul(cc, cmul((a & 1) ? g1[0] : g0[0], (a & 2) ? g1[1] : g0[1]));
+        V2<R> x = cmul(cc, cmul((a & 1) ? g1[0] : g0[0], (a & 2) ? g1[1] : g0[1]));
         if (a == 3 && adj(0, 1)) {
             x.x = -x.x;
             x.y = -x.y;
         }
         t.lo[a] = x;
-        float2 h = cmul((a & 1) ? g1[2] : g0[2], (a & 2) ? g1[3] : g0[3]);
+        V2<R> h = cmul((a & 1) ? g1[2] : g0[2], (a & 2) ? g1[3] : g0[3]);
         if (a == 3 && adj(2, 3)) {
             h.x = -h.x;
             h.y = -h.y;
@@ -1723,7 +1766,8 @@ __device__ __forceinline__ HDiag hdiag_tables(const float *dw, int n, int layer,
 }
 
 // s * D^dagger on a half tile (the tables of its layout).
-__device__ __forceinline__ void hdiag_dag(HTile &t, HDiag d, float s)
+template <typename R>
+__device__ __forceinline__ void hdiag_dag(HTile<R> &t, HDiag<R> d, R s)
 {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -1732,21 +1776,21 @@ __device__ __forceinline__ void hdiag_dag(HTile &t, HDiag d, float s)
     }
 #pragma unroll
     for (int j = 0; j < kHalfRegs; ++j) {
-        float2 f = cmul(d.lo[j & 3], d.hi[j >> 2]);
+        V2<R> f = cmul(d.lo[j & 3], d.hi[j >> 2]);
         f.y = -f.y;
-        const float r = t.re[j], i = t.im[j];
+        const R r = t.re[j], i = t.im[j];
         t.re[j] = r * f.x - i * f.y;
         t.im[j] = r * f.y + i * f.x;
     }
 }
 
-template <int ST>
-__global__ __launch_bounds__(kThreads, 4) void k_tile_bwdh(TilePassArgs a)
+template <int ST, typename R>
+__global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 4 : 2) void k_tile_bwdh(TilePassArgs a)
 {
-    __shared__ float2 lds[1 << kHalfBits];
-    __shared__ float lds_stat[kSlots * 16 + 16];
-    const float *rot_tf = static_cast<const float *>(a.rot_tf);
-    const float *dw = static_cast<const float *>(a.dw);
+    __shared__ V2<R> lds[1 << kHalfBits];
+    __shared__ R lds_stat[kSlots * 16 + 16];
+    const R *rot_tf = static_cast<const R *>(a.rot_tf);
+    const R *dw = static_cast<const R *>(a.dw);
     const ViewDevH &v = *a.hview;
     const int T2 = a.T * 2, n = a.n, la = a.rotA, lb = a.rotB;
     HCtx c;
@@ -1754,22 +1798,25 @@ __global__ __launch_bounds__(kThreads, 4) void k_tile_bwdh(TilePassArgs a)
     zero_stats(lds_stat);
     __syncthreads();
     const uint64_t nelem = 1ull << n;
-    HTile p, l;
+    HTile<R> p, l;
     hload<ST, true>(p, a.psi_in, c, nelem);
-    hload<0, false>(l, a.lam, c, nelem);
+    if constexpr (sizeof(R) == 4)
+        hload<0, false>(l, a.lam, c, nelem);   // through L2 (the XCD-contiguous order keeps it there)
+    else
+        hload<2, true>(l, a.lam, c, nelem);
     {   // merged statistics at the pass output: positions 0, 1 and 4..7 (H1)
-        float dz[4];
-        const float W = hzsum<4, 0>(p, l, dz);
-        float sx, sy;
+        R dz[4];
+        const R W = hzsum<4, 0>(p, l, dz);
+        R sx, sy;
         hxy_lane<0>(p, l, c.lane, sx, sy);
-        hstat_out(sx, sy, (c.lane & 1) ? -W : W, 1.f, nb_odd(c.fixed1, c.q0[0], n), c.q0[0], ldu(&v.slot_pos[0]),
+        hstat_out(sx, sy, (c.lane & 1) ? -W : W, (R)1, nb_odd(c.fixed1, c.q0[0], n), c.q0[0], ldu(&v.slot_pos[0]),
                   lds_stat, c.lane, c.w);
         hxy_lane<1>(p, l, c.lane, sx, sy);
-        hstat_out(sx, sy, (c.lane & 2) ? -W : W, 1.f, nb_odd(c.fixed1, c.q0[1], n), c.q0[1], ldu(&v.slot_pos[1]),
+        hstat_out(sx, sy, (c.lane & 2) ? -W : W, (R)1, nb_odd(c.fixed1, c.q0[1], n), c.q0[1], ldu(&v.slot_pos[1]),
                   lds_stat, c.lane, c.w);
 #define HQML_HSTAT1(M)                                                                                      \
     hxy_reg<M>(p, l, sx, sy);                                                                               \
-    hstat_out(sx, sy, dz[M], 1.f, nb_odd(c.fixed1, c.q1[M], n), c.q1[M], ldu(&v.slot_pos[4 + M]), lds_stat, c.lane,  \
+    hstat_out(sx, sy, dz[M], (R)1, nb_odd(c.fixed1, c.q1[M], n), c.q1[M], ldu(&v.slot_pos[4 + M]), lds_stat, c.lane,  \
               c.w);
         HQML_HSTAT1(0)
         HQML_HSTAT1(1)
@@ -1780,12 +1827,12 @@ __global__ __launch_bounds__(kThreads, 4) void k_tile_bwdh(TilePassArgs a)
     htranspose(p, lds, c.a1, c.a2, true);
     htranspose(l, lds, c.a1, c.a2, true);
     {   // positions 8..11 (H2), also at the pass output
-        float dz[4];
+        R dz[4];
         (void)hzsum<4, 0>(p, l, dz);
-        float sx, sy;
+        R sx, sy;
 #define HQML_HSTAT2(M)                                                                                       \
     hxy_reg<M>(p, l, sx, sy);                                                                                \
-    hstat_out(sx, sy, dz[M], 1.f, nb_odd(c.fixed2, c.q2[M], n), c.q2[M], ldu(&v.slot_pos[8 + M]), lds_stat, c.lane, \
+    hstat_out(sx, sy, dz[M], (R)1, nb_odd(c.fixed2, c.q2[M], n), c.q2[M], ldu(&v.slot_pos[8 + M]), lds_stat, c.lane, \
               c.w);
         HQML_HSTAT2(0)
         HQML_HSTAT2(1)
@@ -1795,25 +1842,25 @@ __global__ __launch_bounds__(kThreads, 4) void k_tile_bwdh(TilePassArgs a)
     }
     // lambda: layer lb at 8..11 and 0, 1 (H2), at 4..7 (H1); D_la^dagger (H1), which removes
     // the scales so far; layer la at 4..7 and 0, 1 (H1), at 8..11 (H2); store from H2
-    const HCoef b2 = hcoef<4>(rot_tf, n, lb, c.q2, c.gm2);
+    const HCoef<R> b2 = hcoef<4>(rot_tf, n, lb, c.q2, c.gm2);
     hunrot_regs(l, b2);
-    const HCoef b0 = hcoef<2>(rot_tf, n, lb, c.q0, c.gm0);
+    const HCoef<R> b0 = hcoef<2>(rot_tf, n, lb, c.q0, c.gm0);
     hunrot_lane<0>(l, b0.k[0], c.lane);
     hunrot_lane<1>(l, b0.k[1], c.lane);
     htranspose(l, lds, c.a1, c.a2, false);
-    const HCoef b1 = hcoef<4>(rot_tf, n, lb, c.q1, c.gm1);
+    const HCoef<R> b1 = hcoef<4>(rot_tf, n, lb, c.q1, c.gm1);
     hunrot_regs(l, b1);
     hdiag_dag(l, hdiag_tables<true>(dw, n, a.diag, c, v, (uint32_t)threadIdx.x), b1.F * b2.F * b0.F);
-    const HCoef a1 = hcoef<4>(rot_tf, n, la, c.q1, c.gm1);
+    const HCoef<R> a1 = hcoef<4>(rot_tf, n, la, c.q1, c.gm1);
     hunrot_regs(l, a1);
-    const HCoef a0 = hcoef<2>(rot_tf, n, la, c.q0, c.gm0);
+    const HCoef<R> a0 = hcoef<2>(rot_tf, n, la, c.q0, c.gm0);
     hunrot_lane<0>(l, a0.k[0], c.lane);
     hunrot_lane<1>(l, a0.k[1], c.lane);
     htranspose(l, lds, c.a1, c.a2, true);
-    const HCoef a2 = hcoef<4>(rot_tf, n, la, c.q2, c.gm2);
+    const HCoef<R> a2 = hcoef<4>(rot_tf, n, la, c.q2, c.gm2);
     hunrot_regs(l, a2);
-    const float sl = a2.F * a0.F * a1.F;
-    if (sl != 1.f) {
+    const R sl = a2.F * a0.F * a1.F;
+    if (sl != (R)1) {
 #pragma unroll
         for (int j = 0; j < kHalfRegs; ++j) {
             l.re[j] *= sl;
@@ -1821,7 +1868,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_tile_bwdh(TilePassArgs a)
         }
     }
     hstore2(l, a.lam, c, nelem);
-    flush_merged(lds_stat, static_cast<float *>(a.stat_part) + ((size_t)c.sample * T2 + c.tile) * kSlots, false,
+    flush_merged(lds_stat, static_cast<R *>(a.stat_part) + ((size_t)c.sample * T2 + c.tile) * kSlots, false,
                  *a.view, rot_tf, dw, n, a.diag, lb);
 }
 
@@ -2339,11 +2386,12 @@ template <int ST, typename R>
 static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s, bool *bad)
 {
     if (a.flags & PF_HALF) {
-        // the general shape on half tiles (fp32 compute, fp32 or bf16 psi): two per full tile
-        if constexpr (std::is_same<R, float>::value && ST != 2) {
+        // the general shape on half tiles (fp32 compute with fp32 or bf16 psi, fp64 compute
+        // with fp32 or fp64 psi): two per full tile
+        if constexpr ((std::is_same<R, float>::value && ST != 2) || (std::is_same<R, double>::value && ST != 1)) {
             if (a.rotA >= 0 && a.diag >= 0 && a.rotB >= 0 && a.hview &&
                 !(a.flags & (PF_CNOT | PF_FUSED | PF_INIT | PF_SEED | PF_STATS_ONLY))) {
-                k_tile_bwdh<ST><<<dim3(grid.x * 2), kThreads, 0, s>>>(a);
+                k_tile_bwdh<ST, R><<<dim3(grid.x * 2), kThreads, 0, s>>>(a);
                 return;
             }
         }

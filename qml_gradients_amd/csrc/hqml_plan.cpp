@@ -238,7 +238,8 @@ bool build_half_view(int n, const ViewDev &full, ViewDevH *out)
 
 int stat_tiles(const Plan &p, int compute64)
 {
-    return (p.half && !compute64) ? 2 * p.T : p.T;
+    (void)compute64;   // both compute types run the general passes on half tiles
+    return (p.half && !p.cnot && !p.small) ? 2 * p.T : p.T;
 }
 
 bool make_obs_view(int n, uint32_t xmask, ViewDev *out, std::string *err)

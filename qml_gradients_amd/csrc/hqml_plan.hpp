@@ -34,7 +34,7 @@ struct Plan {
     int T = 1;                           // tiles per sample
     std::vector<ViewDev> views;
     std::vector<ViewDevH> hviews;        // half-tile views of the same groups (CZ-chain plan)
-    bool half = false;                   // every view has a half-tile view: the fp32 adjoint's
+    bool half = false;                   // every view has a half-tile view: the adjoint's
                                          // general passes run on half tiles
     std::vector<PassPlan> fwd;           // forward passes in order
     std::vector<int> stats_only;         // views needing a layer-0 stats-only backward pass
@@ -74,8 +74,8 @@ struct Workspace {
     size_t total = 0;
 };
 
-// Statistics partials per sample of a backward pass: 2T when the fp32 adjoint runs its
-// general passes on half tiles (p.half and fp32 compute), else T.
+// Statistics partials per sample of a backward pass: 2T when the adjoint runs its general
+// passes on half tiles (p.half, the CZ-chain tile plan), else T.
 int stat_tiles(const Plan &p, int compute64);
 
 // storage: 0 fp32, 1 bf16, 2 fp64 saved states; compute64: arithmetic (and lambda,
