@@ -444,6 +444,30 @@ __device__ __forceinline__ void stats_visit_merged(const Tile<R> &p, const Tile<
 #undef HQML_STAT_BIT
 }
 
+// Factor of qubit q in D_l for bit value 1 (sel) or 0, read as uniform values into scalar
+// registers before the per-lane choice (otherwise the compiler turns the choice into a
+// per-lane address and a vector load per qubit).
+__device__ __forceinline__ float rfl(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ double rfl(double x)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, (uint64_t)lo | ((uint64_t)hi << 32));
+}
+
+template <typename R>
+__device__ __forceinline__ V2<R> hfactor(const V4<R> *wl, int q, bool sel)
+{
+    const V4<R> f = ldu4(reinterpret_cast<const R *>(wl + __builtin_amdgcn_readfirstlane(q)));
+    const R x = rfl(f.x), y = rfl(f.y), z = rfl(f.z), w = rfl(f.w);
+    return sel ? mk2(z, w) : mk2(x, y);
+}
+
 // Per-thread factor tables of the diagonal D_l in layout L2:
 // D(i) = Plo[j & 3] * Phi[j >> 2] for register j of this thread.  dw[l][q] holds the
 // factor (f0, f1) of qubit q for bit value 0 / 1; CZ signs between register and
@@ -457,60 +481,13 @@ struct DiagTables {
 };
 
 // cz = false (CNOT-chain plan): a plain product of single-qubit factors, no CZ signs.
+// The thread constant is a product over the lane and wave qubits of L2 (positions 2..8 and
+// 12, per lane) and the tile's qubits (uniform), every factor read as a uniform value before
+// the per-lane choice.
+struct TileCtx;
 template <typename R>
-__device__ __forceinline__ DiagTables<R> diag_tables(const R *dw, int n, int layer, const int *rq,
-                                                     uint32_t fixed_bits, bool cz = true)
-{
-    const V4<R> *wl = reinterpret_cast<const V4<R> *>(dw) + (size_t)layer * n;
-    uint32_t regq = 0;
-#pragma unroll
-    for (int m = 0; m < 5; ++m) regq |= 1u << rq[m];
-    // Thread constant: product over fixed qubits, CZ signs among fixed neighbours.
-    V2<R> c = mk2((R)1, (R)0);
-    for (int q = 0; q < n; ++q) {
-        if (regq & (1u << q)) continue;
-        const V4<R> f = ldu4(reinterpret_cast<const R *>(wl + q));
-        c = cmul(c, ((fixed_bits >> q) & 1u) ? mk2(f.z, f.w) : mk2(f.x, f.y));
-    }
-    if (cz && (__builtin_popcount(fixed_bits & (fixed_bits >> 1)) & 1)) {
-        c.x = -c.x;
-        c.y = -c.y;
-    }
-    V2<R> g0[5], g1[5];
-#pragma unroll
-    for (int m = 0; m < 5; ++m) {
-        const int q = rq[m];
-        const V4<R> f = ldu4(reinterpret_cast<const R *>(wl + q));
-        g0[m] = mk2(f.x, f.y);
-        g1[m] = mk2(f.z, f.w);
-        uint32_t nb = (fixed_bits >> (q + 1)) & 1u;
-        if (q > 0) nb += (fixed_bits >> (q - 1)) & 1u;
-        if (cz && (nb & 1u)) {
-            g1[m].x = -g1[m].x;
-            g1[m].y = -g1[m].y;
-        }
-    }
-    auto adj = [&](int a, int b) { const int d = rq[a] - rq[b]; return cz && (d == 1 || d == -1); };
-    DiagTables<R> t;
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        V2<R> v = cmul(c, cmul((a & 1) ? g1[0] : g0[0], (a & 2) ? g1[1] : g0[1]));
-        if (a == 3 && adj(0, 1)) { v.x = -v.x; v.y = -v.y; }
-        t.lo[a] = v;
-    }
-#pragma unroll
-    for (int h = 0; h < 8; ++h) {
-        V2<R> v = cmul(cmul((h & 1) ? g1[2] : g0[2], (h & 2) ? g1[3] : g0[3]), (h & 4) ? g1[4] : g0[4]);
-        int flips = 0;
-        if ((h & 3) == 3 && adj(2, 3)) ++flips;
-        if ((h & 6) == 6 && adj(3, 4)) ++flips;
-        if ((h & 5) == 5 && adj(2, 4)) ++flips;
-        if (flips & 1) { v.x = -v.x; v.y = -v.y; }
-        t.hi[h] = v;
-    }
-    return t;
-}
-
+__device__ __forceinline__ DiagTables<R> diag_tables(const R *dw, int n, int layer, const TileCtx &c, const ViewDev &v,
+                                                     bool cz = true);
 template <typename R>
 __device__ __forceinline__ void scale_lo(DiagTables<R> &d, R s)
 {
@@ -656,6 +633,60 @@ __device__ __forceinline__ void tile_ctx(TileCtx &c, const ViewDev &v, int T, in
     tile_retarget(c, v, T, blk, sample0);
 }
 
+template <typename R>
+__device__ __forceinline__ DiagTables<R> diag_tables(const R *dw, int n, int layer, const TileCtx &c, const ViewDev &v,
+                                                     bool cz)
+{
+    const V4<R> *wl = reinterpret_cast<const V4<R> *>(dw) + (size_t)layer * n;
+    const uint32_t fixed_bits = c.fixed2;
+    const int *rq = c.q2;
+    const int l2p[8] = {2, 3, 4, 5, 6, 7, 8, 12};
+    const uint32_t tv = (uint32_t)c.lane | ((uint32_t)c.w << 6);
+    V2<R> ct = mk2((R)1, (R)0);
+#pragma unroll 1
+    for (int k = 0; k < 8; ++k) ct = cmul(ct, hfactor<R>(wl, ldu(&v.perm[l2p[k]]), (tv >> k) & 1u));
+    V2<R> cu = mk2((R)1, (R)0);
+    const int nt = ldu(&v.n_tile);
+    for (int k = 0; k < nt; ++k) cu = cmul(cu, hfactor<R>(wl, ldu(&v.tile_q[k]), (c.tile >> k) & 1));
+    V2<R> cc = cmul(ct, cu);
+    if (cz && (__builtin_popcount(fixed_bits & (fixed_bits >> 1)) & 1)) {
+        cc.x = -cc.x;
+        cc.y = -cc.y;
+    }
+    V2<R> g0[5], g1[5];
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+        const int q = rq[m];
+        g0[m] = hfactor<R>(wl, q, false);
+        g1[m] = hfactor<R>(wl, q, true);
+        uint32_t nb = (fixed_bits >> (q + 1)) & 1u;
+        if (q > 0) nb += (fixed_bits >> (q - 1)) & 1u;
+        if (cz && (nb & 1u)) {
+            g1[m].x = -g1[m].x;
+            g1[m].y = -g1[m].y;
+        }
+    }
+    auto adj = [&](int a, int b) { const int d = rq[a] - rq[b]; return cz && (d == 1 || d == -1); };
+    DiagTables<R> t;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        V2<R> x = cmul(cc, cmul((a & 1) ? g1[0] : g0[0], (a & 2) ? g1[1] : g0[1]));
+        if (a == 3 && adj(0, 1)) { x.x = -x.x; x.y = -x.y; }
+        t.lo[a] = x;
+    }
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+        V2<R> x = cmul(cmul((h & 1) ? g1[2] : g0[2], (h & 2) ? g1[3] : g0[3]), (h & 4) ? g1[4] : g0[4]);
+        int flips = 0;
+        if ((h & 3) == 3 && adj(2, 3)) ++flips;
+        if ((h & 6) == 6 && adj(3, 4)) ++flips;
+        if ((h & 5) == 5 && adj(2, 4)) ++flips;
+        if (flips & 1) { x.x = -x.x; x.y = -x.y; }
+        t.hi[h] = x;
+    }
+    return t;
+}
+
 // Amplitude offset of register j in layout L1 (sum of the strides of its set bits).
 __device__ __forceinline__ uint32_t roff(const TileCtx &c, int j)
 {
@@ -765,9 +796,7 @@ __device__ __forceinline__ void init_l1(Tile<R> &t, const R *init_u, const TileC
     V2<R> cst = mk2((R)1, (R)0);
     for (int q = 0; q < n; ++q) {
         if (regq & (1u << q)) continue;
-        const V4<R> f = ldu4(reinterpret_cast<const R *>(u + q));
-        const V2<R> g = ((c.fixed1 >> q) & 1u) ? mk2(f.z, f.w) : mk2(f.x, f.y);
-        cst = cmul(cst, g);
+        cst = cmul(cst, hfactor<R>(u, q, (c.fixed1 >> q) & 1u));
     }
     t.re[0] = cst.x;
     t.im[0] = cst.y;
@@ -881,7 +910,7 @@ __device__ __forceinline__ void fwd_ops(Tile<R> &t, const TilePassArgs &a, const
         if (a.diag >= 0) {
             // fold the pending scale and the scale of the rotations that follow into D
             const R fb = a.rotB >= 0 ? rb1.F * rb2.F : (R)1;
-            apply_diag(t, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2, !(a.flags & PF_CNOT)),
+            apply_diag(t, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c, *a.view, !(a.flags & PF_CNOT)),
                        sigma * fb);
             sigma = (R)1 / fb;
         }
@@ -1182,7 +1211,7 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
             const RotCoef<R> b2 = load_coef(rot_tf, a.n, a.rotB, c.q2, c.gm2);
             rot_layer<true>(l, b2);
             // lambda carries scale fb1 * b2.F; D^dagger removes it
-            apply_diag_dag(l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2), fb1 * b2.F);
+            apply_diag_dag(l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c, *a.view), fb1 * b2.F);
             if constexpr (SHAPE == BW_GENERAL) {
                 const RotCoef<R> a2 = load_coef(rot_tf, a.n, la, c.q2, c.gm2);
                 rot_layer<true>(l, a2);
@@ -1209,13 +1238,13 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
             const RotCoef<R> b2 = load_coef(rot_tf, a.n, a.rotB, c.q2, c.gm2);
             rot_layer<true>(l, b2);
             // lambda carries scale fb1 * b2.F; diag(r_l)^dagger removes it
-            apply_diag_dag(l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2, false),
+            apply_diag_dag(l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c, *a.view, false),
                            fb1 * b2.F);
             transpose(l, lds, c.a1, c.a2, false);
         } else if constexpr (SHAPE == BW_ROTAD) {
             transpose(p, lds, c.a1, c.a2, true);
             transpose(l, lds, c.a1, c.a2, true);
-            apply_diag2(p, l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2, false), (R)1);
+            apply_diag2(p, l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c, *a.view, false), (R)1);
             stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
             const RotCoef<R> a2 = load_coef(rot_tf, a.n, la, c.q2, c.gm2);
             rot_layer2<true>(p, l, a2);
@@ -1231,7 +1260,7 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
             // pass, after diag(p_0)) is taken back through diag(p_0).
             transpose(p, lds, c.a1, c.a2, true);
             transpose(l, lds, c.a1, c.a2, true);
-            apply_diag_dag(l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2, false), (R)1);
+            apply_diag_dag(l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c, *a.view, false), (R)1);
             stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
             transpose(p, lds, c.a1, c.a2, false);
             transpose(l, lds, c.a1, c.a2, false);
@@ -1246,7 +1275,7 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 2 : 1) void k_tile_bwd(T
             transpose(p, lds, c.a1, c.a2, true);
             transpose(l, lds, c.a1, c.a2, true);
             stats_visit<true>(p, l, 0, lds_stat, c.lane, c.w, (R)1);
-            apply_diag(l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c.q2, c.fixed2, false), (R)1);
+            apply_diag(l, diag_tables(static_cast<const R *>(a.dw), a.n, a.diag, c, *a.view, false), (R)1);
             transpose(l, lds, c.a1, c.a2, false);
             store_l1<LIO>(l, a.lam, c, nelem);
             flush_stats(lds_stat, stat_row<R>(a, c), a.stat_mul == 2);
@@ -1681,30 +1710,6 @@ struct HDiag {
     V2<R> lo[4];
     V2<R> hi[4];
 };
-
-// Factor of qubit q in D_l for bit value 1 (sel) or 0, read as uniform values into scalar
-// registers before the per-lane choice (otherwise the compiler turns the choice into a
-// per-lane address and a vector load per qubit).
-__device__ __forceinline__ float rfl(float x)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
-}
-
-__device__ __forceinline__ double rfl(double x)
-{
-    const uint64_t u = __builtin_bit_cast(uint64_t, x);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
-    return __builtin_bit_cast(double, (uint64_t)lo | ((uint64_t)hi << 32));
-}
-
-template <typename R>
-__device__ __forceinline__ V2<R> hfactor(const V4<R> *wl, int q, bool sel)
-{
-    const V4<R> f = ldu4(reinterpret_cast<const R *>(wl + __builtin_amdgcn_readfirstlane(q)));
-    const R x = rfl(f.x), y = rfl(f.y), z = rfl(f.z), w = rfl(f.w);
-    return sel ? mk2(z, w) : mk2(x, y);
-}
 
 // Factor tables of D_l in layout H1 (H1 = true: registers at positions 4..7, lo = 4, 5 and
 // hi = 6, 7) or H2 (registers at 8..11, lo = 8, 9 and hi = 10, 11).  tv: the thread's lane
