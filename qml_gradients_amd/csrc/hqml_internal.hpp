@@ -52,7 +52,9 @@ constexpr int kRegBits = 5;
 constexpr int kRegs = 32;
 constexpr int kThreads = 256;
 constexpr int kGbgPairsPerBlock = 4096; // gate-by-gate kernels: amplitude pairs per workgroup
-constexpr int kTileChunk = 256;     // tiles per first-stage reduction block (samples with more tiles)
+constexpr int kTileChunk = 256;     // tiles per first-stage <O> reduction block (samples with more tiles)
+constexpr int kStatChunk = 64;      // tiles per first-stage statistics reduction block (samples with more
+                                    // tiles): a block reads whole rows of partials, coalesced
 constexpr int kSlots = 80;           // per-tile statistics slots: (sel*13 + pos)*3 + pauli
 constexpr int kMaxQubits = 29;
 constexpr int kSmallMaxQubits = 13;  // whole state of one sample in one workgroup

@@ -2227,19 +2227,19 @@ __global__ void k_copy_dlde(const IO *src, int B, double *dlde)
 
 // First stage for samples with many tiles: for pass p (relative to the first pass
 // of the range), sample b0+bi and chunk ch, out[p][bi][ch][slot] = sum of the slot
-// over tiles ch*kTileChunk .. (ch+1)*kTileChunk-1.  Thread i owns slot i % kSlots of
+// over tiles ch*kStatChunk .. (ch+1)*kStatChunk-1.  Thread i owns slot i % kSlots of
 // every fourth tile starting at i / kSlots (consecutive threads read consecutive
 // floats); the four lanes are then added in a fixed order.
-// Grid (T / kTileChunk, Bc, passes), 4 * kSlots threads.
+// Grid (T / kStatChunk, Bc, passes), 4 * kSlots threads.
 template <typename P>
 __global__ void __launch_bounds__(4 * kSlots) k_stats_chunks(const P *part, int Bs, int b0, int T, double *out)
 {
     __shared__ double red[4 * kSlots];
     const int nch = gridDim.x, ch = blockIdx.x, bi = blockIdx.y, p = blockIdx.z, Bc = gridDim.y;
     const int i = threadIdx.x, slot = i % kSlots, lane = i / kSlots;
-    const P *src = part + (((size_t)p * Bs + b0 + bi) * T + (size_t)ch * kTileChunk) * kSlots + slot;
+    const P *src = part + (((size_t)p * Bs + b0 + bi) * T + (size_t)ch * kStatChunk) * kSlots + slot;
     double acc = 0.0;
-    for (int t = lane; t < kTileChunk; t += 4) acc += (double)src[(size_t)t * kSlots];
+    for (int t = lane; t < kStatChunk; t += 4) acc += (double)src[(size_t)t * kSlots];
     red[i] = acc;
     __syncthreads();
     if (i < kSlots)
@@ -2513,8 +2513,8 @@ static void stats_typed(const void *part, const int2 *map, int Bs, int b0, int B
 {
     const size_t total = (size_t)Bc * L * n * 3;
     const unsigned grid = (unsigned)((total + 255) / 256);
-    if (T > kTileChunk) {
-        const int nch = T / kTileChunk;
+    if (T > kStatChunk) {
+        const int nch = T / kStatChunk;
         k_stats_chunks<P><<<dim3((unsigned)nch, (unsigned)Bc, (unsigned)(pass_hi - pass_lo)), 4 * kSlots, 0, s>>>(
             static_cast<const P *>(part), Bs, b0, T, chunks);
         k_stats_reduce<double><<<grid, 256, 0, s>>>(chunks, map, Bc, b0, b0, Bc, L, n, nch, pass_lo, pass_hi, S);

@@ -469,8 +469,8 @@ Workspace size_workspace(const Plan &p, int max_batch, int storage, int compute6
     const int Ts = stat_tiles(p, compute64);
     w.part_bytes = (size_t)w.part_passes * B * Ts * kSlots * r;
     const size_t epart = B * p.T * r;
-    if (Ts > kTileChunk) {
-        w.tile_chunks = Ts / kTileChunk;
+    if (Ts > kStatChunk) {
+        w.tile_chunks = Ts / kStatChunk;
         w.part2_bytes = (size_t)w.part_passes * B * w.tile_chunks * kSlots * 8;
     }
     if (p.T > kTileChunk) w.epart2_bytes = B * (size_t)(p.T / kTileChunk) * 8;
