@@ -100,9 +100,9 @@ def algorithmic_bytes(plan: dict, B: int, storage: str, compute: str = "fp32"):
 
 
 def half_tiles(plan: dict, compute: str = "fp32") -> bool:
-    """Whether the general adjoint passes run on half tiles (k_tile_bwdh): the CZ-chain
-    tile plan with a half view for every view (either compute type)."""
-    return bool(plan.get("half")) and not plan.get("cnot")
+    """Whether the adjoint passes run on half tiles (k_tile_bwdh): a tile plan with a half
+    view for every view (either compute type, either entangler)."""
+    return bool(plan.get("half"))
 
 
 def algorithmic_flops_bwd(plan: dict, B: int, compute: str = "fp32"):
@@ -114,7 +114,7 @@ def algorithmic_flops_bwd(plan: dict, B: int, compute: str = "fp32"):
     g = qubits the pass's view rotates, g1 / g2 = those at L1 / L2 register positions.
     The general and product-state shapes take both layers' statistics from one set of
     sums (merged statistics) and rotate psi only by the L1 half of the later layer; on
-    half tiles that is the group's qubits at H1 register positions 4..7."""
+    half tiles every statistic is taken at the pass output and psi is not rotated."""
     N = 1 << plan["n"]
     P = len(plan["passes"])
     half = half_tiles(plan, compute)
@@ -125,7 +125,7 @@ def algorithmic_flops_bwd(plan: dict, B: int, compute: str = "fp32"):
         g2 = sum((gm >> p) & 1 for p in L2_POSITIONS)
         g1 = g - g2
         if half and k != P - 1 and ps["rotA"] >= 0 and ps["diag"] >= 0 and ps["rotB"] >= 0 and not ps["init"]:
-            g1 = bin(plan["hviews"][ps["view"]]["group_mask"] & 0xF0).count("1")
+            g1 = 0
         if k == P - 1 and not ps["init"]:
             # forward rotations, E, seed, statistics, un-rotations, scale
             f = 4 * g + 3 + 8 * g + 10 + 4 * g2 + 4 * g + 2

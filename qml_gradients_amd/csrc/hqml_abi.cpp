@@ -58,7 +58,7 @@ struct hqml_ctx {
     void *init_u = nullptr;
     ViewDev *views = nullptr;
     ViewDevH *hviews = nullptr;  // half-tile views (general adjoint passes on half tiles)
-    bool half = false;           // CZ-chain tile plan whose views all have half views
+    bool half = false;           // tile plan whose views all have half views
     int stat_mul = 1;            // statistics partials per full tile: 2 with half tiles
     int2 *statmap = nullptr;
     double *dlde = nullptr;
@@ -277,9 +277,13 @@ int bwd_pass(hqml_ctx *c, hipStream_t st, Span sp, int k, int part_lo, char *par
             a.psi_in = k == 0 ? nullptr : pass_out(c, k - 1);
         else
             a.psi_in = pass_out(c, k);
-        // the general shape [rotA, D, rotB] on a saved output: half tiles when the context has them
-        if (c->half && !pp.init && pp.rotA >= 0 && pp.diag >= 0 && pp.rotB >= 0 &&
-            !(extra_flags & (PF_FUSED | PF_SEED))) {
+        // half tiles when the context has them: the general shape [rotA, D, rotB] of the CZ
+        // chain, the CNOT chain's [rotA, diag(p_l)] and [diag(r_l), rotB] (on a saved output,
+        // lambda not seeded here)
+        const bool shape_ok = pl.cnot ? (pp.diag >= 0 && ((pp.rotA >= 0 && pp.rotB < 0) ||
+                                                          (pp.gather && pp.rotA < 0 && pp.rotB >= 0)))
+                                      : (pp.rotA >= 0 && pp.diag >= 0 && pp.rotB >= 0);
+        if (c->half && !pp.init && shape_ok && !(extra_flags & (PF_FUSED | PF_SEED))) {
             a.flags |= PF_HALF;
             a.hview = c->hviews + pp.view;
         }
@@ -780,7 +784,7 @@ int hqml_create(const hqml_config *cfg, hqml_ctx **out)
     c->H = static_cast<double *>(grab(Ln * 9 * 8));
     c->init_u = grab((size_t)B * plan.n * 4 * c->rb);
     if (!plan.small) c->views = static_cast<ViewDev *>(grab((plan.views.size() + 1) * sizeof(ViewDev)));
-    c->half = !plan.small && !plan.cnot && plan.half;
+    c->half = !plan.small && plan.half;
     c->stat_mul = plan.small ? 1 : stat_tiles(plan, c->r64) / plan.T;
     if (c->half) c->hviews = static_cast<ViewDevH *>(grab(plan.hviews.size() * sizeof(ViewDevH)));
     c->statmap = static_cast<int2 *>(grab(Ln * sizeof(int2)));

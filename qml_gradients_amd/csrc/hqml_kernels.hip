@@ -1450,6 +1450,38 @@ __device__ __forceinline__ void hstore2(const HTile<R> &t, void *state, const HC
     }
 }
 
+// Store lambda in layout H1: at its own amplitudes, or (CHAIN) at P^-1 of them, P the CNOT
+// chain's index map (P^-1 is linear over XOR, so the tile, thread and register parts of the
+// index map separately); non-temporal (the CNOT-chain passes keep the plain tile order).
+template <bool CHAIN, typename R>
+__device__ __forceinline__ void hstore1(const HTile<R> &t, void *state, const HCtx &c, uint64_t nelem)
+{
+    using IO = StateIO<kLamIO<R>>;
+    constexpr uint32_t esz = sizeof(typename IO::elem);
+    using Off = TileOff<esz>;
+    if constexpr (CHAIN) {
+        const uint32_t mask = (uint32_t)(nelem - 1);
+        char *base = reinterpret_cast<char *>(state) + (uint64_t)c.sample * nelem * esz;
+        const uint32_t pt = chain_inv((uint32_t)c.tile_off | opaque_u32(c.t1), mask);
+#pragma unroll
+        for (int j = 0; j < kHalfRegs; ++j) {
+            const Off off = (Off)(pt ^ chain_inv(hroff(c, j), mask)) * esz;
+            IO::store(reinterpret_cast<typename IO::elem *>(base + off), t.re[j], t.im[j]);
+        }
+    } else {
+        char *base = reinterpret_cast<char *>(state) + ((uint64_t)c.sample * nelem + c.tile_off) * esz;
+        const Off tb = (Off)opaque_u32(c.t1) * esz;
+#pragma unroll
+        for (int j = 0; j < kHalfRegs; ++j) {
+            const Off off = tb + (Off)hroff(c, j) * esz;
+            if constexpr (sizeof(R) == 4)
+                IO::store_nt(reinterpret_cast<typename IO::elem *>(base + off), t.re[j], t.im[j]);
+            else
+                IO::store(reinterpret_cast<typename IO::elem *>(base + off), t.re[j], t.im[j]);
+        }
+    }
+}
+
 // Move a half tile between H1 and H2 through the LDS buffer (32 KB in fp32, 64 KB in fp64).
 template <typename R>
 __device__ __forceinline__ void htranspose(HTile<R> &t, V2<R> *lds, uint32_t a1, uint32_t a2, bool from_h1)
@@ -1702,6 +1734,13 @@ __device__ __forceinline__ void hstat_out(R sx, R sy, R sz, R corr, bool odd, in
     }
 }
 
+// Statistics of one position into its slots (sel*13 + pos)*3 (one rotation layer per pass).
+template <typename R>
+__device__ __forceinline__ void hstat_plain(R sx, R sy, R sz, int sel, int sp, R *lds_stat, int lane, int w)
+{
+    stat_out3(sx, sy, sz, lds_stat, (sel * 13 + sp) * 3, lane, w);
+}
+
 // Factor tables of D_l in layout H2: D(i) = lo[j & 3] * hi[j >> 2] for register j
 // (positions 8, 9 and 10, 11), thread constant and CZ signs with fixed qubits folded in
 // as in diag_tables; the half view keeps positions 8, 9 apart from 10, 11 in the chain.
@@ -1716,7 +1755,7 @@ struct HDiag {
 // and wave bits, at H1 positions 0,1,2,3,8,9,10,11 or H2 positions 0..7.
 template <bool H1, typename R>
 __device__ __forceinline__ HDiag<R> hdiag_tables(const R *dw, int n, int layer, const HCtx &c, const ViewDevH &v,
-                                                 uint32_t tv)
+                                                 uint32_t tv, bool cz = true)
 {
     const V4<R> *wl = reinterpret_cast<const V4<R> *>(dw) + (size_t)layer * n;
     const uint32_t fixed_bits = H1 ? c.fixed1 : c.fixed2;
@@ -1734,7 +1773,7 @@ __device__ __forceinline__ HDiag<R> hdiag_tables(const R *dw, int n, int layer, 
         cu = cmul(cu, hfactor<R>(wl, q, (c.tile >> k) & 1));
     }
     V2<R> cc = cmul(ct, cu);
-    if (__builtin_popcount(fixed_bits & (fixed_bits >> 1)) & 1) {   // CZ signs among fixed qubits
+    if (cz && (__builtin_popcount(fixed_bits & (fixed_bits >> 1)) & 1)) {   // CZ signs among fixed qubits
         cc.x = -cc.x;
         cc.y = -cc.y;
     }
@@ -1745,12 +1784,12 @@ __device__ __forceinline__ HDiag<R> hdiag_tables(const R *dw, int n, int layer, 
         const int q = rq[m];
         g0[m] = hfactor<R>(wl, q, false);
         g1[m] = hfactor<R>(wl, q, true);
-        if (nb_odd(fixed_bits, q, n)) {   // CZ with a fixed neighbour at 1
+        if (cz && nb_odd(fixed_bits, q, n)) {   // CZ with a fixed neighbour at 1
             g1[m].x = -g1[m].x;
             g1[m].y = -g1[m].y;
         }
     }
-    auto adj = [&](int a, int b) { const int d = rq[a] - rq[b]; return d == 1 || d == -1; };
+    auto adj = [&](int a, int b) { const int d = rq[a] - rq[b]; return cz && (d == 1 || d == -1); };
     HDiag<R> t;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -1789,7 +1828,14 @@ __device__ __forceinline__ void hdiag_dag(HTile<R> &t, HDiag<R> d, R s)
     }
 }
 
-template <int ST, typename R>
+// Shapes of the half-tile adjoint pass.
+enum HalfShape : int {
+    HB_GENERAL = 0,   // CZ-chain plan: [rotA(la), D_la, rotB(lb)], merged statistics
+    HB_ROTAD = 1,     // CNOT-chain plan: [rotA(l), diag(p_l)]
+    HB_DROTB = 2      // CNOT-chain plan: [diag(r_l), rotB(l)], lambda written back through P^-1
+};
+
+template <int ST, int HS, typename R>
 __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 4 : 2) void k_tile_bwdh(TilePassArgs a)
 {
     __shared__ V2<R> lds[1 << kHalfBits];
@@ -1798,31 +1844,52 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 4 : 2) void k_tile_bwdh(
     const R *dw = static_cast<const R *>(a.dw);
     const ViewDevH &v = *a.hview;
     const int T2 = a.T * 2, n = a.n, la = a.rotA, lb = a.rotB;
+    const uint32_t tv = (uint32_t)threadIdx.x;
+    // the CZ plan's general passes go in the XCD-contiguous order with lambda through L2;
+    // the CNOT-chain passes (lambda moves through the chain's index map) in the plain order
+    constexpr bool kXcd = HS == HB_GENERAL;
     HCtx c;
-    hctx(c, v, T2, xcd_slot((int)blockIdx.x, (int)gridDim.x), a.sample0);
+    hctx(c, v, T2, kXcd ? xcd_slot((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x, a.sample0);
     zero_stats(lds_stat);
     __syncthreads();
     const uint64_t nelem = 1ull << n;
     HTile<R> p, l;
     hload<ST, true>(p, a.psi_in, c, nelem);
-    if constexpr (sizeof(R) == 4)
+    if constexpr (sizeof(R) == 4 && kXcd)
         hload<0, false>(l, a.lam, c, nelem);   // through L2 (the XCD-contiguous order keeps it there)
     else
-        hload<2, true>(l, a.lam, c, nelem);
-    {   // merged statistics at the pass output: positions 0, 1 and 4..7 (H1)
+        hload<kLamIO<R>, true>(l, a.lam, c, nelem);
+    if constexpr (HS == HB_ROTAD) {   // diag(p_l)^dagger on both states: to the point after rotA
+        const HDiag<R> d = hdiag_tables<true>(dw, n, a.diag, c, v, tv, false);
+        hdiag_dag(p, d, (R)1);
+        hdiag_dag(l, d, (R)1);
+    }
+    // statistics of every position at one point (the pass output, or after diag(p_l)^dagger)
+    // the CZ plan's merged statistics; a CNOT-chain pass's single rotation layer: slot group sel
+    constexpr int sel = HS == HB_DROTB ? 1 : 0;
+    {   // positions 0, 1 and 4..7 (H1)
         R dz[4];
         const R W = hzsum<4, 0>(p, l, dz);
         R sx, sy;
         hxy_lane<0>(p, l, c.lane, sx, sy);
-        hstat_out(sx, sy, (c.lane & 1) ? -W : W, (R)1, nb_odd(c.fixed1, c.q0[0], n), c.q0[0], ldu(&v.slot_pos[0]),
-                  lds_stat, c.lane, c.w);
+        if constexpr (HS == HB_GENERAL)
+            hstat_out(sx, sy, (c.lane & 1) ? -W : W, (R)1, nb_odd(c.fixed1, c.q0[0], n), c.q0[0], ldu(&v.slot_pos[0]),
+                      lds_stat, c.lane, c.w);
+        else
+            hstat_plain(sx, sy, (c.lane & 1) ? -W : W, sel, ldu(&v.slot_pos[0]), lds_stat, c.lane, c.w);
         hxy_lane<1>(p, l, c.lane, sx, sy);
-        hstat_out(sx, sy, (c.lane & 2) ? -W : W, (R)1, nb_odd(c.fixed1, c.q0[1], n), c.q0[1], ldu(&v.slot_pos[1]),
-                  lds_stat, c.lane, c.w);
-#define HQML_HSTAT1(M)                                                                                      \
-    hxy_reg<M>(p, l, sx, sy);                                                                               \
-    hstat_out(sx, sy, dz[M], (R)1, nb_odd(c.fixed1, c.q1[M], n), c.q1[M], ldu(&v.slot_pos[4 + M]), lds_stat, c.lane,  \
-              c.w);
+        if constexpr (HS == HB_GENERAL)
+            hstat_out(sx, sy, (c.lane & 2) ? -W : W, (R)1, nb_odd(c.fixed1, c.q0[1], n), c.q0[1], ldu(&v.slot_pos[1]),
+                      lds_stat, c.lane, c.w);
+        else
+            hstat_plain(sx, sy, (c.lane & 2) ? -W : W, sel, ldu(&v.slot_pos[1]), lds_stat, c.lane, c.w);
+#define HQML_HSTAT1(M)                                                                                         \
+    hxy_reg<M>(p, l, sx, sy);                                                                                  \
+    if constexpr (HS == HB_GENERAL)                                                                            \
+        hstat_out(sx, sy, dz[M], (R)1, nb_odd(c.fixed1, c.q1[M], n), c.q1[M], ldu(&v.slot_pos[4 + M]), lds_stat, \
+                  c.lane, c.w);                                                                                \
+    else                                                                                                       \
+        hstat_plain(sx, sy, dz[M], sel, ldu(&v.slot_pos[4 + M]), lds_stat, c.lane, c.w);
         HQML_HSTAT1(0)
         HQML_HSTAT1(1)
         HQML_HSTAT1(2)
@@ -1831,50 +1898,82 @@ __global__ __launch_bounds__(kThreads, sizeof(R) == 4 ? 4 : 2) void k_tile_bwdh(
     }
     htranspose(p, lds, c.a1, c.a2, true);
     htranspose(l, lds, c.a1, c.a2, true);
-    {   // positions 8..11 (H2), also at the pass output
+    {   // positions 8..11 (H2), at the same point
         R dz[4];
         (void)hzsum<4, 0>(p, l, dz);
         R sx, sy;
-#define HQML_HSTAT2(M)                                                                                       \
-    hxy_reg<M>(p, l, sx, sy);                                                                                \
-    hstat_out(sx, sy, dz[M], (R)1, nb_odd(c.fixed2, c.q2[M], n), c.q2[M], ldu(&v.slot_pos[8 + M]), lds_stat, c.lane, \
-              c.w);
+#define HQML_HSTAT2(M)                                                                                         \
+    hxy_reg<M>(p, l, sx, sy);                                                                                  \
+    if constexpr (HS == HB_GENERAL)                                                                            \
+        hstat_out(sx, sy, dz[M], (R)1, nb_odd(c.fixed2, c.q2[M], n), c.q2[M], ldu(&v.slot_pos[8 + M]), lds_stat, \
+                  c.lane, c.w);                                                                                \
+    else                                                                                                       \
+        hstat_plain(sx, sy, dz[M], sel, ldu(&v.slot_pos[8 + M]), lds_stat, c.lane, c.w);
         HQML_HSTAT2(0)
         HQML_HSTAT2(1)
         HQML_HSTAT2(2)
         HQML_HSTAT2(3)
 #undef HQML_HSTAT2
     }
-    // lambda: layer lb at 8..11 and 0, 1 (H2), at 4..7 (H1); D_la^dagger (H1), which removes
-    // the scales so far; layer la at 4..7 and 0, 1 (H1), at 8..11 (H2); store from H2
-    const HCoef<R> b2 = hcoef<4>(rot_tf, n, lb, c.q2, c.gm2);
-    hunrot_regs(l, b2);
-    const HCoef<R> b0 = hcoef<2>(rot_tf, n, lb, c.q0, c.gm0);
-    hunrot_lane<0>(l, b0.k[0], c.lane);
-    hunrot_lane<1>(l, b0.k[1], c.lane);
-    htranspose(l, lds, c.a1, c.a2, false);
-    const HCoef<R> b1 = hcoef<4>(rot_tf, n, lb, c.q1, c.gm1);
-    hunrot_regs(l, b1);
-    hdiag_dag(l, hdiag_tables<true>(dw, n, a.diag, c, v, (uint32_t)threadIdx.x), b1.F * b2.F * b0.F);
-    const HCoef<R> a1 = hcoef<4>(rot_tf, n, la, c.q1, c.gm1);
-    hunrot_regs(l, a1);
-    const HCoef<R> a0 = hcoef<2>(rot_tf, n, la, c.q0, c.gm0);
-    hunrot_lane<0>(l, a0.k[0], c.lane);
-    hunrot_lane<1>(l, a0.k[1], c.lane);
-    htranspose(l, lds, c.a1, c.a2, true);
-    const HCoef<R> a2 = hcoef<4>(rot_tf, n, la, c.q2, c.gm2);
-    hunrot_regs(l, a2);
-    const R sl = a2.F * a0.F * a1.F;
-    if (sl != (R)1) {
+    R *dst = static_cast<R *>(a.stat_part) + ((size_t)c.sample * T2 + c.tile) * kSlots;
+    if constexpr (HS == HB_GENERAL) {
+        // lambda: layer lb at 8..11 and 0, 1 (H2), at 4..7 (H1); D_la^dagger (H1), which removes
+        // the scales so far; layer la at 4..7 and 0, 1 (H1), at 8..11 (H2); store from H2
+        const HCoef<R> b2 = hcoef<4>(rot_tf, n, lb, c.q2, c.gm2);
+        hunrot_regs(l, b2);
+        const HCoef<R> b0 = hcoef<2>(rot_tf, n, lb, c.q0, c.gm0);
+        hunrot_lane<0>(l, b0.k[0], c.lane);
+        hunrot_lane<1>(l, b0.k[1], c.lane);
+        htranspose(l, lds, c.a1, c.a2, false);
+        const HCoef<R> b1 = hcoef<4>(rot_tf, n, lb, c.q1, c.gm1);
+        hunrot_regs(l, b1);
+        hdiag_dag(l, hdiag_tables<true>(dw, n, a.diag, c, v, tv), b1.F * b2.F * b0.F);
+        const HCoef<R> a1 = hcoef<4>(rot_tf, n, la, c.q1, c.gm1);
+        hunrot_regs(l, a1);
+        const HCoef<R> a0 = hcoef<2>(rot_tf, n, la, c.q0, c.gm0);
+        hunrot_lane<0>(l, a0.k[0], c.lane);
+        hunrot_lane<1>(l, a0.k[1], c.lane);
+        htranspose(l, lds, c.a1, c.a2, true);
+        const HCoef<R> a2 = hcoef<4>(rot_tf, n, la, c.q2, c.gm2);
+        hunrot_regs(l, a2);
+        const R sl = a2.F * a0.F * a1.F;
+        if (sl != (R)1) {
 #pragma unroll
-        for (int j = 0; j < kHalfRegs; ++j) {
-            l.re[j] *= sl;
-            l.im[j] *= sl;
+            for (int j = 0; j < kHalfRegs; ++j) {
+                l.re[j] *= sl;
+                l.im[j] *= sl;
+            }
         }
+        hstore2(l, a.lam, c, nelem);
+        flush_merged(lds_stat, dst, false, *a.view, rot_tf, dw, n, a.diag, lb);
+    } else {
+        // the pass's rotation layer lr at 8..11 and 0, 1 (H2) and at 4..7 (H1); DROTB then takes
+        // lambda back through diag(r_l) (removing the scales) and writes it through P^-1
+        const int lr = HS == HB_DROTB ? lb : la;
+        const HCoef<R> r2 = hcoef<4>(rot_tf, n, lr, c.q2, c.gm2);
+        hunrot_regs(l, r2);
+        const HCoef<R> r0 = hcoef<2>(rot_tf, n, lr, c.q0, c.gm0);
+        hunrot_lane<0>(l, r0.k[0], c.lane);
+        hunrot_lane<1>(l, r0.k[1], c.lane);
+        htranspose(l, lds, c.a1, c.a2, false);
+        const HCoef<R> r1 = hcoef<4>(rot_tf, n, lr, c.q1, c.gm1);
+        hunrot_regs(l, r1);
+        const R sl = r2.F * r0.F * r1.F;
+        if constexpr (HS == HB_DROTB) {
+            hdiag_dag(l, hdiag_tables<true>(dw, n, a.diag, c, v, tv, false), sl);
+            hstore1<true>(l, a.psi_out, c, nelem);   // the second lambda buffer (other tiles read a.lam)
+        } else {
+            if (sl != (R)1) {
+#pragma unroll
+                for (int j = 0; j < kHalfRegs; ++j) {
+                    l.re[j] *= sl;
+                    l.im[j] *= sl;
+                }
+            }
+            hstore1<false>(l, a.lam, c, nelem);
+        }
+        flush_stats(lds_stat, dst, false);
     }
-    hstore2(l, a.lam, c, nelem);
-    flush_merged(lds_stat, static_cast<R *>(a.stat_part) + ((size_t)c.sample * T2 + c.tile) * kSlots, false,
-                 *a.view, rot_tf, dw, n, a.diag, lb);
 }
 
 // ------------------------------------------------------------------ table preparation (fp64)
@@ -2391,13 +2490,24 @@ template <int ST, typename R>
 static void launch_bwd_shape(const TilePassArgs &a, dim3 grid, hipStream_t s, bool *bad)
 {
     if (a.flags & PF_HALF) {
-        // the general shape on half tiles (fp32 compute with fp32 or bf16 psi, fp64 compute
-        // with fp32 or fp64 psi): two per full tile
+        // the general shape (CZ chain) and the CNOT chain's [rotA, diag] and [diag, rotB] shapes on
+        // half tiles (fp32 compute with fp32 or bf16 psi, fp64 compute with fp32 or fp64 psi): two
+        // per full tile
         if constexpr ((std::is_same<R, float>::value && ST != 2) || (std::is_same<R, double>::value && ST != 1)) {
-            if (a.rotA >= 0 && a.diag >= 0 && a.rotB >= 0 && a.hview &&
-                !(a.flags & (PF_CNOT | PF_FUSED | PF_INIT | PF_SEED | PF_STATS_ONLY))) {
-                k_tile_bwdh<ST, R><<<dim3(grid.x * 2), kThreads, 0, s>>>(a);
-                return;
+            const dim3 g2(grid.x * 2);
+            if (a.hview && !(a.flags & (PF_FUSED | PF_INIT | PF_SEED | PF_STATS_ONLY))) {
+                if (!(a.flags & PF_CNOT) && a.rotA >= 0 && a.diag >= 0 && a.rotB >= 0) {
+                    k_tile_bwdh<ST, HB_GENERAL, R><<<g2, kThreads, 0, s>>>(a);
+                    return;
+                }
+                if ((a.flags & PF_CNOT) && a.rotA >= 0 && a.diag >= 0 && a.rotB < 0) {
+                    k_tile_bwdh<ST, HB_ROTAD, R><<<g2, kThreads, 0, s>>>(a);
+                    return;
+                }
+                if ((a.flags & PF_CNOT) && (a.flags & PF_GATHER) && a.rotA < 0 && a.diag >= 0 && a.rotB >= 0) {
+                    k_tile_bwdh<ST, HB_DROTB, R><<<g2, kThreads, 0, s>>>(a);
+                    return;
+                }
             }
         }
         *bad = true;

@@ -238,8 +238,8 @@ bool build_half_view(int n, const ViewDev &full, ViewDevH *out)
 
 int stat_tiles(const Plan &p, int compute64)
 {
-    (void)compute64;   // both compute types run the general passes on half tiles
-    return (p.half && !p.cnot && !p.small) ? 2 * p.T : p.T;
+    (void)compute64;   // both compute types run the half-tile adjoint shapes
+    return (p.half && !p.small) ? 2 * p.T : p.T;
 }
 
 bool make_obs_view(int n, uint32_t xmask, ViewDev *out, std::string *err)
@@ -350,17 +350,17 @@ bool make_plan(int n, int L, int ckpt_block, Plan *out, std::string *err, bool c
         return true;
     }
     if (!build_views(n, p, err)) return false;
+    p.hviews.assign(p.V, ViewDevH{});
+    p.half = true;
+    for (int v = 0; v < p.V; ++v)
+        if (!build_half_view(n, p.views[v], &p.hviews[v])) p.half = false;
+    if (!p.half) p.hviews.clear();
     if (cnot) {
         if (!make_plan_cnot(p, ckpt_block, err)) return false;
         *out = p;
         return true;
     }
     const int V = p.V;
-    p.hviews.assign(V, ViewDevH{});
-    p.half = true;
-    for (int v = 0; v < V; ++v)
-        if (!build_half_view(n, p.views[v], &p.hviews[v])) p.half = false;
-    if (!p.half) p.hviews.clear();
     auto group_has = [&](int v, int q) {
         const int pos = p.views[v].inv[q];
         return pos >= 0 && ((p.views[v].group_mask >> pos) & 1);

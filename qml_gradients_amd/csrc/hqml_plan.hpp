@@ -33,9 +33,10 @@ struct Plan {
     int V = 0;                           // views (tile path)
     int T = 1;                           // tiles per sample
     std::vector<ViewDev> views;
-    std::vector<ViewDevH> hviews;        // half-tile views of the same groups (CZ-chain plan)
-    bool half = false;                   // every view has a half-tile view: the adjoint's
-                                         // general passes run on half tiles
+    std::vector<ViewDevH> hviews;        // half-tile views of the same groups
+    bool half = false;                   // every view has a half-tile view: the adjoint passes of
+                                         // the general shape (and the CNOT chain's two shapes with a
+                                         // diagonal) run on half tiles
     std::vector<PassPlan> fwd;           // forward passes in order
     std::vector<int> stats_only;         // views needing a layer-0 stats-only backward pass
     std::vector<StatLoc> statmap;        // [L*n]
@@ -74,8 +75,8 @@ struct Workspace {
     size_t total = 0;
 };
 
-// Statistics partials per sample of a backward pass: 2T when the adjoint runs its general
-// passes on half tiles (p.half, the CZ-chain tile plan), else T.
+// Statistics partials per sample of a backward pass: 2T when the adjoint runs passes on half
+// tiles (p.half), else T.
 int stat_tiles(const Plan &p, int compute64);
 
 // storage: 0 fp32, 1 bf16, 2 fp64 saved states; compute64: arithmetic (and lambda,
