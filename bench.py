@@ -52,7 +52,7 @@ L2_POSITIONS = (0, 1, 9, 10, 11)
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     # what the tile kernels are built from: their sources and the build's compile flags
-    for f in ("hqml_kernels.hip", "hqml_device.hpp", "hqml_internal.hpp"):
+    for f in ("hqml_kernels.hip", "hqml_half.hpp", "hqml_device.hpp", "hqml_internal.hpp"):
         with open(os.path.join(ROOT, "qml_gradients_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     from qml_gradients_amd import build as hq_build

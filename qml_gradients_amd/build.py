@@ -15,8 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libhqml.so")
-SOURCES = ["hqml_kernels.hip", "hqml_small.hip", "hqml_gbg.hip", "hqml_noalloc.hip", "hqml_abi.cpp",
-           "hqml_plan.cpp"]
+SOURCES = ["hqml_kernels.hip", "hqml_small.hip", "hqml_small12.hip", "hqml_gbg.hip", "hqml_noalloc.hip",
+           "hqml_abi.cpp", "hqml_plan.cpp"]
 # Compilation units: (source, extra flags).  hqml_kernels.hip is compiled a second time
 # for the fp32 adjoint launches alone, with the backend's max-ilp instruction schedule;
 # the whole-circuit kernel takes the iterative-maxocc schedule (measured 1.5-2 % faster

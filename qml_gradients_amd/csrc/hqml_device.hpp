@@ -72,6 +72,17 @@ __device__ __forceinline__ double2 mk2(double a, double b) { return make_double2
 __device__ __forceinline__ float fmar(float a, float b, float c) { return fmaf(a, b, c); }
 __device__ __forceinline__ double fmar(double a, double b, double c) { return fma(a, b, c); }
 
+// Table entry (factor for bit value 0 in x, y; for 1 in z, w) as a uniform value held in
+// scalar registers.  Without the pin the compiler may turn a per-lane choice between the
+// two factors into a per-lane load address: one vector load, waited on, per use.
+template <typename R>
+__device__ __forceinline__ V4<R> uniform_v4(const V4<R> *p)
+{
+    V4<R> f = ldu4(reinterpret_cast<const R *>(p));
+    asm volatile("" : "+s"(f.x), "+s"(f.y), "+s"(f.z), "+s"(f.w));
+    return f;
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dppf(float v)
 {

@@ -27,6 +27,10 @@ hipError_t launch_small(const SmallArgs &a, int B, int r64, hipStream_t s);
 // amplitudes, 128 KiB) on the current device.  Never lowered, so contexts and calls of
 // different sizes can interleave.
 hipError_t configure_small();
+// 12 qubits, CZ chain, fp32 compute: the register-resident whole-circuit kernel
+// (hqml_small12.hip), reached through launch_small / configure_small.
+hipError_t launch_small12(const SmallArgs &a, int B, hipStream_t s);
+hipError_t configure_small12();
 hipError_t launch_ez_reduce(const void *e_part, int r64, int B, int T, const void *y, void *e_out, void *loss,
                             int io64, double *dlde, double *e_work, double *chunks, hipStream_t s);
 hipError_t launch_copy_dlde(const void *src, int io64, int B, double *dlde, hipStream_t s);

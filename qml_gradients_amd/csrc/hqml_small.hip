@@ -9,6 +9,7 @@
 #include <stdint.h>
 
 #include "hqml_device.hpp"
+#include "hqml_host.hpp"
 #include "hqml_internal.hpp"
 
 namespace hqml {
@@ -18,17 +19,6 @@ namespace hqml {
 constexpr int kSmallThreads = 512;               // eight waves: two per SIMD hide each other's latency
 constexpr int kRoundBits = 3;                    // qubits per register round
 constexpr int kSmallRows = kSmallThreads / 16;   // DPP row partials per workgroup
-
-// Table entry (factor for bit value 0 in x, y; for 1 in z, w) as a uniform value held in
-// scalar registers.  Without the pin the compiler may turn a per-lane choice between the
-// two factors into a per-lane load address: one vector load, waited on, per use.
-template <typename R>
-__device__ __forceinline__ V4<R> uniform_v4(const V4<R> *p)
-{
-    V4<R> f = ldu4(reinterpret_cast<const R *>(p));
-    asm volatile("" : "+s"(f.x), "+s"(f.y), "+s"(f.z), "+s"(f.w));
-    return f;
-}
 
 // D_l of amplitude i: CZ-chain sign times the per-qubit factors f0 / f1.
 template <typename R>
@@ -868,11 +858,12 @@ hipError_t configure_small()
         const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxShm);
         if (e != hipSuccess) return e;
     }
-    return hipSuccess;
+    return configure_small12();
 }
 
 hipError_t launch_small(const SmallArgs &a, int B, int r64, hipStream_t s)
 {
+    if (!r64 && a.ent == 0 && a.n == 12) return launch_small12(a, B, s);
     const size_t shm = (size_t)2 * ((size_t)1 << a.n) * (r64 ? sizeof(double2) : sizeof(float2));
     if (r64) {
         if (a.ent)

@@ -262,9 +262,10 @@ def _whole_circuit_obs(n):
 @pytest.mark.parametrize("L", [1, 4])
 @pytest.mark.parametrize("n", list(range(1, 14)))
 def test_whole_circuit_every_width(n, L):
-    """Whole-circuit kernel at every width 1..13: the register rounds cover qubits
-    0..3, 4..7, 8..11, 12 and so leave remainders of 1..3 qubits; the diagonal's CZ
-    between qubits 3 and 4 exists only for n > 4; small n leaves most threads idle.
+    """Whole-circuit kernels at every width 1..13 (n = 12: the register-resident kernel):
+    the register rounds cover qubits 0..2, 3..5, 6..8, 9..11, 12 and so leave remainders of
+    1..2 qubits; the diagonal's CZ between qubits 3 and 4 exists only for n > 4; small n leaves
+    most threads idle.
     Train step and forward/backward split, a smaller batch on the same context."""
     import qml_gradients_amd as hq
     zm, xm = _whole_circuit_obs(n)
@@ -286,6 +287,55 @@ def test_whole_circuit_every_width(n, L):
     assert_e_close(e2, e2_ref, n, L)
     assert_grad_close(g2, g2_ref)
     ctx.close()
+
+
+# Pauli strings (z mask, x mask) for the 12-qubit register kernel: factors on qubits held
+# in registers and at lane bits of either layout, Y factors (both masks), and a string over
+# all twelve qubits.
+_S12_STRINGS = [(0x001, 0x000), (0x800, 0x001), (0x018, 0x018), (0x0c3, 0x30c), (0x000, 0x900), (0xfff, 0xa5a)]
+
+
+@pytest.mark.parametrize("L", [1, 2, 5])
+@pytest.mark.parametrize("zm,xm", _S12_STRINGS)
+def test_whole_circuit_12_qubits(zm, xm, L):
+    """12 qubits with the CZ chain run on the register-resident whole-circuit kernel (two
+    layouts, one LDS transpose per layer and state; layers alternate between starting in
+    either layout, so odd and even L end the forward pass in different layouts).  Train
+    step with a ragged second batch on the same context, then a forward / backward split."""
+    import qml_gradients_amd as hq
+    n, maxB = 12, 3
+    x, th, y = hqml_inputs.make_inputs(n, L, maxB, seed=3900 + 7 * L + zm % 97 + xm % 89)
+    say(f"[gpu] 12-qubit register kernel L={L} z={zm:#x} x={xm:#x}")
+    ctx = hq.Context(n, L, maxB, obs_mask=zm, obs_x_mask=xm)
+    for B in (maxB, 1):
+        X, TH, Y = (torch.from_numpy(a) for a in (x[:B], th, y[:B]))
+        e, loss, g = (t.cpu().numpy() for t in ctx.train_step(X, TH, Y))
+        e_ref, loss_ref, g_ref = oracle.train_step(x[:B], th, y[:B], zm, xm)
+        assert_e_close(e, e_ref, n, L)
+        assert abs(float(loss[0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
+        assert_grad_close(g, g_ref)
+    w = np.linspace(-0.5, 1.5, maxB).astype(np.float32)
+    e2 = ctx.forward(torch.from_numpy(x), torch.from_numpy(th)).cpu().numpy()
+    g2 = ctx.backward(torch.from_numpy(w)).cpu().numpy()
+    g2_ref, e2_ref = oracle.backward(x, th, w.astype(np.float64), zm, xm)
+    assert_e_close(e2, e2_ref, n, L)
+    assert_grad_close(g2, g2_ref)
+    ctx.close()
+
+
+def test_whole_circuit_12_qubits_deep():
+    """300 layers on the 12-qubit register kernel: the rotation scales carried through both
+    layouts and folded into each layer's diagonal must not drift."""
+    import qml_gradients_amd as hq
+    n, L, B = 12, 300, 2
+    x, th, y = hqml_inputs.make_inputs(n, L, B, seed=3990)
+    say(f"[gpu] 12-qubit register kernel deep L={L}")
+    ctx = hq.Context(n, L, B)
+    e, loss, g = (t.cpu().numpy() for t in ctx.train_step(*(torch.from_numpy(a) for a in (x, th, y))))
+    ctx.close()
+    e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
+    assert_e_close(e, e_ref, n, L)
+    assert_grad_close(g, g_ref)
 
 
 @pytest.mark.parametrize("entangler", ["cz", "cnot"])
