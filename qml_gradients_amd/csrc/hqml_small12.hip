@@ -161,41 +161,50 @@ __device__ __forceinline__ void s12_rotate(HTile<float> &t, const S12Coef &c, in
     dpp_self8<1>(t.im + 8, k1);
 }
 
-// Row sums of one qubit's (X, Y, Z) statistics; the row leader writes them, times corr, to
+// Statistics S_X, S_Y, S_Z of the six qubits of layout LA from (psi p, lambda l): all
+// eighteen thread sums first, then their DPP row sums interleaved (eighteen independent
+// chains hide the DPP latency), then one leader branch writes them, times corr, to
 // red[(q * 3 + s) * kS12Rows + row].
-__device__ __forceinline__ void s12_stat_out(float sx, float sy, float sz, float corr, int q, float *red, int lane,
-                                             int w)
-{
-    row_sum16x3(sx, sy, sz);
-    if ((lane & 15) == 15) {
-        const int r = w * 4 + (lane >> 4);
-        red[(q * 3 + 0) * kS12Rows + r] = sx * corr;
-        red[(q * 3 + 1) * kS12Rows + r] = sy * corr;
-        red[(q * 3 + 2) * kS12Rows + r] = sz * corr;
-    }
-}
-
-// Statistics S_X, S_Y, S_Z of the six qubits of layout LA from (psi p, lambda l).
 template <bool LA>
 __device__ __forceinline__ void s12_stats(const HTile<float> &p, const HTile<float> &l, float corr, float *red,
                                           int lane, int w)
 {
     constexpr int qa = LA ? 0 : 2, q0 = LA ? 4 : 8;
+    float v[18];   // (x, y, z) of lane bit 0, lane bit 1, register bits 0..3
     float dz[4];
     const float W = hzsum<4, 0>(p, l, dz);
-    float sx, sy;
-    hxy_lane<0>(p, l, lane, sx, sy);
-    s12_stat_out(sx, sy, (lane & 1) ? -W : W, corr, qa, red, lane, w);
-    hxy_lane<1>(p, l, lane, sx, sy);
-    s12_stat_out(sx, sy, (lane & 2) ? -W : W, corr, qa + 1, red, lane, w);
-    hxy_reg<0>(p, l, sx, sy);
-    s12_stat_out(sx, sy, dz[0], corr, q0, red, lane, w);
-    hxy_reg<1>(p, l, sx, sy);
-    s12_stat_out(sx, sy, dz[1], corr, q0 + 1, red, lane, w);
-    hxy_reg<2>(p, l, sx, sy);
-    s12_stat_out(sx, sy, dz[2], corr, q0 + 2, red, lane, w);
-    hxy_reg<3>(p, l, sx, sy);
-    s12_stat_out(sx, sy, dz[3], corr, q0 + 3, red, lane, w);
+    hxy_lane<0>(p, l, lane, v[0], v[1]);
+    v[2] = (lane & 1) ? -W : W;
+    hxy_lane<1>(p, l, lane, v[3], v[4]);
+    v[5] = (lane & 2) ? -W : W;
+    hxy_reg<0>(p, l, v[6], v[7]);
+    v[8] = dz[0];
+    hxy_reg<1>(p, l, v[9], v[10]);
+    v[11] = dz[1];
+    hxy_reg<2>(p, l, v[12], v[13]);
+    v[14] = dz[2];
+    hxy_reg<3>(p, l, v[15], v[16]);
+    v[17] = dz[3];
+#pragma unroll
+    for (int k = 0; k < 18; ++k) v[k] += dppf<0xB1>(v[k]);   // quad_perm [1,0,3,2]
+#pragma unroll
+    for (int k = 0; k < 18; ++k) v[k] += dppf<0x4E>(v[k]);   // quad_perm [2,3,0,1]
+#pragma unroll
+    for (int k = 0; k < 18; ++k) v[k] += dppf<0x141>(v[k]);  // row_half_mirror
+#pragma unroll
+    for (int k = 0; k < 18; ++k) {
+        v[k] += dppf<0x140>(v[k]);                            // row_mirror
+        // keep the last add out of the leader's branch (where it cannot take the DPP operand)
+        asm volatile("" : "+v"(v[k]));
+    }
+    if ((lane & 15) == 15) {
+        const int r = w * 4 + (lane >> 4);
+#pragma unroll
+        for (int k = 0; k < 18; ++k) {
+            const int q = k < 6 ? qa + k / 3 : q0 + (k - 6) / 3;
+            red[(q * 3 + k % 3) * kS12Rows + r] = v[k] * corr;
+        }
+    }
 }
 
 template <bool LA>
