@@ -144,6 +144,24 @@ def algorithmic_flops_bwd(plan: dict, B: int, compute: str = "fp32"):
     return total
 
 
+def algorithmic_flops_small(n: int, L: int, B: int):
+    """Floating-point operations of the whole-circuit kernel per train step (FMA = 2,
+    multiply or add = 1), per amplitude and sample: each of the L - 1 forward steps applies
+    a merged diagonal (6) and rotates n qubits in tan form (4 per qubit); the adjoint takes
+    X and Y statistics of every qubit at each of the L points (8 per qubit), the Z
+    statistics (1 per qubit and 2 per amplitude for Im(conj(lambda) psi)), and each of its
+    L - 1 steps applies the conjugate diagonal to psi and lambda (12) and un-rotates both
+    (8 per qubit)."""
+    per_amp = (L - 1) * (6 + 4 * n) + L * (9 * n + 2) + (L - 1) * (12 + 8 * n)
+    return per_amp * (1 << n) * B
+
+
+def small_kernel_name(n: int, entangler: str, compute: str) -> str:
+    """The whole-circuit kernel a context runs: the register-resident one at 12 qubits with
+    the CZ chain in fp32 compute, the register-round one otherwise."""
+    return "k_small12" if n == 12 and entangler == "cz" and compute == "fp32" else "k_small"
+
+
 def traffic_record(kernel: str, workload: str, entangler: str = "cz"):
     """Counter-measured HBM bytes per launch (CZ-chain plan), while the source matches."""
     if entangler != "cz":
@@ -434,6 +452,14 @@ def main():
         roof_bwd_alu["peak_basis"] = ("non-packed fp32 FMA: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz "
                                       "(self-derived; packed FP32 is excluded from the build)")
     roof_fwd = roof_hbm(hq.HQML_K_FWD_PASS, fwd_b, "k_tile_fwd")
+    roof_small = None
+    if plan.get("small"):   # the whole circuit in one kernel: the state never leaves the chip
+        roof_small = roof_alu(hq.HQML_K_SMALL, algorithmic_flops_small(w.n_qubits, w.n_layers, B), 0,
+                              small_kernel_name(w.n_qubits, args.entangler, args.compute))
+        if roof_small:
+            roof_small["peak_basis"] = ("non-packed fp32 FMA: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz "
+                                        "(self-derived); one workgroup per sample, so a batch of B uses at most B "
+                                        "of the 256 compute units")
     step_bytes = fwd_b + bwd_b
     out = {
         "metric": "train samples/sec (fwd+adjoint bwd) 20q HEA 100L; achieved HBM GB/s vs peak",
@@ -460,7 +486,7 @@ def main():
         "step_hbm_frac": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
         "passes": {"fwd": len(plan["passes"]), "bwd": len(plan["passes"]) + len(plan["stats_only"]),
                    "per_layer": round(len(plan["passes"]) / w.n_layers, 3)},
-        "roofline": roof_bwd if roof_bwd else roof_fwd,
+        "roofline": roof_bwd if roof_bwd else roof_fwd if roof_fwd else roof_small,
         "roofline_alu": roof_bwd_alu,
         "roofline_fwd": roof_fwd,
         "kernel_ms_per_step": {k: round(ms_k[i] / max(n_steps, 1), 3) for i, k in

@@ -329,3 +329,53 @@ def test_tile_layouts_bijective_and_conflict_free():
     for t in range(0, 8192, 97):
         for j in range(32):
             assert swz(l1(t & 63, t >> 6 & 3, 0) ^ (j << 4)) == swz(l1(t & 63, t >> 6 & 3, 0)) ^ swz(j << 4)
+
+
+def chain_pair_slot(blk, G, T2):
+    """Grid slot of workgroup blk in the passes that move a state through the CNOT chain's
+    index map (hqml_kernels.hip, chain_pair_slot), restated."""
+    if (G & 15) or T2 < 2:
+        return blk
+    p = ((blk >> 4) << 3) | (blk & 7)
+    h = (blk >> 3) & 1
+    half = T2 >> 1
+    rel, t = divmod(p, half)
+    return rel * T2 + (T2 - 1 - t if h else t)
+
+
+@pytest.mark.parametrize("T2", [2, 4, 8, 64, 256, 4096])
+@pytest.mark.parametrize("samples", [1, 2, 3, 5, 32])
+def test_chain_pair_slot_pairs_complementary_tiles(T2, samples):
+    """A bijection of the grid; where 16 divides it, workgroups b and b + 8 (one XCD, b % 8
+    equal) take tiles t and T2 - 1 - t of the same sample: the two tiles whose amplitudes
+    share each 128-byte line of a state moved through the chain's index map."""
+    G = samples * T2
+    slots = [chain_pair_slot(b, G, T2) for b in range(G)]
+    assert sorted(slots) == list(range(G))
+    if G % 16:
+        assert slots == list(range(G))
+        return
+    for b in range(G):
+        if (b >> 3) & 1:
+            continue
+        s0, s1 = slots[b], slots[b + 8]
+        assert s0 // T2 == s1 // T2 and (s0 % T2) ^ (s1 % T2) == T2 - 1
+
+
+@pytest.mark.parametrize("n", [14, 17, 20])
+def test_chain_line_halves_come_from_complementary_tiles(n):
+    """The reason for the pairing: for a line of 16 consecutive indices a (bits 4.. fixed),
+    the indices j = P(a) of its amplitudes (P: bit k = parity of bits 0..k) split into two
+    halves of 8 whose bits 4.. differ in every position."""
+    def chain(i):
+        out, par = 0, 0
+        for k in range(n):
+            par ^= (i >> k) & 1
+            out |= par << k
+        return out
+    hi_mask = ((1 << n) - 1) & ~15
+    for line in (0, 1, 0x2a, (1 << (n - 4)) - 1):
+        js = [chain((line << 4) | a) for a in range(16)]
+        highs = sorted({j & hi_mask for j in js})
+        assert len(highs) == 2 and highs[0] ^ highs[1] == hi_mask
+        assert sum((j & hi_mask) == highs[0] for j in js) == 8

@@ -104,3 +104,66 @@ def test_cnot_adjoint_gather_source_is_the_chain(n):
             src = (hi << G) | chain(j, G)
             assert src == chain((g << G) | j, n)
             assert chain_inv(src, n) == (g << G) | j
+
+
+# ---- the register-resident 12-qubit kernel (k_small12) ----
+#
+# 256 threads (lane 0..63, wave 0..3) x 16 registers j; amplitude index of (lane, wave, j):
+#   layout A: lanes 0..3 -> qubits 0..3, lanes 4, 5 -> 8, 9, waves -> 10, 11, j -> 4..7
+#   layout B: lanes 0, 1 -> 2, 3, lanes 2, 3 -> 0, 1, lanes 4, 5 -> 4, 5, waves -> 6, 7, j -> 8..11
+# LDS slot of index i: hswz(i) = i ^ (bit 8 of i) << 4.
+
+
+def s12_index(la, lane, w, j):
+    if la:
+        return (lane & 15) | ((lane >> 4) << 8) | (w << 10) | (j << 4)
+    return ((lane >> 2) & 3) | ((lane & 3) << 2) | (((lane >> 4) & 3) << 4) | (w << 6) | (j << 8)
+
+
+def hswz(i):
+    return i ^ (((i >> 8) & 1) << 4)
+
+
+@pytest.mark.parametrize("la", [True, False])
+def test_s12_layouts_are_bijections(la):
+    idx = {s12_index(la, lane, w, j) for lane in range(64) for w in range(4) for j in range(16)}
+    assert idx == set(range(1 << 12))
+    assert {hswz(i) for i in range(1 << 12)} == set(range(1 << 12))
+
+
+def test_s12_layouts_rotate_every_qubit():
+    """A layout rotates the qubits of its register bits and of lane bits 0, 1 (DPP quad
+    permutations): A covers 0, 1, 4..7, B covers 2, 3, 8..11; together all twelve, once."""
+    def qubit_of(la, what):
+        base = s12_index(la, 0, 0, 0)
+        assert base == 0
+        i = s12_index(la, *what)
+        assert bin(i).count("1") == 1
+        return i.bit_length() - 1
+    rot = {}
+    for la in (True, False):
+        qs = [qubit_of(la, (1 << b, 0, 0)) for b in (0, 1)] + [qubit_of(la, (0, 0, 1 << m)) for m in range(4)]
+        rot[la] = qs
+    assert rot[True] == [0, 1, 4, 5, 6, 7] and rot[False] == [2, 3, 8, 9, 10, 11]
+
+
+@pytest.mark.parametrize("la", [True, False])
+def test_s12_transposes_are_bank_conflict_free(la):
+    """For every register and half-wave, the 32 lanes' 8-byte slots are distinct modulo 32
+    (256 bytes = the 64 four-byte banks)."""
+    for w in range(4):
+        for j in range(16):
+            for h in (0, 32):
+                banks = {hswz(s12_index(la, lane, w, j)) % 32 for lane in range(h, h + 32)}
+                assert len(banks) == 32, (la, w, j, h)
+
+
+@pytest.mark.parametrize("la", [True, False])
+def test_s12_rows_store_whole_lines(la):
+    """Lanes 0..15 of a register hold 16 consecutive amplitudes (128 bytes of a saved
+    state) in both layouts."""
+    for w in range(4):
+        for j in range(16):
+            for r in range(4):
+                idx = sorted(s12_index(la, lane, w, j) for lane in range(16 * r, 16 * r + 16))
+                assert idx == list(range(idx[0], idx[0] + 16)) and idx[0] % 16 == 0
