@@ -34,7 +34,8 @@ constexpr int kS12Rows = kS12Threads / 16;        // DPP rows: statistics partia
 constexpr int kS12Stats = 3 * kS12Qubits;          // statistics per layer
 
 // Amplitude index of register 0 of this thread in layout A / B (register j adds j << 4 in A,
-// j << 8 in B).  The thread's "fixed" qubits are the index bits set here.
+// j << 8 in B).  Its lane and wave bits are the values of the thread's fixed qubits (those
+// not at register bits, which are zero here).
 __device__ __forceinline__ uint32_t s12_base(bool la, int lane, int w)
 {
     const uint32_t l = (uint32_t)lane, ww = (uint32_t)w;
