@@ -162,38 +162,24 @@ __device__ __forceinline__ void s12_rotate(HTile<float> &t, const S12Coef &c, in
     dpp_self8<1>(t.im + 8, k1);
 }
 
-// Statistics S_X, S_Y, S_Z of the six qubits of layout LA from (psi p, lambda l): all
-// eighteen thread sums first, then their DPP row sums interleaved (eighteen independent
-// chains hide the DPP latency), then one leader branch writes them, times corr, to
-// red[(q * 3 + s) * kS12Rows + row].
-template <bool LA>
-__device__ __forceinline__ void s12_stats(const HTile<float> &p, const HTile<float> &l, float corr, float *red,
-                                          int lane, int w)
+// Statistics S_X, S_Y, S_Z of the qubits of layout LA that sel names (bit 0: those at lane
+// bits 0, 1 and register bit 0; bit 1: those at register bits 1..3) from (psi p, lambda l):
+// the thread sums first, then their DPP row sums interleaved (independent chains hide the
+// DPP latency), then one leader branch writes them, times corr, to
+// red[(q * 3 + s) * kS12Rows + row].  Every value goes through the same operations whatever
+// sel is, so a split of the qubits over workgroups gives the same bits.
+template <int NV>
+__device__ __forceinline__ void s12_rows_out(float (&v)[NV], const int (&qv)[NV / 3], float corr, float *red, int lane,
+                                             int w)
 {
-    constexpr int qa = LA ? 0 : 2, q0 = LA ? 4 : 8;
-    float v[18];   // (x, y, z) of lane bit 0, lane bit 1, register bits 0..3
-    float dz[4];
-    const float W = hzsum<4, 0>(p, l, dz);
-    hxy_lane<0>(p, l, lane, v[0], v[1]);
-    v[2] = (lane & 1) ? -W : W;
-    hxy_lane<1>(p, l, lane, v[3], v[4]);
-    v[5] = (lane & 2) ? -W : W;
-    hxy_reg<0>(p, l, v[6], v[7]);
-    v[8] = dz[0];
-    hxy_reg<1>(p, l, v[9], v[10]);
-    v[11] = dz[1];
-    hxy_reg<2>(p, l, v[12], v[13]);
-    v[14] = dz[2];
-    hxy_reg<3>(p, l, v[15], v[16]);
-    v[17] = dz[3];
 #pragma unroll
-    for (int k = 0; k < 18; ++k) v[k] += dppf<0xB1>(v[k]);   // quad_perm [1,0,3,2]
+    for (int k = 0; k < NV; ++k) v[k] += dppf<0xB1>(v[k]);   // quad_perm [1,0,3,2]
 #pragma unroll
-    for (int k = 0; k < 18; ++k) v[k] += dppf<0x4E>(v[k]);   // quad_perm [2,3,0,1]
+    for (int k = 0; k < NV; ++k) v[k] += dppf<0x4E>(v[k]);   // quad_perm [2,3,0,1]
 #pragma unroll
-    for (int k = 0; k < 18; ++k) v[k] += dppf<0x141>(v[k]);  // row_half_mirror
+    for (int k = 0; k < NV; ++k) v[k] += dppf<0x141>(v[k]);  // row_half_mirror
 #pragma unroll
-    for (int k = 0; k < 18; ++k) {
+    for (int k = 0; k < NV; ++k) {
         v[k] += dppf<0x140>(v[k]);                            // row_mirror
         // keep the last add out of the leader's branch (where it cannot take the DPP operand)
         asm volatile("" : "+v"(v[k]));
@@ -201,10 +187,48 @@ __device__ __forceinline__ void s12_stats(const HTile<float> &p, const HTile<flo
     if ((lane & 15) == 15) {
         const int r = w * 4 + (lane >> 4);
 #pragma unroll
-        for (int k = 0; k < 18; ++k) {
-            const int q = k < 6 ? qa + k / 3 : q0 + (k - 6) / 3;
-            red[(q * 3 + k % 3) * kS12Rows + r] = v[k] * corr;
+        for (int k = 0; k < NV; ++k) red[(qv[k / 3] * 3 + k % 3) * kS12Rows + r] = v[k] * corr;
+    }
+}
+
+template <bool LA>
+__device__ __forceinline__ void s12_stats(const HTile<float> &p, const HTile<float> &l, float corr, float *red,
+                                          int lane, int w, int sel)
+{
+    constexpr int qa = LA ? 0 : 2, q0 = LA ? 4 : 8;
+    float dz[4];
+    const float W = hzsum<4, 0>(p, l, dz);
+    float v0[9], v1[9];   // (x, y, z) of lane bit 0, lane bit 1, register bit 0 / register bits 1..3
+    if (sel & 1) {
+        hxy_lane<0>(p, l, lane, v0[0], v0[1]);
+        v0[2] = (lane & 1) ? -W : W;
+        hxy_lane<1>(p, l, lane, v0[3], v0[4]);
+        v0[5] = (lane & 2) ? -W : W;
+        hxy_reg<0>(p, l, v0[6], v0[7]);
+        v0[8] = dz[0];
+    }
+    if (sel & 2) {
+        hxy_reg<1>(p, l, v1[0], v1[1]);
+        v1[2] = dz[1];
+        hxy_reg<2>(p, l, v1[3], v1[4]);
+        v1[5] = dz[2];
+        hxy_reg<3>(p, l, v1[6], v1[7]);
+        v1[8] = dz[3];
+    }
+    constexpr int q0s[3] = {qa, qa + 1, q0}, q1s[3] = {q0 + 1, q0 + 2, q0 + 3};
+    if (sel == 3) {   // both halves: eighteen chains in one interleaved set
+        float v[18];
+        constexpr int qv[6] = {qa, qa + 1, q0, q0 + 1, q0 + 2, q0 + 3};
+#pragma unroll
+        for (int k = 0; k < 9; ++k) {
+            v[k] = v0[k];
+            v[9 + k] = v1[k];
         }
+        s12_rows_out<18>(v, qv, corr, red, lane, w);
+    } else if (sel == 1) {
+        s12_rows_out<9>(v0, q0s, corr, red, lane, w);
+    } else if (sel == 2) {
+        s12_rows_out<9>(v1, q1s, corr, red, lane, w);
     }
 }
 
@@ -226,11 +250,12 @@ __device__ __forceinline__ void s12_get(HTile<float> &t, const float2 *buf, uint
     }
 }
 
-// Sum of the 16 row partials of each statistic of layer l, in row order, into the output.
-__device__ __forceinline__ void s12_stats_flush(const float *red, const SmallArgs &a, int b, int l)
+// Sum of the 16 row partials of each statistic of layer l, in row order, into the output
+// (the statistics of the qubits in qmask: those this workgroup takes).
+__device__ __forceinline__ void s12_stats_flush(const float *red, const SmallArgs &a, int b, int l, uint32_t qmask)
 {
     const int tid = threadIdx.x;
-    if (tid < kS12Stats) {
+    if (tid < kS12Stats && ((qmask >> (tid / 3)) & 1u)) {
         double s = 0.0;
         for (int r = 0; r < kS12Rows; ++r) s += (double)red[tid * kS12Rows + r];
         a.stats[((size_t)b * a.L + l) * kS12Stats + tid] = s;
@@ -275,7 +300,8 @@ __device__ __forceinline__ float s12_fwd_step(HTile<float> &p, const SmallArgs &
 // undone on those].  Returns the next pending scale.
 template <bool LA>
 __device__ __forceinline__ float s12_adj_step(HTile<float> &p, HTile<float> &q, const SmallArgs &a, int b, int l,
-                                              float c, float2 *bufs, float *red, int lane, int w)
+                                              float c, float2 *bufs, float *red, const int (&sel)[2], uint32_t qmask,
+                                              int lane, int w)
 {
     const uint32_t bx = s12_base(LA, lane, w), by = s12_base(!LA, lane, w);
     const float *rot = static_cast<const float *>(a.rot_tf);
@@ -292,7 +318,8 @@ __device__ __forceinline__ float s12_adj_step(HTile<float> &p, HTile<float> &q, 
         }
     }
     float *rl = red + (l % 3) * kS12Red;
-    s12_stats<LA>(p, q, 1.0f, rl, lane, w);
+    const int selx = sel[LA ? 0 : 1], sely = sel[LA ? 1 : 0];
+    if (selx) s12_stats<LA>(p, q, 1.0f, rl, lane, w, selx);
     float2 *P = bufs + 2 * (l & 1) * kS12Buf, *Q = P + kS12Buf;
     float fx = 1.0f, fy = 1.0f;
     if (l > 0) {
@@ -308,8 +335,8 @@ __device__ __forceinline__ float s12_adj_step(HTile<float> &p, HTile<float> &q, 
     __syncthreads();   // also: layer l+1's partials are complete
     s12_get<!LA>(p, P, by);
     s12_get<!LA>(q, Q, by);
-    if (l + 1 < a.L) s12_stats_flush(red + ((l + 1) % 3) * kS12Red, a, b, l + 1);
-    s12_stats<!LA>(p, q, fx * fx, rl, lane, w);
+    if (l + 1 < a.L) s12_stats_flush(red + ((l + 1) % 3) * kS12Red, a, b, l + 1, qmask);
+    if (sely) s12_stats<!LA>(p, q, fx * fx, rl, lane, w, sely);
     if (l > 0) {
         s12_rotate<!LA, true>(p, cy, lane);
         s12_rotate<!LA, true>(q, cy, lane);
@@ -367,15 +394,41 @@ __device__ __forceinline__ void s12_save(const HTile<float> &p, float2 *save, in
     for (int j = 0; j < kHalfRegs; ++j) save[bx ^ s12_reg<LA>(j)] = mk2(p.re[j], p.im[j]);
 }
 
+// Qubits whose statistics workgroup `part` of a sample takes when `parts` workgroups share the
+// sample (1, 2 or 4): sel[0] / sel[1] name them among layout A's / B's qubits as s12_stats
+// does; the mask lists them.  Every part runs the whole forward pass and un-computes psi and
+// lambda itself: the split costs no exchange between workgroups, and at small batches it
+// puts otherwise idle compute units to work on the statistics.
+__device__ __forceinline__ uint32_t s12_part(int parts, int part, int (&sel)[2])
+{
+    constexpr uint32_t a0 = 0x013u, a1 = 0x0e0u, b0 = 0x10cu, b1 = 0xe00u;   // {0,1,4} {5,6,7} {2,3,8} {9,10,11}
+    if (parts == 4) {
+        sel[0] = part == 0 ? 1 : part == 1 ? 2 : 0;
+        sel[1] = part == 2 ? 1 : part == 3 ? 2 : 0;
+        return part == 0 ? a0 : part == 1 ? a1 : part == 2 ? b0 : b1;
+    }
+    if (parts == 2) {
+        sel[0] = part == 0 ? 3 : 0;
+        sel[1] = part == 1 ? 3 : 0;
+        return part == 0 ? a0 | a1 : b0 | b1;
+    }
+    sel[0] = sel[1] = 3;
+    return 0xfffu;
+}
+
 // The whole step of one sample (modes as k_small: 0 forward, 1 backward from psi_save, 2
-// both).  Statistics of layer l go to a.stats[b][l][q][s] (fp64 sums of 16 row partials in
-// row order), <O> to a.e_out[b].
-__global__ __launch_bounds__(kS12Threads, 1) void k_small12(SmallArgs a)
+// both), on `parts` workgroups (consecutive blocks; part 0 writes <O> and the saved state).
+// Statistics of layer l go to a.stats[b][l][q][s] (fp64 sums of 16 row partials in row
+// order), <O> to a.e_out[b].
+__global__ __launch_bounds__(kS12Threads, 1) void k_small12(SmallArgs a, int parts)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float red[3 * kS12Red + kS12Rows];
     float2 *bufs = reinterpret_cast<float2 *>(smem);
-    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, L = a.L;
+    const int b = (int)blockIdx.x / parts, part = (int)blockIdx.x - b * parts;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, L = a.L;
+    int sel[2];
+    const uint32_t qmask = s12_part(parts, part, sel);
     float2 *save = reinterpret_cast<float2 *>(a.psi_save) + ((size_t)b << kS12Qubits);
     HTile<float> p, q;
     bool inA = true;
@@ -410,7 +463,7 @@ __global__ __launch_bounds__(kS12Threads, 1) void k_small12(SmallArgs a)
             p.im[j] = v.y;
         }
     }
-    if (a.mode == 0) {   // forward only: the final state for a later backward
+    if (a.mode == 0 && part == 0) {   // forward only: the final state for a later backward
         if (inA)
             s12_save<true>(p, save, lane, w);
         else
@@ -424,7 +477,7 @@ __global__ __launch_bounds__(kS12Threads, 1) void k_small12(SmallArgs a)
         float *re = red + 3 * kS12Red;
         if ((lane & 15) == 15) re[w * 4 + (lane >> 4)] = e;
         __syncthreads();
-        if (tid == 0) {
+        if (tid == 0 && part == 0) {
             double s = 0.0;
             for (int r = 0; r < kS12Rows; ++r) s += (double)re[r];
             static_cast<float *>(a.e_out)[b] = (float)s;
@@ -434,12 +487,12 @@ __global__ __launch_bounds__(kS12Threads, 1) void k_small12(SmallArgs a)
     __syncthreads();   // the seed's reads of buffer 2 are done before the adjoint steps write it
     float c = 1.0f;
     for (int l = L - 1; l >= 0; --l) {
-        c = inA ? s12_adj_step<true>(p, q, a, b, l, c, bufs, red, lane, w)
-                : s12_adj_step<false>(p, q, a, b, l, c, bufs, red, lane, w);
+        c = inA ? s12_adj_step<true>(p, q, a, b, l, c, bufs, red, sel, qmask, lane, w)
+                : s12_adj_step<false>(p, q, a, b, l, c, bufs, red, sel, qmask, lane, w);
         inA = !inA;
     }
     __syncthreads();
-    s12_stats_flush(red, a, b, 0);
+    s12_stats_flush(red, a, b, 0, qmask);
 }
 
 hipError_t configure_small12()
@@ -448,9 +501,17 @@ hipError_t configure_small12()
                                kS12Shm);
 }
 
+// Workgroups per sample: 4 or 2 while the whole grid still fits one workgroup per compute
+// unit (the kernel's LDS allows one), else 1; 1 for a forward-only launch (no statistics).
+// The split changes no result bit.
 hipError_t launch_small12(const SmallArgs &a, int B, hipStream_t s)
 {
-    k_small12<<<B, kS12Threads, kS12Shm, s>>>(a);
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int parts = a.mode == 0 ? 1 : 4 * (long long)B <= cus ? 4 : 2 * (long long)B <= cus ? 2 : 1;
+    k_small12<<<(unsigned)B * (unsigned)parts, kS12Threads, kS12Shm, s>>>(a, parts);
     return hipGetLastError();
 }
 

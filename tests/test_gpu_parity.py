@@ -338,6 +338,34 @@ def test_whole_circuit_12_qubits_deep():
     assert_grad_close(g, g_ref)
 
 
+def test_whole_circuit_12_qubits_split_is_bitwise():
+    """At small batches the 12-qubit kernel runs a sample on 4 (batch <= CUs / 4) or 2
+    (batch <= CUs / 2) workgroups that split the statistics by qubit, else on one.  Per-sample
+    E and per-sample gradients (a one-hot dL/dE makes the batch sum that sample's term alone)
+    must be bitwise the same in all three regimes, and match the oracle."""
+    import qml_gradients_amd as hq
+    n, L = 12, 4
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    batches = sorted({1, cus // 2, cus + 3})   # 4, 2 and 1 workgroups per sample
+    x, th, _ = hqml_inputs.make_inputs(n, L, max(batches), seed=3995)
+    ref = None
+    for B in batches:
+        say(f"[gpu] 12-qubit split regimes: batch {B} of {batches}")
+        ctx = hq.Context(n, L, B, obs_mask=0x801, obs_x_mask=0x090)
+        e = ctx.forward(torch.from_numpy(x[:B]), torch.from_numpy(th)).cpu().numpy()
+        w = np.zeros(B, dtype=np.float32)
+        w[0] = 1.0
+        g = ctx.backward(torch.from_numpy(w)).cpu().numpy()
+        ctx.close()
+        if ref is None:
+            ref = (e[0], g)
+            g_ref, e_ref = oracle.backward(x[:1], th, np.ones(1), 0x801, 0x090)
+            assert_e_close(e[:1], e_ref, n, L)
+            assert_grad_close(g, g_ref)
+        else:
+            assert e[0] == ref[0] and np.array_equal(g, ref[1]), f"batch {B} differs from batch {batches[0]}"
+
+
 @pytest.mark.parametrize("entangler", ["cz", "cnot"])
 def test_whole_circuit_deep(entangler):
     """600 layers on the whole-circuit kernel (n = 9: a 4-qubit remainder round plus a
