@@ -998,11 +998,10 @@ int train_impl(hqml_ctx *c, int B, const void *x, const void *theta, const void 
         const SmallArgs a = small_args(c, 2);
         if ((rc = run(c, HQML_K_SMALL, "small-circuit kernel", [&] { return launch_small(a, B, c->r64, c->stream); })))
             return rc;
-        rc = run(c, HQML_K_OTHER, "E reduction", [&] {
-            return launch_ez_reduce(c->e_part, c->r64, B, 1, y, expz, loss, io64, c->dlde, c->e_work, c->epart2,
-                                    c->stream);
+        return run(c, HQML_K_OTHER, "E and gradient reduction", [&] {
+            return launch_small_reduce(c->e_part, c->r64, B, y, expz, loss, io64, c->dlde, c->S, c->H, pl.L, pl.n, grad,
+                                       c->stream);
         });
-        if (rc) return rc;
     } else {
         // The fused last pass emits E; the loss and dL/dE are needed only by the final
         // gradient reduction, so the E reduction runs after the backward sweeps.

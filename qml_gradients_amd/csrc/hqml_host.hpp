@@ -38,6 +38,12 @@ hipError_t launch_stats_reduce(const void *part, int r64, const int2 *map, int B
                                int T, int pass_lo, int pass_hi, double *S, double *chunks, hipStream_t s);
 hipError_t launch_grad_reduce(const double *S, const double *H, const double *dlde, int B, int L, int n,
                               void *grad, int io64, hipStream_t s);
+// The training step's reductions on the whole-circuit path (one <O> partial per sample) in
+// one launch: E, loss, dL/dE (kept in dlde) and the gradient, bitwise as launch_ez_reduce
+// followed by launch_grad_reduce.
+hipError_t launch_small_reduce(const void *e_part, int r64, int B, const void *y, void *e_out, void *loss, int io64,
+                               double *dlde, const double *S, const double *H, int L, int n, void *grad,
+                               hipStream_t s);
 // gate-by-gate comparator (hqml_gbg.hip)
 hipError_t launch_gbg_zero(float2 *psi, int n, int B, hipStream_t s);
 hipError_t launch_gbg_rot(int gate, float2 *psi, int n, int B, int q, const float *ang, int ang_stride,

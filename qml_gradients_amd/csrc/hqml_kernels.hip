@@ -1932,38 +1932,61 @@ __global__ void k_prep_zyz(const TI *theta, int L, int n, double *zyz)
 // tile passes): the same rewrite, but an X^g moved left through the chain P becomes
 // X^(P^-1 g), P^-1 g = g ^ (g << 1) (no Z appears), so the frame is a qubit mask carried
 // from layer to layer by one thread.
+// Rewrite flags (sin > cos, layers l >= 1) of qubit q for the 32 layers lhi, lhi - 1, ...:
+// bit k for layer lhi - k.  The 64 loads are issued before any is used (the scan below
+// stores between its reads, and a byte store may alias the table, so reading layer by
+// layer would wait a memory round trip per layer).
+__device__ __forceinline__ uint32_t prep_rewrite_flags(const double *zyz, int n, int q, int lhi)
+{
+    double s[32], c[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+        const int l = lhi - k;
+        const double *z = zyz + ((size_t)(l >= 1 ? l : 1) * n + q) * 6;
+        c[k] = z[0];
+        s[k] = z[1];
+    }
+    uint32_t f = 0;
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+        if (lhi - k >= 1 && s[k] > c[k]) f |= 1u << k;
+    return f;
+}
+
 __device__ __forceinline__ void prep_frame_at(const double *zyz, int L, int n, int ent, unsigned char *G, int q)
 {
     if (ent == 2) {
         // one wave, lane q = qubit q (n <= 29 < 64); the mask g is the same in every lane
         const uint32_t full = (uint32_t)((1ull << n) - 1ull);
         uint32_t g = 0;
-        for (int l = L - 1; l >= 0; --l) {
-            if (q < n) G[(size_t)l * n + q] = (unsigned char)((g >> q) & 1u);
-            if (l == 0) break;
-            // qubits rewritten at layer l: their X enters before Ry, after diag(r_l)
-            bool rwq = false;
-            if (q < n) {
-                const double *z = zyz + ((size_t)l * n + q) * 6;
-                rwq = z[1] > z[0];
+        for (int lhi = L - 1; lhi >= 0; lhi -= 32) {
+            const uint32_t f = (q < n && L > 1) ? prep_rewrite_flags(zyz, n, q, lhi) : 0u;
+            for (int k = 0; k < 32 && lhi - k >= 0; ++k) {
+                const int l = lhi - k;
+                if (q < n) G[(size_t)l * n + q] = (unsigned char)((g >> q) & 1u);
+                if (l == 0) break;
+                // qubits rewritten at layer l: their X enters before Ry, after diag(r_l)
+                const uint32_t rw = (uint32_t)__ballot((f >> k) & 1u) & full;
+                const uint32_t gb = g ^ rw;
+                g = (gb ^ (gb << 1)) & full;
             }
-            const uint32_t rw = (uint32_t)__ballot(rwq) & full;
-            const uint32_t gb = g ^ rw;
-            g = (gb ^ (gb << 1)) & full;
         }
         return;
     }
     if (q >= n) return;
     unsigned char g = 0;
-    for (int l = L - 1; l >= 0; --l) {
-        G[(size_t)l * n + q] = g;
-        const double *z = zyz + ((size_t)l * n + q) * 6;
-        if (ent == 0 && l >= 1 && z[1] > z[0]) g ^= 1;
+    for (int lhi = L - 1; lhi >= 0; lhi -= 32) {
+        const uint32_t f = (ent == 0 && L > 1) ? prep_rewrite_flags(zyz, n, q, lhi) : 0u;
+        for (int k = 0; k < 32 && lhi - k >= 0; ++k) {
+            const int l = lhi - k;
+            G[(size_t)l * n + q] = g;
+            if ((f >> k) & 1u) g ^= 1;
+        }
     }
 }
 
 #if HQML_BWD32_UNIT == 0   // a non-template kernel: defined in one compilation unit only
-__global__ void k_prep_frame(const double *zyz, int L, int n, int ent, unsigned char *G)
+__global__ void __launch_bounds__(64) k_prep_frame(const double *zyz, int L, int n, int ent, unsigned char *G)
 {
     prep_frame_at(zyz, L, n, ent, G, blockIdx.x * blockDim.x + threadIdx.x);
 }
@@ -2149,26 +2172,33 @@ __global__ void __launch_bounds__(kTileChunk) k_ez_chunks(const P *e_part, int T
 
 // E_b = sum over the T per-tile (or per-chunk) partials of sample b in order; with
 // labels y also the MSE loss and dL/dE_b = 2 (E_b - y_b) / B.  IO is the caller's
-// array type (float or double).
+// array type (float or double).  One workgroup of kEzThreads threads.
+constexpr int kEzThreads = 256;
+// The loss: thread t adds the squared errors of samples t, t + 256, ... in order, then
+// thread 0 adds the 256 partials in order (a fixed order; the partials stay on chip).
 template <typename P, typename IO>
-__global__ void k_ez_reduce(const P *e_part, int B, int T, const IO *y, IO *e_out, IO *loss, double *dlde,
-                            double *e_work)
+__global__ void __launch_bounds__(kEzThreads) k_ez_reduce(const P *e_part, int B, int T, const IO *y, IO *e_out,
+                                                         IO *loss, double *dlde, double *e_work)
 {
-    for (int b = threadIdx.x; b < B; b += blockDim.x) {
+    __shared__ double part[kEzThreads];
+    double acc = 0.0;
+    for (int b = threadIdx.x; b < B; b += kEzThreads) {
         double s = 0.0;
         for (int t = 0; t < T; ++t) s += (double)e_part[(size_t)b * T + t];
         e_work[b] = s;
         e_out[b] = (IO)s;
-        if (y) dlde[b] = 2.0 * (s - (double)y[b]) / (double)B;
-    }
-    __syncthreads();
-    if (y && threadIdx.x == 0) {
-        double acc = 0.0;
-        for (int b = 0; b < B; ++b) {
-            const double d = e_work[b] - (double)y[b];
+        if (y) {
+            const double d = s - (double)y[b];
+            dlde[b] = 2.0 * d / (double)B;
             acc += d * d;
         }
-        *loss = (IO)(acc / (double)B);
+    }
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    if (y && threadIdx.x == 0) {
+        double sum = 0.0;
+        for (int k = 0; k < kEzThreads; ++k) sum += part[k];
+        *loss = (IO)(sum / (double)B);
     }
 }
 
@@ -2238,6 +2268,52 @@ __global__ void __launch_bounds__(256) k_grad_reduce(const double *S, const doub
     for (int b = lane; b < B; b += 64) {
         const double *sb = S + ((size_t)b * L * n + lq) * 3;
         acc += dlde[b] * (h0 * sb[0] + h1 * sb[1] + h2 * sb[2]);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    if (lane == 0) grad[idx] = (IO)acc;
+}
+
+// The training step's reductions on the whole-circuit path (one <O> per sample) in one
+// launch: block 0 also forms E_b, the loss and dL/dE_b exactly as k_ez_reduce does with one
+// partial per sample, and every wave of the gradient reduction (as k_grad_reduce) forms the
+// dL/dE_b = 2 (E_b - y_b) / B it needs itself, by the same operations, so no block waits for
+// another.  Grid and block as k_grad_reduce (4 outputs per 256-thread block, at least one
+// block).
+template <typename P, typename IO>
+__global__ void __launch_bounds__(256) k_small_reduce(const P *e_part, const IO *y, int B, const double *S,
+                                                       const double *H, int L, int n, IO *e_out, IO *loss,
+                                                       double *dlde, IO *grad)
+{
+    static_assert(kEzThreads == 256, "block 0 reduces the loss as k_ez_reduce does");
+    if (blockIdx.x == 0) {
+        __shared__ double part[kEzThreads];
+        double acc = 0.0;
+        for (int b = threadIdx.x; b < B; b += kEzThreads) {
+            const double s = (double)e_part[b];
+            e_out[b] = (IO)s;
+            const double d = s - (double)y[b];
+            dlde[b] = 2.0 * d / (double)B;
+            acc += d * d;
+        }
+        part[threadIdx.x] = acc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double sum = 0.0;
+            for (int k = 0; k < kEzThreads; ++k) sum += part[k];
+            *loss = (IO)(sum / (double)B);
+        }
+    }
+    const int idx = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (idx >= L * n * 3) return;   // whole waves leave together
+    const int lq = idx / 3;
+    const double *h = H + (size_t)idx * 3;
+    const double h0 = h[0], h1 = h[1], h2 = h[2];
+    double acc = 0.0;
+    for (int b = lane; b < B; b += 64) {
+        const double *sb = S + ((size_t)b * L * n + lq) * 3;
+        const double g = 2.0 * ((double)e_part[b] - (double)y[b]) / (double)B;
+        acc += g * (h0 * sb[0] + h1 * sb[1] + h2 * sb[2]);
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
@@ -2440,9 +2516,9 @@ static void ez_typed(const void *e_part, int B, int T, const void *y, void *e_ou
         const int nch = T / kTileChunk;
         k_ez_chunks<P><<<dim3((unsigned)nch, (unsigned)B), kTileChunk, 0, s>>>(static_cast<const P *>(e_part), T,
                                                                                chunks);
-        k_ez_reduce<double, IO><<<1, 256, 0, s>>>(chunks, B, nch, yy, eo, lo, dlde, e_work);
+        k_ez_reduce<double, IO><<<1, kEzThreads, 0, s>>>(chunks, B, nch, yy, eo, lo, dlde, e_work);
     } else {
-        k_ez_reduce<P, IO><<<1, 256, 0, s>>>(static_cast<const P *>(e_part), B, T, yy, eo, lo, dlde, e_work);
+        k_ez_reduce<P, IO><<<1, kEzThreads, 0, s>>>(static_cast<const P *>(e_part), B, T, yy, eo, lo, dlde, e_work);
     }
 }
 
@@ -2507,6 +2583,30 @@ hipError_t launch_grad_reduce(const double *S, const double *H, const double *dl
         k_grad_reduce<double><<<blocks, 256, 0, s>>>(S, H, dlde, B, L, n, static_cast<double *>(grad));
     else
         k_grad_reduce<float><<<blocks, 256, 0, s>>>(S, H, dlde, B, L, n, static_cast<float *>(grad));
+    return hipGetLastError();
+}
+
+hipError_t launch_small_reduce(const void *e_part, int r64, int B, const void *y, void *e_out, void *loss, int io64,
+                               double *dlde, const double *S, const double *H, int L, int n, void *grad,
+                               hipStream_t s)
+{
+    const unsigned blocks = (unsigned)std::max(1, (L * n * 3 + 3) / 4);
+#define HQML_SMALL_REDUCE(P, IO)                                                                               \
+    k_small_reduce<P, IO><<<blocks, 256, 0, s>>>(static_cast<const P *>(e_part), static_cast<const IO *>(y), B, S, H, \
+                                                 L, n, static_cast<IO *>(e_out), static_cast<IO *>(loss), dlde,     \
+                                                 static_cast<IO *>(grad))
+    if (r64) {
+        if (io64)
+            HQML_SMALL_REDUCE(double, double);
+        else
+            HQML_SMALL_REDUCE(double, float);
+    } else {
+        if (io64)
+            HQML_SMALL_REDUCE(float, double);
+        else
+            HQML_SMALL_REDUCE(float, float);
+    }
+#undef HQML_SMALL_REDUCE
     return hipGetLastError();
 }
 #endif  // HQML_BWD32_UNIT

@@ -4,7 +4,7 @@
 // hqml_train_step_noalloc runs the whole-circuit training step (n <= 13: the circuit of
 // one sample per workgroup) with the same kernels, in the same order, as
 // hqml_train_step on a context: table preparation, the whole-circuit kernel (forward,
-// <O>, adjoint statistics), the <O> / loss reduction and the gradient reduction.  What a
+// <O>, adjoint statistics), then <O>, the loss and the gradient reduced in one launch.  What a
 // context keeps in its workspace (tables, per-sample statistics, sums) lives here in one
 // fixed device buffer, `scratch`, of HQML_NOALLOC_SCRATCH_BYTES.  Each GPU holds its own
 // copy from the moment the library's code is loaded on it until the process ends; the
@@ -73,7 +73,7 @@ struct Parts {
     void *rot_tf, *dw;
     double *H;
     void *init_u, *e_part;
-    double *S, *dlde, *e_work;
+    double *S, *dlde;
 };
 
 // The parts a step of B samples needs (base == nullptr: sizes only); returns the bytes.
@@ -90,7 +90,6 @@ size_t carve_parts(char *base, int B, int L, int n, size_t rb, Parts *p)
     p->e_part = c.take(b * rb);
     p->S = static_cast<double *>(c.take(b * Ln * 3 * 8));
     p->dlde = static_cast<double *>(c.take(b * 8));
-    p->e_work = static_cast<double *>(c.take(b * 8));
     return c.used;
 }
 
@@ -161,9 +160,8 @@ extern "C" int hqml_train_step_noalloc(const hqml_config *cfg, int B, const floa
     config_observable(cfg, plan, &a.obs, &a.obs_x, &neg);
     e = launch_small(a, B, r64, st);
     if (e != hipSuccess) return noalloc_fail(HQML_ERR_HIP, std::string("small-circuit kernel: ") + hipGetErrorString(e));
-    e = launch_ez_reduce(parts.e_part, r64, B, 1, y, expz, loss, 0, parts.dlde, parts.e_work, nullptr, st);
-    if (e != hipSuccess) return noalloc_fail(HQML_ERR_HIP, std::string("E reduction: ") + hipGetErrorString(e));
-    e = launch_grad_reduce(parts.S, parts.H, parts.dlde, B, L, n, grad, 0, st);
-    if (e != hipSuccess) return noalloc_fail(HQML_ERR_HIP, std::string("gradient reduction: ") + hipGetErrorString(e));
+    e = launch_small_reduce(parts.e_part, r64, B, y, expz, loss, 0, parts.dlde, parts.S, parts.H, L, n, grad, st);
+    if (e != hipSuccess)
+        return noalloc_fail(HQML_ERR_HIP, std::string("E and gradient reduction: ") + hipGetErrorString(e));
     return HQML_OK;
 }
