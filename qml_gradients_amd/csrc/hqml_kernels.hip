@@ -2135,19 +2135,24 @@ __global__ void k_prep_init(const TI *x, const double *zyz, const unsigned char 
 
 // All four preparation steps in one workgroup, for small tables (one launch instead of
 // four: at 12 qubits / 20 layers the separate launches cost 19 us of a 0.27 ms step).
-// Global writes by the workgroup are visible to it after each barrier.
 template <typename TI, typename R>
 __global__ void __launch_bounds__(kPrepThreads) k_prep_fused(const TI *theta, const TI *x, int L, int n, int B, int ent,
                                                               double *zyz, unsigned char *G, R *rot_tf, R *dw,
                                                               double *H, R *init_u)
 {
+    // the factorisation and the frame stay in LDS (no later kernel reads them), so the steps
+    // after each barrier read them without a memory round trip
+    (void)zyz;
+    (void)G;
+    __shared__ double zs[kPrepThreads * 6];
+    __shared__ unsigned char gs[kPrepThreads];
     const int t = threadIdx.x;
-    for (int i = t; i < L * n; i += kPrepThreads) prep_zyz_at(theta, L, n, zyz, i);
+    for (int i = t; i < L * n; i += kPrepThreads) prep_zyz_at(theta, L, n, zs, i);
     __syncthreads();
-    if (t < 64) prep_frame_at(zyz, L, n, ent, G, t);   // wave 0: the frame is a scan over layers
+    if (t < 64) prep_frame_at(zs, L, n, ent, gs, t);   // wave 0: the frame is a scan over layers
     __syncthreads();
-    for (int i = t; i < L * n; i += kPrepThreads) prep_tables_at(theta, zyz, G, L, n, ent, rot_tf, dw, H, i);
-    for (int i = t; i < B * n; i += kPrepThreads) prep_init_at(x, zyz, G, B, n, init_u, i);
+    for (int i = t; i < L * n; i += kPrepThreads) prep_tables_at(theta, zs, gs, L, n, ent, rot_tf, dw, H, i);
+    for (int i = t; i < B * n; i += kPrepThreads) prep_init_at(x, zs, gs, B, n, init_u, i);
 }
 
 // ------------------------------------------------------------------ reductions (fixed order)
