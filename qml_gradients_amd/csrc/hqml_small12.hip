@@ -297,7 +297,8 @@ __device__ __forceinline__ float s12_fwd_step(HTile<float> &p, const SmallArgs &
 // undone on LA's qubits], transpose through buffers 2 (l & 1) and 2 (l & 1) + 1, the sums of
 // layer l+1's statistics, statistics of the other qubits (their values unchanged by the
 // first undone rotations, which act on other qubits: only their scale enters), [Ry-layer l
-// undone on those].  Returns the next pending scale.
+// undone on those].  Statistics only of the workgroup's share of the qubits (sel, qmask; see
+// s12_part).  Returns the next pending scale.
 template <bool LA>
 __device__ __forceinline__ float s12_adj_step(HTile<float> &p, HTile<float> &q, const SmallArgs &a, int b, int l,
                                               float c, float2 *bufs, float *red, const int (&sel)[2], uint32_t qmask,
