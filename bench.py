@@ -458,8 +458,9 @@ def main():
                               small_kernel_name(w.n_qubits, args.entangler, args.compute))
         if roof_small:
             roof_small["peak_basis"] = ("non-packed fp32 FMA: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz "
-                                        "(self-derived); one workgroup per sample, so a batch of B uses at most B "
-                                        "of the 256 compute units")
+                                        "(self-derived); one workgroup per sample (at 12 qubits up to four, which "
+                                        "repeat the forward pass and the un-computation: work the algorithmic "
+                                        "count leaves out), so a batch of B keeps at most B (4B) compute units busy")
     step_bytes = fwd_b + bwd_b
     out = {
         "metric": "train samples/sec (fwd+adjoint bwd) 20q HEA 100L; achieved HBM GB/s vs peak",
