@@ -9,7 +9,7 @@ import pytest
 
 import hqml_inputs
 import oracle
-from gpu_util import assert_e_close, assert_grad_close, say
+from gpu_util import assert_e_close, assert_grad_close, assert_grad_rel, say
 
 pytestmark = pytest.mark.gpu
 
@@ -108,7 +108,12 @@ def test_named_workload_full(name):
     torch.cuda.synchronize()
     e_ref, loss_ref, g_ref = oracle.train_step(x, th, y)
     assert_e_close(e.cpu().numpy(), e_ref, w.n_qubits, w.n_layers)
+    assert abs(float(loss.cpu()[0]) - loss_ref) <= 1e-5 * max(1.0, loss_ref)
     assert_grad_close(g.cpu().numpy(), g_ref)
+    # the bound that binds where gradients are small: relative to the largest entry (measured
+    # 3.5e-7 at 4 qubits / 2 layers and 2.1e-6 at 12 qubits / 20 layers)
+    r = assert_grad_rel(g.cpu().numpy(), g_ref, 1e-4, f"{name} batch gradient")
+    say(f"[gpu] {name}: max|dg| / max|g_ref| = {r:.2e}")
     ctx.close()
 
 
